@@ -1,0 +1,428 @@
+"""CPU oracle of the dropless MoE layer hot path.
+
+TEST INFRASTRUCTURE, NOT PRODUCT CODE.  Only the test-suite, the smoke entry
+point and the CPU-baseline leg of the benchmark may import or call this module.
+The HIP library never routes through it, and it shares no code, table or helper
+with the HIP path: every conversion below (bf16 rounding, E4M3 coding, the MX
+block scale) is written out here from its definition.
+
+Precision: float64 throughout.  Results are rounded only where the layer
+stores a value in a narrower type (fp32 logits/probabilities, bf16 or fp32
+activations and outputs, MXFP8 codes and scales).
+
+The layer, as the pages describe it (bpdata article "Dropless MoE ... JAX ...
+Transformer Engine", figure "an expert-parallel MoE layer across two GPUs"):
+the router assigns each token to K experts, token rows are grouped by expert,
+a grouped MLP runs two grouped GEMMs on the variable-length groups, and the
+combine restores the original token order.  The single-GPU share of that path
+is computed here by plain definitions:
+
+  route_topk            sort-based top-K with lowest-index tie-break
+  route_topk_repeated_argmax   the K-repeated-scan selection the "Preserve a
+                        compact route" section of the sparser-MoE page names as
+                        the original path (kept as an independent second
+                        oracle for the pins)
+  count_and_permute     stable counting sort of the valid local routes
+  mx_quantize_rows      OCP Microscaling (MX) v1.0 block quantization, E4M3
+  grouped_mlp           per-expert dense SwiGLU MLP in float64
+  combine               probability-weighted sum in k order
+
+Every function is parity-pinned by tests/test_oracle_*.py (pages' worked sizes,
+closed forms, brute force, a second algorithm, library reductions); the whole
+layer against the pages is "parity unpinned" because the pages print no layer
+values (only its parts are pinned).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+# ---------------------------------------------------------------------------
+# Number formats (written from their definitions)
+# ---------------------------------------------------------------------------
+
+BF16_MAX = float.fromhex("0x1.fep127")
+
+
+def _floor_log2(a: np.ndarray) -> np.ndarray:
+    """floor(log2 |a|) for finite non-zero a, read exactly from frexp."""
+    _, e = np.frexp(np.asarray(a, dtype=np.float64))
+    return e.astype(np.int64) - 1
+
+
+def bf16_round(v) -> np.ndarray:
+    """Round float64 values to the nearest bf16 value, ties to even.
+
+    bf16 keeps 8 significant bits and fp32's exponent range: the spacing of
+    representable values near |v| is 2^(max(floor(log2|v|), -126) - 7).
+    Values beyond the largest finite bf16 become +-inf.
+    """
+    v = np.asarray(v, dtype=np.float64)
+    out = np.zeros_like(v)
+    nz = v != 0
+    e = np.maximum(_floor_log2(np.where(nz, v, 1.0)), -126)
+    q = np.ldexp(1.0, (e - 7).astype(np.int64))
+    r = np.round(v / q) * q  # np.round is round-half-to-even; v/q is exact
+    r = np.where(np.abs(r) > BF16_MAX, np.copysign(np.inf, v), r)
+    out[nz] = r[nz]
+    out[~nz] = v[~nz]  # keeps the sign of zero
+    return out
+
+
+def bf16_to_bits(v) -> np.ndarray:
+    """Bit patterns (uint16) of values that are already exact bf16 values."""
+    f = np.asarray(v, dtype=np.float64).astype(np.float32)
+    return (f.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+
+
+def bits_to_bf16(bits) -> np.ndarray:
+    """bf16 bit patterns -> float64 values (exact)."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    with np.errstate(invalid="ignore"):
+        return b.view(np.float32).astype(np.float64)
+
+
+# OCP 8-bit floating point E4M3 ("fn" variant): bias 7, 3 mantissa bits, no
+# infinities, S.1111.111 is NaN, largest finite magnitude 448, smallest normal
+# 2^-6, smallest subnormal 2^-9.
+E4M3_MAX = 448.0
+E4M3_EMIN = -6
+E4M3_MBITS = 3
+E4M3_EMAX_ELEM = 8  # exponent of the largest normal (448 = 1.75 * 2^8)
+
+
+def e4m3_decode(codes) -> np.ndarray:
+    """E4M3 byte codes -> float64 values (NaN for the NaN codes)."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    s = np.where((c >> 7) & 1, -1.0, 1.0)
+    ex = (c >> 3) & 15
+    m = c & 7
+    sub = np.ldexp(m / 8.0, E4M3_EMIN)
+    nrm = np.ldexp(1.0 + m / 8.0, (ex - 7))
+    val = s * np.where(ex == 0, sub, nrm)
+    return np.where((ex == 15) & (m == 7), np.nan, val)
+
+
+def e4m3_round(q) -> np.ndarray:
+    """Round float64 values to the E4M3 grid, ties to even, saturating at +-448.
+
+    The spacing near |q| is 2^(max(floor(log2|q|), -6) - 3); magnitudes that
+    round above 448 are clamped to 448 (the MX conversion saturates normals).
+    The sign of zero is kept.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    nz = q != 0
+    e = np.maximum(_floor_log2(np.where(nz, q, 1.0)), E4M3_EMIN)
+    quantum = np.ldexp(1.0, (e - E4M3_MBITS).astype(np.int64))
+    r = np.round(q / quantum) * quantum
+    r = np.where(np.abs(r) > E4M3_MAX, np.copysign(E4M3_MAX, q), r)
+    r = np.where(nz, r, q)
+    # a non-zero value that rounds to zero keeps its sign
+    return np.where((r == 0) & np.signbit(q), -0.0, r)
+
+
+def e4m3_encode(r) -> np.ndarray:
+    """Exact E4M3 grid values (from e4m3_round) -> byte codes."""
+    r = np.asarray(r, dtype=np.float64)
+    sign = np.signbit(r).astype(np.int64) << 7
+    a = np.abs(r)
+    code = np.zeros(a.shape, dtype=np.int64)
+    sub = (a > 0) & (a < np.ldexp(1.0, E4M3_EMIN))
+    code = np.where(sub, np.round(a / np.ldexp(1.0, E4M3_EMIN - E4M3_MBITS)).astype(np.int64), code)
+    nrm = a >= np.ldexp(1.0, E4M3_EMIN)
+    e = _floor_log2(np.where(nrm, a, 1.0))
+    man = np.round((np.where(nrm, a, 1.0) / np.ldexp(1.0, e) - 1.0) * 8).astype(np.int64)
+    code = np.where(nrm, ((e + 7) << 3) | man, code)
+    return (code | sign).astype(np.uint8)
+
+
+# ---------------------------------------------------------------------------
+# MX block quantization (OCP Microscaling Formats Specification v1.0)
+# ---------------------------------------------------------------------------
+
+MX_BLOCK = 32
+
+
+def mx_quantize_rows(v):
+    """Quantize each row of v (bf16 values as float64) in blocks of 32.
+
+    Follows the OCP MX v1.0 conversion with E4M3 elements: for each block of
+    32 consecutive elements along the row (the contraction dimension), the
+    shared exponent is E = floor(log2(max|v|)) - 8 (8 = exponent of E4M3's
+    largest normal), clamped to the E8M0 range [-127, 127] (E = -127 for an
+    all-zero block).  Each element is v * 2^-E rounded to E4M3 (nearest, ties
+    to even, saturating at 448).  Returns (codes uint8 [R,C], scales uint8
+    [R,C/32] holding E + 127).
+
+    The pages name group-aware MXFP8 quantization as a building block
+    (bpdata article, "Transformer Engine building blocks for dropless MoE in
+    JAX"; "Optimization 1: Grouped GEMM" for MXFP8 block scaling of the expert
+    matmuls); the block rule is the published MX specification's.
+    """
+    v = np.asarray(v, dtype=np.float64)
+    R, C = v.shape
+    if C % MX_BLOCK:
+        raise ValueError("row length must be a multiple of 32")
+    blk = v.reshape(R, C // MX_BLOCK, MX_BLOCK)
+    amax = np.abs(blk).max(axis=2)
+    E = np.where(amax > 0, _floor_log2(np.where(amax > 0, amax, 1.0)) - E4M3_EMAX_ELEM, -127)
+    E = np.clip(E, -127, 127)
+    q = blk * np.ldexp(1.0, -E)[:, :, None]  # exact: a power-of-two scaling
+    codes = e4m3_encode(e4m3_round(q)).reshape(R, C)
+    scales = (E + 127).astype(np.uint8)
+    return codes, scales
+
+
+def mx_dequantize_rows(codes, scales) -> np.ndarray:
+    codes = np.asarray(codes)
+    R, C = codes.shape
+    vals = e4m3_decode(codes).reshape(R, C // MX_BLOCK, MX_BLOCK)
+    s = np.ldexp(1.0, np.asarray(scales).astype(np.int64) - 127)
+    return (vals * s[:, :, None]).reshape(R, C)
+
+
+# ---------------------------------------------------------------------------
+# Route: projection, score, top-K, probabilities
+# ---------------------------------------------------------------------------
+
+def router_logits(x, w_router) -> np.ndarray:
+    """logits[T,E] = x[T,H] . W_r[H,E], exact products summed in float64,
+    stored as fp32 (the router works in fp32; the pages' layer figure starts
+    with the router assigning tokens to experts)."""
+    return (np.asarray(x, np.float64) @ np.asarray(w_router, np.float64)).astype(np.float32)
+
+
+def selection_keys(logits, bias=None) -> np.ndarray:
+    """z = logit (+ per-expert bias, one fp32 rounding), -0.0 replaced by +0.0."""
+    z = np.asarray(logits, dtype=np.float32)
+    if bias is not None:
+        z = (z + np.asarray(bias, dtype=np.float32)[None, :]).astype(np.float32)
+    z = np.where(z == 0, np.float32(0.0), z).astype(np.float32)
+    if not np.all(np.isfinite(z)):
+        raise ValueError("non-finite router logits")
+    return z
+
+
+def _probabilities(zs, score):
+    zs = np.asarray(zs, dtype=np.float64)
+    if score == "softmax":
+        e = np.exp(zs - zs[:, :1])
+        p = e / e.sum(axis=1, keepdims=True)
+    elif score == "sigmoid":
+        s = 1.0 / (1.0 + np.exp(-zs))
+        p = s / s.sum(axis=1, keepdims=True)
+    else:
+        raise ValueError(score)
+    return p.astype(np.float32)
+
+
+def route_topk(logits, K, score="softmax", bias=None, mask=None):
+    """Top-K experts per token and their probabilities.
+
+    Selection: the K largest keys z (logit plus optional bias), ties broken by
+    the lower expert index; the IDs are listed in that order (descending key).
+    The result is the compact [T,K] int16 ID list of the sparser-MoE page,
+    "Preserve a compact route"; masked tokens carry -1 routes (same section:
+    invalid -1 routes are preserved).
+    Probabilities: softmax over the K selected keys, or for score="sigmoid"
+    sigma(z_k) / sum_j sigma(z_j) over the selected keys; fp32.
+    """
+    z = selection_keys(logits, bias)
+    T, E = z.shape
+    if not (1 <= K <= E):
+        raise ValueError("need 1 <= K <= E")
+    order = np.argsort(-z, axis=1, kind="stable")  # stable: equal keys keep index order
+    ids = order[:, :K].astype(np.int64)
+    zs = np.take_along_axis(z, ids, axis=1)
+    p = _probabilities(zs, score)
+    ids = ids.astype(np.int16)
+    if mask is not None:
+        m = np.asarray(mask).astype(bool)
+        ids[m] = -1
+        p[m] = 0.0
+    return ids, p
+
+
+def route_topk_repeated_argmax(logits, K, score="softmax", bias=None, mask=None):
+    """Second, independent selection: K passes, each scanning the whole row
+    for the next maximum (np.argmax returns the first, i.e. lowest-index,
+    maximum).  This is the T x E x K scan the sparser-MoE page ("Preserve a
+    compact route") says the radix/threshold selection replaced."""
+    z = selection_keys(logits, bias).astype(np.float64)
+    T, E = z.shape
+    ids = np.zeros((T, K), dtype=np.int64)
+    work = z.copy()
+    for k in range(K):
+        j = np.argmax(work, axis=1)
+        ids[:, k] = j
+        work[np.arange(T), j] = -np.inf
+    zs = np.take_along_axis(z, ids, axis=1)
+    p = _probabilities(zs, score)
+    ids = ids.astype(np.int16)
+    if mask is not None:
+        m = np.asarray(mask).astype(bool)
+        ids[m] = -1
+        p[m] = 0.0
+    return ids, p
+
+
+# ---------------------------------------------------------------------------
+# Count / scan / permute
+# ---------------------------------------------------------------------------
+
+def count_and_permute(ids, e0, L, x=None, E_global=None):
+    """Group the valid local routes by expert (a stable counting sort).
+
+    A slot (t,k) is local when e0 <= ids[t,k] < e0+L; -1 slots and other
+    ranks' experts are skipped (sparser-MoE page, "Remove work that has no
+    selected route": only selected local slots are visited).  Rows are ordered
+    by local expert, and within an expert by flat slot index f = t*K + k.
+
+    Returns counts [L], offsets [L+1] (offsets[L] = N), row_to_slot [N]
+    (= f), slot_to_row [T,K] (-1 where not local) and, when x is given,
+    x_perm [N,H] = x[f // K].  Nothing is padded and nothing is dropped
+    (bpdata article, "Optimization 1: Grouped GEMM": only valid regions).
+    """
+    ids = np.asarray(ids).astype(np.int64)
+    T, K = ids.shape
+    if E_global is not None and ((ids < -1) | (ids >= E_global)).any():
+        raise ValueError("expert id out of range")
+    flat_ids = ids.ravel()
+    valid = (flat_ids >= e0) & (flat_ids < e0 + L)
+    f = np.flatnonzero(valid)
+    le = flat_ids[f] - e0
+    order = np.argsort(le, kind="stable")
+    row_to_slot = f[order].astype(np.int64)
+    counts = np.bincount(le, minlength=L).astype(np.int64)
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
+    slot_to_row = np.full(T * K, -1, dtype=np.int64)
+    slot_to_row[row_to_slot] = np.arange(row_to_slot.size)
+    out = {
+        "counts": counts,
+        "offsets": offsets,
+        "row_to_slot": row_to_slot,
+        "slot_to_row": slot_to_row.reshape(T, K),
+    }
+    if x is not None:
+        out["x_perm"] = np.asarray(x)[row_to_slot // K]
+    return out
+
+
+# ---------------------------------------------------------------------------
+# Grouped SwiGLU MLP
+# ---------------------------------------------------------------------------
+
+def swiglu(h, F):
+    """a = silu(gate) * up with gate = h[:, :F], up = h[:, F:], silu(g) = g*sigma(g)
+    (Shazeer 2020, "GLU Variants Improve Transformer")."""
+    g = h[:, :F]
+    u = h[:, F:]
+    return g / (1.0 + np.exp(-g)) * u
+
+
+def round_to(v, dtype):
+    if dtype == "f32":
+        return np.asarray(v, np.float64).astype(np.float32).astype(np.float64)
+    if dtype in ("bf16", "mxfp8"):
+        return bf16_round(v)
+    if dtype == "f64":
+        return np.asarray(v, np.float64)
+    raise ValueError(dtype)
+
+
+def expert_mlp(X, W1e, W2e, dtype):
+    """One expert's SwiGLU MLP on rows X (float64 values of the stored rows).
+
+    dtype "f32"/"bf16": h = X.W1e (float64), a = swiglu(h) stored in dtype,
+    y = a.W2e stored in dtype.
+    dtype "mxfp8": X, W1e (per column, along H), a (after bf16 rounding,
+    along F) and W2e (per column, along F) are MX-quantized and dequantized
+    exactly before each float64 product; y is stored as bf16.
+    Returns (y, a_stored) with a_stored the activations as stored before GEMM2
+    (bf16 values for mxfp8, before their quantization).
+    """
+    X = np.asarray(X, np.float64)
+    W1e = np.asarray(W1e, np.float64)
+    W2e = np.asarray(W2e, np.float64)
+    F = W2e.shape[0]
+    if dtype == "mxfp8":
+        Xq = mx_dequantize_rows(*mx_quantize_rows(X))
+        W1q = mx_dequantize_rows(*mx_quantize_rows(W1e.T)).T
+        h = Xq @ W1q
+        a = bf16_round(swiglu(h, F))
+        aq = mx_dequantize_rows(*mx_quantize_rows(a))
+        W2q = mx_dequantize_rows(*mx_quantize_rows(W2e.T)).T
+        y = bf16_round(aq @ W2q)
+        return y, a
+    h = X @ W1e
+    a = round_to(swiglu(h, F), dtype)
+    y = round_to(a @ W2e, dtype)
+    return y, a
+
+
+def grouped_mlp(x_perm, offsets, W1, W2, dtype):
+    """Grouped MLP over the expert-ordered rows (bpdata article, "Optimization
+    1: Grouped GEMM": every expert's matmuls use its actual token count and only
+    valid regions are computed).  Rows [offsets[e], offsets[e+1]) go through
+    expert e's MLP; empty experts produce nothing.  W1[e], W2[e] may be any
+    indexable sequence of per-expert matrices.  Returns (y_perm, a)."""
+    x_perm = np.asarray(x_perm, np.float64)
+    N = int(offsets[-1])
+    H = x_perm.shape[1] if x_perm.ndim == 2 else 0
+    y = np.zeros((N, H), np.float64)
+    a_all = None
+    for e in range(len(offsets) - 1):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        if hi == lo:
+            continue
+        ye, ae = expert_mlp(x_perm[lo:hi], W1[e], W2[e], dtype)
+        if a_all is None:
+            a_all = np.zeros((N, ae.shape[1]), np.float64)
+        y[lo:hi] = ye
+        a_all[lo:hi] = ae
+    return y, a_all
+
+
+# ---------------------------------------------------------------------------
+# Unpermute + probability-weighted combine
+# ---------------------------------------------------------------------------
+
+def combine(y_perm, slot_to_row, probs, out_dtype):
+    """out[t] = sum over k (in k order) of probs[t,k] * y_perm[slot_to_row[t,k]]
+    for the slots with a row; tokens without one get a zero row.  This restores
+    the original token order (bpdata article, layer figure: "combine restores
+    token order")."""
+    y_perm = np.asarray(y_perm, np.float64)
+    s2r = np.asarray(slot_to_row)
+    p = np.asarray(probs, np.float64)
+    T, K = s2r.shape
+    H = y_perm.shape[1]
+    out = np.zeros((T, H), np.float64)
+    for k in range(K):
+        r = s2r[:, k]
+        ok = r >= 0
+        out[ok] += p[ok, k][:, None] * y_perm[r[ok]]
+    return round_to(out, out_dtype)
+
+
+# ---------------------------------------------------------------------------
+# Whole layer
+# ---------------------------------------------------------------------------
+
+def layer(x, K, W1, W2, dtype, *, w_router=None, logits=None, score="softmax",
+          bias=None, mask=None, e0=0, L=None):
+    """Route -> count/permute -> grouped MLP -> combine on the CPU.
+
+    x: float64 values of the token rows [T,H]; W1/W2 per expert (float64).
+    Either w_router (the projection is computed) or logits is given.
+    """
+    x = np.asarray(x, np.float64)
+    if logits is None:
+        logits = router_logits(x, w_router)
+    E = logits.shape[1]
+    L = E if L is None else L
+    ids, probs = route_topk(logits, K, score, bias, mask)
+    perm = count_and_permute(ids, e0, L, x, E_global=E)
+    y, a = grouped_mlp(perm["x_perm"], perm["offsets"], W1, W2, dtype)
+    out_dtype = dtype if dtype in ("f32", "f64") else "bf16"
+    out = combine(y, perm["slot_to_row"], probs, out_dtype)
+    return {"logits": logits, "ids": ids, "probs": probs, "y_perm": y, "a": a, "out": out, **perm}

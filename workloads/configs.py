@@ -1,0 +1,81 @@
+"""The workload shapes of the dropless MoE layer (one GPU's share).
+
+Shapes follow the layer description: router top-K over E experts, SwiGLU
+expert FFN with W1 [E,H,2F] (gate columns [0,F), up columns [F,2F)) and
+W2 [E,F,H].  The large-top-K sparse share mirrors the motivating setup of the
+"sparser-moe-end-to-end" page, section "The workload changes the bottleneck":
+2,304 experts, top-36, 32 local experts, a 512-wide latent.
+"""
+from dataclasses import dataclass, field
+
+
+@dataclass(frozen=True)
+class MoEConfig:
+    name: str
+    number: int
+    T: int            # tokens
+    H: int            # hidden / latent width
+    E: int            # global experts
+    K: int            # routes per token
+    F: int            # expert FFN width (SwiGLU: W1 has 2F columns)
+    dtype: str        # "f32" | "bf16" | "mxfp8" (expert path)
+    x_dtype: str      # "f32" | "bf16"
+    wr_dtype: str     # router weight dtype: "f32" | "bf16" | "none" (logits given)
+    score: str        # "softmax" | "sigmoid"
+    e0: int = 0       # first local expert id
+    L: int = 0        # number of local experts (0 -> E)
+    x_std: float = 1.0
+    w_std: float = 0.02
+    bias: str = "none"        # "none" | "zipf"
+    logits: str = "proj"      # "proj" (x . W_r) | "grouped" (cfg-5 construction)
+    mask_every: int = 0       # mask token t when t % mask_every == mask_every-1
+    extra: dict = field(default_factory=dict)
+
+    @property
+    def local(self) -> int:
+        return self.L if self.L else self.E
+
+    @property
+    def seed(self) -> int:
+        return self.number
+
+
+# Gain of the Zipf(s=1.2) per-expert router bias of the DeepSeek-V3-like
+# workload: b_e = -1.2 * gamma * ln(rank_e).  The value is the smallest gain
+# (bisection to 1e-3) for which the seeded draw leaves at least 26 of 256
+# experts (~10%) with no routed token under top-8 selection.  It is produced
+# by tests/golden/calibrate_zipf_gain.py, which runs only the CPU oracle, and
+# re-checked by tests/test_workloads.py.
+ZIPF_GAIN_CFG3 = 1.341
+
+# Offset added to the logits of the 8 expert groups a token draws in the
+# large-top-K share (32 experts per group, group 0 = the local experts).  It
+# is far above the N(0,1) spread, so the top-36 always falls inside the drawn
+# groups and each group receives 36/8 = 4.5 routes per token on average.
+GROUP_OFFSET_CFG5 = 16.0
+
+CONFIGS = {
+    "micro": MoEConfig("micro", 0, T=8, H=32, E=4, K=2, F=32, dtype="f32",
+                       x_dtype="f32", wr_dtype="f32", score="softmax", x_std=1.0, w_std=0.5),
+    "tiny_f32": MoEConfig("tiny_f32", 1, T=256, H=64, E=8, K=2, F=128, dtype="f32",
+                          x_dtype="f32", wr_dtype="f32", score="softmax", x_std=0.02),
+    "mixtral_bf16": MoEConfig("mixtral_bf16", 2, T=4096, H=4096, E=8, K=2, F=14336,
+                              dtype="bf16", x_dtype="bf16", wr_dtype="f32", score="softmax"),
+    "dsv3_bf16": MoEConfig("dsv3_bf16", 3, T=8192, H=7168, E=256, K=8, F=2048,
+                           dtype="bf16", x_dtype="bf16", wr_dtype="bf16", score="sigmoid",
+                           bias="zipf"),
+    "mixtral_mxfp8": MoEConfig("mixtral_mxfp8", 4, T=4096, H=4096, E=8, K=2, F=14336,
+                               dtype="mxfp8", x_dtype="bf16", wr_dtype="f32", score="softmax"),
+    "sparse_share": MoEConfig("sparse_share", 5, T=8192, H=512, E=2304, K=36, F=512,
+                              dtype="bf16", x_dtype="bf16", wr_dtype="none", score="softmax",
+                              e0=0, L=32, logits="grouped", mask_every=64),
+}
+
+
+def get_config(name_or_number) -> MoEConfig:
+    if isinstance(name_or_number, int):
+        for c in CONFIGS.values():
+            if c.number == name_or_number:
+                return c
+        raise KeyError(name_or_number)
+    return CONFIGS[name_or_number]
