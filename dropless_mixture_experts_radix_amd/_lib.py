@@ -1,0 +1,173 @@
+"""ctypes binding of libmoe_mi355x.so (the C ABI in include/moe.h).
+
+Argument marshalling only: every function takes torch tensors that already
+live on the GPU, passes their data pointers, shapes and the current HIP stream
+to the library, and raises MoEError on a non-zero status.  No computation of
+the layer happens here.  Loading fails loudly when the library is missing.
+"""
+import ctypes
+import os
+
+import torch
+
+F32, BF16, MXFP8 = 0, 1, 2
+SOFTMAX, SIGMOID = 0, 1
+DEVERR_BAD_ID, DEVERR_OVERFLOW, DEVERR_NONFINITE = 1, 2, 4
+MAX_K, MAX_E, MAX_L = 64, 4096, 2048
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_mi355x.so")
+
+_I, _I64, _SZ, _P = ctypes.c_int, ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p
+
+_SIGS = {
+    "moe_abi_version": (_I, []),
+    "moe_status_str": (ctypes.c_char_p, [_I]),
+    "moe_router_prepared_bytes": (_SZ, [_I, _I, _I, _I]),
+    "moe_prepare_router": (_I, [_P, _I, _I, _I, _I, _P, _P]),
+    "moe_route_workspace_bytes": (_SZ, [_I, _I, _I, _I]),
+    "moe_route_topk": (_I, [_I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "moe_permute_workspace_bytes": (_SZ, [_I, _I, _I]),
+    "moe_permute": (_I, [_I, _I, _I, _I, _I, _I, _I64, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "moe_prepared_weight_bytes": (_SZ, [_I, _I, _I, _I, _I]),
+    "moe_prepare_weights": (_I, [_I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P]),
+    "moe_grouped_mlp_workspace_bytes": (_SZ, [_I64, _I, _I]),
+    "moe_grouped_mlp": (_I, [_I, _I, _I, _I64, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "moe_unpermute_combine": (_I, [_I, _I, _I, _I, _P, _P, _P, _P, _P]),
+    "moe_mx_quantize": (_I, [_I64, _I, _P, _P, _P, _P, _P]),
+}
+
+
+class MoEError(RuntimeError):
+    pass
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build it with `python -m dropless_mixture_experts_radix_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    for name, (res, args) in _SIGS.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    if lib.moe_abi_version() != 1:
+        raise ImportError("libmoe_mi355x.so ABI version mismatch")
+    return lib
+
+
+lib = _load()
+
+
+def symbols():
+    return list(_SIGS)
+
+
+def status_str(st: int) -> str:
+    return lib.moe_status_str(st).decode()
+
+
+def _check(st, name):
+    if st != 0:
+        raise MoEError(f"{name}: {status_str(st)} (status {st})")
+
+
+def _p(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def dtype_code(t: torch.dtype) -> int:
+    return {torch.float32: F32, torch.bfloat16: BF16, torch.uint8: MXFP8}[t]
+
+
+def _nbytes(t):
+    return 0 if t is None else t.numel() * t.element_size()
+
+
+# ----------------------------------------------------------------- route
+def moe_router_prepared_bytes(H, E, w_dtype, x_dtype):
+    return lib.moe_router_prepared_bytes(H, E, w_dtype, x_dtype)
+
+
+def moe_prepare_router(w_router, x_dtype, prepared):
+    H, E = w_router.shape
+    _check(lib.moe_prepare_router(_p(w_router), dtype_code(w_router.dtype), x_dtype, H, E, _p(prepared),
+                                  _stream()), "moe_prepare_router")
+
+
+def moe_route_workspace_bytes(T, E, H, x_dtype):
+    return lib.moe_route_workspace_bytes(T, E, H, x_dtype)
+
+
+def moe_route_topk(ids, probs, score, *, logits=None, x=None, w_prepared=None, w_dtype=F32, E=None,
+                   bias=None, mask=None, logits_out=None, err=None, workspace=None):
+    T, K = ids.shape
+    if logits is not None:
+        E = logits.shape[1]
+        H, x_dtype = 0, F32
+    else:
+        H = x.shape[1]
+        x_dtype = dtype_code(x.dtype)
+    _check(lib.moe_route_topk(T, E, K, H, score, x_dtype, w_dtype, _p(x), _p(w_prepared), _p(logits), _p(bias),
+                              _p(mask), _p(ids), _p(probs), _p(logits_out), _p(err), _p(workspace),
+                              _nbytes(workspace), _stream()), "moe_route_topk")
+
+
+# ----------------------------------------------------------------- permute
+def moe_permute_workspace_bytes(T, K, L):
+    return lib.moe_permute_workspace_bytes(T, K, L)
+
+
+def moe_permute(x, ids, E_global, e0, L, counts, offsets, x_perm, row_to_slot, slot_to_row, workspace,
+                x_perm_scales=None, err=None, out_dtype=None):
+    T, H = x.shape
+    K = ids.shape[1]
+    capacity = row_to_slot.shape[0]
+    x_dtype = dtype_code(x.dtype)
+    out_dtype = x_dtype if out_dtype is None else out_dtype
+    _check(lib.moe_permute(T, H, K, E_global, e0, L, capacity, x_dtype, out_dtype, _p(x), _p(ids), _p(counts),
+                           _p(offsets), _p(x_perm), _p(x_perm_scales), _p(row_to_slot), _p(slot_to_row), _p(err),
+                           _p(workspace), _nbytes(workspace), _stream()), "moe_permute")
+
+
+# ----------------------------------------------------------------- weights
+def moe_prepared_weight_bytes(L, H, F, dtype, which):
+    return lib.moe_prepared_weight_bytes(L, H, F, dtype, which)
+
+
+def moe_prepare_weights(w1, w2, dtype, w1p, w2p, w1p_scales=None, w2p_scales=None):
+    L, H, F2 = w1.shape
+    _check(lib.moe_prepare_weights(L, H, F2 // 2, dtype_code(w1.dtype), dtype, _p(w1), _p(w2), _p(w1p), _p(w2p),
+                                   _p(w1p_scales), _p(w2p_scales), _stream()), "moe_prepare_weights")
+
+
+# ----------------------------------------------------------------- grouped MLP
+def moe_grouped_mlp_workspace_bytes(capacity, F, dtype):
+    return lib.moe_grouped_mlp_workspace_bytes(capacity, F, dtype)
+
+
+def moe_grouped_mlp(x_perm, offsets, w1p, w2p, y_perm, workspace, dtype, H, F, x_perm_scales=None,
+                    w1p_scales=None, w2p_scales=None):
+    L = offsets.shape[0] - 1
+    capacity = y_perm.shape[0]
+    _check(lib.moe_grouped_mlp(L, H, F, capacity, dtype, _p(x_perm), _p(x_perm_scales), _p(offsets), _p(w1p),
+                               _p(w1p_scales), _p(w2p), _p(w2p_scales), _p(y_perm), _p(workspace),
+                               _nbytes(workspace), _stream()), "moe_grouped_mlp")
+
+
+# ----------------------------------------------------------------- combine
+def moe_unpermute_combine(y_perm, slot_to_row, probs, out):
+    T, K = slot_to_row.shape
+    H = out.shape[1]
+    _check(lib.moe_unpermute_combine(T, K, H, dtype_code(out.dtype), _p(y_perm), _p(slot_to_row), _p(probs),
+                                     _p(out), _stream()), "moe_unpermute_combine")
+
+
+# ----------------------------------------------------------------- MX quantizer
+def moe_mx_quantize(inp, codes, scales, row_limit=None):
+    rows, cols = inp.shape
+    _check(lib.moe_mx_quantize(rows, cols, _p(inp), _p(row_limit), _p(codes), _p(scales), _stream()),
+           "moe_mx_quantize")

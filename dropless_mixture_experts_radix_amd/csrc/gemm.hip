@@ -1,0 +1,282 @@
+// Ragged grouped GEMMs of the expert SwiGLU MLP (fp32 and bf16).
+//
+// bpdata article, "Optimization 1: Grouped GEMM": all expert matmuls in one
+// kernel, each with its expert's actual token count, computing only valid
+// regions, with no device-to-host counts and no worst-case padding.
+//
+// Every workgroup builds the tile schedule from `offsets` on the device: expert
+// e owns ceil(m_e/BM) x (N/BN) output tiles (none when m_e = 0), tiles of one
+// weight panel (same expert and column tile) are consecutive, and a
+// persistent grid walks them.  Workgroups are assigned to the 8 XCDs in turn, so
+// workgroup b works on the virtual slot (b % 8) * (G/8) + b/8: the 32 CUs of an
+// XCD take consecutive tiles and share their A and B panels in that XCD's L2.
+#include "gemm_common.h"
+
+namespace moe {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// ---------------------------------------------------------------------------
+// bf16 grouped GEMM: out tile 256 x 256, k step 64, 512 threads (8 wavefronts
+// as 2 x 4), wavefront tile 128 x 64 = 4 x 2 of v_mfma_f32_32x32x16_bf16.
+// A [rows][Kd] bf16 (expert-ordered rows), B [L][N][Kd] bf16 (prepared,
+// contraction-contiguous).  LDS tiles are double-buffered; their 16-byte
+// chunks are XOR-swizzled by (row % 8) so the fragment reads of 32 rows at one
+// k offset spread over all banks.
+// EPI 0: out[row][col] = bf16(acc)                       (N columns)
+// EPI 1: gate/up column chunks of 32 are interleaved in B; out[row][j] =
+//        bf16(silu(gate) * up)                            (N/2 columns)
+// ---------------------------------------------------------------------------
+#define GB_BM 256
+#define GB_BN 256
+#define GB_BK 64
+
+template <int EPI>
+__global__ __launch_bounds__(512, 1) void k_gemm_bf16(int L, int N, int Kd, int64_t capacity,
+                                                      const bf16_t* __restrict__ A,
+                                                      const int32_t* __restrict__ offsets,
+                                                      const bf16_t* __restrict__ B, bf16_t* __restrict__ out) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  bf16_t* sA = (bf16_t*)smem;                       // [2][256][64]
+  bf16_t* sB = sA + 2 * GB_BM * GB_BK;              // [2][256][64]
+  int32_t* s_pre = (int32_t*)(sB + 2 * GB_BN * GB_BK);  // [L+1]
+  int32_t* s_tmp = s_pre + (L + 1);                 // [16]
+  const int NT = (N + GB_BN - 1) / GB_BN;
+  build_schedule(L, capacity, GB_BM, NT, offsets, s_pre, s_tmp);
+  const int total = s_pre[L];
+  const int tid = threadIdx.x, wv = tid >> 6, l = tid & 63;
+  const int wm = wv >> 2, wn = wv & 3;
+  const int g = l >> 5, r32 = l & 31;
+  const int KT = Kd / GB_BK;
+
+  for (int it = virtual_block(); it < total; it += gridDim.x) {
+    const TileInfo ti = locate_tile(it, L, capacity, GB_BM, NT, offsets, s_pre);
+    const int col0 = ti.nt * GB_BN;
+    // global load assignment: 4 chunks of 16 bytes per thread for A and for B
+    const bf16_t* ga[4];
+    const bf16_t* gb[4];
+    int lds_off[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c = tid + 512 * i, row = c >> 3, kc = c & 7;
+      const int ar = ti.row0 + min(row, ti.rows - 1);
+      ga[i] = A + (long)ar * Kd + kc * 8;
+      const int bc = min(col0 + row, N - 1);
+      gb[i] = B + ((long)ti.e * N + bc) * Kd + kc * 8;
+      lds_off[i] = row * GB_BK + ((kc ^ (row & 7)) << 3);
+    }
+    u32x4 ra[4], rb[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      ra[i] = *(const u32x4*)ga[i];
+      rb[i] = *(const u32x4*)gb[i];
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      *(u32x4*)(sA + lds_off[i]) = ra[i];
+      *(u32x4*)(sB + lds_off[i]) = rb[i];
+    }
+    __syncthreads();
+
+    f32x16 acc[4][2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
+    // m sub-tiles of this wavefront that hold valid rows
+    const int msub = min(4, max(0, (ti.rows - wm * 128 + 31) / 32));
+
+    for (int kt = 0; kt < KT; ++kt) {
+      const int cur = kt & 1;
+      if (kt + 1 < KT) {
+        const int ko = (kt + 1) * GB_BK;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          ra[i] = *(const u32x4*)(ga[i] + ko);
+          rb[i] = *(const u32x4*)(gb[i] + ko);
+        }
+      }
+      const bf16_t* cA = sA + cur * GB_BM * GB_BK;
+      const bf16_t* cB = sB + cur * GB_BN * GB_BK;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const int kc = 2 * s + g;
+        bf16x8 fb[2];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int n = wn * 64 + j * 32 + r32;
+          fb[j] = *(const bf16x8*)(cB + n * GB_BK + ((kc ^ (n & 7)) << 3));
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if (i < msub) {
+            const int m = wm * 128 + i * 32 + r32;
+            const bf16x8 fa = *(const bf16x8*)(cA + m * GB_BK + ((kc ^ (m & 7)) << 3));
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa, fb[j], acc[i][j], 0, 0, 0);
+          }
+        }
+      }
+      if (kt + 1 < KT) {
+        bf16_t* nA = sA + (cur ^ 1) * GB_BM * GB_BK;
+        bf16_t* nB = sB + (cur ^ 1) * GB_BN * GB_BK;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          *(u32x4*)(nA + lds_off[i]) = ra[i];
+          *(u32x4*)(nB + lds_off[i]) = rb[i];
+        }
+      }
+      __syncthreads();
+    }
+
+    // epilogue
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (i >= msub) continue;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int row = wm * 128 + i * 32 + 8 * (v >> 2) + 4 * g + (v & 3);
+        if (row >= ti.rows) continue;
+        const long grow = ti.row0 + row;
+        if (EPI == 0) {
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            const int col = col0 + wn * 64 + j * 32 + r32;
+            if (col < N) out[grow * N + col] = (bf16_t)f32_to_bf16(acc[i][j][v]);
+          }
+        } else {
+          const int jcol = (col0 >> 1) + wn * 32 + r32;
+          if (jcol < (N >> 1))
+            out[grow * (N >> 1) + jcol] = (bf16_t)f32_to_bf16(silu_mul(acc[i][0][v], acc[i][1][v]));
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// fp32 grouped GEMM (VALU): out tile 64 x 64, k step 16, 256 threads, each
+// thread 4 rows x 4 columns: prepared columns 2tx, 2tx+1 and 32+2tx, 32+2tx+1
+// of the tile, which are a matching (gate, up) pair for EPI 1.
+// ---------------------------------------------------------------------------
+#define GF_BM 64
+#define GF_BN 64
+#define GF_BK 16
+
+template <int EPI>
+__global__ __launch_bounds__(256) void k_gemm_f32(int L, int N, int Kd, int64_t capacity,
+                                                  const float* __restrict__ A,
+                                                  const int32_t* __restrict__ offsets,
+                                                  const float* __restrict__ B, float* __restrict__ out) {
+  __shared__ float sA[GF_BM][GF_BK + 1];
+  __shared__ float sB[GF_BN][GF_BK + 1];
+  __shared__ int32_t s_pre[MOE_MAX_L + 1];
+  __shared__ int32_t s_tmp[16];
+  const int NT = (N + GF_BN - 1) / GF_BN;
+  build_schedule(L, capacity, GF_BM, NT, offsets, s_pre, s_tmp);
+  const int total = s_pre[L];
+  const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
+  for (int it = blockIdx.x; it < total; it += gridDim.x) {
+    const TileInfo ti = locate_tile(it, L, capacity, GF_BM, NT, offsets, s_pre);
+    const int col0 = ti.nt * GF_BN;
+    float acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = 0.f;
+    const int lr = tid >> 2, lk = (tid & 3) * 4;
+    const int ar = ti.row0 + min(lr, ti.rows - 1);
+    const int bc = min(col0 + lr, N - 1);
+    const float* pa = A + (long)ar * Kd + lk;
+    const float* pb = B + ((long)ti.e * N + bc) * Kd + lk;
+    for (int k0 = 0; k0 < Kd; k0 += GF_BK) {
+      const float4 va = *(const float4*)(pa + k0);
+      const float4 vb = *(const float4*)(pb + k0);
+      __syncthreads();
+      sA[lr][lk] = va.x; sA[lr][lk + 1] = va.y; sA[lr][lk + 2] = va.z; sA[lr][lk + 3] = va.w;
+      sB[lr][lk] = vb.x; sB[lr][lk + 1] = vb.y; sB[lr][lk + 2] = vb.z; sB[lr][lk + 3] = vb.w;
+      __syncthreads();
+#pragma unroll
+      for (int k = 0; k < GF_BK; ++k) {
+        float a[4], b[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) a[i] = sA[ty * 4 + i][k];
+        b[0] = sB[2 * tx][k];
+        b[1] = sB[2 * tx + 1][k];
+        b[2] = sB[32 + 2 * tx][k];
+        b[3] = sB[32 + 2 * tx + 1][k];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = ty * 4 + i;
+      if (row >= ti.rows) continue;
+      const long grow = ti.row0 + row;
+      if (EPI == 0) {
+        const int cols[4] = {2 * tx, 2 * tx + 1, 32 + 2 * tx, 33 + 2 * tx};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int col = col0 + cols[j];
+          if (col < N) out[grow * N + col] = acc[i][j];
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int jcol = (col0 >> 1) + 2 * tx + j;
+          if (jcol < (N >> 1)) out[grow * (N >> 1) + jcol] = silu_mul(acc[i][j], acc[i][2 + j]);
+        }
+      }
+    }
+  }
+}
+
+static int grid_for(int64_t capacity, int L, int BM, int NT, int per_cu) {
+  const int64_t upper = ((capacity + BM - 1) / BM + L) * (int64_t)NT;
+  int64_t g = (int64_t)num_cus() * per_cu;
+  if (upper < g) g = upper;
+  return (int)(g > 0 ? g : 1);
+}
+
+hipError_t launch_grouped_mlp_f32(int L, int H, int F, int64_t capacity, const float* x,
+                                  const int32_t* offsets, const float* w1p, const float* w2p,
+                                  float* act, float* y, hipStream_t s) {
+  if (capacity == 0) return hipSuccess;
+  const int N1 = 2 * F, N2 = H;
+  hipLaunchKernelGGL(k_gemm_f32<1>, dim3(grid_for(capacity, L, GF_BM, (N1 + GF_BN - 1) / GF_BN, 4)), dim3(256),
+                     0, s, L, N1, H, capacity, x, offsets, w1p, act);
+  hipLaunchKernelGGL(k_gemm_f32<0>, dim3(grid_for(capacity, L, GF_BM, (N2 + GF_BN - 1) / GF_BN, 4)), dim3(256),
+                     0, s, L, N2, F, capacity, act, offsets, w2p, y);
+  return hipGetLastError();
+}
+
+static size_t gemm_bf16_lds(int L) {
+  return (size_t)2 * (GB_BM + GB_BN) * GB_BK * sizeof(bf16_t) + (size_t)(L + 1 + 16) * sizeof(int32_t);
+}
+
+hipError_t launch_grouped_mlp_bf16(int L, int H, int F, int64_t capacity, const bf16_t* x,
+                                   const int32_t* offsets, const bf16_t* w1p, const bf16_t* w2p,
+                                   bf16_t* act, bf16_t* y, hipStream_t s) {
+  if (capacity == 0) return hipSuccess;
+  const size_t lds = gemm_bf16_lds(L);
+  static bool attr_done = false;
+  if (!attr_done) {
+    (void)hipFuncSetAttribute((const void*)k_gemm_bf16<0>, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    (void)hipFuncSetAttribute((const void*)k_gemm_bf16<1>, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    attr_done = true;
+  }
+  const int N1 = 2 * F, N2 = H;
+  hipLaunchKernelGGL(k_gemm_bf16<1>, dim3(grid_for(capacity, L, GB_BM, (N1 + GB_BN - 1) / GB_BN, 1)), dim3(512),
+                     lds, s, L, N1, H, capacity, x, offsets, w1p, act);
+  hipLaunchKernelGGL(k_gemm_bf16<0>, dim3(grid_for(capacity, L, GB_BM, (N2 + GB_BN - 1) / GB_BN, 1)), dim3(512),
+                     lds, s, L, N2, F, capacity, act, offsets, w2p, y);
+  return hipGetLastError();
+}
+
+}  // namespace moe

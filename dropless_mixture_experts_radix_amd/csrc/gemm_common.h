@@ -1,0 +1,99 @@
+// Device tile schedule shared by the grouped GEMM kernels.
+#pragma once
+#include "moe_internal.h"
+
+namespace moe {
+
+static inline int num_cus() {
+  static int g_num_cus = 0;
+  if (g_num_cus == 0) {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
+      g_num_cus = n;
+    else
+      g_num_cus = 256;
+  }
+  return g_num_cus;
+}
+
+// ---------------------------------------------------------------------------
+// Device tile schedule.  s_pre[e] = first tile of expert e, s_pre[L] = total.
+// Row range of expert e: [min(offsets[e], cap), min(offsets[e+1], cap)).
+// ---------------------------------------------------------------------------
+__device__ inline void build_schedule(int L, int64_t capacity, int BM, int NT, const int32_t* __restrict__ offsets,
+                               int32_t* s_pre, int32_t* s_tmp) {
+  const int nth = blockDim.x, tid = threadIdx.x;
+  const int per = (L + nth - 1) / nth;
+  const int b0 = tid * per;
+  int loc = 0;
+  for (int i = 0; i < per; ++i) {
+    const int e = b0 + i;
+    if (e < L) {
+      int64_t lo = offsets[e], hi = offsets[e + 1];
+      lo = lo < capacity ? lo : capacity;
+      hi = hi < capacity ? hi : capacity;
+      const int m = hi > lo ? (int)(hi - lo) : 0;
+      loc += ((m + BM - 1) / BM) * NT;
+    }
+  }
+  const int incl = wave_incl_scan(loc);
+  const int w = tid >> 6, l = tid & 63;
+  if (l == 63) s_tmp[w] = incl;
+  __syncthreads();
+  int base = 0;
+  for (int i = 0; i < w; ++i) base += s_tmp[i];
+  int run = base + incl - loc;
+  for (int i = 0; i < per; ++i) {
+    const int e = b0 + i;
+    if (e < L) {
+      s_pre[e] = run;
+      int64_t lo = offsets[e], hi = offsets[e + 1];
+      lo = lo < capacity ? lo : capacity;
+      hi = hi < capacity ? hi : capacity;
+      const int m = hi > lo ? (int)(hi - lo) : 0;
+      run += ((m + BM - 1) / BM) * NT;
+    }
+  }
+  if (tid == nth - 1) s_pre[L] = run;
+  __syncthreads();
+}
+
+struct TileInfo {
+  int e, row0, rows, nt;
+};
+
+__device__ __forceinline__ TileInfo locate_tile(int it, int L, int64_t capacity, int BM, int NT,
+                                                const int32_t* __restrict__ offsets, const int32_t* s_pre) {
+  // largest e with s_pre[e] <= it (empty experts share their start with the next)
+  int lo = 0, hi = L - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (s_pre[mid] <= it) lo = mid; else hi = mid - 1;
+  }
+  const int e = lo;
+  int64_t r0 = offsets[e], r1 = offsets[e + 1];
+  r0 = r0 < capacity ? r0 : capacity;
+  r1 = r1 < capacity ? r1 : capacity;
+  const int m = (int)(r1 - r0);
+  const int mt_e = (m + BM - 1) / BM;
+  const int local = it - s_pre[e];
+  TileInfo ti;
+  ti.e = e;
+  ti.nt = local / mt_e;
+  const int mt = local % mt_e;
+  ti.row0 = (int)r0 + mt * BM;
+  ti.rows = min(BM, m - mt * BM);
+  return ti;
+}
+
+__device__ __forceinline__ int virtual_block() {
+  const int G = gridDim.x, b = blockIdx.x;
+  return (G % 8 == 0) ? (b % 8) * (G / 8) + b / 8 : b;
+}
+
+__device__ __forceinline__ float silu_mul(float g, float u) {
+  return g / (1.0f + __expf(-g)) * u;
+}
+
+}  // namespace moe

@@ -1,0 +1,241 @@
+// C ABI entry points: argument checks (before any HIP call), workspace
+// carving, kernel dispatch by shape and dtype.
+#include "moe_internal.h"
+
+using namespace moe;
+
+namespace {
+
+inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+inline size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+inline int launch_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH; }
+
+}  // namespace
+
+extern "C" {
+
+int moe_abi_version(void) { return MOE_ABI_VERSION; }
+
+const char* moe_status_str(int status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_NULL: return "a required pointer is NULL";
+    case MOE_ERR_SHAPE: return "a size is out of the supported range";
+    case MOE_ERR_ALIGN: return "a pointer is not 16-byte aligned";
+    case MOE_ERR_DTYPE: return "unsupported dtype or dtype combination";
+    case MOE_ERR_WORKSPACE: return "workspace missing or too small";
+    case MOE_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Route
+// ---------------------------------------------------------------------------
+size_t moe_router_prepared_bytes(int H, int E, int w_dtype, int x_dtype) {
+  if (H <= 0 || E <= 0) return 0;
+  if (x_dtype == MOE_BF16) {
+    const int P = w_dtype == MOE_F32 ? 3 : 1, ept = 32 / P;
+    const size_t C = (size_t)((E + ept - 1) / ept) * 32;
+    return C * (size_t)H * 2;
+  }
+  return (size_t)H * E * 4;
+}
+
+int moe_prepare_router(const void* w_router, int w_dtype, int x_dtype, int H, int E, void* prepared,
+                       void* stream) {
+  if (!w_router || !prepared) return MOE_ERR_NULL;
+  if (H <= 0 || E <= 0 || E > MOE_MAX_E) return MOE_ERR_SHAPE;
+  if (!((x_dtype == MOE_BF16 && (w_dtype == MOE_F32 || w_dtype == MOE_BF16)) ||
+        (x_dtype == MOE_F32 && w_dtype == MOE_F32)))
+    return MOE_ERR_DTYPE;
+  if (!aligned16(w_router) || !aligned16(prepared)) return MOE_ERR_ALIGN;
+  return launch_status(launch_prepare_router(w_router, w_dtype, x_dtype, H, E, prepared, (hipStream_t)stream));
+}
+
+size_t moe_route_workspace_bytes(int T, int E, int H, int x_dtype) {
+  if (T <= 0 || E <= 0) return 0;
+  const RouteSplit sp = route_split(T, E, H > 0 ? H : 64, x_dtype);
+  return round_up((size_t)sp.S * T * E * sizeof(float), 256);
+}
+
+int moe_route_topk(int T, int E, int K, int H, int score, int x_dtype, int w_dtype, const void* x,
+                   const void* w_prepared, const float* logits, const float* bias, const uint8_t* mask,
+                   int16_t* ids, float* probs, float* logits_out, int32_t* err, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+  if (T < 0 || E <= 0 || E > MOE_MAX_E || K < 1 || K > E || K > MOE_MAX_K) return MOE_ERR_SHAPE;
+  if (score != MOE_SCORE_SOFTMAX && score != MOE_SCORE_SIGMOID) return MOE_ERR_DTYPE;
+  const bool from_x = logits == nullptr;
+  if (T > 0 && (!ids || !probs)) return MOE_ERR_NULL;
+  if (from_x) {
+    if (T > 0 && (!x || !w_prepared)) return MOE_ERR_NULL;
+    if (H <= 0) return MOE_ERR_SHAPE;
+    if (x_dtype == MOE_BF16) {
+      if (H % 64 != 0) return MOE_ERR_SHAPE;
+      if (w_dtype != MOE_F32 && w_dtype != MOE_BF16) return MOE_ERR_DTYPE;
+    } else if (x_dtype == MOE_F32) {
+      if (w_dtype != MOE_F32) return MOE_ERR_DTYPE;
+    } else {
+      return MOE_ERR_DTYPE;
+    }
+    if (!aligned16(x) || !aligned16(w_prepared)) return MOE_ERR_ALIGN;
+    if (T > 0 && (!workspace || workspace_bytes < moe_route_workspace_bytes(T, E, H, x_dtype)))
+      return MOE_ERR_WORKSPACE;
+    if (T > 0 && !aligned16(workspace)) return MOE_ERR_ALIGN;
+  } else {
+    if (!aligned16(logits)) return MOE_ERR_ALIGN;
+  }
+  if (T == 0) return MOE_OK;
+  hipStream_t s = (hipStream_t)stream;
+  const float* partial = logits;
+  int S = 1;
+  if (from_x) {
+    float* ws = (float*)workspace;
+    hipError_t e = launch_router_proj(T, E, H, x_dtype, w_dtype, x, w_prepared, ws, s);
+    if (e != hipSuccess) return MOE_ERR_LAUNCH;
+    partial = ws;
+    S = route_split(T, E, H, x_dtype).S;
+  }
+  return launch_status(launch_route_select(T, E, K, S, score, partial, bias, mask, ids, probs,
+                                           logits_out, err, s));
+}
+
+// ---------------------------------------------------------------------------
+// Permute
+// ---------------------------------------------------------------------------
+size_t moe_permute_workspace_bytes(int T, int K, int L) {
+  if (T < 0 || K <= 0 || L <= 0) return 0;
+  const int TT = permute_tile_tokens(T, K);
+  const size_t ntiles = (size_t)((T + TT - 1) / TT);
+  return round_up((ntiles * L + (size_t)T * K) * sizeof(int32_t), 256) + 256;
+}
+
+int moe_permute(int T, int H, int K, int E_global, int e0, int L, int64_t capacity, int x_dtype,
+                int out_dtype, const void* x, const int16_t* ids, int32_t* counts, int32_t* offsets,
+                void* x_perm, uint8_t* x_perm_scales, int32_t* row_to_slot, int32_t* slot_to_row,
+                int32_t* err, void* workspace, size_t workspace_bytes, void* stream) {
+  if (T < 0 || H <= 0 || K < 1 || K > MOE_MAX_K || E_global <= 0 || E_global > 32767 || L < 1 ||
+      L > MOE_MAX_L || e0 < 0 || e0 + L > E_global || capacity < 0)
+    return MOE_ERR_SHAPE;
+  if (x_dtype != MOE_BF16 && x_dtype != MOE_F32) return MOE_ERR_DTYPE;
+  if (!(out_dtype == x_dtype || (out_dtype == MOE_MXFP8 && x_dtype == MOE_BF16))) return MOE_ERR_DTYPE;
+  if ((x_dtype == MOE_BF16 && H % 8) || (x_dtype == MOE_F32 && H % 4)) return MOE_ERR_SHAPE;
+  if (out_dtype == MOE_MXFP8 && H % 32) return MOE_ERR_SHAPE;
+  if (!counts || !offsets) return MOE_ERR_NULL;
+  if (T > 0 && (!x || !ids || !slot_to_row)) return MOE_ERR_NULL;
+  if (capacity > 0 && (!x_perm || !row_to_slot)) return MOE_ERR_NULL;
+  if (out_dtype == MOE_MXFP8 && capacity > 0 && !x_perm_scales) return MOE_ERR_NULL;
+  if (!aligned16(x) || !aligned16(x_perm)) return MOE_ERR_ALIGN;
+  if (!workspace || workspace_bytes < moe_permute_workspace_bytes(T, K, L)) return MOE_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return MOE_ERR_ALIGN;
+  return launch_status(launch_permute(T, H, K, E_global, e0, L, capacity, x_dtype, out_dtype, x, ids, counts,
+                                      offsets, x_perm, x_perm_scales, row_to_slot, slot_to_row, err, workspace,
+                                      (hipStream_t)stream));
+}
+
+// ---------------------------------------------------------------------------
+// Weights
+// ---------------------------------------------------------------------------
+size_t moe_prepared_weight_bytes(int L, int H, int F, int dtype, int which) {
+  if (L <= 0 || H <= 0 || F <= 0) return 0;
+  const size_t el = dtype == MOE_F32 ? 4 : (dtype == MOE_BF16 ? 2 : 1);
+  const size_t n1 = (size_t)L * 2 * F * H, n2 = (size_t)L * H * F;
+  switch (which) {
+    case 1: return n1 * el;
+    case 2: return n2 * el;
+    case 3: return dtype == MOE_MXFP8 ? n1 / 32 : 0;
+    case 4: return dtype == MOE_MXFP8 ? n2 / 32 : 0;
+    default: return 0;
+  }
+}
+
+int moe_prepare_weights(int L, int H, int F, int in_dtype, int dtype, const void* w1, const void* w2,
+                        void* w1p, void* w2p, uint8_t* w1p_scales, uint8_t* w2p_scales, void* stream) {
+  if (L < 1 || L > MOE_MAX_L || H <= 0 || F <= 0 || H % 32 || F % 32) return MOE_ERR_SHAPE;
+  if (!((dtype == MOE_F32 && in_dtype == MOE_F32) || (dtype == MOE_BF16 && in_dtype == MOE_BF16) ||
+        (dtype == MOE_MXFP8 && in_dtype == MOE_BF16)))
+    return MOE_ERR_DTYPE;
+  if (!w1 || !w2 || !w1p || !w2p) return MOE_ERR_NULL;
+  if (dtype == MOE_MXFP8 && (!w1p_scales || !w2p_scales)) return MOE_ERR_NULL;
+  if (!aligned16(w1) || !aligned16(w2) || !aligned16(w1p) || !aligned16(w2p)) return MOE_ERR_ALIGN;
+  return launch_status(launch_prepare_weights(L, H, F, dtype, w1, w2, w1p, w2p, w1p_scales, w2p_scales,
+                                              (hipStream_t)stream));
+}
+
+// ---------------------------------------------------------------------------
+// Grouped MLP
+// ---------------------------------------------------------------------------
+size_t moe_grouped_mlp_workspace_bytes(int64_t capacity, int F, int dtype) {
+  if (capacity <= 0 || F <= 0) return 256;
+  size_t a;
+  if (dtype == MOE_F32) a = (size_t)capacity * F * 4;
+  else if (dtype == MOE_BF16) a = (size_t)capacity * F * 2;
+  else a = round_up((size_t)capacity * F, 256) + (size_t)capacity * (F / 32);
+  return round_up(a, 256);
+}
+
+int moe_grouped_mlp(int L, int H, int F, int64_t capacity, int dtype, const void* x_perm,
+                    const uint8_t* x_perm_scales, const int32_t* offsets, const void* w1p,
+                    const uint8_t* w1p_scales, const void* w2p, const uint8_t* w2p_scales, void* y_perm,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+  if (L < 1 || L > MOE_MAX_L || H <= 0 || F <= 0 || capacity < 0 || capacity > (int64_t)1 << 31)
+    return MOE_ERR_SHAPE;
+  if (dtype == MOE_F32) {
+    if (H % 16 || F % 32) return MOE_ERR_SHAPE;
+  } else if (dtype == MOE_BF16) {
+    if (H % 64 || F % 64) return MOE_ERR_SHAPE;
+  } else if (dtype == MOE_MXFP8) {
+    if (H % 128 || F % 128) return MOE_ERR_SHAPE;
+  } else {
+    return MOE_ERR_DTYPE;
+  }
+  if (!offsets) return MOE_ERR_NULL;
+  if (capacity > 0 && (!x_perm || !w1p || !w2p || !y_perm)) return MOE_ERR_NULL;
+  if (dtype == MOE_MXFP8 && capacity > 0 && (!x_perm_scales || !w1p_scales || !w2p_scales)) return MOE_ERR_NULL;
+  if (!aligned16(x_perm) || !aligned16(w1p) || !aligned16(w2p) || !aligned16(y_perm)) return MOE_ERR_ALIGN;
+  if (!workspace || workspace_bytes < moe_grouped_mlp_workspace_bytes(capacity, F, dtype))
+    return MOE_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return MOE_ERR_ALIGN;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e;
+  if (dtype == MOE_F32) {
+    e = launch_grouped_mlp_f32(L, H, F, capacity, (const float*)x_perm, offsets, (const float*)w1p,
+                               (const float*)w2p, (float*)workspace, (float*)y_perm, s);
+  } else if (dtype == MOE_BF16) {
+    e = launch_grouped_mlp_bf16(L, H, F, capacity, (const bf16_t*)x_perm, offsets, (const bf16_t*)w1p,
+                                (const bf16_t*)w2p, (bf16_t*)workspace, (bf16_t*)y_perm, s);
+  } else {
+    uint8_t* act = (uint8_t*)workspace;
+    uint8_t* act_s = act + round_up((size_t)capacity * F, 256);
+    e = launch_grouped_mlp_mx(L, H, F, capacity, (const uint8_t*)x_perm, x_perm_scales, offsets,
+                              (const uint8_t*)w1p, w1p_scales, (const uint8_t*)w2p, w2p_scales, act, act_s,
+                              (bf16_t*)y_perm, s);
+  }
+  return launch_status(e);
+}
+
+// ---------------------------------------------------------------------------
+// Combine
+// ---------------------------------------------------------------------------
+int moe_unpermute_combine(int T, int K, int H, int dtype, const void* y_perm, const int32_t* slot_to_row,
+                          const float* probs, void* out, void* stream) {
+  if (T < 0 || K < 1 || K > MOE_MAX_K || H <= 0 || H % 8) return MOE_ERR_SHAPE;
+  if (dtype != MOE_BF16 && dtype != MOE_F32) return MOE_ERR_DTYPE;
+  if (T > 0 && (!slot_to_row || !probs || !out)) return MOE_ERR_NULL;
+  if (!aligned16(y_perm) || !aligned16(out)) return MOE_ERR_ALIGN;
+  return launch_status(launch_combine(T, K, H, dtype, y_perm, slot_to_row, probs, out, (hipStream_t)stream));
+}
+
+// ---------------------------------------------------------------------------
+// Standalone MX quantizer
+// ---------------------------------------------------------------------------
+int moe_mx_quantize(int64_t rows, int cols, const void* in, const int32_t* row_limit, uint8_t* codes,
+                    uint8_t* scales, void* stream) {
+  if (rows < 0 || cols <= 0 || cols % 32) return MOE_ERR_SHAPE;
+  if (rows > 0 && (!in || !codes || !scales)) return MOE_ERR_NULL;
+  if (!aligned16(in) || !aligned16(codes)) return MOE_ERR_ALIGN;
+  return launch_status(launch_mx_quantize(rows, cols, (const bf16_t*)in, row_limit, codes, scales,
+                                          (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,199 @@
+// Internal helpers shared by the HIP kernels of the MoE hot path (gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/moe.h"
+
+#define MOE_WAVE 64
+
+typedef uint16_t bf16_t;  // raw bfloat16 bits
+
+// ---------------------------------------------------------------------------
+// bf16 <-> fp32
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float bf16_to_f32(uint32_t b) {
+  return __uint_as_float(b << 16);
+}
+
+// Round-to-nearest-even fp32 -> bf16 (NaN stays a quiet NaN).
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return ((u >> 16) | 0x40u) & 0xffffu;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+// ---------------------------------------------------------------------------
+// Order-preserving uint32 keys of fp32 values (larger float -> larger key).
+// -0.0 is read as +0.0 first, so equal floats give equal keys.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t float_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float key_float(uint32_t k) {
+  uint32_t u = (k & 0x80000000u) ? (k & 0x7fffffffu) : ~k;
+  return __uint_as_float(u);
+}
+__device__ __forceinline__ bool key_finite(uint32_t k) {
+  float f = key_float(k);
+  return (__float_as_uint(f) & 0x7f800000u) != 0x7f800000u;
+}
+
+// ---------------------------------------------------------------------------
+// Wavefront helpers (wave64)
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+__device__ __forceinline__ uint64_t wave_ballot(bool p) { return __ballot(p); }
+
+// number of set bits of m below this lane
+__device__ __forceinline__ int mask_rank(uint64_t m) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
+}
+
+__device__ __forceinline__ int wave_sum_i(int v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+__device__ __forceinline__ float wave_sum_f(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+__device__ __forceinline__ uint32_t wave_max_u(uint32_t v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    uint32_t w = __shfl_xor(v, o, 64);
+    v = v > w ? v : w;
+  }
+  return v;
+}
+
+// inclusive prefix sum over the wave
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  const int l = lane_id();
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    int w = __shfl_up(v, o, 64);
+    if (l >= o) v += w;
+  }
+  return v;
+}
+
+__device__ __forceinline__ int readlane_i(int v, int lane) {
+  return __builtin_amdgcn_readlane(v, lane);
+}
+__device__ __forceinline__ float readlane_f(float v, int lane) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+}
+
+__device__ __forceinline__ void set_err(int32_t* err, int bits) {
+  if (err) atomicOr(err, bits);
+}
+
+// ---------------------------------------------------------------------------
+// OCP MX (v1.0) E4M3 block quantization of bf16 values, integer arithmetic.
+//   scale exponent E = clamp(floor(log2 amax) - 8, -127, 127)  (-127 if amax==0)
+//   code = E4M3(v * 2^-E): round to nearest, ties to even, saturate to 448,
+//   the sign of zero kept.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int bf16_floor_log2(uint32_t absbits) {  // absbits != 0
+  uint32_t ef = absbits >> 7;
+  if (ef) return (int)ef - 127;
+  return -133 + (31 - __clz(absbits));
+}
+
+__device__ __forceinline__ int mx_scale_exp(uint32_t amax_abs_bits) {
+  if (amax_abs_bits == 0) return -127;
+  int e = bf16_floor_log2(amax_abs_bits) - 8;
+  return e < -127 ? -127 : (e > 127 ? 127 : e);
+}
+
+__device__ __forceinline__ uint32_t mx_e4m3(uint32_t b, int E) {
+  const uint32_t s = (b >> 15) & 1u;
+  const uint32_t a = b & 0x7fffu;
+  const uint32_t ef = a >> 7;
+  uint32_t M;
+  int x;  // |v| = M * 2^x
+  if (ef) { M = 128u | (a & 127u); x = (int)ef - 134; }
+  else { M = a & 127u; x = -133; }
+  if (M == 0) return s << 7;
+  const int msb = 31 - __clz(M);
+  const int fl = msb + x - E;               // floor(log2 |v * 2^-E|)
+  int qe = (fl > -6 ? fl : -6) - 3;         // exponent of the E4M3 spacing there
+  const int sh = qe - (x - E);              // M is divided by 2^sh
+  uint32_t n;
+  if (sh <= 0) {
+    n = M << (-sh);
+  } else if (sh > 9) {
+    n = 0;
+  } else {
+    const uint32_t q = M >> sh, rem = M & ((1u << sh) - 1u), half = 1u << (sh - 1);
+    n = q + ((rem > half) || (rem == half && (q & 1u)) ? 1u : 0u);
+  }
+  if (n >= 16) { n >>= 1; qe += 1; }
+  uint32_t code;
+  if (n >= 8) {
+    const int field = qe + 10;
+    const uint32_t mant = n - 8;
+    code = (field > 15 || (field == 15 && mant == 7)) ? 0x7eu : (((uint32_t)field << 3) | mant);
+  } else {
+    code = n;
+  }
+  return (s << 7) | code;
+}
+
+// ---------------------------------------------------------------------------
+// Host-side launchers (one per kernel family, defined in the kernel sources).
+// All return hipError_t of the launch.
+// ---------------------------------------------------------------------------
+namespace moe {
+
+struct RouteSplit {
+  int S;         // number of H chunks (partial logit sets)
+  int Hc;        // chunk length
+  int C;         // prepared router rows (multiple of 32)
+};
+RouteSplit route_split(int T, int E, int H, int x_dtype);
+
+hipError_t launch_prepare_router(const void* w, int w_dtype, int x_dtype, int H, int E, void* out,
+                                 hipStream_t s);
+hipError_t launch_router_proj(int T, int E, int H, int x_dtype, int w_dtype, const void* x,
+                              const void* wp, float* partial, hipStream_t s);
+hipError_t launch_route_select(int T, int E, int K, int S, int score, const float* partial,
+                               const float* bias, const uint8_t* mask, int16_t* ids, float* probs,
+                               float* logits_out, int32_t* err, hipStream_t s);
+
+int permute_tile_tokens(int T, int K);
+hipError_t launch_permute(int T, int H, int K, int E_global, int e0, int L, int64_t capacity,
+                          int x_dtype, int out_dtype, const void* x, const int16_t* ids,
+                          int32_t* counts, int32_t* offsets, void* x_perm, uint8_t* x_scales,
+                          int32_t* row_to_slot, int32_t* slot_to_row, int32_t* err, void* ws,
+                          hipStream_t s);
+
+hipError_t launch_prepare_weights(int L, int H, int F, int dtype, const void* w1, const void* w2,
+                                  void* w1p, void* w2p, uint8_t* w1s, uint8_t* w2s, hipStream_t s);
+
+hipError_t launch_grouped_mlp_f32(int L, int H, int F, int64_t capacity, const float* x,
+                                  const int32_t* offsets, const float* w1p, const float* w2p,
+                                  float* act, float* y, hipStream_t s);
+hipError_t launch_grouped_mlp_bf16(int L, int H, int F, int64_t capacity, const bf16_t* x,
+                                   const int32_t* offsets, const bf16_t* w1p, const bf16_t* w2p,
+                                   bf16_t* act, bf16_t* y, hipStream_t s);
+hipError_t launch_grouped_mlp_mx(int L, int H, int F, int64_t capacity, const uint8_t* x,
+                                 const uint8_t* xs, const int32_t* offsets, const uint8_t* w1p,
+                                 const uint8_t* w1s, const uint8_t* w2p, const uint8_t* w2s,
+                                 uint8_t* act, uint8_t* act_s, bf16_t* y, hipStream_t s);
+
+hipError_t launch_combine(int T, int K, int H, int dtype, const void* y, const int32_t* s2r,
+                          const float* probs, void* out, hipStream_t s);
+
+hipError_t launch_mx_quantize(int64_t rows, int cols, const bf16_t* in, const int32_t* row_limit,
+                              uint8_t* codes, uint8_t* scales, hipStream_t s);
+
+}  // namespace moe

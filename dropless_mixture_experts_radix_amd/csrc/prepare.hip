@@ -1,0 +1,125 @@
+// One-time expert weight layout (+ MX quantization) and the standalone MX
+// quantizer.
+//
+// bpdata article, reproduction settings: the expert weights are pre-fused once.
+// Prepared layout (per expert): W1p [2F][H], row p = column c(p) of W1[e] with
+// gate/up chunks of 32 interleaved, c(p) = (p/64)*32 + p%32 + ((p/32)%2 ? F : 0);
+// W2p [H][F], row n = column n of W2[e].  Rows are contraction-contiguous, the
+// layout the grouped GEMM streams.
+#include "moe_internal.h"
+
+namespace moe {
+
+// One 32 x 32 tile of one expert: logical W [Kd][Ncols] -> prepared [Ncols][Kd].
+// MODE 0: fp32 -> fp32, 1: bf16 -> bf16, 2: bf16 -> MX E4M3 codes + scales.
+template <int MODE>
+__global__ __launch_bounds__(256) void k_prepare(int Kd, int Ncols, int F_interleave,
+                                                 const void* __restrict__ w, void* __restrict__ wp,
+                                                 uint8_t* __restrict__ ws) {
+  __shared__ uint32_t tile[32][33];
+  const int e = blockIdx.z;
+  const int pc = blockIdx.x;  // prepared 32-row chunk
+  const int k0 = blockIdx.y * 32;
+  const int cbase = F_interleave ? (pc >> 1) * 32 + ((pc & 1) ? F_interleave : 0) : pc * 32;
+  const long in_off = (long)e * Kd * Ncols;
+  const long out_off = (long)e * Ncols * Kd;
+  const int tid = threadIdx.x;
+  // load: 32 k rows x 32 logical columns
+  for (int i = tid; i < 1024; i += 256) {
+    const int kk = i >> 5, cc = i & 31;
+    const long src = in_off + (long)(k0 + kk) * Ncols + cbase + cc;
+    uint32_t v = MODE == 0 ? __float_as_uint(((const float*)w)[src]) : ((const bf16_t*)w)[src];
+    tile[cc][kk] = v;
+  }
+  __syncthreads();
+  if (MODE < 2) {
+    for (int i = tid; i < 1024; i += 256) {
+      const int pp = i >> 5, kk = i & 31;
+      const long dst = out_off + (long)(pc * 32 + pp) * Kd + k0 + kk;
+      if (MODE == 0) ((float*)wp)[dst] = __uint_as_float(tile[pp][kk]);
+      else ((bf16_t*)wp)[dst] = (bf16_t)tile[pp][kk];
+    }
+  } else if (tid < 32) {
+    const int pp = tid;
+    uint32_t am = 0;
+    for (int kk = 0; kk < 32; ++kk) {
+      const uint32_t a = tile[pp][kk] & 0x7fffu;
+      am = am > a ? am : a;
+    }
+    const int E = mx_scale_exp(am);
+    const long row = (long)e * Ncols + pc * 32 + pp;
+    uint8_t* dst = (uint8_t*)wp + row * Kd + k0;
+    for (int kk = 0; kk < 32; ++kk) dst[kk] = (uint8_t)mx_e4m3(tile[pp][kk], E);
+    ws[row * (Kd / 32) + (k0 >> 5)] = (uint8_t)(E + 127);
+  }
+}
+
+hipError_t launch_prepare_weights(int L, int H, int F, int dtype, const void* w1, const void* w2,
+                                  void* w1p, void* w2p, uint8_t* w1s, uint8_t* w2s, hipStream_t s) {
+  if (L == 0) return hipSuccess;
+  const dim3 g1(2 * F / 32, H / 32, L), g2(H / 32, F / 32, L), b(256);
+  if (dtype == MOE_F32) {
+    hipLaunchKernelGGL(k_prepare<0>, g1, b, 0, s, H, 2 * F, F, w1, w1p, (uint8_t*)nullptr);
+    hipLaunchKernelGGL(k_prepare<0>, g2, b, 0, s, F, H, 0, w2, w2p, (uint8_t*)nullptr);
+  } else if (dtype == MOE_BF16) {
+    hipLaunchKernelGGL(k_prepare<1>, g1, b, 0, s, H, 2 * F, F, w1, w1p, (uint8_t*)nullptr);
+    hipLaunchKernelGGL(k_prepare<1>, g2, b, 0, s, F, H, 0, w2, w2p, (uint8_t*)nullptr);
+  } else {
+    hipLaunchKernelGGL(k_prepare<2>, g1, b, 0, s, H, 2 * F, F, w1, w1p, w1s);
+    hipLaunchKernelGGL(k_prepare<2>, g2, b, 0, s, F, H, 0, w2, w2p, w2s);
+  }
+  return hipGetLastError();
+}
+
+// Standalone MX quantization: one thread per 32-element block of a row.
+__global__ __launch_bounds__(256) void k_mx_quantize(int64_t rows, int cols, const bf16_t* __restrict__ in,
+                                                     const int32_t* __restrict__ row_limit,
+                                                     uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
+  const int nb = cols / 32;
+  int64_t lim = rows;
+  if (row_limit) {
+    const int64_t rl = *row_limit;
+    lim = rl < rows ? (rl > 0 ? rl : 0) : rows;
+  }
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < lim * nb;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t r = i / nb;
+    const int b = (int)(i % nb);
+    const uint32_t* src = (const uint32_t*)(in + r * cols + b * 32);
+    uint32_t v[16];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint4 u = ((const uint4*)src)[q];
+      v[4 * q] = u.x; v[4 * q + 1] = u.y; v[4 * q + 2] = u.z; v[4 * q + 3] = u.w;
+    }
+    uint32_t am = 0;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const uint32_t a0 = v[q] & 0x7fffu, a1 = (v[q] >> 16) & 0x7fffu;
+      am = am > a0 ? am : a0;
+      am = am > a1 ? am : a1;
+    }
+    const int E = mx_scale_exp(am);
+    uint32_t out[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      out[q] = mx_e4m3(v[2 * q] & 0xffffu, E) | (mx_e4m3(v[2 * q] >> 16, E) << 8) |
+               (mx_e4m3(v[2 * q + 1] & 0xffffu, E) << 16) | (mx_e4m3(v[2 * q + 1] >> 16, E) << 24);
+    }
+    uint4* dst = (uint4*)(codes + r * cols + b * 32);
+    dst[0] = make_uint4(out[0], out[1], out[2], out[3]);
+    dst[1] = make_uint4(out[4], out[5], out[6], out[7]);
+    scales[r * nb + b] = (uint8_t)(E + 127);
+  }
+}
+
+hipError_t launch_mx_quantize(int64_t rows, int cols, const bf16_t* in, const int32_t* row_limit,
+                              uint8_t* codes, uint8_t* scales, hipStream_t s) {
+  if (rows == 0) return hipSuccess;
+  const int64_t work = rows * (cols / 32);
+  const int blocks = (int)((work + 255) / 256 < 8192 ? (work + 255) / 256 : 8192);
+  hipLaunchKernelGGL(k_mx_quantize, dim3(blocks), dim3(256), 0, s, rows, cols, in, row_limit, codes, scales);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,259 @@
+/*
+ * moe.h -- C ABI of the single-GPU dropless mixture-of-experts layer hot path
+ * for AMD Instinct MI355X (CDNA4, gfx950).
+ *
+ * The layer (bpdata article on dropless MoE in JAX with Transformer Engine,
+ * figure "an expert-parallel MoE layer across two GPUs"): a router assigns each
+ * token to K experts, token rows are grouped by expert, a grouped MLP runs two
+ * grouped GEMMs on the variable-length groups, and a combine restores the
+ * original token order.  One GPU's share of that path is four calls:
+ *
+ *   moe_route_topk         logits (or x . W_r) -> int16 [T,K] expert ids + fp32 probs
+ *   moe_permute            per-expert count, scan and permute of the token rows
+ *   moe_grouped_mlp        ragged grouped SwiGLU MLP (fp32, bf16 or MXFP8)
+ *   moe_unpermute_combine  probability-weighted sum back in token order
+ *
+ * plus one-time weight preparation and a standalone MX quantizer.
+ *
+ * Conventions shared by every call
+ *  - Pointers named as device pointers must point to device memory (HBM) the
+ *    caller owns; the library never allocates or frees memory.  Every tensor is
+ *    row-major and contiguous, 16-byte aligned.
+ *  - Host arguments are shapes only.  Data-dependent sizes (expert counts,
+ *    offsets, the number N of routed rows) stay on the device: no call copies
+ *    anything to the host or synchronises, so a whole layer can be captured in
+ *    one HIP graph (bpdata article, "Optimization 1: Grouped GEMM": GEMM loops
+ *    that needed device-to-host token counts broke graph capture).
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Work is enqueued
+ *    on it in order; nothing else is waited for.
+ *  - Return value: MOE_OK, or an error status when an argument is invalid or a
+ *    launch fails.  A non-zero status other than MOE_ERR_LAUNCH means nothing
+ *    was enqueued; argument checks run before any HIP call, so they work on a
+ *    machine without a GPU.
+ *  - Data errors found on the device (an expert id out of range, more routed
+ *    rows than `capacity`, a non-finite logit) set bits of the optional device
+ *    word `err` with an atomic OR; the caller reads it whenever it likes.
+ *  - Outputs are bitwise deterministic: no floating-point atomics, no split
+ *    reductions whose order depends on scheduling.
+ *  - Calls may be issued from several host threads; calls on one stream run in
+ *    order, calls on different streams that share buffers race.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_ABI_VERSION 1
+
+/* Status codes. */
+enum {
+  MOE_OK = 0,
+  MOE_ERR_NULL = 1,      /* a required pointer is NULL */
+  MOE_ERR_SHAPE = 2,     /* a size is out of the supported range */
+  MOE_ERR_ALIGN = 3,     /* a pointer is not 16-byte aligned */
+  MOE_ERR_DTYPE = 4,     /* unsupported dtype or dtype combination */
+  MOE_ERR_WORKSPACE = 5, /* workspace missing or smaller than required */
+  MOE_ERR_LAUNCH = 6     /* a kernel launch failed (hipGetLastError) */
+};
+
+/* Element types. */
+enum {
+  MOE_F32 = 0,   /* IEEE fp32 */
+  MOE_BF16 = 1,  /* bfloat16 (16-bit, fp32 exponent range) */
+  MOE_MXFP8 = 2  /* OCP MX: E4M3 codes (uint8) + one E8M0 scale byte per 32
+                    consecutive elements of a row (value = code * 2^(scale-127)) */
+};
+
+/* Router score functions. */
+enum {
+  MOE_SCORE_SOFTMAX = 0, /* p_k = exp(z_k) / sum_j exp(z_j) over the K selected keys */
+  MOE_SCORE_SIGMOID = 1  /* p_k = sigma(z_k) / sum_j sigma(z_j) over the K selected keys */
+};
+
+/* Device error-word bits. */
+enum {
+  MOE_DEVERR_BAD_ID = 1,    /* an expert id < -1 or >= E_global reached moe_permute */
+  MOE_DEVERR_OVERFLOW = 2,  /* more routed local rows than `capacity` */
+  MOE_DEVERR_NONFINITE = 4  /* a router key was NaN or +-inf */
+};
+
+/* Limits of this implementation (checked; MOE_ERR_SHAPE otherwise). */
+#define MOE_MAX_K 64          /* routes per token */
+#define MOE_MAX_E 4096        /* experts seen by the router */
+#define MOE_MAX_L 2048        /* local experts */
+
+int moe_abi_version(void);
+const char* moe_status_str(int status);
+
+/* ------------------------------------------------------------------------
+ * Route: score + top-K selection (+ optional fused router projection)
+ *
+ * Sparser-MoE page (harryzhou2000), sections "Preserve a compact route" and
+ * "The workload changes the bottleneck": the selected experts are carried as a
+ * dense int16 [T,K] list instead of a [T,E] boolean map, selection uses bounded
+ * histogram passes over a narrowed candidate range instead of K full-row
+ * scans, invalid routes are -1, and small top-K shapes keep a direct path.
+ *
+ * Keys: z[t,e] = logit[t,e] (+ bias[e], one fp32 add), -0.0 read as +0.0.
+ * Selection: the K largest keys per token, ties broken by the lower expert
+ * index; ids[t,0..K-1] list them by descending key (ties: ascending index).
+ * probs[t,k]: MOE_SCORE_SOFTMAX or MOE_SCORE_SIGMOID over the K selected keys,
+ * fp32.  A token with mask[t] != 0 gets ids -1 and probs 0.
+ *
+ * Logit source (exactly one):
+ *  - logits  [T,E] fp32 device pointer, or
+ *  - x [T,H] (x_dtype MOE_BF16 or MOE_F32) with router weights prepared by
+ *    moe_prepare_router: logits = x . W_r accumulated in fp32 (for bf16 x and
+ *    fp32 W_r each weight is split into three bf16 terms, which keeps fp32
+ *    accuracy on bf16 matrix cores).
+ * Optional (NULL = absent): bias [E] fp32, mask [T] uint8, logits_out [T,E]
+ * fp32 (receives the logits before the bias), err.
+ * Outputs: ids [T,K] int16, probs [T,K] fp32.
+ * Limits: 1 <= K <= min(E, 64); E <= 4096; H % 32 == 0 for the projection.
+ * Workspace: moe_route_workspace_bytes(T, E, H, x_dtype) bytes (0 allowed when
+ * logits are given).
+ * ------------------------------------------------------------------------ */
+size_t moe_router_prepared_bytes(int H, int E, int w_dtype, int x_dtype);
+
+/* Lay out the router weights W_r [H,E] (w_dtype MOE_F32 or MOE_BF16, device)
+ * for moe_route_topk with activations of type x_dtype.  Output `prepared`
+ * (device) has moe_router_prepared_bytes(...) bytes:
+ *  x_dtype MOE_BF16: bf16 [C][H], C = ceil(P*E/32)*32 rows, row p*E+e holds
+ *    term p of column e of W_r (P = 3 terms hi/mid/lo for fp32 W_r with
+ *    W = hi + mid + lo, P = 1 for bf16 W_r); the remaining rows are zero.
+ *  x_dtype MOE_F32: fp32 W_r [H,E] copied unchanged. */
+int moe_prepare_router(const void* w_router, int w_dtype, int x_dtype, int H, int E,
+                       void* prepared, void* stream);
+
+size_t moe_route_workspace_bytes(int T, int E, int H, int x_dtype);
+
+int moe_route_topk(int T, int E, int K, int H, int score, int x_dtype, int w_dtype,
+                   const void* x, const void* w_prepared, const float* logits,
+                   const float* bias, const uint8_t* mask,
+                   int16_t* ids, float* probs, float* logits_out, int32_t* err,
+                   void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Permute: device count, single-pass scan and permute to expert order
+ *
+ * Sparser-MoE page, section "Remove work that has no selected route": local
+ * pre-processing visits only the selected local slots of a token (a wavefront
+ * ballot over its K slots, iterating set bits).  bpdata article, "Optimization
+ * 1: Grouped GEMM": no device-to-host counts, no padding, no dropping.
+ *
+ * Local experts are ids e0 .. e0+L-1 of E_global.  For each valid local slot
+ * (t,k), in flat order f = t*K + k:
+ *   counts[e]      number of local slots of expert e0+e               int32 [L]
+ *   offsets[e]     exclusive prefix of counts; offsets[L] = N          int32 [L+1]
+ *   row r of expert e = offsets[e] + (number of earlier flat slots of e)
+ *   x_perm[r]      = x[t]                                   [capacity,H]
+ *   row_to_slot[r] = f                                      int32 [capacity]
+ *   slot_to_row[t,k] = r, or -1 for -1 / non-local slots      int32 [T,K]
+ * Rows r >= N of x_perm and row_to_slot are never written.  If N > capacity,
+ * MOE_DEVERR_OVERFLOW is set in err, offsets still report the true counts and
+ * rows >= capacity are dropped from x_perm/row_to_slot (their slot_to_row is
+ * -1).  Ids < -1 or >= E_global set MOE_DEVERR_BAD_ID and count as -1.
+ * x_dtype MOE_BF16 or MOE_F32; out_dtype = x_dtype, or MOE_MXFP8 with bf16 x:
+ * x_perm then receives E4M3 codes [capacity,H] uint8 and x_perm_scales the
+ * E8M0 scales [capacity,H/32] uint8 of 32-element blocks along H (OCP MX v1.0
+ * rule: scale exponent floor(log2 max|v|) - 8, round to nearest even,
+ * saturate at 448), which requires H % 32 == 0.
+ * Workspace: moe_permute_workspace_bytes(T, K, L) bytes.
+ * ------------------------------------------------------------------------ */
+size_t moe_permute_workspace_bytes(int T, int K, int L);
+
+int moe_permute(int T, int H, int K, int E_global, int e0, int L, int64_t capacity,
+                int x_dtype, int out_dtype,
+                const void* x, const int16_t* ids,
+                int32_t* counts, int32_t* offsets, void* x_perm, uint8_t* x_perm_scales,
+                int32_t* row_to_slot, int32_t* slot_to_row, int32_t* err,
+                void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Expert weights: one-time layout (+ MX quantization)
+ *
+ * bpdata article, reproduction settings: expert weights are pre-fused once.
+ * Logical weights (device): W1 [L,H,2F] (gate columns [0,F), up columns
+ * [F,2F)), W2 [L,F,H], in_dtype MOE_BF16 or MOE_F32.  Prepared layout, one
+ * contiguous block per expert:
+ *   W1p [L][2F][H]: row p holds column c(p) of W1[e] along H, where
+ *       c(p) = (p/64)*32 + p%32 + ((p/32)%2 ? F : 0)   (gate/up chunks of 32
+ *       interleaved so one output tile holds matching gate and up columns)
+ *   W2p [L][H][F]: row n holds column n of W2[e] along F.
+ * dtype MOE_F32 / MOE_BF16: values in that type (in_dtype must match).
+ * dtype MOE_MXFP8 (in_dtype MOE_BF16): W1p/W2p hold E4M3 codes (uint8) and
+ *   w1p_scales [L][2F][H/32], w2p_scales [L][H][F/32] the E8M0 block scales
+ *   of 32 consecutive elements along each prepared row.
+ * Requires F % 32 == 0 (and H % 32 == 0, F % 32 == 0 for MXFP8).  Byte sizes:
+ * moe_prepared_weight_bytes(L, H, F, dtype, which) with which = 1 (W1p),
+ * 2 (W2p), 3 (W1p scales), 4 (W2p scales).
+ * ------------------------------------------------------------------------ */
+size_t moe_prepared_weight_bytes(int L, int H, int F, int dtype, int which);
+
+int moe_prepare_weights(int L, int H, int F, int in_dtype, int dtype,
+                        const void* w1, const void* w2,
+                        void* w1p, void* w2p, uint8_t* w1p_scales, uint8_t* w2p_scales,
+                        void* stream);
+
+/* ------------------------------------------------------------------------
+ * Grouped SwiGLU MLP over the expert-ordered rows
+ *
+ * bpdata article, "Optimization 1: Grouped GEMM": all expert matmuls in one
+ * kernel, each with its actual token count, computing only valid regions;
+ * "Transformer Engine building blocks": MXFP8 grouped GEMM for the expert
+ * matmuls with group-aware MXFP8 quantization.
+ *
+ * For each local expert e with rows [offsets[e], offsets[e+1]) (clipped to
+ * capacity):  h = x_perm[rows] . W1[e]  (fp32 accumulation),
+ *             a = silu(h[:, :F]) * h[:, F:],  silu(g) = g * sigma(g),
+ *             y_perm[rows] = a . W2[e].
+ * dtype MOE_F32: x_perm, a, y_perm fp32.  MOE_BF16: x_perm, a, y_perm bf16.
+ * MOE_MXFP8: x_perm as E4M3 codes + x_perm_scales (from moe_permute), `a`
+ *   rounded to bf16 and then MX-quantized along F, y_perm bf16.
+ * The schedule of output tiles is built on the device from `offsets`: empty
+ * experts get no tiles.  Requires H % 64 == 0 and F % 64 == 0 for MOE_BF16 and
+ * MOE_MXFP8, F % 32 == 0 for MOE_F32.
+ * Workspace: moe_grouped_mlp_workspace_bytes(capacity, F, dtype) bytes; it
+ * starts with `a` ([capacity][F] in the activation type; for MXFP8 the codes
+ * [capacity][F] followed by the scales [capacity][F/32]).
+ * ------------------------------------------------------------------------ */
+size_t moe_grouped_mlp_workspace_bytes(int64_t capacity, int F, int dtype);
+
+int moe_grouped_mlp(int L, int H, int F, int64_t capacity, int dtype,
+                    const void* x_perm, const uint8_t* x_perm_scales, const int32_t* offsets,
+                    const void* w1p, const uint8_t* w1p_scales,
+                    const void* w2p, const uint8_t* w2p_scales,
+                    void* y_perm, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Unpermute + probability-weighted combine
+ *
+ * bpdata article, layer figure: the combine restores token order.
+ *   out[t] = sum over k = 0..K-1 with slot_to_row[t,k] >= 0 (in k order, fp32
+ *            accumulation) of probs[t,k] * y_perm[slot_to_row[t,k]]
+ * A token with no such slot gets a zero row.  dtype MOE_BF16 (y_perm, out
+ * bf16) or MOE_F32.  H % 8 == 0.
+ * ------------------------------------------------------------------------ */
+int moe_unpermute_combine(int T, int K, int H, int dtype,
+                          const void* y_perm, const int32_t* slot_to_row, const float* probs,
+                          void* out, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Standalone MX quantization of bf16 rows (OCP MX v1.0, E4M3 + E8M0, blocks
+ * of 32 along a row): in [rows][cols] bf16 -> codes [rows][cols] uint8,
+ * scales [rows][cols/32] uint8.  If row_limit (device int32, may be NULL) is
+ * given, only rows < *row_limit are quantized (ragged rows bounded by a device
+ * value such as offsets[L]).  cols % 32 == 0.
+ * ------------------------------------------------------------------------ */
+int moe_mx_quantize(int64_t rows, int cols, const void* in, const int32_t* row_limit,
+                    uint8_t* codes, uint8_t* scales, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_MI355X_H */

@@ -1,0 +1,130 @@
+"""The C-ABI library loads without a GPU, exports every entry point declared in
+include/moe.h, and rejects invalid arguments before touching HIP (these calls
+pass NULL streams and pointers, so any HIP call would be visible)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.abspath(os.path.join(os.path.dirname(__file__), ".."))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "moe.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    from dropless_mixture_experts_radix_amd import _lib
+    names = _declared()
+    assert len(names) >= 14
+    for n in names:
+        assert hasattr(_lib.lib, n), n
+    assert set(names) == set(_lib.symbols())
+    assert _lib.lib.moe_abi_version() == 1
+
+
+def test_status_strings():
+    from dropless_mixture_experts_radix_amd import _lib
+    for st in range(7):
+        assert _lib.status_str(st)
+    assert _lib.status_str(99) == "unknown status"
+
+
+def _route(**kw):
+    from dropless_mixture_experts_radix_amd import _lib
+    a = dict(T=16, E=8, K=2, H=64, score=0, x_dtype=1, w_dtype=0, x=None, w=None, logits=None, bias=None,
+             mask=None, ids=None, probs=None, lo=None, err=None, ws=None, wsb=0)
+    a.update(kw)
+    return _lib.lib.moe_route_topk(a["T"], a["E"], a["K"], a["H"], a["score"], a["x_dtype"], a["w_dtype"], a["x"],
+                                   a["w"], a["logits"], a["bias"], a["mask"], a["ids"], a["probs"], a["lo"], a["err"],
+                                   a["ws"], a["wsb"], None)
+
+
+P = 1 << 20  # a fake, 16-byte aligned "device" address: validation never dereferences
+
+
+def test_route_validation():
+    assert _route(K=9) == 2          # K > E
+    assert _route(K=0) == 2
+    assert _route(E=5000) == 2       # E > 4096
+    assert _route(K=65, E=100) == 2  # K > 64
+    assert _route(score=7) == 4
+    assert _route(ids=P, probs=P) == 1                     # no x / weights, no logits
+    assert _route(ids=P, probs=P, x=P, w=P, H=96) == 2     # bf16 x needs H % 64 == 0
+    assert _route(ids=P, probs=P, x=P, w=P, x_dtype=0, w_dtype=1) == 4
+    assert _route(ids=P, probs=P, x=P + 2, w=P) == 3
+    assert _route(ids=P, probs=P, x=P, w=P) == 5           # workspace missing
+    assert _route(ids=P, probs=P, x=P, w=P, ws=P, wsb=16) == 5
+    assert _route(T=0) == 0                                 # empty batch: a valid no-op
+
+
+def test_permute_validation():
+    from dropless_mixture_experts_radix_amd import _lib
+    f = _lib.lib.moe_permute
+
+    def call(T=4, H=64, K=2, E=8, e0=0, L=8, cap=8, xd=1, od=1, x=P, ids=P, counts=P, offs=P, xp=P, xs=None,
+             r2s=P, s2r=P, ws=P, wsb=1 << 20):
+        return f(T, H, K, E, e0, L, cap, xd, od, x, ids, counts, offs, xp, xs, r2s, s2r, None, ws, wsb, None)
+
+    assert call(e0=4, L=8) == 2          # local range beyond E
+    assert call(K=65) == 2
+    assert call(E=40000, L=8) == 2
+    assert call(L=3000, E=4000) == 2     # L > MOE_MAX_L
+    assert call(xd=0, od=2) == 4         # MX output needs bf16 rows
+    assert call(od=2, H=48) == 2         # MX needs H % 32 == 0
+    assert call(od=2) == 1               # MX scales missing
+    assert call(counts=None) == 1
+    assert call(ws=None) == 5
+    assert call(wsb=8) == 5
+    assert call(x=P + 8) == 3
+    assert call(H=12) == 2               # bf16 rows need H % 8 == 0
+
+
+def test_mlp_validation():
+    from dropless_mixture_experts_radix_amd import _lib
+    f = _lib.lib.moe_grouped_mlp
+
+    def call(L=8, H=128, F=128, cap=64, dt=1, x=P, xs=None, offs=P, w1=P, w1s=None, w2=P, w2s=None, y=P, ws=P,
+             wsb=1 << 24):
+        return f(L, H, F, cap, dt, x, xs, offs, w1, w1s, w2, w2s, y, ws, wsb, None)
+
+    assert call(H=96) == 2               # bf16 needs H % 64 == 0
+    assert call(dt=2, F=192) == 2        # MXFP8 needs F % 128 == 0
+    assert call(dt=2) == 1               # MX scales missing
+    assert call(dt=9) == 4
+    assert call(offs=None) == 1
+    assert call(wsb=100) == 5
+    assert call(L=0) == 2
+    assert call(y=P + 4) == 3
+
+
+def test_other_validation():
+    from dropless_mixture_experts_radix_amd import _lib
+    lib = _lib.lib
+    assert lib.moe_unpermute_combine(4, 2, 12, 1, P, P, P, P, None) == 2      # H % 8
+    assert lib.moe_unpermute_combine(4, 2, 64, 2, P, P, P, P, None) == 4      # MX output not supported
+    assert lib.moe_unpermute_combine(4, 2, 64, 1, P, None, P, P, None) == 1
+    assert lib.moe_mx_quantize(4, 48, P, None, P, P, None) == 2
+    assert lib.moe_mx_quantize(4, 64, None, None, P, P, None) == 1
+    assert lib.moe_prepare_weights(2, 64, 48, 1, 1, P, P, P, P, None, None, None) == 2   # F % 32
+    assert lib.moe_prepare_weights(2, 64, 64, 0, 2, P, P, P, P, P, P, None) == 4         # MX from fp32
+    assert lib.moe_prepare_weights(2, 64, 64, 1, 2, P, P, P, P, None, P, None) == 1
+    assert lib.moe_prepare_router(P, 1, 0, 64, 8, P, None) == 4                          # bf16 W_r, fp32 x
+    assert lib.moe_prepare_router(None, 0, 1, 64, 8, P, None) == 1
+
+
+def test_size_queries():
+    from dropless_mixture_experts_radix_amd import _lib
+    lib = _lib.lib
+    # fp32 router weights for bf16 rows: 3 bf16 terms per weight, 10 experts per 32-row tile
+    assert lib.moe_router_prepared_bytes(4096, 8, 0, 1) == 32 * 4096 * 2
+    assert lib.moe_router_prepared_bytes(7168, 256, 1, 1) == 256 * 7168 * 2
+    assert lib.moe_router_prepared_bytes(64, 8, 0, 0) == 64 * 8 * 4
+    assert lib.moe_prepared_weight_bytes(8, 4096, 14336, 1, 1) == 8 * 2 * 14336 * 4096 * 2
+    assert lib.moe_prepared_weight_bytes(8, 4096, 14336, 2, 3) == 8 * 2 * 14336 * 4096 // 32
+    assert lib.moe_prepared_weight_bytes(8, 4096, 14336, 1, 3) == 0
+    assert lib.moe_grouped_mlp_workspace_bytes(8192, 14336, 1) >= 8192 * 14336 * 2
+    assert lib.moe_permute_workspace_bytes(8192, 36, 32) >= 8192 * 36 * 4

@@ -1,0 +1,149 @@
+"""GPU parity of the grouped SwiGLU MLP (fp32 1e-5, bf16 2e-2, MXFP8 3e-2 of
+the oracle's largest magnitude), the prepared weight layouts (bit-exact,
+including the MX codes and scales of the weights), ragged groups spanning
+several tiles, empty experts, partial column tiles and untouched rows."""
+import numpy as np
+import pytest
+import torch
+
+import dropless_mixture_experts_radix_amd as D
+from oracle import moe_oracle as O
+from tests.gpu_util import DEV, TOL, bf16_from_f64, np_of, rel_inf, say, to_f64
+
+pytestmark = pytest.mark.gpu
+
+DT = {"f32": D.F32, "bf16": D.BF16, "mxfp8": D.MXFP8}
+
+
+def _interleave_rows(F):
+    p = np.arange(2 * F)
+    return (p // 64) * 32 + p % 32 + np.where((p // 32) % 2 == 1, F, 0)
+
+
+def _weights(rng, L, H, F, dt, scale=0.05):
+    W1 = [rng.standard_normal((H, 2 * F)) * scale for _ in range(L)]
+    W2 = [rng.standard_normal((F, H)) * scale for _ in range(L)]
+    if dt == "f32":
+        W1 = [w.astype(np.float32).astype(np.float64) for w in W1]
+        W2 = [w.astype(np.float32).astype(np.float64) for w in W2]
+    else:
+        W1 = [O.bf16_round(w) for w in W1]
+        W2 = [O.bf16_round(w) for w in W2]
+    return W1, W2
+
+
+def _dev(v, dt):
+    if dt == "f32":
+        return torch.from_numpy(np.asarray(v, np.float32)).to(DEV)
+    return bf16_from_f64(np.asarray(v))
+
+
+def _run_mlp(counts, H, F, dt, seed=0, xscale=1.0, check_layout=True):
+    rng = np.random.default_rng(seed)
+    L = len(counts)
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    N = int(offsets[-1])
+    cap = N + 40
+    W1, W2 = _weights(rng, L, H, F, dt)
+    x64 = rng.standard_normal((cap, H)) * xscale
+    x64 = x64.astype(np.float32).astype(np.float64) if dt == "f32" else O.bf16_round(x64)
+    code = DT[dt]
+    w1 = torch.stack([_dev(w, dt) for w in W1])
+    w2 = torch.stack([_dev(w, dt) for w in W2])
+    wdt = {"f32": torch.float32, "bf16": torch.bfloat16, "mxfp8": torch.uint8}[dt]
+    w1p = torch.empty((L, 2 * F, H), dtype=wdt, device=DEV)
+    w2p = torch.empty((L, H, F), dtype=wdt, device=DEV)
+    w1s = w2s = None
+    if dt == "mxfp8":
+        w1s = torch.empty((L, 2 * F, H // 32), dtype=torch.uint8, device=DEV)
+        w2s = torch.empty((L, H, F // 32), dtype=torch.uint8, device=DEV)
+    D.moe_prepare_weights(w1, w2, code, w1p, w2p, w1s, w2s)
+    perm = _interleave_rows(F)
+    if check_layout:
+        e = L - 1
+        if dt == "mxfp8":
+            c1, s1 = O.mx_quantize_rows(W1[e].T[perm])
+            c2, s2 = O.mx_quantize_rows(W2[e].T)
+            np.testing.assert_array_equal(np_of(w1p[e]), c1)
+            np.testing.assert_array_equal(np_of(w1s[e]), s1)
+            np.testing.assert_array_equal(np_of(w2p[e]), c2)
+            np.testing.assert_array_equal(np_of(w2s[e]), s2)
+        else:
+            np.testing.assert_array_equal(to_f64(w1p[e]), W1[e].T[perm])
+            np.testing.assert_array_equal(to_f64(w2p[e]), W2[e].T)
+    xd = _dev(x64, "f32" if dt == "f32" else "bf16")
+    xs = None
+    if dt == "mxfp8":
+        xq = torch.empty((cap, H), dtype=torch.uint8, device=DEV)
+        xs = torch.empty((cap, H // 32), dtype=torch.uint8, device=DEV)
+        D.moe_mx_quantize(xd, xq, xs)
+        xd = xq
+    ydt = torch.float32 if dt == "f32" else torch.bfloat16
+    y = torch.full((cap, H), 5.0, dtype=ydt, device=DEV)
+    ws = torch.empty(D.moe_grouped_mlp_workspace_bytes(cap, F, code), dtype=torch.uint8, device=DEV)
+    off_d = torch.from_numpy(offsets).to(DEV)
+    say("mlp", dt, "L", L, "H", H, "F", F, "N", N)
+    D.moe_grouped_mlp(xd, off_d, w1p, w2p, y, ws, code, H, F, x_perm_scales=xs, w1p_scales=w1s, w2p_scales=w2s)
+    torch.cuda.synchronize()
+    want_y, want_a = O.grouped_mlp(x64[:N], offsets, W1, W2, dt)
+    got_y = to_f64(y)
+    assert (got_y[N:] == 5.0).all()
+    if N:
+        say("  y rel err", rel_inf(got_y[:N], want_y))
+        assert rel_inf(got_y[:N], want_y) <= TOL[dt], rel_inf(got_y[:N], want_y)
+        if dt == "f32":
+            a = ws[: cap * F * 4].view(torch.float32).view(cap, F)
+            assert rel_inf(to_f64(a)[:N], want_a) <= TOL[dt]
+        elif dt == "bf16":
+            a = ws[: cap * F * 2].view(torch.bfloat16).view(cap, F)
+            assert rel_inf(to_f64(a)[:N], want_a) <= TOL[dt]
+        else:
+            codes = np_of(ws[: cap * F].view(cap, F))[:N]
+            off = (cap * F + 255) // 256 * 256
+            sc = np_of(ws[off: off + cap * (F // 32)].view(cap, F // 32))[:N]
+            a_dq = O.mx_dequantize_rows(codes, sc)
+            # every element within half an E4M3 step of the oracle's bf16 `a`, or clamped
+            # at 448 * 2^E where the MX conversion saturates, plus an absolute slack of
+            # 1e-3 of the largest |a| for the fp32 accumulation inside the matrix cores
+            scl = np.ldexp(1.0, sc.astype(np.int64) - 127).repeat(32, axis=1)
+            bound = (np.abs(want_a) * (2.0 ** -4 + 2.0 ** -7) + 1e-3 * np.abs(want_a).max() +
+                     np.maximum(0.0, np.abs(want_a) * (1 + 2.0 ** -7) - 448 * scl))
+            bad = np.argwhere(np.abs(a_dq - want_a) > bound)
+            assert bad.size == 0, (len(bad), [(int(r), int(c), float(a_dq[r, c]), float(want_a[r, c]))
+                                              for r, c in bad[:8]])
+            # the codes themselves agree except where fp32 and fp64 land on opposite
+            # sides of a bf16 or E4M3 rounding boundary
+            oc, os_ = O.mx_quantize_rows(want_a)
+            assert (codes == oc).mean() > 0.97 and (sc == os_).mean() > 0.99
+            # scale rule: every non-zero block's largest code magnitude lies in [256, 448]
+            mags = O.e4m3_decode(codes & 0x7F).reshape(N, F // 32, 32).max(axis=2)
+            nz = mags > 0
+            big = O.mx_dequantize_rows(codes, sc).reshape(N, F // 32, 32)
+            assert ((mags[nz] >= 256) | (np.abs(big).max(axis=2)[nz] < 2.0 ** -118)).all()
+    return got_y, want_y
+
+
+@pytest.mark.parametrize("counts,H,F", [([100, 0, 37, 256], 64, 128), ([3, 1, 0, 4], 32, 32),
+                                        ([300, 65, 0, 1, 64], 96, 64)])
+def test_grouped_mlp_f32(counts, H, F):
+    _run_mlp(counts, H, F, "f32", seed=sum(counts))
+
+
+@pytest.mark.parametrize("counts,H,F", [
+    ([0, 1, 255, 256, 257, 600, 0, 31], 256, 512),
+    ([1000, 24, 0, 513], 1024, 1536),
+    ([70, 300, 0, 5], 320, 192),          # partial column tiles in both GEMMs
+    ([0, 0, 0, 0], 256, 256),             # no rows at all
+    ([2048], 512, 512),
+])
+def test_grouped_mlp_bf16(counts, H, F):
+    _run_mlp(counts, H, F, "bf16", seed=sum(counts) + H)
+
+
+@pytest.mark.parametrize("counts,H,F", [
+    ([0, 1, 255, 256, 257, 600, 0, 31], 256, 512),
+    ([900, 24, 0, 513], 1024, 1536),
+    ([70, 300, 0, 5], 384, 384),
+])
+def test_grouped_mlp_mxfp8(counts, H, F):
+    _run_mlp(counts, H, F, "mxfp8", seed=sum(counts) + H)
