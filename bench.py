@@ -1,0 +1,234 @@
+"""Benchmark of the dropless MoE layer hot path on one MI355X.
+
+One step = one pass of the whole layer over one batch: route (fused x.W_r
+projection + top-K), count/scan/permute, grouped SwiGLU MLP, combine.
+Workload: the Mixtral-like layer, T=4096 tokens, H=4096, E=8 experts, top-2,
+SwiGLU F=14336, bf16 activations/weights, fp32 router; synthetic seeded
+inputs resident in HBM before the timed region.
+
+    python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--no-cpu] [--no-mx]
+
+Prints one JSON line: layer microseconds (the metric), per-stage times, the
+grouped-GEMM TFLOP/s, route/permute/combine GB/s, the roofline of the dominant
+launch pair (the two grouped GEMMs of moe_grouped_mlp, timed with events on the
+stream they run on), and the CPU oracle timed on a bounded sample.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+FP8_PEAK_TFLOPS = 5000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-mx", action="store_true", help="skip the MXFP8 variant")
+    ap.add_argument("--cpu-tokens", type=int, default=4096, help="tokens in the CPU oracle sample")
+    return ap.parse_args()
+
+
+def build(cfgname):
+    import dropless_mixture_experts_radix_amd as D
+    from workloads import get_config
+    from workloads.gen import make_expert_weights, make_router_inputs, make_tokens
+
+    cfg = get_config(cfgname)
+    dt = {"bf16": D.BF16, "mxfp8": D.MXFP8, "f32": D.F32}
+    x = make_tokens(cfg).cuda()
+    r = make_router_inputs(cfg)
+    layer = D.MoELayer(cfg.T, cfg.H, cfg.E, cfg.K, cfg.F, dt[cfg.dtype], dt[cfg.x_dtype], L=cfg.local, e0=cfg.e0,
+                       score=D.SIGMOID if cfg.score == "sigmoid" else D.SOFTMAX, w_router=r["w_router"].cuda(),
+                       bias=None if r["bias"] is None else r["bias"].cuda())
+    for e in range(cfg.local):
+        w1, w2 = make_expert_weights(cfg, cfg.e0 + e, device="cuda")
+        layer.set_expert_weights(e, w1, w2)
+        del w1, w2
+    torch.cuda.synchronize()
+    return cfg, layer, x, r
+
+
+def time_steps(layer, x, steps, warmup):
+    for _ in range(warmup):
+        layer.forward(x)
+    torch.cuda.synchronize()
+    s = torch.cuda.current_stream()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(s)
+    for _ in range(steps):
+        layer.forward(x)
+    t1.record(s)
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) / steps
+
+
+def time_stages(layer, x, reps):
+    """Per-stage times with events between the four calls (same stream)."""
+    s = torch.cuda.current_stream()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+    acc = np.zeros(4)
+    for _ in range(reps):
+        ev[0].record(s)
+        layer.route(x=x)
+        ev[1].record(s)
+        layer.permute(x)
+        ev[2].record(s)
+        layer.mlp()
+        ev[3].record(s)
+        layer.combine()
+        ev[4].record(s)
+        torch.cuda.synchronize()
+        acc += [ev[i].elapsed_time(ev[i + 1]) for i in range(4)]
+    return acc / reps * 1000.0  # us
+
+
+def time_graph(layer, x, reps):
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        layer.forward(x)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        g.replay()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(reps):
+        g.replay()
+    t1.record()
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) / reps * 1000.0
+
+
+def algorithmic(cfg, N):
+    T, H, E, K, F = cfg.T, cfg.H, cfg.E, cfg.K, cfg.F
+    bx = 2
+    route_b = T * H * bx + H * E * (4 if cfg.wr_dtype == "f32" else 2) + T * K * (2 + 4)
+    row_b = H + H // 32 if cfg.dtype == "mxfp8" else H * bx
+    permute_b = T * H * bx + N * row_b + T * K * 2 + T * K * 4 + N * 4
+    combine_b = N * H * 2 + T * K * 4 + T * K * 4 + T * H * 2
+    flops = 6.0 * N * H * F
+    return route_b, permute_b, combine_b, flops
+
+
+def cpu_baseline(cfg, layer, x, r, ntok):
+    """The oracle as it stands, on the first `ntok` tokens of the same workload
+    (route from the projection, count/permute, float64 grouped MLP, combine),
+    scaled to the whole layer (x T/ntok).  Weights are converted to float64
+    before the clock starts."""
+    from oracle import moe_oracle as O
+    from workloads.gen import make_expert_weights, to_numpy_f64
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:
+        cores = len(os.sched_getaffinity(0))
+    xs = to_numpy_f64(x[:ntok])
+    wr = to_numpy_f64(r["w_router"])
+    W1, W2 = [], []
+    for e in range(cfg.local):
+        w1, w2 = make_expert_weights(cfg, cfg.e0 + e, device="cuda")
+        W1.append(to_numpy_f64(w1))
+        W2.append(to_numpy_f64(w2))
+        del w1, w2
+    t0 = time.perf_counter()
+    res = O.layer(xs, cfg.K, W1, W2, cfg.dtype, w_router=wr, score=cfg.score, e0=cfg.e0, L=cfg.local)
+    dt = time.perf_counter() - t0
+    del W1, W2
+    # sanity: the sample's output agrees with the GPU layer on the same tokens
+    gpu = to_numpy_f64(layer.out[:ntok])
+    err = float(np.abs(gpu - res["out"]).max() / max(np.abs(res["out"]).max(), 1e-30))
+    return {"value": dt * 1e6 * cfg.T / ntok, "unit": "us", "cores": int(cores), "kind": "oracle",
+            "sample": f"first {ntok} of {cfg.T} tokens, whole layer (route, permute, fp64 grouped MLP, combine), "
+                      f"{dt:.2f} s measured, scaled x{cfg.T // ntok}; max rel diff vs GPU on the sample {err:.2e}"}
+
+
+def mx_variant(steps, warmup):
+    cfg, layer, x, r = build("mixtral_mxfp8")
+    ms = time_steps(layer, x, steps, warmup)
+    st = time_stages(layer, x, 10)
+    N = int(layer.offsets[-1].item())
+    route_b, permute_b, combine_b, flops = algorithmic(cfg, N)
+    out = {"layer_us": ms * 1000.0, "stage_us": dict(zip(["route", "permute", "grouped_mlp", "combine"],
+                                                         [round(v, 2) for v in st])),
+           "grouped_gemm_tflops": flops / (st[2] * 1e-6) / 1e12,
+           "grouped_gemm_frac_fp8_peak": flops / (st[2] * 1e-6) / 1e12 / FP8_PEAK_TFLOPS,
+           "permute_quantize_gbs": permute_b / (st[1] * 1e-6) / 1e9}
+    del layer
+    torch.cuda.empty_cache()
+    return out
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {a.gpus} is not supported (this build has no multi-GPU "
+              f"path)", file=sys.stderr)
+        sys.exit(2)
+    cfg, layer, x, r = build("mixtral_bf16")
+    layer.forward(x)
+    torch.cuda.synchronize()
+    N = int(layer.offsets[-1].item())
+    torch.cuda.synchronize()
+    ms = time_steps(layer, x, a.steps, a.warmup)
+    st = time_stages(layer, x, 20)
+    gus = time_graph(layer, x, a.steps)
+    route_b, permute_b, combine_b, flops = algorithmic(cfg, N)
+    t_route, t_perm, t_mlp, t_comb = st
+    tflops = flops / (t_mlp * 1e-6) / 1e12
+    line = {
+        "metric": "MoE layer us; grouped-GEMM TFLOPS + permute/combine GB/s, 1 MI355X",
+        "value": round(ms * 1000.0, 2),
+        "unit": "us",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "mixtral_bf16: T=4096 H=4096 E=8 K=2 SwiGLU F=14336, bf16 rows/weights, "
+                               "fp32 router", "tokens": cfg.T, "routed_rows": N},
+        "stage_us": {"route": round(t_route, 2), "permute": round(t_perm, 2), "grouped_mlp": round(t_mlp, 2),
+                     "combine": round(t_comb, 2)},
+        "graph_replay_us": round(gus, 2),
+        "grouped_gemm_tflops": round(tflops, 1),
+        "route_gbs": round(route_b / (t_route * 1e-6) / 1e9, 1),
+        "permute_gbs": round(permute_b / (t_perm * 1e-6) / 1e9, 1),
+        "combine_gbs": round(combine_b / (t_comb * 1e-6) / 1e9, 1),
+        "roofline": {"kernel": "moe_grouped_mlp: k_gemm_bf16<1> (GEMM1+SwiGLU) + k_gemm_bf16<0> (GEMM2)",
+                     "bound": "mfma", "achieved": round(tflops, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tflops / BF16_PEAK_TFLOPS, 4), "traffic": None},
+    }
+    if not a.no_mx:
+        try:
+            del layer
+            torch.cuda.empty_cache()
+            line["mxfp8"] = mx_variant(max(a.steps // 2, 5), a.warmup)
+            cfg, layer, x, r = build("mixtral_bf16")
+            layer.forward(x)
+            torch.cuda.synchronize()
+        except Exception as ex:  # report, do not hide the main line
+            line["mxfp8"] = {"error": repr(ex)}
+    if not a.no_cpu:
+        line["cpu_baseline"] = cpu_baseline(cfg, layer, x, r, a.cpu_tokens)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
