@@ -19,30 +19,44 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 // ---------------------------------------------------------------------------
-// bf16 grouped GEMM: out tile 256 x 256, k step 64, 512 threads (8 wavefronts
-// as 2 x 4), wavefront tile 128 x 64 = 4 x 2 of v_mfma_f32_32x32x16_bf16.
-// A [rows][Kd] bf16 (expert-ordered rows), B [L][N][Kd] bf16 (prepared,
-// contraction-contiguous).  LDS tiles are double-buffered; their 16-byte
-// chunks are XOR-swizzled by (row % 8) so the fragment reads of 32 rows at one
-// k offset spread over all banks.
-// EPI 0: out[row][col] = bf16(acc)                       (N columns)
-// EPI 1: gate/up column chunks of 32 are interleaved in B; out[row][j] =
-//        bf16(silu(gate) * up)                            (N/2 columns)
+// bf16 grouped GEMM: out tile 256 x 256, k step 64, 512 threads = 8 wavefronts
+// as 2 (rows) x 4 (columns), each wavefront 128 x 64 = 4 x 2 tiles of
+// v_mfma_f32_32x32x16_bf16; two wavefronts per SIMD hide each other's waits.
+//
+// LDS bandwidth (about 128 B/clk per CU) is the scarce resource of this loop:
+// staging both operands through LDS costs more LDS cycles than the MFMAs they
+// feed.  So only A goes through LDS; B (the expert weights) is prepared in
+// MFMA fragment order and loaded straight into registers:
+//   B block of one 256-column panel and one 64-wide k step = 32 KiB,
+//   [j: 8 groups of 32 columns][s: 4 k sub-steps of 16][lane: 64][8 bf16],
+//   lane l holds column 32 j + l%32, k = 16 s + 8 (l/32) .. +8,
+// so each wavefront reads its 8 fragments of a k step as 8 contiguous 1 KiB
+// pieces, one k step ahead.  A [rows][Kd] (EPI 1: x_perm) or k-blocked
+// [Kd/64][capacity][64] (EPI 0: the activations) is read with buffer loads
+// (past the tile's rows they return zeros), staged in registers one k step
+// ahead and stored to padded LDS rows (144 bytes: 16 consecutive rows start in
+// 16 different bank groups).  Prefetch indices are clamped to the last k step
+// instead of branching, and Kd is a multiple of 128 so k steps come in pairs:
+// the k loop has no branches.
+// EPI 0: out[row][col] = bf16(acc)                                   (N columns)
+// EPI 1: gate/up chunks of 32 columns are interleaved in B; out = k-blocked
+//        activations [N/128][capacity][64], a[row][j] = bf16(silu(gate) * up)
 // ---------------------------------------------------------------------------
 #define GB_BM 256
 #define GB_BN 256
 #define GB_BK 64
+#define GB_LDK 72  // padded LDS row (elements)
+#define GB_THREADS 512
 
 template <int EPI>
-__global__ __launch_bounds__(512, 1) void k_gemm_bf16(int L, int N, int Kd, int64_t capacity,
-                                                      const bf16_t* __restrict__ A,
-                                                      const int32_t* __restrict__ offsets,
-                                                      const bf16_t* __restrict__ B, bf16_t* __restrict__ out) {
+__global__ __launch_bounds__(GB_THREADS, 1) void k_gemm_bf16(int L, int N, int Kd, int64_t capacity,
+                                                             const bf16_t* __restrict__ A,
+                                                             const int32_t* __restrict__ offsets,
+                                                             const bf16_t* __restrict__ B, bf16_t* __restrict__ out) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  bf16_t* sA = (bf16_t*)smem;                       // [2][256][64]
-  bf16_t* sB = sA + 2 * GB_BM * GB_BK;              // [2][256][64]
-  int32_t* s_pre = (int32_t*)(sB + 2 * GB_BN * GB_BK);  // [L+1]
-  int32_t* s_tmp = s_pre + (L + 1);                 // [16]
+  bf16_t* sA = (bf16_t*)smem;                            // [2][256][72]
+  int32_t* s_pre = (int32_t*)(sA + 2 * GB_BM * GB_LDK);  // [L+1]
+  int32_t* s_tmp = s_pre + (L + 1);                      // [16]
   const int NT = (N + GB_BN - 1) / GB_BN;
   build_schedule(L, capacity, GB_BM, NT, offsets, s_pre, s_tmp);
   const int total = s_pre[L];
@@ -50,89 +64,94 @@ __global__ __launch_bounds__(512, 1) void k_gemm_bf16(int L, int N, int Kd, int6
   const int wm = wv >> 2, wn = wv & 3;
   const int g = l >> 5, r32 = l & 31;
   const int KT = Kd / GB_BK;
+  // A global -> LDS: thread loads 16-byte chunk lkc of rows lrow + 64 i (i < 4)
+  const int lrow = tid >> 3, lkc = tid & 7;
+  const int st_off = lrow * GB_LDK + lkc * 8;
+  // A fragment reads: row wm*128 + i*32 + r32, k chunk 2s + g
+  const int fa_base = (wm * 128 + r32) * GB_LDK + g * 8;
+  // B fragment (jj, s) of this wavefront: byte offset in a k-step block
+  const int vbf = (wn * 8) * 1024 + l * 16;
 
   for (int it = virtual_block(); it < total; it += gridDim.x) {
     const TileInfo ti = locate_tile(it, L, capacity, GB_BM, NT, offsets, s_pre);
     const int col0 = ti.nt * GB_BN;
-    // global load assignment: 4 chunks of 16 bytes per thread for A and for B
-    const bf16_t* ga[4];
-    const bf16_t* gb[4];
-    int lds_off[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = tid + 512 * i, row = c >> 3, kc = c & 7;
-      const int ar = ti.row0 + min(row, ti.rows - 1);
-      ga[i] = A + (long)ar * Kd + kc * 8;
-      const int bc = min(col0 + row, N - 1);
-      gb[i] = B + ((long)ti.e * N + bc) * Kd + kc * 8;
-      lds_off[i] = row * GB_BK + ((kc ^ (row & 7)) << 3);
-    }
-    u32x4 ra[4], rb[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      ra[i] = *(const u32x4*)ga[i];
-      rb[i] = *(const u32x4*)gb[i];
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      *(u32x4*)(sA + lds_off[i]) = ra[i];
-      *(u32x4*)(sB + lds_off[i]) = rb[i];
-    }
-    __syncthreads();
+    const int NPAN = (N + GB_BN - 1) / GB_BN;
+    const __amdgpu_buffer_rsrc_t rB = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(B + ((long)ti.e * NPAN + ti.nt) * (long)KT * GB_BN * GB_BK), (short)0,
+        KT * GB_BN * GB_BK * 2, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rA =
+        EPI == 1 ? __builtin_amdgcn_make_buffer_rsrc((void*)(A + (long)ti.row0 * Kd), (short)0, ti.rows * Kd * 2,
+                                                     0x00020000)
+                 : __builtin_amdgcn_make_buffer_rsrc((void*)A, (short)0, (int)(KT * capacity * GB_BK * 2), 0x00020000);
+    const int va = EPI == 1 ? (lrow * Kd + lkc * 8) * 2 : ((ti.row0 + lrow) * GB_BK + lkc * 8) * 2;
+    const int astride = EPI == 1 ? 64 * Kd * 2 : 64 * GB_BK * 2;
+    const int akstep = EPI == 1 ? GB_BK * 2 : (int)(capacity * GB_BK * 2);
 
+    u32x4 ast[4];             // A register stage
+    bf16x8 bf0[8], bf1[8];    // B fragments of two k steps, index jj*4 + s
+#define GB_ALOAD(KT_)                                                                       \
+  {                                                                                         \
+    const int koa = va + (KT_) * akstep;                                                    \
+    _Pragma("unroll") for (int i = 0; i < 4; ++i)                                           \
+      ast[i] = __builtin_amdgcn_raw_buffer_load_b128(rA, koa + i * astride, 0, 0);          \
+  }
+#define GB_ASTORE(BUF)                                                                      \
+  {                                                                                         \
+    bf16_t* dA = sA + (BUF) * GB_BM * GB_LDK + st_off;                                      \
+    _Pragma("unroll") for (int i = 0; i < 4; ++i)                                           \
+      *(u32x4*)(dA + i * 64 * GB_LDK) = ast[i];                                             \
+  }
+#define GB_BLOAD(BF, KT_)                                                                   \
+  {                                                                                         \
+    const int kb = (KT_) * (GB_BN * GB_BK * 2);                                             \
+    _Pragma("unroll") for (int q = 0; q < 8; ++q)                                           \
+      BF[q] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rB, vbf, kb + q * 1024, 0)); \
+  }
+#define GB_COMPUTE(BUF, BF)                                                                 \
+  {                                                                                         \
+    const bf16_t* cA = sA + (BUF) * GB_BM * GB_LDK + fa_base;                               \
+    _Pragma("unroll") for (int s = 0; s < 4; ++s) {                                         \
+      bf16x8 fa[4];                                                                         \
+      _Pragma("unroll") for (int i = 0; i < 4; ++i)                                         \
+        fa[i] = *(const bf16x8*)(cA + i * 32 * GB_LDK + s * 16);                            \
+      _Pragma("unroll") for (int i = 0; i < 4; ++i)                                         \
+        _Pragma("unroll") for (int jj = 0; jj < 2; ++jj)                                    \
+          acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], BF[jj * 4 + s], acc[i][jj], 0, 0, 0); \
+    }                                                                                       \
+  }
     f32x16 acc[4][2];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
-    // m sub-tiles of this wavefront that hold valid rows
-    const int msub = min(4, max(0, (ti.rows - wm * 128 + 31) / 32));
 
-    for (int kt = 0; kt < KT; ++kt) {
-      const int cur = kt & 1;
-      if (kt + 1 < KT) {
-        const int ko = (kt + 1) * GB_BK;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          ra[i] = *(const u32x4*)(ga[i] + ko);
-          rb[i] = *(const u32x4*)(gb[i] + ko);
-        }
-      }
-      const bf16_t* cA = sA + cur * GB_BM * GB_BK;
-      const bf16_t* cB = sB + cur * GB_BN * GB_BK;
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const int kc = 2 * s + g;
-        bf16x8 fb[2];
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const int n = wn * 64 + j * 32 + r32;
-          fb[j] = *(const bf16x8*)(cB + n * GB_BK + ((kc ^ (n & 7)) << 3));
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          if (i < msub) {
-            const int m = wm * 128 + i * 32 + r32;
-            const bf16x8 fa = *(const bf16x8*)(cA + m * GB_BK + ((kc ^ (m & 7)) << 3));
-#pragma unroll
-            for (int j = 0; j < 2; ++j)
-              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa, fb[j], acc[i][j], 0, 0, 0);
-          }
-        }
-      }
-      if (kt + 1 < KT) {
-        bf16_t* nA = sA + (cur ^ 1) * GB_BM * GB_BK;
-        bf16_t* nB = sB + (cur ^ 1) * GB_BN * GB_BK;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          *(u32x4*)(nA + lds_off[i]) = ra[i];
-          *(u32x4*)(nB + lds_off[i]) = rb[i];
-        }
-      }
+    // prologue: A(0) into LDS buffer 0, A(1) in registers, B(0) in bf0
+    GB_ALOAD(0);
+    GB_BLOAD(bf0, 0);
+    GB_ASTORE(0);
+    GB_ALOAD(1);
+    __syncthreads();
+    // steady state (KT even): at an even step kt, LDS buffer 0 holds A(kt),
+    // ast holds A(kt+1), bf0 holds B(kt)
+    for (int kt = 0; kt < KT; kt += 2) {
+      GB_BLOAD(bf1, kt + 1);
+      GB_COMPUTE(0, bf0);
+      GB_ASTORE(1);
+      GB_ALOAD(min(kt + 2, KT - 1));
+      __syncthreads();
+      GB_BLOAD(bf0, min(kt + 2, KT - 1));
+      GB_COMPUTE(1, bf1);
+      GB_ASTORE(0);
+      GB_ALOAD(min(kt + 3, KT - 1));
       __syncthreads();
     }
+#undef GB_ALOAD
+#undef GB_ASTORE
+#undef GB_BLOAD
+#undef GB_COMPUTE
 
     // epilogue
+    const int msub = min(4, max(0, (ti.rows - wm * 128 + 31) / 32));
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       if (i >= msub) continue;
@@ -150,7 +169,8 @@ __global__ __launch_bounds__(512, 1) void k_gemm_bf16(int L, int N, int Kd, int6
         } else {
           const int jcol = (col0 >> 1) + wn * 32 + r32;
           if (jcol < (N >> 1))
-            out[grow * (N >> 1) + jcol] = (bf16_t)f32_to_bf16(silu_mul(acc[i][0][v], acc[i][1][v]));
+            out[((long)(jcol >> 6) * capacity + grow) * GB_BK + (jcol & 63)] =
+                (bf16_t)f32_to_bf16(silu_mul(acc[i][0][v], acc[i][1][v]));
         }
       }
     }
@@ -257,7 +277,7 @@ hipError_t launch_grouped_mlp_f32(int L, int H, int F, int64_t capacity, const f
 }
 
 static size_t gemm_bf16_lds(int L) {
-  return (size_t)2 * (GB_BM + GB_BN) * GB_BK * sizeof(bf16_t) + (size_t)(L + 1 + 16) * sizeof(int32_t);
+  return (size_t)2 * GB_BM * GB_LDK * sizeof(bf16_t) + (size_t)(L + 1 + 16) * sizeof(int32_t);
 }
 
 hipError_t launch_grouped_mlp_bf16(int L, int H, int F, int64_t capacity, const bf16_t* x,
@@ -272,9 +292,9 @@ hipError_t launch_grouped_mlp_bf16(int L, int H, int F, int64_t capacity, const 
     attr_done = true;
   }
   const int N1 = 2 * F, N2 = H;
-  hipLaunchKernelGGL(k_gemm_bf16<1>, dim3(grid_for(capacity, L, GB_BM, (N1 + GB_BN - 1) / GB_BN, 1)), dim3(512),
+  hipLaunchKernelGGL(k_gemm_bf16<1>, dim3(grid_for(capacity, L, GB_BM, (N1 + GB_BN - 1) / GB_BN, 1)), dim3(GB_THREADS),
                      lds, s, L, N1, H, capacity, x, offsets, w1p, act);
-  hipLaunchKernelGGL(k_gemm_bf16<0>, dim3(grid_for(capacity, L, GB_BM, (N2 + GB_BN - 1) / GB_BN, 1)), dim3(512),
+  hipLaunchKernelGGL(k_gemm_bf16<0>, dim3(grid_for(capacity, L, GB_BM, (N2 + GB_BN - 1) / GB_BN, 1)), dim3(GB_THREADS),
                      lds, s, L, N2, F, capacity, act, offsets, w2p, y);
   return hipGetLastError();
 }

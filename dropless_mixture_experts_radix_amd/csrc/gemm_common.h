@@ -87,6 +87,11 @@ __device__ __forceinline__ TileInfo locate_tile(int it, int L, int64_t capacity,
   return ti;
 }
 
+// XOR swizzle of the 16-byte chunks of a 128-byte LDS row: rows 0..7 get
+// distinct chunks, and rows r, r+8 (which share banks when 16 lanes are
+// served per cycle from 64 banks) differ too.
+__device__ __forceinline__ int lds_swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+
 __device__ __forceinline__ int virtual_block() {
   const int G = gridDim.x, b = blockIdx.x;
   return (G % 8 == 0) ? (b % 8) * (G / 8) + b / 8 : b;

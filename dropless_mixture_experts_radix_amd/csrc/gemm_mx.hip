@@ -92,7 +92,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_mx(int L, int N, int Kd, int64_
       ga[i] = A + (long)ar * Kd + kc * 16;
       const int bc = min(col0 + row, N - 1);
       gb[i] = B + ((long)ti.e * N + bc) * Kd + kc * 16;
-      lds_off[i] = row * GM_BK + ((kc ^ (row & 7)) << 4);
+      lds_off[i] = row * GM_BK + ((kc ^ lds_swz(row)) << 4);
     }
     // scales: thread tid < 256 loads the 4 A scale bytes of row tid, 256.. the B ones
     const int srow = tid & 255;
@@ -147,8 +147,8 @@ __global__ __launch_bounds__(512, 1) void k_gemm_mx(int L, int N, int Kd, int64_
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
           const int n = wn * 64 + j * 32 + r32;
-          const u32x4 lo = *(const u32x4*)(cB + n * GM_BK + ((c0 ^ (n & 7)) << 4));
-          const u32x4 hi = *(const u32x4*)(cB + n * GM_BK + ((c1 ^ (n & 7)) << 4));
+          const u32x4 lo = *(const u32x4*)(cB + n * GM_BK + ((c0 ^ lds_swz(n)) << 4));
+          const u32x4 hi = *(const u32x4*)(cB + n * GM_BK + ((c1 ^ lds_swz(n)) << 4));
           fb[j] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
           sb[j] = cBs[n * 4 + 2 * s + g];
         }
@@ -156,8 +156,8 @@ __global__ __launch_bounds__(512, 1) void k_gemm_mx(int L, int N, int Kd, int64_
         for (int i = 0; i < 4; ++i) {
           if (i < msub) {
             const int m = wm * 128 + i * 32 + r32;
-            const u32x4 lo = *(const u32x4*)(cA + m * GM_BK + ((c0 ^ (m & 7)) << 4));
-            const u32x4 hi = *(const u32x4*)(cA + m * GM_BK + ((c1 ^ (m & 7)) << 4));
+            const u32x4 lo = *(const u32x4*)(cA + m * GM_BK + ((c0 ^ lds_swz(m)) << 4));
+            const u32x4 hi = *(const u32x4*)(cA + m * GM_BK + ((c1 ^ lds_swz(m)) << 4));
             const i32x8 fa = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
             const int sa = cAs[m * 4 + 2 * s + g];
 #pragma unroll

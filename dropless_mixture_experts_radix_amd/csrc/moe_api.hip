@@ -139,7 +139,11 @@ int moe_permute(int T, int H, int K, int E_global, int e0, int L, int64_t capaci
 size_t moe_prepared_weight_bytes(int L, int H, int F, int dtype, int which) {
   if (L <= 0 || H <= 0 || F <= 0) return 0;
   const size_t el = dtype == MOE_F32 ? 4 : (dtype == MOE_BF16 ? 2 : 1);
-  const size_t n1 = (size_t)L * 2 * F * H, n2 = (size_t)L * H * F;
+  size_t n1 = (size_t)L * 2 * F * H, n2 = (size_t)L * H * F;
+  if (dtype == MOE_BF16) {  // whole 256-row panels
+    n1 = (size_t)L * ((2 * (size_t)F + 255) / 256 * 256) * H;
+    n2 = (size_t)L * (((size_t)H + 255) / 256 * 256) * F;
+  }
   switch (which) {
     case 1: return n1 * el;
     case 2: return n2 * el;
@@ -152,6 +156,7 @@ size_t moe_prepared_weight_bytes(int L, int H, int F, int dtype, int which) {
 int moe_prepare_weights(int L, int H, int F, int in_dtype, int dtype, const void* w1, const void* w2,
                         void* w1p, void* w2p, uint8_t* w1p_scales, uint8_t* w2p_scales, void* stream) {
   if (L < 1 || L > MOE_MAX_L || H <= 0 || F <= 0 || H % 32 || F % 32) return MOE_ERR_SHAPE;
+  if (dtype == MOE_BF16 && (H % 128 || F % 128)) return MOE_ERR_SHAPE;  // pairs of 64-wide k steps
   if (!((dtype == MOE_F32 && in_dtype == MOE_F32) || (dtype == MOE_BF16 && in_dtype == MOE_BF16) ||
         (dtype == MOE_MXFP8 && in_dtype == MOE_BF16)))
     return MOE_ERR_DTYPE;
@@ -183,9 +188,12 @@ int moe_grouped_mlp(int L, int H, int F, int64_t capacity, int dtype, const void
   if (dtype == MOE_F32) {
     if (H % 16 || F % 32) return MOE_ERR_SHAPE;
   } else if (dtype == MOE_BF16) {
-    if (H % 64 || F % 64) return MOE_ERR_SHAPE;
+    if (H % 128 || F % 128) return MOE_ERR_SHAPE;
+    // byte offsets of the activation buffers stay within 31 bits
+    if (capacity * (int64_t)(H > F ? H : F) * 2 > (int64_t)INT32_MAX) return MOE_ERR_SHAPE;
   } else if (dtype == MOE_MXFP8) {
     if (H % 128 || F % 128) return MOE_ERR_SHAPE;
+    if (capacity * (int64_t)(H > F ? H : F) > (int64_t)INT32_MAX) return MOE_ERR_SHAPE;
   } else {
     return MOE_ERR_DTYPE;
   }

@@ -2,16 +2,23 @@
 // quantizer.
 //
 // bpdata article, reproduction settings: the expert weights are pre-fused once.
-// Prepared layout (per expert): W1p [2F][H], row p = column c(p) of W1[e] with
-// gate/up chunks of 32 interleaved, c(p) = (p/64)*32 + p%32 + ((p/32)%2 ? F : 0);
-// W2p [H][F], row n = column n of W2[e].  Rows are contraction-contiguous, the
-// layout the grouped GEMM streams.
+// Prepared rows (per expert): W1 row p = column c(p) of W1[e] with gate/up
+// chunks of 32 interleaved, c(p) = (p/64)*32 + p%32 + ((p/32)%2 ? F : 0);
+// W2 row n = column n of W2[e].  Rows run along the contraction dimension; the
+// bf16 layout is additionally blocked so the grouped GEMM streams contiguous
+// 32 KiB pieces.
 #include "moe_internal.h"
 
 namespace moe {
 
-// One 32 x 32 tile of one expert: logical W [Kd][Ncols] -> prepared [Ncols][Kd].
-// MODE 0: fp32 -> fp32, 1: bf16 -> bf16, 2: bf16 -> MX E4M3 codes + scales.
+// One 32 x 32 tile of one expert: logical W [Kd][Ncols] -> prepared rows.
+// MODE 0: fp32 -> fp32, row-major [Ncols][Kd].
+// MODE 1: bf16 -> bf16 in MFMA fragment order: per 256-row panel and 64-wide
+//         k step one contiguous 32 KiB block [j: 8][s: 4][lane: 64][8], where
+//         lane l holds row 32 j + l%32 and k = 16 s + 8 (l/32) .. +8 of the step
+//         (the B-operand layout of v_mfma_f32_32x32x16_bf16); rows past Ncols in
+//         the last panel are zero.
+// MODE 2: bf16 -> MX E4M3 codes [Ncols][Kd] + scales [Ncols][Kd/32].
 template <int MODE>
 __global__ __launch_bounds__(256) void k_prepare(int Kd, int Ncols, int F_interleave,
                                                  const void* __restrict__ w, void* __restrict__ wp,
@@ -20,24 +27,37 @@ __global__ __launch_bounds__(256) void k_prepare(int Kd, int Ncols, int F_interl
   const int e = blockIdx.z;
   const int pc = blockIdx.x;  // prepared 32-row chunk
   const int k0 = blockIdx.y * 32;
+  const bool live = pc * 32 < Ncols;
   const int cbase = F_interleave ? (pc >> 1) * 32 + ((pc & 1) ? F_interleave : 0) : pc * 32;
   const long in_off = (long)e * Kd * Ncols;
-  const long out_off = (long)e * Ncols * Kd;
   const int tid = threadIdx.x;
-  // load: 32 k rows x 32 logical columns
   for (int i = tid; i < 1024; i += 256) {
     const int kk = i >> 5, cc = i & 31;
-    const long src = in_off + (long)(k0 + kk) * Ncols + cbase + cc;
-    uint32_t v = MODE == 0 ? __float_as_uint(((const float*)w)[src]) : ((const bf16_t*)w)[src];
+    uint32_t v = 0;
+    if (live) {
+      const long src = in_off + (long)(k0 + kk) * Ncols + cbase + cc;
+      v = MODE == 0 ? __float_as_uint(((const float*)w)[src]) : ((const bf16_t*)w)[src];
+    }
     tile[cc][kk] = v;
   }
   __syncthreads();
-  if (MODE < 2) {
+  if (MODE == 0) {
+    const long out_off = (long)e * Ncols * Kd;
     for (int i = tid; i < 1024; i += 256) {
       const int pp = i >> 5, kk = i & 31;
-      const long dst = out_off + (long)(pc * 32 + pp) * Kd + k0 + kk;
-      if (MODE == 0) ((float*)wp)[dst] = __uint_as_float(tile[pp][kk]);
-      else ((bf16_t*)wp)[dst] = (bf16_t)tile[pp][kk];
+      ((float*)wp)[out_off + (long)(pc * 32 + pp) * Kd + k0 + kk] = __uint_as_float(tile[pp][kk]);
+    }
+  } else if (MODE == 1) {
+    const int NP = (Ncols + 255) / 256, KT = Kd / 64;
+    const long out_off = (long)e * NP * 256 * Kd;
+    for (int i = tid; i < 1024; i += 256) {
+      const int pp = i >> 5, kk = i & 31;
+      const int p = pc * 32 + pp, k = k0 + kk;
+      const int r = p & 255, q = k & 63;
+      const int lane = (r & 31) + 32 * ((q >> 3) & 1);
+      const long o = out_off + ((long)(p >> 8) * KT + (k >> 6)) * (256 * 64) +
+                     ((((r >> 5) * 4 + (q >> 4)) * 64 + lane) * 8) + (q & 7);
+      ((bf16_t*)wp)[o] = (bf16_t)tile[pp][kk];
     }
   } else if (tid < 32) {
     const int pp = tid;
@@ -57,16 +77,19 @@ __global__ __launch_bounds__(256) void k_prepare(int Kd, int Ncols, int F_interl
 hipError_t launch_prepare_weights(int L, int H, int F, int dtype, const void* w1, const void* w2,
                                   void* w1p, void* w2p, uint8_t* w1s, uint8_t* w2s, hipStream_t s) {
   if (L == 0) return hipSuccess;
-  const dim3 g1(2 * F / 32, H / 32, L), g2(H / 32, F / 32, L), b(256);
+  const dim3 b(256);
   if (dtype == MOE_F32) {
-    hipLaunchKernelGGL(k_prepare<0>, g1, b, 0, s, H, 2 * F, F, w1, w1p, (uint8_t*)nullptr);
-    hipLaunchKernelGGL(k_prepare<0>, g2, b, 0, s, F, H, 0, w2, w2p, (uint8_t*)nullptr);
+    hipLaunchKernelGGL(k_prepare<0>, dim3(2 * F / 32, H / 32, L), b, 0, s, H, 2 * F, F, w1, w1p, (uint8_t*)nullptr);
+    hipLaunchKernelGGL(k_prepare<0>, dim3(H / 32, F / 32, L), b, 0, s, F, H, 0, w2, w2p, (uint8_t*)nullptr);
   } else if (dtype == MOE_BF16) {
-    hipLaunchKernelGGL(k_prepare<1>, g1, b, 0, s, H, 2 * F, F, w1, w1p, (uint8_t*)nullptr);
-    hipLaunchKernelGGL(k_prepare<1>, g2, b, 0, s, F, H, 0, w2, w2p, (uint8_t*)nullptr);
+    // prepared rows padded to whole 256-row panels
+    hipLaunchKernelGGL(k_prepare<1>, dim3((2 * F + 255) / 256 * 8, H / 32, L), b, 0, s, H, 2 * F, F, w1, w1p,
+                       (uint8_t*)nullptr);
+    hipLaunchKernelGGL(k_prepare<1>, dim3((H + 255) / 256 * 8, F / 32, L), b, 0, s, F, H, 0, w2, w2p,
+                       (uint8_t*)nullptr);
   } else {
-    hipLaunchKernelGGL(k_prepare<2>, g1, b, 0, s, H, 2 * F, F, w1, w1p, w1s);
-    hipLaunchKernelGGL(k_prepare<2>, g2, b, 0, s, F, H, 0, w2, w2p, w2s);
+    hipLaunchKernelGGL(k_prepare<2>, dim3(2 * F / 32, H / 32, L), b, 0, s, H, 2 * F, F, w1, w1p, w1s);
+    hipLaunchKernelGGL(k_prepare<2>, dim3(H / 32, F / 32, L), b, 0, s, F, H, 0, w2, w2p, w2s);
   }
   return hipGetLastError();
 }

@@ -36,8 +36,10 @@ class MoELayer:
             self.w_prep = torch.empty(nb, dtype=torch.uint8, device=dev)
             M.moe_prepare_router(w_router, x_dtype, self.w_prep)
         wdt = {M.F32: torch.float32, M.BF16: torch.bfloat16, M.MXFP8: torch.uint8}[dtype]
-        self.w1p = torch.empty((L, 2 * F, H), dtype=wdt, device=dev)
-        self.w2p = torch.empty((L, H, F), dtype=wdt, device=dev)
+        # bf16 prepared weights come in whole 256-row panels (blocked layout)
+        pad = (lambda n: (n + 255) // 256 * 256) if dtype == M.BF16 else (lambda n: n)
+        self.w1p = torch.empty((L, pad(2 * F), H), dtype=wdt, device=dev)
+        self.w2p = torch.empty((L, pad(H), F), dtype=wdt, device=dev)
         self.w1s = self.w2s = None
         if dtype == M.MXFP8:
             self.w1s = torch.empty((L, 2 * F, H // 32), dtype=torch.uint8, device=dev)
@@ -76,8 +78,9 @@ class MoELayer:
         cap, F = self.capacity, self.F
         if self.dtype == M.F32:
             return self.mlp_ws[: cap * F * 4].view(torch.float32).view(cap, F)
-        if self.dtype == M.BF16:
-            return self.mlp_ws[: cap * F * 2].view(torch.bfloat16).view(cap, F)
+        if self.dtype == M.BF16:  # k-blocked [F/64][capacity][64]
+            blk = self.mlp_ws[: cap * F * 2].view(torch.bfloat16).view(F // 64, cap, 64)
+            return blk.permute(1, 0, 2).reshape(cap, F)
         codes = self.mlp_ws[: cap * F].view(cap, F)
         off = (cap * F + 255) // 256 * 256
         scales = self.mlp_ws[off: off + cap * (F // 32)].view(cap, F // 32)

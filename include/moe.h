@@ -216,8 +216,8 @@ int moe_prepare_weights(int L, int H, int F, int in_dtype, int dtype,
  * MOE_MXFP8: x_perm as E4M3 codes + x_perm_scales (from moe_permute), `a`
  *   rounded to bf16 and then MX-quantized along F, y_perm bf16.
  * The schedule of output tiles is built on the device from `offsets`: empty
- * experts get no tiles.  Requires H % 64 == 0 and F % 64 == 0 for MOE_BF16 and
- * MOE_MXFP8, F % 32 == 0 for MOE_F32.
+ * experts get no tiles.  Requires H % 128 == 0 and F % 128 == 0 for MOE_BF16
+ * and MOE_MXFP8, H % 16 == 0 and F % 32 == 0 for MOE_F32.
  * Workspace: moe_grouped_mlp_workspace_bytes(capacity, F, dtype) bytes; it
  * starts with `a` ([capacity][F] in the activation type; for MXFP8 the codes
  * [capacity][F] followed by the scales [capacity][F/32]).

@@ -91,7 +91,8 @@ def test_mlp_validation():
              wsb=1 << 24):
         return f(L, H, F, cap, dt, x, xs, offs, w1, w1s, w2, w2s, y, ws, wsb, None)
 
-    assert call(H=96) == 2               # bf16 needs H % 64 == 0
+    assert call(H=96) == 2               # bf16 needs H % 128 == 0
+    assert call(H=192) == 2
     assert call(dt=2, F=192) == 2        # MXFP8 needs F % 128 == 0
     assert call(dt=2) == 1               # MX scales missing
     assert call(dt=9) == 4

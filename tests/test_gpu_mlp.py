@@ -20,6 +20,16 @@ def _interleave_rows(F):
     return (p // 64) * 32 + p % 32 + np.where((p // 32) % 2 == 1, F, 0)
 
 
+def _unblock(wp):
+    """bf16 prepared weights of one expert, in MFMA fragment order
+    [rows/256][Kd/64][j 8][s 4][lane 64][8] (lane l: row 32j + l%32, k 16s + 8(l/32)),
+    back to rows x Kd (float64)."""
+    rows, kd = wp.shape
+    t = wp.reshape(rows // 256, kd // 64, 8, 4, 2, 32, 8)      # panel, kt, j, s, g, r, e
+    t = t.permute(0, 2, 5, 1, 3, 4, 6)                          # panel, j, r, kt, s, g, e
+    return to_f64(t.reshape(rows, kd))
+
+
 def _weights(rng, L, H, F, dt, scale=0.05):
     W1 = [rng.standard_normal((H, 2 * F)) * scale for _ in range(L)]
     W2 = [rng.standard_normal((F, H)) * scale for _ in range(L)]
@@ -51,8 +61,9 @@ def _run_mlp(counts, H, F, dt, seed=0, xscale=1.0, check_layout=True):
     w1 = torch.stack([_dev(w, dt) for w in W1])
     w2 = torch.stack([_dev(w, dt) for w in W2])
     wdt = {"f32": torch.float32, "bf16": torch.bfloat16, "mxfp8": torch.uint8}[dt]
-    w1p = torch.empty((L, 2 * F, H), dtype=wdt, device=DEV)
-    w2p = torch.empty((L, H, F), dtype=wdt, device=DEV)
+    pad = (lambda n: (n + 255) // 256 * 256) if dt == "bf16" else (lambda n: n)
+    w1p = torch.empty((L, pad(2 * F), H), dtype=wdt, device=DEV)
+    w2p = torch.empty((L, pad(H), F), dtype=wdt, device=DEV)
     w1s = w2s = None
     if dt == "mxfp8":
         w1s = torch.empty((L, 2 * F, H // 32), dtype=torch.uint8, device=DEV)
@@ -68,6 +79,10 @@ def _run_mlp(counts, H, F, dt, seed=0, xscale=1.0, check_layout=True):
             np.testing.assert_array_equal(np_of(w1s[e]), s1)
             np.testing.assert_array_equal(np_of(w2p[e]), c2)
             np.testing.assert_array_equal(np_of(w2s[e]), s2)
+        elif dt == "bf16":
+            np.testing.assert_array_equal(_unblock(w1p[e])[: 2 * F], W1[e].T[perm])
+            np.testing.assert_array_equal(_unblock(w2p[e])[:H], W2[e].T)
+            assert (_unblock(w1p[e])[2 * F:] == 0).all() and (_unblock(w2p[e])[H:] == 0).all()
         else:
             np.testing.assert_array_equal(to_f64(w1p[e]), W1[e].T[perm])
             np.testing.assert_array_equal(to_f64(w2p[e]), W2[e].T)
@@ -94,8 +109,8 @@ def _run_mlp(counts, H, F, dt, seed=0, xscale=1.0, check_layout=True):
         if dt == "f32":
             a = ws[: cap * F * 4].view(torch.float32).view(cap, F)
             assert rel_inf(to_f64(a)[:N], want_a) <= TOL[dt]
-        elif dt == "bf16":
-            a = ws[: cap * F * 2].view(torch.bfloat16).view(cap, F)
+        elif dt == "bf16":  # k-blocked activations [F/64][cap][64]
+            a = ws[: cap * F * 2].view(torch.bfloat16).view(F // 64, cap, 64).permute(1, 0, 2).reshape(cap, F)
             assert rel_inf(to_f64(a)[:N], want_a) <= TOL[dt]
         else:
             codes = np_of(ws[: cap * F].view(cap, F))[:N]
@@ -132,7 +147,7 @@ def test_grouped_mlp_f32(counts, H, F):
 @pytest.mark.parametrize("counts,H,F", [
     ([0, 1, 255, 256, 257, 600, 0, 31], 256, 512),
     ([1000, 24, 0, 513], 1024, 1536),
-    ([70, 300, 0, 5], 320, 192),          # partial column tiles in both GEMMs
+    ([70, 300, 0, 5], 384, 128),          # partial column tiles in both GEMMs
     ([0, 0, 0, 0], 256, 256),             # no rows at all
     ([2048], 512, 512),
 ])
