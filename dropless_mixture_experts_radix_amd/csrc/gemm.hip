@@ -23,21 +23,18 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 // as 2 (rows) x 4 (columns), each wavefront 128 x 64 = 4 x 2 tiles of
 // v_mfma_f32_32x32x16_bf16; two wavefronts per SIMD hide each other's waits.
 //
-// LDS bandwidth (about 128 B/clk per CU) is the scarce resource of this loop:
-// staging both operands through LDS costs more LDS cycles than the MFMAs they
-// feed.  So only A goes through LDS; B (the expert weights) is prepared in
-// MFMA fragment order and loaded straight into registers:
-//   B block of one 256-column panel and one 64-wide k step = 32 KiB,
-//   [j: 8 groups of 32 columns][s: 4 k sub-steps of 16][lane: 64][8 bf16],
-//   lane l holds column 32 j + l%32, k = 16 s + 8 (l/32) .. +8,
-// so each wavefront reads its 8 fragments of a k step as 8 contiguous 1 KiB
-// pieces, one k step ahead.  A [rows][Kd] (EPI 1: x_perm) or k-blocked
-// [Kd/64][capacity][64] (EPI 0: the activations) is read with buffer loads
-// (past the tile's rows they return zeros), staged in registers one k step
-// ahead and stored to padded LDS rows (144 bytes: 16 consecutive rows start in
-// 16 different bank groups).  Prefetch indices are clamped to the last k step
-// instead of branching, and Kd is a multiple of 128 so k steps come in pairs:
-// the k loop has no branches.
+// The L2 -> CU path (about 64 B/clk per CU) is the scarce resource of this
+// loop, so every operand byte of a tile crosses it once per k step: each thread
+// moves the same four 16-byte chunks of the A and of the B k-step tile
+// (64 KiB per k step) into registers one k step ahead, then into padded LDS
+// rows (144 bytes: 16 consecutive rows start in 16 different bank groups), and
+// the wavefronts read their MFMA fragments from LDS.  A is [rows][Kd] (EPI 1:
+// x_perm) or k-blocked [Kd/64][capacity][64] (EPI 0: the activations); B is the
+// prepared weight panel of 256 output columns, k-blocked [Kd/64][256][64], so a
+// k-step tile of B is one contiguous 32 KiB block.  Both are read with buffer
+// loads, which return zeros past the tile's rows.  Prefetch indices are clamped
+// to the last k step instead of branching, and Kd is a multiple of 128 so k
+// steps come in pairs: the k loop has no branches.
 // EPI 0: out[row][col] = bf16(acc)                                   (N columns)
 // EPI 1: gate/up chunks of 32 columns are interleaved in B; out = k-blocked
 //        activations [N/128][capacity][64], a[row][j] = bf16(silu(gate) * up)
@@ -45,7 +42,8 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 #define GB_BM 256
 #define GB_BN 256
 #define GB_BK 64
-#define GB_LDK 72  // padded LDS row (elements)
+#define GB_LDK 72                   // padded LDS row (elements)
+#define GB_STAGE (GB_BM * GB_LDK)   // elements of one operand stage
 #define GB_THREADS 512
 
 template <int EPI>
@@ -54,9 +52,10 @@ __global__ __launch_bounds__(GB_THREADS, 1) void k_gemm_bf16(int L, int N, int K
                                                              const int32_t* __restrict__ offsets,
                                                              const bf16_t* __restrict__ B, bf16_t* __restrict__ out) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  bf16_t* sA = (bf16_t*)smem;                            // [2][256][72]
-  int32_t* s_pre = (int32_t*)(sA + 2 * GB_BM * GB_LDK);  // [L+1]
-  int32_t* s_tmp = s_pre + (L + 1);                      // [16]
+  bf16_t* sA = (bf16_t*)smem;                         // [2][256][72]
+  bf16_t* sB = sA + 2 * GB_STAGE;                     // [2][256][72]
+  int32_t* s_pre = (int32_t*)(sB + 2 * GB_STAGE);     // [L+1]
+  int32_t* s_tmp = s_pre + (L + 1);                   // [16]
   const int NT = (N + GB_BN - 1) / GB_BN;
   build_schedule(L, capacity, GB_BM, NT, offsets, s_pre, s_tmp);
   const int total = s_pre[L];
@@ -64,20 +63,22 @@ __global__ __launch_bounds__(GB_THREADS, 1) void k_gemm_bf16(int L, int N, int K
   const int wm = wv >> 2, wn = wv & 3;
   const int g = l >> 5, r32 = l & 31;
   const int KT = Kd / GB_BK;
-  // A global -> LDS: thread loads 16-byte chunk lkc of rows lrow + 64 i (i < 4)
+  // global -> LDS: thread moves 16-byte chunk lkc of rows lrow + 64 i (i < 4)
+  // of both the A and the B k-step tile
   const int lrow = tid >> 3, lkc = tid & 7;
   const int st_off = lrow * GB_LDK + lkc * 8;
-  // A fragment reads: row wm*128 + i*32 + r32, k chunk 2s + g
+  // fragment reads: A row wm*128 + i*32 + r32, B column wn*64 + jj*32 + r32,
+  // k chunk 2s + g of the k step
   const int fa_base = (wm * 128 + r32) * GB_LDK + g * 8;
-  // B fragment (jj, s) of this wavefront: byte offset in a k-step block
-  const int vbf = (wn * 8) * 1024 + l * 16;
+  const int fb_base = (wn * 64 + r32) * GB_LDK + g * 8;
+  const int vb = (lrow * GB_BK + lkc * 8) * 2;
 
   for (int it = virtual_block(); it < total; it += gridDim.x) {
     const TileInfo ti = locate_tile(it, L, capacity, GB_BM, NT, offsets, s_pre);
     const int col0 = ti.nt * GB_BN;
-    const int NPAN = (N + GB_BN - 1) / GB_BN;
+    // the (expert, panel) B tile: KT blocks of [256 columns][64 k]
     const __amdgpu_buffer_rsrc_t rB = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(B + ((long)ti.e * NPAN + ti.nt) * (long)KT * GB_BN * GB_BK), (short)0,
+        (void*)(B + ((long)ti.e * NT + ti.nt) * (long)KT * GB_BN * GB_BK), (short)0,
         KT * GB_BN * GB_BK * 2, 0x00020000);
     const __amdgpu_buffer_rsrc_t rA =
         EPI == 1 ? __builtin_amdgcn_make_buffer_rsrc((void*)(A + (long)ti.row0 * Kd), (short)0, ti.rows * Kd * 2,
@@ -87,36 +88,38 @@ __global__ __launch_bounds__(GB_THREADS, 1) void k_gemm_bf16(int L, int N, int K
     const int astride = EPI == 1 ? 64 * Kd * 2 : 64 * GB_BK * 2;
     const int akstep = EPI == 1 ? GB_BK * 2 : (int)(capacity * GB_BK * 2);
 
-    u32x4 ast[4];             // A register stage
-    bf16x8 bf0[8], bf1[8];    // B fragments of two k steps, index jj*4 + s
-#define GB_ALOAD(KT_)                                                                       \
+    u32x4 ast[4], bst[4];  // register stage of the next k step
+#define GB_LOAD(AS, BS, KT_)                                                                \
   {                                                                                         \
     const int koa = va + (KT_) * akstep;                                                    \
-    _Pragma("unroll") for (int i = 0; i < 4; ++i)                                           \
-      ast[i] = __builtin_amdgcn_raw_buffer_load_b128(rA, koa + i * astride, 0, 0);          \
+    const int kob = (KT_) * (GB_BN * GB_BK * 2);                                            \
+    _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                         \
+      AS[i] = __builtin_amdgcn_raw_buffer_load_b128(rA, koa + i * astride, 0, 0);           \
+      BS[i] = __builtin_amdgcn_raw_buffer_load_b128(rB, vb + i * (64 * GB_BK * 2), kob, 0); \
+    }                                                                                       \
   }
-#define GB_ASTORE(BUF)                                                                      \
+#define GB_STORE(BUF, AS, BS)                                                               \
   {                                                                                         \
-    bf16_t* dA = sA + (BUF) * GB_BM * GB_LDK + st_off;                                      \
-    _Pragma("unroll") for (int i = 0; i < 4; ++i)                                           \
-      *(u32x4*)(dA + i * 64 * GB_LDK) = ast[i];                                             \
+    bf16_t* dA = sA + (BUF) * GB_STAGE + st_off;                                            \
+    bf16_t* dB = sB + (BUF) * GB_STAGE + st_off;                                            \
+    _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                         \
+      *(u32x4*)(dA + i * 64 * GB_LDK) = AS[i];                                              \
+      *(u32x4*)(dB + i * 64 * GB_LDK) = BS[i];                                              \
+    }                                                                                       \
   }
-#define GB_BLOAD(BF, KT_)                                                                   \
+#define GB_COMPUTE(BUF)                                                                     \
   {                                                                                         \
-    const int kb = (KT_) * (GB_BN * GB_BK * 2);                                             \
-    _Pragma("unroll") for (int q = 0; q < 8; ++q)                                           \
-      BF[q] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rB, vbf, kb + q * 1024, 0)); \
-  }
-#define GB_COMPUTE(BUF, BF)                                                                 \
-  {                                                                                         \
-    const bf16_t* cA = sA + (BUF) * GB_BM * GB_LDK + fa_base;                               \
+    const bf16_t* cA = sA + (BUF) * GB_STAGE + fa_base;                                     \
+    const bf16_t* cB = sB + (BUF) * GB_STAGE + fb_base;                                     \
     _Pragma("unroll") for (int s = 0; s < 4; ++s) {                                         \
-      bf16x8 fa[4];                                                                         \
+      bf16x8 fa[4], fb[2];                                                                  \
+      _Pragma("unroll") for (int jj = 0; jj < 2; ++jj)                                      \
+        fb[jj] = *(const bf16x8*)(cB + jj * 32 * GB_LDK + s * 16);                          \
       _Pragma("unroll") for (int i = 0; i < 4; ++i)                                         \
         fa[i] = *(const bf16x8*)(cA + i * 32 * GB_LDK + s * 16);                            \
       _Pragma("unroll") for (int i = 0; i < 4; ++i)                                         \
         _Pragma("unroll") for (int jj = 0; jj < 2; ++jj)                                    \
-          acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], BF[jj * 4 + s], acc[i][jj], 0, 0, 0); \
+          acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[jj], acc[i][jj], 0, 0, 0); \
     }                                                                                       \
   }
     f32x16 acc[4][2];
@@ -125,29 +128,25 @@ __global__ __launch_bounds__(GB_THREADS, 1) void k_gemm_bf16(int L, int N, int K
 #pragma unroll
       for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
 
-    // prologue: A(0) into LDS buffer 0, A(1) in registers, B(0) in bf0
-    GB_ALOAD(0);
-    GB_BLOAD(bf0, 0);
-    GB_ASTORE(0);
-    GB_ALOAD(1);
+    // prologue: k step 0 into LDS buffer 0, k step 1 in registers
+    GB_LOAD(ast, bst, 0);
+    GB_STORE(0, ast, bst);
+    GB_LOAD(ast, bst, 1);
     __syncthreads();
-    // steady state (KT even): at an even step kt, LDS buffer 0 holds A(kt),
-    // ast holds A(kt+1), bf0 holds B(kt)
+    // steady state (KT even): at an even step kt, LDS buffer 0 holds step kt
+    // and the registers hold step kt+1
     for (int kt = 0; kt < KT; kt += 2) {
-      GB_BLOAD(bf1, kt + 1);
-      GB_COMPUTE(0, bf0);
-      GB_ASTORE(1);
-      GB_ALOAD(min(kt + 2, KT - 1));
+      GB_COMPUTE(0);
+      GB_STORE(1, ast, bst);
+      GB_LOAD(ast, bst, min(kt + 2, KT - 1));
       __syncthreads();
-      GB_BLOAD(bf0, min(kt + 2, KT - 1));
-      GB_COMPUTE(1, bf1);
-      GB_ASTORE(0);
-      GB_ALOAD(min(kt + 3, KT - 1));
+      GB_COMPUTE(1);
+      GB_STORE(0, ast, bst);
+      GB_LOAD(ast, bst, min(kt + 3, KT - 1));
       __syncthreads();
     }
-#undef GB_ALOAD
-#undef GB_ASTORE
-#undef GB_BLOAD
+#undef GB_LOAD
+#undef GB_STORE
 #undef GB_COMPUTE
 
     // epilogue
@@ -277,7 +276,7 @@ hipError_t launch_grouped_mlp_f32(int L, int H, int F, int64_t capacity, const f
 }
 
 static size_t gemm_bf16_lds(int L) {
-  return (size_t)2 * GB_BM * GB_LDK * sizeof(bf16_t) + (size_t)(L + 1 + 16) * sizeof(int32_t);
+  return (size_t)4 * GB_STAGE * sizeof(bf16_t) + (size_t)(L + 1 + 16) * sizeof(int32_t);
 }
 
 hipError_t launch_grouped_mlp_bf16(int L, int H, int F, int64_t capacity, const bf16_t* x,

@@ -13,10 +13,8 @@ namespace moe {
 
 // One 32 x 32 tile of one expert: logical W [Kd][Ncols] -> prepared rows.
 // MODE 0: fp32 -> fp32, row-major [Ncols][Kd].
-// MODE 1: bf16 -> bf16 in MFMA fragment order: per 256-row panel and 64-wide
-//         k step one contiguous 32 KiB block [j: 8][s: 4][lane: 64][8], where
-//         lane l holds row 32 j + l%32 and k = 16 s + 8 (l/32) .. +8 of the step
-//         (the B-operand layout of v_mfma_f32_32x32x16_bf16); rows past Ncols in
+// MODE 1: bf16 -> bf16 in k-blocked panels: per 256-row panel and 64-wide k
+//         step one contiguous 32 KiB block [256 rows][64 k]; rows past Ncols in
 //         the last panel are zero.
 // MODE 2: bf16 -> MX E4M3 codes [Ncols][Kd] + scales [Ncols][Kd/32].
 template <int MODE>
@@ -53,10 +51,7 @@ __global__ __launch_bounds__(256) void k_prepare(int Kd, int Ncols, int F_interl
     for (int i = tid; i < 1024; i += 256) {
       const int pp = i >> 5, kk = i & 31;
       const int p = pc * 32 + pp, k = k0 + kk;
-      const int r = p & 255, q = k & 63;
-      const int lane = (r & 31) + 32 * ((q >> 3) & 1);
-      const long o = out_off + ((long)(p >> 8) * KT + (k >> 6)) * (256 * 64) +
-                     ((((r >> 5) * 4 + (q >> 4)) * 64 + lane) * 8) + (q & 7);
+      const long o = out_off + ((long)(p >> 8) * KT + (k >> 6)) * (256 * 64) + (p & 255) * 64 + (k & 63);
       ((bf16_t*)wp)[o] = (bf16_t)tile[pp][kk];
     }
   } else if (tid < 32) {

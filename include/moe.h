@@ -123,9 +123,11 @@ size_t moe_router_prepared_bytes(int H, int E, int w_dtype, int x_dtype);
 /* Lay out the router weights W_r [H,E] (w_dtype MOE_F32 or MOE_BF16, device)
  * for moe_route_topk with activations of type x_dtype.  Output `prepared`
  * (device) has moe_router_prepared_bytes(...) bytes:
- *  x_dtype MOE_BF16: bf16 [C][H], C = ceil(P*E/32)*32 rows, row p*E+e holds
- *    term p of column e of W_r (P = 3 terms hi/mid/lo for fp32 W_r with
- *    W = hi + mid + lo, P = 1 for bf16 W_r); the remaining rows are zero.
+ *  x_dtype MOE_BF16: bf16 [C][H] in tiles of 32 rows.  With P terms per
+ *    weight (P = 3, hi/mid/lo with W = hi + mid + lo, for fp32 W_r; P = 1 for
+ *    bf16 W_r) a tile holds ept = floor(32/P) experts: row 32*t + p*ept + j
+ *    holds term p of column e = t*ept + j of W_r.  C = ceil(E/ept)*32; rows
+ *    with p >= P or e >= E are zero.
  *  x_dtype MOE_F32: fp32 W_r [H,E] copied unchanged. */
 int moe_prepare_router(const void* w_router, int w_dtype, int x_dtype, int H, int E,
                        void* prepared, void* stream);
@@ -185,7 +187,11 @@ int moe_permute(int T, int H, int K, int E_global, int e0, int L, int64_t capaci
  *       c(p) = (p/64)*32 + p%32 + ((p/32)%2 ? F : 0)   (gate/up chunks of 32
  *       interleaved so one output tile holds matching gate and up columns)
  *   W2p [L][H][F]: row n holds column n of W2[e] along F.
- * dtype MOE_F32 / MOE_BF16: values in that type (in_dtype must match).
+ * dtype MOE_F32: values in fp32, rows exactly as above.
+ * dtype MOE_BF16: the rows above padded with zero rows to whole panels of 256
+ *   (W1p [L][ceil(2F/256)*256][H], W2p [L][ceil(H/256)*256][F]), each panel
+ *   k-blocked: [panel][k/64][256 rows][64 k], so one 64-wide k step of a panel
+ *   is a contiguous 32 KiB block.  Requires H % 128 == 0 and F % 128 == 0.
  * dtype MOE_MXFP8 (in_dtype MOE_BF16): W1p/W2p hold E4M3 codes (uint8) and
  *   w1p_scales [L][2F][H/32], w2p_scales [L][H][F/32] the E8M0 block scales
  *   of 32 consecutive elements along each prepared row.

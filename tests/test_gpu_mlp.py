@@ -21,12 +21,10 @@ def _interleave_rows(F):
 
 
 def _unblock(wp):
-    """bf16 prepared weights of one expert, in MFMA fragment order
-    [rows/256][Kd/64][j 8][s 4][lane 64][8] (lane l: row 32j + l%32, k 16s + 8(l/32)),
+    """bf16 prepared weights of one expert, k-blocked panels [rows/256][Kd/64][256][64],
     back to rows x Kd (float64)."""
     rows, kd = wp.shape
-    t = wp.reshape(rows // 256, kd // 64, 8, 4, 2, 32, 8)      # panel, kt, j, s, g, r, e
-    t = t.permute(0, 2, 5, 1, 3, 4, 6)                          # panel, j, r, kt, s, g, e
+    t = wp.reshape(rows // 256, kd // 64, 256, 64).permute(0, 2, 1, 3)   # panel, r, kt, e
     return to_f64(t.reshape(rows, kd))
 
 
