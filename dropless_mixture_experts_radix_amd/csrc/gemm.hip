@@ -33,8 +33,16 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 // prepared weight panel of 256 output columns, k-blocked [Kd/64][256][64], so a
 // k-step tile of B is one contiguous 32 KiB block.  Both are read with buffer
 // loads, which return zeros past the tile's rows.  Prefetch indices are clamped
-// to the last k step instead of branching, and Kd is a multiple of 128 so k
-// steps come in pairs: the k loop has no branches.
+// to the last k step of the range instead of branching, and k ranges have even
+// length so k steps come in pairs: the k loop has no branches.
+//
+// Work units.  With G persistent workgroups and `total` tiles, the first
+// floor(total/G)*G tiles run whole (data parallel).  The `left` tiles of a last,
+// partial round would leave most CUs idle, so when left*2 <= GB_SPLIT_UNITS
+// each of them is split into S pieces along k (split-K), S as large as fits
+// the CUs and the partial buffer.  A piece writes its fp32 partial tile to
+// `part`; k_splitk_reduce then sums the S partials of a tile in piece order
+// (the result does not depend on timing) and applies the epilogue.
 // EPI 0: out[row][col] = bf16(acc)                                   (N columns)
 // EPI 1: gate/up chunks of 32 columns are interleaved in B; out = k-blocked
 //        activations [N/128][capacity][64], a[row][j] = bf16(silu(gate) * up)
@@ -45,12 +53,67 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 #define GB_LDK 72                   // padded LDS row (elements)
 #define GB_STAGE (GB_BM * GB_LDK)   // elements of one operand stage
 #define GB_THREADS 512
+#define GB_SPLIT_UNITS 256          // split-K pieces per launch at most
+#define GB_PART_FLOATS (GB_BM * GB_BN)
+
+struct SplitPlan {
+  int dp;     // tiles run whole: units [0, dp)
+  int S;      // pieces per split tile (1: no split)
+  int units;  // dp + (total - dp) * S
+};
+
+__device__ __forceinline__ SplitPlan split_plan(int total, int G, int KT) {
+  SplitPlan p;
+  const int left = total % G;
+  p.dp = total - left;
+  int S = left > 0 ? min(min(G, GB_SPLIT_UNITS) / left, KT / 2) : 1;
+  S = min(S, 16);
+  if (S < 2) {
+    p.dp = total;
+    S = 1;
+  }
+  p.S = S;
+  p.units = p.dp + (total - p.dp) * S;
+  return p;
+}
+
+// Epilogue of one wavefront's 128 x 64 part of a tile (MFMA D layout: lane l
+// holds column l%32, rows 8 (v/4) + 4 (l/32) + v%4 of each 32 x 32 block).
+template <int EPI>
+__device__ __forceinline__ void store_tile(const f32x16 (&acc)[4][2], const TileInfo& ti, int N, int64_t capacity,
+                                           int wm, int wn, int g, int r32, bf16_t* __restrict__ out) {
+  const int col0 = ti.nt * GB_BN;
+  const int msub = min(4, max(0, (ti.rows - wm * 128 + 31) / 32));
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if (i >= msub) continue;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int row = wm * 128 + i * 32 + 8 * (v >> 2) + 4 * g + (v & 3);
+      if (row >= ti.rows) continue;
+      const long grow = ti.row0 + row;
+      if (EPI == 0) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int col = col0 + wn * 64 + j * 32 + r32;
+          if (col < N) out[grow * N + col] = (bf16_t)f32_to_bf16(acc[i][j][v]);
+        }
+      } else {
+        const int jcol = (col0 >> 1) + wn * 32 + r32;
+        if (jcol < (N >> 1))
+          out[((long)(jcol >> 6) * capacity + grow) * GB_BK + (jcol & 63)] =
+              (bf16_t)f32_to_bf16(silu_mul(acc[i][0][v], acc[i][1][v]));
+      }
+    }
+  }
+}
 
 template <int EPI>
 __global__ __launch_bounds__(GB_THREADS, 1) void k_gemm_bf16(int L, int N, int Kd, int64_t capacity,
                                                              const bf16_t* __restrict__ A,
                                                              const int32_t* __restrict__ offsets,
-                                                             const bf16_t* __restrict__ B, bf16_t* __restrict__ out) {
+                                                             const bf16_t* __restrict__ B, bf16_t* __restrict__ out,
+                                                             float* __restrict__ part) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   bf16_t* sA = (bf16_t*)smem;                         // [2][256][72]
   bf16_t* sB = sA + 2 * GB_STAGE;                     // [2][256][72]
@@ -58,11 +121,11 @@ __global__ __launch_bounds__(GB_THREADS, 1) void k_gemm_bf16(int L, int N, int K
   int32_t* s_tmp = s_pre + (L + 1);                   // [16]
   const int NT = (N + GB_BN - 1) / GB_BN;
   build_schedule(L, capacity, GB_BM, NT, offsets, s_pre, s_tmp);
-  const int total = s_pre[L];
+  const int KT = Kd / GB_BK;
+  const SplitPlan plan = split_plan(s_pre[L], gridDim.x, KT);
   const int tid = threadIdx.x, wv = tid >> 6, l = tid & 63;
   const int wm = wv >> 2, wn = wv & 3;
   const int g = l >> 5, r32 = l & 31;
-  const int KT = Kd / GB_BK;
   // global -> LDS: thread moves 16-byte chunk lkc of rows lrow + 64 i (i < 4)
   // of both the A and the B k-step tile
   const int lrow = tid >> 3, lkc = tid & 7;
@@ -73,9 +136,16 @@ __global__ __launch_bounds__(GB_THREADS, 1) void k_gemm_bf16(int L, int N, int K
   const int fb_base = (wn * 64 + r32) * GB_LDK + g * 8;
   const int vb = (lrow * GB_BK + lkc * 8) * 2;
 
-  for (int it = virtual_block(); it < total; it += gridDim.x) {
-    const TileInfo ti = locate_tile(it, L, capacity, GB_BM, NT, offsets, s_pre);
-    const int col0 = ti.nt * GB_BN;
+  for (int u = virtual_block(); u < plan.units; u += gridDim.x) {
+    int tile = u, k0 = 0, k1 = KT, piece = -1;
+    if (u >= plan.dp) {  // split-K piece: k steps [k0, k1), an even count
+      piece = u - plan.dp;
+      tile = plan.dp + piece / plan.S;
+      const int q = piece % plan.S, half = KT / 2;
+      k0 = 2 * (q * half / plan.S);
+      k1 = 2 * ((q + 1) * half / plan.S);
+    }
+    const TileInfo ti = locate_tile(tile, L, capacity, GB_BM, NT, offsets, s_pre);
     // the (expert, panel) B tile: KT blocks of [256 columns][64 k]
     const __amdgpu_buffer_rsrc_t rB = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(B + ((long)ti.e * NT + ti.nt) * (long)KT * GB_BN * GB_BK), (short)0,
@@ -89,22 +159,22 @@ __global__ __launch_bounds__(GB_THREADS, 1) void k_gemm_bf16(int L, int N, int K
     const int akstep = EPI == 1 ? GB_BK * 2 : (int)(capacity * GB_BK * 2);
 
     u32x4 ast[4], bst[4];  // register stage of the next k step
-#define GB_LOAD(AS, BS, KT_)                                                                \
+#define GB_LOAD(KT_)                                                                        \
   {                                                                                         \
     const int koa = va + (KT_) * akstep;                                                    \
     const int kob = (KT_) * (GB_BN * GB_BK * 2);                                            \
     _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                         \
-      AS[i] = __builtin_amdgcn_raw_buffer_load_b128(rA, koa + i * astride, 0, 0);           \
-      BS[i] = __builtin_amdgcn_raw_buffer_load_b128(rB, vb + i * (64 * GB_BK * 2), kob, 0); \
+      ast[i] = __builtin_amdgcn_raw_buffer_load_b128(rA, koa + i * astride, 0, 0);          \
+      bst[i] = __builtin_amdgcn_raw_buffer_load_b128(rB, vb + i * (64 * GB_BK * 2), kob, 0); \
     }                                                                                       \
   }
-#define GB_STORE(BUF, AS, BS)                                                               \
+#define GB_STORE(BUF)                                                                       \
   {                                                                                         \
     bf16_t* dA = sA + (BUF) * GB_STAGE + st_off;                                            \
     bf16_t* dB = sB + (BUF) * GB_STAGE + st_off;                                            \
     _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                         \
-      *(u32x4*)(dA + i * 64 * GB_LDK) = AS[i];                                              \
-      *(u32x4*)(dB + i * 64 * GB_LDK) = BS[i];                                              \
+      *(u32x4*)(dA + i * 64 * GB_LDK) = ast[i];                                             \
+      *(u32x4*)(dB + i * 64 * GB_LDK) = bst[i];                                             \
     }                                                                                       \
   }
 #define GB_COMPUTE(BUF)                                                                     \
@@ -128,52 +198,74 @@ __global__ __launch_bounds__(GB_THREADS, 1) void k_gemm_bf16(int L, int N, int K
 #pragma unroll
       for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
 
-    // prologue: k step 0 into LDS buffer 0, k step 1 in registers
-    GB_LOAD(ast, bst, 0);
-    GB_STORE(0, ast, bst);
-    GB_LOAD(ast, bst, 1);
+    // prologue: k step k0 into LDS buffer 0, k step k0+1 in registers
+    GB_LOAD(k0);
+    GB_STORE(0);
+    GB_LOAD(k0 + 1);
     __syncthreads();
-    // steady state (KT even): at an even step kt, LDS buffer 0 holds step kt
-    // and the registers hold step kt+1
-    for (int kt = 0; kt < KT; kt += 2) {
+    // steady state: at step kt (kt - k0 even) LDS buffer 0 holds step kt and
+    // the registers hold step kt+1
+    for (int kt = k0; kt < k1; kt += 2) {
       GB_COMPUTE(0);
-      GB_STORE(1, ast, bst);
-      GB_LOAD(ast, bst, min(kt + 2, KT - 1));
+      GB_STORE(1);
+      GB_LOAD(min(kt + 2, k1 - 1));
       __syncthreads();
       GB_COMPUTE(1);
-      GB_STORE(0, ast, bst);
-      GB_LOAD(ast, bst, min(kt + 3, KT - 1));
+      GB_STORE(0);
+      GB_LOAD(min(kt + 3, k1 - 1));
       __syncthreads();
     }
 #undef GB_LOAD
 #undef GB_STORE
 #undef GB_COMPUTE
 
-    // epilogue
-    const int msub = min(4, max(0, (ti.rows - wm * 128 + 31) / 32));
+    if (piece < 0) {
+      store_tile<EPI>(acc, ti, N, capacity, wm, wn, g, r32, out);
+    } else {
+      // partial tile in the MFMA D layout: [wavefront][i][j][v][lane]
+      float* dst = part + (long)piece * GB_PART_FLOATS + wv * 8192 + l;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if (i >= msub) continue;
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int row = wm * 128 + i * 32 + 8 * (v >> 2) + 4 * g + (v & 3);
-        if (row >= ti.rows) continue;
-        const long grow = ti.row0 + row;
-        if (EPI == 0) {
+        for (int j = 0; j < 2; ++j)
 #pragma unroll
-          for (int j = 0; j < 2; ++j) {
-            const int col = col0 + wn * 64 + j * 32 + r32;
-            if (col < N) out[grow * N + col] = (bf16_t)f32_to_bf16(acc[i][j][v]);
-          }
-        } else {
-          const int jcol = (col0 >> 1) + wn * 32 + r32;
-          if (jcol < (N >> 1))
-            out[((long)(jcol >> 6) * capacity + grow) * GB_BK + (jcol & 63)] =
-                (bf16_t)f32_to_bf16(silu_mul(acc[i][0][v], acc[i][1][v]));
-        }
-      }
+          for (int v = 0; v < 16; ++v) dst[((i * 2 + j) * 16 + v) * 64] = acc[i][j][v];
     }
   }
+}
+
+// Sum the S split-K partials of each split tile (in piece order) and apply the
+// epilogue.  Launched with the GEMM's grid size G and GB_SPLIT_UNITS / 2
+// workgroups: split tile b of the plan is handled by workgroup b.
+template <int EPI>
+__global__ __launch_bounds__(GB_THREADS) void k_splitk_reduce(int L, int N, int Kd, int64_t capacity, int G,
+                                                              const int32_t* __restrict__ offsets,
+                                                              const float* __restrict__ part,
+                                                              bf16_t* __restrict__ out) {
+  __shared__ int32_t s_pre[MOE_MAX_L + 1];
+  __shared__ int32_t s_tmp[16];
+  const int NT = (N + GB_BN - 1) / GB_BN;
+  build_schedule(L, capacity, GB_BM, NT, offsets, s_pre, s_tmp);
+  const int total = s_pre[L];
+  const SplitPlan plan = split_plan(total, G, Kd / GB_BK);
+  const int b = blockIdx.x;
+  if (plan.S < 2 || b >= total - plan.dp) return;
+  const TileInfo ti = locate_tile(plan.dp + b, L, capacity, GB_BM, NT, offsets, s_pre);
+  const int tid = threadIdx.x, wv = tid >> 6, l = tid & 63;
+  const float* src = part + (long)b * plan.S * GB_PART_FLOATS + wv * 8192 + l;
+  f32x16 acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int o = ((i * 2 + j) * 16 + v) * 64;
+        float sum = src[o];
+        for (int q = 1; q < plan.S; ++q) sum += src[(long)q * GB_PART_FLOATS + o];
+        acc[i][j][v] = sum;
+      }
+  store_tile<EPI>(acc, ti, N, capacity, wv >> 2, wv & 3, l >> 5, l & 31, out);
 }
 
 // ---------------------------------------------------------------------------
@@ -279,9 +371,11 @@ static size_t gemm_bf16_lds(int L) {
   return (size_t)4 * GB_STAGE * sizeof(bf16_t) + (size_t)(L + 1 + 16) * sizeof(int32_t);
 }
 
+size_t grouped_mlp_bf16_part_bytes() { return (size_t)GB_SPLIT_UNITS * GB_PART_FLOATS * sizeof(float); }
+
 hipError_t launch_grouped_mlp_bf16(int L, int H, int F, int64_t capacity, const bf16_t* x,
                                    const int32_t* offsets, const bf16_t* w1p, const bf16_t* w2p,
-                                   bf16_t* act, bf16_t* y, hipStream_t s) {
+                                   bf16_t* act, float* part, bf16_t* y, hipStream_t s) {
   if (capacity == 0) return hipSuccess;
   const size_t lds = gemm_bf16_lds(L);
   static bool attr_done = false;
@@ -291,10 +385,13 @@ hipError_t launch_grouped_mlp_bf16(int L, int H, int F, int64_t capacity, const 
     attr_done = true;
   }
   const int N1 = 2 * F, N2 = H;
-  hipLaunchKernelGGL(k_gemm_bf16<1>, dim3(grid_for(capacity, L, GB_BM, (N1 + GB_BN - 1) / GB_BN, 1)), dim3(GB_THREADS),
-                     lds, s, L, N1, H, capacity, x, offsets, w1p, act);
-  hipLaunchKernelGGL(k_gemm_bf16<0>, dim3(grid_for(capacity, L, GB_BM, (N2 + GB_BN - 1) / GB_BN, 1)), dim3(GB_THREADS),
-                     lds, s, L, N2, F, capacity, act, offsets, w2p, y);
+  const int G1 = grid_for(capacity, L, GB_BM, (N1 + GB_BN - 1) / GB_BN, 1);
+  const int G2 = grid_for(capacity, L, GB_BM, (N2 + GB_BN - 1) / GB_BN, 1);
+  const dim3 rgrid(GB_SPLIT_UNITS / 2), blk(GB_THREADS);
+  hipLaunchKernelGGL(k_gemm_bf16<1>, dim3(G1), blk, lds, s, L, N1, H, capacity, x, offsets, w1p, act, part);
+  hipLaunchKernelGGL(k_splitk_reduce<1>, rgrid, blk, 0, s, L, N1, H, capacity, G1, offsets, part, act);
+  hipLaunchKernelGGL(k_gemm_bf16<0>, dim3(G2), blk, lds, s, L, N2, F, capacity, act, offsets, w2p, y, part);
+  hipLaunchKernelGGL(k_splitk_reduce<0>, rgrid, blk, 0, s, L, N2, F, capacity, G2, offsets, part, y);
   return hipGetLastError();
 }
 

@@ -174,7 +174,7 @@ size_t moe_grouped_mlp_workspace_bytes(int64_t capacity, int F, int dtype) {
   if (capacity <= 0 || F <= 0) return 256;
   size_t a;
   if (dtype == MOE_F32) a = (size_t)capacity * F * 4;
-  else if (dtype == MOE_BF16) a = (size_t)capacity * F * 2;
+  else if (dtype == MOE_BF16) a = round_up((size_t)capacity * F * 2, 256) + grouped_mlp_bf16_part_bytes();
   else a = round_up((size_t)capacity * F, 256) + (size_t)capacity * (F / 32);
   return round_up(a, 256);
 }
@@ -210,8 +210,9 @@ int moe_grouped_mlp(int L, int H, int F, int64_t capacity, int dtype, const void
     e = launch_grouped_mlp_f32(L, H, F, capacity, (const float*)x_perm, offsets, (const float*)w1p,
                                (const float*)w2p, (float*)workspace, (float*)y_perm, s);
   } else if (dtype == MOE_BF16) {
+    float* part = (float*)((uint8_t*)workspace + round_up((size_t)capacity * F * 2, 256));
     e = launch_grouped_mlp_bf16(L, H, F, capacity, (const bf16_t*)x_perm, offsets, (const bf16_t*)w1p,
-                                (const bf16_t*)w2p, (bf16_t*)workspace, (bf16_t*)y_perm, s);
+                                (const bf16_t*)w2p, (bf16_t*)workspace, part, (bf16_t*)y_perm, s);
   } else {
     uint8_t* act = (uint8_t*)workspace;
     uint8_t* act_s = act + round_up((size_t)capacity * F, 256);

@@ -182,9 +182,10 @@ hipError_t launch_prepare_weights(int L, int H, int F, int dtype, const void* w1
 hipError_t launch_grouped_mlp_f32(int L, int H, int F, int64_t capacity, const float* x,
                                   const int32_t* offsets, const float* w1p, const float* w2p,
                                   float* act, float* y, hipStream_t s);
+size_t grouped_mlp_bf16_part_bytes();
 hipError_t launch_grouped_mlp_bf16(int L, int H, int F, int64_t capacity, const bf16_t* x,
                                    const int32_t* offsets, const bf16_t* w1p, const bf16_t* w2p,
-                                   bf16_t* act, bf16_t* y, hipStream_t s);
+                                   bf16_t* act, float* part, bf16_t* y, hipStream_t s);
 hipError_t launch_grouped_mlp_mx(int L, int H, int F, int64_t capacity, const uint8_t* x,
                                  const uint8_t* xs, const int32_t* offsets, const uint8_t* w1p,
                                  const uint8_t* w1s, const uint8_t* w2p, const uint8_t* w2s,

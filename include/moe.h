@@ -225,8 +225,11 @@ int moe_prepare_weights(int L, int H, int F, int in_dtype, int dtype,
  * experts get no tiles.  Requires H % 128 == 0 and F % 128 == 0 for MOE_BF16
  * and MOE_MXFP8, H % 16 == 0 and F % 32 == 0 for MOE_F32.
  * Workspace: moe_grouped_mlp_workspace_bytes(capacity, F, dtype) bytes; it
- * starts with `a` ([capacity][F] in the activation type; for MXFP8 the codes
- * [capacity][F] followed by the scales [capacity][F/32]).
+ * starts with `a`: MOE_F32 [capacity][F] fp32; MOE_BF16 k-blocked
+ * [F/64][capacity][64] bf16, followed at the next 256-byte boundary by 64 MiB
+ * of fp32 split-K partial tiles (the tiles of a last, partial round of the
+ * CUs are split along the contraction and summed in a fixed order); MOE_MXFP8
+ * the codes [capacity][F] followed by the scales [capacity][F/32].
  * ------------------------------------------------------------------------ */
 size_t moe_grouped_mlp_workspace_bytes(int64_t capacity, int F, int dtype);
 

@@ -28,6 +28,9 @@ def _unblock(wp):
     return to_f64(t.reshape(rows, kd))
 
 
+MIXTRAL_COUNTS = [1011, 1049, 983, 992, 1052, 1081, 977, 1047]
+
+
 def _weights(rng, L, H, F, dt, scale=0.05):
     W1 = [rng.standard_normal((H, 2 * F)) * scale for _ in range(L)]
     W2 = [rng.standard_normal((F, H)) * scale for _ in range(L)]
@@ -148,6 +151,11 @@ def test_grouped_mlp_f32(counts, H, F):
     ([70, 300, 0, 5], 384, 128),          # partial column tiles in both GEMMs
     ([0, 0, 0, 0], 256, 256),             # no rows at all
     ([2048], 512, 512),
+    # 8192 routed rows over 8 experts on a 256-CU grid: the tiles of the last,
+    # partial round are split along k (second GEMM: 576 tiles, 64 split in 4
+    # uneven k ranges; first GEMM: 1152 tiles, 128 split in 2)
+    (MIXTRAL_COUNTS, 4096, 640),
+    (MIXTRAL_COUNTS, 512, 4096),
 ])
 def test_grouped_mlp_bf16(counts, H, F):
     _run_mlp(counts, H, F, "bf16", seed=sum(counts) + H)
