@@ -16,6 +16,7 @@ namespace moe {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 // ---------------------------------------------------------------------------
@@ -198,23 +199,33 @@ __global__ __launch_bounds__(GB_THREADS, 1) void k_gemm_bf16(int L, int N, int K
 #pragma unroll
       for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
 
-    // prologue: k step k0 into LDS buffer 0, k step k0+1 in registers
-    GB_LOAD(k0);
-    GB_STORE(0);
-    GB_LOAD(k0 + 1);
-    __syncthreads();
+    // prologue: k step k0 into LDS buffer 0, k step k0+1 in registers;
     // steady state: at step kt (kt - k0 even) LDS buffer 0 holds step kt and
     // the registers hold step kt+1
-    for (int kt = k0; kt < k1; kt += 2) {
-      GB_COMPUTE(0);
-      GB_STORE(1);
-      GB_LOAD(min(kt + 2, k1 - 1));
-      __syncthreads();
-      GB_COMPUTE(1);
-      GB_STORE(0);
-      GB_LOAD(min(kt + 3, k1 - 1));
-      __syncthreads();
+#define GB_KLOOP(C0, C1)                                                                    \
+  GB_LOAD(k0);                                                                              \
+  GB_STORE(0);                                                                              \
+  GB_LOAD(k0 + 1);                                                                          \
+  __syncthreads();                                                                          \
+  for (int kt = k0; kt < k1; kt += 2) {                                                     \
+    C0;                                                                                     \
+    GB_STORE(1);                                                                            \
+    GB_LOAD(min(kt + 2, k1 - 1));                                                           \
+    __syncthreads();                                                                        \
+    C1;                                                                                     \
+    GB_STORE(0);                                                                            \
+    GB_LOAD(min(kt + 3, k1 - 1));                                                           \
+    __syncthreads();                                                                        \
+  }
+    // in a tile of at most 128 rows (the short last tile of an expert) the
+    // second row of wavefronts has no rows: it only moves data.  The two loop
+    // versions have the same barriers.
+    if (ti.rows > 128 || wm == 0) {
+      GB_KLOOP(GB_COMPUTE(0), GB_COMPUTE(1));
+    } else {
+      GB_KLOOP(, );
     }
+#undef GB_KLOOP
 #undef GB_LOAD
 #undef GB_STORE
 #undef GB_COMPUTE
@@ -222,49 +233,59 @@ __global__ __launch_bounds__(GB_THREADS, 1) void k_gemm_bf16(int L, int N, int K
     if (piece < 0) {
       store_tile<EPI>(acc, ti, N, capacity, wm, wn, g, r32, out);
     } else {
-      // partial tile in the MFMA D layout: [wavefront][i][j][v][lane]
-      float* dst = part + (long)piece * GB_PART_FLOATS + wv * 8192 + l;
+      // partial tile, per wavefront [i][j][lane][16 values of the MFMA D layout]
+      float* dst = part + (long)piece * GB_PART_FLOATS + wv * 8192 + l * 16;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
 #pragma unroll
-          for (int v = 0; v < 16; ++v) dst[((i * 2 + j) * 16 + v) * 64] = acc[i][j][v];
+          for (int c = 0; c < 4; ++c)
+            *(f32x4*)(dst + (i * 2 + j) * 1024 + c * 4) =
+                f32x4{acc[i][j][4 * c], acc[i][j][4 * c + 1], acc[i][j][4 * c + 2], acc[i][j][4 * c + 3]};
     }
   }
 }
 
 // Sum the S split-K partials of each split tile (in piece order) and apply the
-// epilogue.  Launched with the GEMM's grid size G and GB_SPLIT_UNITS / 2
-// workgroups: split tile b of the plan is handled by workgroup b.
+// epilogue.  Launched with the GEMM's grid size G on GB_SPLIT_UNITS / 2 x 8
+// workgroups of one wavefront: workgroup (b, w) handles the part of wavefront w
+// of split tile b of the plan.
 template <int EPI>
-__global__ __launch_bounds__(GB_THREADS) void k_splitk_reduce(int L, int N, int Kd, int64_t capacity, int G,
-                                                              const int32_t* __restrict__ offsets,
-                                                              const float* __restrict__ part,
-                                                              bf16_t* __restrict__ out) {
+__global__ __launch_bounds__(64) void k_splitk_reduce(int L, int N, int Kd, int64_t capacity, int G,
+                                                      const int32_t* __restrict__ offsets,
+                                                      const float* __restrict__ part, bf16_t* __restrict__ out) {
   __shared__ int32_t s_pre[MOE_MAX_L + 1];
   __shared__ int32_t s_tmp[16];
   const int NT = (N + GB_BN - 1) / GB_BN;
   build_schedule(L, capacity, GB_BM, NT, offsets, s_pre, s_tmp);
   const int total = s_pre[L];
   const SplitPlan plan = split_plan(total, G, Kd / GB_BK);
-  const int b = blockIdx.x;
+  const int b = blockIdx.x >> 3, wv = blockIdx.x & 7, l = threadIdx.x;
   if (plan.S < 2 || b >= total - plan.dp) return;
   const TileInfo ti = locate_tile(plan.dp + b, L, capacity, GB_BM, NT, offsets, s_pre);
-  const int tid = threadIdx.x, wv = tid >> 6, l = tid & 63;
-  const float* src = part + (long)b * plan.S * GB_PART_FLOATS + wv * 8192 + l;
+  const float* src = part + (long)b * plan.S * GB_PART_FLOATS + wv * 8192 + l * 16;
+  f32x4 sum[8][4];
+#pragma unroll
+  for (int ij = 0; ij < 8; ++ij)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) sum[ij][c] = *(const f32x4*)(src + ij * 1024 + c * 4);
+  for (int q = 1; q < plan.S; ++q) {
+    const float* sq = src + (long)q * GB_PART_FLOATS;
+#pragma unroll
+    for (int ij = 0; ij < 8; ++ij)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) sum[ij][c] += *(const f32x4*)(sq + ij * 1024 + c * 4);
+  }
   f32x16 acc[4][2];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int o = ((i * 2 + j) * 16 + v) * 64;
-        float sum = src[o];
-        for (int q = 1; q < plan.S; ++q) sum += src[(long)q * GB_PART_FLOATS + o];
-        acc[i][j][v] = sum;
-      }
+      for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) acc[i][j][4 * c + t] = sum[i * 2 + j][c][t];
   store_tile<EPI>(acc, ti, N, capacity, wv >> 2, wv & 3, l >> 5, l & 31, out);
 }
 
@@ -387,11 +408,11 @@ hipError_t launch_grouped_mlp_bf16(int L, int H, int F, int64_t capacity, const 
   const int N1 = 2 * F, N2 = H;
   const int G1 = grid_for(capacity, L, GB_BM, (N1 + GB_BN - 1) / GB_BN, 1);
   const int G2 = grid_for(capacity, L, GB_BM, (N2 + GB_BN - 1) / GB_BN, 1);
-  const dim3 rgrid(GB_SPLIT_UNITS / 2), blk(GB_THREADS);
+  const dim3 rgrid(GB_SPLIT_UNITS / 2 * 8), rblk(64), blk(GB_THREADS);
   hipLaunchKernelGGL(k_gemm_bf16<1>, dim3(G1), blk, lds, s, L, N1, H, capacity, x, offsets, w1p, act, part);
-  hipLaunchKernelGGL(k_splitk_reduce<1>, rgrid, blk, 0, s, L, N1, H, capacity, G1, offsets, part, act);
+  hipLaunchKernelGGL(k_splitk_reduce<1>, rgrid, rblk, 0, s, L, N1, H, capacity, G1, offsets, part, act);
   hipLaunchKernelGGL(k_gemm_bf16<0>, dim3(G2), blk, lds, s, L, N2, F, capacity, act, offsets, w2p, y, part);
-  hipLaunchKernelGGL(k_splitk_reduce<0>, rgrid, blk, 0, s, L, N2, F, capacity, G2, offsets, part, y);
+  hipLaunchKernelGGL(k_splitk_reduce<0>, rgrid, rblk, 0, s, L, N2, F, capacity, G2, offsets, part, y);
   return hipGetLastError();
 }
 
