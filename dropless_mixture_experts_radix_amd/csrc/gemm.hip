@@ -39,7 +39,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 //
 // Work units.  With G persistent workgroups and `total` tiles, the first
 // floor(total/G)*G tiles run whole (data parallel).  The `left` tiles of a last,
-// partial round would leave most CUs idle, so when left*2 <= GB_SPLIT_UNITS
+// partial round would leave most CUs idle, so when left*2 <= GEMM_SPLIT_UNITS
 // each of them is split into S pieces along k (split-K), S as large as fits
 // the CUs and the partial buffer.  A piece writes its fp32 partial tile to
 // `part`; k_splitk_reduce then sums the S partials of a tile in piece order
@@ -54,29 +54,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 #define GB_LDK 72                   // padded LDS row (elements)
 #define GB_STAGE (GB_BM * GB_LDK)   // elements of one operand stage
 #define GB_THREADS 512
-#define GB_SPLIT_UNITS 256          // split-K pieces per launch at most
 #define GB_PART_FLOATS (GB_BM * GB_BN)
-
-struct SplitPlan {
-  int dp;     // tiles run whole: units [0, dp)
-  int S;      // pieces per split tile (1: no split)
-  int units;  // dp + (total - dp) * S
-};
-
-__device__ __forceinline__ SplitPlan split_plan(int total, int G, int KT) {
-  SplitPlan p;
-  const int left = total % G;
-  p.dp = total - left;
-  int S = left > 0 ? min(min(G, GB_SPLIT_UNITS) / left, KT / 2) : 1;
-  S = min(S, 16);
-  if (S < 2) {
-    p.dp = total;
-    S = 1;
-  }
-  p.S = S;
-  p.units = p.dp + (total - p.dp) * S;
-  return p;
-}
 
 // Epilogue of one wavefront's 128 x 64 part of a tile (MFMA D layout: lane l
 // holds column l%32, rows 8 (v/4) + 4 (l/32) + v%4 of each 32 x 32 block).
@@ -248,7 +226,7 @@ __global__ __launch_bounds__(GB_THREADS, 1) void k_gemm_bf16(int L, int N, int K
 }
 
 // Sum the S split-K partials of each split tile (in piece order) and apply the
-// epilogue.  Launched with the GEMM's grid size G on GB_SPLIT_UNITS / 2 x 8
+// epilogue.  Launched with the GEMM's grid size G on GEMM_SPLIT_UNITS / 2 x 8
 // workgroups of one wavefront: workgroup (b, w) handles the part of wavefront w
 // of split tile b of the plan.
 template <int EPI>
@@ -392,7 +370,7 @@ static size_t gemm_bf16_lds(int L) {
   return (size_t)4 * GB_STAGE * sizeof(bf16_t) + (size_t)(L + 1 + 16) * sizeof(int32_t);
 }
 
-size_t grouped_mlp_bf16_part_bytes() { return (size_t)GB_SPLIT_UNITS * GB_PART_FLOATS * sizeof(float); }
+size_t grouped_mlp_bf16_part_bytes() { return (size_t)GEMM_SPLIT_UNITS * GB_PART_FLOATS * sizeof(float); }
 
 hipError_t launch_grouped_mlp_bf16(int L, int H, int F, int64_t capacity, const bf16_t* x,
                                    const int32_t* offsets, const bf16_t* w1p, const bf16_t* w2p,
@@ -408,7 +386,7 @@ hipError_t launch_grouped_mlp_bf16(int L, int H, int F, int64_t capacity, const 
   const int N1 = 2 * F, N2 = H;
   const int G1 = grid_for(capacity, L, GB_BM, (N1 + GB_BN - 1) / GB_BN, 1);
   const int G2 = grid_for(capacity, L, GB_BM, (N2 + GB_BN - 1) / GB_BN, 1);
-  const dim3 rgrid(GB_SPLIT_UNITS / 2 * 8), rblk(64), blk(GB_THREADS);
+  const dim3 rgrid(GEMM_SPLIT_UNITS / 2 * 8), rblk(64), blk(GB_THREADS);
   hipLaunchKernelGGL(k_gemm_bf16<1>, dim3(G1), blk, lds, s, L, N1, H, capacity, x, offsets, w1p, act, part);
   hipLaunchKernelGGL(k_splitk_reduce<1>, rgrid, rblk, 0, s, L, N1, H, capacity, G1, offsets, part, act);
   hipLaunchKernelGGL(k_gemm_bf16<0>, dim3(G2), blk, lds, s, L, N2, F, capacity, act, offsets, w2p, y, part);

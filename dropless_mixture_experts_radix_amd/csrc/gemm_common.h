@@ -87,6 +87,36 @@ __device__ __forceinline__ TileInfo locate_tile(int it, int L, int64_t capacity,
   return ti;
 }
 
+// ---------------------------------------------------------------------------
+// Work units of a persistent grid of G workgroups over `total` tiles of KT k
+// steps: the first floor(total/G)*G tiles run whole; when the `left` tiles of
+// the last, partial round number at most GEMM_SPLIT_UNITS/2, each is split
+// into S >= 2 pieces along k (at most GEMM_SPLIT_UNITS pieces, at most 16 per
+// tile, each piece at least one pair of k steps).
+// ---------------------------------------------------------------------------
+#define GEMM_SPLIT_UNITS 256
+
+struct SplitPlan {
+  int dp;     // tiles run whole: units [0, dp)
+  int S;      // pieces per split tile (1: no split)
+  int units;  // dp + (total - dp) * S
+};
+
+__device__ __forceinline__ SplitPlan split_plan(int total, int G, int KT) {
+  SplitPlan p;
+  const int left = total % G;
+  p.dp = total - left;
+  int S = left > 0 ? min(min(G, GEMM_SPLIT_UNITS) / left, KT / 2) : 1;
+  S = min(S, 16);
+  if (S < 2) {
+    p.dp = total;
+    S = 1;
+  }
+  p.S = S;
+  p.units = p.dp + (total - p.dp) * S;
+  return p;
+}
+
 // XOR swizzle of the 16-byte chunks of a 128-byte LDS row: rows 0..7 get
 // distinct chunks, and rows r, r+8 (which share banks when 16 lanes are
 // served per cycle from 64 banks) differ too.

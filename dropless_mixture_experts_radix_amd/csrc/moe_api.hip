@@ -140,7 +140,7 @@ size_t moe_prepared_weight_bytes(int L, int H, int F, int dtype, int which) {
   if (L <= 0 || H <= 0 || F <= 0) return 0;
   const size_t el = dtype == MOE_F32 ? 4 : (dtype == MOE_BF16 ? 2 : 1);
   size_t n1 = (size_t)L * 2 * F * H, n2 = (size_t)L * H * F;
-  if (dtype == MOE_BF16) {  // whole 256-row panels
+  if (dtype != MOE_F32) {  // whole 256-row panels
     n1 = (size_t)L * ((2 * (size_t)F + 255) / 256 * 256) * H;
     n2 = (size_t)L * (((size_t)H + 255) / 256 * 256) * F;
   }
@@ -157,6 +157,7 @@ int moe_prepare_weights(int L, int H, int F, int in_dtype, int dtype, const void
                         void* w1p, void* w2p, uint8_t* w1p_scales, uint8_t* w2p_scales, void* stream) {
   if (L < 1 || L > MOE_MAX_L || H <= 0 || F <= 0 || H % 32 || F % 32) return MOE_ERR_SHAPE;
   if (dtype == MOE_BF16 && (H % 128 || F % 128)) return MOE_ERR_SHAPE;  // pairs of 64-wide k steps
+  if (dtype == MOE_MXFP8 && (H % 256 || F % 256)) return MOE_ERR_SHAPE;  // pairs of 128-wide k steps
   if (!((dtype == MOE_F32 && in_dtype == MOE_F32) || (dtype == MOE_BF16 && in_dtype == MOE_BF16) ||
         (dtype == MOE_MXFP8 && in_dtype == MOE_BF16)))
     return MOE_ERR_DTYPE;
@@ -175,7 +176,8 @@ size_t moe_grouped_mlp_workspace_bytes(int64_t capacity, int F, int dtype) {
   size_t a;
   if (dtype == MOE_F32) a = (size_t)capacity * F * 4;
   else if (dtype == MOE_BF16) a = round_up((size_t)capacity * F * 2, 256) + grouped_mlp_bf16_part_bytes();
-  else a = round_up((size_t)capacity * F, 256) + (size_t)capacity * (F / 32);
+  else a = round_up((size_t)capacity * F, 256) + round_up((size_t)capacity * (F / 32), 256) +
+           grouped_mlp_mx_part_bytes();
   return round_up(a, 256);
 }
 
@@ -192,7 +194,7 @@ int moe_grouped_mlp(int L, int H, int F, int64_t capacity, int dtype, const void
     // byte offsets of the activation buffers stay within 31 bits
     if (capacity * (int64_t)(H > F ? H : F) * 2 > (int64_t)INT32_MAX) return MOE_ERR_SHAPE;
   } else if (dtype == MOE_MXFP8) {
-    if (H % 128 || F % 128) return MOE_ERR_SHAPE;
+    if (H % 256 || F % 256) return MOE_ERR_SHAPE;
     if (capacity * (int64_t)(H > F ? H : F) > (int64_t)INT32_MAX) return MOE_ERR_SHAPE;
   } else {
     return MOE_ERR_DTYPE;
@@ -201,6 +203,8 @@ int moe_grouped_mlp(int L, int H, int F, int64_t capacity, int dtype, const void
   if (capacity > 0 && (!x_perm || !w1p || !w2p || !y_perm)) return MOE_ERR_NULL;
   if (dtype == MOE_MXFP8 && capacity > 0 && (!x_perm_scales || !w1p_scales || !w2p_scales)) return MOE_ERR_NULL;
   if (!aligned16(x_perm) || !aligned16(w1p) || !aligned16(w2p) || !aligned16(y_perm)) return MOE_ERR_ALIGN;
+  if (dtype == MOE_MXFP8 && (((uintptr_t)x_perm_scales | (uintptr_t)w1p_scales | (uintptr_t)w2p_scales) & 3u))
+    return MOE_ERR_ALIGN;  // scale words are read 4 bytes at a time
   if (!workspace || workspace_bytes < moe_grouped_mlp_workspace_bytes(capacity, F, dtype))
     return MOE_ERR_WORKSPACE;
   if (!aligned16(workspace)) return MOE_ERR_ALIGN;
@@ -216,9 +220,10 @@ int moe_grouped_mlp(int L, int H, int F, int64_t capacity, int dtype, const void
   } else {
     uint8_t* act = (uint8_t*)workspace;
     uint8_t* act_s = act + round_up((size_t)capacity * F, 256);
+    float* part = (float*)(act_s + round_up((size_t)capacity * (F / 32), 256));
     e = launch_grouped_mlp_mx(L, H, F, capacity, (const uint8_t*)x_perm, x_perm_scales, offsets,
                               (const uint8_t*)w1p, w1p_scales, (const uint8_t*)w2p, w2p_scales, act, act_s,
-                              (bf16_t*)y_perm, s);
+                              part, (bf16_t*)y_perm, s);
   }
   return launch_status(e);
 }

@@ -186,10 +186,11 @@ size_t grouped_mlp_bf16_part_bytes();
 hipError_t launch_grouped_mlp_bf16(int L, int H, int F, int64_t capacity, const bf16_t* x,
                                    const int32_t* offsets, const bf16_t* w1p, const bf16_t* w2p,
                                    bf16_t* act, float* part, bf16_t* y, hipStream_t s);
+size_t grouped_mlp_mx_part_bytes();
 hipError_t launch_grouped_mlp_mx(int L, int H, int F, int64_t capacity, const uint8_t* x,
                                  const uint8_t* xs, const int32_t* offsets, const uint8_t* w1p,
                                  const uint8_t* w1s, const uint8_t* w2p, const uint8_t* w2s,
-                                 uint8_t* act, uint8_t* act_s, bf16_t* y, hipStream_t s);
+                                 uint8_t* act, uint8_t* act_s, float* part, bf16_t* y, hipStream_t s);
 
 hipError_t launch_combine(int T, int K, int H, int dtype, const void* y, const int32_t* s2r,
                           const float* probs, void* out, hipStream_t s);

@@ -16,7 +16,10 @@ namespace moe {
 // MODE 1: bf16 -> bf16 in k-blocked panels: per 256-row panel and 64-wide k
 //         step one contiguous 32 KiB block [256 rows][64 k]; rows past Ncols in
 //         the last panel are zero.
-// MODE 2: bf16 -> MX E4M3 codes [Ncols][Kd] + scales [Ncols][Kd/32].
+// MODE 2: bf16 -> MX E4M3 codes and E8M0 scales in k-blocked panels: per
+//         256-row panel and 128-wide k step one contiguous 32 KiB block of codes
+//         [256 rows][128 k] and one 1 KiB block of scales [256 rows][4 blocks];
+//         rows past Ncols in the last panel are zero (codes and scales).
 template <int MODE>
 __global__ __launch_bounds__(256) void k_prepare(int Kd, int Ncols, int F_interleave,
                                                  const void* __restrict__ w, void* __restrict__ wp,
@@ -62,10 +65,12 @@ __global__ __launch_bounds__(256) void k_prepare(int Kd, int Ncols, int F_interl
       am = am > a ? am : a;
     }
     const int E = mx_scale_exp(am);
-    const long row = (long)e * Ncols + pc * 32 + pp;
-    uint8_t* dst = (uint8_t*)wp + row * Kd + k0;
+    const int NP = (Ncols + 255) / 256, KT = Kd / 128;
+    const int p = pc * 32 + pp;
+    const long blk = ((long)e * NP + (p >> 8)) * KT + (k0 >> 7);  // (expert, panel, k step)
+    uint8_t* dst = (uint8_t*)wp + blk * (256 * 128) + (p & 255) * 128 + (k0 & 127);
     for (int kk = 0; kk < 32; ++kk) dst[kk] = (uint8_t)mx_e4m3(tile[pp][kk], E);
-    ws[row * (Kd / 32) + (k0 >> 5)] = (uint8_t)(E + 127);
+    ws[blk * (256 * 4) + (p & 255) * 4 + ((k0 >> 5) & 3)] = (uint8_t)(E + 127);
   }
 }
 
@@ -83,8 +88,8 @@ hipError_t launch_prepare_weights(int L, int H, int F, int dtype, const void* w1
     hipLaunchKernelGGL(k_prepare<1>, dim3((H + 255) / 256 * 8, F / 32, L), b, 0, s, F, H, 0, w2, w2p,
                        (uint8_t*)nullptr);
   } else {
-    hipLaunchKernelGGL(k_prepare<2>, dim3(2 * F / 32, H / 32, L), b, 0, s, H, 2 * F, F, w1, w1p, w1s);
-    hipLaunchKernelGGL(k_prepare<2>, dim3(H / 32, F / 32, L), b, 0, s, F, H, 0, w2, w2p, w2s);
+    hipLaunchKernelGGL(k_prepare<2>, dim3((2 * F + 255) / 256 * 8, H / 32, L), b, 0, s, H, 2 * F, F, w1, w1p, w1s);
+    hipLaunchKernelGGL(k_prepare<2>, dim3((H + 255) / 256 * 8, F / 32, L), b, 0, s, F, H, 0, w2, w2p, w2s);
   }
   return hipGetLastError();
 }

@@ -36,14 +36,14 @@ class MoELayer:
             self.w_prep = torch.empty(nb, dtype=torch.uint8, device=dev)
             M.moe_prepare_router(w_router, x_dtype, self.w_prep)
         wdt = {M.F32: torch.float32, M.BF16: torch.bfloat16, M.MXFP8: torch.uint8}[dtype]
-        # bf16 prepared weights come in whole 256-row panels (blocked layout)
-        pad = (lambda n: (n + 255) // 256 * 256) if dtype == M.BF16 else (lambda n: n)
+        # bf16 and MXFP8 prepared weights come in whole 256-row panels (k-blocked)
+        pad = (lambda n: (n + 255) // 256 * 256) if dtype != M.F32 else (lambda n: n)
         self.w1p = torch.empty((L, pad(2 * F), H), dtype=wdt, device=dev)
         self.w2p = torch.empty((L, pad(H), F), dtype=wdt, device=dev)
         self.w1s = self.w2s = None
         if dtype == M.MXFP8:
-            self.w1s = torch.empty((L, 2 * F, H // 32), dtype=torch.uint8, device=dev)
-            self.w2s = torch.empty((L, H, F // 32), dtype=torch.uint8, device=dev)
+            self.w1s = torch.empty((L, pad(2 * F), H // 32), dtype=torch.uint8, device=dev)
+            self.w2s = torch.empty((L, pad(H), F // 32), dtype=torch.uint8, device=dev)
         # per-call buffers
         i32 = dict(dtype=torch.int32, device=dev)
         self.ids = torch.empty((T, K), dtype=torch.int16, device=dev)

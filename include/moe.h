@@ -192,10 +192,13 @@ int moe_permute(int T, int H, int K, int E_global, int e0, int L, int64_t capaci
  *   (W1p [L][ceil(2F/256)*256][H], W2p [L][ceil(H/256)*256][F]), each panel
  *   k-blocked: [panel][k/64][256 rows][64 k], so one 64-wide k step of a panel
  *   is a contiguous 32 KiB block.  Requires H % 128 == 0 and F % 128 == 0.
- * dtype MOE_MXFP8 (in_dtype MOE_BF16): W1p/W2p hold E4M3 codes (uint8) and
- *   w1p_scales [L][2F][H/32], w2p_scales [L][H][F/32] the E8M0 block scales
- *   of 32 consecutive elements along each prepared row.
- * Requires F % 32 == 0 (and H % 32 == 0, F % 32 == 0 for MXFP8).  Byte sizes:
+ * dtype MOE_MXFP8 (in_dtype MOE_BF16): E4M3 codes (uint8) of the rows above
+ *   with one E8M0 scale per 32 consecutive elements along a row, padded with
+ *   zero rows (codes and scales) to whole panels of 256 rows and k-blocked:
+ *   codes [L][panel][k/128][256 rows][128 k] (W1p: ceil(2F/256) panels over
+ *   H, W2p: ceil(H/256) panels over F), scales [L][panel][k/128][256 rows][4]
+ *   (w1p_scales, w2p_scales).  Requires H % 256 == 0 and F % 256 == 0.
+ * Requires H % 32 == 0 and F % 32 == 0 (MOE_F32).  Byte sizes:
  * moe_prepared_weight_bytes(L, H, F, dtype, which) with which = 1 (W1p),
  * 2 (W2p), 3 (W1p scales), 4 (W2p scales).
  * ------------------------------------------------------------------------ */
@@ -222,14 +225,17 @@ int moe_prepare_weights(int L, int H, int F, int in_dtype, int dtype,
  * MOE_MXFP8: x_perm as E4M3 codes + x_perm_scales (from moe_permute), `a`
  *   rounded to bf16 and then MX-quantized along F, y_perm bf16.
  * The schedule of output tiles is built on the device from `offsets`: empty
- * experts get no tiles.  Requires H % 128 == 0 and F % 128 == 0 for MOE_BF16
- * and MOE_MXFP8, H % 16 == 0 and F % 32 == 0 for MOE_F32.
+ * experts get no tiles.  Requires H % 128 == 0 and F % 128 == 0 for MOE_BF16,
+ * H % 256 == 0 and F % 256 == 0 for MOE_MXFP8 (scale pointers 4-byte
+ * aligned), H % 16 == 0 and F % 32 == 0 for MOE_F32.
  * Workspace: moe_grouped_mlp_workspace_bytes(capacity, F, dtype) bytes; it
  * starts with `a`: MOE_F32 [capacity][F] fp32; MOE_BF16 k-blocked
  * [F/64][capacity][64] bf16, followed at the next 256-byte boundary by 64 MiB
  * of fp32 split-K partial tiles (the tiles of a last, partial round of the
  * CUs are split along the contraction and summed in a fixed order); MOE_MXFP8
- * the codes [capacity][F] followed by the scales [capacity][F/32].
+ * the codes [capacity][F], then at the next 256-byte boundary the scales
+ * [capacity][F/32], then at the next 256-byte boundary 64 MiB of split-K
+ * partial tiles.
  * ------------------------------------------------------------------------ */
 size_t moe_grouped_mlp_workspace_bytes(int64_t capacity, int F, int dtype);
 

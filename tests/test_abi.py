@@ -93,8 +93,8 @@ def test_mlp_validation():
 
     assert call(H=96) == 2               # bf16 needs H % 128 == 0
     assert call(H=192) == 2
-    assert call(dt=2, F=192) == 2        # MXFP8 needs F % 128 == 0
-    assert call(dt=2) == 1               # MX scales missing
+    assert call(dt=2, F=384) == 2        # MXFP8 needs F % 256 == 0
+    assert call(dt=2, H=256, F=256) == 1  # MX scales missing
     assert call(dt=9) == 4
     assert call(offs=None) == 1
     assert call(wsb=100) == 5
@@ -111,8 +111,9 @@ def test_other_validation():
     assert lib.moe_mx_quantize(4, 48, P, None, P, P, None) == 2
     assert lib.moe_mx_quantize(4, 64, None, None, P, P, None) == 1
     assert lib.moe_prepare_weights(2, 64, 48, 1, 1, P, P, P, P, None, None, None) == 2   # F % 32
-    assert lib.moe_prepare_weights(2, 64, 64, 0, 2, P, P, P, P, P, P, None) == 4         # MX from fp32
-    assert lib.moe_prepare_weights(2, 64, 64, 1, 2, P, P, P, P, None, P, None) == 1
+    assert lib.moe_prepare_weights(2, 256, 256, 0, 2, P, P, P, P, P, P, None) == 4       # MX from fp32
+    assert lib.moe_prepare_weights(2, 256, 384, 1, 2, P, P, P, P, P, P, None) == 2       # MX needs F % 256
+    assert lib.moe_prepare_weights(2, 256, 256, 1, 2, P, P, P, P, None, P, None) == 1
     assert lib.moe_prepare_router(P, 1, 0, 64, 8, P, None) == 4                          # bf16 W_r, fp32 x
     assert lib.moe_prepare_router(None, 0, 1, 64, 8, P, None) == 1
 

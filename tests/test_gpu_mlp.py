@@ -28,6 +28,16 @@ def _unblock(wp):
     return to_f64(t.reshape(rows, kd))
 
 
+def _unblock_mx(wp, ws):
+    """MXFP8 prepared weights of one expert, k-blocked panels: codes
+    [rows/256][Kd/128][256][128] and scales [rows/256][Kd/128][256][4], back to
+    row-major codes [rows][Kd] and scales [rows][Kd/32] (numpy uint8)."""
+    rows, kd = wp.shape
+    c = np_of(wp).reshape(rows // 256, kd // 128, 256, 128).transpose(0, 2, 1, 3).reshape(rows, kd)
+    s = np_of(ws).reshape(rows // 256, kd // 128, 256, 4).transpose(0, 2, 1, 3).reshape(rows, kd // 32)
+    return c, s
+
+
 MIXTRAL_COUNTS = [1011, 1049, 983, 992, 1052, 1081, 977, 1047]
 
 
@@ -62,13 +72,13 @@ def _run_mlp(counts, H, F, dt, seed=0, xscale=1.0, check_layout=True):
     w1 = torch.stack([_dev(w, dt) for w in W1])
     w2 = torch.stack([_dev(w, dt) for w in W2])
     wdt = {"f32": torch.float32, "bf16": torch.bfloat16, "mxfp8": torch.uint8}[dt]
-    pad = (lambda n: (n + 255) // 256 * 256) if dt == "bf16" else (lambda n: n)
+    pad = (lambda n: (n + 255) // 256 * 256) if dt != "f32" else (lambda n: n)
     w1p = torch.empty((L, pad(2 * F), H), dtype=wdt, device=DEV)
     w2p = torch.empty((L, pad(H), F), dtype=wdt, device=DEV)
     w1s = w2s = None
     if dt == "mxfp8":
-        w1s = torch.empty((L, 2 * F, H // 32), dtype=torch.uint8, device=DEV)
-        w2s = torch.empty((L, H, F // 32), dtype=torch.uint8, device=DEV)
+        w1s = torch.empty((L, pad(2 * F), H // 32), dtype=torch.uint8, device=DEV)
+        w2s = torch.empty((L, pad(H), F // 32), dtype=torch.uint8, device=DEV)
     D.moe_prepare_weights(w1, w2, code, w1p, w2p, w1s, w2s)
     perm = _interleave_rows(F)
     if check_layout:
@@ -76,10 +86,14 @@ def _run_mlp(counts, H, F, dt, seed=0, xscale=1.0, check_layout=True):
         if dt == "mxfp8":
             c1, s1 = O.mx_quantize_rows(W1[e].T[perm])
             c2, s2 = O.mx_quantize_rows(W2[e].T)
-            np.testing.assert_array_equal(np_of(w1p[e]), c1)
-            np.testing.assert_array_equal(np_of(w1s[e]), s1)
-            np.testing.assert_array_equal(np_of(w2p[e]), c2)
-            np.testing.assert_array_equal(np_of(w2s[e]), s2)
+            w1c, w1sc = _unblock_mx(w1p[e], w1s[e])
+            w2c, w2sc = _unblock_mx(w2p[e], w2s[e])
+            np.testing.assert_array_equal(w1c[: 2 * F], c1)
+            np.testing.assert_array_equal(w1sc[: 2 * F], s1)
+            np.testing.assert_array_equal(w2c[:H], c2)
+            np.testing.assert_array_equal(w2sc[:H], s2)
+            assert (w1c[2 * F:] == 0).all() and (w1sc[2 * F:] == 0).all()
+            assert (w2c[H:] == 0).all() and (w2sc[H:] == 0).all()
         elif dt == "bf16":
             np.testing.assert_array_equal(_unblock(w1p[e])[: 2 * F], W1[e].T[perm])
             np.testing.assert_array_equal(_unblock(w2p[e])[:H], W2[e].T)
@@ -164,7 +178,11 @@ def test_grouped_mlp_bf16(counts, H, F):
 @pytest.mark.parametrize("counts,H,F", [
     ([0, 1, 255, 256, 257, 600, 0, 31], 256, 512),
     ([900, 24, 0, 513], 1024, 1536),
-    ([70, 300, 0, 5], 384, 384),
+    ([70, 300, 0, 5], 768, 256),          # partial column tiles in both GEMMs
+    ([0, 0, 0, 0], 256, 256),             # no rows at all
+    # the tiles of a last, partial round split along k (as in the bf16 cases)
+    (MIXTRAL_COUNTS, 4096, 768),
+    (MIXTRAL_COUNTS, 512, 4096),
 ])
 def test_grouped_mlp_mxfp8(counts, H, F):
     _run_mlp(counts, H, F, "mxfp8", seed=sum(counts) + H)
