@@ -114,38 +114,24 @@ __device__ __forceinline__ int mx_scale_exp(uint32_t amax_abs_bits) {
   return e < -127 ? -127 : (e > 127 ? 127 : e);
 }
 
+__device__ __forceinline__ float mx_scaled(uint32_t b, int E) {
+  // bf16 value times 2^-E, clamped to the largest E4M3 magnitude (448): the
+  // power-of-two scaling is exact (results below 2^-126 all become zero codes)
+  const float y = __builtin_amdgcn_ldexpf(__uint_as_float(b << 16), -E);
+  return fminf(fmaxf(y, -448.0f), 448.0f);
+}
+// E4M3 code of bf16 value b (bits) under block scale 2^E: round to nearest
+// even, saturate at 448, keep the sign of zero.  The hardware conversion does
+// the rounding; it agrees bit for bit with a step-by-step integer conversion
+// of the OCP rules for every finite bf16 pattern and every E in [-127, 127].
 __device__ __forceinline__ uint32_t mx_e4m3(uint32_t b, int E) {
-  const uint32_t s = (b >> 15) & 1u;
-  const uint32_t a = b & 0x7fffu;
-  const uint32_t ef = a >> 7;
-  uint32_t M;
-  int x;  // |v| = M * 2^x
-  if (ef) { M = 128u | (a & 127u); x = (int)ef - 134; }
-  else { M = a & 127u; x = -133; }
-  if (M == 0) return s << 7;
-  const int msb = 31 - __clz(M);
-  const int fl = msb + x - E;               // floor(log2 |v * 2^-E|)
-  int qe = (fl > -6 ? fl : -6) - 3;         // exponent of the E4M3 spacing there
-  const int sh = qe - (x - E);              // M is divided by 2^sh
-  uint32_t n;
-  if (sh <= 0) {
-    n = M << (-sh);
-  } else if (sh > 9) {
-    n = 0;
-  } else {
-    const uint32_t q = M >> sh, rem = M & ((1u << sh) - 1u), half = 1u << (sh - 1);
-    n = q + ((rem > half) || (rem == half && (q & 1u)) ? 1u : 0u);
-  }
-  if (n >= 16) { n >>= 1; qe += 1; }
-  uint32_t code;
-  if (n >= 8) {
-    const int field = qe + 10;
-    const uint32_t mant = n - 8;
-    code = (field > 15 || (field == 15 && mant == 7)) ? 0x7eu : (((uint32_t)field << 3) | mant);
-  } else {
-    code = n;
-  }
-  return (s << 7) | code;
+  const float y = mx_scaled(b, E);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y, y, 0, false) & 0xffu;
+}
+// four codes (bytes 0..3) of the bf16 pairs p0 = (e0 | e1 << 16), p1 = (e2 | e3 << 16)
+__device__ __forceinline__ uint32_t mx_e4m3x4(uint32_t p0, uint32_t p1, int E) {
+  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(mx_scaled(p0 & 0xffffu, E), mx_scaled(p0 >> 16, E), 0, false);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(mx_scaled(p1 & 0xffffu, E), mx_scaled(p1 >> 16, E), lo, true);
 }
 
 // ---------------------------------------------------------------------------

@@ -205,53 +205,59 @@ __global__ __launch_bounds__(256) void k_permute(int T, int K, int e0, int L, in
       if (p0 + j < npiece && off < row_bytes) v[j] = *(const u32x4*)(src + off);
       else v[j] = u32x4{0, 0, 0, 0};
     }
-    uint64_t b = bits;
-    while (b) {
-      const int k = __builtin_ctzll(b);
-      b &= b - 1;
-      const int d = readlane_i(dest, k);
-      if (p0 == 0 && l == 0) row_to_slot[d] = t * K + k;
-      if (OUT == 0) {
+    if (OUT == 0) {
+      uint64_t b = bits;
+      while (b) {
+        const int k = __builtin_ctzll(b);
+        b &= b - 1;
+        const int d = readlane_i(dest, k);
+        if (p0 == 0 && l == 0) row_to_slot[d] = t * K + k;
         uint8_t* dst = x_perm + (long)d * row_bytes;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           const int off = (p0 + j) * 1024 + l * 16;
           if (p0 + j < npiece && off < row_bytes) *(u32x4*)(dst + off) = v[j];
         }
-      } else {
-        // bf16 row of H = row_bytes/2 elements -> codes [H] + scales [H/32]
-        const int H = row_bytes >> 1;
+      }
+    } else {
+      // quantize the pieces once: the 8 bf16 of a lane -> 8 codes; 4 lanes
+      // share a 32-element block and its scale
+      uint32_t lo[8], hi[8], sc[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        uint32_t am = 0;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const uint32_t a0 = v[j][q] & 0x7fffu, a1 = (v[j][q] >> 16) & 0x7fffu;
+          am = am > a0 ? am : a0;
+          am = am > a1 ? am : a1;
+        }
+        uint32_t o = (uint32_t)__shfl_xor((int)am, 1, 64);
+        am = am > o ? am : o;
+        o = (uint32_t)__shfl_xor((int)am, 2, 64);
+        am = am > o ? am : o;
+        const int E = mx_scale_exp(am);
+        lo[j] = mx_e4m3x4(v[j][0], v[j][1], E);
+        hi[j] = mx_e4m3x4(v[j][2], v[j][3], E);
+        sc[j] = (uint32_t)(E + 127);
+      }
+      // bf16 row of H = row_bytes/2 elements -> codes [H] + scales [H/32]
+      const int H = row_bytes >> 1;
+      uint64_t b = bits;
+      while (b) {
+        const int k = __builtin_ctzll(b);
+        b &= b - 1;
+        const int d = readlane_i(dest, k);
+        if (p0 == 0 && l == 0) row_to_slot[d] = t * K + k;
         uint8_t* dst = x_perm + (long)d * H;
         uint8_t* dsc = x_scales + (long)d * (H >> 5);
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           const int off = (p0 + j) * 1024 + l * 16;  // byte offset in the bf16 row
-          const bool in = p0 + j < npiece && off < row_bytes;
-          // 4 lanes share a 32-element block
-          uint32_t am = 0;
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const uint32_t a0 = v[j][q] & 0x7fffu, a1 = (v[j][q] >> 16) & 0x7fffu;
-            am = am > a0 ? am : a0;
-            am = am > a1 ? am : a1;
-          }
-          uint32_t o = (uint32_t)__shfl_xor((int)am, 1, 64);
-          am = am > o ? am : o;
-          o = (uint32_t)__shfl_xor((int)am, 2, 64);
-          am = am > o ? am : o;
-          const int E = mx_scale_exp(am);
-          uint32_t lo = 0, hi = 0;
-#pragma unroll
-          for (int q = 0; q < 2; ++q) {
-            lo |= mx_e4m3(v[j][q] & 0xffffu, E) << (16 * q);
-            lo |= mx_e4m3(v[j][q] >> 16, E) << (16 * q + 8);
-            hi |= mx_e4m3(v[j][2 + q] & 0xffffu, E) << (16 * q);
-            hi |= mx_e4m3(v[j][2 + q] >> 16, E) << (16 * q + 8);
-          }
-          if (in) {
+          if (p0 + j < npiece && off < row_bytes) {
             const int e_off = off >> 1;  // element offset
-            *(uint2*)(dst + e_off) = make_uint2(lo, hi);
-            if ((l & 3) == 0) dsc[e_off >> 5] = (uint8_t)(E + 127);
+            *(uint2*)(dst + e_off) = make_uint2(lo[j], hi[j]);
+            if ((l & 3) == 0) dsc[e_off >> 5] = (uint8_t)sc[j];
           }
         }
       }

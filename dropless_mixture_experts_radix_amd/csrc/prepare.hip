@@ -126,8 +126,7 @@ __global__ __launch_bounds__(256) void k_mx_quantize(int64_t rows, int cols, con
     uint32_t out[8];
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
-      out[q] = mx_e4m3(v[2 * q] & 0xffffu, E) | (mx_e4m3(v[2 * q] >> 16, E) << 8) |
-               (mx_e4m3(v[2 * q + 1] & 0xffffu, E) << 16) | (mx_e4m3(v[2 * q + 1] >> 16, E) << 24);
+      out[q] = mx_e4m3x4(v[2 * q], v[2 * q + 1], E);
     }
     uint4* dst = (uint4*)(codes + r * cols + b * 32);
     dst[0] = make_uint4(out[0], out[1], out[2], out[3]);
