@@ -20,68 +20,108 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 // ---------------------------------------------------------------------------
-// bf16 grouped GEMM: out tile 256 x 256, k step 64, 512 threads = 8 wavefronts
-// as 2 (rows) x 4 (columns), each wavefront 128 x 64 = 4 x 2 tiles of
-// v_mfma_f32_32x32x16_bf16; two wavefronts per SIMD hide each other's waits.
+// bf16 grouped GEMM: out tile 256 x 256, k step 32, 512 threads = 8 wavefronts
+// as 2 (rows) x 4 (columns), two per SIMD, each wavefront 128 x 64 = 4 x 2
+// tiles of v_mfma_f32_32x32x16_bf16.
 //
-// The L2 -> CU path (about 64 B/clk per CU) is the scarce resource of this
-// loop, so every operand byte of a tile crosses it once per k step: each thread
-// moves the same four 16-byte chunks of the A and of the B k-step tile
-// (64 KiB per k step) into registers one k step ahead, then into padded LDS
-// rows (144 bytes: 16 consecutive rows start in 16 different bank groups), and
-// the wavefronts read their MFMA fragments from LDS.  A is [rows][Kd] (EPI 1:
-// x_perm) or k-blocked [Kd/64][capacity][64] (EPI 0: the activations); B is the
-// prepared weight panel of 256 output columns, k-blocked [Kd/64][256][64], so a
-// k-step tile of B is one contiguous 32 KiB block.  Both are read with buffer
-// loads, which return zeros past the tile's rows.  Prefetch indices are clamped
-// to the last k step of the range instead of branching, and k ranges have even
-// length so k steps come in pairs: the k loop has no branches.
+// What bounds this loop on gfx950 is how many operand bytes are in flight
+// between global memory and LDS: a k step of a 256 x 256 tile needs 32 KiB,
+// and under the load of all CUs the latency of a global read is of the order
+// of a microsecond, several k steps.  So the tiles go straight from global
+// memory into LDS (buffer loads with the LDS destination, no registers), into
+// a ring of 4 LDS stages filled three k steps ahead.  Two wavefronts share
+// each SIMD, so while one waits for its loads to be accepted or for a barrier
+// the other keeps the matrix core busy.  A wavefront tile of 128 x 64 reads
+// 12 KiB of MFMA fragments per k step from LDS for its 16 MFMAs.
+//
+// Pipeline of k step kt (stage kt % 4), 2 sub-steps of k = 16:
+//   read the fragments of sub-step 1; MFMAs of sub-step 0 and the first 2 of
+//   sub-step 1; wait until this wavefront's loads of step kt+1 have landed and
+//   its fragment reads are done; barrier (step kt+1 is complete in LDS for
+//   every wavefront, and stage kt % 4 is free); read the fragments of step
+//   kt+1, sub-step 0; load step kt+4 into stage kt % 4, interleaved with the
+//   remaining 6 MFMAs.
+//
+// LDS layout: stage s at s * 32 KiB, A rows then B rows (256 each, 64 bytes:
+// 32 k values); a 1 KiB block holds 16 rows and is written by one load
+// instruction (lane i -> bytes 16i..16i+15), and the 16-byte chunk c of row r
+// sits at chunk position c ^ swz4(r), so the 8 (or 16) lanes served together
+// by a fragment read hit distinct banks.  A is [rows][Kd] (EPI 1: x_perm) or
+// k-blocked [Kd/32][capacity][32] (EPI 0: the activations); B is the prepared
+// weight panel of 256 output columns, k-blocked [Kd/32][256][32], so a k step
+// of B is one contiguous 16 KiB block.  Buffer loads return zeros past the
+// tile's rows.  Prefetch indices are clamped to the last k step of the range.
 //
 // Work units.  With G persistent workgroups and `total` tiles, the first
 // floor(total/G)*G tiles run whole (data parallel).  The `left` tiles of a last,
 // partial round would leave most CUs idle, so when left*2 <= GEMM_SPLIT_UNITS
 // each of them is split into S pieces along k (split-K), S as large as fits
-// the CUs and the partial buffer.  A piece writes its fp32 partial tile to
-// `part`; k_splitk_reduce then sums the S partials of a tile in piece order
-// (the result does not depend on timing) and applies the epilogue.
+// the CUs and the partial buffer, each piece a whole number of 4-step groups.
+// A piece writes its fp32 partial tile to `part`; k_splitk_reduce then sums the
+// S partials of a tile in piece order (the result does not depend on timing)
+// and applies the epilogue.
 // EPI 0: out[row][col] = bf16(acc)                                   (N columns)
 // EPI 1: gate/up chunks of 32 columns are interleaved in B; out = k-blocked
-//        activations [N/128][capacity][64], a[row][j] = bf16(silu(gate) * up)
+//        activations [N/64][capacity][32], a[row][j] = bf16(silu(gate) * up)
 // ---------------------------------------------------------------------------
 #define GB_BM 256
 #define GB_BN 256
-#define GB_BK 64
-#define GB_LDK 72                   // padded LDS row (elements)
-#define GB_STAGE (GB_BM * GB_LDK)   // elements of one operand stage
+#define GB_BK 32
 #define GB_THREADS 512
+#define GB_STAGE_BYTES 32768        // A and B k-step tiles of one stage
 #define GB_PART_FLOATS (GB_BM * GB_BN)
 
-// Epilogue of one wavefront's 128 x 64 part of a tile (MFMA D layout: lane l
-// holds column l%32, rows 8 (v/4) + 4 (l/32) + v%4 of each 32 x 32 block).
-template <int EPI>
-__device__ __forceinline__ void store_tile(const f32x16 (&acc)[4][2], const TileInfo& ti, int N, int64_t capacity,
-                                           int wm, int wn, int g, int r32, bf16_t* __restrict__ out) {
+// chunk position swizzle of a 64-byte row in its 16-row block
+__device__ __forceinline__ int swz4(int r) {
+  return (((r >> 1) ^ (r >> 3)) & 1) | ((((r >> 2) ^ (r >> 3)) & 1) << 1);
+}
+
+// 16 bytes per lane from buffer `rsrc` at voff + soff into LDS at
+// lds_addr + 16 * lane.  Issued as inline assembly so that the compiler does
+// not wait for it at every LDS read and barrier; its completion is awaited
+// explicitly (vmcnt, in issue order) before the barrier that publishes it.
+__device__ __forceinline__ void lds_dma_b128(uint32_t lds_addr, int voff, __amdgpu_buffer_rsrc_t rsrc, int soff) {
+  // s_nop 4: the wait states after an SALU write of M0 (1) and after a VALU
+  // write of an SGPR that a VMEM instruction reads (5)
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 4\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :
+               : "s"(lds_addr), "v"(voff), "s"(rsrc), "s"(soff)
+               : "memory", "m0");
+}
+
+// split plan of the bf16 kernel: pieces are whole groups of 4 k steps
+__device__ __forceinline__ SplitPlan gb_split_plan(int total, int G, int Kd) {
+  return split_plan(total, G, Kd / 64);
+}
+
+// Epilogue of rows [i0, i0+NI) x 32 of one wavefront's 128 x 64 part of a
+// tile (MFMA D layout: lane l holds column l%32, rows 8 (v/4) + 4 (l/32) + v%4
+// of each 32 x 32 block).
+template <int EPI, int NI>
+__device__ __forceinline__ void store_tile(const f32x16 (&acc)[NI][2], int i0, const TileInfo& ti, int N,
+                                           int64_t capacity, int wm, int wn, int g, int r32,
+                                           bf16_t* __restrict__ out) {
   const int col0 = ti.nt * GB_BN;
-  const int msub = min(4, max(0, (ti.rows - wm * 128 + 31) / 32));
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    if (i >= msub) continue;
+  for (int ii = 0; ii < NI; ++ii) {
+    const int rb = wm * 128 + (i0 + ii) * 32;
+    if (rb >= ti.rows) continue;
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
-      const int row = wm * 128 + i * 32 + 8 * (v >> 2) + 4 * g + (v & 3);
+      const int row = rb + 8 * (v >> 2) + 4 * g + (v & 3);
       if (row >= ti.rows) continue;
       const long grow = ti.row0 + row;
       if (EPI == 0) {
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
           const int col = col0 + wn * 64 + j * 32 + r32;
-          if (col < N) out[grow * N + col] = (bf16_t)f32_to_bf16(acc[i][j][v]);
+          if (col < N) out[grow * N + col] = (bf16_t)f32_to_bf16(acc[ii][j][v]);
         }
       } else {
         const int jcol = (col0 >> 1) + wn * 32 + r32;
         if (jcol < (N >> 1))
-          out[((long)(jcol >> 6) * capacity + grow) * GB_BK + (jcol & 63)] =
-              (bf16_t)f32_to_bf16(silu_mul(acc[i][0][v], acc[i][1][v]));
+          out[((long)(jcol >> 5) * capacity + grow) * GB_BK + (jcol & 31)] =
+              (bf16_t)f32_to_bf16(silu_mul(acc[ii][0][v], acc[ii][1][v]));
       }
     }
   }
@@ -94,38 +134,37 @@ __global__ __launch_bounds__(GB_THREADS, 1) void k_gemm_bf16(int L, int N, int K
                                                              const bf16_t* __restrict__ B, bf16_t* __restrict__ out,
                                                              float* __restrict__ part) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  bf16_t* sA = (bf16_t*)smem;                         // [2][256][72]
-  bf16_t* sB = sA + 2 * GB_STAGE;                     // [2][256][72]
-  int32_t* s_pre = (int32_t*)(sB + 2 * GB_STAGE);     // [L+1]
-  int32_t* s_tmp = s_pre + (L + 1);                   // [16]
+  int32_t* s_pre = (int32_t*)(smem + 4 * GB_STAGE_BYTES);  // [L+1]
+  int32_t* s_tmp = s_pre + (L + 1);                         // [8]
   const int NT = (N + GB_BN - 1) / GB_BN;
   build_schedule(L, capacity, GB_BM, NT, offsets, s_pre, s_tmp);
   const int KT = Kd / GB_BK;
-  const SplitPlan plan = split_plan(s_pre[L], gridDim.x, KT);
-  const int tid = threadIdx.x, wv = tid >> 6, l = tid & 63;
+  const SplitPlan plan = gb_split_plan(s_pre[L], gridDim.x, Kd);
+  const int tid = threadIdx.x, l = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wv >> 2, wn = wv & 3;
   const int g = l >> 5, r32 = l & 31;
-  // global -> LDS: thread moves 16-byte chunk lkc of rows lrow + 64 i (i < 4)
-  // of both the A and the B k-step tile
-  const int lrow = tid >> 3, lkc = tid & 7;
-  const int st_off = lrow * GB_LDK + lkc * 8;
-  // fragment reads: A row wm*128 + i*32 + r32, B column wn*64 + jj*32 + r32,
-  // k chunk 2s + g of the k step
-  const int fa_base = (wm * 128 + r32) * GB_LDK + g * 8;
-  const int fb_base = (wn * 64 + r32) * GB_LDK + g * 8;
-  const int vb = (lrow * GB_BK + lkc * 8) * 2;
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)smem;
+  // loads: wavefront wv fills rows [32 wv, 32 wv + 32) of the A and of the B
+  // tile of a stage, 2 blocks of 16 rows each; lane l moves row 16q + l/4,
+  // chunk (l%4) ^ swz4(l/4) of block q
+  const int drow = l >> 2, dch = (l & 3) ^ swz4(drow);
+  // fragment reads: A row wm*128 + i*32 + r32, B column wn*128 + j*32 + r32,
+  // chunk 2s + g of the k step (sub-step s)
+  const int fr0 = r32 * 64 + ((g ^ swz4(r32)) << 4);
+  const int fr1 = r32 * 64 + (((2 + g) ^ swz4(r32)) << 4);
 
   for (int u = virtual_block(); u < plan.units; u += gridDim.x) {
     int tile = u, k0 = 0, k1 = KT, piece = -1;
-    if (u >= plan.dp) {  // split-K piece: k steps [k0, k1), an even count
+    if (u >= plan.dp) {  // split-K piece: k steps [k0, k1), whole groups of 4
       piece = u - plan.dp;
       tile = plan.dp + piece / plan.S;
-      const int q = piece % plan.S, half = KT / 2;
-      k0 = 2 * (q * half / plan.S);
-      k1 = 2 * ((q + 1) * half / plan.S);
+      const int q = piece % plan.S, nq = KT / 4;
+      k0 = 4 * (q * nq / plan.S);
+      k1 = 4 * ((q + 1) * nq / plan.S);
     }
     const TileInfo ti = locate_tile(tile, L, capacity, GB_BM, NT, offsets, s_pre);
-    // the (expert, panel) B tile: KT blocks of [256 columns][64 k]
+    // the (expert, panel) B tile: KT blocks of [256 columns][32 k]
     const __amdgpu_buffer_rsrc_t rB = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(B + ((long)ti.e * NT + ti.nt) * (long)KT * GB_BN * GB_BK), (short)0,
         KT * GB_BN * GB_BK * 2, 0x00020000);
@@ -133,83 +172,89 @@ __global__ __launch_bounds__(GB_THREADS, 1) void k_gemm_bf16(int L, int N, int K
         EPI == 1 ? __builtin_amdgcn_make_buffer_rsrc((void*)(A + (long)ti.row0 * Kd), (short)0, ti.rows * Kd * 2,
                                                      0x00020000)
                  : __builtin_amdgcn_make_buffer_rsrc((void*)A, (short)0, (int)(KT * capacity * GB_BK * 2), 0x00020000);
-    const int va = EPI == 1 ? (lrow * Kd + lkc * 8) * 2 : ((ti.row0 + lrow) * GB_BK + lkc * 8) * 2;
-    const int astride = EPI == 1 ? 64 * Kd * 2 : 64 * GB_BK * 2;
+    // per-lane byte offsets of the 4 A and the 4 B blocks of a wavefront; the
+    // k step enters through the scalar offset
+    int va[2], vb[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int r = wv * 32 + q * 16 + drow;
+      va[q] = EPI == 1 ? (r * Kd + dch * 8) * 2 : ((ti.row0 + r) * GB_BK + dch * 8) * 2;
+      vb[q] = r * 64 + dch * 16;
+    }
     const int akstep = EPI == 1 ? GB_BK * 2 : (int)(capacity * GB_BK * 2);
 
-    u32x4 ast[4], bst[4];  // register stage of the next k step
-#define GB_LOAD(KT_)                                                                        \
+#define GB_DMA(ST, KT_, Q)                                                                  \
   {                                                                                         \
-    const int koa = va + (KT_) * akstep;                                                    \
-    const int kob = (KT_) * (GB_BN * GB_BK * 2);                                            \
-    _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                         \
-      ast[i] = __builtin_amdgcn_raw_buffer_load_b128(rA, koa + i * astride, 0, 0);          \
-      bst[i] = __builtin_amdgcn_raw_buffer_load_b128(rB, vb + i * (64 * GB_BK * 2), kob, 0); \
-    }                                                                                       \
+    const int kq = (KT_);                                                                   \
+    if ((Q) < 2)                                                                            \
+      lds_dma_b128(lds0 + (ST) * GB_STAGE_BYTES + (wv * 2 + (Q)) * 1024, va[Q], rA, kq * akstep); \
+    else                                                                                    \
+      lds_dma_b128(lds0 + (ST) * GB_STAGE_BYTES + 16384 + (wv * 2 + (Q) - 2) * 1024, vb[(Q) - 2], rB, \
+                   kq * (GB_BN * GB_BK * 2));                                               \
   }
-#define GB_STORE(BUF)                                                                       \
+#define GB_READ(FA, FB, ST, FR)                                                             \
   {                                                                                         \
-    bf16_t* dA = sA + (BUF) * GB_STAGE + st_off;                                            \
-    bf16_t* dB = sB + (BUF) * GB_STAGE + st_off;                                            \
-    _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                         \
-      *(u32x4*)(dA + i * 64 * GB_LDK) = ast[i];                                             \
-      *(u32x4*)(dB + i * 64 * GB_LDK) = bst[i];                                             \
-    }                                                                                       \
+    const uint8_t* pa = smem + (ST) * GB_STAGE_BYTES + wm * 8192 + (FR);                    \
+    const uint8_t* pb = smem + (ST) * GB_STAGE_BYTES + 16384 + wn * 4096 + (FR);            \
+    _Pragma("unroll") for (int i = 0; i < 4; ++i) FA[i] = *(const bf16x8*)(pa + i * 2048); \
+    _Pragma("unroll") for (int j = 0; j < 2; ++j) FB[j] = *(const bf16x8*)(pb + j * 2048); \
   }
-#define GB_COMPUTE(BUF)                                                                     \
-  {                                                                                         \
-    const bf16_t* cA = sA + (BUF) * GB_STAGE + fa_base;                                     \
-    const bf16_t* cB = sB + (BUF) * GB_STAGE + fb_base;                                     \
-    _Pragma("unroll") for (int s = 0; s < 4; ++s) {                                         \
-      bf16x8 fa[4], fb[2];                                                                  \
-      _Pragma("unroll") for (int jj = 0; jj < 2; ++jj)                                      \
-        fb[jj] = *(const bf16x8*)(cB + jj * 32 * GB_LDK + s * 16);                          \
-      _Pragma("unroll") for (int i = 0; i < 4; ++i)                                         \
-        fa[i] = *(const bf16x8*)(cA + i * 32 * GB_LDK + s * 16);                            \
-      _Pragma("unroll") for (int i = 0; i < 4; ++i)                                         \
-        _Pragma("unroll") for (int jj = 0; jj < 2; ++jj)                                    \
-          acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[jj], acc[i][jj], 0, 0, 0); \
-    }                                                                                       \
-  }
+#define GB_MMA1(FA, FB, T)                                                                  \
+  acc[(T) >> 1][(T) & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(FA[(T) >> 1], FB[(T) & 1], acc[(T) >> 1][(T) & 1], 0, 0, 0);
+#define GB_FENCE __builtin_amdgcn_sched_barrier(0);
+
+    bf16x8 fa0[4], fb0[2], fa1[4], fb1[2];
     f32x16 acc[4][2];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
 
-    // prologue: k step k0 into LDS buffer 0, k step k0+1 in registers;
-    // steady state: at step kt (kt - k0 even) LDS buffer 0 holds step kt and
-    // the registers hold step kt+1
-#define GB_KLOOP(C0, C1)                                                                    \
-  GB_LOAD(k0);                                                                              \
-  GB_STORE(0);                                                                              \
-  GB_LOAD(k0 + 1);                                                                          \
-  __syncthreads();                                                                          \
-  for (int kt = k0; kt < k1; kt += 2) {                                                     \
-    C0;                                                                                     \
-    GB_STORE(1);                                                                            \
-    GB_LOAD(min(kt + 2, k1 - 1));                                                           \
-    __syncthreads();                                                                        \
-    C1;                                                                                     \
-    GB_STORE(0);                                                                            \
-    GB_LOAD(min(kt + 3, k1 - 1));                                                           \
-    __syncthreads();                                                                        \
-  }
-    // in a tile of at most 128 rows (the short last tile of an expert) the
-    // second row of wavefronts has no rows: it only moves data.  The two loop
-    // versions have the same barriers.
-    if (ti.rows > 128 || wm == 0) {
-      GB_KLOOP(GB_COMPUTE(0), GB_COMPUTE(1));
-    } else {
-      GB_KLOOP(, );
+    // prologue: steps k0 .. k0+3 into stages 0..3, wait for step k0, read the
+    // fragments of its sub-step 0
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) GB_DMA(st, min(k0 + st, k1 - 1), q);
     }
-#undef GB_KLOOP
-#undef GB_LOAD
-#undef GB_STORE
-#undef GB_COMPUTE
+    asm volatile("s_waitcnt vmcnt(12)\n\ts_barrier" ::: "memory");
+    GB_READ(fa0, fb0, 0, fr0);
+    GB_FENCE;
+    for (int kt = k0; kt < k1; kt += 4) {
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        // step kt + h in stage h; fa0/fb0 hold its sub-step 0 fragments
+        GB_READ(fa1, fb1, h, fr1);
+        GB_FENCE;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) { GB_MMA1(fa0, fb0, t); }
+#pragma unroll
+        for (int t = 0; t < 2; ++t) { GB_MMA1(fa1, fb1, t); }
+        GB_FENCE;
+        asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        GB_FENCE;
+        GB_READ(fa0, fb0, (h + 1) & 3, fr0);
+        GB_FENCE;
+        const int kn = min(kt + h + 4, k1 - 1);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          GB_DMA(h, kn, q);
+          GB_FENCE;
+          if (q < 3) {
+            GB_MMA1(fa1, fb1, 2 + 2 * q);
+            GB_MMA1(fa1, fb1, 3 + 2 * q);
+            GB_FENCE;
+          }
+        }
+      }
+    }
+#undef GB_DMA
+#undef GB_READ
+#undef GB_MMA1
+#undef GB_FENCE
 
     if (piece < 0) {
-      store_tile<EPI>(acc, ti, N, capacity, wm, wn, g, r32, out);
+      store_tile<EPI, 4>(acc, 0, ti, N, capacity, wm, wn, g, r32, out);
     } else {
       // partial tile, per wavefront [i][j][lane][16 values of the MFMA D layout]
       float* dst = part + (long)piece * GB_PART_FLOATS + wv * 8192 + l * 16;
@@ -223,12 +268,14 @@ __global__ __launch_bounds__(GB_THREADS, 1) void k_gemm_bf16(int L, int N, int K
                 f32x4{acc[i][j][4 * c], acc[i][j][4 * c + 1], acc[i][j][4 * c + 2], acc[i][j][4 * c + 3]};
     }
   }
+  // the last prefetches of the ring (clamped repeats) land before the exit
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
 // Sum the S split-K partials of each split tile (in piece order) and apply the
 // epilogue.  Launched with the GEMM's grid size G on GEMM_SPLIT_UNITS / 2 x 8
-// workgroups of one wavefront: workgroup (b, w) handles the part of wavefront w
-// of split tile b of the plan.
+// workgroups of one wavefront: workgroup (b, w) handles the part of wavefront
+// w of split tile b of the plan.
 template <int EPI>
 __global__ __launch_bounds__(64) void k_splitk_reduce(int L, int N, int Kd, int64_t capacity, int G,
                                                       const int32_t* __restrict__ offsets,
@@ -238,7 +285,7 @@ __global__ __launch_bounds__(64) void k_splitk_reduce(int L, int N, int Kd, int6
   const int NT = (N + GB_BN - 1) / GB_BN;
   build_schedule(L, capacity, GB_BM, NT, offsets, s_pre, s_tmp);
   const int total = s_pre[L];
-  const SplitPlan plan = split_plan(total, G, Kd / GB_BK);
+  const SplitPlan plan = gb_split_plan(total, G, Kd);
   const int b = blockIdx.x >> 3, wv = blockIdx.x & 7, l = threadIdx.x;
   if (plan.S < 2 || b >= total - plan.dp) return;
   const TileInfo ti = locate_tile(plan.dp + b, L, capacity, GB_BM, NT, offsets, s_pre);
@@ -264,7 +311,7 @@ __global__ __launch_bounds__(64) void k_splitk_reduce(int L, int N, int Kd, int6
       for (int c = 0; c < 4; ++c)
 #pragma unroll
         for (int t = 0; t < 4; ++t) acc[i][j][4 * c + t] = sum[i * 2 + j][c][t];
-  store_tile<EPI>(acc, ti, N, capacity, wv >> 2, wv & 3, l >> 5, l & 31, out);
+  store_tile<EPI, 4>(acc, 0, ti, N, capacity, wv >> 2, wv & 3, l >> 5, l & 31, out);
 }
 
 // ---------------------------------------------------------------------------
@@ -367,7 +414,7 @@ hipError_t launch_grouped_mlp_f32(int L, int H, int F, int64_t capacity, const f
 }
 
 static size_t gemm_bf16_lds(int L) {
-  return (size_t)4 * GB_STAGE * sizeof(bf16_t) + (size_t)(L + 1 + 16) * sizeof(int32_t);
+  return (size_t)4 * GB_STAGE_BYTES + (size_t)(L + 1 + 16) * sizeof(int32_t);
 }
 
 size_t grouped_mlp_bf16_part_bytes() { return (size_t)GEMM_SPLIT_UNITS * GB_PART_FLOATS * sizeof(float); }

@@ -6,15 +6,15 @@
 // chunks of 32 interleaved, c(p) = (p/64)*32 + p%32 + ((p/32)%2 ? F : 0);
 // W2 row n = column n of W2[e].  Rows run along the contraction dimension; the
 // bf16 layout is additionally blocked so the grouped GEMM streams contiguous
-// 32 KiB pieces.
+// 16 KiB pieces.
 #include "moe_internal.h"
 
 namespace moe {
 
 // One 32 x 32 tile of one expert: logical W [Kd][Ncols] -> prepared rows.
 // MODE 0: fp32 -> fp32, row-major [Ncols][Kd].
-// MODE 1: bf16 -> bf16 in k-blocked panels: per 256-row panel and 64-wide k
-//         step one contiguous 32 KiB block [256 rows][64 k]; rows past Ncols in
+// MODE 1: bf16 -> bf16 in k-blocked panels: per 256-row panel and 32-wide k
+//         step one contiguous 16 KiB block [256 rows][32 k]; rows past Ncols in
 //         the last panel are zero.
 // MODE 2: bf16 -> MX E4M3 codes and E8M0 scales in k-blocked panels: per
 //         256-row panel and 128-wide k step one contiguous 32 KiB block of codes
@@ -49,12 +49,12 @@ __global__ __launch_bounds__(256) void k_prepare(int Kd, int Ncols, int F_interl
       ((float*)wp)[out_off + (long)(pc * 32 + pp) * Kd + k0 + kk] = __uint_as_float(tile[pp][kk]);
     }
   } else if (MODE == 1) {
-    const int NP = (Ncols + 255) / 256, KT = Kd / 64;
+    const int NP = (Ncols + 255) / 256, KT = Kd / 32;
     const long out_off = (long)e * NP * 256 * Kd;
     for (int i = tid; i < 1024; i += 256) {
       const int pp = i >> 5, kk = i & 31;
       const int p = pc * 32 + pp, k = k0 + kk;
-      const long o = out_off + ((long)(p >> 8) * KT + (k >> 6)) * (256 * 64) + (p & 255) * 64 + (k & 63);
+      const long o = out_off + ((long)(p >> 8) * KT + (k >> 5)) * (256 * 32) + (p & 255) * 32 + (k & 31);
       ((bf16_t*)wp)[o] = (bf16_t)tile[pp][kk];
     }
   } else if (tid < 32) {

@@ -78,8 +78,8 @@ class MoELayer:
         cap, F = self.capacity, self.F
         if self.dtype == M.F32:
             return self.mlp_ws[: cap * F * 4].view(torch.float32).view(cap, F)
-        if self.dtype == M.BF16:  # k-blocked [F/64][capacity][64]
-            blk = self.mlp_ws[: cap * F * 2].view(torch.bfloat16).view(F // 64, cap, 64)
+        if self.dtype == M.BF16:  # k-blocked [F/32][capacity][32]
+            blk = self.mlp_ws[: cap * F * 2].view(torch.bfloat16).view(F // 32, cap, 32)
             return blk.permute(1, 0, 2).reshape(cap, F)
         codes = self.mlp_ws[: cap * F].view(cap, F)
         off = (cap * F + 255) // 256 * 256

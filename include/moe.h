@@ -190,8 +190,8 @@ int moe_permute(int T, int H, int K, int E_global, int e0, int L, int64_t capaci
  * dtype MOE_F32: values in fp32, rows exactly as above.
  * dtype MOE_BF16: the rows above padded with zero rows to whole panels of 256
  *   (W1p [L][ceil(2F/256)*256][H], W2p [L][ceil(H/256)*256][F]), each panel
- *   k-blocked: [panel][k/64][256 rows][64 k], so one 64-wide k step of a panel
- *   is a contiguous 32 KiB block.  Requires H % 128 == 0 and F % 128 == 0.
+ *   k-blocked: [panel][k/32][256 rows][32 k], so one 32-wide k step of a panel
+ *   is a contiguous 16 KiB block.  Requires H % 128 == 0 and F % 128 == 0.
  * dtype MOE_MXFP8 (in_dtype MOE_BF16): E4M3 codes (uint8) of the rows above
  *   with one E8M0 scale per 32 consecutive elements along a row, padded with
  *   zero rows (codes and scales) to whole panels of 256 rows and k-blocked:
@@ -230,7 +230,7 @@ int moe_prepare_weights(int L, int H, int F, int in_dtype, int dtype,
  * aligned), H % 16 == 0 and F % 32 == 0 for MOE_F32.
  * Workspace: moe_grouped_mlp_workspace_bytes(capacity, F, dtype) bytes; it
  * starts with `a`: MOE_F32 [capacity][F] fp32; MOE_BF16 k-blocked
- * [F/64][capacity][64] bf16, followed at the next 256-byte boundary by 64 MiB
+ * [F/32][capacity][32] bf16, followed at the next 256-byte boundary by 64 MiB
  * of fp32 split-K partial tiles (the tiles of a last, partial round of the
  * CUs are split along the contraction and summed in a fixed order); MOE_MXFP8
  * the codes [capacity][F], then at the next 256-byte boundary the scales

@@ -21,10 +21,10 @@ def _interleave_rows(F):
 
 
 def _unblock(wp):
-    """bf16 prepared weights of one expert, k-blocked panels [rows/256][Kd/64][256][64],
+    """bf16 prepared weights of one expert, k-blocked panels [rows/256][Kd/32][256][32],
     back to rows x Kd (float64)."""
     rows, kd = wp.shape
-    t = wp.reshape(rows // 256, kd // 64, 256, 64).permute(0, 2, 1, 3)   # panel, r, kt, e
+    t = wp.reshape(rows // 256, kd // 32, 256, 32).permute(0, 2, 1, 3)   # panel, r, kt, e
     return to_f64(t.reshape(rows, kd))
 
 
@@ -124,8 +124,8 @@ def _run_mlp(counts, H, F, dt, seed=0, xscale=1.0, check_layout=True):
         if dt == "f32":
             a = ws[: cap * F * 4].view(torch.float32).view(cap, F)
             assert rel_inf(to_f64(a)[:N], want_a) <= TOL[dt]
-        elif dt == "bf16":  # k-blocked activations [F/64][cap][64]
-            a = ws[: cap * F * 2].view(torch.bfloat16).view(F // 64, cap, 64).permute(1, 0, 2).reshape(cap, F)
+        elif dt == "bf16":  # k-blocked activations [F/32][cap][32]
+            a = ws[: cap * F * 2].view(torch.bfloat16).view(F // 32, cap, 32).permute(1, 0, 2).reshape(cap, F)
             assert rel_inf(to_f64(a)[:N], want_a) <= TOL[dt]
         else:
             codes = np_of(ws[: cap * F].view(cap, F))[:N]
