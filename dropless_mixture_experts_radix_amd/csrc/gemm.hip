@@ -143,6 +143,7 @@ __global__ __launch_bounds__(GB_THREADS, 1) void k_gemm_bf16(int L, int N, int K
   const int tid = threadIdx.x, l = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wv >> 2, wn = wv & 3;
+  const int gp = wm;  // group: wavefronts 0-3 and 4-7, one of each per SIMD
   const int g = l >> 5, r32 = l & 31;
   const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)smem;
   // loads: wavefront wv fills rows [32 wv, 32 wv + 32) of the A and of the B
@@ -203,51 +204,61 @@ __global__ __launch_bounds__(GB_THREADS, 1) void k_gemm_bf16(int L, int N, int K
   acc[(T) >> 1][(T) & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(FA[(T) >> 1], FB[(T) & 1], acc[(T) >> 1][(T) & 1], 0, 0, 0);
 #define GB_FENCE __builtin_amdgcn_sched_barrier(0);
 
-    bf16x8 fa0[4], fb0[2], fa1[4], fb1[2];
+    bf16x8 fa[2][4], fb[2][2];  // fragments of both sub-steps of one k step
     f32x16 acc[4][2];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
 
-    // prologue: steps k0 .. k0+3 into stages 0..3, wait for step k0, read the
-    // fragments of its sub-step 0
+    // prologue: steps k0 .. k0+2 into stages 0..2, wait for step k0
 #pragma unroll
-    for (int st = 0; st < 4; ++st) {
+    for (int st = 0; st < 3; ++st) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) GB_DMA(st, min(k0 + st, k1 - 1), q);
     }
-    asm volatile("s_waitcnt vmcnt(12)\n\ts_barrier" ::: "memory");
-    GB_READ(fa0, fb0, 0, fr0);
-    GB_FENCE;
-    for (int kt = k0; kt < k1; kt += 4) {
-#pragma unroll
-      for (int h = 0; h < 4; ++h) {
-        // step kt + h in stage h; fa0/fb0 hold its sub-step 0 fragments
-        GB_READ(fa1, fb1, h, fr1);
-        GB_FENCE;
-#pragma unroll
-        for (int t = 0; t < 8; ++t) { GB_MMA1(fa0, fb0, t); }
-#pragma unroll
-        for (int t = 0; t < 2; ++t) { GB_MMA1(fa1, fb1, t); }
-        GB_FENCE;
-        asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-        GB_FENCE;
-        GB_READ(fa0, fb0, (h + 1) & 3, fr0);
-        GB_FENCE;
-        const int kn = min(kt + h + 4, k1 - 1);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          GB_DMA(h, kn, q);
-          GB_FENCE;
-          if (q < 3) {
-            GB_MMA1(fa1, fb1, 2 + 2 * q);
-            GB_MMA1(fa1, fb1, 3 + 2 * q);
-            GB_FENCE;
-          }
-        }
-      }
+    asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");
+    // the second group of wavefronts runs one phase behind the first
+    if (gp) asm volatile("s_barrier" ::: "memory");
+    // Phases, each ended by a barrier of all 8 wavefronts:
+    //   memory phase of step kt: read both sub-steps' fragments from stage
+    //     kt % 4, load step kt+3 into stage (kt+3) % 4 (read by both groups
+    //     in steps kt-1 .. , free since the barrier before this phase), then
+    //     wait for the reads and for this wavefront's loads of step kt+1;
+    //   compute phase of step kt: its 16 MFMAs back to back.
+    // Group 0 computes step kt while group 1 reads step kt; group 1 computes
+    // step kt while group 0 reads step kt+1.  The stage of step kt+1 is complete
+    // for all wavefronts at the barrier that starts group 0's memory phase of
+    // step kt+1.
+#define GB_KLOOP(MM)                                                                        \
+  for (int kt = k0; kt < k1; kt += 4) {                                                     \
+    _Pragma("unroll") for (int h = 0; h < 4; ++h) {                                         \
+      GB_READ(fa[0], fb[0], h, fr0);                                                        \
+      GB_READ(fa[1], fb[1], h, fr1);                                                        \
+      {                                                                                     \
+        const int kn = min(kt + h + 3, k1 - 1);                                             \
+        _Pragma("unroll") for (int q = 0; q < 4; ++q) GB_DMA((h + 3) & 3, kn, q);          \
+      }                                                                                     \
+      asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory");              \
+      GB_FENCE;                                                                             \
+      if (MM) {                                                                             \
+        _Pragma("unroll") for (int t = 0; t < 8; ++t) { GB_MMA1(fa[0], fb[0], t); }         \
+        _Pragma("unroll") for (int t = 0; t < 8; ++t) { GB_MMA1(fa[1], fb[1], t); }         \
+      }                                                                                     \
+      GB_FENCE;                                                                             \
+      asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");                          \
+    }                                                                                       \
+  }
+    // in a tile of at most 128 rows (the short last tile of an expert) the
+    // second group has no rows: it only reads and loads, and its compute
+    // phases are empty.  Both loop versions have the same loads and barriers.
+    if (ti.rows > wm * 128) {
+      GB_KLOOP(1);
+    } else {
+      GB_KLOOP(0);
     }
+#undef GB_KLOOP
+    if (!gp) asm volatile("s_barrier" ::: "memory");
 #undef GB_DMA
 #undef GB_READ
 #undef GB_MMA1
