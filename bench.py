@@ -113,6 +113,51 @@ def time_graph(layer, x, reps):
     return t0.elapsed_time(t1) / reps * 1000.0
 
 
+def calibration_copy(nbytes=512 << 20):
+    """One device-to-device copy of a known size (read nbytes, write nbytes).
+    Under rocprofv3 --pmc its FETCH_SIZE / WRITE_SIZE give the factor that turns
+    those counters into bytes for the kernels of the same run."""
+    src = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+    torch.cuda.empty_cache()
+
+
+GEMM_SOURCES = ["dropless_mixture_experts_radix_amd/csrc/gemm.hip", "dropless_mixture_experts_radix_amd/csrc/gemm_common.h"]
+TRAFFIC_FILE = "profiles/mixtral_bf16_grouped_mlp_traffic.txt"
+
+
+def gemm_source_sha():
+    import hashlib
+    h = hashlib.sha256()
+    for f in GEMM_SOURCES:
+        with open(os.path.join(os.path.dirname(os.path.abspath(__file__)), f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per moe_grouped_mlp call (FETCH_SIZE + WRITE_SIZE, scaled by the
+    calibration copy) from the committed counter summary, or None when the
+    grouped GEMM sources changed since the counters were taken."""
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), TRAFFIC_FILE)
+    try:
+        kv = {}
+        with open(path) as fh:
+            for ln in fh:
+                if "=" in ln and not ln.lstrip().startswith("#"):
+                    k, v = ln.split("=", 1)
+                    kv[k.strip()] = v.strip()
+        if kv.get("source_sha256") != gemm_source_sha():
+            return None
+        return int(float(kv["hbm_bytes_per_call"]))
+    except (OSError, KeyError, ValueError):
+        return None
+
+
 def algorithmic(cfg, N):
     T, H, E, K, F = cfg.T, cfg.H, cfg.E, cfg.K, cfg.F
     bx = 2
@@ -178,6 +223,7 @@ def main():
         print(f"bench.py measures one GPU only; --gpus {a.gpus} is not supported (this build has no multi-GPU "
               f"path)", file=sys.stderr)
         sys.exit(2)
+    calibration_copy()
     cfg, layer, x, r = build("mixtral_bf16")
     layer.forward(x)
     torch.cuda.synchronize()
@@ -211,9 +257,11 @@ def main():
         "route_gbs": round(route_b / (t_route * 1e-6) / 1e9, 1),
         "permute_gbs": round(permute_b / (t_perm * 1e-6) / 1e9, 1),
         "combine_gbs": round(combine_b / (t_comb * 1e-6) / 1e9, 1),
-        "roofline": {"kernel": "moe_grouped_mlp: k_gemm_bf16<1> (GEMM1+SwiGLU) + k_gemm_bf16<0> (GEMM2)",
+        "roofline": {"kernel": "moe_grouped_mlp: k_gemm_bf16<1> (GEMM1+SwiGLU) + k_gemm_bf16<0> (GEMM2) "
+                               "+ k_splitk_reduce<1,0>",
                      "bound": "mfma", "achieved": round(tflops, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(tflops / BF16_PEAK_TFLOPS, 4), "traffic": None},
+                     "frac": round(tflops / BF16_PEAK_TFLOPS, 4), "traffic": measured_traffic(),
+                     "traffic_unit": "HBM bytes per launch", "algorithmic_flops_per_launch": flops},
     }
     if not a.no_mx:
         try:
