@@ -19,8 +19,13 @@ namespace moe {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
+// Tokens per count tile: about T*K/256 slots per tile (at least 64, at most
+// 512), so that small-K layers still spread the counting over many CUs.
 int permute_tile_tokens(int T, int K) {
-  int tt = 512 / (K > 0 ? K : 1);
+  if (K < 1) K = 1;
+  long slots = (long)T * K / 256;
+  slots = slots < 64 ? 64 : (slots > 512 ? 512 : slots);
+  int tt = (int)(slots / K);
   if (tt < 1) tt = 1;
   return tt;
 }

@@ -112,6 +112,8 @@ __global__ __launch_bounds__(256) void k_router_proj_bf16(int T, int E, int H, i
     const bf16_t* pa = x + (long)ra * H + (long)s * Hc + 32 * g;
     const bf16_t* pb = x + (long)rb * H + (long)s * Hc + 32 * g;
     const bf16_t* pw = wp + (long)(ct * 32 + r) * H + (long)s * Hc + 32 * g;
+    // unrolled so that the loads of several k steps are in flight together
+#pragma unroll 4
     for (int k0 = 0; k0 < Hc; k0 += 64) {
       bf16x8 a0[4], a1[4], b[4];
 #pragma unroll
@@ -197,7 +199,7 @@ __device__ __forceinline__ float score_of(float z, float zmax, int score) {
 // Small-E path (E <= 32): one thread per token, keys in registers, each key's
 // output position is its rank (number of keys that beat it).
 template <int EMAX>
-__global__ __launch_bounds__(256) void k_route_select_small(int T, int E, int K, int S, int score,
+__global__ __launch_bounds__(64) void k_route_select_small(int T, int E, int K, int S, int score,
                                                             const float* __restrict__ partial,
                                                             const float* __restrict__ bias,
                                                             const uint8_t* __restrict__ mask,
@@ -209,10 +211,30 @@ __global__ __launch_bounds__(256) void k_route_select_small(int T, int E, int K,
   uint32_t key[EMAX];
   bool bad = false;
 #pragma unroll
+  for (int e = 0; e < EMAX; ++e) z[e] = 0.f;
+  // the S partial sets in order; a token's E logits of one set are contiguous
+  if ((E & 3) == 0) {
+    for (int s = 0; s < S; ++s) {
+      const float4* ps = (const float4*)(partial + ((long)s * T + t) * E);
+#pragma unroll
+      for (int c = 0; c < EMAX / 4; ++c) {
+        if (4 * c < E) {
+          const float4 q = ps[c];
+          z[4 * c] += q.x; z[4 * c + 1] += q.y; z[4 * c + 2] += q.z; z[4 * c + 3] += q.w;
+        }
+      }
+    }
+  } else {
+    for (int s = 0; s < S; ++s) {
+#pragma unroll
+      for (int e = 0; e < EMAX; ++e)
+        if (e < E) z[e] += partial[((long)s * T + t) * E + e];
+    }
+  }
+#pragma unroll
   for (int e = 0; e < EMAX; ++e) {
-    float v = 0.f;
+    float v = z[e];
     if (e < E) {
-      for (int s = 0; s < S; ++s) v += partial[((long)s * T + t) * E + e];
       if (logits_out) logits_out[(long)t * E + e] = v;
       if (bias) v += bias[e];
     }
@@ -462,7 +484,7 @@ hipError_t launch_route_select(int T, int E, int K, int S, int score, const floa
                                float* logits_out, int32_t* err, hipStream_t s) {
   if (T == 0) return hipSuccess;
   if (E <= 32) {
-    const dim3 g((T + 255) / 256), b(256);
+    const dim3 g((T + 63) / 64), b(64);  // one thread per token, many small workgroups
     if (E <= 8)
       hipLaunchKernelGGL(k_route_select_small<8>, g, b, 0, s, T, E, K, S, score, partial, bias, mask, ids,
                          probs, logits_out, err);
