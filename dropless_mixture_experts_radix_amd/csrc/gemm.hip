@@ -155,43 +155,62 @@ __global__ __launch_bounds__(GB_THREADS, 1) void k_gemm_bf16(int L, int N, int K
   const int fr0 = r32 * 64 + ((g ^ swz4(r32)) << 4);
   const int fr1 = r32 * 64 + (((2 + g) ^ swz4(r32)) << 4);
 
-  for (int u = virtual_block(); u < plan.units; u += gridDim.x) {
-    int tile = u, k0 = 0, k1 = KT, piece = -1;
-    if (u >= plan.dp) {  // split-K piece: k steps [k0, k1), whole groups of 4
-      piece = u - plan.dp;
-      tile = plan.dp + piece / plan.S;
-      const int q = piece % plan.S, nq = KT / 4;
-      k0 = 4 * (q * nq / plan.S);
-      k1 = 4 * ((q + 1) * nq / plan.S);
-    }
-    const TileInfo ti = locate_tile(tile, L, capacity, GB_BM, NT, offsets, s_pre);
-    // the (expert, panel) B tile: KT blocks of [256 columns][32 k]
-    const __amdgpu_buffer_rsrc_t rB = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(B + ((long)ti.e * NT + ti.nt) * (long)KT * GB_BN * GB_BK), (short)0,
-        KT * GB_BN * GB_BK * 2, 0x00020000);
-    const __amdgpu_buffer_rsrc_t rA =
-        EPI == 1 ? __builtin_amdgcn_make_buffer_rsrc((void*)(A + (long)ti.row0 * Kd), (short)0, ti.rows * Kd * 2,
-                                                     0x00020000)
-                 : __builtin_amdgcn_make_buffer_rsrc((void*)A, (short)0, (int)(KT * capacity * GB_BK * 2), 0x00020000);
-    // per-lane byte offsets of the 4 A and the 4 B blocks of a wavefront; the
-    // k step enters through the scalar offset
+  // one work unit: a whole tile or a split-K piece of one
+  struct Unit {
+    TileInfo ti;
+    int piece, k0, k1, akstep;
+    __amdgpu_buffer_rsrc_t rA, rB;
     int va[2], vb[2];
+  };
+  auto setup = [&](int u) {
+    Unit w;
+    int tile = u;
+    w.piece = -1;
+    w.k0 = 0;
+    w.k1 = KT;
+    if (u >= plan.dp) {  // split-K piece: k steps [k0, k1), whole groups of 4
+      w.piece = u - plan.dp;
+      tile = plan.dp + w.piece / plan.S;
+      const int q = w.piece % plan.S, nq = KT / 4;
+      w.k0 = 4 * (q * nq / plan.S);
+      w.k1 = 4 * ((q + 1) * nq / plan.S);
+    }
+    w.ti = locate_tile(tile, L, capacity, GB_BM, NT, offsets, s_pre);
+    // the (expert, panel) B tile: KT blocks of [256 columns][32 k]
+    w.rB = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(B + ((long)w.ti.e * NT + w.ti.nt) * (long)KT * GB_BN * GB_BK), (short)0,
+        KT * GB_BN * GB_BK * 2, 0x00020000);
+    w.rA = EPI == 1 ? __builtin_amdgcn_make_buffer_rsrc((void*)(A + (long)w.ti.row0 * Kd), (short)0,
+                                                        w.ti.rows * Kd * 2, 0x00020000)
+                    : __builtin_amdgcn_make_buffer_rsrc((void*)A, (short)0, (int)(KT * capacity * GB_BK * 2),
+                                                        0x00020000);
+    // per-lane byte offsets of the 2 A and the 2 B blocks of a wavefront; the
+    // k step enters through the scalar offset
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
       const int r = wv * 32 + q * 16 + drow;
-      va[q] = EPI == 1 ? (r * Kd + dch * 8) * 2 : ((ti.row0 + r) * GB_BK + dch * 8) * 2;
-      vb[q] = r * 64 + dch * 16;
+      w.va[q] = EPI == 1 ? (r * Kd + dch * 8) * 2 : ((w.ti.row0 + r) * GB_BK + dch * 8) * 2;
+      w.vb[q] = r * 64 + dch * 16;
     }
-    const int akstep = EPI == 1 ? GB_BK * 2 : (int)(capacity * GB_BK * 2);
+    w.akstep = EPI == 1 ? GB_BK * 2 : (int)(capacity * GB_BK * 2);
+    return w;
+  };
 
-#define GB_DMA(ST, KT_, Q)                                                                  \
+#define GB_DMA(W, ST, KT_, Q)                                                               \
   {                                                                                         \
     const int kq = (KT_);                                                                   \
     if ((Q) < 2)                                                                            \
-      lds_dma_b128(lds0 + (ST) * GB_STAGE_BYTES + (wv * 2 + (Q)) * 1024, va[Q], rA, kq * akstep); \
+      lds_dma_b128(lds0 + (ST) * GB_STAGE_BYTES + (wv * 2 + (Q)) * 1024, (W).va[Q], (W).rA, kq * (W).akstep); \
     else                                                                                    \
-      lds_dma_b128(lds0 + (ST) * GB_STAGE_BYTES + 16384 + (wv * 2 + (Q) - 2) * 1024, vb[(Q) - 2], rB, \
+      lds_dma_b128(lds0 + (ST) * GB_STAGE_BYTES + 16384 + (wv * 2 + (Q) - 2) * 1024, (W).vb[(Q) - 2], (W).rB, \
                    kq * (GB_BN * GB_BK * 2));                                               \
+  }
+// the ring prologue of a unit: its steps k0 .. k0+2 into stages 0..2
+#define GB_PROLOGUE(W)                                                                      \
+  {                                                                                         \
+    _Pragma("unroll") for (int st = 0; st < 3; ++st) {                                      \
+      _Pragma("unroll") for (int q = 0; q < 4; ++q) GB_DMA(W, st, min((W).k0 + st, (W).k1 - 1), q); \
+    }                                                                                       \
   }
 #define GB_READ(FA, FB, ST, FR)                                                             \
   {                                                                                         \
@@ -204,27 +223,31 @@ __global__ __launch_bounds__(GB_THREADS, 1) void k_gemm_bf16(int L, int N, int K
   acc[(T) >> 1][(T) & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(FA[(T) >> 1], FB[(T) & 1], acc[(T) >> 1][(T) & 1], 0, 0, 0);
 #define GB_FENCE __builtin_amdgcn_sched_barrier(0);
 
+  int u = virtual_block();
+  Unit cu;
+  if (u < plan.units) {
+    cu = setup(u);
+    GB_PROLOGUE(cu);
+  }
+  while (u < plan.units) {
+    const int k0 = cu.k0, k1 = cu.k1;
     bf16x8 fa[2][4], fb[2][2];  // fragments of both sub-steps of one k step
     f32x16 acc[4][2];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
-
-    // prologue: steps k0 .. k0+2 into stages 0..2, wait for step k0
-#pragma unroll
-    for (int st = 0; st < 3; ++st) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) GB_DMA(st, min(k0 + st, k1 - 1), q);
-    }
+    // wait for step k0 (the younger steps k0+1, k0+2 may still be loading;
+    // loads complete in issue order, and the previous unit's epilogue stores
+    // were issued after them)
     asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");
     // the second group of wavefronts runs one phase behind the first
     if (gp) asm volatile("s_barrier" ::: "memory");
     // Phases, each ended by a barrier of all 8 wavefronts:
     //   memory phase of step kt: read both sub-steps' fragments from stage
     //     kt % 4, load step kt+3 into stage (kt+3) % 4 (read by both groups
-    //     in steps kt-1 .. , free since the barrier before this phase), then
-    //     wait for the reads and for this wavefront's loads of step kt+1;
+    //     in step kt-1, free since the barrier before this phase), then wait
+    //     for the reads and for this wavefront's loads of step kt+1;
     //   compute phase of step kt: its 16 MFMAs back to back.
     // Group 0 computes step kt while group 1 reads step kt; group 1 computes
     // step kt while group 0 reads step kt+1.  The stage of step kt+1 is complete
@@ -237,7 +260,7 @@ __global__ __launch_bounds__(GB_THREADS, 1) void k_gemm_bf16(int L, int N, int K
       GB_READ(fa[1], fb[1], h, fr1);                                                        \
       {                                                                                     \
         const int kn = min(kt + h + 3, k1 - 1);                                             \
-        _Pragma("unroll") for (int q = 0; q < 4; ++q) GB_DMA((h + 3) & 3, kn, q);          \
+        _Pragma("unroll") for (int q = 0; q < 4; ++q) GB_DMA(cu, (h + 3) & 3, kn, q);      \
       }                                                                                     \
       asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory");              \
       GB_FENCE;                                                                             \
@@ -252,23 +275,26 @@ __global__ __launch_bounds__(GB_THREADS, 1) void k_gemm_bf16(int L, int N, int K
     // in a tile of at most 128 rows (the short last tile of an expert) the
     // second group has no rows: it only reads and loads, and its compute
     // phases are empty.  Both loop versions have the same loads and barriers.
-    if (ti.rows > wm * 128) {
+    if (cu.ti.rows > wm * 128) {
       GB_KLOOP(1);
     } else {
       GB_KLOOP(0);
     }
 #undef GB_KLOOP
     if (!gp) asm volatile("s_barrier" ::: "memory");
-#undef GB_DMA
-#undef GB_READ
-#undef GB_MMA1
-#undef GB_FENCE
-
-    if (piece < 0) {
-      store_tile<EPI, 4>(acc, 0, ti, N, capacity, wm, wn, g, r32, out);
+    // every wavefront is past its last fragment read of this unit: start the
+    // ring of the next unit, then store this one while those loads travel
+    const Unit done = cu;
+    u += gridDim.x;
+    if (u < plan.units) {
+      cu = setup(u);
+      GB_PROLOGUE(cu);
+    }
+    if (done.piece < 0) {
+      store_tile<EPI, 4>(acc, 0, done.ti, N, capacity, wm, wn, g, r32, out);
     } else {
       // partial tile, per wavefront [i][j][lane][16 values of the MFMA D layout]
-      float* dst = part + (long)piece * GB_PART_FLOATS + wv * 8192 + l * 16;
+      float* dst = part + (long)done.piece * GB_PART_FLOATS + wv * 8192 + l * 16;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -279,6 +305,11 @@ __global__ __launch_bounds__(GB_THREADS, 1) void k_gemm_bf16(int L, int N, int K
                 f32x4{acc[i][j][4 * c], acc[i][j][4 * c + 1], acc[i][j][4 * c + 2], acc[i][j][4 * c + 3]};
     }
   }
+#undef GB_DMA
+#undef GB_PROLOGUE
+#undef GB_READ
+#undef GB_MMA1
+#undef GB_FENCE
   // the last prefetches of the ring (clamped repeats) land before the exit
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
