@@ -71,24 +71,6 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 #define GB_STAGE_BYTES 32768        // A and B k-step tiles of one stage
 #define GB_PART_FLOATS (GB_BM * GB_BN)
 
-// chunk position swizzle of a 64-byte row in its 16-row block
-__device__ __forceinline__ int swz4(int r) {
-  return (((r >> 1) ^ (r >> 3)) & 1) | ((((r >> 2) ^ (r >> 3)) & 1) << 1);
-}
-
-// 16 bytes per lane from buffer `rsrc` at voff + soff into LDS at
-// lds_addr + 16 * lane.  Issued as inline assembly so that the compiler does
-// not wait for it at every LDS read and barrier; its completion is awaited
-// explicitly (vmcnt, in issue order) before the barrier that publishes it.
-__device__ __forceinline__ void lds_dma_b128(uint32_t lds_addr, int voff, __amdgpu_buffer_rsrc_t rsrc, int soff) {
-  // s_nop 4: the wait states after an SALU write of M0 (1) and after a VALU
-  // write of an SGPR that a VMEM instruction reads (5)
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 4\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-               :
-               : "s"(lds_addr), "v"(voff), "s"(rsrc), "s"(soff)
-               : "memory", "m0");
-}
-
 // split plan of the bf16 kernel: pieces are whole groups of 4 k steps
 __device__ __forceinline__ SplitPlan gb_split_plan(int total, int G, int Kd) {
   return split_plan(total, G, Kd / 64);
@@ -176,6 +158,12 @@ __global__ __launch_bounds__(GB_THREADS, 1) void k_gemm_bf16(int L, int N, int K
       w.k1 = 4 * ((q + 1) * nq / plan.S);
     }
     w.ti = locate_tile(tile, L, capacity, GB_BM, NT, offsets, s_pre);
+    // the unit is the same for every lane: keep it in scalar registers (the
+    // buffer resources built from it are scalar operands of the loads)
+    w.ti.e = __builtin_amdgcn_readfirstlane(w.ti.e);
+    w.ti.row0 = __builtin_amdgcn_readfirstlane(w.ti.row0);
+    w.ti.rows = __builtin_amdgcn_readfirstlane(w.ti.rows);
+    w.ti.nt = __builtin_amdgcn_readfirstlane(w.ti.nt);
     // the (expert, panel) B tile: KT blocks of [256 columns][32 k]
     w.rB = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(B + ((long)w.ti.e * NT + w.ti.nt) * (long)KT * GB_BN * GB_BK), (short)0,

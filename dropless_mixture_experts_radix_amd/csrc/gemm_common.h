@@ -122,6 +122,35 @@ __device__ __forceinline__ SplitPlan split_plan(int total, int G, int KT) {
 // served per cycle from 64 banks) differ too.
 __device__ __forceinline__ int lds_swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
+// chunk position swizzle of a 64-byte row in its 16-row block
+__device__ __forceinline__ int swz4(int r) {
+  return (((r >> 1) ^ (r >> 3)) & 1) | ((((r >> 2) ^ (r >> 3)) & 1) << 1);
+}
+
+// 16 bytes per lane from buffer `rsrc` at voff + soff into LDS at
+// lds_addr + 16 * lane.  Issued as inline assembly so that the compiler does
+// not wait for it at every LDS read and barrier; its completion is awaited
+// explicitly (vmcnt, in issue order) before the barrier that publishes it.
+__device__ __forceinline__ void lds_dma_b128(uint32_t lds_addr, int voff, __amdgpu_buffer_rsrc_t rsrc, int soff) {
+  // s_nop 4: the wait states after an SALU write of M0 (1) and after a VALU
+  // write of an SGPR that a VMEM instruction reads (5)
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 4\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :
+               : "s"(lds_addr), "v"(voff), "s"(rsrc), "s"(soff)
+               : "memory", "m0");
+}
+
+// lds_dma_b128 when `sel` == `want` (both wave-uniform).  The test and branch
+// are inside the assembly so that the compiler sees straight-line code.
+__device__ __forceinline__ void lds_dma_b128_if(int sel, int want, uint32_t lds_addr, int voff,
+                                                __amdgpu_buffer_rsrc_t rsrc, int soff) {
+  asm volatile("s_cmp_eq_u32 %4, %5\n\ts_cbranch_scc0 1f\n\ts_mov_b32 m0, %0\n\ts_nop 4\n\t"
+               "buffer_load_dwordx4 %1, %2, %3 offen lds\n1:"
+               :
+               : "s"(lds_addr), "v"(voff), "s"(rsrc), "s"(soff), "s"(sel), "s"(want)
+               : "memory", "m0", "scc");
+}
+
 __device__ __forceinline__ int virtual_block() {
   const int G = gridDim.x, b = blockIdx.x;
   return (G % 8 == 0) ? (b % 8) * (G / 8) + b / 8 : b;

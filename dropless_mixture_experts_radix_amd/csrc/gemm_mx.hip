@@ -34,11 +34,18 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 #define GM_BM 256
 #define GM_BN 256
-#define GM_BK 128                      // codes per row and k step
-#define GM_LDB 144                     // padded LDS row (bytes)
-#define GM_STAGE (GM_BM * GM_LDB)      // bytes of one operand stage
+#define GM_BK 64                       // codes per row and ring stage
 #define GM_THREADS 512
+#define GM_STAGE_BYTES 32768           // A and B tiles of one ring stage
+#define GM_LDS_SCALES (4 * GM_STAGE_BYTES)  // scale buffers after the 4 stages
+#define GM_SGROUP_HALF 4096            // 256 rows x 16 scale bytes (512 codes)
+#define GM_SGROUP_BYTES (2 * GM_SGROUP_HALF)  // A then B
 #define GM_PART_FLOATS (GM_BM * GM_BN)
+
+// split plan of the MX kernel: pieces are whole groups of 4 stages
+__device__ __forceinline__ SplitPlan gm_split_plan(int total, int G, int Kd) {
+  return split_plan(total, G, Kd / 128);
+}
 
 // Epilogue of one wavefront's 128 x 64 part of a tile (MFMA D layout: lane l
 // holds column l%32, rows 8 (v/4) + 4 (l/32) + v%4 of each 32 x 32 block).
@@ -103,136 +110,199 @@ __global__ __launch_bounds__(GM_THREADS, 1) void k_gemm_mx(int L, int N, int Kd,
                                                            const uint8_t* __restrict__ Bs, uint8_t* __restrict__ out,
                                                            uint8_t* __restrict__ out_s, float* __restrict__ part) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  uint8_t* sA = smem;                                  // [2][256][144]
-  uint8_t* sB = sA + 2 * GM_STAGE;                     // [2][256][144]
-  uint32_t* sS = (uint32_t*)(sB + 2 * GM_STAGE);       // [2][512]: A rows, then B rows
-  int32_t* s_pre = (int32_t*)(sS + 2 * 512);           // [L+1]
-  int32_t* s_tmp = s_pre + (L + 1);                    // [16]
+  int32_t* s_pre = (int32_t*)(smem + GM_LDS_SCALES + 2 * GM_SGROUP_BYTES);  // [L+1]
+  int32_t* s_tmp = s_pre + (L + 1);                                          // [8]
   const int NT = (N + GM_BN - 1) / GM_BN;
   build_schedule(L, capacity, GM_BM, NT, offsets, s_pre, s_tmp);
-  const int KT = Kd / GM_BK, KB = Kd / 32;
-  const SplitPlan plan = split_plan(s_pre[L], gridDim.x, KT);
-  const int tid = threadIdx.x, wv = tid >> 6, l = tid & 63;
+  const int KT = Kd / GM_BK, KB = Kd / 32, NG = (Kd + 511) / 512;
+  const SplitPlan plan = gm_split_plan(s_pre[L], gridDim.x, Kd);
+  const int tid = threadIdx.x, l = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wv >> 2, wn = wv & 3;
+  const int gp = wm;  // group: wavefronts 0-3 and 4-7, one of each per SIMD
   const int g = l >> 5, r32 = l & 31;
-  // global -> LDS: thread moves 16-byte chunk lkc of rows lrow + 64 i (i < 4)
-  // of the A and the B k-step tile, and the scale word of row tid (A rows for
-  // tid < 256, B rows above)
-  const int lrow = tid >> 3, lkc = tid & 7;
-  const int st_off = lrow * GM_LDB + lkc * 16;
-  const int fa_base = (wm * 128 + r32) * GM_LDB + g * 16;
-  const int fb_base = (wn * 64 + r32) * GM_LDB + g * 16;
-  const int vb = lrow * GM_BK + lkc * 16;
-  const int va = lrow * Kd + lkc * 16;
-  const bool a_scale = tid < 256;
-  const int vs = a_scale ? tid * KB : (tid - 256) * 4;
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)smem;
+  // code loads: wavefront wv fills rows [32 wv, 32 wv + 32) of the A and of the
+  // B tile of a stage, 2 blocks of 16 rows each; lane l moves row 16q + l/4,
+  // chunk (l%4) ^ swz4(l/4) of block q
+  const int drow = l >> 2, dch = (l & 3) ^ swz4(drow);
+  // scale loads (once per 8 stages): wavefronts 0-3 the 16-byte groups of A
+  // rows [64 w, 64 w + 64), wavefronts 4-7 those of B rows
+  const int srow = (wv & 3) * 64 + l;
+  // fragment reads: row wm*128 + i*32 + r32 of A, column wn*64 + j*32 + r32 of
+  // B; bytes 0..15 of an operand are chunk g, bytes 16..31 chunk 2 + g
+  const int fr0 = r32 * 64 + ((g ^ swz4(r32)) << 4);
+  const int fr1 = r32 * 64 + (((2 + g) ^ swz4(r32)) << 4);
 
-  for (int u = virtual_block(); u < plan.units; u += gridDim.x) {
-    int tile = u, k0 = 0, k1 = KT, piece = -1;
-    if (u >= plan.dp) {  // split-K piece: k steps [k0, k1), an even count
-      piece = u - plan.dp;
-      tile = plan.dp + piece / plan.S;
-      const int q = piece % plan.S, half = KT / 2;
-      k0 = 2 * (q * half / plan.S);
-      k1 = 2 * ((q + 1) * half / plan.S);
+  struct Unit {
+    TileInfo ti;
+    int piece, k0, k1;
+    __amdgpu_buffer_rsrc_t rA, rB, rS;
+    int va[2], vb[2], vs, sgstep;
+  };
+  auto setup = [&](int u) {
+    Unit w;
+    int tile = u;
+    w.piece = -1;
+    w.k0 = 0;
+    w.k1 = KT;
+    if (u >= plan.dp) {  // split-K piece: stages [k0, k1), whole groups of 4
+      w.piece = u - plan.dp;
+      tile = plan.dp + w.piece / plan.S;
+      const int q = w.piece % plan.S, nq = KT / 4;
+      w.k0 = 4 * (q * nq / plan.S);
+      w.k1 = 4 * ((q + 1) * nq / plan.S);
     }
-    const TileInfo ti = locate_tile(tile, L, capacity, GM_BM, NT, offsets, s_pre);
-    const long pblk = ((long)ti.e * NT + ti.nt) * KT;  // first k-step block of this panel
-    const __amdgpu_buffer_rsrc_t rB =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(B + pblk * (GM_BN * GM_BK)), (short)0, KT * GM_BN * GM_BK, 0x00020000);
-    const __amdgpu_buffer_rsrc_t rA = __builtin_amdgcn_make_buffer_rsrc((void*)(A + (long)ti.row0 * Kd), (short)0,
-                                                                        ti.rows * Kd, 0x00020000);
-    // scale words: A rows of the tile (past them: zeros), or the panel's B block
-    const __amdgpu_buffer_rsrc_t rS =
-        a_scale ? __builtin_amdgcn_make_buffer_rsrc((void*)(As + (long)ti.row0 * KB), (short)0, ti.rows * KB, 0x00020000)
-                : __builtin_amdgcn_make_buffer_rsrc((void*)(Bs + pblk * (GM_BN * 4)), (short)0, KT * GM_BN * 4,
-                                                    0x00020000);
-    const int sstep = a_scale ? 4 : GM_BN * 4;
+    w.ti = locate_tile(tile, L, capacity, GM_BM, NT, offsets, s_pre);
+    // the unit is the same for every lane: keep it in scalar registers (the
+    // buffer resources built from it are scalar operands of the loads)
+    w.ti.e = __builtin_amdgcn_readfirstlane(w.ti.e);
+    w.ti.row0 = __builtin_amdgcn_readfirstlane(w.ti.row0);
+    w.ti.rows = __builtin_amdgcn_readfirstlane(w.ti.rows);
+    w.ti.nt = __builtin_amdgcn_readfirstlane(w.ti.nt);
+    const long panel = (long)w.ti.e * NT + w.ti.nt;
+    w.rB = __builtin_amdgcn_make_buffer_rsrc((void*)(B + panel * KT * (GM_BN * GM_BK)), (short)0,
+                                             KT * GM_BN * GM_BK, 0x00020000);
+    w.rA = __builtin_amdgcn_make_buffer_rsrc((void*)(A + (long)w.ti.row0 * Kd), (short)0, w.ti.rows * Kd,
+                                             0x00020000);
+    if (wv < 4) {  // A scale groups: row-major [rows][Kd/32] bytes
+      w.rS = __builtin_amdgcn_make_buffer_rsrc((void*)(As + (long)w.ti.row0 * KB), (short)0, w.ti.rows * KB,
+                                               0x00020000);
+      w.vs = srow * KB;
+      w.sgstep = 16;
+    } else {  // B scale groups of the panel: [NG][256][16]
+      w.rS = __builtin_amdgcn_make_buffer_rsrc((void*)(Bs + panel * NG * GM_SGROUP_HALF), (short)0,
+                                               NG * GM_SGROUP_HALF, 0x00020000);
+      w.vs = srow * 16;
+      w.sgstep = GM_SGROUP_HALF;
+    }
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int r = wv * 32 + q * 16 + drow;
+      w.va[q] = r * Kd + dch * 16;
+      w.vb[q] = r * GM_BK + dch * 16;
+    }
+    return w;
+  };
 
-    u32x4 ast[4], bst[4];  // register stage of the next k step
-    uint32_t sst;
-#define GM_LOAD(KT_)                                                                        \
+#define GM_DMA(W, ST, KT_, Q)                                                               \
   {                                                                                         \
-    const int koa = va + (KT_) * GM_BK;                                                     \
-    const int kob = (KT_) * (GM_BN * GM_BK);                                                \
+    const int kq = (KT_);                                                                   \
+    if ((Q) < 2)                                                                            \
+      lds_dma_b128(lds0 + (ST) * GM_STAGE_BYTES + (wv * 2 + (Q)) * 1024, (W).va[Q], (W).rA, kq * GM_BK); \
+    else                                                                                    \
+      lds_dma_b128(lds0 + (ST) * GM_STAGE_BYTES + 8192 * 2 + (wv * 2 + (Q) - 2) * 1024, (W).vb[(Q) - 2], (W).rB, \
+                   kq * (GM_BN * GM_BK));                                                   \
+  }
+// the scale group G_ of the unit into scale buffer G_ % 2 (when SEL == WANT)
+#define GM_SDMA_IF(W, G_, SEL, WANT)                                                        \
+  {                                                                                         \
+    const int gq = (G_);                                                                    \
+    lds_dma_b128_if((SEL), (WANT),                                                          \
+                    lds0 + GM_LDS_SCALES + (gq & 1) * GM_SGROUP_BYTES + (wv >= 4 ? GM_SGROUP_HALF : 0) + \
+                        (wv & 3) * 1024,                                                    \
+                    (W).vs, (W).rS, gq * (W).sgstep);                                       \
+  }
+// the ring prologue of a unit: the scale group of k0, then stages k0 .. k0+2
+#define GM_PROLOGUE(W)                                                                      \
+  {                                                                                         \
+    GM_SDMA_IF(W, (W).k0 >> 3, 0, 0);                                                       \
+    _Pragma("unroll") for (int st = 0; st < 3; ++st) {                                      \
+      _Pragma("unroll") for (int q = 0; q < 4; ++q) GM_DMA(W, st, min((W).k0 + st, (W).k1 - 1), q); \
+    }                                                                                       \
+  }
+// fragments and scale bytes of stage KS_ (in ring stage ST)
+#define GM_READ(ST, KS_)                                                                    \
+  {                                                                                         \
+    const uint8_t* pa = smem + (ST) * GM_STAGE_BYTES + wm * 8192;                           \
+    const uint8_t* pb = smem + (ST) * GM_STAGE_BYTES + 16384 + wn * 4096;                   \
     _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                         \
-      ast[i] = __builtin_amdgcn_raw_buffer_load_b128(rA, koa + i * 64 * Kd, 0, 0);          \
-      bst[i] = __builtin_amdgcn_raw_buffer_load_b128(rB, vb + i * (64 * GM_BK), kob, 0);    \
+      const u32x4 lo = *(const u32x4*)(pa + i * 2048 + fr0);                                \
+      const u32x4 hi = *(const u32x4*)(pa + i * 2048 + fr1);                                \
+      fa[i] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]}; \
     }                                                                                       \
-    sst = __builtin_amdgcn_raw_buffer_load_b32(rS, vs + (KT_) * sstep, 0, 0);               \
-  }
-#define GM_STORE(BUF)                                                                       \
-  {                                                                                         \
-    uint8_t* dA = sA + (BUF) * GM_STAGE + st_off;                                           \
-    uint8_t* dB = sB + (BUF) * GM_STAGE + st_off;                                           \
-    _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                         \
-      *(u32x4*)(dA + i * 64 * GM_LDB) = ast[i];                                             \
-      *(u32x4*)(dB + i * 64 * GM_LDB) = bst[i];                                             \
+    _Pragma("unroll") for (int j = 0; j < 2; ++j) {                                         \
+      const u32x4 lo = *(const u32x4*)(pb + j * 2048 + fr0);                                \
+      const u32x4 hi = *(const u32x4*)(pb + j * 2048 + fr1);                                \
+      fb[j] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]}; \
     }                                                                                       \
-    sS[(BUF) * 512 + tid] = sst;                                                            \
+    const int ks = (KS_);                                                                   \
+    const uint8_t* ps = smem + GM_LDS_SCALES + ((ks >> 3) & 1) * GM_SGROUP_BYTES + (ks & 7) * 2 + g; \
+    _Pragma("unroll") for (int i = 0; i < 4; ++i) sa[i] = ps[(wm * 128 + i * 32 + r32) * 16]; \
+    _Pragma("unroll") for (int j = 0; j < 2; ++j) sb[j] = ps[GM_SGROUP_HALF + (wn * 64 + j * 32 + r32) * 16]; \
   }
-#define GM_COMPUTE(BUF)                                                                     \
-  {                                                                                         \
-    const uint8_t* cA = sA + (BUF) * GM_STAGE + fa_base;                                    \
-    const uint8_t* cB = sB + (BUF) * GM_STAGE + fb_base;                                    \
-    const uint32_t* cS = sS + (BUF) * 512;                                                  \
-    uint32_t sa4[4], sb4[2];                                                                \
-    _Pragma("unroll") for (int i = 0; i < 4; ++i) sa4[i] = cS[wm * 128 + i * 32 + r32];     \
-    _Pragma("unroll") for (int j = 0; j < 2; ++j) sb4[j] = cS[256 + wn * 64 + j * 32 + r32]; \
-    _Pragma("unroll") for (int s = 0; s < 2; ++s) {                                         \
-      const int sh = 8 * (2 * s + g);                                                       \
-      i32x8 fa[4], fb[2];                                                                   \
-      _Pragma("unroll") for (int j = 0; j < 2; ++j) {                                       \
-        const u32x4 lo = *(const u32x4*)(cB + j * 32 * GM_LDB + s * 64);                   \
-        const u32x4 hi = *(const u32x4*)(cB + j * 32 * GM_LDB + s * 64 + 32);               \
-        fb[j] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],                       \
-                      (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};                      \
-      }                                                                                     \
-      _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                       \
-        const u32x4 lo = *(const u32x4*)(cA + i * 32 * GM_LDB + s * 64);                    \
-        const u32x4 hi = *(const u32x4*)(cA + i * 32 * GM_LDB + s * 64 + 32);               \
-        fa[i] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],                       \
-                      (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};                      \
-      }                                                                                     \
-      _Pragma("unroll") for (int i = 0; i < 4; ++i)                                         \
-        _Pragma("unroll") for (int j = 0; j < 2; ++j)                                       \
-          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(                      \
-              fa[i], fb[j], acc[i][j], 0, 0, 0, (int)((sa4[i] >> sh) & 255u), 0,            \
-              (int)((sb4[j] >> sh) & 255u));                                                \
-    }                                                                                       \
+#define GM_MMA1(T)                                                                          \
+  acc[(T) >> 1][(T) & 1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(                 \
+      fa[(T) >> 1], fb[(T) & 1], acc[(T) >> 1][(T) & 1], 0, 0, 0, (int)sa[(T) >> 1], 0, (int)sb[(T) & 1]);
+#define GM_FENCE __builtin_amdgcn_sched_barrier(0);
+
+  int u = virtual_block();
+  Unit cu;
+  if (u < plan.units) {
+    cu = setup(u);
+    GM_PROLOGUE(cu);
   }
+  while (u < plan.units) {
+    const int k0 = cu.k0, k1 = cu.k1;
+    i32x8 fa[4], fb[2];
+    uint32_t sa[4], sb[2];
     f32x16 acc[4][2];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
-
-    // prologue: k step k0 into LDS buffer 0, k step k0+1 in registers;
-    // steady state: at step kt (kt - k0 even) LDS buffer 0 holds step kt and
-    // the registers hold step kt+1
-    GM_LOAD(k0);
-    GM_STORE(0);
-    GM_LOAD(k0 + 1);
-    __syncthreads();
-    for (int kt = k0; kt < k1; kt += 2) {
-      GM_COMPUTE(0);
-      GM_STORE(1);
-      GM_LOAD(min(kt + 2, k1 - 1));
-      __syncthreads();
-      GM_COMPUTE(1);
-      GM_STORE(0);
-      GM_LOAD(min(kt + 3, k1 - 1));
-      __syncthreads();
+    // wait for stage k0 and the scale group issued before it (the younger
+    // stages k0+1, k0+2 may still be loading; loads complete in issue order)
+    asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");
+    // the second group of wavefronts runs one phase behind the first
+    if (gp) asm volatile("s_barrier" ::: "memory");
+    // Phases as in the bf16 kernel: the memory phase of stage ks reads its
+    // fragments and scale bytes, loads stage ks+3 (and, at ks % 8 == 5, the
+    // scale group of stage ks+3 first) and waits; the compute phase is the
+    // stage's 8 MFMAs.  A scale group is complete with the stage loaded after
+    // it.  The vmcnt(8) waits allow the two younger stages' 8 loads in flight;
+    // where a scale load is among them the wait is one load stronger than
+    // needed.
+#define GM_KLOOP(MM)                                                                        \
+  for (int kt = k0; kt < k1; kt += 4) {                                                     \
+    _Pragma("unroll") for (int h = 0; h < 4; ++h) {                                         \
+      GM_READ(h, kt + h);                                                                   \
+      {                                                                                     \
+        const int kn = min(kt + h + 3, k1 - 1);                                             \
+        GM_SDMA_IF(cu, min(((kt + h) >> 3) + 1, NG - 1), (kt + h) & 7, 5);                  \
+        _Pragma("unroll") for (int q = 0; q < 4; ++q) GM_DMA(cu, (h + 3) & 3, kn, q);      \
+      }                                                                                     \
+      asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory");              \
+      GM_FENCE;                                                                             \
+      if (MM) {                                                                             \
+        _Pragma("unroll") for (int t = 0; t < 8; ++t) { GM_MMA1(t); }                       \
+      }                                                                                     \
+      GM_FENCE;                                                                             \
+      asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");                          \
+    }                                                                                       \
+  }
+    // in a tile of at most 128 rows the second group has no rows: it only
+    // reads and loads.  Both loop versions have the same loads and barriers.
+    if (cu.ti.rows > wm * 128) {
+      GM_KLOOP(1);
+    } else {
+      GM_KLOOP(0);
     }
-#undef GM_LOAD
-#undef GM_STORE
-#undef GM_COMPUTE
-
-    if (piece < 0) {
-      mx_store_tile<EPI>(acc, ti, N, wm, wn, g, r32, out, out_s);
+#undef GM_KLOOP
+    if (!gp) asm volatile("s_barrier" ::: "memory");
+    // every wavefront is past its last read of this unit: start the next
+    // unit's loads, then store this one while they travel
+    const Unit done = cu;
+    u += gridDim.x;
+    if (u < plan.units) {
+      cu = setup(u);
+      GM_PROLOGUE(cu);
+    }
+    if (done.piece < 0) {
+      mx_store_tile<EPI>(acc, done.ti, N, wm, wn, g, r32, out, out_s);
     } else {
       // partial tile, per wavefront [i][j][lane][16 values of the MFMA D layout]
-      float* dst = part + (long)piece * GM_PART_FLOATS + wv * 8192 + l * 16;
+      float* dst = part + (long)done.piece * GM_PART_FLOATS + wv * 8192 + l * 16;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -243,6 +313,14 @@ __global__ __launch_bounds__(GM_THREADS, 1) void k_gemm_mx(int L, int N, int Kd,
                 f32x4{acc[i][j][4 * c], acc[i][j][4 * c + 1], acc[i][j][4 * c + 2], acc[i][j][4 * c + 3]};
     }
   }
+#undef GM_DMA
+#undef GM_SDMA_IF
+#undef GM_PROLOGUE
+#undef GM_READ
+#undef GM_MMA1
+#undef GM_FENCE
+  // the last prefetches of the ring (clamped repeats) land before the exit
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
 // Sum the S split-K partials of each split tile (in piece order) and apply the
@@ -258,7 +336,7 @@ __global__ __launch_bounds__(64) void k_mx_splitk_reduce(int L, int N, int Kd, i
   const int NT = (N + GM_BN - 1) / GM_BN;
   build_schedule(L, capacity, GM_BM, NT, offsets, s_pre, s_tmp);
   const int total = s_pre[L];
-  const SplitPlan plan = split_plan(total, G, Kd / GM_BK);
+  const SplitPlan plan = gm_split_plan(total, G, Kd);
   const int b = blockIdx.x >> 3, wv = blockIdx.x & 7, l = threadIdx.x;
   if (plan.S < 2 || b >= total - plan.dp) return;
   const TileInfo ti = locate_tile(plan.dp + b, L, capacity, GM_BM, NT, offsets, s_pre);
@@ -300,7 +378,7 @@ hipError_t launch_grouped_mlp_mx(int L, int H, int F, int64_t capacity, const ui
     (void)hipFuncSetAttribute((const void*)k_gemm_mx<1>, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     attr_done = true;
   }
-  const size_t lds = (size_t)4 * GM_STAGE + (size_t)2 * 512 * 4 + (size_t)(L + 1 + 16) * sizeof(int32_t);
+  const size_t lds = (size_t)GM_LDS_SCALES + 2 * GM_SGROUP_BYTES + (size_t)(L + 1 + 16) * sizeof(int32_t);
   auto grid = [&](int N) {
     const int NT = (N + GM_BN - 1) / GM_BN;
     const int64_t upper = ((capacity + GM_BM - 1) / GM_BM + L) * (int64_t)NT;

@@ -147,8 +147,9 @@ size_t moe_prepared_weight_bytes(int L, int H, int F, int dtype, int which) {
   switch (which) {
     case 1: return n1 * el;
     case 2: return n2 * el;
-    case 3: return dtype == MOE_MXFP8 ? n1 / 32 : 0;
-    case 4: return dtype == MOE_MXFP8 ? n2 / 32 : 0;
+    // MX scales: 16 bytes per prepared row and 512-wide k group
+    case 3: return dtype == MOE_MXFP8 ? n1 / H * (((size_t)H + 511) / 512) * 16 : 0;
+    case 4: return dtype == MOE_MXFP8 ? n2 / F * (((size_t)F + 511) / 512) * 16 : 0;
     default: return 0;
   }
 }

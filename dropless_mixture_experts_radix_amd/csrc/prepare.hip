@@ -17,9 +17,11 @@ namespace moe {
 //         step one contiguous 16 KiB block [256 rows][32 k]; rows past Ncols in
 //         the last panel are zero.
 // MODE 2: bf16 -> MX E4M3 codes and E8M0 scales in k-blocked panels: per
-//         256-row panel and 128-wide k step one contiguous 32 KiB block of codes
-//         [256 rows][128 k] and one 1 KiB block of scales [256 rows][4 blocks];
-//         rows past Ncols in the last panel are zero (codes and scales).
+//         256-row panel and 64-wide k step one contiguous 16 KiB block of codes
+//         [256 rows][64 k], and per 512-wide k group one 4 KiB block of scales
+//         [256 rows][16 blocks] (bytes past the last block of a short final
+//         group are not written); rows past Ncols in the last panel are zero
+//         (codes and scales).
 template <int MODE>
 __global__ __launch_bounds__(256) void k_prepare(int Kd, int Ncols, int F_interleave,
                                                  const void* __restrict__ w, void* __restrict__ wp,
@@ -65,12 +67,12 @@ __global__ __launch_bounds__(256) void k_prepare(int Kd, int Ncols, int F_interl
       am = am > a ? am : a;
     }
     const int E = mx_scale_exp(am);
-    const int NP = (Ncols + 255) / 256, KT = Kd / 128;
+    const int NP = (Ncols + 255) / 256, KT = Kd / 64, NG = (Kd + 511) / 512;
     const int p = pc * 32 + pp;
-    const long blk = ((long)e * NP + (p >> 8)) * KT + (k0 >> 7);  // (expert, panel, k step)
-    uint8_t* dst = (uint8_t*)wp + blk * (256 * 128) + (p & 255) * 128 + (k0 & 127);
+    const long panel = (long)e * NP + (p >> 8);
+    uint8_t* dst = (uint8_t*)wp + (panel * KT + (k0 >> 6)) * (256 * 64) + (p & 255) * 64 + (k0 & 63);
     for (int kk = 0; kk < 32; ++kk) dst[kk] = (uint8_t)mx_e4m3(tile[pp][kk], E);
-    ws[blk * (256 * 4) + (p & 255) * 4 + ((k0 >> 5) & 3)] = (uint8_t)(E + 127);
+    ws[(panel * NG + (k0 >> 9)) * (256 * 16) + (p & 255) * 16 + ((k0 >> 5) & 15)] = (uint8_t)(E + 127);
   }
 }
 

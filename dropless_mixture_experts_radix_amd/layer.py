@@ -42,8 +42,9 @@ class MoELayer:
         self.w2p = torch.empty((L, pad(H), F), dtype=wdt, device=dev)
         self.w1s = self.w2s = None
         if dtype == M.MXFP8:
-            self.w1s = torch.empty((L, pad(2 * F), H // 32), dtype=torch.uint8, device=dev)
-            self.w2s = torch.empty((L, pad(H), F // 32), dtype=torch.uint8, device=dev)
+            # E8M0 scales: 16 bytes per prepared row and 512-wide k group
+            self.w1s = torch.empty((L, pad(2 * F), (H + 511) // 512 * 16), dtype=torch.uint8, device=dev)
+            self.w2s = torch.empty((L, pad(H), (F + 511) // 512 * 16), dtype=torch.uint8, device=dev)
         # per-call buffers
         i32 = dict(dtype=torch.int32, device=dev)
         self.ids = torch.empty((T, K), dtype=torch.int16, device=dev)

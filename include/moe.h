@@ -195,9 +195,11 @@ int moe_permute(int T, int H, int K, int E_global, int e0, int L, int64_t capaci
  * dtype MOE_MXFP8 (in_dtype MOE_BF16): E4M3 codes (uint8) of the rows above
  *   with one E8M0 scale per 32 consecutive elements along a row, padded with
  *   zero rows (codes and scales) to whole panels of 256 rows and k-blocked:
- *   codes [L][panel][k/128][256 rows][128 k] (W1p: ceil(2F/256) panels over
- *   H, W2p: ceil(H/256) panels over F), scales [L][panel][k/128][256 rows][4]
- *   (w1p_scales, w2p_scales).  Requires H % 256 == 0 and F % 256 == 0.
+ *   codes [L][panel][k/64][256 rows][64 k] (W1p: ceil(2F/256) panels over
+ *   H, W2p: ceil(H/256) panels over F), scales [L][panel][ceil(k/512)][256
+ *   rows][16] (w1p_scales, w2p_scales; the bytes past the last 32-block of a
+ *   short final group are left as they are).  Requires H % 256 == 0 and
+ *   F % 256 == 0.
  * Requires H % 32 == 0 and F % 32 == 0 (MOE_F32).  Byte sizes:
  * moe_prepared_weight_bytes(L, H, F, dtype, which) with which = 1 (W1p),
  * 2 (W2p), 3 (W1p scales), 4 (W2p scales).

@@ -127,6 +127,9 @@ def test_size_queries():
     assert lib.moe_router_prepared_bytes(64, 8, 0, 0) == 64 * 8 * 4
     assert lib.moe_prepared_weight_bytes(8, 4096, 14336, 1, 1) == 8 * 2 * 14336 * 4096 * 2
     assert lib.moe_prepared_weight_bytes(8, 4096, 14336, 2, 3) == 8 * 2 * 14336 * 4096 // 32
+    # MX scales: 16 bytes per prepared row and 512-wide k group (short last group padded)
+    assert lib.moe_prepared_weight_bytes(2, 768, 256, 2, 3) == 2 * 512 * 2 * 16
+    assert lib.moe_prepared_weight_bytes(2, 768, 256, 2, 4) == 2 * 768 * 1 * 16
     assert lib.moe_prepared_weight_bytes(8, 4096, 14336, 1, 3) == 0
     assert lib.moe_grouped_mlp_workspace_bytes(8192, 14336, 1) >= 8192 * 14336 * 2
     assert lib.moe_permute_workspace_bytes(8192, 36, 32) >= 8192 * 36 * 4

@@ -30,11 +30,12 @@ def _unblock(wp):
 
 def _unblock_mx(wp, ws):
     """MXFP8 prepared weights of one expert, k-blocked panels: codes
-    [rows/256][Kd/128][256][128] and scales [rows/256][Kd/128][256][4], back to
-    row-major codes [rows][Kd] and scales [rows][Kd/32] (numpy uint8)."""
+    [rows/256][Kd/64][256][64] and scales [rows/256][ceil(Kd/512)][256][16], back
+    to row-major codes [rows][Kd] and scales [rows][Kd/32] (numpy uint8)."""
     rows, kd = wp.shape
-    c = np_of(wp).reshape(rows // 256, kd // 128, 256, 128).transpose(0, 2, 1, 3).reshape(rows, kd)
-    s = np_of(ws).reshape(rows // 256, kd // 128, 256, 4).transpose(0, 2, 1, 3).reshape(rows, kd // 32)
+    ng = (kd + 511) // 512
+    c = np_of(wp).reshape(rows // 256, kd // 64, 256, 64).transpose(0, 2, 1, 3).reshape(rows, kd)
+    s = np_of(ws).reshape(rows // 256, ng, 256, 16).transpose(0, 2, 1, 3).reshape(rows, ng * 16)[:, : kd // 32]
     return c, s
 
 
@@ -77,8 +78,8 @@ def _run_mlp(counts, H, F, dt, seed=0, xscale=1.0, check_layout=True):
     w2p = torch.empty((L, pad(H), F), dtype=wdt, device=DEV)
     w1s = w2s = None
     if dt == "mxfp8":
-        w1s = torch.empty((L, pad(2 * F), H // 32), dtype=torch.uint8, device=DEV)
-        w2s = torch.empty((L, pad(H), F // 32), dtype=torch.uint8, device=DEV)
+        w1s = torch.empty((L, pad(2 * F), (H + 511) // 512 * 16), dtype=torch.uint8, device=DEV)
+        w2s = torch.empty((L, pad(H), (F + 511) // 512 * 16), dtype=torch.uint8, device=DEV)
     D.moe_prepare_weights(w1, w2, code, w1p, w2p, w1s, w2s)
     perm = _interleave_rows(F)
     if check_layout:
