@@ -89,6 +89,9 @@ int moe_route_topk(int T, int E, int K, int H, int score, int x_dtype, int w_dty
   hipStream_t s = (hipStream_t)stream;
   const float* partial = logits;
   int S = 1;
+  if (from_x && route_fused_ok(E, H, x_dtype, w_dtype))
+    return launch_status(launch_route_fused(T, E, K, H, score, w_dtype, x, w_prepared, bias, mask, ids, probs,
+                                            logits_out, err, s));
   if (from_x) {
     float* ws = (float*)workspace;
     hipError_t e = launch_router_proj(T, E, H, x_dtype, w_dtype, x, w_prepared, ws, s);

@@ -151,6 +151,10 @@ hipError_t launch_prepare_router(const void* w, int w_dtype, int x_dtype, int H,
                                  hipStream_t s);
 hipError_t launch_router_proj(int T, int E, int H, int x_dtype, int w_dtype, const void* x,
                               const void* wp, float* partial, hipStream_t s);
+bool route_fused_ok(int E, int H, int x_dtype, int w_dtype);
+hipError_t launch_route_fused(int T, int E, int K, int H, int score, int w_dtype, const void* x, const void* wp,
+                              const float* bias, const uint8_t* mask, int16_t* ids, float* probs,
+                              float* logits_out, int32_t* err, hipStream_t s);
 hipError_t launch_route_select(int T, int E, int K, int S, int score, const float* partial,
                                const float* bias, const uint8_t* mask, int16_t* ids, float* probs,
                                float* logits_out, int32_t* err, hipStream_t s);

@@ -198,39 +198,18 @@ __device__ __forceinline__ float score_of(float z, float zmax, int score) {
 
 // Small-E path (E <= 32): one thread per token, keys in registers, each key's
 // output position is its rank (number of keys that beat it).
+// Selection for one token of a small-E router (E <= EMAX <= 32): z holds the
+// token's E logits.  Writes logits_out, applies the bias, and writes the K ids
+// (descending key, lower index first on ties) and their probabilities; each
+// key's output position is its rank (the number of keys that beat it).
 template <int EMAX>
-__global__ __launch_bounds__(64) void k_route_select_small(int T, int E, int K, int S, int score,
-                                                            const float* __restrict__ partial,
-                                                            const float* __restrict__ bias,
-                                                            const uint8_t* __restrict__ mask,
-                                                            int16_t* __restrict__ ids, float* __restrict__ probs,
-                                                            float* __restrict__ logits_out, int32_t* err) {
-  const int t = blockIdx.x * blockDim.x + threadIdx.x;
-  if (t >= T) return;
-  float z[EMAX];
+__device__ __forceinline__ void select_small_token(int t, int E, int K, int score, float (&z)[EMAX],
+                                                   const float* __restrict__ bias,
+                                                   const uint8_t* __restrict__ mask, int16_t* __restrict__ ids,
+                                                   float* __restrict__ probs, float* __restrict__ logits_out,
+                                                   int32_t* err) {
   uint32_t key[EMAX];
   bool bad = false;
-#pragma unroll
-  for (int e = 0; e < EMAX; ++e) z[e] = 0.f;
-  // the S partial sets in order; a token's E logits of one set are contiguous
-  if ((E & 3) == 0) {
-    for (int s = 0; s < S; ++s) {
-      const float4* ps = (const float4*)(partial + ((long)s * T + t) * E);
-#pragma unroll
-      for (int c = 0; c < EMAX / 4; ++c) {
-        if (4 * c < E) {
-          const float4 q = ps[c];
-          z[4 * c] += q.x; z[4 * c + 1] += q.y; z[4 * c + 2] += q.z; z[4 * c + 3] += q.w;
-        }
-      }
-    }
-  } else {
-    for (int s = 0; s < S; ++s) {
-#pragma unroll
-      for (int e = 0; e < EMAX; ++e)
-        if (e < E) z[e] += partial[((long)s * T + t) * E + e];
-    }
-  }
 #pragma unroll
   for (int e = 0; e < EMAX; ++e) {
     float v = z[e];
@@ -238,7 +217,6 @@ __global__ __launch_bounds__(64) void k_route_select_small(int T, int E, int K, 
       if (logits_out) logits_out[(long)t * E + e] = v;
       if (bias) v += bias[e];
     }
-    z[e] = v;
     key[e] = e < E ? float_key(v) : 0u;
     if (e < E && !key_finite(key[e])) bad = true;
   }
@@ -278,7 +256,149 @@ __global__ __launch_bounds__(64) void k_route_select_small(int T, int E, int K, 
       probs[(long)t * K + rank[e]] = sc[e] * inv;
     }
   }
-  (void)z;
+}
+
+// Small-E path from logits or split-H partials (E <= 32): one thread per token.
+template <int EMAX>
+__global__ __launch_bounds__(64) void k_route_select_small(int T, int E, int K, int S, int score,
+                                                            const float* __restrict__ partial,
+                                                            const float* __restrict__ bias,
+                                                            const uint8_t* __restrict__ mask,
+                                                            int16_t* __restrict__ ids, float* __restrict__ probs,
+                                                            float* __restrict__ logits_out, int32_t* err) {
+  const int t = blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= T) return;
+  float z[EMAX];
+#pragma unroll
+  for (int e = 0; e < EMAX; ++e) z[e] = 0.f;
+  // the S partial sets in order; a token's E logits of one set are contiguous
+  if ((E & 3) == 0) {
+    for (int s = 0; s < S; ++s) {
+      const float4* ps = (const float4*)(partial + ((long)s * T + t) * E);
+#pragma unroll
+      for (int c = 0; c < EMAX / 4; ++c) {
+        if (4 * c < E) {
+          const float4 q = ps[c];
+          z[4 * c] += q.x; z[4 * c + 1] += q.y; z[4 * c + 2] += q.z; z[4 * c + 3] += q.w;
+        }
+      }
+    }
+  } else {
+    for (int s = 0; s < S; ++s) {
+#pragma unroll
+      for (int e = 0; e < EMAX; ++e)
+        if (e < E) z[e] += partial[((long)s * T + t) * E + e];
+    }
+  }
+  select_small_token<EMAX>(t, E, K, score, z, bias, mask, ids, probs, logits_out, err);
+}
+
+// Fused projection + selection for a small router (bf16 x, all P*E prepared
+// rows in one 32-row tile): a workgroup of 8 wavefronts takes 16 tokens; each
+// wavefront computes the 16 x 32 logit tile over its eighth of H on
+// v_mfma_f32_16x16x32_bf16 (two 16-column tiles); the eight partial tiles are
+// summed in LDS in wavefront order, the P terms of each expert in term order,
+// and one thread per token selects.  No partial logits go through HBM.  With
+// the 16-row instruction four lanes share a token row, so one 16-byte-per-lane
+// load covers 64 contiguous bytes of each of 16 rows.
+template <int EMAX>
+__global__ __launch_bounds__(512) void k_route_fused_small(int T, int E, int K, int H, int P, int score,
+                                                           const bf16_t* __restrict__ x,
+                                                           const bf16_t* __restrict__ wp,
+                                                           const float* __restrict__ bias,
+                                                           const uint8_t* __restrict__ mask,
+                                                           int16_t* __restrict__ ids, float* __restrict__ probs,
+                                                           float* __restrict__ logits_out, int32_t* err) {
+  __shared__ float s_part[8][16][33];
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63, q = l >> 4, r = l & 15;
+  const int t0 = blockIdx.x * 16;
+  const int ra = min(t0 + r, T - 1);
+  // 32-wide k slices of this wavefront: [k0s, k1s)
+  const int nks = H / 32, per = (nks + 7) / 8;
+  const int k0s = min(w * per, nks), k1s = min(k0s + per, nks);
+  // lane (q, r): token row r (A) or prepared rows r and 16 + r (B), k = 8q..8q+7 of a slice
+  const bf16_t* pa = x + (long)ra * H + 8 * q;
+  const bf16_t* pw0 = wp + (long)r * H + 8 * q;
+  const bf16_t* pw1 = wp + (long)(16 + r) * H + 8 * q;
+  typedef float f32x4v __attribute__((ext_vector_type(4)));
+  f32x4v acc[2][2] = {};  // [slice parity][column tile]
+  int ks = k0s;
+  // eight slices at a time; the fence keeps all their loads ahead of the MFMAs
+  for (; ks + 8 <= k1s; ks += 8) {
+    bf16x8 a[8], b0[8], b1[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      a[u] = *(const bf16x8*)(pa + (ks + u) * 32);
+      b0[u] = *(const bf16x8*)(pw0 + (ks + u) * 32);
+      b1[u] = *(const bf16x8*)(pw1 + (ks + u) * 32);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      acc[u & 1][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[u], b0[u], acc[u & 1][0], 0, 0, 0);
+      acc[u & 1][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[u], b1[u], acc[u & 1][1], 0, 0, 0);
+    }
+  }
+  for (; ks < k1s; ++ks) {
+    const bf16x8 a = *(const bf16x8*)(pa + ks * 32);
+    const bf16x8 b0 = *(const bf16x8*)(pw0 + ks * 32);
+    const bf16x8 b1 = *(const bf16x8*)(pw1 + ks * 32);
+    acc[0][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b0, acc[0][0], 0, 0, 0);
+    acc[0][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b1, acc[0][1], 0, 0, 0);
+  }
+  // D layout: lane l holds column l%16, rows 4*(l/16) + i
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    const f32x4v v = acc[0][c] + acc[1][c];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s_part[w][4 * q + i][16 * c + r] = v[i];
+  }
+  __syncthreads();
+  // sum the eight partial tiles in wavefront order (one value per thread)
+  {
+    const int row = threadIdx.x >> 5, col = threadIdx.x & 31;
+    float v = 0.f;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v += s_part[u][row][col];
+    __syncthreads();
+    s_part[0][row][col] = v;
+  }
+  __syncthreads();
+  const int t = t0 + threadIdx.x;
+  if (threadIdx.x >= 16 || t >= T) return;
+  const int ept = router_ept(P);
+  float z[EMAX];
+#pragma unroll
+  for (int e = 0; e < EMAX; ++e) {
+    float v = 0.f;
+    if (e < E)
+      for (int p = 0; p < P; ++p) v += s_part[0][threadIdx.x][p * ept + e];
+    z[e] = v;
+  }
+  select_small_token<EMAX>(t, E, K, score, z, bias, mask, ids, probs, logits_out, err);
+}
+
+bool route_fused_ok(int E, int H, int x_dtype, int w_dtype) {
+  const int P = router_terms(w_dtype), ept = router_ept(P);
+  return x_dtype == MOE_BF16 && E <= ept && E <= 32 && H % 32 == 0;
+}
+
+hipError_t launch_route_fused(int T, int E, int K, int H, int score, int w_dtype, const void* x, const void* wp,
+                              const float* bias, const uint8_t* mask, int16_t* ids, float* probs,
+                              float* logits_out, int32_t* err, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  const int P = router_terms(w_dtype);
+  const dim3 g((T + 15) / 16), b(512);
+  if (E <= 8)
+    hipLaunchKernelGGL(k_route_fused_small<8>, g, b, 0, s, T, E, K, H, P, score, (const bf16_t*)x,
+                       (const bf16_t*)wp, bias, mask, ids, probs, logits_out, err);
+  else if (E <= 16)
+    hipLaunchKernelGGL(k_route_fused_small<16>, g, b, 0, s, T, E, K, H, P, score, (const bf16_t*)x,
+                       (const bf16_t*)wp, bias, mask, ids, probs, logits_out, err);
+  else
+    hipLaunchKernelGGL(k_route_fused_small<32>, g, b, 0, s, T, E, K, H, P, score, (const bf16_t*)x,
+                       (const bf16_t*)wp, bias, mask, ids, probs, logits_out, err);
+  return hipGetLastError();
 }
 
 // Large-E path: one wavefront per token, VPL keys per lane (element index of

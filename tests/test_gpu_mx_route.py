@@ -82,7 +82,7 @@ def _check_route(ids, probs, lo, T, K, score, bias=None, mask=None):
 
 
 @pytest.mark.parametrize("cfgname,T", [("tiny_f32", 256), ("mixtral_bf16", 1024), ("mixtral_bf16", 4096),
-                                       ("dsv3_bf16", 1024), ("dsv3_bf16", 8192)])
+                                       ("mixtral_bf16", 1000), ("dsv3_bf16", 1024), ("dsv3_bf16", 8192)])
 def test_route_fused_projection_workloads(cfgname, T):
     cfg = get_config(cfgname)
     say("route", cfgname, T)
@@ -97,6 +97,26 @@ def test_route_fused_projection_workloads(cfgname, T):
     want = O.router_logits(to_numpy_f64(x[rows]), to_numpy_f64(r["w_router"]))
     assert rel_inf(lo[rows], want) <= TOL["logits"]
     _check_route(ids, probs, lo, T, cfg.K, cfg.score, None if bias is None else r["bias"].numpy())
+
+
+@pytest.mark.parametrize("E,K,H,wdt,T", [(32, 4, 576, torch.bfloat16, 77), (10, 3, 640, torch.float32, 300),
+                                         (5, 5, 64, torch.bfloat16, 33)])
+def test_route_small_router_from_x(E, K, H, wdt, T):
+    """Small routers from bf16 rows (one workgroup per 32 tokens sums the H
+    split across its wavefronts): ragged token tail, H that does not split
+    evenly over 8 wavefronts, K = E, bf16 and fp32 router weights, bias and mask."""
+    g = torch.Generator().manual_seed(E * 1000 + H)
+    x = torch.randn((T, H), generator=g).to(torch.bfloat16)
+    w = (torch.randn((H, E), generator=g) * 0.05).to(wdt)
+    bias = torch.randn(E, generator=g) * 0.1
+    mask = (torch.arange(T) % 7 == 3).to(torch.uint8)
+    say("route small router", E, K, H, wdt, T)
+    ids, probs, lo, err = _route_gpu(T, E, K, D.SOFTMAX, x=x.to(DEV), w_router=w.to(DEV), bias=bias.to(DEV),
+                                     mask=mask.to(DEV))
+    assert err == 0
+    want = O.router_logits(to_numpy_f64(x), to_numpy_f64(w))
+    assert rel_inf(lo, want) <= TOL["logits"]
+    _check_route(ids, probs, lo, T, K, "softmax", bias.numpy(), mask.numpy())
 
 
 @pytest.mark.parametrize("T", [2048, 8192])
