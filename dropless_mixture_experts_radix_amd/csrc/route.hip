@@ -402,16 +402,90 @@ hipError_t launch_route_fused(int T, int E, int K, int H, int score, int w_dtype
 }
 
 // Large-E path: one wavefront per token, VPL keys per lane (element index of
-// key j of lane l: (j/4)*256 + 4*l + j%4, so keys are read with 16-byte loads).
-//  1. Candidate bound: lb = K-th largest of the 64 per-lane maxima; at least K
-//     keys are >= lb, so the K selected keys all satisfy key >= lb.
-//  2. If at most CMAX keys are >= lb, they are gathered (in index order) and
-//     ranked directly.
-//  3. Otherwise radix threshold select: 4 histogram passes over 8-bit digits
-//     (most significant first, 256 LDS bins per wave) narrow the candidates to
-//     the K-th key tau; the keys > tau and the first keys == tau in index order
-//     are gathered and ranked.
-#define SEL_CMAX 256
+// key j of lane l: (j/4)*256 + 4*l + j%4, so keys are read with 16-byte loads;
+// slots past E hold key 0, below every real key).
+//  1. Candidate bound: lb = K-th largest of the 128 keys formed by the two
+//     largest keys of every lane.  They are keys of distinct elements, so at
+//     least K keys are >= lb and the K selected keys all satisfy key >= lb.
+//  2. If at most CMAX keys are >= lb, they are the candidates.
+//  3. Otherwise (many equal keys) radix threshold select over the keys >= lb:
+//     4 histogram passes over 8-bit digits (most significant first, 256 LDS
+//     bins per wave) find the K-th key tau; the keys > tau and the first keys
+//     == tau in index order are the candidates (exactly K).
+//  4. The candidates are sorted by a wavefront bitonic network of 64 or 128
+//     slots (key descending, lower index first); the first K are the output.
+// For K <= 64 the bound of step 1 leaves at most a few dozen keys beyond K on
+// continuous logits; step 3 is for logits with many equal values.
+#define SEL_CMAX 128
+
+// a before b: larger key, or equal key and lower index
+__device__ __forceinline__ bool sel_better(uint32_t ka, int ia, uint32_t kb, int ib) {
+  return ka > kb || (ka == kb && ia < ib);
+}
+
+// Bitonic sort of the 64*SL slots of one wavefront (slot p = SL*lane + s) into
+// "better first" order; with IDX false the keys alone are sorted, descending.
+template <int SL, bool IDX>
+__device__ __forceinline__ void wave_bitonic(uint32_t (&k)[SL], int (&ix)[SL], int l) {
+  auto better = [](uint32_t ka, int ia, uint32_t kb, int ib) {
+    return IDX ? sel_better(ka, ia, kb, ib) : ka > kb;
+  };
+#pragma unroll
+  for (int kk = 2; kk <= 64 * SL; kk <<= 1) {
+#pragma unroll
+    for (int j = kk >> 1; j > 0; j >>= 1) {
+      if (j < SL) {
+#pragma unroll
+        for (int a = 0; a < SL; ++a) {
+          const int b = a ^ j;
+          if (b <= a) continue;
+          const bool desc = ((SL * l + a) & kk) == 0;  // a is the lower slot of the pair
+          if (desc == better(k[b], ix[b], k[a], ix[a])) {
+            const uint32_t tk = k[a]; k[a] = k[b]; k[b] = tk;
+            if (IDX) { const int ti = ix[a]; ix[a] = ix[b]; ix[b] = ti; }
+          }
+        }
+      } else {
+        const int lx = j / SL;
+#pragma unroll
+        for (int a = 0; a < SL; ++a) {
+          const uint32_t ok = (uint32_t)__shfl_xor((int)k[a], lx, 64);
+          const int oi = IDX ? __shfl_xor(ix[a], lx, 64) : 0;
+          const int p = SL * l + a;
+          const bool lower = (p & j) == 0, desc = (p & kk) == 0;
+          if ((lower == desc) != better(k[a], ix[a], ok, oi)) {
+            k[a] = ok;
+            if (IDX) ix[a] = oi;
+          }
+        }
+      }
+    }
+  }
+}
+
+// sorts the ncan candidates of one wavefront in LDS and leaves the first K
+// (key, index) in lanes 0..K-1 of (selkey, selidx)
+template <int SL>
+__device__ __forceinline__ void sel_sort_take(const uint32_t* ck, const int* ci, int ncan, int l,
+                                              uint32_t& selkey, int& selidx) {
+  uint32_t k[SL];
+  int ix[SL];
+#pragma unroll
+  for (int a = 0; a < SL; ++a) {
+    const int p = SL * l + a;
+    k[a] = p < ncan ? ck[p] : 0u;  // empty slots sort last
+    ix[a] = p < ncan ? ci[p] : 0x7fffffff;
+  }
+  wave_bitonic<SL, true>(k, ix, l);
+  // element q of the sorted order is slot q % SL of lane q / SL
+#pragma unroll
+  for (int a = 0; a < SL; ++a) {
+    const uint32_t vk = (uint32_t)__shfl((int)k[a], l / SL, 64);
+    const int vi = __shfl(ix[a], l / SL, 64);
+    if (l % SL == a) { selkey = vk; selidx = vi; }
+  }
+}
+
 template <int VPL>
 __global__ __launch_bounds__(256) void k_route_select_wave(int T, int E, int K, int S, int score,
                                                            const float* __restrict__ partial,
@@ -426,71 +500,125 @@ __global__ __launch_bounds__(256) void k_route_select_wave(int T, int E, int K, 
   const int t = blockIdx.x * 4 + w;
   if (t >= T) return;  // wave-uniform; no block-wide barrier below
   constexpr int NC = VPL / 4;
-  uint32_t key[VPL];
-  bool bad = false;
+  // logits (+ bias): every chunk's loads are issued before any is used
+  float4 v[NC];
   const bool vec = (E & 3) == 0;
+  if (vec) {
 #pragma unroll
-  for (int c = 0; c < NC; ++c) {
-    const int e0 = c * 256 + 4 * l;
-    float v[4] = {0.f, 0.f, 0.f, 0.f};
-    if (vec && e0 < E) {
-      for (int s = 0; s < S; ++s) {
-        const float4 q = *(const float4*)(partial + ((long)s * T + t) * E + e0);
-        v[0] += q.x; v[1] += q.y; v[2] += q.z; v[3] += q.w;
-      }
-    } else if (!vec) {
-      for (int s = 0; s < S; ++s)
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-          if (e0 + q < E) v[q] += partial[((long)s * T + t) * E + e0 + q];
+    for (int c = 0; c < NC; ++c) {
+      const int e0 = c * 256 + 4 * l;
+      v[c] = e0 < E ? *(const float4*)(partial + (long)t * E + e0) : float4{0.f, 0.f, 0.f, 0.f};
     }
+    for (int s = 1; s < S; ++s)
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int e = e0 + q;
-      if (e < E) {
-        if (logits_out) logits_out[(long)t * E + e] = v[q];
-        float zz = bias ? v[q] + bias[e] : v[q];
-        key[c * 4 + q] = float_key(zz);
-        if (!key_finite(key[c * 4 + q])) bad = true;
-      } else {
-        key[c * 4 + q] = 0u;
+      for (int c = 0; c < NC; ++c) {
+        const int e0 = c * 256 + 4 * l;
+        if (e0 < E) {
+          const float4 q = *(const float4*)(partial + ((long)s * T + t) * E + e0);
+          v[c].x += q.x; v[c].y += q.y; v[c].z += q.z; v[c].w += q.w;
+        }
+      }
+  } else {  // rows not 16-byte aligned
+#pragma unroll
+    for (int c = 0; c < NC; ++c) v[c] = float4{0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < S; ++s)
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        const int e0 = c * 256 + 4 * l;
+        const float* r = partial + ((long)s * T + t) * E + e0;
+        if (e0 < E) v[c].x += r[0];
+        if (e0 + 1 < E) v[c].y += r[1];
+        if (e0 + 2 < E) v[c].z += r[2];
+        if (e0 + 3 < E) v[c].w += r[3];
+      }
+  }
+  if (logits_out) {
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const int e0 = c * 256 + 4 * l;
+      float* o = logits_out + (long)t * E + e0;
+      if (vec && e0 < E) {
+        *(float4*)o = v[c];
+      } else if (!vec) {
+        if (e0 < E) o[0] = v[c].x;
+        if (e0 + 1 < E) o[1] = v[c].y;
+        if (e0 + 2 < E) o[2] = v[c].z;
+        if (e0 + 3 < E) o[3] = v[c].w;
       }
     }
   }
+  if (bias) {
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const int e0 = c * 256 + 4 * l;
+      float4 b = float4{0.f, 0.f, 0.f, 0.f};
+      if (vec && e0 < E) {
+        b = *(const float4*)(bias + e0);
+      } else if (!vec) {
+        if (e0 < E) b.x = bias[e0];
+        if (e0 + 1 < E) b.y = bias[e0 + 1];
+        if (e0 + 2 < E) b.z = bias[e0 + 2];
+        if (e0 + 3 < E) b.w = bias[e0 + 3];
+      }
+      v[c].x += b.x; v[c].y += b.y; v[c].z += b.z; v[c].w += b.w;
+    }
+  }
+  // order-preserving keys (-0 taken as +0); slots past E get 0
+  uint32_t key[VPL];
+  uint32_t emax = 0;  // largest (bits << 1): >= 0xff000000 for inf and NaN
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const float z[4] = {v[c].x, v[c].y, v[c].z, v[c].w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t u = __float_as_uint(z[q] + 0.0f);
+      const uint32_t k = u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
+      const bool in = c * 256 + 4 * l + q < E;
+      emax = max(emax, in ? u << 1 : 0u);
+      key[c * 4 + q] = in ? k : 0u;
+    }
+  }
+  const bool bad = emax >= 0xff000000u;
   if (wave_ballot(bad) != 0 && l == 0) set_err(err, MOE_DEVERR_NONFINITE);
   if (mask && mask[t]) {
     if (l < K) { ids[(long)t * K + l] = -1; probs[(long)t * K + l] = 0.f; }
     return;
   }
-  auto valid = [&](int j) { return ((j >> 2) * 256 + 4 * l + (j & 3)) < E; };
 
-  // 1. bound from the per-lane maxima (bitonic sort of 64 values, descending)
-  uint32_t m = 0;
+  // 1. bound: the K-th largest of the lanes' top-two keys (K <= 64 < 128)
+  uint32_t top[2] = {0u, 0u};
 #pragma unroll
-  for (int j = 0; j < VPL; ++j) m = (valid(j) && key[j] > m) ? key[j] : m;
+  for (int j = 0; j < VPL; ++j) {
+    top[1] = max(top[1], min(top[0], key[j]));
+    top[0] = max(top[0], key[j]);
+  }
+  {
+    int dummy[2] = {0, 0};
+    wave_bitonic<2, false>(top, dummy, l);
+  }
+  const uint32_t lbs = (uint32_t)readlane_i((int)top[(K - 1) & 1], (K - 1) >> 1);
+  const uint32_t lb = lbs > 1u ? lbs : 1u;  // at least K real keys are >= 1
+  // 2. every key >= lb (if they are few), appended in (slot, lane) order: the
+  // sort breaks ties by index, so the order is free
+  int ncand = 0;  // wave-uniform
 #pragma unroll
-  for (int k = 2; k <= 64; k <<= 1) {
-#pragma unroll
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      const uint32_t o = (uint32_t)__shfl_xor((int)m, j, 64);
-      const bool asc = (l & k) == 0, lower = (l & j) == 0;
-      m = (asc == lower) ? (m > o ? m : o) : (m < o ? m : o);
+  for (int j = 0; j < VPL; ++j) {
+    const bool c = key[j] >= lb;
+    const uint64_t b = wave_ballot(c);
+    if (b != 0) {
+      const int pos = ncand + mask_rank(b);
+      if (c && pos < SEL_CMAX) {
+        s_ckey[w][pos] = key[j];
+        s_cidx[w][pos] = (j >> 2) * 256 + 4 * l + (j & 3);
+      }
+      ncand += __popcll(b);
     }
   }
-  const uint32_t lb = (uint32_t)readlane_i((int)m, K - 1);
-  int mine = 0;
-#pragma unroll
-  for (int j = 0; j < VPL; ++j) mine += (valid(j) && key[j] >= lb);
-  const int ncand = wave_sum_i(mine);
-
-  uint32_t tau;
-  int need_eq;  // keys == tau taken (first ones in index order); keys > tau always taken
-  bool direct = ncand <= SEL_CMAX;
-  if (direct) {
-    tau = lb;  // gather every key >= lb
-    need_eq = 1 << 30;
+  int ncan;
+  if (ncand <= SEL_CMAX) {
+    ncan = ncand;
   } else {
-    // 3. radix threshold select
+    // 3. radix threshold select over the keys >= lb
     uint32_t prefix = 0, pmask = 0;
     int krem = K;
     for (int d = 3; d >= 0; --d) {
@@ -500,7 +628,7 @@ __global__ __launch_bounds__(256) void k_route_select_wave(int T, int E, int K, 
       wave_sync();
 #pragma unroll
       for (int j = 0; j < VPL; ++j)
-        if (valid(j) && (key[j] & pmask) == prefix) atomicAdd(&s_hist[w][(key[j] >> sh) & 255u], 1u);
+        if (key[j] >= lb && (key[j] & pmask) == prefix) atomicAdd(&s_hist[w][(key[j] >> sh) & 255u], 1u);
       wave_sync();
       // lane l owns bins 255-4l, 254-4l, 253-4l, 252-4l (descending)
       int c4[4], tot = 0;
@@ -514,7 +642,7 @@ __global__ __launch_bounds__(256) void k_route_select_wave(int T, int E, int K, 
         run += c4[i];
       }
       const uint64_t hb = wave_ballot(hit_bin >= 0);
-      if (hb == 0) break;  // cannot happen: the candidates always hold >= krem keys
+      if (hb == 0) break;  // cannot happen: the keys >= lb always number >= krem
       const int src = __builtin_ctzll(hb);
       const int bin = readlane_i(hit_bin, src);
       const int above = readlane_i(hit_above, src);
@@ -523,74 +651,48 @@ __global__ __launch_bounds__(256) void k_route_select_wave(int T, int E, int K, 
       pmask |= 0xffu << sh;
       wave_sync();
     }
-    tau = prefix;
-    need_eq = krem;
-  }
-
-  // gather: keys > tau (all, in index order), then keys == tau (all of them on
-  // the direct path; the first need_eq in index order on the radix path)
-  int cgt = 0;
+    const uint32_t tau = prefix;  // the K-th largest key; >= lb >= 1
+    const int need_eq = krem;     // keys == tau taken, first in index order
+    const int ngt = K - krem;     // keys > tau, at [0, ngt); then the keys == tau
+    int base = 0, eqbase = 0;
 #pragma unroll
-  for (int j = 0; j < VPL; ++j) cgt += valid(j) && key[j] > tau;
-  const int ngt_tot = wave_sum_i(cgt);
-  int base = 0, eqbase = 0;
+    for (int c = 0; c < NC; ++c) {
+      int ng = 0, neq = 0;
 #pragma unroll
-  for (int c = 0; c < NC; ++c) {
-    int ngt = 0, neq = 0;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int j = c * 4 + q;
-      const bool v = valid(j);
-      ngt += v && key[j] > tau;
-      neq += v && key[j] == tau;
-    }
-    const int igt = wave_incl_scan(ngt), ieq = wave_incl_scan(neq);
-    int pg = base + igt - ngt, pe = eqbase + ieq - neq;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int j = c * 4 + q;
-      const int e = c * 256 + 4 * l + q;
-      if (!valid(j)) continue;
-      if (key[j] > tau) {
-        const int pos = pg++;
-        if (pos < SEL_CMAX) { s_ckey[w][pos] = key[j]; s_cidx[w][pos] = e; }
-      } else if (key[j] == tau) {
-        const int er = pe++;
-        const int pos = ngt_tot + er;
-        if (er < need_eq && pos < SEL_CMAX) { s_ckey[w][pos] = key[j]; s_cidx[w][pos] = e; }
+      for (int q = 0; q < 4; ++q) {
+        ng += key[c * 4 + q] > tau;
+        neq += key[c * 4 + q] == tau;
       }
+      const int ig = wave_incl_scan(ng), ieq = wave_incl_scan(neq);
+      int pg = base + ig - ng, pe = eqbase + ieq - neq;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t kq = key[c * 4 + q];
+        const int e = c * 256 + 4 * l + q;
+        if (kq > tau) {
+          const int at = pg++;
+          if (at < SEL_CMAX) { s_ckey[w][at] = kq; s_cidx[w][at] = e; }
+        } else if (kq == tau) {
+          const int er = pe++;
+          if (er < need_eq && ngt + er < SEL_CMAX) { s_ckey[w][ngt + er] = kq; s_cidx[w][ngt + er] = e; }
+        }
+      }
+      base += readlane_i(ig, 63);
+      eqbase += readlane_i(ieq, 63);
     }
-    base += readlane_i(igt, 63);
-    eqbase += readlane_i(ieq, 63);
+    ncan = ngt + (eqbase < need_eq ? eqbase : need_eq);
+    ncan = ncan < SEL_CMAX ? ncan : SEL_CMAX;
   }
   wave_sync();
-  int ncan = ngt_tot + (eqbase < need_eq ? eqbase : need_eq);
-  ncan = ncan < SEL_CMAX ? ncan : SEL_CMAX;
 
-  // rank every candidate; ranks < K are the output positions
+  // 4. sort the candidates (at least K of them); lanes 0..K-1 take the first K
   uint32_t selkey = 0;
   int selidx = -1;
-  for (int i = l; i < ncan; i += 64) {
-    const uint32_t ki = s_ckey[w][i];
-    const int ii = s_cidx[w][i];
-    int rk = 0;
-    for (int j = 0; j < ncan; ++j) {
-      const uint32_t kj = s_ckey[w][j];
-      const int ij = s_cidx[w][j];
-      rk += (kj > ki) || (kj == ki && ij < ii);
-    }
-    if (rk < K) {
-      // stash by rank in the histogram area (free now)
-      s_hist[w][rk] = ki;
-      s_hist[w][128 + rk] = (uint32_t)ii;
-    }
-  }
-  wave_sync();
-  if (l < K) {
-    selkey = s_hist[w][l];
-    selidx = (int)s_hist[w][128 + l];
-  }
-  const float zmax = key_float(s_hist[w][0]);
+  if (ncan <= 64)
+    sel_sort_take<1>(s_ckey[w], s_cidx[w], ncan, l, selkey, selidx);
+  else
+    sel_sort_take<2>(s_ckey[w], s_cidx[w], ncan, l, selkey, selidx);
+  const float zmax = key_float((uint32_t)readlane_i((int)selkey, 0));
   const float sc = l < K ? score_of(key_float(selkey), zmax, score) : 0.f;
   const float sum = wave_sum_f(sc);
   if (l < K) {
@@ -621,6 +723,9 @@ hipError_t launch_route_select(int T, int E, int K, int S, int score, const floa
                          probs, logits_out, err);
     else if (E <= 1024)
       hipLaunchKernelGGL(k_route_select_wave<16>, g, b, 0, s, T, E, K, S, score, partial, bias, mask, ids,
+                         probs, logits_out, err);
+    else if (E <= 2560)
+      hipLaunchKernelGGL(k_route_select_wave<40>, g, b, 0, s, T, E, K, S, score, partial, bias, mask, ids,
                          probs, logits_out, err);
     else
       hipLaunchKernelGGL(k_route_select_wave<64>, g, b, 0, s, T, E, K, S, score, partial, bias, mask, ids,

@@ -168,7 +168,7 @@ def test_route_nonfinite_sets_error_bit():
 
 
 def test_route_bias_and_mask_small_and_large():
-    for E, K in ((8, 2), (256, 8)):
+    for E, K in ((8, 2), (256, 8), (1025, 4), (2304, 36)):
         T = 200
         z = torch.randn((T, E), generator=torch.Generator().manual_seed(3))
         bias = torch.randn(E, generator=torch.Generator().manual_seed(4))
