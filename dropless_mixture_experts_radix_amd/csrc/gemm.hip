@@ -63,6 +63,12 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 // EPI 0: out[row][col] = bf16(acc)                                   (N columns)
 // EPI 1: gate/up chunks of 32 columns are interleaved in B; out = k-blocked
 //        activations [N/64][capacity][32], a[row][j] = bf16(silu(gate) * up)
+// EPI 2: the router projection, one dense GEMM of the `capacity` = T token
+//        rows of x [T][Kd] with the prepared router weights [ceil(N/32)*32][Kd]
+//        (row-major, loaded like A), N = E output columns.  Every tile is cut
+//        into L pieces along k and piece q writes its fp32 partial logits to
+//        part[q][T][N]; the selection kernel sums the L partials of a token in
+//        piece order.  No expert schedule, no reduce kernel.
 // ---------------------------------------------------------------------------
 #define GB_BM 256
 #define GB_BN 256
@@ -119,9 +125,16 @@ __global__ __launch_bounds__(GB_THREADS, 1) void k_gemm_bf16(int L, int N, int K
   int32_t* s_pre = (int32_t*)(smem + 4 * GB_STAGE_BYTES);  // [L+1]
   int32_t* s_tmp = s_pre + (L + 1);                         // [8]
   const int NT = (N + GB_BN - 1) / GB_BN;
-  build_schedule(L, capacity, GB_BM, NT, offsets, s_pre, s_tmp);
   const int KT = Kd / GB_BK;
-  const SplitPlan plan = gb_split_plan(s_pre[L], gridDim.x, Kd);
+  SplitPlan plan;
+  if constexpr (EPI == 2) {  // every tile in L pieces, piece-major unit order
+    plan.dp = 0;
+    plan.S = L;
+    plan.units = (int)((capacity + GB_BM - 1) / GB_BM) * NT * L;
+  } else {
+    build_schedule(L, capacity, GB_BM, NT, offsets, s_pre, s_tmp);
+    plan = gb_split_plan(s_pre[L], gridDim.x, Kd);
+  }
   const int tid = threadIdx.x, l = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wv >> 2, wn = wv & 3;
@@ -140,7 +153,7 @@ __global__ __launch_bounds__(GB_THREADS, 1) void k_gemm_bf16(int L, int N, int K
   // one work unit: a whole tile or a split-K piece of one
   struct Unit {
     TileInfo ti;
-    int piece, k0, k1, akstep;
+    int piece, k0, k1, akstep, bkstep;
     __amdgpu_buffer_rsrc_t rA, rB;
     int va[2], vb[2];
   };
@@ -150,25 +163,45 @@ __global__ __launch_bounds__(GB_THREADS, 1) void k_gemm_bf16(int L, int N, int K
     w.piece = -1;
     w.k0 = 0;
     w.k1 = KT;
-    if (u >= plan.dp) {  // split-K piece: k steps [k0, k1), whole groups of 4
-      w.piece = u - plan.dp;
-      tile = plan.dp + w.piece / plan.S;
-      const int q = w.piece % plan.S, nq = KT / 4;
+    if constexpr (EPI == 2) {  // unit u: piece u / tiles of tile u % tiles
+      const int tiles = plan.units / plan.S;
+      const int q = u / tiles, nq = KT / 4;
+      tile = u - q * tiles;
+      w.piece = q;
       w.k0 = 4 * (q * nq / plan.S);
       w.k1 = 4 * ((q + 1) * nq / plan.S);
+      w.ti.e = 0;
+      w.ti.nt = tile % NT;
+      w.ti.row0 = (tile / NT) * GB_BM;
+      w.ti.rows = min(GB_BM, (int)capacity - w.ti.row0);
+    } else {
+      if (u >= plan.dp) {  // split-K piece: k steps [k0, k1), whole groups of 4
+        w.piece = u - plan.dp;
+        tile = plan.dp + w.piece / plan.S;
+        const int q = w.piece % plan.S, nq = KT / 4;
+        w.k0 = 4 * (q * nq / plan.S);
+        w.k1 = 4 * ((q + 1) * nq / plan.S);
+      }
+      w.ti = locate_tile(tile, L, capacity, GB_BM, NT, offsets, s_pre);
     }
-    w.ti = locate_tile(tile, L, capacity, GB_BM, NT, offsets, s_pre);
     // the unit is the same for every lane: keep it in scalar registers (the
     // buffer resources built from it are scalar operands of the loads)
     w.ti.e = __builtin_amdgcn_readfirstlane(w.ti.e);
     w.ti.row0 = __builtin_amdgcn_readfirstlane(w.ti.row0);
     w.ti.rows = __builtin_amdgcn_readfirstlane(w.ti.rows);
     w.ti.nt = __builtin_amdgcn_readfirstlane(w.ti.nt);
-    // the (expert, panel) B tile: KT blocks of [256 columns][32 k]
-    w.rB = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(B + ((long)w.ti.e * NT + w.ti.nt) * (long)KT * GB_BN * GB_BK), (short)0,
-        KT * GB_BN * GB_BK * 2, 0x00020000);
-    w.rA = EPI == 1 ? __builtin_amdgcn_make_buffer_rsrc((void*)(A + (long)w.ti.row0 * Kd), (short)0,
+    if constexpr (EPI == 2) {
+      // the router weight rows of column tile nt, [rows][Kd]; rows past the
+      // prepared ceil(N/32)*32 read as zeros
+      const int c0 = w.ti.nt * GB_BN, crows = min(GB_BN, ((N + 31) & ~31) - c0);
+      w.rB = __builtin_amdgcn_make_buffer_rsrc((void*)(B + (long)c0 * Kd), (short)0, crows * Kd * 2, 0x00020000);
+    } else {
+      // the (expert, panel) B tile: KT blocks of [256 columns][32 k]
+      w.rB = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(B + ((long)w.ti.e * NT + w.ti.nt) * (long)KT * GB_BN * GB_BK), (short)0,
+          KT * GB_BN * GB_BK * 2, 0x00020000);
+    }
+    w.rA = EPI != 0 ? __builtin_amdgcn_make_buffer_rsrc((void*)(A + (long)w.ti.row0 * Kd), (short)0,
                                                         w.ti.rows * Kd * 2, 0x00020000)
                     : __builtin_amdgcn_make_buffer_rsrc((void*)A, (short)0, (int)(KT * capacity * GB_BK * 2),
                                                         0x00020000);
@@ -177,10 +210,11 @@ __global__ __launch_bounds__(GB_THREADS, 1) void k_gemm_bf16(int L, int N, int K
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
       const int r = wv * 32 + q * 16 + drow;
-      w.va[q] = EPI == 1 ? (r * Kd + dch * 8) * 2 : ((w.ti.row0 + r) * GB_BK + dch * 8) * 2;
-      w.vb[q] = r * 64 + dch * 16;
+      w.va[q] = EPI != 0 ? (r * Kd + dch * 8) * 2 : ((w.ti.row0 + r) * GB_BK + dch * 8) * 2;
+      w.vb[q] = EPI == 2 ? (r * Kd + dch * 8) * 2 : r * 64 + dch * 16;
     }
-    w.akstep = EPI == 1 ? GB_BK * 2 : (int)(capacity * GB_BK * 2);
+    w.akstep = EPI != 0 ? GB_BK * 2 : (int)(capacity * GB_BK * 2);
+    w.bkstep = EPI == 2 ? GB_BK * 2 : GB_BN * GB_BK * 2;
     return w;
   };
 
@@ -191,7 +225,7 @@ __global__ __launch_bounds__(GB_THREADS, 1) void k_gemm_bf16(int L, int N, int K
       lds_dma_b128(lds0 + (ST) * GB_STAGE_BYTES + (wv * 2 + (Q)) * 1024, (W).va[Q], (W).rA, kq * (W).akstep); \
     else                                                                                    \
       lds_dma_b128(lds0 + (ST) * GB_STAGE_BYTES + 16384 + (wv * 2 + (Q) - 2) * 1024, (W).vb[(Q) - 2], (W).rB, \
-                   kq * (GB_BN * GB_BK * 2));                                               \
+                   kq * (W).bkstep);                                                        \
   }
 // the ring prologue of a unit: its steps k0 .. k0+2 into stages 0..2
 #define GB_PROLOGUE(W)                                                                      \
@@ -278,7 +312,22 @@ __global__ __launch_bounds__(GB_THREADS, 1) void k_gemm_bf16(int L, int N, int K
       cu = setup(u);
       GB_PROLOGUE(cu);
     }
-    if (done.piece < 0) {
+    if constexpr (EPI == 2) {
+      // fp32 partial logits of piece q: part[q][T][N]
+      float* dst = part + (long)done.piece * capacity * N;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int row = wm * 128 + i * 32 + 8 * (v >> 2) + 4 * g + (v & 3);
+          if (row >= done.ti.rows) continue;
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            const int col = done.ti.nt * GB_BN + wn * 64 + j * 32 + r32;
+            if (col < N) dst[(long)(done.ti.row0 + row) * N + col] = acc[i][j][v];
+          }
+        }
+    } else if (done.piece < 0) {
       store_tile<EPI, 4>(acc, 0, done.ti, N, capacity, wm, wn, g, r32, out);
     } else {
       // partial tile, per wavefront [i][j][lane][16 values of the MFMA D layout]
@@ -448,6 +497,33 @@ static size_t gemm_bf16_lds(int L) {
 }
 
 size_t grouped_mlp_bf16_part_bytes() { return (size_t)GEMM_SPLIT_UNITS * GB_PART_FLOATS * sizeof(float); }
+
+// Pieces along k of the router projection GEMM for T tokens, E experts and H
+// (a multiple of 128): enough units to give every CU one, at most 16 and at
+// most one 4-step group per piece.
+int router_gemm_pieces(int T, int E, int H) {
+  const long tiles = (long)((T + GB_BM - 1) / GB_BM) * ((E + GB_BN - 1) / GB_BN);
+  if (tiles <= 0 || H % 128 != 0) return 0;
+  long S = (num_cus() + tiles - 1) / tiles;
+  S = S < 16 ? S : 16;
+  S = S < H / 128 ? S : H / 128;
+  return (int)(S > 1 ? S : 1);
+}
+
+hipError_t launch_router_gemm_bf16(int T, int E, int H, int S, const bf16_t* x, const bf16_t* wp, float* partial,
+                                   hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  static bool attr_done = false;
+  if (!attr_done) {
+    (void)hipFuncSetAttribute((const void*)k_gemm_bf16<2>, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    attr_done = true;
+  }
+  const long units = (long)((T + GB_BM - 1) / GB_BM) * ((E + GB_BN - 1) / GB_BN) * S;
+  const int G = (int)(units < num_cus() ? units : num_cus());
+  hipLaunchKernelGGL(k_gemm_bf16<2>, dim3(G), dim3(GB_THREADS), gemm_bf16_lds(S), s, S, E, H, (int64_t)T, x,
+                     (const int32_t*)nullptr, wp, (bf16_t*)nullptr, partial);
+  return hipGetLastError();
+}
 
 hipError_t launch_grouped_mlp_bf16(int L, int H, int F, int64_t capacity, const bf16_t* x,
                                    const int32_t* offsets, const bf16_t* w1p, const bf16_t* w2p,

@@ -56,7 +56,8 @@ int moe_prepare_router(const void* w_router, int w_dtype, int x_dtype, int H, in
 size_t moe_route_workspace_bytes(int T, int E, int H, int x_dtype) {
   if (T <= 0 || E <= 0) return 0;
   const RouteSplit sp = route_split(T, E, H > 0 ? H : 64, x_dtype);
-  return round_up((size_t)sp.S * T * E * sizeof(float), 256);
+  const int S = sp.S > sp.Sg ? sp.S : sp.Sg;  // either projection may run (it depends on the weights' type)
+  return round_up((size_t)S * T * E * sizeof(float), 256);
 }
 
 int moe_route_topk(int T, int E, int K, int H, int score, int x_dtype, int w_dtype, const void* x,
@@ -94,10 +95,17 @@ int moe_route_topk(int T, int E, int K, int H, int score, int x_dtype, int w_dty
                                             logits_out, err, s));
   if (from_x) {
     float* ws = (float*)workspace;
-    hipError_t e = launch_router_proj(T, E, H, x_dtype, w_dtype, x, w_prepared, ws, s);
+    const RouteSplit sp = route_split(T, E, H, x_dtype);
+    hipError_t e;
+    if (x_dtype == MOE_BF16 && w_dtype == MOE_BF16 && sp.Sg > 0) {
+      e = launch_router_gemm_bf16(T, E, H, sp.Sg, (const bf16_t*)x, (const bf16_t*)w_prepared, ws, s);
+      S = sp.Sg;
+    } else {
+      e = launch_router_proj(T, E, H, x_dtype, w_dtype, x, w_prepared, ws, s);
+      S = sp.S;
+    }
     if (e != hipSuccess) return MOE_ERR_LAUNCH;
     partial = ws;
-    S = route_split(T, E, H, x_dtype).S;
   }
   return launch_status(launch_route_select(T, E, K, S, score, partial, bias, mask, ids, probs,
                                            logits_out, err, s));

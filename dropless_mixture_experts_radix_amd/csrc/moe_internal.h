@@ -141,11 +141,15 @@ __device__ __forceinline__ uint32_t mx_e4m3x4(uint32_t p0, uint32_t p1, int E) {
 namespace moe {
 
 struct RouteSplit {
-  int S;         // number of H chunks (partial logit sets)
+  int S;         // number of H chunks (partial logit sets) of the wavefront projection
   int Hc;        // chunk length
   int C;         // prepared router rows (multiple of 32)
+  int Sg;        // pieces of the GEMM projection (bf16 x and weights), 0: not used
 };
 RouteSplit route_split(int T, int E, int H, int x_dtype);
+int router_gemm_pieces(int T, int E, int H);
+hipError_t launch_router_gemm_bf16(int T, int E, int H, int S, const bf16_t* x, const bf16_t* wp, float* partial,
+                                   hipStream_t s);
 
 hipError_t launch_prepare_router(const void* w, int w_dtype, int x_dtype, int H, int E, void* out,
                                  hipStream_t s);

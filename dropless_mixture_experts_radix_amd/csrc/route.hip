@@ -20,7 +20,11 @@ RouteSplit route_split(int T, int E, int H, int x_dtype) {
   r.S = 1;
   r.Hc = H;
   r.C = 0;
+  r.Sg = 0;
   if (x_dtype != MOE_BF16) return r;
+  // bf16 weights and at least 128 experts: the projection is one dense GEMM on
+  // the grouped GEMM's matrix-core pipeline (256 x 256 tiles, pieces along H)
+  if (E >= 128 && H % 128 == 0) r.Sg = router_gemm_pieces(T, E, H);
   const int ttiles = (T + 63) / 64;
   const int ctiles = (E + 31) / 32;  // the split depends on (T, E, H) only
   long waves = (long)ttiles * ctiles;

@@ -119,6 +119,27 @@ def test_route_small_router_from_x(E, K, H, wdt, T):
     _check_route(ids, probs, lo, T, K, "softmax", bias.numpy(), mask.numpy())
 
 
+@pytest.mark.parametrize("E,K,H,T", [(160, 6, 640, 1000), (300, 8, 1152, 777), (256, 8, 128, 100),
+                                     (4096, 64, 256, 300)])
+def test_route_gemm_projection(E, K, H, T):
+    """bf16 router weights with at least 128 experts: the projection runs as a
+    dense matrix-core GEMM in pieces along H.  Ragged token tiles, expert counts
+    that leave part of a 256-column tile (or a second one) empty, H that splits
+    into uneven pieces or a single one, bias and mask."""
+    g = torch.Generator().manual_seed(E * 1000 + H + T)
+    x = torch.randn((T, H), generator=g).to(torch.bfloat16)
+    w = (torch.randn((H, E), generator=g) * 0.05).to(torch.bfloat16)
+    bias = torch.randn(E, generator=g) * 0.1
+    mask = (torch.arange(T) % 9 == 4).to(torch.uint8)
+    say("route gemm projection", E, K, H, T)
+    ids, probs, lo, err = _route_gpu(T, E, K, D.SIGMOID, x=x.to(DEV), w_router=w.to(DEV), bias=bias.to(DEV),
+                                     mask=mask.to(DEV))
+    assert err == 0
+    want = O.router_logits(to_numpy_f64(x), to_numpy_f64(w))
+    assert rel_inf(lo, want) <= TOL["logits"]
+    _check_route(ids, probs, lo, T, K, "sigmoid", bias.numpy(), mask.numpy())
+
+
 @pytest.mark.parametrize("T", [2048, 8192])
 def test_route_sparse_share_logits(T):
     cfg = get_config("sparse_share")
