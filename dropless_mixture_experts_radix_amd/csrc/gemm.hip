@@ -5,8 +5,8 @@
 // regions, with no device-to-host counts and no worst-case padding.
 //
 // Every workgroup builds the tile schedule from `offsets` on the device: expert
-// e owns ceil(m_e/BM) x (N/BN) output tiles (none when m_e = 0), tiles of one
-// weight panel (same expert and column tile) are consecutive, and a
+// e owns ceil(m_e/BM) x (N/BN) output tiles (none when m_e = 0), ordered in
+// groups of 4 row tiles (all column tiles of a group, row tile fastest), and a
 // persistent grid walks them.  Workgroups are assigned to the 8 XCDs in turn, so
 // workgroup b works on the virtual slot (b % 8) * (G/8) + b/8: the 32 CUs of an
 // XCD take consecutive tiles and share their A and B panels in that XCD's L2.

@@ -59,6 +59,8 @@ __device__ inline void build_schedule(int L, int64_t capacity, int BM, int NT, c
   __syncthreads();
 }
 
+#define TILE_MGROUP 4
+
 struct TileInfo {
   int e, row0, rows, nt;
 };
@@ -78,10 +80,18 @@ __device__ __forceinline__ TileInfo locate_tile(int it, int L, int64_t capacity,
   const int m = (int)(r1 - r0);
   const int mt_e = (m + BM - 1) / BM;
   const int local = it - s_pre[e];
+  // an expert's tiles go in groups of up to TILE_MGROUP row tiles: all column
+  // tiles of a group, row tile fastest, then the next group.  The 32 CUs of an
+  // XCD run 32 consecutive tiles; for an expert with many rows that is a block
+  // of 4 row tiles x 8 column tiles, whose A rows and B panels both stay in
+  // that XCD's L2, instead of one B panel with 32 row tiles of A.
+  const int g = local / (TILE_MGROUP * NT);
+  const int rem = local - g * (TILE_MGROUP * NT);
+  const int mg = min(TILE_MGROUP, mt_e - g * TILE_MGROUP);
   TileInfo ti;
   ti.e = e;
-  ti.nt = local / mt_e;
-  const int mt = local % mt_e;
+  ti.nt = rem / mg;
+  const int mt = g * TILE_MGROUP + rem % mg;
   ti.row0 = (int)r0 + mt * BM;
   ti.rows = min(BM, m - mt * BM);
   return ti;
