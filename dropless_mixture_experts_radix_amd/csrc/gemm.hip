@@ -353,44 +353,25 @@ __global__ __launch_bounds__(GB_THREADS, 1) void k_gemm_bf16(int L, int N, int K
 
 // Sum the S split-K partials of each split tile (in piece order) and apply the
 // epilogue.  Launched with the GEMM's grid size G on GEMM_SPLIT_UNITS / 2 x 8
-// workgroups of one wavefront: workgroup (b, w) handles the part of wavefront
-// w of split tile b of the plan.
+// workgroups of four wavefronts: workgroup (b, w) handles the part of GEMM
+// wavefront w of split tile b of the plan, its wavefront i row block i.
 template <int EPI>
-__global__ __launch_bounds__(64) void k_splitk_reduce(int L, int N, int Kd, int64_t capacity, int G,
-                                                      const int32_t* __restrict__ offsets,
-                                                      const float* __restrict__ part, bf16_t* __restrict__ out) {
+__global__ __launch_bounds__(256) void k_splitk_reduce(int L, int N, int Kd, int64_t capacity, int G,
+                                                       const int32_t* __restrict__ offsets,
+                                                       const float* __restrict__ part, bf16_t* __restrict__ out) {
   __shared__ int32_t s_pre[MOE_MAX_L + 1];
   __shared__ int32_t s_tmp[16];
   const int NT = (N + GB_BN - 1) / GB_BN;
   build_schedule(L, capacity, GB_BM, NT, offsets, s_pre, s_tmp);
   const int total = s_pre[L];
   const SplitPlan plan = gb_split_plan(total, G, Kd);
-  const int b = blockIdx.x >> 3, wv = blockIdx.x & 7, l = threadIdx.x;
+  const int b = blockIdx.x >> 3, wv = blockIdx.x & 7, i = threadIdx.x >> 6, l = threadIdx.x & 63;
   if (plan.S < 2 || b >= total - plan.dp) return;
   const TileInfo ti = locate_tile(plan.dp + b, L, capacity, GB_BM, NT, offsets, s_pre);
-  const float* src = part + (long)b * plan.S * GB_PART_FLOATS + wv * 8192 + l * 16;
-  f32x4 sum[8][4];
-#pragma unroll
-  for (int ij = 0; ij < 8; ++ij)
-#pragma unroll
-    for (int c = 0; c < 4; ++c) sum[ij][c] = *(const f32x4*)(src + ij * 1024 + c * 4);
-  for (int q = 1; q < plan.S; ++q) {
-    const float* sq = src + (long)q * GB_PART_FLOATS;
-#pragma unroll
-    for (int ij = 0; ij < 8; ++ij)
-#pragma unroll
-      for (int c = 0; c < 4; ++c) sum[ij][c] += *(const f32x4*)(sq + ij * 1024 + c * 4);
-  }
-  f32x16 acc[4][2];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int c = 0; c < 4; ++c)
-#pragma unroll
-        for (int t = 0; t < 4; ++t) acc[i][j][4 * c + t] = sum[i * 2 + j][c][t];
-  store_tile<EPI, 4>(acc, 0, ti, N, capacity, wv >> 2, wv & 3, l >> 5, l & 31, out);
+  if (ti.rows <= (wv >> 2) * 128 + i * 32) return;  // row block past the tile's rows
+  f32x16 acc[1][2];
+  sum_partials(part + (long)b * plan.S * GB_PART_FLOATS + wv * 8192 + i * 2048 + l * 16, plan.S, acc);
+  store_tile<EPI, 1>(acc, i, ti, N, capacity, wv >> 2, wv & 3, l >> 5, l & 31, out);
 }
 
 // ---------------------------------------------------------------------------
@@ -539,7 +520,7 @@ hipError_t launch_grouped_mlp_bf16(int L, int H, int F, int64_t capacity, const 
   const int N1 = 2 * F, N2 = H;
   const int G1 = grid_for(capacity, L, GB_BM, (N1 + GB_BN - 1) / GB_BN, 1);
   const int G2 = grid_for(capacity, L, GB_BM, (N2 + GB_BN - 1) / GB_BN, 1);
-  const dim3 rgrid(GEMM_SPLIT_UNITS / 2 * 8), rblk(64), blk(GB_THREADS);
+  const dim3 rgrid(GEMM_SPLIT_UNITS / 2 * 8), rblk(256), blk(GB_THREADS);
   hipLaunchKernelGGL(k_gemm_bf16<1>, dim3(G1), blk, lds, s, L, N1, H, capacity, x, offsets, w1p, act, part);
   hipLaunchKernelGGL(k_splitk_reduce<1>, rgrid, rblk, 0, s, L, N1, H, capacity, G1, offsets, part, act);
   hipLaunchKernelGGL(k_gemm_bf16<0>, dim3(G2), blk, lds, s, L, N2, F, capacity, act, offsets, w2p, y, part);

@@ -161,6 +161,45 @@ __device__ __forceinline__ void lds_dma_b128_if(int sel, int want, uint32_t lds_
                : "memory", "m0", "scc");
 }
 
+// Split-K partial tiles: piece q of a split tile at part + q * 65536 floats,
+// wavefront w's 128 x 64 part at w * 8192, its 32 x 32 block (i, j) at
+// (i * 2 + j) * 1024, lane l's 16 values of the MFMA D layout at l * 16.
+// sum_partials adds the S pieces of row block i of one wavefront part in
+// piece order (the result does not depend on timing); up to 4 pieces are
+// loaded before they are added.
+typedef float f32x4_p __attribute__((ext_vector_type(4)));
+typedef float f32x16_p __attribute__((ext_vector_type(16)));
+__device__ __forceinline__ void sum_partials(const float* __restrict__ src, int S, f32x16_p (&acc)[1][2]) {
+  f32x4_p sum[2][4];
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) sum[j][c] = *(const f32x4_p*)(src + j * 1024 + c * 4);
+  for (int q = 1; q < S; q += 4) {
+    f32x4_p t[4][2][4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (q + u < S)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int c = 0; c < 4; ++c) t[u][j][c] = *(const f32x4_p*)(src + (long)(q + u) * 65536 + j * 1024 + c * 4);
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (q + u < S)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int c = 0; c < 4; ++c) sum[j][c] += t[u][j][c];
+  }
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) acc[0][j][4 * c + t] = sum[j][c][t];
+}
+
 __device__ __forceinline__ int virtual_block() {
   const int G = gridDim.x, b = blockIdx.x;
   return (G % 8 == 0) ? (b % 8) * (G / 8) + b / 8 : b;

@@ -47,11 +47,12 @@ __device__ __forceinline__ SplitPlan gm_split_plan(int total, int G, int Kd) {
   return split_plan(total, G, Kd / 128);
 }
 
-// Epilogue of one wavefront's 128 x 64 part of a tile (MFMA D layout: lane l
-// holds column l%32, rows 8 (v/4) + 4 (l/32) + v%4 of each 32 x 32 block).
-// Every lane of the wavefront must call it (EPI 1 reduces across lanes).
-template <int EPI>
-__device__ __forceinline__ void mx_store_tile(const f32x16 (&acc)[4][2], const TileInfo& ti, int N, int wm, int wn,
+// Epilogue of row blocks [i0, i0+NI) of one wavefront's 128 x 64 part of a
+// tile (MFMA D layout: lane l holds column l%32, rows 8 (v/4) + 4 (l/32) + v%4
+// of each 32 x 32 block).  Every lane of the wavefront must call it (EPI 1
+// reduces across lanes).
+template <int EPI, int NI>
+__device__ __forceinline__ void mx_store_tile(const f32x16 (&acc)[NI][2], int i0, const TileInfo& ti, int N, int wm, int wn,
                                               int g, int r32, uint8_t* __restrict__ out,
                                               uint8_t* __restrict__ out_s) {
   const int col0 = ti.nt * GM_BN;
@@ -59,11 +60,11 @@ __device__ __forceinline__ void mx_store_tile(const f32x16 (&acc)[4][2], const T
   if (EPI == 0) {
     bf16_t* y = (bf16_t*)out;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if (i >= msub) continue;
+    for (int i = 0; i < NI; ++i) {
+      if (i0 + i >= msub) continue;
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int row = wm * 128 + i * 32 + 8 * (v >> 2) + 4 * g + (v & 3);
+        const int row = wm * 128 + (i0 + i) * 32 + 8 * (v >> 2) + 4 * g + (v & 3);
         if (row >= ti.rows) continue;
         const long grow = ti.row0 + row;
 #pragma unroll
@@ -77,11 +78,11 @@ __device__ __forceinline__ void mx_store_tile(const f32x16 (&acc)[4][2], const T
     const int Fh = N >> 1;
     const int jcol = (col0 >> 1) + wn * 32 + r32;  // this lane's column of a
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if (i >= msub) continue;  // uniform over the wavefront
+    for (int i = 0; i < NI; ++i) {
+      if (i0 + i >= msub) continue;  // uniform over the wavefront
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int row = wm * 128 + i * 32 + 8 * (v >> 2) + 4 * g + (v & 3);
+        const int row = wm * 128 + (i0 + i) * 32 + 8 * (v >> 2) + 4 * g + (v & 3);
         // bf16 value of a, then the amax of its MX block (the 32 lanes of this half)
         const uint32_t ab = f32_to_bf16(silu_mul(acc[i][0][v], acc[i][1][v]));
         uint32_t am = ab & 0x7fffu;
@@ -299,7 +300,7 @@ __global__ __launch_bounds__(GM_THREADS, 1) void k_gemm_mx(int L, int N, int Kd,
       GM_PROLOGUE(cu);
     }
     if (done.piece < 0) {
-      mx_store_tile<EPI>(acc, done.ti, N, wm, wn, g, r32, out, out_s);
+      mx_store_tile<EPI, 4>(acc, 0, done.ti, N, wm, wn, g, r32, out, out_s);
     } else {
       // partial tile, per wavefront [i][j][lane][16 values of the MFMA D layout]
       float* dst = part + (long)done.piece * GM_PART_FLOATS + wv * 8192 + l * 16;
@@ -324,45 +325,27 @@ __global__ __launch_bounds__(GM_THREADS, 1) void k_gemm_mx(int L, int N, int Kd,
 }
 
 // Sum the S split-K partials of each split tile (in piece order) and apply the
-// epilogue; workgroup (b, w) of one wavefront handles wavefront w's part of
-// split tile b of the plan of a GEMM launched with G workgroups.
+// epilogue; workgroup (b, w) of four wavefronts handles GEMM wavefront w's
+// part of split tile b of the plan of a GEMM launched with G workgroups, its
+// wavefront i row block i.
 template <int EPI>
-__global__ __launch_bounds__(64) void k_mx_splitk_reduce(int L, int N, int Kd, int64_t capacity, int G,
-                                                         const int32_t* __restrict__ offsets,
-                                                         const float* __restrict__ part, uint8_t* __restrict__ out,
-                                                         uint8_t* __restrict__ out_s) {
+__global__ __launch_bounds__(256) void k_mx_splitk_reduce(int L, int N, int Kd, int64_t capacity, int G,
+                                                          const int32_t* __restrict__ offsets,
+                                                          const float* __restrict__ part, uint8_t* __restrict__ out,
+                                                          uint8_t* __restrict__ out_s) {
   __shared__ int32_t s_pre[MOE_MAX_L + 1];
   __shared__ int32_t s_tmp[16];
   const int NT = (N + GM_BN - 1) / GM_BN;
   build_schedule(L, capacity, GM_BM, NT, offsets, s_pre, s_tmp);
   const int total = s_pre[L];
   const SplitPlan plan = gm_split_plan(total, G, Kd);
-  const int b = blockIdx.x >> 3, wv = blockIdx.x & 7, l = threadIdx.x;
+  const int b = blockIdx.x >> 3, wv = blockIdx.x & 7, i = threadIdx.x >> 6, l = threadIdx.x & 63;
   if (plan.S < 2 || b >= total - plan.dp) return;
   const TileInfo ti = locate_tile(plan.dp + b, L, capacity, GM_BM, NT, offsets, s_pre);
-  const float* src = part + (long)b * plan.S * GM_PART_FLOATS + wv * 8192 + l * 16;
-  f32x4 sum[8][4];
-#pragma unroll
-  for (int ij = 0; ij < 8; ++ij)
-#pragma unroll
-    for (int c = 0; c < 4; ++c) sum[ij][c] = *(const f32x4*)(src + ij * 1024 + c * 4);
-  for (int q = 1; q < plan.S; ++q) {
-    const float* sq = src + (long)q * GM_PART_FLOATS;
-#pragma unroll
-    for (int ij = 0; ij < 8; ++ij)
-#pragma unroll
-      for (int c = 0; c < 4; ++c) sum[ij][c] += *(const f32x4*)(sq + ij * 1024 + c * 4);
-  }
-  f32x16 acc[4][2];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int c = 0; c < 4; ++c)
-#pragma unroll
-        for (int t = 0; t < 4; ++t) acc[i][j][4 * c + t] = sum[i * 2 + j][c][t];
-  mx_store_tile<EPI>(acc, ti, N, wv >> 2, wv & 3, l >> 5, l & 31, out, out_s);
+  if (ti.rows <= (wv >> 2) * 128 + i * 32) return;  // row block past the tile's rows
+  f32x16 acc[1][2];
+  sum_partials(part + (long)b * plan.S * GM_PART_FLOATS + wv * 8192 + i * 2048 + l * 16, plan.S, acc);
+  mx_store_tile<EPI, 1>(acc, i, ti, N, wv >> 2, wv & 3, l >> 5, l & 31, out, out_s);
 }
 
 size_t grouped_mlp_mx_part_bytes() { return (size_t)GEMM_SPLIT_UNITS * GM_PART_FLOATS * sizeof(float); }
@@ -387,7 +370,7 @@ hipError_t launch_grouped_mlp_mx(int L, int H, int F, int64_t capacity, const ui
     return (int)(gsz > 0 ? gsz : 1);
   };
   const int G1 = grid(2 * F), G2 = grid(H);
-  const dim3 rgrid(GEMM_SPLIT_UNITS / 2 * 8), rblk(64), blk(GM_THREADS);
+  const dim3 rgrid(GEMM_SPLIT_UNITS / 2 * 8), rblk(256), blk(GM_THREADS);
   hipLaunchKernelGGL(k_gemm_mx<1>, dim3(G1), blk, lds, s, L, 2 * F, H, capacity, x, xs, offsets, w1p, w1s, act,
                      act_s, part);
   hipLaunchKernelGGL(k_mx_splitk_reduce<1>, rgrid, rblk, 0, s, L, 2 * F, H, capacity, G1, offsets, part, act, act_s);
