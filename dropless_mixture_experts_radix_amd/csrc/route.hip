@@ -298,27 +298,30 @@ __global__ __launch_bounds__(64) void k_route_select_small(int T, int E, int K, 
 }
 
 // Fused projection + selection for a small router (bf16 x, all P*E prepared
-// rows in one 32-row tile): a workgroup of 8 wavefronts takes 16 tokens; each
-// wavefront computes the 16 x 32 logit tile over its eighth of H on
-// v_mfma_f32_16x16x32_bf16 (two 16-column tiles); the eight partial tiles are
+// rows in one 32-row tile): a workgroup of RF_WAVES wavefronts takes 16
+// tokens; each wavefront computes the 16 x 32 logit tile over its share of H
+// on v_mfma_f32_16x16x32_bf16 (two 16-column tiles); the partial tiles are
 // summed in LDS in wavefront order, the P terms of each expert in term order,
 // and one thread per token selects.  No partial logits go through HBM.  With
 // the 16-row instruction four lanes share a token row, so one 16-byte-per-lane
-// load covers 64 contiguous bytes of each of 16 rows.
+// load covers 64 contiguous bytes of each of 16 rows.  The prepared rows past
+// P*E are zero and are not read.
+#define RF_WAVES 16
 template <int EMAX>
-__global__ __launch_bounds__(512) void k_route_fused_small(int T, int E, int K, int H, int P, int score,
+__global__ __launch_bounds__(64 * RF_WAVES) void k_route_fused_small(int T, int E, int K, int H, int P, int score,
                                                            const bf16_t* __restrict__ x,
                                                            const bf16_t* __restrict__ wp,
                                                            const float* __restrict__ bias,
                                                            const uint8_t* __restrict__ mask,
                                                            int16_t* __restrict__ ids, float* __restrict__ probs,
                                                            float* __restrict__ logits_out, int32_t* err) {
-  __shared__ float s_part[8][16][33];
+  __shared__ float s_part[RF_WAVES][16][33];
   const int w = threadIdx.x >> 6, l = threadIdx.x & 63, q = l >> 4, r = l & 15;
   const int t0 = blockIdx.x * 16;
   const int ra = min(t0 + r, T - 1);
+  const int PE = P * E;  // prepared rows in use
   // 32-wide k slices of this wavefront: [k0s, k1s)
-  const int nks = H / 32, per = (nks + 7) / 8;
+  const int nks = H / 32, per = (nks + RF_WAVES - 1) / RF_WAVES;
   const int k0s = min(w * per, nks), k1s = min(k0s + per, nks);
   // lane (q, r): token row r (A) or prepared rows r and 16 + r (B), k = 8q..8q+7 of a slice
   const bf16_t* pa = x + (long)ra * H + 8 * q;
@@ -333,8 +336,8 @@ __global__ __launch_bounds__(512) void k_route_fused_small(int T, int E, int K, 
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       a[u] = *(const bf16x8*)(pa + (ks + u) * 32);
-      b0[u] = *(const bf16x8*)(pw0 + (ks + u) * 32);
-      b1[u] = *(const bf16x8*)(pw1 + (ks + u) * 32);
+      b0[u] = r < PE ? *(const bf16x8*)(pw0 + (ks + u) * 32) : bf16x8{};
+      b1[u] = 16 + r < PE ? *(const bf16x8*)(pw1 + (ks + u) * 32) : bf16x8{};
     }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -345,8 +348,8 @@ __global__ __launch_bounds__(512) void k_route_fused_small(int T, int E, int K, 
   }
   for (; ks < k1s; ++ks) {
     const bf16x8 a = *(const bf16x8*)(pa + ks * 32);
-    const bf16x8 b0 = *(const bf16x8*)(pw0 + ks * 32);
-    const bf16x8 b1 = *(const bf16x8*)(pw1 + ks * 32);
+    const bf16x8 b0 = r < PE ? *(const bf16x8*)(pw0 + ks * 32) : bf16x8{};
+    const bf16x8 b1 = 16 + r < PE ? *(const bf16x8*)(pw1 + ks * 32) : bf16x8{};
     acc[0][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b0, acc[0][0], 0, 0, 0);
     acc[0][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b1, acc[0][1], 0, 0, 0);
   }
@@ -358,14 +361,14 @@ __global__ __launch_bounds__(512) void k_route_fused_small(int T, int E, int K, 
     for (int i = 0; i < 4; ++i) s_part[w][4 * q + i][16 * c + r] = v[i];
   }
   __syncthreads();
-  // sum the eight partial tiles in wavefront order (one value per thread)
+  // sum the partial tiles in wavefront order (one value per thread)
   {
-    const int row = threadIdx.x >> 5, col = threadIdx.x & 31;
+    const int row = (threadIdx.x >> 5) & 15, col = threadIdx.x & 31;
     float v = 0.f;
 #pragma unroll
-    for (int u = 0; u < 8; ++u) v += s_part[u][row][col];
+    for (int u = 0; u < RF_WAVES; ++u) v += s_part[u][row][col];
     __syncthreads();
-    s_part[0][row][col] = v;
+    if (threadIdx.x < 512) s_part[0][row][col] = v;
   }
   __syncthreads();
   const int t = t0 + threadIdx.x;
@@ -392,7 +395,7 @@ hipError_t launch_route_fused(int T, int E, int K, int H, int score, int w_dtype
                               float* logits_out, int32_t* err, hipStream_t s) {
   if (T == 0) return hipSuccess;
   const int P = router_terms(w_dtype);
-  const dim3 g((T + 15) / 16), b(512);
+  const dim3 g((T + 15) / 16), b(64 * RF_WAVES);
   if (E <= 8)
     hipLaunchKernelGGL(k_route_fused_small<8>, g, b, 0, s, T, E, K, H, P, score, (const bf16_t*)x,
                        (const bf16_t*)wp, bias, mask, ids, probs, logits_out, err);

@@ -104,7 +104,7 @@ def test_route_fused_projection_workloads(cfgname, T):
 def test_route_small_router_from_x(E, K, H, wdt, T):
     """Small routers from bf16 rows (one workgroup per 32 tokens sums the H
     split across its wavefronts): ragged token tail, H that does not split
-    evenly over 8 wavefronts, K = E, bf16 and fp32 router weights, bias and mask."""
+    evenly over the wavefronts, K = E, bf16 and fp32 router weights, bias and mask."""
     g = torch.Generator().manual_seed(E * 1000 + H)
     x = torch.randn((T, H), generator=g).to(torch.bfloat16)
     w = (torch.randn((H, E), generator=g) * 0.05).to(wdt)
