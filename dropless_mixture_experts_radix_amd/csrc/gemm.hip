@@ -234,12 +234,14 @@ __global__ __launch_bounds__(GB_THREADS, 1) void k_gemm_bf16(int L, int N, int K
       _Pragma("unroll") for (int q = 0; q < 4; ++q) GB_DMA(W, st, min((W).k0 + st, (W).k1 - 1), q); \
     }                                                                                       \
   }
-#define GB_READ(FA, FB, ST, FR)                                                             \
+#define GB_READ(FA, FB, ST, FR, NB)                                                         \
   {                                                                                         \
     const uint8_t* pa = smem + (ST) * GB_STAGE_BYTES + wm * 8192 + (FR);                    \
     const uint8_t* pb = smem + (ST) * GB_STAGE_BYTES + 16384 + wn * 4096 + (FR);            \
-    _Pragma("unroll") for (int i = 0; i < 4; ++i) FA[i] = *(const bf16x8*)(pa + i * 2048); \
-    _Pragma("unroll") for (int j = 0; j < 2; ++j) FB[j] = *(const bf16x8*)(pb + j * 2048); \
+    _Pragma("unroll") for (int i = 0; i < (NB); ++i) FA[i] = *(const bf16x8*)(pa + i * 2048); \
+    if ((NB) > 0) {                                                                         \
+      _Pragma("unroll") for (int j = 0; j < 2; ++j) FB[j] = *(const bf16x8*)(pb + j * 2048); \
+    }                                                                                       \
   }
 #define GB_MMA1(FA, FB, T)                                                                  \
   acc[(T) >> 1][(T) & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(FA[(T) >> 1], FB[(T) & 1], acc[(T) >> 1][(T) & 1], 0, 0, 0);
@@ -275,32 +277,36 @@ __global__ __launch_bounds__(GB_THREADS, 1) void k_gemm_bf16(int L, int N, int K
     // step kt while group 0 reads step kt+1.  The stage of step kt+1 is complete
     // for all wavefronts at the barrier that starts group 0's memory phase of
     // step kt+1.
-#define GB_KLOOP(MM)                                                                        \
+#define GB_KLOOP(NB)                                                                        \
   for (int kt = k0; kt < k1; kt += 4) {                                                     \
     _Pragma("unroll") for (int h = 0; h < 4; ++h) {                                         \
-      GB_READ(fa[0], fb[0], h, fr0);                                                        \
-      GB_READ(fa[1], fb[1], h, fr1);                                                        \
+      GB_READ(fa[0], fb[0], h, fr0, NB);                                                    \
+      GB_READ(fa[1], fb[1], h, fr1, NB);                                                    \
       {                                                                                     \
         const int kn = min(kt + h + 3, k1 - 1);                                             \
         _Pragma("unroll") for (int q = 0; q < 4; ++q) GB_DMA(cu, (h + 3) & 3, kn, q);      \
       }                                                                                     \
       asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory");              \
       GB_FENCE;                                                                             \
-      if (MM) {                                                                             \
-        _Pragma("unroll") for (int t = 0; t < 8; ++t) { GB_MMA1(fa[0], fb[0], t); }         \
-        _Pragma("unroll") for (int t = 0; t < 8; ++t) { GB_MMA1(fa[1], fb[1], t); }         \
+      _Pragma("unroll") for (int t = 0; t < 8; ++t) {                                       \
+        if ((t >> 1) < (NB)) GB_MMA1(fa[0], fb[0], t);                                       \
+      }                                                                                     \
+      _Pragma("unroll") for (int t = 0; t < 8; ++t) {                                       \
+        if ((t >> 1) < (NB)) GB_MMA1(fa[1], fb[1], t);                                       \
       }                                                                                     \
       GB_FENCE;                                                                             \
       asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");                          \
     }                                                                                       \
   }
-    // in a tile of at most 128 rows (the short last tile of an expert) the
-    // second group has no rows: it only reads and loads, and its compute
-    // phases are empty.  Both loop versions have the same loads and barriers.
-    if (cu.ti.rows > wm * 128) {
-      GB_KLOOP(1);
-    } else {
-      GB_KLOOP(0);
+    // a wavefront reads fragments for and multiplies only the 32-row blocks of
+    // its 128 rows that hold rows of the tile (the short last tile of an
+    // expert); all versions of the loop have the same loads and barriers
+    switch (min(4, max(0, (cu.ti.rows - wm * 128 + 31) / 32))) {
+      case 4: GB_KLOOP(4); break;
+      case 3: GB_KLOOP(3); break;
+      case 2: GB_KLOOP(2); break;
+      case 1: GB_KLOOP(1); break;
+      default: GB_KLOOP(0); break;
     }
 #undef GB_KLOOP
     if (!gp) asm volatile("s_barrier" ::: "memory");
