@@ -213,11 +213,11 @@ __global__ __launch_bounds__(GM_THREADS, 1) void k_gemm_mx(int L, int N, int Kd,
     }                                                                                       \
   }
 // fragments and scale bytes of stage KS_ (in ring stage ST)
-#define GM_READ(ST, KS_)                                                                    \
-  {                                                                                         \
+#define GM_READ(ST, KS_, NB)                                                                \
+  if ((NB) > 0) {                                                                           \
     const uint8_t* pa = smem + (ST) * GM_STAGE_BYTES + wm * 8192;                           \
     const uint8_t* pb = smem + (ST) * GM_STAGE_BYTES + 16384 + wn * 4096;                   \
-    _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                         \
+    _Pragma("unroll") for (int i = 0; i < (NB); ++i) {                                      \
       const u32x4 lo = *(const u32x4*)(pa + i * 2048 + fr0);                                \
       const u32x4 hi = *(const u32x4*)(pa + i * 2048 + fr1);                                \
       fa[i] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]}; \
@@ -229,7 +229,7 @@ __global__ __launch_bounds__(GM_THREADS, 1) void k_gemm_mx(int L, int N, int Kd,
     }                                                                                       \
     const int ks = (KS_);                                                                   \
     const uint8_t* ps = smem + GM_LDS_SCALES + ((ks >> 3) & 1) * GM_SGROUP_BYTES + (ks & 7) * 2 + g; \
-    _Pragma("unroll") for (int i = 0; i < 4; ++i) sa[i] = ps[(wm * 128 + i * 32 + r32) * 16]; \
+    _Pragma("unroll") for (int i = 0; i < (NB); ++i) sa[i] = ps[(wm * 128 + i * 32 + r32) * 16]; \
     _Pragma("unroll") for (int j = 0; j < 2; ++j) sb[j] = ps[GM_SGROUP_HALF + (wn * 64 + j * 32 + r32) * 16]; \
   }
 #define GM_MMA1(T)                                                                          \
@@ -264,10 +264,10 @@ __global__ __launch_bounds__(GM_THREADS, 1) void k_gemm_mx(int L, int N, int Kd,
     // it.  The vmcnt(8) waits allow the two younger stages' 8 loads in flight;
     // where a scale load is among them the wait is one load stronger than
     // needed.
-#define GM_KLOOP(MM)                                                                        \
+#define GM_KLOOP(NB)                                                                        \
   for (int kt = k0; kt < k1; kt += 4) {                                                     \
     _Pragma("unroll") for (int h = 0; h < 4; ++h) {                                         \
-      GM_READ(h, kt + h);                                                                   \
+      GM_READ(h, kt + h, NB);                                                               \
       {                                                                                     \
         const int kn = min(kt + h + 3, k1 - 1);                                             \
         GM_SDMA_IF(cu, min(((kt + h) >> 3) + 1, NG - 1), (kt + h) & 7, 5);                  \
@@ -275,19 +275,22 @@ __global__ __launch_bounds__(GM_THREADS, 1) void k_gemm_mx(int L, int N, int Kd,
       }                                                                                     \
       asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory");              \
       GM_FENCE;                                                                             \
-      if (MM) {                                                                             \
-        _Pragma("unroll") for (int t = 0; t < 8; ++t) { GM_MMA1(t); }                       \
+      _Pragma("unroll") for (int t = 0; t < 8; ++t) {                                       \
+        if ((t >> 1) < (NB)) GM_MMA1(t);                                                     \
       }                                                                                     \
       GM_FENCE;                                                                             \
       asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");                          \
     }                                                                                       \
   }
-    // in a tile of at most 128 rows the second group has no rows: it only
-    // reads and loads.  Both loop versions have the same loads and barriers.
-    if (cu.ti.rows > wm * 128) {
-      GM_KLOOP(1);
-    } else {
-      GM_KLOOP(0);
+    // a wavefront reads fragments for and multiplies only the 32-row blocks of
+    // its 128 rows that hold rows of the tile; all versions of the loop have
+    // the same loads and barriers
+    switch (min(4, max(0, (cu.ti.rows - wm * 128 + 31) / 32))) {
+      case 4: GM_KLOOP(4); break;
+      case 3: GM_KLOOP(3); break;
+      case 2: GM_KLOOP(2); break;
+      case 1: GM_KLOOP(1); break;
+      default: GM_KLOOP(0); break;
     }
 #undef GM_KLOOP
     if (!gp) asm volatile("s_barrier" ::: "memory");
