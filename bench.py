@@ -34,6 +34,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-mx", action="store_true", help="skip the MXFP8 variant")
+    ap.add_argument("--no-other", action="store_true", help="skip the other full-size workloads")
+    ap.add_argument("--workload", choices=["dsv3_bf16", "sparse_share"], default=None,
+                    help="time only this other workload (its layer and grouped MLP) and print its line")
     ap.add_argument("--cpu-tokens", type=int, default=4096, help="tokens in the CPU oracle sample")
     return ap.parse_args()
 
@@ -48,7 +51,8 @@ def build(cfgname):
     x = make_tokens(cfg).cuda()
     r = make_router_inputs(cfg)
     layer = D.MoELayer(cfg.T, cfg.H, cfg.E, cfg.K, cfg.F, dt[cfg.dtype], dt[cfg.x_dtype], L=cfg.local, e0=cfg.e0,
-                       score=D.SIGMOID if cfg.score == "sigmoid" else D.SOFTMAX, w_router=r["w_router"].cuda(),
+                       score=D.SIGMOID if cfg.score == "sigmoid" else D.SOFTMAX,
+                       w_router=None if r["w_router"] is None else r["w_router"].cuda(),
                        bias=None if r["bias"] is None else r["bias"].cuda())
     for e in range(cfg.local):
         w1, w2 = make_expert_weights(cfg, cfg.e0 + e, device="cuda")
@@ -91,6 +95,35 @@ def time_stages(layer, x, reps):
         torch.cuda.synchronize()
         acc += [ev[i].elapsed_time(ev[i + 1]) for i in range(4)]
     return acc / reps * 1000.0  # us
+
+
+def time_stages_graph(layer, x, reps):
+    """Per-stage GPU times without host launch gaps: each stage captured
+    `inner` times back to back in one HIP graph (same stream), the graph
+    replayed `reps` times between two events."""
+    stages = [(lambda: layer.route(x=x), 20), (lambda: layer.permute(x), 20), (layer.mlp, 2), (layer.combine, 20)]
+    out = []
+    for fn, inner in stages:
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            for _ in range(inner):
+                fn()
+        torch.cuda.synchronize()
+        for _ in range(2):
+            g.replay()
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for _ in range(reps):
+            g.replay()
+        t1.record()
+        torch.cuda.synchronize()
+        out.append(t0.elapsed_time(t1) / (reps * inner) * 1000.0)
+        del g
+    return np.array(out)  # us
 
 
 def time_graph(layer, x, reps):
@@ -217,12 +250,60 @@ def mx_variant(steps, warmup):
     return out
 
 
+def other_workload(name, steps, warmup):
+    """Layer time of another full-size workload of the method (not the metric's
+    configuration): the DeepSeek-like layer (256 experts, Zipf-skewed loads,
+    sigmoid scores) and the sparse large-top-K share (32 of 2304 experts, K=36,
+    routed from given logits with masked tokens)."""
+    cfg, layer, x, r = build(name)
+    logits = None if r["logits"] is None else r["logits"].cuda()
+    mask = None if r["mask"] is None else r["mask"].cuda()
+
+    def fwd():
+        layer.forward(x, logits=logits, mask=mask)
+
+    for _ in range(warmup):
+        fwd()
+    torch.cuda.synchronize()
+    s = torch.cuda.current_stream()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(s)
+    for _ in range(steps):
+        fwd()
+    t1.record(s)
+    torch.cuda.synchronize()
+    us = t0.elapsed_time(t1) / steps * 1000.0
+    N = int(layer.offsets[-1].item())
+    flops = 6.0 * N * cfg.H * cfg.F
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record(s)
+    for _ in range(steps):
+        layer.mlp()
+    ev[1].record(s)
+    torch.cuda.synchronize()
+    mlp_us = ev[0].elapsed_time(ev[1]) / steps * 1000.0
+    out = {"workload": f"{name}: T={cfg.T} H={cfg.H} E={cfg.E} local={cfg.local} K={cfg.K} F={cfg.F}",
+           "layer_us": round(us, 2), "grouped_mlp_us": round(mlp_us, 2), "routed_rows": N,
+           "grouped_gemm_tflops": round(flops / (mlp_us * 1e-6) / 1e12, 1)}
+    del layer, x
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     a = parse()
     if a.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {a.gpus} is not supported (this build has no multi-GPU "
               f"path)", file=sys.stderr)
         sys.exit(2)
+    if a.workload:
+        line = other_workload(a.workload, a.steps, a.warmup)
+        line.update({"metric": "MoE layer us (" + a.workload + ")", "value": line["layer_us"], "unit": "us",
+                     "n_gpus": 1, "steps": a.steps, "warmup": a.warmup, "higher_is_better": False,
+                     "dtype": "bf16", "data": "synthetic"})
+        print(json.dumps(line), flush=True)
+        return
     calibration_copy()
     cfg, layer, x, r = build("mixtral_bf16")
     layer.forward(x)
@@ -230,10 +311,12 @@ def main():
     N = int(layer.offsets[-1].item())
     torch.cuda.synchronize()
     ms = time_steps(layer, x, a.steps, a.warmup)
-    st = time_stages(layer, x, 20)
+    st_eager = time_stages(layer, x, 20)
+    st = time_stages_graph(layer, x, 5)
     gus = time_graph(layer, x, a.steps)
     route_b, permute_b, combine_b, flops = algorithmic(cfg, N)
-    t_route, t_perm, t_mlp, t_comb = st
+    t_route, t_perm, t_comb = st[0], st[1], st[3]
+    t_mlp = st_eager[2]  # events on the launch stream around the call
     tflops = flops / (t_mlp * 1e-6) / 1e12
     line = {
         "metric": "MoE layer us; grouped-GEMM TFLOPS + permute/combine GB/s, 1 MI355X",
@@ -252,6 +335,10 @@ def main():
                                "fp32 router", "tokens": cfg.T, "routed_rows": N},
         "stage_us": {"route": round(t_route, 2), "permute": round(t_perm, 2), "grouped_mlp": round(t_mlp, 2),
                      "combine": round(t_comb, 2)},
+        "stage_us_note": "route/permute/combine: GPU time per call from HIP-graph replays of 20 back-to-back "
+                         "calls; grouped_mlp: events around the eager call",
+        "stage_us_eager": {k: round(float(v), 2) for k, v in
+                           zip(["route", "permute", "grouped_mlp", "combine"], st_eager)},
         "graph_replay_us": round(gus, 2),
         "grouped_gemm_tflops": round(tflops, 1),
         "route_gbs": round(route_b / (t_route * 1e-6) / 1e9, 1),
@@ -275,6 +362,15 @@ def main():
             line["mxfp8"] = {"error": repr(ex)}
     if not a.no_cpu:
         line["cpu_baseline"] = cpu_baseline(cfg, layer, x, r, a.cpu_tokens)
+    if not a.no_other:
+        del layer, x
+        torch.cuda.empty_cache()
+        line["other_workloads"] = []
+        for name in ("dsv3_bf16", "sparse_share"):
+            try:
+                line["other_workloads"].append(other_workload(name, 10, 3))
+            except Exception as ex:  # report, do not hide the main line
+                line["other_workloads"].append({"workload": name, "error": repr(ex)})
     print(json.dumps(line), flush=True)
 
 

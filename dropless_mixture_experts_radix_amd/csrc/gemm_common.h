@@ -98,11 +98,11 @@ __device__ __forceinline__ TileInfo locate_tile(int it, int L, int64_t capacity,
 }
 
 // ---------------------------------------------------------------------------
-// Work units of a persistent grid of G workgroups over `total` tiles of KT k
-// steps: the first floor(total/G)*G tiles run whole; when the `left` tiles of
-// the last, partial round number at most GEMM_SPLIT_UNITS/2, each is split
-// into S >= 2 pieces along k (at most GEMM_SPLIT_UNITS pieces, at most 16 per
-// tile, each piece at least one pair of k steps).
+// Work units of a persistent grid of G workgroups over `total` tiles of 2*KT
+// k steps (KT pairs): the first floor(total/G)*G tiles run whole; when the
+// `left` tiles of the last, partial round number at most GEMM_SPLIT_UNITS/2,
+// each is split into S >= 2 pieces along k (at most GEMM_SPLIT_UNITS pieces,
+// at most 16 per tile, each piece at least 8 whole groups of 4 k steps).
 // ---------------------------------------------------------------------------
 #define GEMM_SPLIT_UNITS 256
 
@@ -116,7 +116,9 @@ __device__ __forceinline__ SplitPlan split_plan(int total, int G, int KT) {
   SplitPlan p;
   const int left = total % G;
   p.dp = total - left;
-  int S = left > 0 ? min(min(G, GEMM_SPLIT_UNITS) / left, KT / 2) : 1;
+  // pieces of at least 8 groups of 4 k steps: shorter pieces cost more in
+  // partial-tile traffic and the reduce than they save
+  int S = left > 0 ? min(min(G, GEMM_SPLIT_UNITS) / left, KT / 16) : 1;
   S = min(S, 16);
   if (S < 2) {
     p.dp = total;

@@ -130,11 +130,17 @@ __global__ __launch_bounds__(1024) void k_scan(int ntiles, int L, int64_t capaci
       int base = 0;
       for (int p = 0; p < part; ++p) base += s_part[p * Lb + e];
       const int t0 = part * per, t1 = min(ntiles, t0 + per);
-      for (int t = t0; t < t1; ++t) {
-        const long i = (long)t * L + eb + e;
-        const int c = hist[i];
-        hist[i] = base;
-        base += c;
+      // 16 tiles at a time: all their loads are issued before the in-place
+      // stores, which the compiler could not move the next loads across
+      for (int tb = t0; tb < t1; tb += 16) {
+        int c[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) c[u] = tb + u < t1 ? hist[(long)(tb + u) * L + eb + e] : 0;
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+          if (tb + u < t1) hist[(long)(tb + u) * L + eb + e] = base;
+          base += c[u];
+        }
       }
       if (part == nparts - 1) s_tot[eb + e] = base;
     }

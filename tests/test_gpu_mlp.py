@@ -166,10 +166,10 @@ def test_grouped_mlp_f32(counts, H, F):
     ([70, 300, 0, 5], 384, 128),          # partial column tiles in both GEMMs
     ([0, 0, 0, 0], 256, 256),             # no rows at all
     ([2048], 512, 512),
-    # 8192 routed rows over 8 experts on a 256-CU grid: the tiles of the last,
-    # partial round are split along k (second GEMM: 576 tiles, 64 split in 4
-    # uneven k ranges; first GEMM: 1152 tiles, 128 split in 2)
-    (MIXTRAL_COUNTS, 4096, 640),
+    # 8192 routed rows over 8 experts (36 row tiles) on a 256-CU grid: the 72
+    # tiles of a partial round are split along k into 3 uneven pieces (first
+    # GEMM: k = 3584, 28 groups of 4 steps; second GEMM: k = 4096, 32 groups)
+    (MIXTRAL_COUNTS, 3584, 256),
     (MIXTRAL_COUNTS, 512, 4096),
 ])
 def test_grouped_mlp_bf16(counts, H, F):
@@ -181,8 +181,9 @@ def test_grouped_mlp_bf16(counts, H, F):
     ([900, 24, 0, 513], 1024, 1536),
     ([70, 300, 0, 5], 768, 256),          # partial column tiles in both GEMMs
     ([0, 0, 0, 0], 256, 256),             # no rows at all
-    # the tiles of a last, partial round split along k (as in the bf16 cases)
-    (MIXTRAL_COUNTS, 4096, 768),
+    # the 72 tiles of a partial round split along k into 2 pieces (first GEMM:
+    # k = 4096; second GEMM: k = 4096)
+    (MIXTRAL_COUNTS, 4096, 256),
     (MIXTRAL_COUNTS, 512, 4096),
 ])
 def test_grouped_mlp_mxfp8(counts, H, F):
