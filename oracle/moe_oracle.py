@@ -24,6 +24,7 @@ is computed here by plain definitions:
                         oracle for the pins)
   count_and_permute     stable counting sort of the valid local routes
   mx_quantize_rows      OCP Microscaling (MX) v1.0 block quantization, E4M3
+  mx4_quantize_rows     the same with E2M1 (MXFP4) elements
   grouped_mlp           per-expert dense SwiGLU MLP in float64
   combine               probability-weighted sum in k order
 
@@ -180,6 +181,102 @@ def mx_dequantize_rows(codes, scales) -> np.ndarray:
     return (vals * s[:, :, None]).reshape(R, C)
 
 
+# OCP 4-bit floating point E2M1 (OCP MX v1.0, FP4 element): 1 sign bit, 2
+# exponent bits with bias 1, 1 mantissa bit, no infinities or NaN.  Magnitudes
+# 0, 0.5 (the one subnormal), 1, 1.5, 2, 3, 4, 6; largest normal 6 = 1.5 * 2^2,
+# smallest normal 1 = 2^0.
+E2M1_MAX = 6.0
+E2M1_EMIN = 0
+E2M1_MBITS = 1
+E2M1_EMAX_ELEM = 2  # exponent of the largest normal
+
+
+def e2m1_decode(codes) -> np.ndarray:
+    """E2M1 codes (low 4 bits of each byte) -> float64 values."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64) & 15
+    s = np.where((c >> 3) & 1, -1.0, 1.0)
+    ex = (c >> 1) & 3
+    m = c & 1
+    sub = np.ldexp(m / 2.0, E2M1_EMIN)
+    nrm = np.ldexp(1.0 + m / 2.0, ex - 1)
+    return s * np.where(ex == 0, sub, nrm)
+
+
+def e2m1_round(q) -> np.ndarray:
+    """Round float64 values to the E2M1 grid, ties to even, saturating at +-6.
+
+    The spacing near |q| is 2^(max(floor(log2|q|), 0) - 1); magnitudes that
+    round above 6 are clamped to 6 (the MX conversion saturates).  The sign of
+    zero is kept."""
+    q = np.asarray(q, dtype=np.float64)
+    nz = q != 0
+    e = np.maximum(_floor_log2(np.where(nz, q, 1.0)), E2M1_EMIN)
+    quantum = np.ldexp(1.0, (e - E2M1_MBITS).astype(np.int64))
+    r = np.round(q / quantum) * quantum
+    r = np.where(np.abs(r) > E2M1_MAX, np.copysign(E2M1_MAX, q), r)
+    r = np.where(nz, r, q)
+    return np.where((r == 0) & np.signbit(q), -0.0, r)
+
+
+def e2m1_encode(r) -> np.ndarray:
+    """Exact E2M1 grid values (from e2m1_round) -> codes 0..15 (uint8)."""
+    r = np.asarray(r, dtype=np.float64)
+    sign = np.signbit(r).astype(np.int64) << 3
+    a = np.abs(r)
+    code = np.where(a == 0.5, 1, 0).astype(np.int64)
+    nrm = a >= 1.0
+    e = _floor_log2(np.where(nrm, a, 1.0))
+    man = np.round((np.where(nrm, a, 1.0) / np.ldexp(1.0, e) - 1.0) * 2).astype(np.int64)
+    code = np.where(nrm, ((e + 1) << 1) | man, code)
+    return (code | sign).astype(np.uint8)
+
+
+def mx4_quantize_rows(v):
+    """MXFP4: quantize each row of v (bf16 values as float64) in blocks of 32.
+
+    The OCP MX v1.0 conversion with E2M1 elements: per block of 32 consecutive
+    elements along the row, E = floor(log2(max|v|)) - 2 (2 = exponent of
+    E2M1's largest normal), clamped to [-127, 127] (E = -127 for an all-zero
+    block); each element is v * 2^-E rounded to E2M1 (nearest, ties to even,
+    saturating at 6).  Returns (codes uint8 [R,C] holding one 4-bit code each,
+    scales uint8 [R,C/32] holding E + 127).  pack_fp4 gives the two-per-byte
+    storage form."""
+    v = np.asarray(v, dtype=np.float64)
+    R, C = v.shape
+    if C % MX_BLOCK:
+        raise ValueError("row length must be a multiple of 32")
+    blk = v.reshape(R, C // MX_BLOCK, MX_BLOCK)
+    amax = np.abs(blk).max(axis=2)
+    E = np.where(amax > 0, _floor_log2(np.where(amax > 0, amax, 1.0)) - E2M1_EMAX_ELEM, -127)
+    E = np.clip(E, -127, 127)
+    q = blk * np.ldexp(1.0, -E)[:, :, None]  # exact: a power-of-two scaling
+    codes = e2m1_encode(e2m1_round(q)).reshape(R, C)
+    scales = (E + 127).astype(np.uint8)
+    return codes, scales
+
+
+def mx4_dequantize_rows(codes, scales) -> np.ndarray:
+    codes = np.asarray(codes)
+    R, C = codes.shape
+    vals = e2m1_decode(codes).reshape(R, C // MX_BLOCK, MX_BLOCK)
+    s = np.ldexp(1.0, np.asarray(scales).astype(np.int64) - 127)
+    return (vals * s[:, :, None]).reshape(R, C)
+
+
+def pack_fp4(codes) -> np.ndarray:
+    """[R,C] codes 0..15 -> [R,C/2] bytes, element 2i in the low nibble."""
+    c = np.asarray(codes, dtype=np.uint8)
+    return (c[:, 0::2] & 15) | ((c[:, 1::2] & 15) << 4)
+
+
+def unpack_fp4(packed) -> np.ndarray:
+    p = np.asarray(packed, dtype=np.uint8)
+    out = np.empty((p.shape[0], p.shape[1] * 2), np.uint8)
+    out[:, 0::2] = p & 15
+    out[:, 1::2] = p >> 4
+    return out
+
+
 # ---------------------------------------------------------------------------
 # Route: projection, score, top-K, probabilities
 # ---------------------------------------------------------------------------
@@ -322,7 +419,7 @@ def swiglu(h, F):
 def round_to(v, dtype):
     if dtype == "f32":
         return np.asarray(v, np.float64).astype(np.float32).astype(np.float64)
-    if dtype in ("bf16", "mxfp8"):
+    if dtype in ("bf16", "mxfp8", "mxfp4"):
         return bf16_round(v)
     if dtype == "f64":
         return np.asarray(v, np.float64)
@@ -334,23 +431,26 @@ def expert_mlp(X, W1e, W2e, dtype):
 
     dtype "f32"/"bf16": h = X.W1e (float64), a = swiglu(h) stored in dtype,
     y = a.W2e stored in dtype.
-    dtype "mxfp8": X, W1e (per column, along H), a (after bf16 rounding,
-    along F) and W2e (per column, along F) are MX-quantized and dequantized
-    exactly before each float64 product; y is stored as bf16.
+    dtype "mxfp8" / "mxfp4": X, W1e (per column, along H), a (after bf16
+    rounding, along F) and W2e (per column, along F) are MX-quantized (E4M3 /
+    E2M1 elements) and dequantized exactly before each float64 product; y is
+    stored as bf16.
     Returns (y, a_stored) with a_stored the activations as stored before GEMM2
-    (bf16 values for mxfp8, before their quantization).
+    (bf16 values for the MX types, before their quantization).
     """
     X = np.asarray(X, np.float64)
     W1e = np.asarray(W1e, np.float64)
     W2e = np.asarray(W2e, np.float64)
     F = W2e.shape[0]
-    if dtype == "mxfp8":
-        Xq = mx_dequantize_rows(*mx_quantize_rows(X))
-        W1q = mx_dequantize_rows(*mx_quantize_rows(W1e.T)).T
+    if dtype in ("mxfp8", "mxfp4"):
+        quant, dequant = ((mx_quantize_rows, mx_dequantize_rows) if dtype == "mxfp8"
+                          else (mx4_quantize_rows, mx4_dequantize_rows))
+        Xq = dequant(*quant(X))
+        W1q = dequant(*quant(W1e.T)).T
         h = Xq @ W1q
         a = bf16_round(swiglu(h, F))
-        aq = mx_dequantize_rows(*mx_quantize_rows(a))
-        W2q = mx_dequantize_rows(*mx_quantize_rows(W2e.T)).T
+        aq = dequant(*quant(a))
+        W2q = dequant(*quant(W2e.T)).T
         y = bf16_round(aq @ W2q)
         return y, a
     h = X @ W1e

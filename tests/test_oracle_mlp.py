@@ -119,3 +119,33 @@ def test_mxfp8_on_grid_values_equals_unquantized_path():
     np.testing.assert_array_equal(a_mx, a)
     aq = O.mx_dequantize_rows(*O.mx_quantize_rows(a))
     np.testing.assert_array_equal(y_mx, O.bf16_round(aq @ w2))
+
+
+def test_mxfp4_on_grid_values_equals_unquantized_path():
+    """Inputs whose every 32-block lies on the E2M1 grid at its own MX scale
+    quantize exactly; the MXFP4 expert MLP then equals the bf16 one fed the
+    same values except for the quantization of `a`."""
+    rng = np.random.default_rng(6)
+    grid = O.e2m1_decode(np.arange(1, 8, dtype=np.uint8))  # 0.5 .. 6
+
+    def on_grid(shape):
+        v = rng.choice(grid, size=shape) * rng.choice([-1.0, 1.0], size=shape)
+        v.reshape(-1, 32)[:, 0] = 6.0  # fix every block's scale at 2^0
+        return v
+
+    T, H, F = 8, 64, 64
+    x = on_grid((T, H)) * 2.0 ** -3
+    w1 = on_grid((2 * F, H)).T * 2.0 ** -6
+    w2 = on_grid((H, F)).T * 2.0 ** -6
+    for m in (x, w1.T, w2.T):
+        c, s = O.mx4_quantize_rows(m)
+        np.testing.assert_array_equal(O.mx4_dequantize_rows(c, s), m)
+    y_mx, a_mx = O.expert_mlp(x, w1, w2, "mxfp4")
+    h = x @ w1
+    a = O.bf16_round(O.swiglu(h, F))
+    np.testing.assert_array_equal(a_mx, a)
+    aq = O.mx4_dequantize_rows(*O.mx4_quantize_rows(a))
+    np.testing.assert_array_equal(y_mx, O.bf16_round(aq @ w2))
+    # the quantized activations differ from the exact ones by at most half a
+    # step of their block
+    assert np.abs(aq - a).max() <= np.abs(a).max() / 4

@@ -141,3 +141,89 @@ def test_mx_special_blocks():
 def test_mx_row_length_must_be_block_multiple():
     with pytest.raises(ValueError):
         O.mx_quantize_rows(np.zeros((2, 33)))
+
+
+# ---------------------------------------------------------------------------
+# MXFP4: E2M1 elements (OCP MX v1.0 FP4), same E8M0 block scale
+# ---------------------------------------------------------------------------
+
+def test_e2m1_decode_matches_spec_values():
+    g = json.load(open(os.path.join(GOLD, "e2m1_reference_values.json")))
+    for code, val in g["e2m1"].items():
+        d = O.e2m1_decode(np.array([int(code, 16)], np.uint8))[0]
+        assert d == val and math.copysign(1, d) == math.copysign(1, val), code
+    assert O.E2M1_MAX == g["e2m1_max_normal"] and O.E2M1_EMAX_ELEM == g["e2m1_emax"]
+
+
+def test_e2m1_encode_roundtrips_every_code():
+    codes = np.arange(16, dtype=np.uint8)
+    np.testing.assert_array_equal(O.e2m1_encode(O.e2m1_decode(codes)), codes)
+
+
+def _nearest_e2m1(q):
+    """Brute force: nearest E2M1 value to q over all 16 codes (ties -> even
+    code, the sign of q kept for zeros), magnitudes above 6 going to +-6."""
+    codes = np.arange(16, dtype=np.uint8)
+    vals = O.e2m1_decode(codes)
+    d = np.abs(vals[None, :] - np.clip(q, -6.0, 6.0)[:, None])
+    cand = d == d.min(axis=1, keepdims=True)
+    sign_ok = np.signbit(vals)[None, :] == np.signbit(q)[:, None]
+    even = (codes % 2 == 0)[None, :]
+    return codes[np.argmax(cand * (4 + 2 * sign_ok + even), axis=1)]
+
+
+def test_e2m1_round_against_bruteforce():
+    # every midpoint and grid value, dense values around them, beyond +-6
+    mids = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0])
+    grid = O.e2m1_decode(np.arange(8, dtype=np.uint8))
+    q = np.concatenate([mids, grid, np.linspace(0, 9, 90001), mids + 1e-9, mids - 1e-9,
+                        [7.0, 100.0, 1e30]])
+    q = np.concatenate([q, -q])
+    np.testing.assert_array_equal(O.e2m1_encode(O.e2m1_round(q)), _nearest_e2m1(q))
+    # the ties go to the even code: 0.25 -> 0, 0.75 -> 1.0, 1.25 -> 1.0, 1.75 -> 2,
+    # 2.5 -> 2, 3.5 -> 4, 5 -> 4
+    np.testing.assert_array_equal(O.e2m1_round(mids), [0.0, 1.0, 1.0, 2.0, 2.0, 4.0, 4.0])
+
+
+def test_mx4_random_blocks_against_bruteforce():
+    rng = np.random.default_rng(12)
+    raw = rng.standard_normal((3000, 64)) * np.exp(rng.uniform(-30, 30, size=(3000, 1)))
+    v = O.bf16_round(raw)
+    codes, scales = O.mx4_quantize_rows(v)
+    for row, blk in ((0, 0), (17, 1), (2999, 1)):
+        amax = max(abs(float(t)) for t in v[row, 32 * blk:32 * blk + 32])
+        assert scales[row, blk] == math.frexp(amax)[1] - 1 - 2 + 127
+    E = scales.astype(np.int64) - 127
+    q = v.reshape(3000, 2, 32) * np.ldexp(1.0, -E)[:, :, None]
+    np.testing.assert_array_equal(codes.ravel(), _nearest_e2m1(q.ravel()))
+    # every block's largest magnitude maps to 4 or 6 (amax / 2^E lies in [4, 8))
+    mags = O.e2m1_decode(codes & 7).reshape(3000, 2, 32).max(axis=2)
+    assert np.isin(mags, [4.0, 6.0]).all()
+    # dequantization error: half a step (0.25 * 2^E below 2, 1 * 2^E at 4..6)
+    # plus what saturation at 6 * 2^E removes
+    dq = O.mx4_dequantize_rows(codes, scales)
+    sc = np.ldexp(1.0, E).repeat(32, axis=1)
+    bound = np.maximum(0.25 * sc, np.abs(v) / 4) + np.maximum(0.0, np.abs(v) - 6 * sc)
+    assert (np.abs(dq - v) <= bound).all()
+
+
+def test_mx4_special_blocks_and_packing():
+    c, s = O.mx4_quantize_rows(np.ones((1, 32)))      # 1 = 1.0 * 2^-2 * 4: code 4 -> 4.0 at 2^-2
+    assert s.tolist() == [[125]] and (c == 0x6).all()
+    c, s = O.mx4_quantize_rows(np.zeros((1, 32)))
+    assert s.tolist() == [[0]] and (c == 0).all()
+    c, _ = O.mx4_quantize_rows(-np.zeros((1, 32)))
+    assert (c == 0x8).all()
+    blk = np.zeros((1, 32))
+    blk[0, :4] = [7.5, -7.5, 5.0, 0.2]                  # E = 0: 7.5 saturates to 6, 5 ties to 4
+    c, s = O.mx4_quantize_rows(blk)
+    assert s[0, 0] == 127 and c[0, :4].tolist() == [0x7, 0xF, 0x6, 0x0]
+    # values on the E2M1 grid at their block scale come back exactly
+    grid = O.e2m1_decode(np.arange(16, dtype=np.uint8))
+    blk = np.tile(grid, (3, 2)) * np.array([[2.0 ** -9], [1.0], [2.0 ** 20]])
+    c, s = O.mx4_quantize_rows(blk)
+    np.testing.assert_array_equal(O.mx4_dequantize_rows(c, s), blk)
+    # packing: element 2i in the low nibble
+    p = O.pack_fp4(np.array([[1, 2, 0xF, 0x3]], np.uint8))
+    assert p.tolist() == [[0x21, 0x3F]]
+    np.testing.assert_array_equal(O.unpack_fp4(p), [[1, 2, 0xF, 0x3]])
