@@ -10,7 +10,7 @@ import os
 
 import torch
 
-F32, BF16, MXFP8 = 0, 1, 2
+F32, BF16, MXFP8, MXFP4 = 0, 1, 2, 3
 SOFTMAX, SIGMOID = 0, 1
 DEVERR_BAD_ID, DEVERR_OVERFLOW, DEVERR_NONFINITE = 1, 2, 4
 MAX_K, MAX_E, MAX_L = 64, 4096, 2048

@@ -1,24 +1,30 @@
-// MXFP8 ragged grouped GEMMs of the expert SwiGLU MLP.
+// MX (MXFP8 and MXFP4) ragged grouped GEMMs of the expert SwiGLU MLP.
 //
 // bpdata article, "Transformer Engine building blocks for dropless MoE in JAX":
 // group-aware MXFP8 quantization and an MXFP8 grouped GEMM for the expert
 // matmuls ("Optimization 1: Grouped GEMM": MXFP8 block scaling).  Operands are
-// OCP MX E4M3 codes with one E8M0 scale per 32 consecutive contraction
-// elements; the CDNA4 instruction v_mfma_scale_f32_32x32x64_f8f6f4 applies the
-// scales inside the matrix core (fp32 accumulation).
+// OCP MX codes (E4M3 bytes, or E2M1 nibbles two per byte) with one E8M0 scale
+// per 32 consecutive contraction elements; the CDNA4 instruction
+// v_mfma_scale_f32_32x32x64_f8f6f4 applies the scales inside the matrix core
+// (fp32 accumulation).
 //
 // Lane layout of one 32x32x64 instruction (checked on the hardware): lane
-// l = 32g + r holds row/column r; its bytes 0..15 are k = 16g..16g+15 (scale
-// block 0) and bytes 16..31 are k = 32+16g..32+16g+15 (scale block 1); its scale
-// operand is the scale of block g of row/column r.
+// l = 32g + r holds row/column r and its scale operand is the scale of block g
+// of row/column r.  E4M3: its bytes 0..15 are k = 16g..16g+15 (block 0) and
+// bytes 16..31 are k = 32+16g..32+16g+15 (block 1).  E2M1 (format code 4):
+// only its first 16 bytes are read, and all 32 nibbles belong to block g, so a
+// lane takes the 16 code bytes of block g as they lie in memory.
 //
 // Structure as in the bf16 kernel: 256 x 256 output tiles, 8 wavefronts of
-// 128 x 64, a k step of 128 codes (two instructions) moves the same 64 KiB as a
-// bf16 k step (a 256 x 128-byte A and B tile) through registers into padded
-// LDS rows of 144 bytes, plus the 4 scale bytes of each of the 512 rows.  A is
-// row-major codes [rows][Kd] with scales [rows][Kd/32]; B is the prepared
-// weight panel, k-blocked codes [Kd/128][256][128] and scales [Kd/128][256][4].
-// The tiles of a last, partial round of the CUs are split along k and summed by
+// 128 x 64, a ring of 4 LDS stages filled by LDS DMA, two groups of wavefronts
+// one phase apart.  A stage holds 64 code bytes of each of the 256 A and 256 B
+// rows: 64 E4M3 elements (2 blocks, one instruction per 32 x 32 block) or 128
+// E2M1 elements (4 blocks, two instructions).  A is row-major codes with
+// scales [rows][Kd/32]; B is the prepared weight panel, codes k-blocked by
+// stage [Kd/stage][256][64 bytes] and scales [ceil(Kd/512)][256][16].  The 16
+// scale bytes of a row and 512-wide k group (8 E4M3 or 4 E2M1 stages) travel
+// in one 16-byte DMA granule into a double-buffered LDS scale ring.  The tiles
+// of a last, partial round of the CUs are split along k and summed by
 // k_mx_splitk_reduce in a fixed order (the split plan of the bf16 kernel).
 // EPI 1 (GEMM1): a = silu(gate) * up is rounded to bf16 and MX-quantized along
 // F in the epilogue (one 32-column gate chunk = one MX block of a row).
@@ -42,16 +48,16 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 #define GM_SGROUP_BYTES (2 * GM_SGROUP_HALF)  // A then B
 #define GM_PART_FLOATS (GM_BM * GM_BN)
 
-// split plan of the MX kernel: pieces are whole groups of 4 stages
-__device__ __forceinline__ SplitPlan gm_split_plan(int total, int G, int Kd) {
-  return split_plan(total, G, Kd / 128);
+// split plan of the MX kernel over KT stages: pieces are whole groups of 4
+__device__ __forceinline__ SplitPlan gm_split_plan(int total, int G, int KT) {
+  return split_plan(total, G, KT / 2);
 }
 
 // Epilogue of row blocks [i0, i0+NI) of one wavefront's 128 x 64 part of a
 // tile (MFMA D layout: lane l holds column l%32, rows 8 (v/4) + 4 (l/32) + v%4
 // of each 32 x 32 block).  Every lane of the wavefront must call it (EPI 1
 // reduces across lanes).
-template <int EPI, int NI>
+template <int EPI, int NI, bool FP4>
 __device__ __forceinline__ void mx_store_tile(const f32x16 (&acc)[NI][2], int i0, const TileInfo& ti, int N, int wm, int wn,
                                               int g, int r32, uint8_t* __restrict__ out,
                                               uint8_t* __restrict__ out_s) {
@@ -91,18 +97,30 @@ __device__ __forceinline__ void mx_store_tile(const f32x16 (&acc)[NI][2], int i0
           const uint32_t x = (uint32_t)__shfl_xor((int)am, o, 64);
           am = am > x ? am : x;
         }
-        const int E = mx_scale_exp(am);
-        if (row < ti.rows && jcol < Fh) {
-          const long grow = ti.row0 + row;
-          out[grow * Fh + jcol] = (uint8_t)mx_e4m3(ab, E);
-          if (r32 == 0) out_s[grow * (Fh >> 5) + (jcol >> 5)] = (uint8_t)(E + 127);
+        if (FP4) {
+          // E2M1 codes of columns 2c and 2c+1 share byte c (low nibble first)
+          const int E = mx4_scale_exp(am);
+          const uint32_t code = mx_e2m1(ab, E);
+          const uint32_t next = (uint32_t)__shfl_xor((int)code, 1, 64);
+          if (row < ti.rows && jcol < Fh) {
+            const long grow = ti.row0 + row;
+            if ((r32 & 1) == 0) out[grow * (Fh >> 1) + (jcol >> 1)] = (uint8_t)(code | (next << 4));
+            if (r32 == 0) out_s[grow * (Fh >> 5) + (jcol >> 5)] = (uint8_t)(E + 127);
+          }
+        } else {
+          const int E = mx_scale_exp(am);
+          if (row < ti.rows && jcol < Fh) {
+            const long grow = ti.row0 + row;
+            out[grow * Fh + jcol] = (uint8_t)mx_e4m3(ab, E);
+            if (r32 == 0) out_s[grow * (Fh >> 5) + (jcol >> 5)] = (uint8_t)(E + 127);
+          }
         }
       }
     }
   }
 }
 
-template <int EPI>
+template <int EPI, bool FP4>
 __global__ __launch_bounds__(GM_THREADS, 1) void k_gemm_mx(int L, int N, int Kd, int64_t capacity,
                                                            const uint8_t* __restrict__ A,
                                                            const uint8_t* __restrict__ As,
@@ -115,8 +133,11 @@ __global__ __launch_bounds__(GM_THREADS, 1) void k_gemm_mx(int L, int N, int Kd,
   int32_t* s_tmp = s_pre + (L + 1);                                          // [8]
   const int NT = (N + GM_BN - 1) / GM_BN;
   build_schedule(L, capacity, GM_BM, NT, offsets, s_pre, s_tmp);
-  const int KT = Kd / GM_BK, KB = Kd / 32, NG = (Kd + 511) / 512;
-  const SplitPlan plan = gm_split_plan(s_pre[L], gridDim.x, Kd);
+  // RB code bytes per row; KT stages of 64 bytes; SG stages per 16-block scale group
+  constexpr int SG = FP4 ? 4 : 8, LG = FP4 ? 2 : 3;
+  const int RB = FP4 ? Kd / 2 : Kd;
+  const int KT = RB / GM_BK, KB = Kd / 32, NG = (Kd + 511) / 512;
+  const SplitPlan plan = gm_split_plan(s_pre[L], gridDim.x, KT);
   const int tid = threadIdx.x, l = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wv >> 2, wn = wv & 3;
@@ -164,7 +185,7 @@ __global__ __launch_bounds__(GM_THREADS, 1) void k_gemm_mx(int L, int N, int Kd,
     const long panel = (long)w.ti.e * NT + w.ti.nt;
     w.rB = __builtin_amdgcn_make_buffer_rsrc((void*)(B + panel * KT * (GM_BN * GM_BK)), (short)0,
                                              KT * GM_BN * GM_BK, 0x00020000);
-    w.rA = __builtin_amdgcn_make_buffer_rsrc((void*)(A + (long)w.ti.row0 * Kd), (short)0, w.ti.rows * Kd,
+    w.rA = __builtin_amdgcn_make_buffer_rsrc((void*)(A + (long)w.ti.row0 * RB), (short)0, w.ti.rows * RB,
                                              0x00020000);
     if (wv < 4) {  // A scale groups: row-major [rows][Kd/32] bytes
       w.rS = __builtin_amdgcn_make_buffer_rsrc((void*)(As + (long)w.ti.row0 * KB), (short)0, w.ti.rows * KB,
@@ -180,7 +201,7 @@ __global__ __launch_bounds__(GM_THREADS, 1) void k_gemm_mx(int L, int N, int Kd,
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
       const int r = wv * 32 + q * 16 + drow;
-      w.va[q] = r * Kd + dch * 16;
+      w.va[q] = r * RB + dch * 16;
       w.vb[q] = r * GM_BK + dch * 16;
     }
     return w;
@@ -207,7 +228,7 @@ __global__ __launch_bounds__(GM_THREADS, 1) void k_gemm_mx(int L, int N, int Kd,
 // the ring prologue of a unit: the scale group of k0, then stages k0 .. k0+2
 #define GM_PROLOGUE(W)                                                                      \
   {                                                                                         \
-    GM_SDMA_IF(W, (W).k0 >> 3, 0, 0);                                                       \
+    GM_SDMA_IF(W, (W).k0 >> LG, 0, 0);                                                      \
     _Pragma("unroll") for (int st = 0; st < 3; ++st) {                                      \
       _Pragma("unroll") for (int q = 0; q < 4; ++q) GM_DMA(W, st, min((W).k0 + st, (W).k1 - 1), q); \
     }                                                                                       \
@@ -228,13 +249,30 @@ __global__ __launch_bounds__(GM_THREADS, 1) void k_gemm_mx(int L, int N, int Kd,
       fb[j] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]}; \
     }                                                                                       \
     const int ks = (KS_);                                                                   \
-    const uint8_t* ps = smem + GM_LDS_SCALES + ((ks >> 3) & 1) * GM_SGROUP_BYTES + (ks & 7) * 2 + g; \
+    const uint8_t* ps = smem + GM_LDS_SCALES + ((ks >> LG) & 1) * GM_SGROUP_BYTES + (ks & (SG - 1)) * (FP4 ? 4 : 2) + g; \
     _Pragma("unroll") for (int i = 0; i < (NB); ++i) sa[i] = ps[(wm * 128 + i * 32 + r32) * 16]; \
     _Pragma("unroll") for (int j = 0; j < 2; ++j) sb[j] = ps[GM_SGROUP_HALF + (wn * 64 + j * 32 + r32) * 16]; \
+    if (FP4) {                                                                              \
+      _Pragma("unroll") for (int i = 0; i < (NB); ++i) sa2[i] = ps[(wm * 128 + i * 32 + r32) * 16 + 2]; \
+      _Pragma("unroll") for (int j = 0; j < 2; ++j) sb2[j] = ps[GM_SGROUP_HALF + (wn * 64 + j * 32 + r32) * 16 + 2]; \
+    }                                                                                       \
   }
+// E4M3: one instruction per 32 x 32 block and stage.  E2M1: two, on the
+// fragment's first 16 bytes (blocks 0, 1 of the stage) and its last 16 bytes
+// (blocks 2, 3), each with its own scales.
 #define GM_MMA1(T)                                                                          \
-  acc[(T) >> 1][(T) & 1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(                 \
-      fa[(T) >> 1], fb[(T) & 1], acc[(T) >> 1][(T) & 1], 0, 0, 0, (int)sa[(T) >> 1], 0, (int)sb[(T) & 1]);
+  if (FP4) {                                                                                \
+    const i32x8 a_ = fa[(T) >> 1], b_ = fb[(T) & 1];                                        \
+    acc[(T) >> 1][(T) & 1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(               \
+        __builtin_shufflevector(a_, a_, 0, 1, 2, 3, 0, 1, 2, 3), __builtin_shufflevector(b_, b_, 0, 1, 2, 3, 0, 1, 2, 3), \
+        acc[(T) >> 1][(T) & 1], 4, 4, 0, (int)sa[(T) >> 1], 0, (int)sb[(T) & 1]);          \
+    acc[(T) >> 1][(T) & 1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(               \
+        __builtin_shufflevector(a_, a_, 4, 5, 6, 7, 4, 5, 6, 7), __builtin_shufflevector(b_, b_, 4, 5, 6, 7, 4, 5, 6, 7), \
+        acc[(T) >> 1][(T) & 1], 4, 4, 0, (int)sa2[(T) >> 1], 0, (int)sb2[(T) & 1]);        \
+  } else {                                                                                  \
+    acc[(T) >> 1][(T) & 1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(               \
+        fa[(T) >> 1], fb[(T) & 1], acc[(T) >> 1][(T) & 1], 0, 0, 0, (int)sa[(T) >> 1], 0, (int)sb[(T) & 1]); \
+  }
 #define GM_FENCE __builtin_amdgcn_sched_barrier(0);
 
   int u = virtual_block();
@@ -246,7 +284,7 @@ __global__ __launch_bounds__(GM_THREADS, 1) void k_gemm_mx(int L, int N, int Kd,
   while (u < plan.units) {
     const int k0 = cu.k0, k1 = cu.k1;
     i32x8 fa[4], fb[2];
-    uint32_t sa[4], sb[2];
+    uint32_t sa[4], sb[2], sa2[4], sb2[2];  // sa2, sb2: scales of blocks 2, 3 of an E2M1 stage
     f32x16 acc[4][2];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -270,7 +308,7 @@ __global__ __launch_bounds__(GM_THREADS, 1) void k_gemm_mx(int L, int N, int Kd,
       GM_READ(h, kt + h, NB);                                                               \
       {                                                                                     \
         const int kn = min(kt + h + 3, k1 - 1);                                             \
-        GM_SDMA_IF(cu, min(((kt + h) >> 3) + 1, NG - 1), (kt + h) & 7, 5);                  \
+        GM_SDMA_IF(cu, min(((kt + h) >> LG) + 1, NG - 1), (kt + h) & (SG - 1), SG - 3);     \
         _Pragma("unroll") for (int q = 0; q < 4; ++q) GM_DMA(cu, (h + 3) & 3, kn, q);      \
       }                                                                                     \
       asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory");              \
@@ -303,7 +341,7 @@ __global__ __launch_bounds__(GM_THREADS, 1) void k_gemm_mx(int L, int N, int Kd,
       GM_PROLOGUE(cu);
     }
     if (done.piece < 0) {
-      mx_store_tile<EPI, 4>(acc, 0, done.ti, N, wm, wn, g, r32, out, out_s);
+      mx_store_tile<EPI, 4, FP4>(acc, 0, done.ti, N, wm, wn, g, r32, out, out_s);
     } else {
       // partial tile, per wavefront [i][j][lane][16 values of the MFMA D layout]
       float* dst = part + (long)done.piece * GM_PART_FLOATS + wv * 8192 + l * 16;
@@ -331,7 +369,7 @@ __global__ __launch_bounds__(GM_THREADS, 1) void k_gemm_mx(int L, int N, int Kd,
 // epilogue; workgroup (b, w) of four wavefronts handles GEMM wavefront w's
 // part of split tile b of the plan of a GEMM launched with G workgroups, its
 // wavefront i row block i.
-template <int EPI>
+template <int EPI, bool FP4>
 __global__ __launch_bounds__(256) void k_mx_splitk_reduce(int L, int N, int Kd, int64_t capacity, int G,
                                                           const int32_t* __restrict__ offsets,
                                                           const float* __restrict__ part, uint8_t* __restrict__ out,
@@ -341,27 +379,28 @@ __global__ __launch_bounds__(256) void k_mx_splitk_reduce(int L, int N, int Kd, 
   const int NT = (N + GM_BN - 1) / GM_BN;
   build_schedule(L, capacity, GM_BM, NT, offsets, s_pre, s_tmp);
   const int total = s_pre[L];
-  const SplitPlan plan = gm_split_plan(total, G, Kd);
+  const SplitPlan plan = gm_split_plan(total, G, (FP4 ? Kd / 2 : Kd) / GM_BK);
   const int b = blockIdx.x >> 3, wv = blockIdx.x & 7, i = threadIdx.x >> 6, l = threadIdx.x & 63;
   if (plan.S < 2 || b >= total - plan.dp) return;
   const TileInfo ti = locate_tile(plan.dp + b, L, capacity, GM_BM, NT, offsets, s_pre);
   if (ti.rows <= (wv >> 2) * 128 + i * 32) return;  // row block past the tile's rows
   f32x16 acc[1][2];
   sum_partials(part + (long)b * plan.S * GM_PART_FLOATS + wv * 8192 + i * 2048 + l * 16, plan.S, acc);
-  mx_store_tile<EPI, 1>(acc, i, ti, N, wv >> 2, wv & 3, l >> 5, l & 31, out, out_s);
+  mx_store_tile<EPI, 1, FP4>(acc, i, ti, N, wv >> 2, wv & 3, l >> 5, l & 31, out, out_s);
 }
 
 size_t grouped_mlp_mx_part_bytes() { return (size_t)GEMM_SPLIT_UNITS * GM_PART_FLOATS * sizeof(float); }
 
-hipError_t launch_grouped_mlp_mx(int L, int H, int F, int64_t capacity, const uint8_t* x,
-                                 const uint8_t* xs, const int32_t* offsets, const uint8_t* w1p,
-                                 const uint8_t* w1s, const uint8_t* w2p, const uint8_t* w2s,
-                                 uint8_t* act, uint8_t* act_s, float* part, bf16_t* y, hipStream_t s) {
-  if (capacity == 0) return hipSuccess;
+template <bool FP4>
+static void launch_mx(int L, int H, int F, int64_t capacity, const uint8_t* x, const uint8_t* xs,
+                      const int32_t* offsets, const uint8_t* w1p, const uint8_t* w1s, const uint8_t* w2p,
+                      const uint8_t* w2s, uint8_t* act, uint8_t* act_s, float* part, bf16_t* y, hipStream_t s) {
   static bool attr_done = false;
   if (!attr_done) {
-    (void)hipFuncSetAttribute((const void*)k_gemm_mx<0>, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-    (void)hipFuncSetAttribute((const void*)k_gemm_mx<1>, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    (void)hipFuncSetAttribute((const void*)k_gemm_mx<0, FP4>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              160 * 1024);
+    (void)hipFuncSetAttribute((const void*)k_gemm_mx<1, FP4>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              160 * 1024);
     attr_done = true;
   }
   const size_t lds = (size_t)GM_LDS_SCALES + 2 * GM_SGROUP_BYTES + (size_t)(L + 1 + 16) * sizeof(int32_t);
@@ -374,13 +413,25 @@ hipError_t launch_grouped_mlp_mx(int L, int H, int F, int64_t capacity, const ui
   };
   const int G1 = grid(2 * F), G2 = grid(H);
   const dim3 rgrid(GEMM_SPLIT_UNITS / 2 * 8), rblk(256), blk(GM_THREADS);
-  hipLaunchKernelGGL(k_gemm_mx<1>, dim3(G1), blk, lds, s, L, 2 * F, H, capacity, x, xs, offsets, w1p, w1s, act,
-                     act_s, part);
-  hipLaunchKernelGGL(k_mx_splitk_reduce<1>, rgrid, rblk, 0, s, L, 2 * F, H, capacity, G1, offsets, part, act, act_s);
-  hipLaunchKernelGGL(k_gemm_mx<0>, dim3(G2), blk, lds, s, L, H, F, capacity, act, act_s, offsets, w2p, w2s,
-                     (uint8_t*)y, (uint8_t*)nullptr, part);
-  hipLaunchKernelGGL(k_mx_splitk_reduce<0>, rgrid, rblk, 0, s, L, H, F, capacity, G2, offsets, part, (uint8_t*)y,
-                     (uint8_t*)nullptr);
+  hipLaunchKernelGGL((k_gemm_mx<1, FP4>), dim3(G1), blk, lds, s, L, 2 * F, H, capacity, x, xs, offsets, w1p, w1s,
+                     act, act_s, part);
+  hipLaunchKernelGGL((k_mx_splitk_reduce<1, FP4>), rgrid, rblk, 0, s, L, 2 * F, H, capacity, G1, offsets, part,
+                     act, act_s);
+  hipLaunchKernelGGL((k_gemm_mx<0, FP4>), dim3(G2), blk, lds, s, L, H, F, capacity, act, act_s, offsets, w2p,
+                     w2s, (uint8_t*)y, (uint8_t*)nullptr, part);
+  hipLaunchKernelGGL((k_mx_splitk_reduce<0, FP4>), rgrid, rblk, 0, s, L, H, F, capacity, G2, offsets, part,
+                     (uint8_t*)y, (uint8_t*)nullptr);
+}
+
+hipError_t launch_grouped_mlp_mx(int L, int H, int F, int64_t capacity, bool fp4, const uint8_t* x,
+                                 const uint8_t* xs, const int32_t* offsets, const uint8_t* w1p,
+                                 const uint8_t* w1s, const uint8_t* w2p, const uint8_t* w2s,
+                                 uint8_t* act, uint8_t* act_s, float* part, bf16_t* y, hipStream_t s) {
+  if (capacity == 0) return hipSuccess;
+  if (fp4)
+    launch_mx<true>(L, H, F, capacity, x, xs, offsets, w1p, w1s, w2p, w2s, act, act_s, part, y, s);
+  else
+    launch_mx<false>(L, H, F, capacity, x, xs, offsets, w1p, w1s, w2p, w2s, act, act_s, part, y, s);
   return hipGetLastError();
 }
 

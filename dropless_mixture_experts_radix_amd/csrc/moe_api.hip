@@ -129,13 +129,14 @@ int moe_permute(int T, int H, int K, int E_global, int e0, int L, int64_t capaci
       L > MOE_MAX_L || e0 < 0 || e0 + L > E_global || capacity < 0)
     return MOE_ERR_SHAPE;
   if (x_dtype != MOE_BF16 && x_dtype != MOE_F32) return MOE_ERR_DTYPE;
-  if (!(out_dtype == x_dtype || (out_dtype == MOE_MXFP8 && x_dtype == MOE_BF16))) return MOE_ERR_DTYPE;
+  const bool mx_out = out_dtype == MOE_MXFP8 || out_dtype == MOE_MXFP4;
+  if (!(out_dtype == x_dtype || (mx_out && x_dtype == MOE_BF16))) return MOE_ERR_DTYPE;
   if ((x_dtype == MOE_BF16 && H % 8) || (x_dtype == MOE_F32 && H % 4)) return MOE_ERR_SHAPE;
-  if (out_dtype == MOE_MXFP8 && H % 32) return MOE_ERR_SHAPE;
+  if (mx_out && H % 32) return MOE_ERR_SHAPE;
   if (!counts || !offsets) return MOE_ERR_NULL;
   if (T > 0 && (!x || !ids || !slot_to_row)) return MOE_ERR_NULL;
   if (capacity > 0 && (!x_perm || !row_to_slot)) return MOE_ERR_NULL;
-  if (out_dtype == MOE_MXFP8 && capacity > 0 && !x_perm_scales) return MOE_ERR_NULL;
+  if (mx_out && capacity > 0 && !x_perm_scales) return MOE_ERR_NULL;
   if (!aligned16(x) || !aligned16(x_perm)) return MOE_ERR_ALIGN;
   if (!workspace || workspace_bytes < moe_permute_workspace_bytes(T, K, L)) return MOE_ERR_WORKSPACE;
   if (!aligned16(workspace)) return MOE_ERR_ALIGN;
@@ -149,18 +150,22 @@ int moe_permute(int T, int H, int K, int E_global, int e0, int L, int64_t capaci
 // ---------------------------------------------------------------------------
 size_t moe_prepared_weight_bytes(int L, int H, int F, int dtype, int which) {
   if (L <= 0 || H <= 0 || F <= 0) return 0;
-  const size_t el = dtype == MOE_F32 ? 4 : (dtype == MOE_BF16 ? 2 : 1);
-  size_t n1 = (size_t)L * 2 * F * H, n2 = (size_t)L * H * F;
+  if (dtype != MOE_F32 && dtype != MOE_BF16 && dtype != MOE_MXFP8 && dtype != MOE_MXFP4) return 0;
+  const bool mx = dtype == MOE_MXFP8 || dtype == MOE_MXFP4;
+  size_t n1 = (size_t)L * 2 * F * H, n2 = (size_t)L * H * F;  // elements
   if (dtype != MOE_F32) {  // whole 256-row panels
     n1 = (size_t)L * ((2 * (size_t)F + 255) / 256 * 256) * H;
     n2 = (size_t)L * (((size_t)H + 255) / 256 * 256) * F;
   }
+  auto bytes = [&](size_t n) {
+    return dtype == MOE_F32 ? n * 4 : dtype == MOE_BF16 ? n * 2 : dtype == MOE_MXFP8 ? n : n / 2;
+  };
   switch (which) {
-    case 1: return n1 * el;
-    case 2: return n2 * el;
+    case 1: return bytes(n1);
+    case 2: return bytes(n2);
     // MX scales: 16 bytes per prepared row and 512-wide k group
-    case 3: return dtype == MOE_MXFP8 ? n1 / H * (((size_t)H + 511) / 512) * 16 : 0;
-    case 4: return dtype == MOE_MXFP8 ? n2 / F * (((size_t)F + 511) / 512) * 16 : 0;
+    case 3: return mx ? n1 / H * (((size_t)H + 511) / 512) * 16 : 0;
+    case 4: return mx ? n2 / F * (((size_t)F + 511) / 512) * 16 : 0;
     default: return 0;
   }
 }
@@ -169,12 +174,13 @@ int moe_prepare_weights(int L, int H, int F, int in_dtype, int dtype, const void
                         void* w1p, void* w2p, uint8_t* w1p_scales, uint8_t* w2p_scales, void* stream) {
   if (L < 1 || L > MOE_MAX_L || H <= 0 || F <= 0 || H % 32 || F % 32) return MOE_ERR_SHAPE;
   if (dtype == MOE_BF16 && (H % 128 || F % 128)) return MOE_ERR_SHAPE;  // pairs of 64-wide k steps
-  if (dtype == MOE_MXFP8 && (H % 256 || F % 256)) return MOE_ERR_SHAPE;  // pairs of 128-wide k steps
+  if (dtype == MOE_MXFP8 && (H % 256 || F % 256)) return MOE_ERR_SHAPE;  // groups of 4 64-wide k stages
+  if (dtype == MOE_MXFP4 && (H % 512 || F % 512)) return MOE_ERR_SHAPE;  // groups of 4 128-wide k stages
   if (!((dtype == MOE_F32 && in_dtype == MOE_F32) || (dtype == MOE_BF16 && in_dtype == MOE_BF16) ||
-        (dtype == MOE_MXFP8 && in_dtype == MOE_BF16)))
+        ((dtype == MOE_MXFP8 || dtype == MOE_MXFP4) && in_dtype == MOE_BF16)))
     return MOE_ERR_DTYPE;
   if (!w1 || !w2 || !w1p || !w2p) return MOE_ERR_NULL;
-  if (dtype == MOE_MXFP8 && (!w1p_scales || !w2p_scales)) return MOE_ERR_NULL;
+  if ((dtype == MOE_MXFP8 || dtype == MOE_MXFP4) && (!w1p_scales || !w2p_scales)) return MOE_ERR_NULL;
   if (!aligned16(w1) || !aligned16(w2) || !aligned16(w1p) || !aligned16(w2p)) return MOE_ERR_ALIGN;
   return launch_status(launch_prepare_weights(L, H, F, dtype, w1, w2, w1p, w2p, w1p_scales, w2p_scales,
                                               (hipStream_t)stream));
@@ -188,8 +194,8 @@ size_t moe_grouped_mlp_workspace_bytes(int64_t capacity, int F, int dtype) {
   size_t a;
   if (dtype == MOE_F32) a = (size_t)capacity * F * 4;
   else if (dtype == MOE_BF16) a = round_up((size_t)capacity * F * 2, 256) + grouped_mlp_bf16_part_bytes();
-  else a = round_up((size_t)capacity * F, 256) + round_up((size_t)capacity * (F / 32), 256) +
-           grouped_mlp_mx_part_bytes();
+  else a = round_up((size_t)capacity * (dtype == MOE_MXFP4 ? F / 2 : F), 256) +
+           round_up((size_t)capacity * (F / 32), 256) + grouped_mlp_mx_part_bytes();
   return round_up(a, 256);
 }
 
@@ -208,14 +214,18 @@ int moe_grouped_mlp(int L, int H, int F, int64_t capacity, int dtype, const void
   } else if (dtype == MOE_MXFP8) {
     if (H % 256 || F % 256) return MOE_ERR_SHAPE;
     if (capacity * (int64_t)(H > F ? H : F) > (int64_t)INT32_MAX) return MOE_ERR_SHAPE;
+  } else if (dtype == MOE_MXFP4) {
+    if (H % 512 || F % 512) return MOE_ERR_SHAPE;
+    if (capacity * (int64_t)(H > F ? H : F) / 2 > (int64_t)INT32_MAX) return MOE_ERR_SHAPE;
   } else {
     return MOE_ERR_DTYPE;
   }
+  const bool mx = dtype == MOE_MXFP8 || dtype == MOE_MXFP4;
   if (!offsets) return MOE_ERR_NULL;
   if (capacity > 0 && (!x_perm || !w1p || !w2p || !y_perm)) return MOE_ERR_NULL;
-  if (dtype == MOE_MXFP8 && capacity > 0 && (!x_perm_scales || !w1p_scales || !w2p_scales)) return MOE_ERR_NULL;
+  if (mx && capacity > 0 && (!x_perm_scales || !w1p_scales || !w2p_scales)) return MOE_ERR_NULL;
   if (!aligned16(x_perm) || !aligned16(w1p) || !aligned16(w2p) || !aligned16(y_perm)) return MOE_ERR_ALIGN;
-  if (dtype == MOE_MXFP8 && (((uintptr_t)x_perm_scales | (uintptr_t)w1p_scales | (uintptr_t)w2p_scales) & 3u))
+  if (mx && (((uintptr_t)x_perm_scales | (uintptr_t)w1p_scales | (uintptr_t)w2p_scales) & 3u))
     return MOE_ERR_ALIGN;  // scale words are read 4 bytes at a time
   if (!workspace || workspace_bytes < moe_grouped_mlp_workspace_bytes(capacity, F, dtype))
     return MOE_ERR_WORKSPACE;
@@ -230,10 +240,11 @@ int moe_grouped_mlp(int L, int H, int F, int64_t capacity, int dtype, const void
     e = launch_grouped_mlp_bf16(L, H, F, capacity, (const bf16_t*)x_perm, offsets, (const bf16_t*)w1p,
                                 (const bf16_t*)w2p, (bf16_t*)workspace, part, (bf16_t*)y_perm, s);
   } else {
+    const bool fp4 = dtype == MOE_MXFP4;
     uint8_t* act = (uint8_t*)workspace;
-    uint8_t* act_s = act + round_up((size_t)capacity * F, 256);
+    uint8_t* act_s = act + round_up((size_t)capacity * (fp4 ? F / 2 : F), 256);
     float* part = (float*)(act_s + round_up((size_t)capacity * (F / 32), 256));
-    e = launch_grouped_mlp_mx(L, H, F, capacity, (const uint8_t*)x_perm, x_perm_scales, offsets,
+    e = launch_grouped_mlp_mx(L, H, F, capacity, fp4, (const uint8_t*)x_perm, x_perm_scales, offsets,
                               (const uint8_t*)w1p, w1p_scales, (const uint8_t*)w2p, w2p_scales, act, act_s,
                               part, (bf16_t*)y_perm, s);
   }

@@ -134,6 +134,26 @@ __device__ __forceinline__ uint32_t mx_e4m3x4(uint32_t p0, uint32_t p1, int E) {
   return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(mx_scaled(p1 & 0xffffu, E), mx_scaled(p1 >> 16, E), lo, true);
 }
 
+// MXFP4 (OCP MX E2M1 elements): the block exponent is floor(log2 amax) - 2
+// (6 = 1.5 * 2^2 is E2M1's largest normal), clamped to the E8M0 range.
+__device__ __forceinline__ int mx4_scale_exp(uint32_t amax_abs_bits) {
+  if (amax_abs_bits == 0) return -127;
+  int e = bf16_floor_log2(amax_abs_bits) - 2;
+  return e < -127 ? -127 : (e > 127 ? 127 : e);
+}
+// E2M1 code (4 bits) of bf16 value b (bits) under block scale 2^E: the
+// magnitude |b| * 2^-E (exact) is compared with the midpoints of the grid
+// 0, 0.5, 1, 1.5, 2, 3, 4, 6; a value on a midpoint goes to the neighbour with
+// the even code (0.25 -> 0, 0.75 -> 1, 1.25 -> 1, 1.75 -> 2, 2.5 -> 2,
+// 3.5 -> 4, 5 -> 4) and everything above 5 to 6 (saturation).  The sign bit is
+// the value's, zeros included.
+__device__ __forceinline__ uint32_t mx_e2m1(uint32_t b, int E) {
+  const float a = __builtin_amdgcn_ldexpf(__uint_as_float((b & 0x7fffu) << 16), -E);
+  const uint32_t m = a <= 0.25f ? 0u : a < 0.75f ? 1u : a <= 1.25f ? 2u : a < 1.75f ? 3u
+                   : a <= 2.5f ? 4u : a < 3.5f ? 5u : a <= 5.0f ? 6u : 7u;
+  return m | ((b >> 12) & 8u);
+}
+
 // ---------------------------------------------------------------------------
 // Host-side launchers (one per kernel family, defined in the kernel sources).
 // All return hipError_t of the launch.
@@ -181,7 +201,7 @@ hipError_t launch_grouped_mlp_bf16(int L, int H, int F, int64_t capacity, const 
                                    const int32_t* offsets, const bf16_t* w1p, const bf16_t* w2p,
                                    bf16_t* act, float* part, bf16_t* y, hipStream_t s);
 size_t grouped_mlp_mx_part_bytes();
-hipError_t launch_grouped_mlp_mx(int L, int H, int F, int64_t capacity, const uint8_t* x,
+hipError_t launch_grouped_mlp_mx(int L, int H, int F, int64_t capacity, bool fp4, const uint8_t* x,
                                  const uint8_t* xs, const int32_t* offsets, const uint8_t* w1p,
                                  const uint8_t* w1s, const uint8_t* w2p, const uint8_t* w2s,
                                  uint8_t* act, uint8_t* act_s, float* part, bf16_t* y, hipStream_t s);

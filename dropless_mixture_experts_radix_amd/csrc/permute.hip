@@ -178,7 +178,7 @@ __global__ __launch_bounds__(1024) void k_scan(int ntiles, int L, int64_t capaci
 // ---------------------------------------------------------------------------
 // k_permute: one wavefront per token, 4 per workgroup.
 // ---------------------------------------------------------------------------
-template <int OUT>  // 0: copy rows (bf16 or fp32, row_bytes), 1: MX-quantize bf16 rows
+template <int OUT>  // 0: copy rows (bf16 or fp32, row_bytes), 1: MXFP8-, 2: MXFP4-quantize bf16 rows
 __global__ __launch_bounds__(256) void k_permute(int T, int K, int e0, int L, int TT, int64_t capacity,
                                                  int row_bytes, const uint8_t* __restrict__ x,
                                                  const int16_t* __restrict__ ids,
@@ -247,12 +247,24 @@ __global__ __launch_bounds__(256) void k_permute(int T, int K, int e0, int L, in
         am = am > o ? am : o;
         o = (uint32_t)__shfl_xor((int)am, 2, 64);
         am = am > o ? am : o;
-        const int E = mx_scale_exp(am);
-        lo[j] = mx_e4m3x4(v[j][0], v[j][1], E);
-        hi[j] = mx_e4m3x4(v[j][2], v[j][3], E);
-        sc[j] = (uint32_t)(E + 127);
+        if (OUT == 1) {
+          const int E = mx_scale_exp(am);
+          lo[j] = mx_e4m3x4(v[j][0], v[j][1], E);
+          hi[j] = mx_e4m3x4(v[j][2], v[j][3], E);
+          sc[j] = (uint32_t)(E + 127);
+        } else {  // 8 E2M1 codes, element 2i in the low nibble of byte i
+          const int E = mx4_scale_exp(am);
+          uint32_t c = 0;
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            c |= (mx_e2m1(v[j][q] & 0xffffu, E) | (mx_e2m1(v[j][q] >> 16, E) << 4)) << (8 * q);
+          lo[j] = c;
+          hi[j] = 0;
+          sc[j] = (uint32_t)(E + 127);
+        }
       }
-      // bf16 row of H = row_bytes/2 elements -> codes [H] + scales [H/32]
+      // bf16 row of H = row_bytes/2 elements -> codes [H] (MXFP4: [H/2]
+      // bytes) + scales [H/32]
       const int H = row_bytes >> 1;
       uint64_t b = bits;
       while (b) {
@@ -260,14 +272,15 @@ __global__ __launch_bounds__(256) void k_permute(int T, int K, int e0, int L, in
         b &= b - 1;
         const int d = readlane_i(dest, k);
         if (p0 == 0 && l == 0) row_to_slot[d] = t * K + k;
-        uint8_t* dst = x_perm + (long)d * H;
+        uint8_t* dst = x_perm + (long)d * (OUT == 1 ? H : H >> 1);
         uint8_t* dsc = x_scales + (long)d * (H >> 5);
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           const int off = (p0 + j) * 1024 + l * 16;  // byte offset in the bf16 row
           if (p0 + j < npiece && off < row_bytes) {
             const int e_off = off >> 1;  // element offset
-            *(uint2*)(dst + e_off) = make_uint2(lo[j], hi[j]);
+            if (OUT == 1) *(uint2*)(dst + e_off) = make_uint2(lo[j], hi[j]);
+            else *(uint32_t*)(dst + (e_off >> 1)) = lo[j];
             if ((l & 3) == 0) dsc[e_off >> 5] = (uint8_t)sc[j];
           }
         }
@@ -296,6 +309,10 @@ hipError_t launch_permute(int T, int H, int K, int E_global, int e0, int L, int6
     const dim3 g((T + 3) / 4), b(256);
     if (out_dtype == MOE_MXFP8)
       hipLaunchKernelGGL(k_permute<1>, g, b, 0, s, T, K, e0, L, TT, capacity, row_bytes,
+                         (const uint8_t*)x, ids, hist, rank, offsets, (uint8_t*)x_perm, x_scales,
+                         row_to_slot, slot_to_row);
+    else if (out_dtype == MOE_MXFP4)
+      hipLaunchKernelGGL(k_permute<2>, g, b, 0, s, T, K, e0, L, TT, capacity, row_bytes,
                          (const uint8_t*)x, ids, hist, rank, offsets, (uint8_t*)x_perm, x_scales,
                          row_to_slot, slot_to_row);
     else

@@ -22,6 +22,9 @@ namespace moe {
 //         [256 rows][16 blocks] (bytes past the last block of a short final
 //         group are not written); rows past Ncols in the last panel are zero
 //         (codes and scales).
+// MODE 3: bf16 -> MXFP4: E2M1 codes two per byte (element 2i in the low
+//         nibble) in k-blocked panels of [256 rows][128 k = 64 bytes] per
+//         128-wide k step, scales as in MODE 2.
 template <int MODE>
 __global__ __launch_bounds__(256) void k_prepare(int Kd, int Ncols, int F_interleave,
                                                  const void* __restrict__ w, void* __restrict__ wp,
@@ -59,6 +62,23 @@ __global__ __launch_bounds__(256) void k_prepare(int Kd, int Ncols, int F_interl
       const long o = out_off + ((long)(p >> 8) * KT + (k >> 5)) * (256 * 32) + (p & 255) * 32 + (k & 31);
       ((bf16_t*)wp)[o] = (bf16_t)tile[pp][kk];
     }
+  } else if (MODE == 3) {
+    if (tid < 32) {
+      const int pp = tid;
+      uint32_t am = 0;
+      for (int kk = 0; kk < 32; ++kk) {
+        const uint32_t a = tile[pp][kk] & 0x7fffu;
+        am = am > a ? am : a;
+      }
+      const int E = mx4_scale_exp(am);
+      const int NP = (Ncols + 255) / 256, KT = Kd / 128, NG = (Kd + 511) / 512;
+      const int p = pc * 32 + pp;
+      const long panel = (long)e * NP + (p >> 8);
+      uint8_t* dst = (uint8_t*)wp + (panel * KT + (k0 >> 7)) * (256 * 64) + (p & 255) * 64 + ((k0 & 127) >> 1);
+      for (int kk = 0; kk < 32; kk += 2)
+        dst[kk >> 1] = (uint8_t)(mx_e2m1(tile[pp][kk], E) | (mx_e2m1(tile[pp][kk + 1], E) << 4));
+      ws[(panel * NG + (k0 >> 9)) * (256 * 16) + (p & 255) * 16 + ((k0 >> 5) & 15)] = (uint8_t)(E + 127);
+    }
   } else if (tid < 32) {
     const int pp = tid;
     uint32_t am = 0;
@@ -89,9 +109,12 @@ hipError_t launch_prepare_weights(int L, int H, int F, int dtype, const void* w1
                        (uint8_t*)nullptr);
     hipLaunchKernelGGL(k_prepare<1>, dim3((H + 255) / 256 * 8, F / 32, L), b, 0, s, F, H, 0, w2, w2p,
                        (uint8_t*)nullptr);
-  } else {
+  } else if (dtype == MOE_MXFP8) {
     hipLaunchKernelGGL(k_prepare<2>, dim3((2 * F + 255) / 256 * 8, H / 32, L), b, 0, s, H, 2 * F, F, w1, w1p, w1s);
     hipLaunchKernelGGL(k_prepare<2>, dim3((H + 255) / 256 * 8, F / 32, L), b, 0, s, F, H, 0, w2, w2p, w2s);
+  } else {
+    hipLaunchKernelGGL(k_prepare<3>, dim3((2 * F + 255) / 256 * 8, H / 32, L), b, 0, s, H, 2 * F, F, w1, w1p, w1s);
+    hipLaunchKernelGGL(k_prepare<3>, dim3((H + 255) / 256 * 8, F / 32, L), b, 0, s, F, H, 0, w2, w2p, w2s);
   }
   return hipGetLastError();
 }

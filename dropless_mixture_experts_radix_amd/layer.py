@@ -13,7 +13,7 @@ class MoELayer:
 
     T, H, E, K, F: tokens, hidden, experts seen by the router, routes per token,
     expert FFN width.  L local experts e0..e0+L-1 (default: all).  dtype: the
-    expert path (M.F32, M.BF16 or M.MXFP8); x_dtype: the token rows (M.F32 or
+    expert path (M.F32, M.BF16, M.MXFP8 or M.MXFP4); x_dtype: the token rows (M.F32 or
     M.BF16).  w_router [H,E] (fp32 or bf16) enables the fused projection; when
     it is None, forward() takes logits.
     """
@@ -35,13 +35,16 @@ class MoELayer:
             nb = M.moe_router_prepared_bytes(H, E, self.w_dtype, x_dtype)
             self.w_prep = torch.empty(nb, dtype=torch.uint8, device=dev)
             M.moe_prepare_router(w_router, x_dtype, self.w_prep)
-        wdt = {M.F32: torch.float32, M.BF16: torch.bfloat16, M.MXFP8: torch.uint8}[dtype]
-        # bf16 and MXFP8 prepared weights come in whole 256-row panels (k-blocked)
+        mx = dtype in (M.MXFP8, M.MXFP4)
+        wdt = torch.uint8 if mx else {M.F32: torch.float32, M.BF16: torch.bfloat16}[dtype]
+        # bf16 and MX prepared weights come in whole 256-row panels (k-blocked);
+        # MXFP4 codes are two per byte
         pad = (lambda n: (n + 255) // 256 * 256) if dtype != M.F32 else (lambda n: n)
-        self.w1p = torch.empty((L, pad(2 * F), H), dtype=wdt, device=dev)
-        self.w2p = torch.empty((L, pad(H), F), dtype=wdt, device=dev)
+        cw = (lambda n: n // 2) if dtype == M.MXFP4 else (lambda n: n)
+        self.w1p = torch.empty((L, pad(2 * F), cw(H)), dtype=wdt, device=dev)
+        self.w2p = torch.empty((L, pad(H), cw(F)), dtype=wdt, device=dev)
         self.w1s = self.w2s = None
-        if dtype == M.MXFP8:
+        if mx:
             # E8M0 scales: 16 bytes per prepared row and 512-wide k group
             self.w1s = torch.empty((L, pad(2 * F), (H + 511) // 512 * 16), dtype=torch.uint8, device=dev)
             self.w2s = torch.empty((L, pad(H), (F + 511) // 512 * 16), dtype=torch.uint8, device=dev)
@@ -54,11 +57,10 @@ class MoELayer:
                                     device=dev)
         self.counts = torch.empty(L, **i32)
         self.offsets = torch.empty(L + 1, **i32)
-        act = {M.F32: torch.float32, M.BF16: torch.bfloat16, M.MXFP8: torch.bfloat16}[dtype]
+        act = torch.float32 if dtype == M.F32 else torch.bfloat16
         self.out_dtype = act
-        self.x_perm = torch.empty((cap, H), dtype=torch.uint8 if dtype == M.MXFP8 else act, device=dev)
-        self.x_perm_scales = (torch.empty((cap, H // 32), dtype=torch.uint8, device=dev)
-                              if dtype == M.MXFP8 else None)
+        self.x_perm = torch.empty((cap, cw(H)), dtype=torch.uint8 if mx else act, device=dev)
+        self.x_perm_scales = torch.empty((cap, H // 32), dtype=torch.uint8, device=dev) if mx else None
         self.row_to_slot = torch.empty(cap, **i32)
         self.slot_to_row = torch.empty((T, K), **i32)
         self.perm_ws = torch.empty(M.moe_permute_workspace_bytes(T, K, L), dtype=torch.uint8, device=dev)
@@ -82,8 +84,9 @@ class MoELayer:
         if self.dtype == M.BF16:  # k-blocked [F/32][capacity][32]
             blk = self.mlp_ws[: cap * F * 2].view(torch.bfloat16).view(F // 32, cap, 32)
             return blk.permute(1, 0, 2).reshape(cap, F)
-        codes = self.mlp_ws[: cap * F].view(cap, F)
-        off = (cap * F + 255) // 256 * 256
+        cb = F // 2 if self.dtype == M.MXFP4 else F  # code bytes per row
+        codes = self.mlp_ws[: cap * cb].view(cap, cb)
+        off = (cap * cb + 255) // 256 * 256
         scales = self.mlp_ws[off: off + cap * (F // 32)].view(cap, F // 32)
         return codes, scales
 

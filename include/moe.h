@@ -10,7 +10,7 @@
  *
  *   moe_route_topk         logits (or x . W_r) -> int16 [T,K] expert ids + fp32 probs
  *   moe_permute            per-expert count, scan and permute of the token rows
- *   moe_grouped_mlp        ragged grouped SwiGLU MLP (fp32, bf16 or MXFP8)
+ *   moe_grouped_mlp        ragged grouped SwiGLU MLP (fp32, bf16, MXFP8 or MXFP4)
  *   moe_unpermute_combine  probability-weighted sum back in token order
  *
  * plus one-time weight preparation and a standalone MX quantizer.
@@ -65,8 +65,11 @@ enum {
 enum {
   MOE_F32 = 0,   /* IEEE fp32 */
   MOE_BF16 = 1,  /* bfloat16 (16-bit, fp32 exponent range) */
-  MOE_MXFP8 = 2  /* OCP MX: E4M3 codes (uint8) + one E8M0 scale byte per 32
+  MOE_MXFP8 = 2, /* OCP MX: E4M3 codes (uint8) + one E8M0 scale byte per 32
                     consecutive elements of a row (value = code * 2^(scale-127)) */
+  MOE_MXFP4 = 3  /* OCP MX: E2M1 codes, two per byte (element 2i in the low
+                    nibble, 2i+1 in the high nibble), + one E8M0 scale byte per
+                    32 consecutive elements of a row */
 };
 
 /* Router score functions. */
@@ -164,7 +167,10 @@ int moe_route_topk(int T, int E, int K, int H, int score, int x_dtype, int w_dty
  * x_perm then receives E4M3 codes [capacity,H] uint8 and x_perm_scales the
  * E8M0 scales [capacity,H/32] uint8 of 32-element blocks along H (OCP MX v1.0
  * rule: scale exponent floor(log2 max|v|) - 8, round to nearest even,
- * saturate at 448), which requires H % 32 == 0.
+ * saturate at 448), which requires H % 32 == 0; or MOE_MXFP4 with bf16 x:
+ * x_perm receives packed E2M1 codes [capacity,H/2] uint8 and x_perm_scales
+ * the E8M0 scales [capacity,H/32] (scale exponent floor(log2 max|v|) - 2,
+ * round to nearest even, saturate at 6).
  * Workspace: moe_permute_workspace_bytes(T, K, L) bytes.
  * ------------------------------------------------------------------------ */
 size_t moe_permute_workspace_bytes(int T, int K, int L);
@@ -200,6 +206,11 @@ int moe_permute(int T, int H, int K, int E_global, int e0, int L, int64_t capaci
  *   rows][16] (w1p_scales, w2p_scales; the bytes past the last 32-block of a
  *   short final group are left as they are).  Requires H % 256 == 0 and
  *   F % 256 == 0.
+ * dtype MOE_MXFP4 (in_dtype MOE_BF16): E2M1 codes of the rows above, two per
+ *   byte (element 2i of a row in the low nibble), in the same zero-padded
+ *   256-row panels, k-blocked by 128 elements: [L][panel][k/128][256 rows][64
+ *   bytes]; scales exactly as for MOE_MXFP8.  Requires H % 512 == 0 and
+ *   F % 512 == 0.
  * Requires H % 32 == 0 and F % 32 == 0 (MOE_F32).  Byte sizes:
  * moe_prepared_weight_bytes(L, H, F, dtype, which) with which = 1 (W1p),
  * 2 (W2p), 3 (W1p scales), 4 (W2p scales).
@@ -226,10 +237,13 @@ int moe_prepare_weights(int L, int H, int F, int in_dtype, int dtype,
  * dtype MOE_F32: x_perm, a, y_perm fp32.  MOE_BF16: x_perm, a, y_perm bf16.
  * MOE_MXFP8: x_perm as E4M3 codes + x_perm_scales (from moe_permute), `a`
  *   rounded to bf16 and then MX-quantized along F, y_perm bf16.
+ * MOE_MXFP4: the same with packed E2M1 codes (x_perm [capacity][H/2] bytes,
+ *   `a` quantized to E2M1 along F).
  * The schedule of output tiles is built on the device from `offsets`: empty
  * experts get no tiles.  Requires H % 128 == 0 and F % 128 == 0 for MOE_BF16,
- * H % 256 == 0 and F % 256 == 0 for MOE_MXFP8 (scale pointers 4-byte
- * aligned), H % 16 == 0 and F % 32 == 0 for MOE_F32.
+ * H % 256 == 0 and F % 256 == 0 for MOE_MXFP8, H % 512 == 0 and F % 512 == 0
+ * for MOE_MXFP4 (MX scale pointers 4-byte aligned), H % 16 == 0 and
+ * F % 32 == 0 for MOE_F32.
  * Workspace: moe_grouped_mlp_workspace_bytes(capacity, F, dtype) bytes; it
  * starts with `a`: MOE_F32 [capacity][F] fp32; MOE_BF16 k-blocked
  * [F/32][capacity][32] bf16, followed at the next 256-byte boundary by 64 MiB
@@ -237,7 +251,7 @@ int moe_prepare_weights(int L, int H, int F, int in_dtype, int dtype,
  * CUs are split along the contraction and summed in a fixed order); MOE_MXFP8
  * the codes [capacity][F], then at the next 256-byte boundary the scales
  * [capacity][F/32], then at the next 256-byte boundary 64 MiB of split-K
- * partial tiles.
+ * partial tiles; MOE_MXFP4 the same with packed codes [capacity][F/2].
  * ------------------------------------------------------------------------ */
 size_t moe_grouped_mlp_workspace_bytes(int64_t capacity, int F, int dtype);
 

@@ -6,7 +6,7 @@ import torch
 from oracle import moe_oracle as O
 
 DEV = "cuda"
-TOL = {"f32": 1e-5, "bf16": 2e-2, "mxfp8": 3e-2, "probs": 1e-5, "logits": 1e-5}
+TOL = {"f32": 1e-5, "bf16": 2e-2, "mxfp8": 3e-2, "mxfp4": 3e-2, "probs": 1e-5, "logits": 1e-5}
 
 
 def rel_inf(got, want):

@@ -76,6 +76,9 @@ def test_permute_validation():
     assert call(xd=0, od=2) == 4         # MX output needs bf16 rows
     assert call(od=2, H=48) == 2         # MX needs H % 32 == 0
     assert call(od=2) == 1               # MX scales missing
+    assert call(xd=0, od=3) == 4         # MXFP4 output needs bf16 rows
+    assert call(od=3, H=48) == 2
+    assert call(od=3) == 1
     assert call(counts=None) == 1
     assert call(ws=None) == 5
     assert call(wsb=8) == 5
@@ -95,6 +98,10 @@ def test_mlp_validation():
     assert call(H=192) == 2
     assert call(dt=2, F=384) == 2        # MXFP8 needs F % 256 == 0
     assert call(dt=2, H=256, F=256) == 1  # MX scales missing
+    assert call(dt=3, H=512, F=768) == 2  # MXFP4 needs F % 512 == 0
+    assert call(dt=3, H=256, F=512) == 2  # ... and H % 512 == 0
+    assert call(dt=3, H=512, F=512) == 1
+    assert call(dt=3, H=512, F=512, xs=P, w1s=P + 2, w2s=P) == 3  # scale pointers 4-byte aligned
     assert call(dt=9) == 4
     assert call(offs=None) == 1
     assert call(wsb=100) == 5
@@ -114,6 +121,8 @@ def test_other_validation():
     assert lib.moe_prepare_weights(2, 256, 256, 0, 2, P, P, P, P, P, P, None) == 4       # MX from fp32
     assert lib.moe_prepare_weights(2, 256, 384, 1, 2, P, P, P, P, P, P, None) == 2       # MX needs F % 256
     assert lib.moe_prepare_weights(2, 256, 256, 1, 2, P, P, P, P, None, P, None) == 1
+    assert lib.moe_prepare_weights(2, 512, 768, 1, 3, P, P, P, P, P, P, None) == 2       # MXFP4 needs F % 512
+    assert lib.moe_prepare_weights(2, 512, 512, 0, 3, P, P, P, P, P, P, None) == 4
     assert lib.moe_prepare_router(P, 1, 0, 64, 8, P, None) == 4                          # bf16 W_r, fp32 x
     assert lib.moe_prepare_router(None, 0, 1, 64, 8, P, None) == 1
 
@@ -131,5 +140,11 @@ def test_size_queries():
     assert lib.moe_prepared_weight_bytes(2, 768, 256, 2, 3) == 2 * 512 * 2 * 16
     assert lib.moe_prepared_weight_bytes(2, 768, 256, 2, 4) == 2 * 768 * 1 * 16
     assert lib.moe_prepared_weight_bytes(8, 4096, 14336, 1, 3) == 0
+    # MXFP4: codes two per byte, scales as for MXFP8
+    assert lib.moe_prepared_weight_bytes(8, 4096, 14336, 3, 1) == 8 * 2 * 14336 * 4096 // 2
+    assert lib.moe_prepared_weight_bytes(2, 1024, 512, 3, 2) == 2 * 1024 * 512 // 2
+    assert lib.moe_prepared_weight_bytes(2, 1024, 512, 3, 3) == lib.moe_prepared_weight_bytes(2, 1024, 512, 2, 3)
+    assert (lib.moe_grouped_mlp_workspace_bytes(8192, 14336, 3) <
+            lib.moe_grouped_mlp_workspace_bytes(8192, 14336, 2))
     assert lib.moe_grouped_mlp_workspace_bytes(8192, 14336, 1) >= 8192 * 14336 * 2
     assert lib.moe_permute_workspace_bytes(8192, 36, 32) >= 8192 * 36 * 4

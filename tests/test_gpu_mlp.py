@@ -12,7 +12,7 @@ from tests.gpu_util import DEV, TOL, bf16_from_f64, np_of, rel_inf, say, to_f64
 
 pytestmark = pytest.mark.gpu
 
-DT = {"f32": D.F32, "bf16": D.BF16, "mxfp8": D.MXFP8}
+DT = {"f32": D.F32, "bf16": D.BF16, "mxfp8": D.MXFP8, "mxfp4": D.MXFP4}
 
 
 def _interleave_rows(F):
@@ -28,13 +28,15 @@ def _unblock(wp):
     return to_f64(t.reshape(rows, kd))
 
 
-def _unblock_mx(wp, ws):
-    """MXFP8 prepared weights of one expert, k-blocked panels: codes
-    [rows/256][Kd/64][256][64] and scales [rows/256][ceil(Kd/512)][256][16], back
-    to row-major codes [rows][Kd] and scales [rows][Kd/32] (numpy uint8)."""
-    rows, kd = wp.shape
+def _unblock_mx(wp, ws, fp4=False):
+    """MX prepared weights of one expert, k-blocked panels: codes
+    [rows/256][Kd/64 bytes][256][64] (MXFP4: 64 bytes = 128 codes) and scales
+    [rows/256][ceil(Kd/512)][256][16], back to row-major code bytes [rows][Kd
+    or Kd/2] and scales [rows][Kd/32] (numpy uint8)."""
+    rows, kb = wp.shape  # code bytes per row
+    kd = kb * 2 if fp4 else kb
     ng = (kd + 511) // 512
-    c = np_of(wp).reshape(rows // 256, kd // 64, 256, 64).transpose(0, 2, 1, 3).reshape(rows, kd)
+    c = np_of(wp).reshape(rows // 256, kb // 64, 256, 64).transpose(0, 2, 1, 3).reshape(rows, kb)
     s = np_of(ws).reshape(rows // 256, ng, 256, 16).transpose(0, 2, 1, 3).reshape(rows, ng * 16)[:, : kd // 32]
     return c, s
 
@@ -72,23 +74,27 @@ def _run_mlp(counts, H, F, dt, seed=0, xscale=1.0, check_layout=True):
     code = DT[dt]
     w1 = torch.stack([_dev(w, dt) for w in W1])
     w2 = torch.stack([_dev(w, dt) for w in W2])
-    wdt = {"f32": torch.float32, "bf16": torch.bfloat16, "mxfp8": torch.uint8}[dt]
+    mx = dt in ("mxfp8", "mxfp4")
+    wdt = {"f32": torch.float32, "bf16": torch.bfloat16, "mxfp8": torch.uint8, "mxfp4": torch.uint8}[dt]
     pad = (lambda n: (n + 255) // 256 * 256) if dt != "f32" else (lambda n: n)
-    w1p = torch.empty((L, pad(2 * F), H), dtype=wdt, device=DEV)
-    w2p = torch.empty((L, pad(H), F), dtype=wdt, device=DEV)
+    cw = (lambda n: n // 2) if dt == "mxfp4" else (lambda n: n)
+    w1p = torch.empty((L, pad(2 * F), cw(H)), dtype=wdt, device=DEV)
+    w2p = torch.empty((L, pad(H), cw(F)), dtype=wdt, device=DEV)
     w1s = w2s = None
-    if dt == "mxfp8":
+    if mx:
         w1s = torch.empty((L, pad(2 * F), (H + 511) // 512 * 16), dtype=torch.uint8, device=DEV)
         w2s = torch.empty((L, pad(H), (F + 511) // 512 * 16), dtype=torch.uint8, device=DEV)
     D.moe_prepare_weights(w1, w2, code, w1p, w2p, w1s, w2s)
     perm = _interleave_rows(F)
     if check_layout:
         e = L - 1
-        if dt == "mxfp8":
-            c1, s1 = O.mx_quantize_rows(W1[e].T[perm])
-            c2, s2 = O.mx_quantize_rows(W2[e].T)
-            w1c, w1sc = _unblock_mx(w1p[e], w1s[e])
-            w2c, w2sc = _unblock_mx(w2p[e], w2s[e])
+        if mx:
+            quant = O.mx_quantize_rows if dt == "mxfp8" else (lambda m: (lambda c, s: (O.pack_fp4(c), s))(
+                *O.mx4_quantize_rows(m)))
+            c1, s1 = quant(W1[e].T[perm])
+            c2, s2 = quant(W2[e].T)
+            w1c, w1sc = _unblock_mx(w1p[e], w1s[e], dt == "mxfp4")
+            w2c, w2sc = _unblock_mx(w2p[e], w2s[e], dt == "mxfp4")
             np.testing.assert_array_equal(w1c[: 2 * F], c1)
             np.testing.assert_array_equal(w1sc[: 2 * F], s1)
             np.testing.assert_array_equal(w2c[:H], c2)
@@ -109,6 +115,10 @@ def _run_mlp(counts, H, F, dt, seed=0, xscale=1.0, check_layout=True):
         xs = torch.empty((cap, H // 32), dtype=torch.uint8, device=DEV)
         D.moe_mx_quantize(xd, xq, xs)
         xd = xq
+    elif dt == "mxfp4":  # quantized rows from the oracle (the permute's own are pinned on their own)
+        c, s_ = O.mx4_quantize_rows(x64)
+        xd = torch.from_numpy(O.pack_fp4(c)).to(DEV)
+        xs = torch.from_numpy(s_).to(DEV)
     ydt = torch.float32 if dt == "f32" else torch.bfloat16
     y = torch.full((cap, H), 5.0, dtype=ydt, device=DEV)
     ws = torch.empty(D.moe_grouped_mlp_workspace_bytes(cap, F, code), dtype=torch.uint8, device=DEV)
@@ -128,6 +138,28 @@ def _run_mlp(counts, H, F, dt, seed=0, xscale=1.0, check_layout=True):
         elif dt == "bf16":  # k-blocked activations [F/32][cap][32]
             a = ws[: cap * F * 2].view(torch.bfloat16).view(F // 32, cap, 32).permute(1, 0, 2).reshape(cap, F)
             assert rel_inf(to_f64(a)[:N], want_a) <= TOL[dt]
+        elif dt == "mxfp4":
+            cb = F // 2
+            codes = O.unpack_fp4(np_of(ws[: cap * cb].view(cap, cb))[:N])
+            off = (cap * cb + 255) // 256 * 256
+            sc = np_of(ws[off: off + cap * (F // 32)].view(cap, F // 32))[:N]
+            a_dq = O.mx4_dequantize_rows(codes, sc)
+            # every element within half an E2M1 step (a quarter of its magnitude,
+            # a quarter of its block scale below 2) of the oracle's bf16 `a`, or
+            # clamped at 6 * 2^E, plus 1e-3 of the largest |a| for the fp32
+            # accumulation inside the matrix cores
+            scl = np.ldexp(1.0, sc.astype(np.int64) - 127).repeat(32, axis=1)
+            bound = (np.maximum(np.abs(want_a) / 4, scl / 4) * (1 + 2.0 ** -7) + 1e-3 * np.abs(want_a).max() +
+                     np.maximum(0.0, np.abs(want_a) * (1 + 2.0 ** -7) - 6 * scl))
+            bad = np.argwhere(np.abs(a_dq - want_a) > bound)
+            assert bad.size == 0, (len(bad), [(int(r), int(c), float(a_dq[r, c]), float(want_a[r, c]))
+                                              for r, c in bad[:8]])
+            oc, os_ = O.mx4_quantize_rows(want_a)
+            assert (codes == oc).mean() > 0.97 and (sc == os_).mean() > 0.99
+            mags = O.e2m1_decode(codes & 7).reshape(N, F // 32, 32).max(axis=2)
+            nz = mags > 0
+            big = O.mx4_dequantize_rows(codes, sc).reshape(N, F // 32, 32)
+            assert ((mags[nz] >= 4) | (np.abs(big).max(axis=2)[nz] < 2.0 ** -124)).all()
         else:
             codes = np_of(ws[: cap * F].view(cap, F))[:N]
             off = (cap * F + 255) // 256 * 256
@@ -188,3 +220,18 @@ def test_grouped_mlp_bf16(counts, H, F):
 ])
 def test_grouped_mlp_mxfp8(counts, H, F):
     _run_mlp(counts, H, F, "mxfp8", seed=sum(counts) + H)
+
+
+@pytest.mark.parametrize("counts,H,F", [
+    ([0, 1, 255, 256, 257, 600, 0, 31], 512, 512),
+    ([900, 24, 0, 513], 1024, 1536),
+    ([70, 300, 0, 5], 1536, 512),         # partial column tiles in both GEMMs
+    ([0, 0, 0, 0], 512, 512),             # no rows at all
+    # 4028 rows (16 row tiles): the 64 tiles of the first GEMM (k = 8192, 16
+    # groups of 4 E2M1 stages) and the 32 of the second (k = 8192) are split
+    # along k into 2 pieces
+    ([1000, 1011, 977, 1040], 8192, 512),
+    ([1000, 1011, 977, 1040], 512, 8192),
+])
+def test_grouped_mlp_mxfp4(counts, H, F):
+    _run_mlp(counts, H, F, "mxfp4", seed=sum(counts) + H + 1)

@@ -30,8 +30,9 @@ def _permute_gpu(x, ids, E, e0, L, capacity, out_dtype=None):
     K = ids.shape[1]
     counts = torch.full((L,), SENT, dtype=torch.int32, device=DEV)
     offsets = torch.full((L + 1,), SENT, dtype=torch.int32, device=DEV)
-    mx = out_dtype == D.MXFP8
-    x_perm = torch.full((max(capacity, 1), H), 0x5A if mx else 3.0,
+    mx = out_dtype in (D.MXFP8, D.MXFP4)
+    width = H // 2 if out_dtype == D.MXFP4 else H
+    x_perm = torch.full((max(capacity, 1), width), 0x5A if mx else 3.0,
                         dtype=torch.uint8 if mx else x.dtype, device=DEV)[:capacity]
     xs = torch.full((max(capacity, 1), H // 32), 0xC3, dtype=torch.uint8, device=DEV)[:capacity] if mx else None
     r2s = torch.full((capacity,), SENT, dtype=torch.int32, device=DEV)
@@ -101,6 +102,42 @@ def test_permute_mx_quantized_rows():
     np.testing.assert_array_equal(np_of(got["x_perm"])[:N], oc)
     np.testing.assert_array_equal(np_of(got["xs"])[:N], os_)
     assert (np_of(got["x_perm"])[N:] == 0x5A).all()
+
+
+def test_permute_mxfp4_quantized_rows():
+    rng = np.random.default_rng(11)
+    T, K, E, H = 600, 2, 8, 512
+    ids = _rand_ids(rng, T, K, E, distinct=True)
+    x64 = O.bf16_round(rng.standard_normal((T, H)) * np.exp(rng.uniform(-8, 8, size=(T, 1))))
+    x64[::11, :64] = 0.0
+    ref = O.count_and_permute(ids, 0, E, x64)
+    N = int(ref["offsets"][-1])
+    got = _permute_gpu(bf16_from_f64(x64), ids, E, 0, E, T * K, out_dtype=D.MXFP4)
+    oc, os_ = O.mx4_quantize_rows(ref["x_perm"])
+    np.testing.assert_array_equal(np_of(got["x_perm"])[:N], O.pack_fp4(oc))
+    np.testing.assert_array_equal(np_of(got["xs"])[:N], os_)
+    assert (np_of(got["x_perm"])[N:] == 0x5A).all()
+
+
+def test_permute_mxfp4_every_bf16_pattern_as_block_max():
+    """Every finite bf16 value as the largest element of a block (with its
+    negation, a smaller neighbour and -0 beside it), routed one row per token."""
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    bits = bits[np.isfinite(O.bits_to_bf16(bits))]
+    blocks = np.zeros((bits.size, 32), np.uint16)
+    blocks[:, 5] = bits
+    blocks[:, 6] = bits ^ 0x8000
+    blocks[:, 7] = (bits & 0x7fff) >> 1
+    blocks[:, 9] = 0x8000
+    x = blocks.reshape(-1, 256)  # 8 blocks per row
+    T = x.shape[0]
+    ids = np.zeros((T, 1), np.int16)
+    say("mxfp4 exhaustive: rows", x.shape)
+    xt = torch.from_numpy(x.astype(np.int16)).view(torch.bfloat16).to(DEV)
+    got = _permute_gpu(xt, ids, 1, 0, 1, T, out_dtype=D.MXFP4)
+    oc, os_ = O.mx4_quantize_rows(O.bits_to_bf16(x))
+    np.testing.assert_array_equal(np_of(got["xs"]), os_)
+    np.testing.assert_array_equal(np_of(got["x_perm"]), O.pack_fp4(oc))
 
 
 def test_permute_overflow_and_bad_ids():
