@@ -25,6 +25,7 @@ import torch
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
 FP8_PEAK_TFLOPS = 5000.0
+FP4_PEAK_TFLOPS = 10100.0
 
 
 def parse():
@@ -47,7 +48,7 @@ def build(cfgname):
     from workloads.gen import make_expert_weights, make_router_inputs, make_tokens
 
     cfg = get_config(cfgname)
-    dt = {"bf16": D.BF16, "mxfp8": D.MXFP8, "f32": D.F32}
+    dt = {"bf16": D.BF16, "mxfp8": D.MXFP8, "mxfp4": D.MXFP4, "f32": D.F32}
     x = make_tokens(cfg).cuda()
     r = make_router_inputs(cfg)
     layer = D.MoELayer(cfg.T, cfg.H, cfg.E, cfg.K, cfg.F, dt[cfg.dtype], dt[cfg.x_dtype], L=cfg.local, e0=cfg.e0,
@@ -234,8 +235,8 @@ def cpu_baseline(cfg, layer, x, r, ntok):
                       f"{dt:.2f} s measured, scaled x{cfg.T // ntok}; max rel diff vs GPU on the sample {err:.2e}"}
 
 
-def mx_variant(steps, warmup):
-    cfg, layer, x, r = build("mixtral_mxfp8")
+def mx_variant(steps, warmup, name="mixtral_mxfp8"):
+    cfg, layer, x, r = build(name)
     ms = time_steps(layer, x, steps, warmup)
     st = time_stages(layer, x, 10)
     N = int(layer.offsets[-1].item())
@@ -243,7 +244,9 @@ def mx_variant(steps, warmup):
     out = {"layer_us": ms * 1000.0, "stage_us": dict(zip(["route", "permute", "grouped_mlp", "combine"],
                                                          [round(v, 2) for v in st])),
            "grouped_gemm_tflops": flops / (st[2] * 1e-6) / 1e12,
-           "grouped_gemm_frac_fp8_peak": flops / (st[2] * 1e-6) / 1e12 / FP8_PEAK_TFLOPS,
+           "peak_tflops": FP8_PEAK_TFLOPS if cfg.dtype == "mxfp8" else FP4_PEAK_TFLOPS,
+           "grouped_gemm_frac_peak": flops / (st[2] * 1e-6) / 1e12 /
+           (FP8_PEAK_TFLOPS if cfg.dtype == "mxfp8" else FP4_PEAK_TFLOPS),
            "permute_quantize_gbs": permute_b / (st[1] * 1e-6) / 1e9}
     del layer
     torch.cuda.empty_cache()
@@ -354,12 +357,16 @@ def main():
         try:
             del layer
             torch.cuda.empty_cache()
-            line["mxfp8"] = mx_variant(max(a.steps // 2, 5), a.warmup)
+            for name, key in (("mixtral_mxfp8", "mxfp8"), ("mixtral_mxfp4", "mxfp4")):
+                try:
+                    line[key] = mx_variant(max(a.steps // 2, 5), a.warmup, name)
+                except Exception as ex:  # report, do not hide the main line
+                    line[key] = {"error": repr(ex)}
             cfg, layer, x, r = build("mixtral_bf16")
             layer.forward(x)
             torch.cuda.synchronize()
         except Exception as ex:  # report, do not hide the main line
-            line["mxfp8"] = {"error": repr(ex)}
+            line["mx"] = {"error": repr(ex)}
     if not a.no_cpu:
         line["cpu_baseline"] = cpu_baseline(cfg, layer, x, r, a.cpu_tokens)
     if not a.no_other:

@@ -19,7 +19,7 @@ from workloads.gen import make_expert_weights, make_router_inputs, make_tokens, 
 
 pytestmark = pytest.mark.gpu
 
-DT = {"f32": D.F32, "bf16": D.BF16, "mxfp8": D.MXFP8}
+DT = {"f32": D.F32, "bf16": D.BF16, "mxfp8": D.MXFP8, "mxfp4": D.MXFP4}
 
 
 def build_layer(cfg, keep=(), T=None):
@@ -116,7 +116,7 @@ def _sampled_expert_rows(offsets, experts, per=6, seed=0):
     return rows
 
 
-@pytest.mark.parametrize("name", ["mixtral_bf16", "mixtral_mxfp8", "dsv3_bf16"])
+@pytest.mark.parametrize("name", ["mixtral_bf16", "mixtral_mxfp8", "mixtral_mxfp4", "dsv3_bf16"])
 def test_layer_large_workloads_sampled(name):
     cfg = get_config(name)
     say("layer", name, "full size, sampled float checks")
@@ -134,6 +134,11 @@ def test_layer_large_workloads_sampled(name):
         sample = np.linspace(0, N - 1, 512).astype(int)
         c, s = O.mx_quantize_rows(to_f64(src[sample]))
         np.testing.assert_array_equal(np_of(layer.x_perm[sample]), c)
+        np.testing.assert_array_equal(np_of(layer.x_perm_scales[sample]), s)
+    elif cfg.dtype == "mxfp4":
+        sample = np.linspace(0, N - 1, 512).astype(int)
+        c, s = O.mx4_quantize_rows(to_f64(src[sample]))
+        np.testing.assert_array_equal(np_of(layer.x_perm[sample]), O.pack_fp4(c))
         np.testing.assert_array_equal(np_of(layer.x_perm_scales[sample]), s)
     else:
         assert torch.equal(layer.x_perm[:N], src)

@@ -18,7 +18,7 @@ class MoEConfig:
     E: int            # global experts
     K: int            # routes per token
     F: int            # expert FFN width (SwiGLU: W1 has 2F columns)
-    dtype: str        # "f32" | "bf16" | "mxfp8" (expert path)
+    dtype: str        # "f32" | "bf16" | "mxfp8" | "mxfp4" (expert path)
     x_dtype: str      # "f32" | "bf16"
     wr_dtype: str     # router weight dtype: "f32" | "bf16" | "none" (logits given)
     score: str        # "softmax" | "sigmoid"
@@ -66,6 +66,9 @@ CONFIGS = {
                            bias="zipf"),
     "mixtral_mxfp8": MoEConfig("mixtral_mxfp8", 4, T=4096, H=4096, E=8, K=2, F=14336,
                                dtype="mxfp8", x_dtype="bf16", wr_dtype="f32", score="softmax"),
+    # the MXFP4 variant of the same layer (OCP MX E2M1 elements); its own seed
+    "mixtral_mxfp4": MoEConfig("mixtral_mxfp4", 6, T=4096, H=4096, E=8, K=2, F=14336,
+                               dtype="mxfp4", x_dtype="bf16", wr_dtype="f32", score="softmax"),
     "sparse_share": MoEConfig("sparse_share", 5, T=8192, H=512, E=2304, K=36, F=512,
                               dtype="bf16", x_dtype="bf16", wr_dtype="none", score="softmax",
                               e0=0, L=32, logits="grouped", mask_every=64),

@@ -43,7 +43,7 @@ def _normal(shape, std, seed, device="cpu", dtype=torch.float32):
 
 
 def _tdtype(name: str) -> torch.dtype:
-    return {"f32": torch.float32, "bf16": torch.bfloat16, "mxfp8": torch.bfloat16}[name]
+    return {"f32": torch.float32, "bf16": torch.bfloat16, "mxfp8": torch.bfloat16, "mxfp4": torch.bfloat16}[name]
 
 
 def make_tokens(cfg: MoEConfig, T: int = None, seed: int = None) -> torch.Tensor:
