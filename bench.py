@@ -36,7 +36,8 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-mx", action="store_true", help="skip the MXFP8 variant")
     ap.add_argument("--no-other", action="store_true", help="skip the other full-size workloads")
-    ap.add_argument("--workload", choices=["dsv3_bf16", "sparse_share"], default=None,
+    ap.add_argument("--workload", choices=["dsv3_bf16", "sparse_share", "mixtral_mxfp8", "mixtral_mxfp4"],
+                    default=None,
                     help="time only this other workload (its layer and grouped MLP) and print its line")
     ap.add_argument("--cpu-tokens", type=int, default=4096, help="tokens in the CPU oracle sample")
     return ap.parse_args()

@@ -249,18 +249,30 @@ __global__ __launch_bounds__(GM_THREADS, 1) void k_gemm_mx(int L, int N, int Kd,
       fb[j] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]}; \
     }                                                                                       \
     const int ks = (KS_);                                                                   \
-    const uint8_t* ps = smem + GM_LDS_SCALES + ((ks >> LG) & 1) * GM_SGROUP_BYTES + (ks & (SG - 1)) * (FP4 ? 4 : 2) + g; \
-    _Pragma("unroll") for (int i = 0; i < (NB); ++i) sa[i] = ps[(wm * 128 + i * 32 + r32) * 16]; \
-    _Pragma("unroll") for (int j = 0; j < 2; ++j) sb[j] = ps[GM_SGROUP_HALF + (wn * 64 + j * 32 + r32) * 16]; \
     if (FP4) {                                                                              \
-      _Pragma("unroll") for (int i = 0; i < (NB); ++i) sa2[i] = ps[(wm * 128 + i * 32 + r32) * 16 + 2]; \
-      _Pragma("unroll") for (int j = 0; j < 2; ++j) sb2[j] = ps[GM_SGROUP_HALF + (wn * 64 + j * 32 + r32) * 16 + 2]; \
+      /* the 4 scale bytes of the stage in one word, shifted so that byte 0 is   */         \
+      /* block g (first instruction) and byte 2 block 2 + g (second)             */         \
+      const uint8_t* pw = smem + GM_LDS_SCALES + ((ks >> LG) & 1) * GM_SGROUP_BYTES + (ks & (SG - 1)) * 4; \
+      _Pragma("unroll") for (int i = 0; i < (NB); ++i)                                      \
+        sa[i] = *(const uint32_t*)(pw + (wm * 128 + i * 32 + r32) * 16) >> (8 * g);         \
+      _Pragma("unroll") for (int j = 0; j < 2; ++j)                                         \
+        sb[j] = *(const uint32_t*)(pw + GM_SGROUP_HALF + (wn * 64 + j * 32 + r32) * 16) >> (8 * g); \
+    } else if (((ST) & 1) == 0) {                                                           \
+      /* stages ks, ks + 1 (ks even: ring stage ST and ks have the same parity) */          \
+      /* share a word: bytes 0, 1 and 2, 3 are their blocks; shifted so that   */           \
+      /* byte 0 (stage ks) or byte 2 (stage ks + 1) is block g                  */           \
+      const uint8_t* pw = smem + GM_LDS_SCALES + ((ks >> LG) & 1) * GM_SGROUP_BYTES + (ks & (SG - 1)) * 2; \
+      _Pragma("unroll") for (int i = 0; i < (NB); ++i)                                      \
+        sa[i] = *(const uint32_t*)(pw + (wm * 128 + i * 32 + r32) * 16) >> (8 * g);         \
+      _Pragma("unroll") for (int j = 0; j < 2; ++j)                                         \
+        sb[j] = *(const uint32_t*)(pw + GM_SGROUP_HALF + (wn * 64 + j * 32 + r32) * 16) >> (8 * g); \
     }                                                                                       \
   }
 // E4M3: one instruction per 32 x 32 block and stage.  E2M1: two, on the
 // fragment's first 16 bytes (blocks 0, 1 of the stage) and its last 16 bytes
-// (blocks 2, 3), each with its own scales.
-#define GM_MMA1(T)                                                                          \
+// (blocks 2, 3); the scale operand's byte select (checked on the hardware:
+// op_sel k takes byte k) picks byte 0 or 2 of the shifted scale word.
+#define GM_MMA1(T, H_)                                                                      \
   if (FP4) {                                                                                \
     const i32x8 a_ = fa[(T) >> 1], b_ = fb[(T) & 1];                                        \
     acc[(T) >> 1][(T) & 1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(               \
@@ -268,10 +280,13 @@ __global__ __launch_bounds__(GM_THREADS, 1) void k_gemm_mx(int L, int N, int Kd,
         acc[(T) >> 1][(T) & 1], 4, 4, 0, (int)sa[(T) >> 1], 0, (int)sb[(T) & 1]);          \
     acc[(T) >> 1][(T) & 1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(               \
         __builtin_shufflevector(a_, a_, 4, 5, 6, 7, 4, 5, 6, 7), __builtin_shufflevector(b_, b_, 4, 5, 6, 7, 4, 5, 6, 7), \
-        acc[(T) >> 1][(T) & 1], 4, 4, 0, (int)sa2[(T) >> 1], 0, (int)sb2[(T) & 1]);        \
-  } else {                                                                                  \
+        acc[(T) >> 1][(T) & 1], 4, 4, 2, (int)sa[(T) >> 1], 2, (int)sb[(T) & 1]);          \
+  } else if ((H_ & 1) == 0) {                                                               \
     acc[(T) >> 1][(T) & 1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(               \
         fa[(T) >> 1], fb[(T) & 1], acc[(T) >> 1][(T) & 1], 0, 0, 0, (int)sa[(T) >> 1], 0, (int)sb[(T) & 1]); \
+  } else {                                                                                  \
+    acc[(T) >> 1][(T) & 1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(               \
+        fa[(T) >> 1], fb[(T) & 1], acc[(T) >> 1][(T) & 1], 0, 0, 2, (int)sa[(T) >> 1], 2, (int)sb[(T) & 1]); \
   }
 #define GM_FENCE __builtin_amdgcn_sched_barrier(0);
 
@@ -284,7 +299,7 @@ __global__ __launch_bounds__(GM_THREADS, 1) void k_gemm_mx(int L, int N, int Kd,
   while (u < plan.units) {
     const int k0 = cu.k0, k1 = cu.k1;
     i32x8 fa[4], fb[2];
-    uint32_t sa[4], sb[2], sa2[4], sb2[2];  // sa2, sb2: scales of blocks 2, 3 of an E2M1 stage
+    uint32_t sa[4], sb[2];
     f32x16 acc[4][2];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -314,7 +329,7 @@ __global__ __launch_bounds__(GM_THREADS, 1) void k_gemm_mx(int L, int N, int Kd,
       asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory");              \
       GM_FENCE;                                                                             \
       _Pragma("unroll") for (int t = 0; t < 8; ++t) {                                       \
-        if ((t >> 1) < (NB)) GM_MMA1(t);                                                     \
+        if ((t >> 1) < (NB)) GM_MMA1(t, h);                                                  \
       }                                                                                     \
       GM_FENCE;                                                                             \
       asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");                          \
