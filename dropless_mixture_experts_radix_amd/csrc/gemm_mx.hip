@@ -53,6 +53,18 @@ __device__ __forceinline__ SplitPlan gm_split_plan(int total, int G, int KT) {
   return split_plan(total, G, KT / 2);
 }
 
+// Largest value over the 32 lanes of a half wavefront (lanes 32g .. 32g+31):
+// DPP within each row of 16 lanes (quad swaps 1 and 2, then the half-row and
+// row mirrors, each pairing a lane with one from the other half of its group),
+// then a swizzle that swaps the two rows of the half.
+__device__ __forceinline__ uint32_t max_half_wave(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));   // quad_perm [1,0,3,2]
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));   // quad_perm [2,3,0,1]
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false));  // row_half_mirror
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xF, 0xF, false));  // row_mirror
+  return max(v, (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x401F));                 // lane ^ 16
+}
+
 // Epilogue of row blocks [i0, i0+NI) of one wavefront's 128 x 64 part of a
 // tile (MFMA D layout: lane l holds column l%32, rows 8 (v/4) + 4 (l/32) + v%4
 // of each 32 x 32 block).  Every lane of the wavefront must call it (EPI 1
@@ -91,17 +103,12 @@ __device__ __forceinline__ void mx_store_tile(const f32x16 (&acc)[NI][2], int i0
         const int row = wm * 128 + (i0 + i) * 32 + 8 * (v >> 2) + 4 * g + (v & 3);
         // bf16 value of a, then the amax of its MX block (the 32 lanes of this half)
         const uint32_t ab = f32_to_bf16(silu_mul(acc[i][0][v], acc[i][1][v]));
-        uint32_t am = ab & 0x7fffu;
-#pragma unroll
-        for (int o = 1; o < 32; o <<= 1) {
-          const uint32_t x = (uint32_t)__shfl_xor((int)am, o, 64);
-          am = am > x ? am : x;
-        }
+        const uint32_t am = max_half_wave(ab & 0x7fffu);
         if (FP4) {
           // E2M1 codes of columns 2c and 2c+1 share byte c (low nibble first)
           const int E = mx4_scale_exp(am);
           const uint32_t code = mx_e2m1(ab, E);
-          const uint32_t next = (uint32_t)__shfl_xor((int)code, 1, 64);
+          const uint32_t next = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)code, 0xB1, 0xF, 0xF, false);
           if (row < ti.rows && jcol < Fh) {
             const long grow = ti.row0 + row;
             if ((r32 & 1) == 0) out[grow * (Fh >> 1) + (jcol >> 1)] = (uint8_t)(code | (next << 4));
@@ -249,23 +256,15 @@ __global__ __launch_bounds__(GM_THREADS, 1) void k_gemm_mx(int L, int N, int Kd,
       fb[j] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]}; \
     }                                                                                       \
     const int ks = (KS_);                                                                   \
-    if (FP4) {                                                                              \
-      /* the 4 scale bytes of the stage in one word, shifted so that byte 0 is   */         \
-      /* block g (first instruction) and byte 2 block 2 + g (second)             */         \
-      const uint8_t* pw = smem + GM_LDS_SCALES + ((ks >> LG) & 1) * GM_SGROUP_BYTES + (ks & (SG - 1)) * 4; \
-      _Pragma("unroll") for (int i = 0; i < (NB); ++i)                                      \
-        sa[i] = *(const uint32_t*)(pw + (wm * 128 + i * 32 + r32) * 16) >> (8 * g);         \
+    /* scale words: E2M1, the 4 bytes of the stage; E4M3, stages ks and ks + 1 */          \
+    /* (ks even: ring stage ST and ks have the same parity), bytes 0, 1 and    */            \
+    /* 2, 3.  They are shifted by 8 g at the instructions, after the barrier,  */            \
+    /* so that the memory phase does not wait for them on its own.             */            \
+    if (FP4 || ((ST) & 1) == 0) {                                                           \
+      const uint8_t* pw = smem + GM_LDS_SCALES + ((ks >> LG) & 1) * GM_SGROUP_BYTES + (ks & (SG - 1)) * (FP4 ? 4 : 2); \
+      _Pragma("unroll") for (int i = 0; i < (NB); ++i) sa[i] = *(const uint32_t*)(pw + (wm * 128 + i * 32 + r32) * 16); \
       _Pragma("unroll") for (int j = 0; j < 2; ++j)                                         \
-        sb[j] = *(const uint32_t*)(pw + GM_SGROUP_HALF + (wn * 64 + j * 32 + r32) * 16) >> (8 * g); \
-    } else if (((ST) & 1) == 0) {                                                           \
-      /* stages ks, ks + 1 (ks even: ring stage ST and ks have the same parity) */          \
-      /* share a word: bytes 0, 1 and 2, 3 are their blocks; shifted so that   */           \
-      /* byte 0 (stage ks) or byte 2 (stage ks + 1) is block g                  */           \
-      const uint8_t* pw = smem + GM_LDS_SCALES + ((ks >> LG) & 1) * GM_SGROUP_BYTES + (ks & (SG - 1)) * 2; \
-      _Pragma("unroll") for (int i = 0; i < (NB); ++i)                                      \
-        sa[i] = *(const uint32_t*)(pw + (wm * 128 + i * 32 + r32) * 16) >> (8 * g);         \
-      _Pragma("unroll") for (int j = 0; j < 2; ++j)                                         \
-        sb[j] = *(const uint32_t*)(pw + GM_SGROUP_HALF + (wn * 64 + j * 32 + r32) * 16) >> (8 * g); \
+        sb[j] = *(const uint32_t*)(pw + GM_SGROUP_HALF + (wn * 64 + j * 32 + r32) * 16);    \
     }                                                                                       \
   }
 // E4M3: one instruction per 32 x 32 block and stage.  E2M1: two, on the
@@ -277,16 +276,16 @@ __global__ __launch_bounds__(GM_THREADS, 1) void k_gemm_mx(int L, int N, int Kd,
     const i32x8 a_ = fa[(T) >> 1], b_ = fb[(T) & 1];                                        \
     acc[(T) >> 1][(T) & 1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(               \
         __builtin_shufflevector(a_, a_, 0, 1, 2, 3, 0, 1, 2, 3), __builtin_shufflevector(b_, b_, 0, 1, 2, 3, 0, 1, 2, 3), \
-        acc[(T) >> 1][(T) & 1], 4, 4, 0, (int)sa[(T) >> 1], 0, (int)sb[(T) & 1]);          \
+        acc[(T) >> 1][(T) & 1], 4, 4, 0, (int)(sa[(T) >> 1] >> (8 * g)), 0, (int)(sb[(T) & 1] >> (8 * g))); \
     acc[(T) >> 1][(T) & 1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(               \
         __builtin_shufflevector(a_, a_, 4, 5, 6, 7, 4, 5, 6, 7), __builtin_shufflevector(b_, b_, 4, 5, 6, 7, 4, 5, 6, 7), \
-        acc[(T) >> 1][(T) & 1], 4, 4, 2, (int)sa[(T) >> 1], 2, (int)sb[(T) & 1]);          \
+        acc[(T) >> 1][(T) & 1], 4, 4, 2, (int)(sa[(T) >> 1] >> (8 * g)), 2, (int)(sb[(T) & 1] >> (8 * g))); \
   } else if ((H_ & 1) == 0) {                                                               \
     acc[(T) >> 1][(T) & 1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(               \
-        fa[(T) >> 1], fb[(T) & 1], acc[(T) >> 1][(T) & 1], 0, 0, 0, (int)sa[(T) >> 1], 0, (int)sb[(T) & 1]); \
+        fa[(T) >> 1], fb[(T) & 1], acc[(T) >> 1][(T) & 1], 0, 0, 0, (int)(sa[(T) >> 1] >> (8 * g)), 0, (int)(sb[(T) & 1] >> (8 * g))); \
   } else {                                                                                  \
     acc[(T) >> 1][(T) & 1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(               \
-        fa[(T) >> 1], fb[(T) & 1], acc[(T) >> 1][(T) & 1], 0, 0, 2, (int)sa[(T) >> 1], 2, (int)sb[(T) & 1]); \
+        fa[(T) >> 1], fb[(T) & 1], acc[(T) >> 1][(T) & 1], 0, 0, 2, (int)(sa[(T) >> 1] >> (8 * g)), 2, (int)(sb[(T) & 1] >> (8 * g))); \
   }
 #define GM_FENCE __builtin_amdgcn_sched_barrier(0);
 
