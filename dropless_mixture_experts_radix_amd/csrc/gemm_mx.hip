@@ -271,15 +271,20 @@ __global__ __launch_bounds__(GM_THREADS, 1) void k_gemm_mx(int L, int N, int Kd,
 // fragment's first 16 bytes (blocks 0, 1 of the stage) and its last 16 bytes
 // (blocks 2, 3); the scale operand's byte select (checked on the hardware:
 // op_sel k takes byte k) picks byte 0 or 2 of the shifted scale word.
-#define GM_MMA1(T, H_)                                                                      \
+// P: the E2M1 instruction of the block (0: first 16 bytes, 1: last); E4M3
+// blocks have one, issued with P = 0
+#define GM_MMA1(T, H_, P)                                                                   \
   if (FP4) {                                                                                \
     const i32x8 a_ = fa[(T) >> 1], b_ = fb[(T) & 1];                                        \
-    acc[(T) >> 1][(T) & 1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(               \
-        __builtin_shufflevector(a_, a_, 0, 1, 2, 3, 0, 1, 2, 3), __builtin_shufflevector(b_, b_, 0, 1, 2, 3, 0, 1, 2, 3), \
-        acc[(T) >> 1][(T) & 1], 4, 4, 0, (int)(sa[(T) >> 1] >> (8 * g)), 0, (int)(sb[(T) & 1] >> (8 * g))); \
-    acc[(T) >> 1][(T) & 1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(               \
-        __builtin_shufflevector(a_, a_, 4, 5, 6, 7, 4, 5, 6, 7), __builtin_shufflevector(b_, b_, 4, 5, 6, 7, 4, 5, 6, 7), \
-        acc[(T) >> 1][(T) & 1], 4, 4, 2, (int)(sa[(T) >> 1] >> (8 * g)), 2, (int)(sb[(T) & 1] >> (8 * g))); \
+    if ((P) == 0)                                                                           \
+      acc[(T) >> 1][(T) & 1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(             \
+          __builtin_shufflevector(a_, a_, 0, 1, 2, 3, 0, 1, 2, 3), __builtin_shufflevector(b_, b_, 0, 1, 2, 3, 0, 1, 2, 3), \
+          acc[(T) >> 1][(T) & 1], 4, 4, 0, (int)(sa[(T) >> 1] >> (8 * g)), 0, (int)(sb[(T) & 1] >> (8 * g))); \
+    else                                                                                    \
+      acc[(T) >> 1][(T) & 1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(             \
+          __builtin_shufflevector(a_, a_, 4, 5, 6, 7, 4, 5, 6, 7), __builtin_shufflevector(b_, b_, 4, 5, 6, 7, 4, 5, 6, 7), \
+          acc[(T) >> 1][(T) & 1], 4, 4, 2, (int)(sa[(T) >> 1] >> (8 * g)), 2, (int)(sb[(T) & 1] >> (8 * g))); \
+  } else if ((P) == 1) {                                                                    \
   } else if ((H_ & 1) == 0) {                                                               \
     acc[(T) >> 1][(T) & 1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(               \
         fa[(T) >> 1], fb[(T) & 1], acc[(T) >> 1][(T) & 1], 0, 0, 0, (int)(sa[(T) >> 1] >> (8 * g)), 0, (int)(sb[(T) & 1] >> (8 * g))); \
@@ -327,8 +332,13 @@ __global__ __launch_bounds__(GM_THREADS, 1) void k_gemm_mx(int L, int N, int Kd,
       }                                                                                     \
       asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory");              \
       GM_FENCE;                                                                             \
+      /* E2M1: all first instructions, then all second ones (8 apart on an    */            \
+      /* accumulator, as in the bf16 kernel)                                   */            \
       _Pragma("unroll") for (int t = 0; t < 8; ++t) {                                       \
-        if ((t >> 1) < (NB)) GM_MMA1(t, h);                                                  \
+        if ((t >> 1) < (NB)) GM_MMA1(t, h, 0);                                               \
+      }                                                                                     \
+      _Pragma("unroll") for (int t = 0; t < 8; ++t) {                                       \
+        if (FP4 && (t >> 1) < (NB)) GM_MMA1(t, h, 1);                                        \
       }                                                                                     \
       GM_FENCE;                                                                             \
       asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");                          \
