@@ -178,7 +178,13 @@ __global__ __launch_bounds__(1024) void k_scan(int ntiles, int L, int64_t capaci
 // ---------------------------------------------------------------------------
 // k_permute: one wavefront per token, 4 per workgroup.
 // ---------------------------------------------------------------------------
-template <int OUT>  // 0: copy rows (bf16 or fp32, row_bytes), 1: MXFP8-, 2: MXFP4-quantize bf16 rows
+// Fused scan (SCAN = 1, for ntiles * L <= PERMUTE_SCAN_MAX and L <= 64, TT a
+// multiple of 4): `tilebase` holds the raw tile histograms of k_count; every
+// workgroup sums the ones it needs (the tiles before its own, and all of them
+// for the offsets) instead of a separate k_scan, and workgroup 0 writes
+// counts, offsets and the overflow flag.
+#define PERMUTE_SCAN_MAX 4096
+template <int OUT, int SCAN>  // OUT 0: copy rows (bf16 or fp32, row_bytes), 1: MXFP8-, 2: MXFP4-quantize bf16 rows
 __global__ __launch_bounds__(256) void k_permute(int T, int K, int e0, int L, int TT, int64_t capacity,
                                                  int row_bytes, const uint8_t* __restrict__ x,
                                                  const int16_t* __restrict__ ids,
@@ -187,9 +193,44 @@ __global__ __launch_bounds__(256) void k_permute(int T, int K, int e0, int L, in
                                                  const int32_t* __restrict__ offsets,
                                                  uint8_t* __restrict__ x_perm, uint8_t* __restrict__ x_scales,
                                                  int32_t* __restrict__ row_to_slot,
-                                                 int32_t* __restrict__ slot_to_row) {
+                                                 int32_t* __restrict__ slot_to_row, int32_t* __restrict__ counts_out,
+                                                 int32_t* __restrict__ offsets_out, int32_t* err) {
   const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + w;
+  __shared__ int32_t s_sum[2][256];  // SCAN: partial sums (before the tile, total)
+  __shared__ int32_t s_base[64], s_off[64];
+  if (SCAN) {
+    // the workgroup's 4 tokens share one tile (TT % 4 == 0); thread i sums
+    // entries (tile' , e) with e = i % L, tile' = i / L, i / L + 256 / L, ...
+    const int tile0 = (blockIdx.x * 4) / TT, ntiles = (T + TT - 1) / TT;
+    const int e = threadIdx.x % L, step = 256 / L;
+    int before = 0, all = 0;
+    if (threadIdx.x < step * L) {
+      for (int tt = threadIdx.x / L; tt < ntiles; tt += step) {
+        const int c = tilebase[(long)tt * L + e];
+        all += c;
+        before += tt < tile0 ? c : 0;
+      }
+    }
+    s_sum[0][threadIdx.x] = before;
+    s_sum[1][threadIdx.x] = all;
+    __syncthreads();
+    if (w == 0) {
+      int b = 0, a = 0;
+      if (l < L)
+        for (int q = 0; q < step; ++q) { b += s_sum[0][q * L + l]; a += s_sum[1][q * L + l]; }
+      const int incl = wave_incl_scan(l < L ? a : 0);
+      if (l < L) { s_base[l] = b; s_off[l] = incl - a; }
+      if (blockIdx.x == 0) {
+        if (l < L) { counts_out[l] = a; offsets_out[l] = incl - a; }
+        if (l == 63) {
+          offsets_out[L] = incl;
+          if ((int64_t)incl > capacity) set_err(err, MOE_DEVERR_OVERFLOW);
+        }
+      }
+    }
+    __syncthreads();
+  }
   if (t >= T) return;
   const int tile = t / TT;
   int dest = -1;
@@ -198,7 +239,8 @@ __global__ __launch_bounds__(256) void k_permute(int T, int K, int e0, int L, in
     const int id = ids[f];
     if (id >= e0 && id < e0 + L) {
       const int le = id - e0;
-      const int64_t d = (int64_t)offsets[le] + tilebase[(long)tile * L + le] + rank[f];
+      const int64_t d = SCAN ? (int64_t)s_off[le] + s_base[le] + rank[f]
+                             : (int64_t)offsets[le] + tilebase[(long)tile * L + le] + rank[f];
       dest = d < capacity ? (int)d : -1;
     }
     slot_to_row[f] = dest;
@@ -289,36 +331,57 @@ __global__ __launch_bounds__(256) void k_permute(int T, int K, int e0, int L, in
   }
 }
 
+template <int SCAN>
+static void launch_permute_rows(int T, int K, int e0, int L, int TT, int64_t capacity, int row_bytes, int out_dtype,
+                                const void* x, const int16_t* ids, const int32_t* hist, const int32_t* rank,
+                                int32_t* offsets, void* x_perm, uint8_t* x_scales, int32_t* row_to_slot,
+                                int32_t* slot_to_row, int32_t* counts, int32_t* err, hipStream_t s) {
+  const dim3 g((T + 3) / 4), b(256);
+  if (out_dtype == MOE_MXFP8)
+    hipLaunchKernelGGL((k_permute<1, SCAN>), g, b, 0, s, T, K, e0, L, TT, capacity, row_bytes, (const uint8_t*)x,
+                       ids, hist, rank, offsets, (uint8_t*)x_perm, x_scales, row_to_slot, slot_to_row, counts,
+                       offsets, err);
+  else if (out_dtype == MOE_MXFP4)
+    hipLaunchKernelGGL((k_permute<2, SCAN>), g, b, 0, s, T, K, e0, L, TT, capacity, row_bytes, (const uint8_t*)x,
+                       ids, hist, rank, offsets, (uint8_t*)x_perm, x_scales, row_to_slot, slot_to_row, counts,
+                       offsets, err);
+  else
+    hipLaunchKernelGGL((k_permute<0, SCAN>), g, b, 0, s, T, K, e0, L, TT, capacity, row_bytes, (const uint8_t*)x,
+                       ids, hist, rank, offsets, (uint8_t*)x_perm, x_scales, row_to_slot, slot_to_row, counts,
+                       offsets, err);
+}
+
 hipError_t launch_permute(int T, int H, int K, int E_global, int e0, int L, int64_t capacity,
                           int x_dtype, int out_dtype, const void* x, const int16_t* ids,
                           int32_t* counts, int32_t* offsets, void* x_perm, uint8_t* x_scales,
                           int32_t* row_to_slot, int32_t* slot_to_row, int32_t* err, void* ws,
                           hipStream_t s) {
-  const int TT = permute_tile_tokens(T, K);
-  const int ntiles = (T + TT - 1) / TT;
+  int TT = permute_tile_tokens(T, K);
+  int ntiles = (T + TT - 1) / TT;
+  // few tiles and experts: the scan is done inside k_permute (tiles of a
+  // multiple of 4 tokens, so that a permute workgroup's tokens share a tile)
+  const int TT4 = (TT + 3) / 4 * 4;
+  const bool fused = T > 0 && L <= 64 && (long)((T + TT4 - 1) / TT4) * L <= PERMUTE_SCAN_MAX;
+  if (fused) {
+    TT = TT4;
+    ntiles = (T + TT - 1) / TT;
+  }
   int32_t* hist = (int32_t*)ws;
-  int32_t* rank = hist + (size_t)ntiles * L;
+  int32_t* rank = hist + (size_t)ntiles * L;  // within the workspace (sized for the unrounded tiling)
   if (ntiles > 0) {
     const size_t lds = (size_t)(4 * L + TT * K) * sizeof(int32_t);
     hipLaunchKernelGGL(k_count, dim3(ntiles), dim3(256), lds, s, T, K, E_global, e0, L, TT, ids, hist,
                        rank, err);
   }
-  hipLaunchKernelGGL(k_scan, dim3(1), dim3(1024), 0, s, ntiles, L, capacity, hist, counts, offsets, err);
-  if (T > 0) {
-    const int row_bytes = H * (x_dtype == MOE_F32 ? 4 : 2);
-    const dim3 g((T + 3) / 4), b(256);
-    if (out_dtype == MOE_MXFP8)
-      hipLaunchKernelGGL(k_permute<1>, g, b, 0, s, T, K, e0, L, TT, capacity, row_bytes,
-                         (const uint8_t*)x, ids, hist, rank, offsets, (uint8_t*)x_perm, x_scales,
-                         row_to_slot, slot_to_row);
-    else if (out_dtype == MOE_MXFP4)
-      hipLaunchKernelGGL(k_permute<2>, g, b, 0, s, T, K, e0, L, TT, capacity, row_bytes,
-                         (const uint8_t*)x, ids, hist, rank, offsets, (uint8_t*)x_perm, x_scales,
-                         row_to_slot, slot_to_row);
-    else
-      hipLaunchKernelGGL(k_permute<0>, g, b, 0, s, T, K, e0, L, TT, capacity, row_bytes,
-                         (const uint8_t*)x, ids, hist, rank, offsets, (uint8_t*)x_perm, x_scales,
-                         row_to_slot, slot_to_row);
+  const int row_bytes = H * (x_dtype == MOE_F32 ? 4 : 2);
+  if (fused) {
+    launch_permute_rows<1>(T, K, e0, L, TT, capacity, row_bytes, out_dtype, x, ids, hist, rank, offsets, x_perm,
+                           x_scales, row_to_slot, slot_to_row, counts, err, s);
+  } else {
+    hipLaunchKernelGGL(k_scan, dim3(1), dim3(1024), 0, s, ntiles, L, capacity, hist, counts, offsets, err);
+    if (T > 0)
+      launch_permute_rows<0>(T, K, e0, L, TT, capacity, row_bytes, out_dtype, x, ids, hist, rank, offsets, x_perm,
+                             x_scales, row_to_slot, slot_to_row, counts, err, s);
   }
   return hipGetLastError();
 }
