@@ -39,7 +39,9 @@ RouteSplit route_split(int T, int E, int H, int x_dtype) {
 // Router weight preparation: W_r [H,E] -> bf16 [C][H] term rows (bf16 x) or a
 // plain fp32 copy (fp32 x).  For fp32 W_r each weight w = hi + mid + lo with
 // hi = bf16(w), mid = bf16(w - hi), lo = bf16(w - hi - mid); both differences
-// are exact in fp32.
+// are exact in fp32.  A single 32-row tile (C = 32, H % 32 == 0: the fused
+// small-router path) is stored k-blocked, [H/32][32 rows][32], so that the 16
+// rows x 32 k of one MFMA operand load are one contiguous KiB.
 // ---------------------------------------------------------------------------
 __global__ void k_prepare_router_bf16(const void* __restrict__ w, int w_dtype, int H, int E, int C,
                                       bf16_t* __restrict__ out) {
@@ -63,7 +65,8 @@ __global__ void k_prepare_router_bf16(const void* __restrict__ w, int w_dtype, i
         v = p == 0 ? hi : (p == 1 ? mid : lo);
       }
     }
-    out[i] = (bf16_t)v;
+    const long o = (C == 32 && H % 32 == 0) ? ((long)(h >> 5) * 32 + row) * 32 + (h & 31) : i;
+    out[o] = (bf16_t)v;
   }
 }
 
@@ -325,8 +328,9 @@ __global__ __launch_bounds__(64 * RF_WAVES) void k_route_fused_small(int T, int 
   const int k0s = min(w * per, nks), k1s = min(k0s + per, nks);
   // lane (q, r): token row r (A) or prepared rows r and 16 + r (B), k = 8q..8q+7 of a slice
   const bf16_t* pa = x + (long)ra * H + 8 * q;
-  const bf16_t* pw0 = wp + (long)r * H + 8 * q;
-  const bf16_t* pw1 = wp + (long)(16 + r) * H + 8 * q;
+  // prepared rows k-blocked [H/32][32][32]: slice ks of row r at (ks*32 + r)*32
+  const bf16_t* pw0 = wp + r * 32 + 8 * q;
+  const bf16_t* pw1 = wp + (16 + r) * 32 + 8 * q;
   typedef float f32x4v __attribute__((ext_vector_type(4)));
   f32x4v acc[2][2] = {};  // [slice parity][column tile]
   int ks = k0s;
@@ -336,8 +340,8 @@ __global__ __launch_bounds__(64 * RF_WAVES) void k_route_fused_small(int T, int 
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       a[u] = *(const bf16x8*)(pa + (ks + u) * 32);
-      b0[u] = r < PE ? *(const bf16x8*)(pw0 + (ks + u) * 32) : bf16x8{};
-      b1[u] = 16 + r < PE ? *(const bf16x8*)(pw1 + (ks + u) * 32) : bf16x8{};
+      b0[u] = r < PE ? *(const bf16x8*)(pw0 + (ks + u) * 1024) : bf16x8{};
+      b1[u] = 16 + r < PE ? *(const bf16x8*)(pw1 + (ks + u) * 1024) : bf16x8{};
     }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -348,8 +352,8 @@ __global__ __launch_bounds__(64 * RF_WAVES) void k_route_fused_small(int T, int 
   }
   for (; ks < k1s; ++ks) {
     const bf16x8 a = *(const bf16x8*)(pa + ks * 32);
-    const bf16x8 b0 = r < PE ? *(const bf16x8*)(pw0 + ks * 32) : bf16x8{};
-    const bf16x8 b1 = 16 + r < PE ? *(const bf16x8*)(pw1 + ks * 32) : bf16x8{};
+    const bf16x8 b0 = r < PE ? *(const bf16x8*)(pw0 + ks * 1024) : bf16x8{};
+    const bf16x8 b1 = 16 + r < PE ? *(const bf16x8*)(pw1 + ks * 1024) : bf16x8{};
     acc[0][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b0, acc[0][0], 0, 0, 0);
     acc[0][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b1, acc[0][1], 0, 0, 0);
   }

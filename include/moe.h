@@ -130,7 +130,9 @@ size_t moe_router_prepared_bytes(int H, int E, int w_dtype, int x_dtype);
  *    weight (P = 3, hi/mid/lo with W = hi + mid + lo, for fp32 W_r; P = 1 for
  *    bf16 W_r) a tile holds ept = floor(32/P) experts: row 32*t + p*ept + j
  *    holds term p of column e = t*ept + j of W_r.  C = ceil(E/ept)*32; rows
- *    with p >= P or e >= E are zero.
+ *    with p >= P or e >= E are zero.  When C == 32 and H % 32 == 0 (one
+ *    tile: the fused small-router path) the tile is k-blocked instead:
+ *    element (row, h) at ((h/32)*32 + row)*32 + h%32.
  *  x_dtype MOE_F32: fp32 W_r [H,E] copied unchanged. */
 int moe_prepare_router(const void* w_router, int w_dtype, int x_dtype, int H, int E,
                        void* prepared, void* stream);

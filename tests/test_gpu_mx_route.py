@@ -82,7 +82,8 @@ def _check_route(ids, probs, lo, T, K, score, bias=None, mask=None):
 
 
 @pytest.mark.parametrize("cfgname,T", [("tiny_f32", 256), ("mixtral_bf16", 1024), ("mixtral_bf16", 4096),
-                                       ("mixtral_bf16", 1000), ("dsv3_bf16", 1024), ("dsv3_bf16", 8192)])
+                                       ("mixtral_bf16", 1000), ("mixtral_bf16", 4113), ("dsv3_bf16", 1024),
+                                       ("dsv3_bf16", 8192)])
 def test_route_fused_projection_workloads(cfgname, T):
     cfg = get_config(cfgname)
     say("route", cfgname, T)
