@@ -90,6 +90,10 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[NI][2], int i0, c
                                            int64_t capacity, int wm, int wn, int g, int r32,
                                            bf16_t* __restrict__ out) {
   const int col0 = ti.nt * GB_BN;
+  // the lane's row and column offsets are made opaque here, so the compiler
+  // cannot hoist the 16 row numbers per block out of the persistent loop into
+  // registers held across the k loop (where they would be spilled)
+  asm volatile("" : "+v"(g), "+v"(r32));
 #pragma unroll
   for (int ii = 0; ii < NI; ++ii) {
     const int rb = wm * 128 + (i0 + ii) * 32;

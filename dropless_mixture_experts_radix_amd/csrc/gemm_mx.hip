@@ -75,6 +75,9 @@ __device__ __forceinline__ void mx_store_tile(const f32x16 (&acc)[NI][2], int i0
                                               uint8_t* __restrict__ out_s) {
   const int col0 = ti.nt * GM_BN;
   const int msub = min(4, max(0, (ti.rows - wm * 128 + 31) / 32));
+  // opaque lane offsets: the compiler cannot hoist the per-row numbers out of
+  // the persistent loop into registers held (and spilled) across the k loop
+  asm volatile("" : "+v"(g), "+v"(r32));
   if (EPI == 0) {
     bf16_t* y = (bf16_t*)out;
 #pragma unroll

@@ -173,7 +173,7 @@ size_t moe_prepared_weight_bytes(int L, int H, int F, int dtype, int which) {
 int moe_prepare_weights(int L, int H, int F, int in_dtype, int dtype, const void* w1, const void* w2,
                         void* w1p, void* w2p, uint8_t* w1p_scales, uint8_t* w2p_scales, void* stream) {
   if (L < 1 || L > MOE_MAX_L || H <= 0 || F <= 0 || H % 32 || F % 32) return MOE_ERR_SHAPE;
-  if (dtype == MOE_BF16 && (H % 128 || F % 128)) return MOE_ERR_SHAPE;  // pairs of 64-wide k steps
+  if (dtype == MOE_BF16 && (H % 128 || F % 128)) return MOE_ERR_SHAPE;  // groups of 4 32-wide k steps
   if (dtype == MOE_MXFP8 && (H % 256 || F % 256)) return MOE_ERR_SHAPE;  // groups of 4 64-wide k stages
   if (dtype == MOE_MXFP4 && (H % 512 || F % 512)) return MOE_ERR_SHAPE;  // groups of 4 128-wide k stages
   if (!((dtype == MOE_F32 && in_dtype == MOE_F32) || (dtype == MOE_BF16 && in_dtype == MOE_BF16) ||
