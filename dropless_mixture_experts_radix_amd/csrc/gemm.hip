@@ -74,12 +74,27 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 #define GB_BN 256
 #define GB_BK 32
 #define GB_THREADS 512
-#define GB_STAGE_BYTES 32768        // A and B k-step tiles of one stage
-#define GB_PART_FLOATS (GB_BM * GB_BN)
+#define GB_X_OFF 32768              // the 32 extra A rows of a tall tile, after A and B
+#define GB_STAGE_BYTES (GB_X_OFF + 2048)
+#define GB_TALL 32                  // rows a tall tile has beyond GB_BM
+// a split-K partial tile: the 8 wavefront parts of 128 x 64, then the 32 x 64
+// extra-row blocks of wavefronts 0-3 (tall tiles)
+#define GB_PART_X (GB_BM * GB_BN)
+#define GB_PART_FLOATS (GB_PART_X + 4 * 2048)
 
 // split plan of the bf16 kernel: pieces are whole groups of 4 k steps
 __device__ __forceinline__ SplitPlan gb_split_plan(int total, int G, int Kd) {
   return split_plan(total, G, Kd / 64);
+}
+
+// Tile schedule and split plan of the bf16 kernel on a grid of G workgroups,
+// with tall tiles: a remainder of up to GB_TALL rows joins the expert's last
+// full tile, which then has up to GB_BM + GB_TALL rows.
+__device__ __forceinline__ SplitPlan gb_schedule(int L, int64_t capacity, int NT, int Kd, int G,
+                                                 const int32_t* __restrict__ offsets, int32_t* s_pre,
+                                                 int32_t* s_tmp) {
+  build_schedule(L, capacity, GB_BM, NT, offsets, s_pre, s_tmp, GB_TALL);
+  return gb_split_plan(s_pre[L], G, Kd);
 }
 
 // Epilogue of rows [i0, i0+NI) x 32 of one wavefront's 128 x 64 part of a
@@ -136,8 +151,7 @@ __global__ __launch_bounds__(GB_THREADS, 1) void k_gemm_bf16(int L, int N, int K
     plan.S = L;
     plan.units = (int)((capacity + GB_BM - 1) / GB_BM) * NT * L;
   } else {
-    build_schedule(L, capacity, GB_BM, NT, offsets, s_pre, s_tmp);
-    plan = gb_split_plan(s_pre[L], gridDim.x, Kd);
+    plan = gb_schedule(L, capacity, NT, Kd, gridDim.x, offsets, s_pre, s_tmp);
   }
   const int tid = threadIdx.x, l = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -159,7 +173,7 @@ __global__ __launch_bounds__(GB_THREADS, 1) void k_gemm_bf16(int L, int N, int K
     TileInfo ti;
     int piece, k0, k1, akstep, bkstep;
     __amdgpu_buffer_rsrc_t rA, rB;
-    int va[2], vb[2];
+    int va[2], vb[2], vx;
   };
   auto setup = [&](int u) {
     Unit w;
@@ -186,7 +200,7 @@ __global__ __launch_bounds__(GB_THREADS, 1) void k_gemm_bf16(int L, int N, int K
         w.k0 = 4 * (q * nq / plan.S);
         w.k1 = 4 * ((q + 1) * nq / plan.S);
       }
-      w.ti = locate_tile(tile, L, capacity, GB_BM, NT, offsets, s_pre);
+      w.ti = locate_tile(tile, L, capacity, GB_BM, NT, offsets, s_pre, GB_TALL);
     }
     // the unit is the same for every lane: keep it in scalar registers (the
     // buffer resources built from it are scalar operands of the loads)
@@ -217,6 +231,11 @@ __global__ __launch_bounds__(GB_THREADS, 1) void k_gemm_bf16(int L, int N, int K
       w.va[q] = EPI != 0 ? (r * Kd + dch * 8) * 2 : ((w.ti.row0 + r) * GB_BK + dch * 8) * 2;
       w.vb[q] = EPI == 2 ? (r * Kd + dch * 8) * 2 : r * 64 + dch * 16;
     }
+    {  // the dword of the extra rows (tall tile) that this lane moves: row
+       // GB_BM + 4 wv + l/16, chunk position (l%16)/4, dword l%4
+      const int xr = 4 * wv + (l >> 4), xc = (((l & 15) >> 2) ^ swz4(xr)) * 16 + (l & 3) * 4;
+      w.vx = EPI != 0 ? (GB_BM + xr) * Kd * 2 + xc : ((w.ti.row0 + GB_BM + xr) * GB_BK) * 2 + xc;
+    }
     w.akstep = EPI != 0 ? GB_BK * 2 : (int)(capacity * GB_BK * 2);
     w.bkstep = EPI == 2 ? GB_BK * 2 : GB_BN * GB_BK * 2;
     return w;
@@ -225,17 +244,26 @@ __global__ __launch_bounds__(GB_THREADS, 1) void k_gemm_bf16(int L, int N, int K
 #define GB_DMA(W, ST, KT_, Q)                                                               \
   {                                                                                         \
     const int kq = (KT_);                                                                   \
-    if ((Q) < 2)                                                                            \
+    if ((Q) == 4)                                                                           \
+      lds_dma_b32(lds0 + (ST) * GB_STAGE_BYTES + GB_X_OFF + wv * 256, (W).vx, (W).rA, kq * (W).akstep); \
+    else if ((Q) < 2)                                                                       \
       lds_dma_b128(lds0 + (ST) * GB_STAGE_BYTES + (wv * 2 + (Q)) * 1024, (W).va[Q], (W).rA, kq * (W).akstep); \
     else                                                                                    \
       lds_dma_b128(lds0 + (ST) * GB_STAGE_BYTES + 16384 + (wv * 2 + (Q) - 2) * 1024, (W).vb[(Q) - 2], (W).rB, \
                    kq * (W).bkstep);                                                        \
   }
-// the ring prologue of a unit: its steps k0 .. k0+2 into stages 0..2
+// the ring prologue of a unit: its steps k0 .. k0+2 into stages 0..2 (a tall
+// tile's steps also carry its extra rows: 5 loads per step instead of 4)
 #define GB_PROLOGUE(W)                                                                      \
   {                                                                                         \
-    _Pragma("unroll") for (int st = 0; st < 3; ++st) {                                      \
-      _Pragma("unroll") for (int q = 0; q < 4; ++q) GB_DMA(W, st, min((W).k0 + st, (W).k1 - 1), q); \
+    if ((W).ti.rows > GB_BM) {                                                              \
+      _Pragma("unroll") for (int st = 0; st < 3; ++st) {                                    \
+        _Pragma("unroll") for (int q = 0; q < 5; ++q) GB_DMA(W, st, min((W).k0 + st, (W).k1 - 1), q); \
+      }                                                                                     \
+    } else {                                                                                \
+      _Pragma("unroll") for (int st = 0; st < 3; ++st) {                                    \
+        _Pragma("unroll") for (int q = 0; q < 4; ++q) GB_DMA(W, st, min((W).k0 + st, (W).k1 - 1), q); \
+      }                                                                                     \
     }                                                                                       \
   }
 #define GB_READ(FA, FB, ST, FR, NB)                                                         \
@@ -247,6 +275,7 @@ __global__ __launch_bounds__(GB_THREADS, 1) void k_gemm_bf16(int L, int N, int K
       _Pragma("unroll") for (int j = 0; j < 2; ++j) FB[j] = *(const bf16x8*)(pb + j * 2048); \
     }                                                                                       \
   }
+#define GB_READX(FX, ST, FR) FX = *(const bf16x8*)(smem + (ST) * GB_STAGE_BYTES + GB_X_OFF + (FR));
 #define GB_MMA1(FA, FB, T)                                                                  \
   acc[(T) >> 1][(T) & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(FA[(T) >> 1], FB[(T) & 1], acc[(T) >> 1][(T) & 1], 0, 0, 0);
 #define GB_FENCE __builtin_amdgcn_sched_barrier(0);
@@ -259,12 +288,13 @@ __global__ __launch_bounds__(GB_THREADS, 1) void k_gemm_bf16(int L, int N, int K
   }
   while (u < plan.units) {
     const int k0 = cu.k0, k1 = cu.k1;
-    bf16x8 fa[2][4], fb[2][2];  // fragments of both sub-steps of one k step
-    f32x16 acc[4][2];
+    bf16x8 fa[2][4], fb[2][2], fx[2];  // fragments of both sub-steps of one k step
+    f32x16 acc[4][2], accx[1][2];      // accx: the extra rows of a tall tile
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
+    accx[0][0] = accx[0][1] = f32x16{};
     // wait for step k0 (the younger steps k0+1, k0+2 may still be loading;
     // loads complete in issue order, and the previous unit's epilogue stores
     // were issued after them)
@@ -281,36 +311,61 @@ __global__ __launch_bounds__(GB_THREADS, 1) void k_gemm_bf16(int L, int N, int K
     // step kt while group 0 reads step kt+1.  The stage of step kt+1 is complete
     // for all wavefronts at the barrier that starts group 0's memory phase of
     // step kt+1.
-#define GB_KLOOP(NB)                                                                        \
+#define GB_KLOOP(NB, NL, XM)                                                                \
   for (int kt = k0; kt < k1; kt += 4) {                                                     \
     _Pragma("unroll") for (int h = 0; h < 4; ++h) {                                         \
       GB_READ(fa[0], fb[0], h, fr0, NB);                                                    \
       GB_READ(fa[1], fb[1], h, fr1, NB);                                                    \
+      if (XM) {                                                                             \
+        GB_READX(fx[0], h, fr0);                                                            \
+        GB_READX(fx[1], h, fr1);                                                            \
+      }                                                                                     \
       {                                                                                     \
         const int kn = min(kt + h + 3, k1 - 1);                                             \
-        _Pragma("unroll") for (int q = 0; q < 4; ++q) GB_DMA(cu, (h + 3) & 3, kn, q);      \
+        _Pragma("unroll") for (int q = 0; q < (NL); ++q) GB_DMA(cu, (h + 3) & 3, kn, q);   \
       }                                                                                     \
-      asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory");              \
+      if ((NL) == 5) asm volatile("s_waitcnt vmcnt(10) lgkmcnt(0)\n\ts_barrier" ::: "memory"); \
+      else asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory");       \
       GB_FENCE;                                                                             \
       _Pragma("unroll") for (int t = 0; t < 8; ++t) {                                       \
         if ((t >> 1) < (NB)) GB_MMA1(fa[0], fb[0], t);                                       \
       }                                                                                     \
+      if (XM) {                                                                             \
+        accx[0][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fx[0], fb[0][0], accx[0][0], 0, 0, 0); \
+        accx[0][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fx[0], fb[0][1], accx[0][1], 0, 0, 0); \
+      }                                                                                     \
       _Pragma("unroll") for (int t = 0; t < 8; ++t) {                                       \
         if ((t >> 1) < (NB)) GB_MMA1(fa[1], fb[1], t);                                       \
       }                                                                                     \
+      if (XM) {                                                                             \
+        accx[0][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fx[1], fb[1][0], accx[0][0], 0, 0, 0); \
+        accx[0][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fx[1], fb[1][1], accx[0][1], 0, 0, 0); \
+      }                                                                                     \
       GB_FENCE;                                                                             \
-      asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");                          \
+      if ((NL) == 5) asm volatile("s_waitcnt vmcnt(10)\n\ts_barrier" ::: "memory");       \
+      else asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");                  \
     }                                                                                       \
   }
     // a wavefront reads fragments for and multiplies only the 32-row blocks of
     // its 128 rows that hold rows of the tile (the short last tile of an
-    // expert); all versions of the loop have the same loads and barriers
-    switch (min(4, max(0, (cu.ti.rows - wm * 128 + 31) / 32))) {
-      case 4: GB_KLOOP(4); break;
-      case 3: GB_KLOOP(3); break;
-      case 2: GB_KLOOP(2); break;
-      case 1: GB_KLOOP(1); break;
-      default: GB_KLOOP(0); break;
+    // expert); all versions of the loop have the same loads and barriers.  A
+    // tall tile (GB_BM + up to GB_TALL rows) moves its extra rows with a fifth
+    // load per step in every wavefront, and wavefronts 0-3 multiply them by
+    // the B fragments they hold (rows 256.. of their 64 columns).
+    if (cu.ti.rows > GB_BM) {
+      if (wm == 0) {
+        GB_KLOOP(4, 5, 1);
+      } else {
+        GB_KLOOP(4, 5, 0);
+      }
+    } else {
+      switch (min(4, max(0, (cu.ti.rows - wm * 128 + 31) / 32))) {
+        case 4: GB_KLOOP(4, 4, 0); break;
+        case 3: GB_KLOOP(3, 4, 0); break;
+        case 2: GB_KLOOP(2, 4, 0); break;
+        case 1: GB_KLOOP(1, 4, 0); break;
+        default: GB_KLOOP(0, 4, 0); break;
+      }
     }
 #undef GB_KLOOP
     if (!gp) asm volatile("s_barrier" ::: "memory");
@@ -339,6 +394,7 @@ __global__ __launch_bounds__(GB_THREADS, 1) void k_gemm_bf16(int L, int N, int K
         }
     } else if (done.piece < 0) {
       store_tile<EPI, 4>(acc, 0, done.ti, N, capacity, wm, wn, g, r32, out);
+      if (done.ti.rows > GB_BM && wm == 0) store_tile<EPI, 1>(accx, 8, done.ti, N, capacity, 0, wn, g, r32, out);
     } else {
       // partial tile, per wavefront [i][j][lane][16 values of the MFMA D layout]
       float* dst = part + (long)done.piece * GB_PART_FLOATS + wv * 8192 + l * 16;
@@ -350,11 +406,21 @@ __global__ __launch_bounds__(GB_THREADS, 1) void k_gemm_bf16(int L, int N, int K
           for (int c = 0; c < 4; ++c)
             *(f32x4*)(dst + (i * 2 + j) * 1024 + c * 4) =
                 f32x4{acc[i][j][4 * c], acc[i][j][4 * c + 1], acc[i][j][4 * c + 2], acc[i][j][4 * c + 3]};
+      if (done.ti.rows > GB_BM && wm == 0) {  // the extra rows: [wavefront][j][lane][16]
+        float* dx = part + (long)done.piece * GB_PART_FLOATS + GB_PART_X + wv * 2048 + l * 16;
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int c = 0; c < 4; ++c)
+            *(f32x4*)(dx + j * 1024 + c * 4) = f32x4{accx[0][j][4 * c], accx[0][j][4 * c + 1],
+                                                     accx[0][j][4 * c + 2], accx[0][j][4 * c + 3]};
+      }
     }
   }
 #undef GB_DMA
 #undef GB_PROLOGUE
 #undef GB_READ
+#undef GB_READX
 #undef GB_MMA1
 #undef GB_FENCE
   // the last prefetches of the ring (clamped repeats) land before the exit
@@ -363,25 +429,32 @@ __global__ __launch_bounds__(GB_THREADS, 1) void k_gemm_bf16(int L, int N, int K
 
 // Sum the S split-K partials of each split tile (in piece order) and apply the
 // epilogue.  Launched with the GEMM's grid size G on GEMM_SPLIT_UNITS / 2 x 8
-// workgroups of four wavefronts: workgroup (b, w) handles the part of GEMM
-// wavefront w of split tile b of the plan, its wavefront i row block i.
+// workgroups of five wavefronts: workgroup (b, w) handles the part of GEMM
+// wavefront w of split tile b of the plan, its wavefront i < 4 row block i,
+// and its wavefront 4 the extra rows of a tall tile (GEMM wavefronts 0-3).
 template <int EPI>
-__global__ __launch_bounds__(256) void k_splitk_reduce(int L, int N, int Kd, int64_t capacity, int G,
+__global__ __launch_bounds__(320) void k_splitk_reduce(int L, int N, int Kd, int64_t capacity, int G,
                                                        const int32_t* __restrict__ offsets,
                                                        const float* __restrict__ part, bf16_t* __restrict__ out) {
   __shared__ int32_t s_pre[MOE_MAX_L + 1];
   __shared__ int32_t s_tmp[16];
   const int NT = (N + GB_BN - 1) / GB_BN;
-  build_schedule(L, capacity, GB_BM, NT, offsets, s_pre, s_tmp);
+  const SplitPlan plan = gb_schedule(L, capacity, NT, Kd, G, offsets, s_pre, s_tmp);
   const int total = s_pre[L];
-  const SplitPlan plan = gb_split_plan(total, G, Kd);
   const int b = blockIdx.x >> 3, wv = blockIdx.x & 7, i = threadIdx.x >> 6, l = threadIdx.x & 63;
   if (plan.S < 2 || b >= total - plan.dp) return;
-  const TileInfo ti = locate_tile(plan.dp + b, L, capacity, GB_BM, NT, offsets, s_pre);
-  if (ti.rows <= (wv >> 2) * 128 + i * 32) return;  // row block past the tile's rows
+  const TileInfo ti = locate_tile(plan.dp + b, L, capacity, GB_BM, NT, offsets, s_pre, GB_TALL);
+  const float* src = part + (long)b * plan.S * GB_PART_FLOATS + l * 16;
   f32x16 acc[1][2];
-  sum_partials(part + (long)b * plan.S * GB_PART_FLOATS + wv * 8192 + i * 2048 + l * 16, plan.S, acc);
-  store_tile<EPI, 1>(acc, i, ti, N, capacity, wv >> 2, wv & 3, l >> 5, l & 31, out);
+  if (i < 4) {
+    if (ti.rows <= (wv >> 2) * 128 + i * 32) return;  // row block past the tile's rows
+    sum_partials(src + wv * 8192 + i * 2048, plan.S, acc, GB_PART_FLOATS);
+    store_tile<EPI, 1>(acc, i, ti, N, capacity, wv >> 2, wv & 3, l >> 5, l & 31, out);
+  } else {
+    if (wv >= 4 || ti.rows <= GB_BM) return;
+    sum_partials(src + GB_PART_X + wv * 2048, plan.S, acc, GB_PART_FLOATS);
+    store_tile<EPI, 1>(acc, 8, ti, N, capacity, 0, wv, l >> 5, l & 31, out);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -530,7 +603,7 @@ hipError_t launch_grouped_mlp_bf16(int L, int H, int F, int64_t capacity, const 
   const int N1 = 2 * F, N2 = H;
   const int G1 = grid_for(capacity, L, GB_BM, (N1 + GB_BN - 1) / GB_BN, 1);
   const int G2 = grid_for(capacity, L, GB_BM, (N2 + GB_BN - 1) / GB_BN, 1);
-  const dim3 rgrid(GEMM_SPLIT_UNITS / 2 * 8), rblk(256), blk(GB_THREADS);
+  const dim3 rgrid(GEMM_SPLIT_UNITS / 2 * 8), rblk(320), blk(GB_THREADS);
   hipLaunchKernelGGL(k_gemm_bf16<1>, dim3(G1), blk, lds, s, L, N1, H, capacity, x, offsets, w1p, act, part);
   hipLaunchKernelGGL(k_splitk_reduce<1>, rgrid, rblk, 0, s, L, N1, H, capacity, G1, offsets, part, act);
   hipLaunchKernelGGL(k_gemm_bf16<0>, dim3(G2), blk, lds, s, L, N2, F, capacity, act, offsets, w2p, y, part);

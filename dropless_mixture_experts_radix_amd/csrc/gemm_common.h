@@ -21,8 +21,16 @@ static inline int num_cus() {
 // Device tile schedule.  s_pre[e] = first tile of expert e, s_pre[L] = total.
 // Row range of expert e: [min(offsets[e], cap), min(offsets[e+1], cap)).
 // ---------------------------------------------------------------------------
+// Row tiles of an expert with m rows: ceil(m/BM); with tall > 0, a remainder
+// of at most `tall` rows after at least one full tile joins the last full tile
+// instead (that tile then has BM + remainder rows).
+__device__ __forceinline__ int row_tiles(int m, int BM, int tall) {
+  const int f = m / BM, r = m - f * BM;
+  return (r > 0 && (r > tall || f == 0)) ? f + 1 : f;
+}
+
 __device__ inline void build_schedule(int L, int64_t capacity, int BM, int NT, const int32_t* __restrict__ offsets,
-                               int32_t* s_pre, int32_t* s_tmp) {
+                               int32_t* s_pre, int32_t* s_tmp, int tall = 0) {
   const int nth = blockDim.x, tid = threadIdx.x;
   const int per = (L + nth - 1) / nth;
   const int b0 = tid * per;
@@ -34,7 +42,7 @@ __device__ inline void build_schedule(int L, int64_t capacity, int BM, int NT, c
       lo = lo < capacity ? lo : capacity;
       hi = hi < capacity ? hi : capacity;
       const int m = hi > lo ? (int)(hi - lo) : 0;
-      loc += ((m + BM - 1) / BM) * NT;
+      loc += row_tiles(m, BM, tall) * NT;
     }
   }
   const int incl = wave_incl_scan(loc);
@@ -52,7 +60,7 @@ __device__ inline void build_schedule(int L, int64_t capacity, int BM, int NT, c
       lo = lo < capacity ? lo : capacity;
       hi = hi < capacity ? hi : capacity;
       const int m = hi > lo ? (int)(hi - lo) : 0;
-      run += ((m + BM - 1) / BM) * NT;
+      run += row_tiles(m, BM, tall) * NT;
     }
   }
   if (tid == nth - 1) s_pre[L] = run;
@@ -66,7 +74,8 @@ struct TileInfo {
 };
 
 __device__ __forceinline__ TileInfo locate_tile(int it, int L, int64_t capacity, int BM, int NT,
-                                                const int32_t* __restrict__ offsets, const int32_t* s_pre) {
+                                                const int32_t* __restrict__ offsets, const int32_t* s_pre,
+                                                int tall = 0) {
   // largest e with s_pre[e] <= it (empty experts share their start with the next)
   int lo = 0, hi = L - 1;
   while (lo < hi) {
@@ -78,7 +87,7 @@ __device__ __forceinline__ TileInfo locate_tile(int it, int L, int64_t capacity,
   r0 = r0 < capacity ? r0 : capacity;
   r1 = r1 < capacity ? r1 : capacity;
   const int m = (int)(r1 - r0);
-  const int mt_e = (m + BM - 1) / BM;
+  const int mt_e = row_tiles(m, BM, tall);
   const int local = it - s_pre[e];
   // an expert's tiles go in groups of up to TILE_MGROUP row tiles: all column
   // tiles of a group, row tile fastest, then the next group.  The 32 CUs of an
@@ -93,7 +102,7 @@ __device__ __forceinline__ TileInfo locate_tile(int it, int L, int64_t capacity,
   ti.nt = rem / mg;
   const int mt = g * TILE_MGROUP + rem % mg;
   ti.row0 = (int)r0 + mt * BM;
-  ti.rows = min(BM, m - mt * BM);
+  ti.rows = mt == mt_e - 1 ? m - mt * BM : BM;  // the last one takes the remainder
   return ti;
 }
 
@@ -152,6 +161,14 @@ __device__ __forceinline__ void lds_dma_b128(uint32_t lds_addr, int voff, __amdg
                : "memory", "m0");
 }
 
+// 4 bytes per lane: lane i's dword lands at lds_addr + 4 * i
+__device__ __forceinline__ void lds_dma_b32(uint32_t lds_addr, int voff, __amdgpu_buffer_rsrc_t rsrc, int soff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 4\n\tbuffer_load_dword %1, %2, %3 offen lds"
+               :
+               : "s"(lds_addr), "v"(voff), "s"(rsrc), "s"(soff)
+               : "memory", "m0");
+}
+
 // lds_dma_b128 when `sel` == `want` (both wave-uniform).  The test and branch
 // are inside the assembly so that the compiler sees straight-line code.
 __device__ __forceinline__ void lds_dma_b128_if(int sel, int want, uint32_t lds_addr, int voff,
@@ -163,7 +180,7 @@ __device__ __forceinline__ void lds_dma_b128_if(int sel, int want, uint32_t lds_
                : "memory", "m0", "scc");
 }
 
-// Split-K partial tiles: piece q of a split tile at part + q * 65536 floats,
+// Split-K partial tiles: piece q of a split tile at part + q * piece_stride floats,
 // wavefront w's 128 x 64 part at w * 8192, its 32 x 32 block (i, j) at
 // (i * 2 + j) * 1024, lane l's 16 values of the MFMA D layout at l * 16.
 // sum_partials adds the S pieces of row block i of one wavefront part in
@@ -171,7 +188,8 @@ __device__ __forceinline__ void lds_dma_b128_if(int sel, int want, uint32_t lds_
 // loaded before they are added.
 typedef float f32x4_p __attribute__((ext_vector_type(4)));
 typedef float f32x16_p __attribute__((ext_vector_type(16)));
-__device__ __forceinline__ void sum_partials(const float* __restrict__ src, int S, f32x16_p (&acc)[1][2]) {
+__device__ __forceinline__ void sum_partials(const float* __restrict__ src, int S, f32x16_p (&acc)[1][2],
+                                             long piece_stride = 65536) {
   f32x4_p sum[2][4];
 #pragma unroll
   for (int j = 0; j < 2; ++j)
@@ -185,7 +203,7 @@ __device__ __forceinline__ void sum_partials(const float* __restrict__ src, int 
 #pragma unroll
         for (int j = 0; j < 2; ++j)
 #pragma unroll
-          for (int c = 0; c < 4; ++c) t[u][j][c] = *(const f32x4_p*)(src + (long)(q + u) * 65536 + j * 1024 + c * 4);
+          for (int c = 0; c < 4; ++c) t[u][j][c] = *(const f32x4_p*)(src + (q + u) * piece_stride + j * 1024 + c * 4);
 #pragma unroll
     for (int u = 0; u < 4; ++u)
       if (q + u < S)

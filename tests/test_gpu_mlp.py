@@ -198,11 +198,17 @@ def test_grouped_mlp_f32(counts, H, F):
     ([70, 300, 0, 5], 384, 128),          # partial column tiles in both GEMMs
     ([0, 0, 0, 0], 256, 256),             # no rows at all
     ([2048], 512, 512),
-    # 8192 routed rows over 8 experts (36 row tiles) on a 256-CU grid: the 72
-    # tiles of a partial round are split along k into 3 uneven pieces (first
-    # GEMM: k = 3584, 28 groups of 4 steps; second GEMM: k = 4096, 32 groups)
+    # 8192 routed rows over 8 experts (33 row tiles, three of them tall) on a
+    # 256-CU grid: the 66 tiles of a partial round are split along k into 3
+    # uneven pieces (first GEMM: k = 3584, 28 groups of 4 steps; second GEMM:
+    # k = 4096, 32 groups), tall tiles among them
     (MIXTRAL_COUNTS, 3584, 256),
     (MIXTRAL_COUNTS, 512, 4096),
+    # tall tiles: remainders of 1, 16 and 32 rows join the expert's last full
+    # tile (257, 272, 288, 544 rows); 289 rows and a lone 31 do not
+    ([257, 272, 288, 289, 544, 0, 31], 512, 512),
+    # tall tiles in whole rounds of the first GEMM (256 tiles on 256 CUs)
+    ([1054, 994, 1030, 1018, 1040, 1008, 1024, 1024], 512, 1024),
 ])
 def test_grouped_mlp_bf16(counts, H, F):
     _run_mlp(counts, H, F, "bf16", seed=sum(counts) + H)
