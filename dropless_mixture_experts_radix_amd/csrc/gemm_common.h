@@ -169,6 +169,16 @@ __device__ __forceinline__ void lds_dma_b32(uint32_t lds_addr, int voff, __amdgp
                : "memory", "m0");
 }
 
+// lds_dma_b32 when `sel` == `want` (both wave-uniform), as lds_dma_b128_if
+__device__ __forceinline__ void lds_dma_b32_if(int sel, int want, uint32_t lds_addr, int voff,
+                                               __amdgpu_buffer_rsrc_t rsrc, int soff) {
+  asm volatile("s_cmp_eq_u32 %4, %5\n\ts_cbranch_scc0 1f\n\ts_mov_b32 m0, %0\n\ts_nop 4\n\t"
+               "buffer_load_dword %1, %2, %3 offen lds\n1:"
+               :
+               : "s"(lds_addr), "v"(voff), "s"(rsrc), "s"(soff), "s"(sel), "s"(want)
+               : "memory", "m0", "scc");
+}
+
 // lds_dma_b128 when `sel` == `want` (both wave-uniform).  The test and branch
 // are inside the assembly so that the compiler sees straight-line code.
 __device__ __forceinline__ void lds_dma_b128_if(int sel, int want, uint32_t lds_addr, int voff,

@@ -42,11 +42,17 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 #define GM_BN 256
 #define GM_BK 64                       // codes per row and ring stage
 #define GM_THREADS 512
-#define GM_STAGE_BYTES 32768           // A and B tiles of one ring stage
+#define GM_TALL 32                     // rows a tall tile has beyond GM_BM
+// LDS layout (TALL: the kernel instance with tall tiles, whose extra rows add
+// 2 KiB of codes to every ring stage and 512 scale bytes to every scale group)
+#define GM_STAGE_BYTES (TALL ? 34816 : 32768)  // A, B (and the extra rows) of one ring stage
 #define GM_LDS_SCALES (4 * GM_STAGE_BYTES)  // scale buffers after the 4 stages
 #define GM_SGROUP_HALF 4096            // 256 rows x 16 scale bytes (512 codes)
-#define GM_SGROUP_BYTES (2 * GM_SGROUP_HALF)  // A then B
-#define GM_PART_FLOATS (GM_BM * GM_BN)
+#define GM_SGROUP_BYTES (TALL ? 2 * GM_SGROUP_HALF + 512 : 2 * GM_SGROUP_HALF)  // A, B (, extra rows)
+// a split-K partial tile: the 8 wavefront parts of 128 x 64, then the 32 x 64
+// extra-row blocks [wn][wm] (tall tiles)
+#define GM_PART_X (GM_BM * GM_BN)
+#define GM_PART_FLOATS (GM_PART_X + 4 * 2048)
 
 // split plan of the MX kernel over KT stages: pieces are whole groups of 4
 __device__ __forceinline__ SplitPlan gm_split_plan(int total, int G, int KT) {
@@ -74,7 +80,7 @@ __device__ __forceinline__ void mx_store_tile(const f32x16 (&acc)[NI][2], int i0
                                               int g, int r32, uint8_t* __restrict__ out,
                                               uint8_t* __restrict__ out_s) {
   const int col0 = ti.nt * GM_BN;
-  const int msub = min(4, max(0, (ti.rows - wm * 128 + 31) / 32));
+  const int msub = max(0, (ti.rows - wm * 128 + 31) / 32);  // row blocks with rows (9: tall tile)
   // opaque lane offsets: the compiler cannot hoist the per-row numbers out of
   // the persistent loop into registers held (and spilled) across the k loop
   asm volatile("" : "+v"(g), "+v"(r32));
@@ -130,7 +136,7 @@ __device__ __forceinline__ void mx_store_tile(const f32x16 (&acc)[NI][2], int i0
   }
 }
 
-template <int EPI, bool FP4>
+template <int EPI, bool FP4, bool TALL>
 __global__ __launch_bounds__(GM_THREADS, 1) void k_gemm_mx(int L, int N, int Kd, int64_t capacity,
                                                            const uint8_t* __restrict__ A,
                                                            const uint8_t* __restrict__ As,
@@ -140,9 +146,9 @@ __global__ __launch_bounds__(GM_THREADS, 1) void k_gemm_mx(int L, int N, int Kd,
                                                            uint8_t* __restrict__ out_s, float* __restrict__ part) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   int32_t* s_pre = (int32_t*)(smem + GM_LDS_SCALES + 2 * GM_SGROUP_BYTES);  // [L+1]
-  int32_t* s_tmp = s_pre + (L + 1);                                          // [8]
+  int32_t* s_tmp = s_pre + (L + 1);                                          // [16]
   const int NT = (N + GM_BN - 1) / GM_BN;
-  build_schedule(L, capacity, GM_BM, NT, offsets, s_pre, s_tmp);
+  build_schedule(L, capacity, GM_BM, NT, offsets, s_pre, s_tmp, TALL ? GM_TALL : 0);
   // RB code bytes per row; KT stages of 64 bytes; SG stages per 16-block scale group
   constexpr int SG = FP4 ? 4 : 8, LG = FP4 ? 2 : 3;
   const int RB = FP4 ? Kd / 2 : Kd;
@@ -170,7 +176,7 @@ __global__ __launch_bounds__(GM_THREADS, 1) void k_gemm_mx(int L, int N, int Kd,
     TileInfo ti;
     int piece, k0, k1;
     __amdgpu_buffer_rsrc_t rA, rB, rS;
-    int va[2], vb[2], vs, sgstep;
+    int va[2], vb[2], vs, sgstep, vx, vxs;
   };
   auto setup = [&](int u) {
     Unit w;
@@ -185,7 +191,7 @@ __global__ __launch_bounds__(GM_THREADS, 1) void k_gemm_mx(int L, int N, int Kd,
       w.k0 = 4 * (q * nq / plan.S);
       w.k1 = 4 * ((q + 1) * nq / plan.S);
     }
-    w.ti = locate_tile(tile, L, capacity, GM_BM, NT, offsets, s_pre);
+    w.ti = locate_tile(tile, L, capacity, GM_BM, NT, offsets, s_pre, TALL ? GM_TALL : 0);
     // the unit is the same for every lane: keep it in scalar registers (the
     // buffer resources built from it are scalar operands of the loads)
     w.ti.e = __builtin_amdgcn_readfirstlane(w.ti.e);
@@ -214,13 +220,21 @@ __global__ __launch_bounds__(GM_THREADS, 1) void k_gemm_mx(int L, int N, int Kd,
       w.va[q] = r * RB + dch * 16;
       w.vb[q] = r * GM_BK + dch * 16;
     }
+    // extra rows of a tall tile: code dword of row GM_BM + 4 wv + l/16, chunk
+    // position (l%16)/4, dword l%4; scale dword l%4 of row GM_BM + 16 wv + l/4
+    // (wavefronts 0 and 1, whose rS holds the A scales)
+    const int xr = 4 * wv + (l >> 4);
+    w.vx = (GM_BM + xr) * RB + ((((l & 15) >> 2) ^ swz4(xr)) << 4) + (l & 3) * 4;
+    w.vxs = (GM_BM + 16 * wv + (l >> 2)) * KB + (l & 3) * 4;
     return w;
   };
 
 #define GM_DMA(W, ST, KT_, Q)                                                               \
   {                                                                                         \
     const int kq = (KT_);                                                                   \
-    if ((Q) < 2)                                                                            \
+    if ((Q) == 4)                                                                           \
+      lds_dma_b32(lds0 + (ST) * GM_STAGE_BYTES + 32768 + wv * 256, (W).vx, (W).rA, kq * GM_BK); \
+    else if ((Q) < 2)                                                                       \
       lds_dma_b128(lds0 + (ST) * GM_STAGE_BYTES + (wv * 2 + (Q)) * 1024, (W).va[Q], (W).rA, kq * GM_BK); \
     else                                                                                    \
       lds_dma_b128(lds0 + (ST) * GM_STAGE_BYTES + 8192 * 2 + (wv * 2 + (Q) - 2) * 1024, (W).vb[(Q) - 2], (W).rB, \
@@ -235,12 +249,30 @@ __global__ __launch_bounds__(GM_THREADS, 1) void k_gemm_mx(int L, int N, int Kd,
                         (wv & 3) * 1024,                                                    \
                     (W).vs, (W).rS, gq * (W).sgstep);                                       \
   }
+// the extra rows' scale group G_ (tall tile; wavefronts 0 and 1)
+// (the wavefront test joins the scalar test inside the assembly: straight-line
+// code for the compiler)
+#define GM_XSDMA_IF(W, G_, SEL, WANT)                                                       \
+  {                                                                                         \
+    const int gq = (G_);                                                                    \
+    lds_dma_b32_if((SEL) + (wv < 2 ? 0 : 0x10000), (WANT),                                  \
+                   lds0 + GM_LDS_SCALES + (gq & 1) * GM_SGROUP_BYTES + 2 * GM_SGROUP_HALF + (wv & 1) * 256, \
+                   (W).vxs, (W).rS, gq * 16);                                               \
+  }
 // the ring prologue of a unit: the scale group of k0, then stages k0 .. k0+2
+// (a tall tile: also its extra rows, 5 loads per stage)
 #define GM_PROLOGUE(W)                                                                      \
   {                                                                                         \
     GM_SDMA_IF(W, (W).k0 >> LG, 0, 0);                                                      \
-    _Pragma("unroll") for (int st = 0; st < 3; ++st) {                                      \
-      _Pragma("unroll") for (int q = 0; q < 4; ++q) GM_DMA(W, st, min((W).k0 + st, (W).k1 - 1), q); \
+    if (TALL && (W).ti.rows > GM_BM) {                                                      \
+      GM_XSDMA_IF(W, (W).k0 >> LG, 0, 0);                                                   \
+      _Pragma("unroll") for (int st = 0; st < 3; ++st) {                                    \
+        _Pragma("unroll") for (int q = 0; q < 5; ++q) GM_DMA(W, st, min((W).k0 + st, (W).k1 - 1), q); \
+      }                                                                                     \
+    } else {                                                                                \
+      _Pragma("unroll") for (int st = 0; st < 3; ++st) {                                    \
+        _Pragma("unroll") for (int q = 0; q < 4; ++q) GM_DMA(W, st, min((W).k0 + st, (W).k1 - 1), q); \
+      }                                                                                     \
     }                                                                                       \
   }
 // fragments and scale bytes of stage KS_ (in ring stage ST)
@@ -295,6 +327,40 @@ __global__ __launch_bounds__(GM_THREADS, 1) void k_gemm_mx(int L, int N, int Kd,
     acc[(T) >> 1][(T) & 1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(               \
         fa[(T) >> 1], fb[(T) & 1], acc[(T) >> 1][(T) & 1], 0, 0, 2, (int)(sa[(T) >> 1] >> (8 * g)), 2, (int)(sb[(T) & 1] >> (8 * g))); \
   }
+// the extra rows of a tall tile: fragment and scale word of stage KS_, and
+// their instructions against B block J (wavefront (wm, wn) takes the 32 x 32
+// block of columns wn * 64 + 32 wm, whose B fragment it holds as block J = wm)
+#define GM_READX(ST, KS_)                                                                   \
+  {                                                                                         \
+    const uint8_t* px = smem + (ST) * GM_STAGE_BYTES + 32768;                               \
+    const u32x4 lo = *(const u32x4*)(px + fr0);                                             \
+    const u32x4 hi = *(const u32x4*)(px + fr1);                                             \
+    fx = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]}; \
+    const int ks = (KS_);                                                                   \
+    if (FP4 || ((ST) & 1) == 0) {                                                           \
+      const uint8_t* pw = smem + GM_LDS_SCALES + ((ks >> LG) & 1) * GM_SGROUP_BYTES + (ks & (SG - 1)) * (FP4 ? 4 : 2); \
+      sx = *(const uint32_t*)(pw + 2 * GM_SGROUP_HALF + r32 * 16);                         \
+    }                                                                                       \
+  }
+#define GM_MMAX(J, H_, P)                                                                   \
+  if (FP4) {                                                                                \
+    const i32x8 a_ = fx, b_ = fb[J];                                                        \
+    if ((P) == 0)                                                                           \
+      accx = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(                               \
+          __builtin_shufflevector(a_, a_, 0, 1, 2, 3, 0, 1, 2, 3), __builtin_shufflevector(b_, b_, 0, 1, 2, 3, 0, 1, 2, 3), \
+          accx, 4, 4, 0, (int)(sx >> (8 * g)), 0, (int)(sb[J] >> (8 * g)));                 \
+    else                                                                                    \
+      accx = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(                               \
+          __builtin_shufflevector(a_, a_, 4, 5, 6, 7, 4, 5, 6, 7), __builtin_shufflevector(b_, b_, 4, 5, 6, 7, 4, 5, 6, 7), \
+          accx, 4, 4, 2, (int)(sx >> (8 * g)), 2, (int)(sb[J] >> (8 * g)));                 \
+  } else if ((P) == 1) {                                                                    \
+  } else if ((H_ & 1) == 0) {                                                               \
+    accx = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(                                 \
+        fx, fb[J], accx, 0, 0, 0, (int)(sx >> (8 * g)), 0, (int)(sb[J] >> (8 * g)));        \
+  } else {                                                                                  \
+    accx = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(                                 \
+        fx, fb[J], accx, 0, 0, 2, (int)(sx >> (8 * g)), 2, (int)(sb[J] >> (8 * g)));        \
+  }
 #define GM_FENCE __builtin_amdgcn_sched_barrier(0);
 
   int u = virtual_block();
@@ -305,13 +371,14 @@ __global__ __launch_bounds__(GM_THREADS, 1) void k_gemm_mx(int L, int N, int Kd,
   }
   while (u < plan.units) {
     const int k0 = cu.k0, k1 = cu.k1;
-    i32x8 fa[4], fb[2];
-    uint32_t sa[4], sb[2];
-    f32x16 acc[4][2];
+    i32x8 fa[4], fb[2], fx;
+    uint32_t sa[4], sb[2], sx;
+    f32x16 acc[4][2], accx;  // accx: this wavefront's block of the extra rows of a tall tile
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
+    accx = f32x16{};
     // wait for stage k0 and the scale group issued before it (the younger
     // stages k0+1, k0+2 may still be loading; loads complete in issue order)
     asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");
@@ -324,38 +391,55 @@ __global__ __launch_bounds__(GM_THREADS, 1) void k_gemm_mx(int L, int N, int Kd,
     // it.  The vmcnt(8) waits allow the two younger stages' 8 loads in flight;
     // where a scale load is among them the wait is one load stronger than
     // needed.
-#define GM_KLOOP(NB)                                                                        \
+#define GM_KLOOP(NB, NL, XM)                                                                \
   for (int kt = k0; kt < k1; kt += 4) {                                                     \
     _Pragma("unroll") for (int h = 0; h < 4; ++h) {                                         \
       GM_READ(h, kt + h, NB);                                                               \
+      if (XM) GM_READX(h, kt + h);                                                          \
       {                                                                                     \
         const int kn = min(kt + h + 3, k1 - 1);                                             \
         GM_SDMA_IF(cu, min(((kt + h) >> LG) + 1, NG - 1), (kt + h) & (SG - 1), SG - 3);     \
-        _Pragma("unroll") for (int q = 0; q < 4; ++q) GM_DMA(cu, (h + 3) & 3, kn, q);      \
+        if ((NL) == 5) GM_XSDMA_IF(cu, min(((kt + h) >> LG) + 1, NG - 1), (kt + h) & (SG - 1), SG - 3); \
+        _Pragma("unroll") for (int q = 0; q < (NL); ++q) GM_DMA(cu, (h + 3) & 3, kn, q);   \
       }                                                                                     \
-      asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory");              \
+      if ((NL) == 5) asm volatile("s_waitcnt vmcnt(10) lgkmcnt(0)\n\ts_barrier" ::: "memory"); \
+      else asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory");       \
       GM_FENCE;                                                                             \
       /* E2M1: all first instructions, then all second ones (8 apart on an    */            \
       /* accumulator, as in the bf16 kernel)                                   */            \
       _Pragma("unroll") for (int t = 0; t < 8; ++t) {                                       \
         if ((t >> 1) < (NB)) GM_MMA1(t, h, 0);                                               \
       }                                                                                     \
+      if (XM) GM_MMAX((XM) - 1, h, 0);                                                      \
       _Pragma("unroll") for (int t = 0; t < 8; ++t) {                                       \
         if (FP4 && (t >> 1) < (NB)) GM_MMA1(t, h, 1);                                        \
       }                                                                                     \
+      if (FP4 && XM) GM_MMAX((XM) - 1, h, 1);                                               \
       GM_FENCE;                                                                             \
-      asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");                          \
+      if ((NL) == 5) asm volatile("s_waitcnt vmcnt(10)\n\ts_barrier" ::: "memory");       \
+      else asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");                  \
     }                                                                                       \
   }
     // a wavefront reads fragments for and multiplies only the 32-row blocks of
     // its 128 rows that hold rows of the tile; all versions of the loop have
-    // the same loads and barriers
-    switch (min(4, max(0, (cu.ti.rows - wm * 128 + 31) / 32))) {
-      case 4: GM_KLOOP(4); break;
-      case 3: GM_KLOOP(3); break;
-      case 2: GM_KLOOP(2); break;
-      case 1: GM_KLOOP(1); break;
-      default: GM_KLOOP(0); break;
+    // the same loads and barriers.  A tall tile (GM_BM + up to GM_TALL rows)
+    // moves its extra rows' codes with a fifth load per stage in every
+    // wavefront (their scales with the scale groups, wavefronts 0 and 1), and
+    // every wavefront multiplies them by one of the two B fragments it holds.
+    if (TALL && cu.ti.rows > GM_BM) {
+      if (wm == 0) {
+        GM_KLOOP(4, 5, 1);
+      } else {
+        GM_KLOOP(4, 5, 2);
+      }
+    } else {
+      switch (min(4, max(0, (cu.ti.rows - wm * 128 + 31) / 32))) {
+        case 4: GM_KLOOP(4, 4, 0); break;
+        case 3: GM_KLOOP(3, 4, 0); break;
+        case 2: GM_KLOOP(2, 4, 0); break;
+        case 1: GM_KLOOP(1, 4, 0); break;
+        default: GM_KLOOP(0, 4, 0); break;
+      }
     }
 #undef GM_KLOOP
     if (!gp) asm volatile("s_barrier" ::: "memory");
@@ -369,6 +453,32 @@ __global__ __launch_bounds__(GM_THREADS, 1) void k_gemm_mx(int L, int N, int Kd,
     }
     if (done.piece < 0) {
       mx_store_tile<EPI, 4, FP4>(acc, 0, done.ti, N, wm, wn, g, r32, out, out_s);
+      if (TALL && done.ti.rows > GM_BM) {
+        // the extra rows: wavefront (1, wn) hands its block (columns wn * 64 +
+        // 32) to wavefront (0, wn) through ring stage 3, which no load of this
+        // unit's tail or of the next unit's prologue writes, and which every
+        // wavefront has finished reading
+        float* xch = (float*)(smem + 3 * GM_STAGE_BYTES) + (wn * 64 + l) * 16;
+        if (wm == 1) {
+#pragma unroll
+          for (int c = 0; c < 4; ++c)
+            *(f32x4*)(xch + 4 * c) = f32x4{accx[4 * c], accx[4 * c + 1], accx[4 * c + 2], accx[4 * c + 3]};
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        if (wm == 0) {
+          f32x16 pair[1][2];
+          pair[0][0] = accx;
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const f32x4 v = *(const f32x4*)(xch + 4 * c);
+            pair[0][1][4 * c] = v[0];
+            pair[0][1][4 * c + 1] = v[1];
+            pair[0][1][4 * c + 2] = v[2];
+            pair[0][1][4 * c + 3] = v[3];
+          }
+          mx_store_tile<EPI, 1, FP4>(pair, 8, done.ti, N, 0, wn, g, r32, out, out_s);
+        }
+      }
     } else {
       // partial tile, per wavefront [i][j][lane][16 values of the MFMA D layout]
       float* dst = part + (long)done.piece * GM_PART_FLOATS + wv * 8192 + l * 16;
@@ -380,9 +490,18 @@ __global__ __launch_bounds__(GM_THREADS, 1) void k_gemm_mx(int L, int N, int Kd,
           for (int c = 0; c < 4; ++c)
             *(f32x4*)(dst + (i * 2 + j) * 1024 + c * 4) =
                 f32x4{acc[i][j][4 * c], acc[i][j][4 * c + 1], acc[i][j][4 * c + 2], acc[i][j][4 * c + 3]};
+      if (TALL && done.ti.rows > GM_BM) {  // the extra rows: [wn][wm][lane][16]
+        float* dx = part + (long)done.piece * GM_PART_FLOATS + GM_PART_X + wn * 2048 + wm * 1024 + l * 16;
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          *(f32x4*)(dx + c * 4) = f32x4{accx[4 * c], accx[4 * c + 1], accx[4 * c + 2], accx[4 * c + 3]};
+      }
     }
   }
 #undef GM_DMA
+#undef GM_XSDMA_IF
+#undef GM_READX
+#undef GM_MMAX
 #undef GM_SDMA_IF
 #undef GM_PROLOGUE
 #undef GM_READ
@@ -393,44 +512,57 @@ __global__ __launch_bounds__(GM_THREADS, 1) void k_gemm_mx(int L, int N, int Kd,
 }
 
 // Sum the S split-K partials of each split tile (in piece order) and apply the
-// epilogue; workgroup (b, w) of four wavefronts handles GEMM wavefront w's
+// epilogue; workgroup (b, w) of five wavefronts handles GEMM wavefront w's
 // part of split tile b of the plan of a GEMM launched with G workgroups, its
-// wavefront i row block i.
-template <int EPI, bool FP4>
-__global__ __launch_bounds__(256) void k_mx_splitk_reduce(int L, int N, int Kd, int64_t capacity, int G,
+// wavefront i < 4 row block i and its wavefront 4 (w < 4) the extra rows of
+// a tall tile in columns w * 64 .. w * 64 + 63.
+template <int EPI, bool FP4, bool TALL>
+__global__ __launch_bounds__(320) void k_mx_splitk_reduce(int L, int N, int Kd, int64_t capacity, int G,
                                                           const int32_t* __restrict__ offsets,
                                                           const float* __restrict__ part, uint8_t* __restrict__ out,
                                                           uint8_t* __restrict__ out_s) {
   __shared__ int32_t s_pre[MOE_MAX_L + 1];
   __shared__ int32_t s_tmp[16];
   const int NT = (N + GM_BN - 1) / GM_BN;
-  build_schedule(L, capacity, GM_BM, NT, offsets, s_pre, s_tmp);
+  build_schedule(L, capacity, GM_BM, NT, offsets, s_pre, s_tmp, TALL ? GM_TALL : 0);
   const int total = s_pre[L];
   const SplitPlan plan = gm_split_plan(total, G, (FP4 ? Kd / 2 : Kd) / GM_BK);
   const int b = blockIdx.x >> 3, wv = blockIdx.x & 7, i = threadIdx.x >> 6, l = threadIdx.x & 63;
   if (plan.S < 2 || b >= total - plan.dp) return;
-  const TileInfo ti = locate_tile(plan.dp + b, L, capacity, GM_BM, NT, offsets, s_pre);
-  if (ti.rows <= (wv >> 2) * 128 + i * 32) return;  // row block past the tile's rows
+  const TileInfo ti = locate_tile(plan.dp + b, L, capacity, GM_BM, NT, offsets, s_pre, TALL ? GM_TALL : 0);
+  const float* src = part + (long)b * plan.S * GM_PART_FLOATS + l * 16;
   f32x16 acc[1][2];
-  sum_partials(part + (long)b * plan.S * GM_PART_FLOATS + wv * 8192 + i * 2048 + l * 16, plan.S, acc);
-  mx_store_tile<EPI, 1, FP4>(acc, i, ti, N, wv >> 2, wv & 3, l >> 5, l & 31, out, out_s);
+  if (i < 4) {
+    if (ti.rows <= (wv >> 2) * 128 + i * 32) return;  // row block past the tile's rows
+    sum_partials(src + wv * 8192 + i * 2048, plan.S, acc, GM_PART_FLOATS);
+    mx_store_tile<EPI, 1, FP4>(acc, i, ti, N, wv >> 2, wv & 3, l >> 5, l & 31, out, out_s);
+  } else {
+    if (wv >= 4 || ti.rows <= GM_BM) return;
+    sum_partials(src + GM_PART_X + wv * 2048, plan.S, acc, GM_PART_FLOATS);
+    mx_store_tile<EPI, 1, FP4>(acc, 8, ti, N, 0, wv, l >> 5, l & 31, out, out_s);
+  }
 }
 
 size_t grouped_mlp_mx_part_bytes() { return (size_t)GEMM_SPLIT_UNITS * GM_PART_FLOATS * sizeof(float); }
 
-template <bool FP4>
+// dynamic LDS of the MX kernel: 4 ring stages, 2 scale groups, the schedule
+static size_t mx_lds_bytes(int L, bool TALL) {
+  return (size_t)GM_LDS_SCALES + 2 * GM_SGROUP_BYTES + (size_t)(L + 1 + 16) * sizeof(int32_t);
+}
+
+template <bool FP4, bool TALL>
 static void launch_mx(int L, int H, int F, int64_t capacity, const uint8_t* x, const uint8_t* xs,
                       const int32_t* offsets, const uint8_t* w1p, const uint8_t* w1s, const uint8_t* w2p,
                       const uint8_t* w2s, uint8_t* act, uint8_t* act_s, float* part, bf16_t* y, hipStream_t s) {
   static bool attr_done = false;
   if (!attr_done) {
-    (void)hipFuncSetAttribute((const void*)k_gemm_mx<0, FP4>, hipFuncAttributeMaxDynamicSharedMemorySize,
+    (void)hipFuncSetAttribute((const void*)k_gemm_mx<0, FP4, TALL>, hipFuncAttributeMaxDynamicSharedMemorySize,
                               160 * 1024);
-    (void)hipFuncSetAttribute((const void*)k_gemm_mx<1, FP4>, hipFuncAttributeMaxDynamicSharedMemorySize,
+    (void)hipFuncSetAttribute((const void*)k_gemm_mx<1, FP4, TALL>, hipFuncAttributeMaxDynamicSharedMemorySize,
                               160 * 1024);
     attr_done = true;
   }
-  const size_t lds = (size_t)GM_LDS_SCALES + 2 * GM_SGROUP_BYTES + (size_t)(L + 1 + 16) * sizeof(int32_t);
+  const size_t lds = mx_lds_bytes(L, TALL);
   auto grid = [&](int N) {
     const int NT = (N + GM_BN - 1) / GM_BN;
     const int64_t upper = ((capacity + GM_BM - 1) / GM_BM + L) * (int64_t)NT;
@@ -439,14 +571,14 @@ static void launch_mx(int L, int H, int F, int64_t capacity, const uint8_t* x, c
     return (int)(gsz > 0 ? gsz : 1);
   };
   const int G1 = grid(2 * F), G2 = grid(H);
-  const dim3 rgrid(GEMM_SPLIT_UNITS / 2 * 8), rblk(256), blk(GM_THREADS);
-  hipLaunchKernelGGL((k_gemm_mx<1, FP4>), dim3(G1), blk, lds, s, L, 2 * F, H, capacity, x, xs, offsets, w1p, w1s,
-                     act, act_s, part);
-  hipLaunchKernelGGL((k_mx_splitk_reduce<1, FP4>), rgrid, rblk, 0, s, L, 2 * F, H, capacity, G1, offsets, part,
-                     act, act_s);
-  hipLaunchKernelGGL((k_gemm_mx<0, FP4>), dim3(G2), blk, lds, s, L, H, F, capacity, act, act_s, offsets, w2p,
-                     w2s, (uint8_t*)y, (uint8_t*)nullptr, part);
-  hipLaunchKernelGGL((k_mx_splitk_reduce<0, FP4>), rgrid, rblk, 0, s, L, H, F, capacity, G2, offsets, part,
+  const dim3 rgrid(GEMM_SPLIT_UNITS / 2 * 8), rblk(320), blk(GM_THREADS);
+  hipLaunchKernelGGL((k_gemm_mx<1, FP4, TALL>), dim3(G1), blk, lds, s, L, 2 * F, H, capacity, x, xs, offsets, w1p,
+                     w1s, act, act_s, part);
+  hipLaunchKernelGGL((k_mx_splitk_reduce<1, FP4, TALL>), rgrid, rblk, 0, s, L, 2 * F, H, capacity, G1, offsets,
+                     part, act, act_s);
+  hipLaunchKernelGGL((k_gemm_mx<0, FP4, TALL>), dim3(G2), blk, lds, s, L, H, F, capacity, act, act_s, offsets,
+                     w2p, w2s, (uint8_t*)y, (uint8_t*)nullptr, part);
+  hipLaunchKernelGGL((k_mx_splitk_reduce<0, FP4, TALL>), rgrid, rblk, 0, s, L, H, F, capacity, G2, offsets, part,
                      (uint8_t*)y, (uint8_t*)nullptr);
 }
 
@@ -455,10 +587,16 @@ hipError_t launch_grouped_mlp_mx(int L, int H, int F, int64_t capacity, bool fp4
                                  const uint8_t* w1s, const uint8_t* w2p, const uint8_t* w2s,
                                  uint8_t* act, uint8_t* act_s, float* part, bf16_t* y, hipStream_t s) {
   if (capacity == 0) return hipSuccess;
+  // E4M3: tall tiles when their larger LDS layout leaves room for the
+  // schedule of L experts.  E2M1: plain tiles (measured on the Mixtral-like
+  // shape: tall tiles 3% faster with E4M3 codes, 2.5% slower with E2M1).
+  const bool tall = mx_lds_bytes(L, true) <= 160 * 1024;
   if (fp4)
-    launch_mx<true>(L, H, F, capacity, x, xs, offsets, w1p, w1s, w2p, w2s, act, act_s, part, y, s);
+    launch_mx<true, false>(L, H, F, capacity, x, xs, offsets, w1p, w1s, w2p, w2s, act, act_s, part, y, s);
+  else if (tall)
+    launch_mx<false, true>(L, H, F, capacity, x, xs, offsets, w1p, w1s, w2p, w2s, act, act_s, part, y, s);
   else
-    launch_mx<false>(L, H, F, capacity, x, xs, offsets, w1p, w1s, w2p, w2s, act, act_s, part, y, s);
+    launch_mx<false, false>(L, H, F, capacity, x, xs, offsets, w1p, w1s, w2p, w2s, act, act_s, part, y, s);
   return hipGetLastError();
 }
 

@@ -219,10 +219,14 @@ def test_grouped_mlp_bf16(counts, H, F):
     ([900, 24, 0, 513], 1024, 1536),
     ([70, 300, 0, 5], 768, 256),          # partial column tiles in both GEMMs
     ([0, 0, 0, 0], 256, 256),             # no rows at all
-    # the 72 tiles of a partial round split along k into 2 pieces (first GEMM:
-    # k = 4096; second GEMM: k = 4096)
+    # the 66 tiles of a partial round (tall ones among them) split along k
+    # into 2 pieces (first GEMM: k = 4096; second GEMM: k = 4096)
     (MIXTRAL_COUNTS, 4096, 256),
     (MIXTRAL_COUNTS, 512, 4096),
+    # tall tiles: remainders of 1, 16 and 32 rows join the expert's last full
+    # tile (257, 272, 288, 544 rows); 289 rows and a lone 31 do not
+    ([257, 272, 288, 289, 544, 0, 31], 512, 512),
+    ([1054, 994, 1030, 1018, 1040, 1008, 1024, 1024], 512, 1024),
 ])
 def test_grouped_mlp_mxfp8(counts, H, F):
     _run_mlp(counts, H, F, "mxfp8", seed=sum(counts) + H)
@@ -233,11 +237,15 @@ def test_grouped_mlp_mxfp8(counts, H, F):
     ([900, 24, 0, 513], 1024, 1536),
     ([70, 300, 0, 5], 1536, 512),         # partial column tiles in both GEMMs
     ([0, 0, 0, 0], 512, 512),             # no rows at all
-    # 4028 rows (16 row tiles): the 64 tiles of the first GEMM (k = 8192, 16
-    # groups of 4 E2M1 stages) and the 32 of the second (k = 8192) are split
+    # 4028 rows (17 row tiles): the 68 tiles of the first GEMM (k = 8192, 16
+    # groups of 4 E2M1 stages) and the 34 of the second (k = 8192) are split
     # along k into 2 pieces
     ([1000, 1011, 977, 1040], 8192, 512),
     ([1000, 1011, 977, 1040], 512, 8192),
+    # remainders of 1 to 33 rows after full tiles (tall tiles in the bf16 and
+    # E4M3 kernels; the E2M1 kernel keeps them in tiles of their own)
+    ([257, 272, 288, 289, 544, 0, 31], 512, 512),
+    ([1054, 994, 1030, 1018, 1040, 1008, 1024, 1024], 512, 1024),
 ])
 def test_grouped_mlp_mxfp4(counts, H, F):
     _run_mlp(counts, H, F, "mxfp4", seed=sum(counts) + H + 1)
