@@ -22,6 +22,9 @@ is computed here by plain definitions:
                         compact route" section of the sparser-MoE page names as
                         the original path (kept as an independent second
                         oracle for the pins)
+  route_grouped         group-limited routing with a selection-only bias (the
+                        DeepSeek-style router refinement; its definition is
+                        the DeepSeek-V3 Technical Report's, not the pages')
   count_and_permute     stable counting sort of the valid local routes
   mx_quantize_rows      OCP Microscaling (MX) v1.0 block quantization, E4M3
   mx4_quantize_rows     the same with E2M1 (MXFP4) elements
@@ -359,6 +362,73 @@ def route_topk_repeated_argmax(logits, K, score="softmax", bias=None, mask=None)
         m = np.asarray(mask).astype(bool)
         ids[m] = -1
         p[m] = 0.0
+    return ids, p
+
+
+def sigmoid_scores(logits) -> np.ndarray:
+    """s = 1 / (1 + exp(-logit)) in float64, stored as fp32."""
+    z = np.asarray(logits, dtype=np.float64)
+    if not np.all(np.isfinite(z)):
+        raise ValueError("non-finite router logits")
+    return (1.0 / (1.0 + np.exp(-z))).astype(np.float32)
+
+
+def _fp32_sum_desc(v):
+    """fp32 left fold of the values along the last axis, taken in descending order."""
+    v = -np.sort(-np.asarray(v, dtype=np.float32), axis=-1)
+    acc = v[..., 0].astype(np.float32)
+    for i in range(1, v.shape[-1]):
+        acc = (acc + v[..., i]).astype(np.float32)
+    return acc
+
+
+def route_grouped(logits, K, n_group, topk_group, bias=None, scale=1.0, mask=None, scores=None):
+    """Group-limited routing with a selection-only bias.
+
+    Not from the pages: the pages' next steps name router refinements, and this
+    is the DeepSeek-style form they point to, as the DeepSeek-V3 Technical
+    Report defines it (section "DeepSeekMoE with Auxiliary-Loss-Free Load
+    Balancing": sigmoid affinities, a per-expert bias that only steers the
+    top-K choice, gates normalized over the selected affinities, and routing
+    limited to the groups (nodes) whose experts score highest, a group scored
+    by the sum of its K/topk_group highest affinities).
+
+    s = sigmoid(logit), fp32 (or `scores`: given fp32 values of s, so that a
+    check can take the selection on another implementation's own fp32 s).
+    Keys: k = s + bias (one fp32 add; bias optional).  The E experts form
+    n_group groups of E/n_group consecutive ids; a group's score is the fp32
+    sum of its m = K/topk_group largest keys, largest first.  The topk_group
+    groups with the highest scores stay (ties: lower group index); the K
+    largest keys among their experts are selected (ties: lower expert id) and
+    listed by descending key.  probs = scale * s_k / sum_j s_j over the
+    selected (fp32).  Masked tokens get -1 and 0.
+    """
+    s = sigmoid_scores(logits) if scores is None else np.asarray(scores, dtype=np.float32)
+    T, E = s.shape
+    if n_group < 1 or E % n_group or not (1 <= topk_group <= n_group) or K % topk_group:
+        raise ValueError("need n_group | E, 1 <= topk_group <= n_group, topk_group | K")
+    gs, m = E // n_group, K // topk_group
+    if not (1 <= K <= topk_group * gs) or m > gs:
+        raise ValueError("need 1 <= K <= topk_group * E / n_group")
+    key = s if bias is None else (s + np.asarray(bias, dtype=np.float32)[None, :]).astype(np.float32)
+    key = np.where(key == 0, np.float32(0.0), key).astype(np.float32)
+    if not np.all(np.isfinite(key)):
+        raise ValueError("non-finite selection keys")
+    gk = key.reshape(T, n_group, gs)
+    gscore = _fp32_sum_desc(-np.sort(-gk, axis=2)[:, :, :m])          # [T, n_group]
+    gkeep = np.argsort(-gscore, axis=1, kind="stable")[:, :topk_group]  # stable: lower group first
+    keep = np.zeros((T, n_group), dtype=bool)
+    keep[np.arange(T)[:, None], gkeep] = True
+    allowed = np.repeat(keep, gs, axis=1)
+    masked = np.where(allowed, key, np.float32(-np.inf)).astype(np.float32)
+    ids = np.argsort(-masked, axis=1, kind="stable")[:, :K].astype(np.int64)
+    ssel = np.take_along_axis(s, ids, axis=1).astype(np.float64)
+    p = (scale * ssel / ssel.sum(axis=1, keepdims=True)).astype(np.float32)
+    ids = ids.astype(np.int16)
+    if mask is not None:
+        mk = np.asarray(mask).astype(bool)
+        ids[mk] = -1
+        p[mk] = 0.0
     return ids, p
 
 
