@@ -8,7 +8,7 @@ from . import _lib  # noqa: F401  (fails loudly when the library is not built)
 from ._lib import (  # noqa: F401
     BF16, F32, MXFP4, MXFP8, SIGMOID, SOFTMAX, DEVERR_BAD_ID, DEVERR_NONFINITE, DEVERR_OVERFLOW, MoEError,
     moe_grouped_mlp, moe_grouped_mlp_workspace_bytes, moe_mx_quantize, moe_permute, moe_permute_workspace_bytes,
-    moe_prepare_router, moe_prepare_weights, moe_prepared_weight_bytes, moe_route_topk, moe_route_workspace_bytes,
-    moe_router_prepared_bytes, moe_unpermute_combine,
+    moe_prepare_router, moe_prepare_weights, moe_prepared_weight_bytes, moe_route_topk, moe_route_topk_grouped,
+    moe_route_workspace_bytes, moe_router_prepared_bytes, moe_unpermute_combine,
 )
 from .layer import MoELayer  # noqa: F401

@@ -26,6 +26,8 @@ _SIGS = {
     "moe_prepare_router": (_I, [_P, _I, _I, _I, _I, _P, _P]),
     "moe_route_workspace_bytes": (_SZ, [_I, _I, _I, _I]),
     "moe_route_topk": (_I, [_I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "moe_route_topk_grouped": (_I, [_I, _I, _I, _I, _I, _I, ctypes.c_float, _I, _I, _P, _P, _P, _P, _P, _P, _P,
+                                    _P, _P, _P, _P, _SZ, _P]),
     "moe_permute_workspace_bytes": (_SZ, [_I, _I, _I]),
     "moe_permute": (_I, [_I, _I, _I, _I, _I, _I, _I64, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "moe_prepared_weight_bytes": (_SZ, [_I, _I, _I, _I, _I]),
@@ -114,6 +116,22 @@ def moe_route_topk(ids, probs, score, *, logits=None, x=None, w_prepared=None, w
     _check(lib.moe_route_topk(T, E, K, H, score, x_dtype, w_dtype, _p(x), _p(w_prepared), _p(logits), _p(bias),
                               _p(mask), _p(ids), _p(probs), _p(logits_out), _p(err), _p(workspace),
                               _nbytes(workspace), _stream()), "moe_route_topk")
+
+
+def moe_route_topk_grouped(ids, probs, n_group, topk_group, scale=1.0, *, logits=None, x=None, w_prepared=None,
+                           w_dtype=F32, E=None, bias=None, mask=None, logits_out=None, scores_out=None, err=None,
+                           workspace=None):
+    T, K = ids.shape
+    if logits is not None:
+        E = logits.shape[1]
+        H, x_dtype = 0, F32
+    else:
+        H = x.shape[1]
+        x_dtype = dtype_code(x.dtype)
+    _check(lib.moe_route_topk_grouped(T, E, K, H, n_group, topk_group, float(scale), x_dtype, w_dtype, _p(x),
+                                      _p(w_prepared), _p(logits), _p(bias), _p(mask), _p(ids), _p(probs),
+                                      _p(logits_out), _p(scores_out), _p(err), _p(workspace), _nbytes(workspace),
+                                      _stream()), "moe_route_topk_grouped")
 
 
 # ----------------------------------------------------------------- permute

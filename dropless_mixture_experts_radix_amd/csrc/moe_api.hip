@@ -60,12 +60,13 @@ size_t moe_route_workspace_bytes(int T, int E, int H, int x_dtype) {
   return round_up((size_t)S * T * E * sizeof(float), 256);
 }
 
-int moe_route_topk(int T, int E, int K, int H, int score, int x_dtype, int w_dtype, const void* x,
-                   const void* w_prepared, const float* logits, const float* bias, const uint8_t* mask,
-                   int16_t* ids, float* probs, float* logits_out, int32_t* err, void* workspace,
-                   size_t workspace_bytes, void* stream) {
+// moe_route_topk and moe_route_topk_grouped (grp != nullptr: score checked
+// by the caller, no fused small-router path)
+static int route_topk(int T, int E, int K, int H, int score, int x_dtype, int w_dtype, const void* x,
+                      const void* w_prepared, const float* logits, const float* bias, const uint8_t* mask,
+                      int16_t* ids, float* probs, float* logits_out, int32_t* err, void* workspace,
+                      size_t workspace_bytes, void* stream, const RouteGroups* grp, float* scores_out) {
   if (T < 0 || E <= 0 || E > MOE_MAX_E || K < 1 || K > E || K > MOE_MAX_K) return MOE_ERR_SHAPE;
-  if (score != MOE_SCORE_SOFTMAX && score != MOE_SCORE_SIGMOID) return MOE_ERR_DTYPE;
   const bool from_x = logits == nullptr;
   if (T > 0 && (!ids || !probs)) return MOE_ERR_NULL;
   if (from_x) {
@@ -90,7 +91,7 @@ int moe_route_topk(int T, int E, int K, int H, int score, int x_dtype, int w_dty
   hipStream_t s = (hipStream_t)stream;
   const float* partial = logits;
   int S = 1;
-  if (from_x && route_fused_ok(E, H, x_dtype, w_dtype))
+  if (from_x && !grp && route_fused_ok(E, H, x_dtype, w_dtype))
     return launch_status(launch_route_fused(T, E, K, H, score, w_dtype, x, w_prepared, bias, mask, ids, probs,
                                             logits_out, err, s));
   if (from_x) {
@@ -108,7 +109,32 @@ int moe_route_topk(int T, int E, int K, int H, int score, int x_dtype, int w_dty
     partial = ws;
   }
   return launch_status(launch_route_select(T, E, K, S, score, partial, bias, mask, ids, probs,
-                                           logits_out, err, s));
+                                           logits_out, err, s, grp, scores_out));
+}
+
+int moe_route_topk(int T, int E, int K, int H, int score, int x_dtype, int w_dtype, const void* x,
+                   const void* w_prepared, const float* logits, const float* bias, const uint8_t* mask,
+                   int16_t* ids, float* probs, float* logits_out, int32_t* err, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+  if (score != MOE_SCORE_SOFTMAX && score != MOE_SCORE_SIGMOID) return MOE_ERR_DTYPE;
+  return route_topk(T, E, K, H, score, x_dtype, w_dtype, x, w_prepared, logits, bias, mask, ids, probs,
+                    logits_out, err, workspace, workspace_bytes, stream, nullptr, nullptr);
+}
+
+int moe_route_topk_grouped(int T, int E, int K, int H, int n_group, int topk_group, float scale, int x_dtype,
+                           int w_dtype, const void* x, const void* w_prepared, const float* logits,
+                           const float* bias, const uint8_t* mask, int16_t* ids, float* probs,
+                           float* logits_out, float* scores_out, int32_t* err, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  if (E <= 32 || E > ROUTE_GRP_MAX_E || n_group < 1 || n_group > 64 || E % n_group || topk_group < 1 ||
+      topk_group > n_group || K < 1 || K % topk_group || K / topk_group > ROUTE_GRP_MAX_M ||
+      K / topk_group > E / n_group || K > topk_group * (E / n_group))
+    return MOE_ERR_SHAPE;
+  if (!(scale > 0.f) || scale > 3.0e38f) return MOE_ERR_SHAPE;
+  if (scores_out && !aligned16(scores_out)) return MOE_ERR_ALIGN;
+  const RouteGroups g{n_group, topk_group, K / topk_group, scale};
+  return route_topk(T, E, K, H, MOE_SCORE_SIGMOID, x_dtype, w_dtype, x, w_prepared, logits, bias, mask, ids,
+                    probs, logits_out, err, workspace, workspace_bytes, stream, &g, scores_out);
 }
 
 // ---------------------------------------------------------------------------

@@ -179,9 +179,20 @@ bool route_fused_ok(int E, int H, int x_dtype, int w_dtype);
 hipError_t launch_route_fused(int T, int E, int K, int H, int score, int w_dtype, const void* x, const void* wp,
                               const float* bias, const uint8_t* mask, int16_t* ids, float* probs,
                               float* logits_out, int32_t* err, hipStream_t s);
+// Group-limited routing with a selection-only bias (moe_route_topk_grouped):
+// n_group groups of E/n_group experts, the topk_group best kept, a group
+// scored by the fp32 sum of its m = K/topk_group largest keys; gates scaled.
+struct RouteGroups {
+  int n_group, topk_group, m;
+  float scale;
+};
+#define ROUTE_GRP_MAX_E 1024   // experts of the grouped selection
+#define ROUTE_GRP_MAX_M 8      // keys summed per group
+
 hipError_t launch_route_select(int T, int E, int K, int S, int score, const float* partial,
                                const float* bias, const uint8_t* mask, int16_t* ids, float* probs,
-                               float* logits_out, int32_t* err, hipStream_t s);
+                               float* logits_out, int32_t* err, hipStream_t s,
+                               const RouteGroups* grp = nullptr, float* scores_out = nullptr);
 
 int permute_tile_tokens(int T, int K);
 hipError_t launch_permute(int T, int H, int K, int E_global, int e0, int L, int64_t capacity,

@@ -497,16 +497,29 @@ __device__ __forceinline__ void sel_sort_take(const uint32_t* ck, const int* ci,
   }
 }
 
-template <int VPL>
+// GRP: group-limited routing with a selection-only bias (DeepSeek-V3
+// Technical Report, section "DeepSeekMoE with Auxiliary-Loss-Free Load
+// Balancing"): the keys are s + bias with s = sigmoid(logit) in fp32; before
+// step 1 the keys of experts outside the topk_group best groups are set to 0
+// (below every real key).  A group's score is the fp32 sum of its m largest
+// keys, largest first; lane g scores group g from the keys in LDS, and every
+// lane ranks its group against all others (ties: lower group index).  The
+// gates are scale * s_k / sum_j s_j over the selected, s from LDS.
+template <int VPL, bool GRP>
 __global__ __launch_bounds__(256) void k_route_select_wave(int T, int E, int K, int S, int score,
                                                            const float* __restrict__ partial,
                                                            const float* __restrict__ bias,
                                                            const uint8_t* __restrict__ mask,
                                                            int16_t* __restrict__ ids, float* __restrict__ probs,
-                                                           float* __restrict__ logits_out, int32_t* err) {
+                                                           float* __restrict__ logits_out, int32_t* err,
+                                                           RouteGroups grp, float* __restrict__ scores_out) {
   __shared__ uint32_t s_hist[4][256];
   __shared__ uint32_t s_ckey[4][SEL_CMAX];
   __shared__ int s_cidx[4][SEL_CMAX];
+  constexpr int GE = GRP ? ROUTE_GRP_MAX_E : 1;
+  __shared__ uint32_t s_gkey[4][GE];  // GRP: keys by expert
+  __shared__ float s_sig[4][GE];      // GRP: sigmoid scores by expert
+  __shared__ float s_gsc[4][GRP ? 64 : 1];
   const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + w;
   if (t >= T) return;  // wave-uniform; no block-wide barrier below
@@ -558,6 +571,24 @@ __global__ __launch_bounds__(256) void k_route_select_wave(int T, int E, int K, 
       }
     }
   }
+  bool nfl = false;  // GRP: a non-finite logit (its sigmoid would be finite)
+  if constexpr (GRP) {
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      float zz[4] = {v[c].x, v[c].y, v[c].z, v[c].w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int e = c * 256 + 4 * l + q;
+        nfl |= e < E && (__float_as_uint(zz[q]) << 1) >= 0xff000000u;
+        zz[q] = 1.0f / (1.0f + expf(-zz[q]));
+        if (e < E) {
+          s_sig[w][e] = zz[q];
+          if (scores_out) scores_out[(long)t * E + e] = zz[q];
+        }
+      }
+      v[c] = float4{zz[0], zz[1], zz[2], zz[3]};
+    }
+  }
   if (bias) {
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
@@ -589,11 +620,51 @@ __global__ __launch_bounds__(256) void k_route_select_wave(int T, int E, int K, 
       key[c * 4 + q] = in ? k : 0u;
     }
   }
-  const bool bad = emax >= 0xff000000u;
+  const bool bad = emax >= 0xff000000u || nfl;
   if (wave_ballot(bad) != 0 && l == 0) set_err(err, MOE_DEVERR_NONFINITE);
   if (mask && mask[t]) {
     if (l < K) { ids[(long)t * K + l] = -1; probs[(long)t * K + l] = 0.f; }
     return;
+  }
+  if constexpr (GRP) {
+    const int gs = E / grp.n_group;
+#pragma unroll
+    for (int j = 0; j < VPL; ++j) {
+      const int e = (j >> 2) * 256 + 4 * l + (j & 3);
+      if (e < E) s_gkey[w][e] = key[j];
+    }
+    wave_sync();
+    // lane g: the m largest keys of group g, descending, then their fp32 sum
+    float gsc = 0.f;
+    if (l < grp.n_group) {
+      uint32_t tk[ROUTE_GRP_MAX_M];
+#pragma unroll
+      for (int i = 0; i < ROUTE_GRP_MAX_M; ++i) tk[i] = 0u;
+      for (int e = l * gs; e < (l + 1) * gs; ++e) {
+        uint32_t x = s_gkey[w][e];
+#pragma unroll
+        for (int i = 0; i < ROUTE_GRP_MAX_M; ++i) {  // insert, keeping tk descending
+          if (i < grp.m && x > tk[i]) { const uint32_t y = tk[i]; tk[i] = x; x = y; }
+        }
+      }
+      gsc = key_float(tk[0]);
+#pragma unroll
+      for (int i = 1; i < ROUTE_GRP_MAX_M; ++i)
+        if (i < grp.m) gsc += key_float(tk[i]);
+      s_gsc[w][l] = gsc;
+    }
+    wave_sync();
+    int rank = 0;
+    for (int h = 0; h < grp.n_group; ++h) {
+      const float o = s_gsc[w][h];
+      rank += (o > gsc) || (o == gsc && h < l);
+    }
+    const uint64_t kept = wave_ballot(l < grp.n_group && rank < grp.topk_group);
+#pragma unroll
+    for (int j = 0; j < VPL; ++j) {
+      const int e = (j >> 2) * 256 + 4 * l + (j & 3);
+      if (e < E && !((kept >> (e / gs)) & 1)) key[j] = 0u;
+    }
   }
 
   // 1. bound: the K-th largest of the lanes' top-two keys (K <= 64 < 128)
@@ -703,19 +774,40 @@ __global__ __launch_bounds__(256) void k_route_select_wave(int T, int E, int K, 
     sel_sort_take<1>(s_ckey[w], s_cidx[w], ncan, l, selkey, selidx);
   else
     sel_sort_take<2>(s_ckey[w], s_cidx[w], ncan, l, selkey, selidx);
-  const float zmax = key_float((uint32_t)readlane_i((int)selkey, 0));
-  const float sc = l < K ? score_of(key_float(selkey), zmax, score) : 0.f;
-  const float sum = wave_sum_f(sc);
-  if (l < K) {
-    ids[(long)t * K + l] = (int16_t)selidx;
-    probs[(long)t * K + l] = sc / sum;
+  if constexpr (GRP) {
+    const float sc = l < K ? s_sig[w][selidx] : 0.f;
+    const float sum = wave_sum_f(sc);
+    if (l < K) {
+      ids[(long)t * K + l] = (int16_t)selidx;
+      probs[(long)t * K + l] = grp.scale * (sc / sum);
+    }
+  } else {
+    const float zmax = key_float((uint32_t)readlane_i((int)selkey, 0));
+    const float sc = l < K ? score_of(key_float(selkey), zmax, score) : 0.f;
+    const float sum = wave_sum_f(sc);
+    if (l < K) {
+      ids[(long)t * K + l] = (int16_t)selidx;
+      probs[(long)t * K + l] = sc / sum;
+    }
   }
 }
 
 hipError_t launch_route_select(int T, int E, int K, int S, int score, const float* partial,
                                const float* bias, const uint8_t* mask, int16_t* ids, float* probs,
-                               float* logits_out, int32_t* err, hipStream_t s) {
+                               float* logits_out, int32_t* err, hipStream_t s, const RouteGroups* grp,
+                               float* scores_out) {
   if (T == 0) return hipSuccess;
+  const RouteGroups g0 = grp ? *grp : RouteGroups{1, 1, 1, 1.f};
+  if (grp) {  // 32 < E <= ROUTE_GRP_MAX_E, checked by the caller
+    const dim3 g((T + 3) / 4), b(256);
+    if (E <= 256)
+      hipLaunchKernelGGL((k_route_select_wave<4, true>), g, b, 0, s, T, E, K, S, score, partial, bias, mask, ids,
+                         probs, logits_out, err, g0, scores_out);
+    else
+      hipLaunchKernelGGL((k_route_select_wave<16, true>), g, b, 0, s, T, E, K, S, score, partial, bias, mask,
+                         ids, probs, logits_out, err, g0, scores_out);
+    return hipGetLastError();
+  }
   if (E <= 32) {
     const dim3 g((T + 63) / 64), b(64);  // one thread per token, many small workgroups
     if (E <= 8)
@@ -730,17 +822,17 @@ hipError_t launch_route_select(int T, int E, int K, int S, int score, const floa
   } else {
     const dim3 g((T + 3) / 4), b(256);
     if (E <= 256)
-      hipLaunchKernelGGL(k_route_select_wave<4>, g, b, 0, s, T, E, K, S, score, partial, bias, mask, ids,
-                         probs, logits_out, err);
+      hipLaunchKernelGGL((k_route_select_wave<4, false>), g, b, 0, s, T, E, K, S, score, partial, bias, mask,
+                         ids, probs, logits_out, err, g0, nullptr);
     else if (E <= 1024)
-      hipLaunchKernelGGL(k_route_select_wave<16>, g, b, 0, s, T, E, K, S, score, partial, bias, mask, ids,
-                         probs, logits_out, err);
+      hipLaunchKernelGGL((k_route_select_wave<16, false>), g, b, 0, s, T, E, K, S, score, partial, bias, mask,
+                         ids, probs, logits_out, err, g0, nullptr);
     else if (E <= 2560)
-      hipLaunchKernelGGL(k_route_select_wave<40>, g, b, 0, s, T, E, K, S, score, partial, bias, mask, ids,
-                         probs, logits_out, err);
+      hipLaunchKernelGGL((k_route_select_wave<40, false>), g, b, 0, s, T, E, K, S, score, partial, bias, mask,
+                         ids, probs, logits_out, err, g0, nullptr);
     else
-      hipLaunchKernelGGL(k_route_select_wave<64>, g, b, 0, s, T, E, K, S, score, partial, bias, mask, ids,
-                         probs, logits_out, err);
+      hipLaunchKernelGGL((k_route_select_wave<64, false>), g, b, 0, s, T, E, K, S, score, partial, bias, mask,
+                         ids, probs, logits_out, err, g0, nullptr);
   }
   return hipGetLastError();
 }

@@ -146,6 +146,31 @@ int moe_route_topk(int T, int E, int K, int H, int score, int x_dtype, int w_dty
                    void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * Route, group-limited with a selection-only bias (a router refinement the
+ * pages list as next work; the definition is the DeepSeek-V3 Technical
+ * Report's, section "DeepSeekMoE with Auxiliary-Loss-Free Load Balancing")
+ *
+ * s[t,e] = sigmoid(logit[t,e]) in fp32.  Keys: s + bias[e] (one fp32 add;
+ * bias optional) steer the choice only.  The E experts form n_group groups of
+ * E/n_group consecutive ids; a group's score is the fp32 sum of its
+ * m = K/topk_group largest keys, largest first; the topk_group groups with the
+ * highest scores stay (ties: lower group index), and the K largest keys among
+ * their experts are selected (ties: lower id), listed by descending key.
+ * probs[t,k] = scale * s_k / sum_j s_j over the selected (bias not included).
+ * Masked tokens: ids -1, probs 0.  Logit source, bias, mask, logits_out,
+ * err, workspace: as moe_route_topk (no fused small-router path).
+ * scores_out (optional, 16-byte aligned) [T,E] fp32 receives s.
+ * Limits: 32 < E <= 1024; 1 <= n_group <= 64, n_group | E; 1 <= topk_group
+ * <= n_group; topk_group | K; K/topk_group <= min(8, E/n_group);
+ * 0 < scale < 3e38.  MOE_ERR_SHAPE otherwise.
+ * ------------------------------------------------------------------------ */
+int moe_route_topk_grouped(int T, int E, int K, int H, int n_group, int topk_group, float scale,
+                           int x_dtype, int w_dtype, const void* x, const void* w_prepared,
+                           const float* logits, const float* bias, const uint8_t* mask,
+                           int16_t* ids, float* probs, float* logits_out, float* scores_out,
+                           int32_t* err, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
  * Permute: device count, single-pass scan and permute to expert order
  *
  * Sparser-MoE page, section "Remove work that has no selected route": local

@@ -61,6 +61,35 @@ def test_route_validation():
     assert _route(T=0) == 0                                 # empty batch: a valid no-op
 
 
+def _groute(**kw):
+    from dropless_mixture_experts_radix_amd import _lib
+    a = dict(T=16, E=256, K=8, H=64, ng=8, tg=4, scale=1.0, x_dtype=1, w_dtype=1, x=None, w=None, logits=P,
+             bias=None, mask=None, ids=P, probs=P, lo=None, so=None, err=None, ws=None, wsb=0)
+    a.update(kw)
+    return _lib.lib.moe_route_topk_grouped(a["T"], a["E"], a["K"], a["H"], a["ng"], a["tg"], a["scale"],
+                                           a["x_dtype"], a["w_dtype"], a["x"], a["w"], a["logits"], a["bias"],
+                                           a["mask"], a["ids"], a["probs"], a["lo"], a["so"], a["err"], a["ws"],
+                                           a["wsb"], None)
+
+
+def test_grouped_route_validation():
+    assert _groute(T=0) == 0                  # empty batch: a valid no-op
+    assert _groute(E=32, ng=4, tg=2, K=4) == 2   # E <= 32: no grouped path
+    assert _groute(E=2048) == 2               # E > 1024
+    assert _groute(ng=7) == 2                 # n_group does not divide E
+    assert _groute(ng=128, E=512) == 2        # n_group > 64
+    assert _groute(tg=0) == 2
+    assert _groute(tg=9) == 2                 # topk_group > n_group
+    assert _groute(tg=3) == 2                 # topk_group does not divide K
+    assert _groute(K=36, tg=4) == 2           # K / topk_group > 8
+    assert _groute(E=64, ng=32, tg=4, K=12) == 2  # K / topk_group > E / n_group
+    assert _groute(scale=0.0) == 2
+    assert _groute(scale=float("nan")) == 2
+    assert _groute(so=P + 4) == 3             # scores_out not 16-byte aligned
+    assert _groute(ids=None) == 1
+    assert _groute(logits=None, x=P, w=P) == 5   # projection needs the workspace
+
+
 def test_permute_validation():
     from dropless_mixture_experts_radix_amd import _lib
     f = _lib.lib.moe_permute
