@@ -254,6 +254,31 @@ def mx_variant(steps, warmup, name="mixtral_mxfp8"):
     return out
 
 
+def graph_us(fn, inner=20, reps=5):
+    """GPU time per call of fn: `inner` calls captured back to back in one HIP
+    graph, replayed `reps` times between two events."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        for _ in range(inner):
+            fn()
+    torch.cuda.synchronize()
+    for _ in range(2):
+        g.replay()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(reps):
+        g.replay()
+    t1.record()
+    torch.cuda.synchronize()
+    us = t0.elapsed_time(t1) / (reps * inner) * 1000.0
+    del g
+    return us
+
+
 def other_workload(name, steps, warmup):
     """Layer time of another full-size workload of the method (not the metric's
     configuration): the DeepSeek-like layer (256 experts, Zipf-skewed loads,
@@ -290,6 +315,16 @@ def other_workload(name, steps, warmup):
     out = {"workload": f"{name}: T={cfg.T} H={cfg.H} E={cfg.E} local={cfg.local} K={cfg.K} F={cfg.F}",
            "layer_us": round(us, 2), "grouped_mlp_us": round(mlp_us, 2), "routed_rows": N,
            "grouped_gemm_tflops": round(flops / (mlp_us * 1e-6) / 1e12, 1)}
+    if logits is None:
+        import dropless_mixture_experts_radix_amd as D
+        # route alone (projection + selection), and its group-limited variant
+        # with a selection-only bias (8 groups of E/8 experts, 4 kept, gates x2.5)
+        out["route_us"] = round(graph_us(lambda: layer.route(x=x)), 2)
+        if cfg.E > 32 and cfg.E % 8 == 0 and cfg.K % 4 == 0:
+            bias = layer.bias if layer.bias is not None else torch.zeros(cfg.E, device=x.device)
+            out["grouped_route_us"] = round(graph_us(lambda: D.moe_route_topk_grouped(
+                layer.ids, layer.probs, 8, 4, 2.5, x=x, w_prepared=layer.w_prep, w_dtype=layer.w_dtype, E=cfg.E,
+                bias=bias, err=layer.err, workspace=layer.route_ws)), 2)
     del layer, x
     torch.cuda.empty_cache()
     return out

@@ -628,6 +628,33 @@ __global__ __launch_bounds__(256) void k_route_select_wave(int T, int E, int K, 
   }
   if constexpr (GRP) {
     const int gs = E / grp.n_group;
+    float gsc = 0.f;
+    if (grp.m <= 2 && (gs & 3) == 0 && gs <= 256 && ((gs >> 2) & ((gs >> 2) - 1)) == 0) {
+      // a group is gs/4 aligned lanes of one 256-expert chunk: the top two of
+      // each lane's 4 keys, merged across the group's lanes by xor shuffles
+      const int lanes = gs >> 2;
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        uint32_t a0 = 0u, a1 = 0u;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const uint32_t x = key[c * 4 + q];
+          a1 = max(a1, min(a0, x));
+          a0 = max(a0, x);
+        }
+        for (int o = 1; o < lanes; o <<= 1) {
+          const uint32_t b0 = (uint32_t)__shfl_xor((int)a0, o, 64), b1 = (uint32_t)__shfl_xor((int)a1, o, 64);
+          const uint32_t n1 = max(min(a0, b0), max(a1, b1));
+          a0 = max(a0, b0);
+          a1 = n1;
+        }
+        const int e = c * 256 + 4 * l;
+        if ((l & (lanes - 1)) == 0 && e < E)
+          s_gsc[w][e / gs] = grp.m == 2 ? key_float(a0) + key_float(a1) : key_float(a0);
+      }
+      wave_sync();
+      if (l < grp.n_group) gsc = s_gsc[w][l];
+    } else {
 #pragma unroll
     for (int j = 0; j < VPL; ++j) {
       const int e = (j >> 2) * 256 + 4 * l + (j & 3);
@@ -635,7 +662,6 @@ __global__ __launch_bounds__(256) void k_route_select_wave(int T, int E, int K, 
     }
     wave_sync();
     // lane g: the m largest keys of group g, descending, then their fp32 sum
-    float gsc = 0.f;
     if (l < grp.n_group) {
       uint32_t tk[ROUTE_GRP_MAX_M];
 #pragma unroll
@@ -654,6 +680,7 @@ __global__ __launch_bounds__(256) void k_route_select_wave(int T, int E, int K, 
       s_gsc[w][l] = gsc;
     }
     wave_sync();
+    }
     int rank = 0;
     for (int h = 0; h < grp.n_group; ++h) {
       const float o = s_gsc[w][h];

@@ -58,6 +58,8 @@ def _check(ids, probs, scores, logits, K, ng, tg, scale, bias, mask):
     (300, 90, 6, 3, 3, 1.0),       # rows not 16-byte aligned, every group kept
     (500, 64, 4, 64, 4, 1.0),      # one expert per group
     (200, 128, 16, 4, 2, 1.0),     # 8 keys summed per group
+    (600, 256, 8, 16, 8, 1.0),     # one key per group score, groups of 4 lanes
+    (333, 512, 4, 2, 2, 1.0),      # groups of 256 experts (64 lanes)
 ])
 def test_grouped_route_from_logits(T, E, K, ng, tg, scale):
     rng = np.random.default_rng(T + E + K)
