@@ -30,6 +30,9 @@ is computed here by plain definitions:
   mx4_quantize_rows     the same with E2M1 (MXFP4) elements
   grouped_mlp           per-expert dense SwiGLU MLP in float64
   combine               probability-weighted sum in k order
+  combine_backward, permute_backward, route_backward
+                        the gradients of those routing steps (by definition:
+                        the adjoint sums and the derivative of the scores)
 
 Every function is parity-pinned by tests/test_oracle_*.py (pages' worked sizes,
 closed forms, brute force, a second algorithm, library reductions); the whole
@@ -572,6 +575,80 @@ def combine(y_perm, slot_to_row, probs, out_dtype):
         ok = r >= 0
         out[ok] += p[ok, k][:, None] * y_perm[r[ok]]
     return round_to(out, out_dtype)
+
+
+# ---------------------------------------------------------------------------
+# Backward of the routing steps (the gradients of route, permute and combine;
+# the pages' router work spans forward and backward kernels)
+# ---------------------------------------------------------------------------
+
+def combine_backward(dout, y_perm, slot_to_row, probs, out_dtype):
+    """Gradients of out[t] = sum_k probs[t,k] * y_perm[slot_to_row[t,k]]:
+    d_y_perm[r] = probs[t,k] * dout[t] for the row r of slot (t,k), rounded to
+    out_dtype; d_probs[t,k] = <dout[t], y_perm[r]> (fp32), 0 without a row.
+    Returns (d_y_perm over rows [0, N), d_probs); N = the rows in use."""
+    dout = np.asarray(dout, np.float64)
+    y_perm = np.asarray(y_perm, np.float64)
+    s2r = np.asarray(slot_to_row)
+    p = np.asarray(probs, np.float64)
+    T, K = s2r.shape
+    N = int(s2r.max()) + 1 if (s2r >= 0).any() else 0
+    dy = np.zeros((N, dout.shape[1]), np.float64)
+    dp = np.zeros((T, K), np.float64)
+    for k in range(K):
+        r = s2r[:, k]
+        ok = r >= 0
+        dy[r[ok]] = p[ok, k][:, None] * dout[ok]
+        dp[ok, k] = np.einsum("th,th->t", dout[ok], y_perm[r[ok]])
+    return round_to(dy, out_dtype), dp.astype(np.float32)
+
+
+def permute_backward(d_x_perm, slot_to_row, out_dtype):
+    """Gradient of x_perm[r] = x[t] for the row r of each slot (t,k):
+    d_x[t] = sum over the token's slots with a row (k order) of d_x_perm[r]."""
+    d = np.asarray(d_x_perm, np.float64)
+    s2r = np.asarray(slot_to_row)
+    T, K = s2r.shape
+    out = np.zeros((T, d.shape[1]), np.float64)
+    for k in range(K):
+        r = s2r[:, k]
+        ok = r >= 0
+        out[ok] += d[r[ok]]
+    return round_to(out, out_dtype)
+
+
+def route_backward(ids, d_probs, score="softmax", probs=None, logits=None, score_bias=None, scale=1.0):
+    """Gradient of the probabilities with respect to the selected keys, for a
+    fixed selection (the choice itself is piecewise constant in the logits):
+    d_z[t,k] = dL/dz at expert ids[t,k], where z = logit (+ score_bias, the
+    bias that entered the scores: moe_route_topk's bias; none for the
+    group-limited route, whose bias only steers the choice).
+      softmax over the K selected keys (p given): d_z_k = p_k (g_k - sum_j p_j g_j);
+      normalized sigmoid, p_k = scale * s_k / S, s = sigma(z), S = sum_j s_j:
+        d_z_k = s_k (1 - s_k) (scale g_k - sum_j g_j p_j) / S.
+    Every other logit's gradient is 0.  Slots with id -1 give 0.  fp32."""
+    ids = np.asarray(ids).astype(np.int64)
+    g = np.asarray(d_probs, np.float64)
+    T, K = ids.shape
+    ok = ids >= 0
+    dz = np.zeros((T, K), np.float64)
+    if score == "softmax":
+        p = np.where(ok, np.asarray(probs, np.float64), 0.0)
+        dz = p * (g - (p * np.where(ok, g, 0.0)).sum(axis=1, keepdims=True))
+    elif score == "sigmoid":
+        lg = np.asarray(logits, np.float32)
+        z = np.take_along_axis(lg, np.where(ok, ids, 0), axis=1)
+        if score_bias is not None:
+            z = (z + np.asarray(score_bias, np.float32)[np.where(ok, ids, 0)]).astype(np.float32)
+        sg = np.where(ok, 1.0 / (1.0 + np.exp(-z.astype(np.float64))), 0.0)
+        S = sg.sum(axis=1, keepdims=True)
+        Ss = np.where(S > 0, S, 1.0)
+        p = scale * sg / Ss
+        gp = (np.where(ok, g, 0.0) * p).sum(axis=1, keepdims=True)
+        dz = sg * (1.0 - sg) * (scale * g - gp) / Ss
+    else:
+        raise ValueError(score)
+    return np.where(ok, dz, 0.0).astype(np.float32)
 
 
 # ---------------------------------------------------------------------------

@@ -1,0 +1,152 @@
+"""Pins of the oracle's routing backward (combine_backward, permute_backward,
+route_backward): adjoint identities of the linear steps, finite differences
+of the forward oracle's own probabilities, closed forms."""
+import numpy as np
+import pytest
+
+from oracle import moe_oracle as O
+
+
+def _routing(T, E, K, seed, mask_every=0):
+    rng = np.random.default_rng(seed)
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    mask = None
+    if mask_every:
+        mask = (np.arange(T) % mask_every == 1).astype(np.uint8)
+    ids, probs = O.route_topk(logits, K, "softmax", mask=mask)
+    perm = O.count_and_permute(ids, 0, E)
+    return rng, logits, ids, probs, perm
+
+
+def test_combine_backward_is_the_adjoint():
+    """sum_t <combine(y, p)[t], dout[t]> = sum_r <y[r], d_y[r]> (linear in y),
+    and the same form is linear in p with gradient d_probs (exact differences)."""
+    T, E, K, H = 50, 8, 3, 16
+    rng, _, ids, probs, perm = _routing(T, E, K, 1, mask_every=9)
+    s2r = perm["slot_to_row"]
+    N = int(perm["offsets"][-1])
+    y = rng.standard_normal((N, H))
+    dout = rng.standard_normal((T, H))
+    p = probs.astype(np.float64)
+    dy, dp = O.combine_backward(dout, y, s2r, p, "f64")
+    f = lambda pp: float((O.combine(y, s2r, pp, "f64") * dout).sum())
+    np.testing.assert_allclose(f(p), float((y * dy).sum()), rtol=1e-12)
+    for t, k in [(0, 0), (3, 2), (T - 1, 1), (1, 0)]:
+        e = np.zeros_like(p)
+        e[t, k] = 1.0
+        want = f(p + e) - f(p)   # exact up to rounding: f is linear in p
+        np.testing.assert_allclose(dp[t, k], want, rtol=1e-5, atol=1e-6)
+    assert (dp[s2r < 0] == 0).all()
+
+
+def test_combine_backward_brute_force():
+    T, E, K, H = 12, 4, 2, 5
+    rng, _, ids, probs, perm = _routing(T, E, K, 2)
+    s2r = perm["slot_to_row"]
+    N = int(perm["offsets"][-1])
+    y = rng.standard_normal((N, H))
+    dout = rng.standard_normal((T, H))
+    dy, dp = O.combine_backward(dout, y, s2r, probs, "f64")
+    for t in range(T):
+        for k in range(K):
+            r = s2r[t, k]
+            np.testing.assert_allclose(dy[r], float(probs[t, k]) * dout[t], rtol=1e-15)
+            np.testing.assert_allclose(dp[t, k], sum(dout[t, h] * y[r, h] for h in range(H)), rtol=1e-6)
+
+
+def test_permute_backward_is_the_adjoint():
+    """<x_perm(x), g> = <x, permute_backward(g)>."""
+    T, E, K, H = 40, 6, 2, 8
+    rng, _, ids, probs, perm = _routing(T, E, K, 3, mask_every=7)
+    x = rng.standard_normal((T, H))
+    xp = O.count_and_permute(ids, 0, E, x)["x_perm"]
+    g = rng.standard_normal(xp.shape)
+    dx = O.permute_backward(g, perm["slot_to_row"], "f64")
+    np.testing.assert_allclose(float((xp * g).sum()), float((x * dx).sum()), rtol=1e-12)
+    masked = (np.arange(T) % 7 == 1)
+    assert (dx[masked] == 0).all()
+
+
+def _fd(fn, z, eps=1e-6):
+    out = np.zeros_like(z)
+    for i in np.ndindex(z.shape):
+        zp, zm = z.copy(), z.copy()
+        zp[i] += eps
+        zm[i] -= eps
+        out[i] = (fn(zp) - fn(zm)) / (2 * eps)
+    return out
+
+
+@pytest.mark.parametrize("K", [1, 2, 4])
+def test_route_backward_softmax_matches_finite_differences(K):
+    rng = np.random.default_rng(10 + K)
+    T, E = 6, 8
+    logits = rng.standard_normal((T, E))
+    ids, probs = O.route_topk(logits.astype(np.float32), K)
+    g = rng.standard_normal((T, K))
+    dz = O.route_backward(ids, g, "softmax", probs=probs)
+    for t in range(T):
+        zs = logits[t, ids[t].astype(int)]
+        # the float64 softmax of the selected keys (the forward stores fp32)
+        fn = lambda zz: float((g[t] * np.exp(zz - zz.max()) / np.exp(zz - zz.max()).sum()).sum())
+        np.testing.assert_allclose(dz[t], _fd(fn, zs.astype(np.float64)), rtol=2e-5, atol=1e-6)
+        assert abs(float(dz[t].sum())) < 1e-6   # shift invariance of softmax
+    if K == 1:
+        assert (dz == 0).all()
+
+
+@pytest.mark.parametrize("scale,with_bias", [(1.0, True), (2.5, False)])
+def test_route_backward_sigmoid_matches_finite_differences(scale, with_bias):
+    rng = np.random.default_rng(20)
+    T, E, K = 5, 12, 4
+    logits = rng.standard_normal((T, E))
+    b = (rng.standard_normal(E) * 0.3).astype(np.float32) if with_bias else None
+    ids, _ = O.route_topk(logits.astype(np.float32), K, "sigmoid", bias=b)
+    g = rng.standard_normal((T, K))
+    dz = O.route_backward(ids, g, "sigmoid", logits=logits.astype(np.float32), score_bias=b, scale=scale)
+    for t in range(T):
+        sel = ids[t].astype(int)
+        bb = np.zeros(K) if b is None else b[sel].astype(np.float64)
+
+        def fn(zz):
+            s = 1.0 / (1.0 + np.exp(-(zz + bb)))
+            return float((g[t] * scale * s / s.sum()).sum())
+        np.testing.assert_allclose(dz[t], _fd(fn, logits[t, sel].astype(np.float64)), rtol=2e-5, atol=1e-6)
+
+
+def test_route_backward_grouped_matches_finite_differences_of_the_forward():
+    """The group-limited route's gates, taken from the forward oracle itself
+    (selection fixed: a step of 1e-4 moves no choice on these logits)."""
+    rng = np.random.default_rng(30)
+    T, E, K, ng, tg = 4, 32, 4, 4, 2
+    logits = rng.standard_normal((T, E)) * 2
+    b = (rng.standard_normal(E) * 0.2).astype(np.float32)
+    ids, p = O.route_grouped(logits.astype(np.float32), K, ng, tg, bias=b, scale=2.5)
+    g = rng.standard_normal((T, K))
+    dz = O.route_backward(ids, g, "sigmoid", logits=logits.astype(np.float32), score_bias=None, scale=2.5)
+    eps = 1e-4
+    for t in range(T):
+        sel = ids[t].astype(int)
+        for k in range(K):
+            zp, zm = logits[t:t + 1].copy(), logits[t:t + 1].copy()
+            zp[0, sel[k]] += eps
+            zm[0, sel[k]] -= eps
+            sp = 1.0 / (1.0 + np.exp(-zp))
+            sm = 1.0 / (1.0 + np.exp(-zm))
+            ip, pp = O.route_grouped(zp.astype(np.float32), K, ng, tg, bias=b, scale=2.5, scores=sp)
+            im, pm = O.route_grouped(zm.astype(np.float32), K, ng, tg, bias=b, scale=2.5, scores=sm)
+            assert (ip == ids[t]).all() and (im == ids[t]).all()
+            # float64 gates of the fixed selection, recomputed from the float64 scores
+            fp = float((g[t] * 2.5 * sp[0, sel] / sp[0, sel].sum()).sum())
+            fm = float((g[t] * 2.5 * sm[0, sel] / sm[0, sel].sum()).sum())
+            np.testing.assert_allclose(dz[t, k], (fp - fm) / (2 * eps), rtol=1e-4, atol=1e-6)
+
+
+def test_route_backward_masked_and_invalid_slots():
+    ids = np.array([[-1, -1], [3, 1]], np.int16)
+    probs = np.array([[0, 0], [0.75, 0.25]], np.float32)
+    g = np.array([[5.0, 7.0], [1.0, -1.0]])
+    dz = O.route_backward(ids, g, "softmax", probs=probs)
+    assert (dz[0] == 0).all()
+    # closed form for K = 2: d_z0 = p0 p1 (g0 - g1) = -d_z1
+    np.testing.assert_allclose(dz[1], [0.75 * 0.25 * 2.0, -0.75 * 0.25 * 2.0], rtol=1e-6)
