@@ -330,6 +330,33 @@ def other_workload(name, steps, warmup):
     return out
 
 
+def backward_stages(layer, cfg, N):
+    """GPU time per call (graph replays) of the routing backward on the layer's
+    own maps: combine backward (d_y_perm and d_probs from a dout), permute
+    backward (a token's gradient from its rows'), route backward (gate
+    gradients with respect to the selected keys); algorithmic GB/s."""
+    import dropless_mixture_experts_radix_amd as D
+    T, H, K = cfg.T, cfg.H, cfg.K
+    g = torch.Generator(device="cuda").manual_seed(99)
+    dout = torch.randn((T, H), generator=g, device="cuda").to(torch.bfloat16)
+    d_y = torch.empty_like(layer.y_perm)
+    d_p = torch.empty((T, K), dtype=torch.float32, device="cuda")
+    d_x = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
+    d_z = torch.empty((T, K), dtype=torch.float32, device="cuda")
+    t_cb = graph_us(lambda: D.moe_unpermute_combine_backward(dout, layer.y_perm, layer.slot_to_row, layer.probs,
+                                                              d_y, d_p))
+    t_pb = graph_us(lambda: D.moe_permute_backward(d_y, layer.slot_to_row, d_x))
+    t_rb = graph_us(lambda: D.moe_route_backward(layer.ids, d_p, d_z, layer.score, probs=layer.probs, E=cfg.E))
+    cb_bytes = T * H * 2 + 2 * N * H * 2 + T * K * 12
+    pb_bytes = N * H * 2 + T * H * 2 + T * K * 4
+    return {"combine_backward_us": round(t_cb, 2), "combine_backward_gbs": round(cb_bytes / (t_cb * 1e-6) / 1e9, 1),
+            "permute_backward_us": round(t_pb, 2), "permute_backward_gbs": round(pb_bytes / (t_pb * 1e-6) / 1e9, 1),
+            "route_backward_us": round(t_rb, 2),
+            "note": "GPU time per call from HIP-graph replays; GB/s = algorithmic bytes (combine backward: dout, "
+                    "y_perm read, d_y_perm written, maps/probs/d_probs; permute backward: rows read, token rows "
+                    "written, map) / time"}
+
+
 def main():
     a = parse()
     if a.gpus != 1:
@@ -389,6 +416,10 @@ def main():
                      "frac": round(tflops / BF16_PEAK_TFLOPS, 4), "traffic": measured_traffic(),
                      "traffic_unit": "HBM bytes per launch", "algorithmic_flops_per_launch": flops},
     }
+    try:
+        line["backward"] = backward_stages(layer, cfg, N)
+    except Exception as ex:  # report, do not hide the main line
+        line["backward"] = {"error": repr(ex)}
     if not a.no_mx:
         try:
             del layer

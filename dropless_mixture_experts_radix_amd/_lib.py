@@ -36,6 +36,9 @@ _SIGS = {
     "moe_grouped_mlp": (_I, [_I, _I, _I, _I64, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "moe_unpermute_combine": (_I, [_I, _I, _I, _I, _P, _P, _P, _P, _P]),
     "moe_mx_quantize": (_I, [_I64, _I, _P, _P, _P, _P, _P]),
+    "moe_unpermute_combine_backward": (_I, [_I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P]),
+    "moe_permute_backward": (_I, [_I, _I, _I, _I, _P, _P, _P, _P]),
+    "moe_route_backward": (_I, [_I, _I, _I, _I, ctypes.c_float, _P, _P, _P, _P, _P, _P, _P]),
 }
 
 
@@ -189,3 +192,39 @@ def moe_mx_quantize(inp, codes, scales, row_limit=None):
     rows, cols = inp.shape
     _check(lib.moe_mx_quantize(rows, cols, _p(inp), _p(row_limit), _p(codes), _p(scales), _stream()),
            "moe_mx_quantize")
+
+
+# ----------------------------------------------------------------- backward
+def _need(t, dtype, name):
+    if t is not None and t.dtype != dtype:
+        raise MoEError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def moe_unpermute_combine_backward(dout, y_perm, slot_to_row, probs, d_y_perm, d_probs):
+    _need(slot_to_row, torch.int32, "slot_to_row")
+    _need(probs, torch.float32, "probs")
+    _need(d_probs, torch.float32, "d_probs")
+    T, K = slot_to_row.shape
+    H = dout.shape[1]
+    _check(lib.moe_unpermute_combine_backward(T, K, H, dtype_code(dout.dtype), _p(dout), _p(y_perm),
+                                              _p(slot_to_row), _p(probs), _p(d_y_perm), _p(d_probs), _stream()),
+           "moe_unpermute_combine_backward")
+
+
+def moe_permute_backward(d_x_perm, slot_to_row, d_x):
+    _need(slot_to_row, torch.int32, "slot_to_row")
+    T, K = slot_to_row.shape
+    H = d_x.shape[1]
+    _check(lib.moe_permute_backward(T, K, H, dtype_code(d_x.dtype), _p(d_x_perm), _p(slot_to_row), _p(d_x),
+                                    _stream()), "moe_permute_backward")
+
+
+def moe_route_backward(ids, d_probs, d_z, score, *, probs=None, logits=None, score_bias=None, scale=1.0, E=None):
+    _need(ids, torch.int16, "ids")
+    for t, n in ((d_probs, "d_probs"), (d_z, "d_z"), (probs, "probs"), (logits, "logits"), (score_bias, "score_bias")):
+        _need(t, torch.float32, n)
+    T, K = ids.shape
+    if logits is not None:
+        E = logits.shape[1]
+    _check(lib.moe_route_backward(T, E, K, score, float(scale), _p(ids), _p(probs), _p(d_probs), _p(logits),
+                                  _p(score_bias), _p(d_z), _stream()), "moe_route_backward")

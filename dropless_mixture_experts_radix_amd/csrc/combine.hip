@@ -10,7 +10,9 @@ namespace moe {
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 // One wavefront per token, 4 per workgroup.  Each lane owns 16 bytes of every
-// 1 KiB piece of the row; up to 8 pieces are accumulated at once.
+// 1 KiB piece of the row; up to 8 pieces are accumulated at once.  With probs
+// NULL every weight is 1: the backward of the permute (a token's gradient is
+// the sum of its routed rows' gradients, k order).
 template <bool BF16>
 __global__ __launch_bounds__(256) void k_combine(int T, int K, int H, const uint8_t* __restrict__ y,
                                                  const int32_t* __restrict__ s2r,
@@ -23,7 +25,7 @@ __global__ __launch_bounds__(256) void k_combine(int T, int K, int H, const uint
   float p = 0.f;
   if (l < K) {
     r = s2r[(long)t * K + l];
-    p = probs[(long)t * K + l];
+    p = probs ? probs[(long)t * K + l] : 1.f;
   }
   const uint64_t bits = wave_ballot(r >= 0);
   const int row_bytes = H * (BF16 ? 2 : 4);
@@ -78,6 +80,150 @@ __global__ __launch_bounds__(256) void k_combine(int T, int K, int H, const uint
       }
     }
   }
+}
+
+// Backward of the combine, one wavefront per token: for each of its slots with
+// a row r (k order) d_y[r] = p * dout[t] (rounded like y) and d_probs[t,k] =
+// <dout[t], y[r]> (each lane's fixed-order fp32 partial, then the wavefront's
+// fixed tree); slots without a row get d_probs 0.  The token's dout pieces are
+// re-read per slot (cache hits after the first).
+template <bool BF16>
+__global__ __launch_bounds__(256) void k_combine_backward(int T, int K, int H, const uint8_t* __restrict__ dout,
+                                                          const uint8_t* __restrict__ y,
+                                                          const int32_t* __restrict__ s2r,
+                                                          const float* __restrict__ probs,
+                                                          uint8_t* __restrict__ dy, float* __restrict__ dprobs) {
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + w;
+  if (t >= T) return;
+  int r = -1;
+  float p = 0.f;
+  if (l < K) {
+    r = s2r[(long)t * K + l];
+    p = probs[(long)t * K + l];
+    if (r < 0) dprobs[(long)t * K + l] = 0.f;
+  }
+  const uint64_t bits = wave_ballot(r >= 0);
+  const int row_bytes = H * (BF16 ? 2 : 4);
+  const int npiece = (row_bytes + 1023) / 1024;
+  const uint8_t* src_g = dout + (long)t * row_bytes;
+  uint64_t b = bits;
+  while (b) {  // k order
+    const int k = __builtin_ctzll(b);
+    b &= b - 1;
+    const int d = readlane_i(r, k);
+    const float pk = readlane_f(p, k);
+    const uint8_t* src_y = y + (long)d * row_bytes;
+    uint8_t* dst = dy + (long)d * row_bytes;
+    float part = 0.f;
+    for (int p0 = 0; p0 < npiece; p0 += 8) {
+      u32x4 gv[8], yv[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int off = (p0 + j) * 1024 + l * 16;
+        const bool in = p0 + j < npiece && off < row_bytes;
+        gv[j] = in ? *(const u32x4*)(src_g + off) : u32x4{0, 0, 0, 0};
+        yv[j] = in ? *(const u32x4*)(src_y + off) : u32x4{0, 0, 0, 0};
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int off = (p0 + j) * 1024 + l * 16;
+        u32x4 o;
+        if (BF16) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const float g0 = bf16_to_f32(gv[j][q] & 0xffffu), g1 = bf16_to_f32(gv[j][q] >> 16);
+            part = fmaf(g0, bf16_to_f32(yv[j][q] & 0xffffu), part);
+            part = fmaf(g1, bf16_to_f32(yv[j][q] >> 16), part);
+            o[q] = f32_to_bf16(pk * g0) | (f32_to_bf16(pk * g1) << 16);
+          }
+        } else {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const float g0 = __uint_as_float(gv[j][q]);
+            part = fmaf(g0, __uint_as_float(yv[j][q]), part);
+            o[q] = __float_as_uint(pk * g0);
+          }
+        }
+        if (p0 + j < npiece && off < row_bytes) *(u32x4*)(dst + off) = o;
+      }
+    }
+    const float dot = wave_sum_f(part);
+    if (l == 0) dprobs[(long)t * K + k] = dot;
+  }
+}
+
+// Backward of the route's gates for a fixed selection, one thread per token:
+// d_z[t,k] = dL/dz at expert ids[t,k] (z = logit + score_bias).  Softmax over
+// the selected keys: d_z_k = p_k (g_k - sum_j p_j g_j).  Normalized sigmoid,
+// p_k = scale s_k / S with s = sigma(z): d_z_k = s_k (1 - s_k) (scale g_k -
+// sum_j g_j p_j) / S.  Slots with id -1 give 0.
+__global__ __launch_bounds__(256) void k_route_backward(int T, int E, int K, int score, float scale,
+                                                        const int16_t* __restrict__ ids,
+                                                        const float* __restrict__ probs,
+                                                        const float* __restrict__ dprobs,
+                                                        const float* __restrict__ logits,
+                                                        const float* __restrict__ score_bias,
+                                                        float* __restrict__ dz) {
+  const int t = blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= T) return;
+  const int16_t* id = ids + (long)t * K;
+  const float* g = dprobs + (long)t * K;
+  float* o = dz + (long)t * K;
+  if (score == MOE_SCORE_SOFTMAX) {
+    const float* p = probs + (long)t * K;
+    float gp = 0.f;
+    for (int k = 0; k < K; ++k)
+      if (id[k] >= 0) gp = fmaf(p[k], g[k], gp);
+    for (int k = 0; k < K; ++k) o[k] = id[k] >= 0 ? p[k] * (g[k] - gp) : 0.f;
+  } else {
+    float S = 0.f;
+    for (int k = 0; k < K; ++k) {
+      if (id[k] < 0) continue;
+      float z = logits[(long)t * E + id[k]];
+      if (score_bias) z += score_bias[id[k]];
+      S += 1.0f / (1.0f + expf(-z));
+    }
+    const float inv = S > 0.f ? 1.0f / S : 0.f;
+    float gp = 0.f;
+    for (int k = 0; k < K; ++k) {
+      if (id[k] < 0) continue;
+      float z = logits[(long)t * E + id[k]];
+      if (score_bias) z += score_bias[id[k]];
+      const float sg = 1.0f / (1.0f + expf(-z));
+      gp = fmaf(g[k], scale * sg * inv, gp);
+    }
+    for (int k = 0; k < K; ++k) {
+      if (id[k] < 0) { o[k] = 0.f; continue; }
+      float z = logits[(long)t * E + id[k]];
+      if (score_bias) z += score_bias[id[k]];
+      const float sg = 1.0f / (1.0f + expf(-z));
+      o[k] = sg * (1.0f - sg) * (scale * g[k] - gp) * inv;
+    }
+  }
+}
+
+hipError_t launch_combine_backward(int T, int K, int H, int dtype, const void* dout, const void* y,
+                                   const int32_t* s2r, const float* probs, void* dy, float* dprobs,
+                                   hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  const dim3 g((T + 3) / 4), b(256);
+  if (dtype == MOE_F32)
+    hipLaunchKernelGGL(k_combine_backward<false>, g, b, 0, s, T, K, H, (const uint8_t*)dout, (const uint8_t*)y,
+                       s2r, probs, (uint8_t*)dy, dprobs);
+  else
+    hipLaunchKernelGGL(k_combine_backward<true>, g, b, 0, s, T, K, H, (const uint8_t*)dout, (const uint8_t*)y,
+                       s2r, probs, (uint8_t*)dy, dprobs);
+  return hipGetLastError();
+}
+
+hipError_t launch_route_backward(int T, int E, int K, int score, float scale, const int16_t* ids,
+                                 const float* probs, const float* dprobs, const float* logits,
+                                 const float* score_bias, float* dz, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_route_backward, dim3((T + 255) / 256), dim3(256), 0, s, T, E, K, score, scale, ids, probs,
+                     dprobs, logits, score_bias, dz);
+  return hipGetLastError();
 }
 
 hipError_t launch_combine(int T, int K, int H, int dtype, const void* y, const int32_t* s2r,

@@ -290,6 +290,42 @@ int moe_unpermute_combine(int T, int K, int H, int dtype, const void* y_perm, co
 }
 
 // ---------------------------------------------------------------------------
+// Backward of the routing steps
+// ---------------------------------------------------------------------------
+int moe_unpermute_combine_backward(int T, int K, int H, int dtype, const void* dout, const void* y_perm,
+                                   const int32_t* slot_to_row, const float* probs, void* d_y_perm,
+                                   float* d_probs, void* stream) {
+  if (T < 0 || K < 1 || K > MOE_MAX_K || H <= 0 || H % 8) return MOE_ERR_SHAPE;
+  if (dtype != MOE_BF16 && dtype != MOE_F32) return MOE_ERR_DTYPE;
+  if (T > 0 && (!dout || !slot_to_row || !probs || !d_probs)) return MOE_ERR_NULL;
+  if (!aligned16(dout) || !aligned16(y_perm) || !aligned16(d_y_perm)) return MOE_ERR_ALIGN;
+  return launch_status(launch_combine_backward(T, K, H, dtype, dout, y_perm, slot_to_row, probs, d_y_perm,
+                                               d_probs, (hipStream_t)stream));
+}
+
+int moe_permute_backward(int T, int K, int H, int dtype, const void* d_x_perm, const int32_t* slot_to_row,
+                         void* d_x, void* stream) {
+  if (T < 0 || K < 1 || K > MOE_MAX_K || H <= 0 || H % 8) return MOE_ERR_SHAPE;
+  if (dtype != MOE_BF16 && dtype != MOE_F32) return MOE_ERR_DTYPE;
+  if (T > 0 && (!slot_to_row || !d_x)) return MOE_ERR_NULL;
+  if (!aligned16(d_x_perm) || !aligned16(d_x)) return MOE_ERR_ALIGN;
+  return launch_status(launch_combine(T, K, H, dtype, d_x_perm, slot_to_row, nullptr, d_x, (hipStream_t)stream));
+}
+
+int moe_route_backward(int T, int E, int K, int score, float scale, const int16_t* ids, const float* probs,
+                       const float* d_probs, const float* logits, const float* score_bias, float* d_z,
+                       void* stream) {
+  if (T < 0 || E <= 0 || E > MOE_MAX_E || K < 1 || K > E || K > MOE_MAX_K) return MOE_ERR_SHAPE;
+  if (score != MOE_SCORE_SOFTMAX && score != MOE_SCORE_SIGMOID) return MOE_ERR_DTYPE;
+  if (!(scale > 0.f) || scale > 3.0e38f) return MOE_ERR_SHAPE;
+  if (T > 0 && (!ids || !d_probs || !d_z)) return MOE_ERR_NULL;
+  if (T > 0 && score == MOE_SCORE_SOFTMAX && !probs) return MOE_ERR_NULL;
+  if (T > 0 && score == MOE_SCORE_SIGMOID && !logits) return MOE_ERR_NULL;
+  return launch_status(launch_route_backward(T, E, K, score, scale, ids, probs, d_probs, logits, score_bias, d_z,
+                                             (hipStream_t)stream));
+}
+
+// ---------------------------------------------------------------------------
 // Standalone MX quantizer
 // ---------------------------------------------------------------------------
 int moe_mx_quantize(int64_t rows, int cols, const void* in, const int32_t* row_limit, uint8_t* codes,

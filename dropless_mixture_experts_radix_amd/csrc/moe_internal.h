@@ -219,6 +219,12 @@ hipError_t launch_grouped_mlp_mx(int L, int H, int F, int64_t capacity, bool fp4
 
 hipError_t launch_combine(int T, int K, int H, int dtype, const void* y, const int32_t* s2r,
                           const float* probs, void* out, hipStream_t s);
+hipError_t launch_combine_backward(int T, int K, int H, int dtype, const void* dout, const void* y,
+                                   const int32_t* s2r, const float* probs, void* dy, float* dprobs,
+                                   hipStream_t s);
+hipError_t launch_route_backward(int T, int E, int K, int score, float scale, const int16_t* ids,
+                                 const float* probs, const float* dprobs, const float* logits,
+                                 const float* score_bias, float* dz, hipStream_t s);
 
 hipError_t launch_mx_quantize(int64_t rows, int cols, const bf16_t* in, const int32_t* row_limit,
                               uint8_t* codes, uint8_t* scales, hipStream_t s);

@@ -13,6 +13,7 @@
  *   moe_grouped_mlp        ragged grouped SwiGLU MLP (fp32, bf16, MXFP8 or MXFP4)
  *   moe_unpermute_combine  probability-weighted sum back in token order
  *
+ * and the backward of the routing steps (combine, permute, route gates),
  * plus one-time weight preparation and a standalone MX quantizer.
  *
  * Conventions shared by every call
@@ -300,6 +301,41 @@ int moe_grouped_mlp(int L, int H, int F, int64_t capacity, int dtype,
 int moe_unpermute_combine(int T, int K, int H, int dtype,
                           const void* y_perm, const int32_t* slot_to_row, const float* probs,
                           void* out, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Backward of the routing steps (the pages' router work covered forward and
+ * backward kernels; sparser-MoE page, "The workload changes the bottleneck").
+ * For a fixed selection, with slot (t,k) routed to row r = slot_to_row[t,k]:
+ *
+ * moe_unpermute_combine_backward: gradients of moe_unpermute_combine's
+ *   out[t] = sum_k probs[t,k] * y_perm[r]:
+ *   d_y_perm[r] = probs[t,k] * dout[t] (dtype as y_perm, rounded once from
+ *   fp32; rows without a slot untouched); d_probs[t,k] = <dout[t], y_perm[r]>
+ *   (fp32, each lane's fixed-order sum then a fixed tree: deterministic), 0 for
+ *   slots without a row.  dout [T,H], y_perm and d_y_perm [capacity,H] device.
+ * moe_permute_backward: gradient of moe_permute's x_perm[r] = x[t]:
+ *   d_x[t] = sum over the token's slots with a row (k order, fp32) of
+ *   d_x_perm[r]; tokens without one get a zero row.
+ * moe_route_backward: gradient of the gates with respect to the selected keys
+ *   z = logit (+ score_bias), d_z [T,K] fp32 aligned with ids; the gradient
+ *   of logit[t, ids[t,k]] is d_z[t,k] and of every other logit 0 (the choice
+ *   is piecewise constant).  MOE_SCORE_SOFTMAX (probs needed): d_z_k = p_k
+ *   (g_k - sum_j p_j g_j), g = d_probs.  MOE_SCORE_SIGMOID (logits [T,E]
+ *   needed): p_k = scale s_k / S, s = sigma(z), S = sum_j s_j, d_z_k = s_k
+ *   (1 - s_k) (scale g_k - sum_j g_j p_j) / S.  score_bias: moe_route_topk's
+ *   bias (it enters the scores); NULL for moe_route_topk_grouped, whose bias
+ *   only steers the choice (pass its scale).  Slots with id -1 give 0.
+ * Limits as the forward calls; dtype MOE_BF16 or MOE_F32; H % 8 == 0;
+ * 0 < scale < 3e38.
+ * ------------------------------------------------------------------------ */
+int moe_unpermute_combine_backward(int T, int K, int H, int dtype, const void* dout, const void* y_perm,
+                                   const int32_t* slot_to_row, const float* probs, void* d_y_perm,
+                                   float* d_probs, void* stream);
+int moe_permute_backward(int T, int K, int H, int dtype, const void* d_x_perm, const int32_t* slot_to_row,
+                         void* d_x, void* stream);
+int moe_route_backward(int T, int E, int K, int score, float scale, const int16_t* ids, const float* probs,
+                       const float* d_probs, const float* logits, const float* score_bias, float* d_z,
+                       void* stream);
 
 /* ------------------------------------------------------------------------
  * Standalone MX quantization of bf16 rows (OCP MX v1.0, E4M3 + E8M0, blocks

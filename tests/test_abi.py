@@ -90,6 +90,29 @@ def test_grouped_route_validation():
     assert _groute(logits=None, x=P, w=P) == 5   # projection needs the workspace
 
 
+def test_backward_validation():
+    from dropless_mixture_experts_radix_amd import _lib
+    L = _lib.lib
+    # combine backward: (T, K, H, dtype, dout, y, s2r, probs, d_y, d_probs, stream)
+    assert L.moe_unpermute_combine_backward(0, 2, 64, 1, None, None, None, None, None, None, None) == 0
+    assert L.moe_unpermute_combine_backward(4, 2, 60, 1, P, P, P, P, P, P, None) == 2   # H % 8
+    assert L.moe_unpermute_combine_backward(4, 2, 64, 3, P, P, P, P, P, P, None) == 4   # dtype
+    assert L.moe_unpermute_combine_backward(4, 2, 64, 1, P, P, P, None, P, P, None) == 1
+    assert L.moe_unpermute_combine_backward(4, 2, 64, 1, P + 8, P, P, P, P, P, None) == 3
+    # permute backward: (T, K, H, dtype, d_x_perm, s2r, d_x, stream)
+    assert L.moe_permute_backward(0, 2, 64, 1, None, None, None, None) == 0
+    assert L.moe_permute_backward(4, 65, 64, 1, P, P, P, None) == 2
+    assert L.moe_permute_backward(4, 2, 64, 1, P, None, P, None) == 1
+    assert L.moe_permute_backward(4, 2, 64, 1, P, P, P + 4, None) == 3
+    # route backward: (T, E, K, score, scale, ids, probs, d_probs, logits, bias, d_z, stream)
+    assert L.moe_route_backward(0, 8, 2, 0, 1.0, None, None, None, None, None, None, None) == 0
+    assert L.moe_route_backward(4, 8, 9, 0, 1.0, P, P, P, None, None, P, None) == 2    # K > E
+    assert L.moe_route_backward(4, 8, 2, 5, 1.0, P, P, P, None, None, P, None) == 4    # score
+    assert L.moe_route_backward(4, 8, 2, 0, 0.0, P, P, P, None, None, P, None) == 2    # scale
+    assert L.moe_route_backward(4, 8, 2, 0, 1.0, P, None, P, None, None, P, None) == 1  # softmax needs probs
+    assert L.moe_route_backward(4, 8, 2, 1, 1.0, P, P, P, None, None, P, None) == 1    # sigmoid needs logits
+
+
 def test_permute_validation():
     from dropless_mixture_experts_radix_amd import _lib
     f = _lib.lib.moe_permute
