@@ -33,6 +33,8 @@ is computed here by plain definitions:
   combine_backward, permute_backward, route_backward
                         the gradients of those routing steps (by definition:
                         the adjoint sums and the derivative of the scores)
+  grouped_mlp_backward_data   the data gradient of the grouped MLP (chain rule
+                        through both GEMMs and SwiGLU, h recomputed)
 
 Every function is parity-pinned by tests/test_oracle_*.py (pages' worked sizes,
 closed forms, brute force, a second algorithm, library reductions); the whole
@@ -649,6 +651,42 @@ def route_backward(ids, d_probs, score="softmax", probs=None, logits=None, score
     else:
         raise ValueError(score)
     return np.where(ok, dz, 0.0).astype(np.float32)
+
+
+def swiglu_backward(h, d_a, F):
+    """Gradient of a = silu(g) * u (g = h[:, :F], u = h[:, F:]) with respect to
+    h: d_g = d_a * u * silu'(g), silu'(g) = sigma(g) (1 + g (1 - sigma(g))),
+    d_u = d_a * silu(g); returns [d_g, d_u]."""
+    g = h[:, :F]
+    u = h[:, F:]
+    sg = 1.0 / (1.0 + np.exp(-g))
+    return np.concatenate([d_a * u * sg * (1.0 + g * (1.0 - sg)), d_a * g * sg], axis=1)
+
+
+def grouped_mlp_backward_data(x_perm, offsets, W1, W2, d_y, dtype):
+    """Data gradient of the grouped SwiGLU MLP: for each expert's rows,
+    d_x = d_h . W1[e]^T with d_h = swiglu'(h, d_a), d_a = d_y . W2[e]^T and
+    h = X . W1[e] recomputed.  Rounding points of the bf16 path: h and d_h
+    are stored as bf16 (d_a is not stored), d_x is bf16; "f64" rounds
+    nothing.  Returns d_x over rows [0, N)."""
+    x_perm = np.asarray(x_perm, np.float64)
+    d_y = np.asarray(d_y, np.float64)
+    N = int(offsets[-1])
+    H = x_perm.shape[1]
+    out = np.zeros((N, H), np.float64)
+    rnd = (lambda v: v) if dtype == "f64" else bf16_round
+    for e in range(len(offsets) - 1):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        if hi == lo:
+            continue
+        W1e = np.asarray(W1[e], np.float64)
+        W2e = np.asarray(W2[e], np.float64)
+        F = W2e.shape[0]
+        h = rnd(x_perm[lo:hi] @ W1e)
+        d_a = d_y[lo:hi] @ W2e.T
+        d_h = rnd(swiglu_backward(h, d_a, F))
+        out[lo:hi] = rnd(d_h @ W1e.T)
+    return out
 
 
 # ---------------------------------------------------------------------------

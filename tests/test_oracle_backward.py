@@ -150,3 +150,47 @@ def test_route_backward_masked_and_invalid_slots():
     assert (dz[0] == 0).all()
     # closed form for K = 2: d_z0 = p0 p1 (g0 - g1) = -d_z1
     np.testing.assert_allclose(dz[1], [0.75 * 0.25 * 2.0, -0.75 * 0.25 * 2.0], rtol=1e-6)
+
+
+def test_mlp_backward_data_matches_torch_autograd():
+    """One expert, float64: the data gradient equals torch's autograd of the
+    dense SwiGLU MLP (a library routine, independent of the oracle's formulas)."""
+    import torch
+    rng = np.random.default_rng(40)
+    m, H, F = 7, 12, 10
+    x = rng.standard_normal((m, H))
+    W1 = rng.standard_normal((H, 2 * F)) * 0.3
+    W2 = rng.standard_normal((F, H)) * 0.3
+    dy = rng.standard_normal((m, H))
+    got = O.grouped_mlp_backward_data(x, np.array([0, m]), [W1], [W2], dy, "f64")
+    xt = torch.tensor(x, requires_grad=True)
+    h = xt @ torch.tensor(W1)
+    y = (torch.nn.functional.silu(h[:, :F]) * h[:, F:]) @ torch.tensor(W2)
+    y.backward(torch.tensor(dy))
+    np.testing.assert_allclose(got, xt.grad.numpy(), rtol=1e-12, atol=1e-12)
+
+
+def test_mlp_backward_data_directional_derivative_and_groups():
+    """Several experts with an empty one: <d_x, v> equals the central
+    difference of <y(x), d_y> along v (the forward oracle in float64)."""
+    rng = np.random.default_rng(41)
+    H, F = 8, 6
+    counts = [3, 0, 5, 1]
+    off = np.concatenate([[0], np.cumsum(counts)])
+    N = int(off[-1])
+    W1 = [rng.standard_normal((H, 2 * F)) * 0.4 for _ in counts]
+    W2 = [rng.standard_normal((F, H)) * 0.4 for _ in counts]
+    x = rng.standard_normal((N, H))
+    dy = rng.standard_normal((N, H))
+    v = rng.standard_normal((N, H))
+    dx = O.grouped_mlp_backward_data(x, off, W1, W2, dy, "f64")
+    f = lambda xx: float((O.grouped_mlp(xx, off, W1, W2, "f64")[0] * dy).sum())
+    eps = 1e-6
+    np.testing.assert_allclose(float((dx * v).sum()), (f(x + eps * v) - f(x - eps * v)) / (2 * eps), rtol=1e-6)
+
+
+def test_swiglu_backward_closed_form():
+    """At g = 0: silu'(0) = 1/2 and silu(0) = 0, so d_g = d_a * u / 2, d_u = 0."""
+    h = np.array([[0.0, 0.0, 3.0, -2.0]])
+    d = O.swiglu_backward(h, np.array([[1.0, 4.0]]), 2)
+    np.testing.assert_allclose(d, [[1.5, -4.0, 0.0, 0.0]])
