@@ -347,12 +347,45 @@ def backward_stages(layer, cfg, N):
                                                               d_y, d_p))
     t_pb = graph_us(lambda: D.moe_permute_backward(d_y, layer.slot_to_row, d_x))
     t_rb = graph_us(lambda: D.moe_route_backward(layer.ids, d_p, d_z, layer.score, probs=layer.probs, E=cfg.E))
+    # data gradient of the grouped MLP (h recomputed, d_h, d_x): 3 GEMMs of 2 N H F flops each... GEMM1
+    # recompute 4 N H F, d_a 2 N H F, d_x 4 N H F: 10 N H F
+    F = cfg.F
+    w1 = torch.empty((cfg.E, H, 2 * F), dtype=torch.bfloat16, device="cuda")
+    w2 = torch.empty((cfg.E, F, H), dtype=torch.bfloat16, device="cuda")
+    w1t = torch.empty(D.moe_prepared_weight_bytes(cfg.E, H, F, D.BF16, 5), dtype=torch.uint8, device="cuda")
+    w2t = torch.empty(D.moe_prepared_weight_bytes(cfg.E, H, F, D.BF16, 6), dtype=torch.uint8, device="cuda")
+    for e in range(cfg.E):  # the layer's own experts, regenerated from their seeds
+        from workloads.gen import make_expert_weights
+        a1, a2 = make_expert_weights(cfg, e, device="cuda")
+        w1[e].copy_(a1)
+        w2[e].copy_(a2)
+    D.moe_prepare_weights_backward(w1, w2, w1t, w2t)
+    del w1, w2
+    ws = torch.empty(D.moe_grouped_mlp_backward_workspace_bytes(layer.capacity, F, D.BF16), dtype=torch.uint8,
+                     device="cuda")
+    d_xp = torch.empty_like(layer.x_perm)
+    bwd = lambda: D.moe_grouped_mlp_backward_data(layer.x_perm, layer.offsets, layer.w1p, w1t, w2t, d_y, d_xp, ws,
+                                                  H, F)
+    for _ in range(2):
+        bwd()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(3):
+        bwd()
+    e1.record()
+    torch.cuda.synchronize()
+    t_mb = e0.elapsed_time(e1) / 3 * 1000.0
+    del ws, w1t, w2t
     cb_bytes = T * H * 2 + 2 * N * H * 2 + T * K * 12
     pb_bytes = N * H * 2 + T * H * 2 + T * K * 4
     return {"combine_backward_us": round(t_cb, 2), "combine_backward_gbs": round(cb_bytes / (t_cb * 1e-6) / 1e9, 1),
             "permute_backward_us": round(t_pb, 2), "permute_backward_gbs": round(pb_bytes / (t_pb * 1e-6) / 1e9, 1),
             "route_backward_us": round(t_rb, 2),
-            "note": "GPU time per call from HIP-graph replays; GB/s = algorithmic bytes (combine backward: dout, "
+            "grouped_mlp_backward_data_us": round(t_mb, 1),
+            "grouped_mlp_backward_data_tflops": round(10.0 * N * H * F / (t_mb * 1e-6) / 1e12, 1),
+            "note": "GPU time per call from HIP-graph replays (the MLP data gradient: events around 3 eager "
+                    "calls; flops 10 N H F: h recomputed 4, d_a 2, d_x 4); GB/s = algorithmic bytes (combine backward: dout, "
                     "y_perm read, d_y_perm written, maps/probs/d_probs; permute backward: rows read, token rows "
                     "written, map) / time"}
 

@@ -10,6 +10,7 @@ from ._lib import (  # noqa: F401
     moe_grouped_mlp, moe_grouped_mlp_workspace_bytes, moe_mx_quantize, moe_permute, moe_permute_workspace_bytes,
     moe_prepare_router, moe_prepare_weights, moe_prepared_weight_bytes, moe_route_topk, moe_route_topk_grouped,
     moe_route_workspace_bytes, moe_router_prepared_bytes, moe_unpermute_combine,
-    moe_unpermute_combine_backward, moe_permute_backward, moe_route_backward,
+    moe_unpermute_combine_backward, moe_permute_backward, moe_route_backward, moe_prepare_weights_backward,
+    moe_grouped_mlp_backward_workspace_bytes, moe_grouped_mlp_backward_data,
 )
 from .layer import MoELayer  # noqa: F401

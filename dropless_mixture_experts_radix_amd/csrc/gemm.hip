@@ -63,6 +63,12 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 // EPI 0: out[row][col] = bf16(acc)                                   (N columns)
 // EPI 1: gate/up chunks of 32 columns are interleaved in B; out = k-blocked
 //        activations [N/64][capacity][32], a[row][j] = bf16(silu(gate) * up)
+// EPI 3: (backward) h = x_perm . W1 recomputed: A as EPI 1, out = k-blocked
+//        [N/32][capacity][32] in the prepared (gate/up interleaved) order
+// EPI 4: (backward) A = d_y row-major, B = the prepared W2^T panels (N = F
+//        columns): acc = d_a; with g, u read from `aux` (EPI 3's output) the
+//        epilogue stores d_h = [d_a u silu'(g), d_a silu(g)] k-blocked
+//        [2N/32][capacity][32] in natural column order (gates, then ups)
 // EPI 2: the router projection, one dense GEMM of the `capacity` = T token
 //        rows of x [T][Kd] with the prepared router weights [ceil(N/32)*32][Kd]
 //        (row-major, loaded like A), N = E output columns.  Every tile is cut
@@ -103,7 +109,7 @@ __device__ __forceinline__ SplitPlan gb_schedule(int L, int64_t capacity, int NT
 template <int EPI, int NI>
 __device__ __forceinline__ void store_tile(const f32x16 (&acc)[NI][2], int i0, const TileInfo& ti, int N,
                                            int64_t capacity, int wm, int wn, int g, int r32,
-                                           bf16_t* __restrict__ out) {
+                                           bf16_t* __restrict__ out, const bf16_t* __restrict__ aux) {
   const int col0 = ti.nt * GB_BN;
   // the lane's row and column offsets are made opaque here, so the compiler
   // cannot hoist the 16 row numbers per block out of the persistent loop into
@@ -124,6 +130,27 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[NI][2], int i0, c
           const int col = col0 + wn * 64 + j * 32 + r32;
           if (col < N) out[grow * N + col] = (bf16_t)f32_to_bf16(acc[ii][j][v]);
         }
+      } else if (EPI == 3) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int col = col0 + wn * 64 + j * 32 + r32;
+          if (col < N) out[((long)(col >> 5) * capacity + grow) * GB_BK + (col & 31)] = (bf16_t)f32_to_bf16(acc[ii][j][v]);
+        }
+      } else if (EPI == 4) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int f = col0 + wn * 64 + j * 32 + r32;  // column of d_a
+          if (f < N) {
+            const int pg = (f >> 5) * 64 + (f & 31);    // gate's prepared column; up's is pg + 32
+            const float gt = bf16_to_f32(aux[((long)(pg >> 5) * capacity + grow) * GB_BK + (f & 31)]);
+            const float up = bf16_to_f32(aux[((long)((pg >> 5) + 1) * capacity + grow) * GB_BK + (f & 31)]);
+            const float da = acc[ii][j][v];
+            const float sg = 1.0f / (1.0f + expf(-gt));
+            out[((long)(f >> 5) * capacity + grow) * GB_BK + (f & 31)] =
+                (bf16_t)f32_to_bf16(da * up * sg * (1.0f + gt * (1.0f - sg)));
+            out[((long)((N + f) >> 5) * capacity + grow) * GB_BK + (f & 31)] = (bf16_t)f32_to_bf16(da * gt * sg);
+          }
+        }
       } else {
         const int jcol = (col0 >> 1) + wn * 32 + r32;
         if (jcol < (N >> 1))
@@ -139,7 +166,8 @@ __global__ __launch_bounds__(GB_THREADS, 1) void k_gemm_bf16(int L, int N, int K
                                                              const bf16_t* __restrict__ A,
                                                              const int32_t* __restrict__ offsets,
                                                              const bf16_t* __restrict__ B, bf16_t* __restrict__ out,
-                                                             float* __restrict__ part) {
+                                                             float* __restrict__ part,
+                                                             const bf16_t* __restrict__ aux) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   int32_t* s_pre = (int32_t*)(smem + 4 * GB_STAGE_BYTES);  // [L+1]
   int32_t* s_tmp = s_pre + (L + 1);                         // [8]
@@ -393,8 +421,9 @@ __global__ __launch_bounds__(GB_THREADS, 1) void k_gemm_bf16(int L, int N, int K
           }
         }
     } else if (done.piece < 0) {
-      store_tile<EPI, 4>(acc, 0, done.ti, N, capacity, wm, wn, g, r32, out);
-      if (done.ti.rows > GB_BM && wm == 0) store_tile<EPI, 1>(accx, 8, done.ti, N, capacity, 0, wn, g, r32, out);
+      store_tile<EPI, 4>(acc, 0, done.ti, N, capacity, wm, wn, g, r32, out, aux);
+      if (done.ti.rows > GB_BM && wm == 0)
+        store_tile<EPI, 1>(accx, 8, done.ti, N, capacity, 0, wn, g, r32, out, aux);
     } else {
       // partial tile, per wavefront [i][j][lane][16 values of the MFMA D layout]
       float* dst = part + (long)done.piece * GB_PART_FLOATS + wv * 8192 + l * 16;
@@ -435,7 +464,8 @@ __global__ __launch_bounds__(GB_THREADS, 1) void k_gemm_bf16(int L, int N, int K
 template <int EPI>
 __global__ __launch_bounds__(320) void k_splitk_reduce(int L, int N, int Kd, int64_t capacity, int G,
                                                        const int32_t* __restrict__ offsets,
-                                                       const float* __restrict__ part, bf16_t* __restrict__ out) {
+                                                       const float* __restrict__ part, bf16_t* __restrict__ out,
+                                                       const bf16_t* __restrict__ aux) {
   __shared__ int32_t s_pre[MOE_MAX_L + 1];
   __shared__ int32_t s_tmp[16];
   const int NT = (N + GB_BN - 1) / GB_BN;
@@ -449,11 +479,11 @@ __global__ __launch_bounds__(320) void k_splitk_reduce(int L, int N, int Kd, int
   if (i < 4) {
     if (ti.rows <= (wv >> 2) * 128 + i * 32) return;  // row block past the tile's rows
     sum_partials(src + wv * 8192 + i * 2048, plan.S, acc, GB_PART_FLOATS);
-    store_tile<EPI, 1>(acc, i, ti, N, capacity, wv >> 2, wv & 3, l >> 5, l & 31, out);
+    store_tile<EPI, 1>(acc, i, ti, N, capacity, wv >> 2, wv & 3, l >> 5, l & 31, out, aux);
   } else {
     if (wv >= 4 || ti.rows <= GB_BM) return;
     sum_partials(src + GB_PART_X + wv * 2048, plan.S, acc, GB_PART_FLOATS);
-    store_tile<EPI, 1>(acc, 8, ti, N, capacity, 0, wv, l >> 5, l & 31, out);
+    store_tile<EPI, 1>(acc, 8, ti, N, capacity, 0, wv, l >> 5, l & 31, out, aux);
   }
 }
 
@@ -585,7 +615,7 @@ hipError_t launch_router_gemm_bf16(int T, int E, int H, int S, const bf16_t* x, 
   const long units = (long)((T + GB_BM - 1) / GB_BM) * ((E + GB_BN - 1) / GB_BN) * S;
   const int G = (int)(units < num_cus() ? units : num_cus());
   hipLaunchKernelGGL(k_gemm_bf16<2>, dim3(G), dim3(GB_THREADS), gemm_bf16_lds(S), s, S, E, H, (int64_t)T, x,
-                     (const int32_t*)nullptr, wp, (bf16_t*)nullptr, partial);
+                     (const int32_t*)nullptr, wp, (bf16_t*)nullptr, partial, (const bf16_t*)nullptr);
   return hipGetLastError();
 }
 
@@ -604,10 +634,44 @@ hipError_t launch_grouped_mlp_bf16(int L, int H, int F, int64_t capacity, const 
   const int G1 = grid_for(capacity, L, GB_BM, (N1 + GB_BN - 1) / GB_BN, 1);
   const int G2 = grid_for(capacity, L, GB_BM, (N2 + GB_BN - 1) / GB_BN, 1);
   const dim3 rgrid(GEMM_SPLIT_UNITS / 2 * 8), rblk(320), blk(GB_THREADS);
-  hipLaunchKernelGGL(k_gemm_bf16<1>, dim3(G1), blk, lds, s, L, N1, H, capacity, x, offsets, w1p, act, part);
-  hipLaunchKernelGGL(k_splitk_reduce<1>, rgrid, rblk, 0, s, L, N1, H, capacity, G1, offsets, part, act);
-  hipLaunchKernelGGL(k_gemm_bf16<0>, dim3(G2), blk, lds, s, L, N2, F, capacity, act, offsets, w2p, y, part);
-  hipLaunchKernelGGL(k_splitk_reduce<0>, rgrid, rblk, 0, s, L, N2, F, capacity, G2, offsets, part, y);
+  hipLaunchKernelGGL(k_gemm_bf16<1>, dim3(G1), blk, lds, s, L, N1, H, capacity, x, offsets, w1p, act, part, (const bf16_t*)nullptr);
+  hipLaunchKernelGGL(k_splitk_reduce<1>, rgrid, rblk, 0, s, L, N1, H, capacity, G1, offsets, part, act, (const bf16_t*)nullptr);
+  hipLaunchKernelGGL(k_gemm_bf16<0>, dim3(G2), blk, lds, s, L, N2, F, capacity, act, offsets, w2p, y, part, (const bf16_t*)nullptr);
+  hipLaunchKernelGGL(k_splitk_reduce<0>, rgrid, rblk, 0, s, L, N2, F, capacity, G2, offsets, part, y, (const bf16_t*)nullptr);
+  return hipGetLastError();
+}
+
+// Data gradient of the grouped SwiGLU MLP (bf16): h = x . W1 recomputed into
+// hbuf (EPI 3), d_h = swiglu'(h, d_y . W2^T) into dhbuf (EPI 4, W2^T panels
+// w2t), d_x = d_h . W1^T (EPI 0 on the W1^T panels w1t), each GEMM followed
+// by its split-K reduce.
+hipError_t launch_grouped_mlp_bf16_backward(int L, int H, int F, int64_t capacity, const bf16_t* x,
+                                            const int32_t* offsets, const bf16_t* w1p, const bf16_t* w1t,
+                                            const bf16_t* w2t, const bf16_t* dy, bf16_t* hbuf, bf16_t* dhbuf,
+                                            float* part, bf16_t* dx, hipStream_t s) {
+  if (capacity == 0) return hipSuccess;
+  const size_t lds = gemm_bf16_lds(L);
+  static bool attr_done = false;
+  if (!attr_done) {
+    (void)hipFuncSetAttribute((const void*)k_gemm_bf16<0>, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    (void)hipFuncSetAttribute((const void*)k_gemm_bf16<3>, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    (void)hipFuncSetAttribute((const void*)k_gemm_bf16<4>, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    attr_done = true;
+  }
+  const bf16_t* nul = nullptr;
+  const int G3 = grid_for(capacity, L, GB_BM, (2 * F + GB_BN - 1) / GB_BN, 1);
+  const int G4 = grid_for(capacity, L, GB_BM, (F + GB_BN - 1) / GB_BN, 1);
+  const int G0 = grid_for(capacity, L, GB_BM, (H + GB_BN - 1) / GB_BN, 1);
+  const dim3 rgrid(GEMM_SPLIT_UNITS / 2 * 8), rblk(320), blk(GB_THREADS);
+  hipLaunchKernelGGL(k_gemm_bf16<3>, dim3(G3), blk, lds, s, L, 2 * F, H, capacity, x, offsets, w1p, hbuf, part, nul);
+  hipLaunchKernelGGL(k_splitk_reduce<3>, rgrid, rblk, 0, s, L, 2 * F, H, capacity, G3, offsets, part, hbuf, nul);
+  hipLaunchKernelGGL(k_gemm_bf16<4>, dim3(G4), blk, lds, s, L, F, H, capacity, dy, offsets, w2t, dhbuf, part,
+                     (const bf16_t*)hbuf);
+  hipLaunchKernelGGL(k_splitk_reduce<4>, rgrid, rblk, 0, s, L, F, H, capacity, G4, offsets, part, dhbuf,
+                     (const bf16_t*)hbuf);
+  hipLaunchKernelGGL(k_gemm_bf16<0>, dim3(G0), blk, lds, s, L, H, 2 * F, capacity, dhbuf, offsets, w1t, dx, part,
+                     nul);
+  hipLaunchKernelGGL(k_splitk_reduce<0>, rgrid, rblk, 0, s, L, H, 2 * F, capacity, G0, offsets, part, dx, nul);
   return hipGetLastError();
 }
 

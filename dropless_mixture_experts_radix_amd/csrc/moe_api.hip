@@ -192,6 +192,9 @@ size_t moe_prepared_weight_bytes(int L, int H, int F, int dtype, int which) {
     // MX scales: 16 bytes per prepared row and 512-wide k group
     case 3: return mx ? n1 / H * (((size_t)H + 511) / 512) * 16 : 0;
     case 4: return mx ? n2 / F * (((size_t)F + 511) / 512) * 16 : 0;
+    // the backward's bf16 panels: W1^T (ceil(H/256) panels over 2F), W2^T (ceil(F/256) panels over H)
+    case 5: return dtype == MOE_BF16 ? (size_t)L * (((size_t)H + 255) / 256 * 256) * 2 * F * 2 : 0;
+    case 6: return dtype == MOE_BF16 ? (size_t)L * (((size_t)F + 255) / 256 * 256) * H * 2 : 0;
     default: return 0;
   }
 }
@@ -287,6 +290,50 @@ int moe_unpermute_combine(int T, int K, int H, int dtype, const void* y_perm, co
   if (T > 0 && (!slot_to_row || !probs || !out)) return MOE_ERR_NULL;
   if (!aligned16(y_perm) || !aligned16(out)) return MOE_ERR_ALIGN;
   return launch_status(launch_combine(T, K, H, dtype, y_perm, slot_to_row, probs, out, (hipStream_t)stream));
+}
+
+// ---------------------------------------------------------------------------
+// Data gradient of the grouped MLP
+// ---------------------------------------------------------------------------
+int moe_prepare_weights_backward(int L, int H, int F, int dtype, const void* w1, const void* w2, void* w1t,
+                                 void* w2t, void* stream) {
+  if (L < 1 || L > MOE_MAX_L || H <= 0 || F <= 0 || H % 128 || F % 128) return MOE_ERR_SHAPE;
+  if (dtype != MOE_BF16) return MOE_ERR_DTYPE;
+  if (!w1 || !w2 || !w1t || !w2t) return MOE_ERR_NULL;
+  if (!aligned16(w1) || !aligned16(w2) || !aligned16(w1t) || !aligned16(w2t)) return MOE_ERR_ALIGN;
+  return launch_status(launch_prepare_weights_backward(L, H, F, w1, w2, w1t, w2t, (hipStream_t)stream));
+}
+
+size_t moe_grouped_mlp_backward_workspace_bytes(int64_t capacity, int F, int dtype) {
+  if (capacity <= 0 || F <= 0 || dtype != MOE_BF16) return 256;
+  // h and d_h ([2F/32][capacity][32] bf16 each), then the split-K partials
+  return round_up(2 * round_up((size_t)capacity * 2 * F * 2, 256) + grouped_mlp_bf16_part_bytes(), 256);
+}
+
+int moe_grouped_mlp_backward_data(int L, int H, int F, int64_t capacity, int dtype, const void* x_perm,
+                                  const int32_t* offsets, const void* w1p, const void* w1t, const void* w2t,
+                                  const void* d_y_perm, void* d_x_perm, void* workspace, size_t workspace_bytes,
+                                  void* stream) {
+  if (L < 1 || L > MOE_MAX_L || H <= 0 || F <= 0 || capacity < 0 || capacity > (int64_t)1 << 31)
+    return MOE_ERR_SHAPE;
+  if (dtype != MOE_BF16) return MOE_ERR_DTYPE;
+  if (H % 128 || F % 128) return MOE_ERR_SHAPE;
+  // byte offsets of the k-blocked h / d_h buffers and of the rows stay within 31 bits
+  if (capacity * (int64_t)(H > 2 * F ? H : 2 * F) * 2 > (int64_t)INT32_MAX) return MOE_ERR_SHAPE;
+  if (!offsets || !w1p || !w1t || !w2t) return MOE_ERR_NULL;
+  if (capacity > 0 && (!x_perm || !d_y_perm || !d_x_perm || !workspace)) return MOE_ERR_NULL;
+  if (!aligned16(x_perm) || !aligned16(w1p) || !aligned16(w1t) || !aligned16(w2t) || !aligned16(d_y_perm) ||
+      !aligned16(d_x_perm) || !aligned16(workspace))
+    return MOE_ERR_ALIGN;
+  if (capacity > 0 && workspace_bytes < moe_grouped_mlp_backward_workspace_bytes(capacity, F, dtype))
+    return MOE_ERR_WORKSPACE;
+  bf16_t* hbuf = (bf16_t*)workspace;
+  bf16_t* dhbuf = (bf16_t*)((uint8_t*)workspace + round_up((size_t)capacity * 2 * F * 2, 256));
+  float* part = (float*)((uint8_t*)workspace + 2 * round_up((size_t)capacity * 2 * F * 2, 256));
+  return launch_status(launch_grouped_mlp_bf16_backward(L, H, F, capacity, (const bf16_t*)x_perm, offsets,
+                                                        (const bf16_t*)w1p, (const bf16_t*)w1t, (const bf16_t*)w2t,
+                                                        (const bf16_t*)d_y_perm, hbuf, dhbuf, part,
+                                                        (bf16_t*)d_x_perm, (hipStream_t)stream));
 }
 
 // ---------------------------------------------------------------------------

@@ -211,6 +211,12 @@ size_t grouped_mlp_bf16_part_bytes();
 hipError_t launch_grouped_mlp_bf16(int L, int H, int F, int64_t capacity, const bf16_t* x,
                                    const int32_t* offsets, const bf16_t* w1p, const bf16_t* w2p,
                                    bf16_t* act, float* part, bf16_t* y, hipStream_t s);
+hipError_t launch_grouped_mlp_bf16_backward(int L, int H, int F, int64_t capacity, const bf16_t* x,
+                                            const int32_t* offsets, const bf16_t* w1p, const bf16_t* w1t,
+                                            const bf16_t* w2t, const bf16_t* dy, bf16_t* hbuf, bf16_t* dhbuf,
+                                            float* part, bf16_t* dx, hipStream_t s);
+hipError_t launch_prepare_weights_backward(int L, int H, int F, const void* w1, const void* w2, void* w1t,
+                                           void* w2t, hipStream_t s);
 size_t grouped_mlp_mx_part_bytes();
 hipError_t launch_grouped_mlp_mx(int L, int H, int F, int64_t capacity, bool fp4, const uint8_t* x,
                                  const uint8_t* xs, const int32_t* offsets, const uint8_t* w1p,

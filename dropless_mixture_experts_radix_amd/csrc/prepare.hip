@@ -25,7 +25,9 @@ namespace moe {
 // MODE 3: bf16 -> MXFP4: E2M1 codes two per byte (element 2i in the low
 //         nibble) in k-blocked panels of [256 rows][128 k = 64 bytes] per
 //         128-wide k step, scales as in MODE 2.
-template <int MODE>
+// TRANS: the input is stored transposed, [Ncols][Kd] (the backward's W2^T and
+// W1^T panels are made from W2 [F][H] and W1 [H][2F] as they are).
+template <int MODE, bool TRANS = false>
 __global__ __launch_bounds__(256) void k_prepare(int Kd, int Ncols, int F_interleave,
                                                  const void* __restrict__ w, void* __restrict__ wp,
                                                  uint8_t* __restrict__ ws) {
@@ -38,10 +40,10 @@ __global__ __launch_bounds__(256) void k_prepare(int Kd, int Ncols, int F_interl
   const long in_off = (long)e * Kd * Ncols;
   const int tid = threadIdx.x;
   for (int i = tid; i < 1024; i += 256) {
-    const int kk = i >> 5, cc = i & 31;
+    const int kk = TRANS ? (i & 31) : (i >> 5), cc = TRANS ? (i >> 5) : (i & 31);
     uint32_t v = 0;
     if (live) {
-      const long src = in_off + (long)(k0 + kk) * Ncols + cbase + cc;
+      const long src = TRANS ? in_off + (long)(cbase + cc) * Kd + k0 + kk : in_off + (long)(k0 + kk) * Ncols + cbase + cc;
       v = MODE == 0 ? __float_as_uint(((const float*)w)[src]) : ((const bf16_t*)w)[src];
     }
     tile[cc][kk] = v;
@@ -116,6 +118,20 @@ hipError_t launch_prepare_weights(int L, int H, int F, int dtype, const void* w1
     hipLaunchKernelGGL(k_prepare<3>, dim3((2 * F + 255) / 256 * 8, H / 32, L), b, 0, s, H, 2 * F, F, w1, w1p, w1s);
     hipLaunchKernelGGL(k_prepare<3>, dim3((H + 255) / 256 * 8, F / 32, L), b, 0, s, F, H, 0, w2, w2p, w2s);
   }
+  return hipGetLastError();
+}
+
+// The backward's bf16 panels: W2^T (columns f of F, k = h of H) from W2
+// [F][H], and W1^T (columns h of H, k = j of 2F in natural order) from W1
+// [H][2F]; layout as MODE 1.
+hipError_t launch_prepare_weights_backward(int L, int H, int F, const void* w1, const void* w2, void* w1t,
+                                           void* w2t, hipStream_t s) {
+  if (L == 0) return hipSuccess;
+  const dim3 b(256);
+  hipLaunchKernelGGL((k_prepare<1, true>), dim3((F + 255) / 256 * 8, H / 32, L), b, 0, s, H, F, 0, w2, w2t,
+                     (uint8_t*)nullptr);
+  hipLaunchKernelGGL((k_prepare<1, true>), dim3((H + 255) / 256 * 8, 2 * F / 32, L), b, 0, s, 2 * F, H, 0, w1, w1t,
+                     (uint8_t*)nullptr);
   return hipGetLastError();
 }
 

@@ -13,7 +13,8 @@
  *   moe_grouped_mlp        ragged grouped SwiGLU MLP (fp32, bf16, MXFP8 or MXFP4)
  *   moe_unpermute_combine  probability-weighted sum back in token order
  *
- * and the backward of the routing steps (combine, permute, route gates),
+ * and the backward of the routing steps (combine, permute, route gates) and
+ * the data gradient of the grouped MLP,
  * plus one-time weight preparation and a standalone MX quantizer.
  *
  * Conventions shared by every call
@@ -241,7 +242,8 @@ int moe_permute(int T, int H, int K, int E_global, int e0, int L, int64_t capaci
  *   F % 512 == 0.
  * Requires H % 32 == 0 and F % 32 == 0 (MOE_F32).  Byte sizes:
  * moe_prepared_weight_bytes(L, H, F, dtype, which) with which = 1 (W1p),
- * 2 (W2p), 3 (W1p scales), 4 (W2p scales).
+ * 2 (W2p), 3 (W1p scales), 4 (W2p scales), and for the backward's bf16
+ * panels (moe_prepare_weights_backward) 5 (W1t), 6 (W2t).
  * ------------------------------------------------------------------------ */
 size_t moe_prepared_weight_bytes(int L, int H, int F, int dtype, int which);
 
@@ -301,6 +303,38 @@ int moe_grouped_mlp(int L, int H, int F, int64_t capacity, int dtype,
 int moe_unpermute_combine(int T, int K, int H, int dtype,
                           const void* y_perm, const int32_t* slot_to_row, const float* probs,
                           void* out, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Data gradient of the grouped SwiGLU MLP (bf16), the first part of the
+ * grouped-GEMM backward (the pages' expert MLP is two grouped GEMMs on
+ * variable-length groups, bpdata article, "Optimization 1: Grouped GEMM"; its
+ * backward is the chain rule through them and SwiGLU).  For the rows of each
+ * expert e: h = x_perm . W1[e] is recomputed and stored as bf16; d_a =
+ * d_y_perm . W2[e]^T (fp32, not stored); d_h = [d_a * u * silu'(g),
+ * d_a * silu(g)] with g = h[:, :F], u = h[:, F:], silu'(g) = sigma(g)
+ * (1 + g (1 - sigma(g))), stored as bf16; d_x_perm = d_h . W1[e]^T (bf16).
+ * All three are ragged grouped GEMMs on the device-built tile schedule.
+ *
+ * moe_prepare_weights_backward: from the logical W1 [L][H][2F] and W2
+ *   [L][F][H] (bf16, as for moe_prepare_weights) lays out the W1^T panels
+ *   (w1t: columns h of H, k = j of 2F in natural order, gate columns then up
+ *   columns) and the W2^T panels (w2t: columns f of F, k = h of H), both
+ *   bf16 [L][panel][k/32][256 rows][32 k], zero-padded to whole 256-row
+ *   panels; sizes moe_prepared_weight_bytes(..., 5) and (..., 6).
+ * moe_grouped_mlp_backward_data: x_perm, d_y_perm, d_x_perm [capacity][H]
+ *   bf16 device; offsets as moe_grouped_mlp; w1p = moe_prepare_weights' W1p
+ *   (bf16); rows >= offsets[L] of d_x_perm are not written.  Workspace:
+ *   moe_grouped_mlp_backward_workspace_bytes(capacity, F, MOE_BF16) bytes
+ *   (h, d_h, split-K partials).  dtype MOE_BF16 only; H % 128 == 0,
+ *   F % 128 == 0, capacity * max(H, 2F) * 2 < 2^31.
+ * ------------------------------------------------------------------------ */
+int moe_prepare_weights_backward(int L, int H, int F, int dtype, const void* w1, const void* w2, void* w1t,
+                                 void* w2t, void* stream);
+size_t moe_grouped_mlp_backward_workspace_bytes(int64_t capacity, int F, int dtype);
+int moe_grouped_mlp_backward_data(int L, int H, int F, int64_t capacity, int dtype, const void* x_perm,
+                                  const int32_t* offsets, const void* w1p, const void* w1t, const void* w2t,
+                                  const void* d_y_perm, void* d_x_perm, void* workspace, size_t workspace_bytes,
+                                  void* stream);
 
 /* ------------------------------------------------------------------------
  * Backward of the routing steps (the pages' router work covered forward and

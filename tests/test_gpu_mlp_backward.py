@@ -1,0 +1,77 @@
+"""GPU parity of the grouped MLP's data gradient (moe_grouped_mlp_backward_data,
+bf16): d_x_perm against the oracle's chain rule with the same rounding points
+(h and d_h stored as bf16), within the bf16 tolerance; the backward's W1^T and
+W2^T panels exactly; rows past N untouched."""
+import numpy as np
+import pytest
+import torch
+
+import dropless_mixture_experts_radix_amd as D
+from oracle import moe_oracle as O
+from tests.gpu_util import DEV, TOL, bf16_from_f64, rel_inf, say, to_f64
+from tests.test_gpu_mlp import MIXTRAL_COUNTS, _unblock, _weights
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(counts, H, F, seed, sample=None):
+    rng = np.random.default_rng(seed)
+    L = len(counts)
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    N = int(offsets[-1])
+    cap = N + 24
+    W1, W2 = _weights(rng, L, H, F, "bf16")
+    x = O.bf16_round(rng.standard_normal((cap, H)))
+    dy = O.bf16_round(rng.standard_normal((cap, H)))
+    w1 = torch.stack([bf16_from_f64(w) for w in W1])
+    w2 = torch.stack([bf16_from_f64(w) for w in W2])
+    w1p = torch.empty(D.moe_prepared_weight_bytes(L, H, F, D.BF16, 1), dtype=torch.uint8, device=DEV)
+    w2p = torch.empty(D.moe_prepared_weight_bytes(L, H, F, D.BF16, 2), dtype=torch.uint8, device=DEV)
+    w1t = torch.empty(D.moe_prepared_weight_bytes(L, H, F, D.BF16, 5), dtype=torch.uint8, device=DEV)
+    w2t = torch.empty(D.moe_prepared_weight_bytes(L, H, F, D.BF16, 6), dtype=torch.uint8, device=DEV)
+    D.moe_prepare_weights(w1, w2, D.BF16, w1p.view(torch.bfloat16), w2p.view(torch.bfloat16))
+    D.moe_prepare_weights_backward(w1, w2, w1t, w2t)
+    ws = torch.empty(D.moe_grouped_mlp_backward_workspace_bytes(cap, F, D.BF16), dtype=torch.uint8, device=DEV)
+    dx = torch.full((cap, H), 5.0, dtype=torch.bfloat16, device=DEV)
+    say("mlp backward data L", L, "H", H, "F", F, "N", N)
+    D.moe_grouped_mlp_backward_data(bf16_from_f64(x), torch.from_numpy(offsets).to(DEV), w1p, w1t, w2t,
+                                    bf16_from_f64(dy), dx, ws, H, F)
+    torch.cuda.synchronize()
+    # the backward panels of the last expert, decoded
+    e = L - 1
+    pw1 = ((H + 255) // 256) * 256
+    pw2 = ((F + 255) // 256) * 256
+    t1 = _unblock(w1t.view(torch.bfloat16).view(L, pw1, 2 * F)[e])
+    t2 = _unblock(w2t.view(torch.bfloat16).view(L, pw2, H)[e])
+    np.testing.assert_array_equal(t1[:H], W1[e])            # row h of W1^T panels = W1[e][h, :]
+    np.testing.assert_array_equal(t2[:F], W2[e])            # row f of W2^T panels = W2[e][f, :]
+    assert (t1[H:] == 0).all() and (t2[F:] == 0).all()
+    got = to_f64(dx)
+    assert (got[N:] == 5.0).all()
+    if N == 0:
+        return
+    # the oracle on all rows, or on a sample of rows per expert (rows are independent)
+    rows = np.arange(N) if sample is None else np.concatenate(
+        [np.arange(offsets[k], offsets[k + 1])[:sample] for k in range(L)])
+    sub_counts = [int(((rows >= offsets[k]) & (rows < offsets[k + 1])).sum()) for k in range(L)]
+    sub_off = np.concatenate([[0], np.cumsum(sub_counts)])
+    want = O.grouped_mlp_backward_data(x[rows], sub_off, W1, W2, dy[rows], "bf16")
+    err = rel_inf(got[rows], want)
+    say("  d_x rel err", err)
+    assert err <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("counts,H,F", [
+    ([0, 1, 255, 256, 257, 600, 0, 31], 256, 256),   # empty experts, ragged and tall tiles
+    ([70, 300, 0, 5], 384, 128),                      # partial column tiles in all three GEMMs
+    ([0, 0, 0], 128, 128),                            # no rows
+    (MIXTRAL_COUNTS, 512, 512),                       # split-K pieces with tall tiles
+])
+def test_grouped_mlp_backward_data(counts, H, F):
+    _run(counts, H, F, seed=sum(counts) + H + F)
+
+
+def test_grouped_mlp_backward_data_mixtral_size():
+    """The Mixtral-like shape (H = 4096, F = 14336, 8192 rows), checked on 48
+    rows per expert."""
+    _run(MIXTRAL_COUNTS, 4096, 14336, seed=7, sample=48)
