@@ -36,6 +36,7 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-mx", action="store_true", help="skip the MXFP8 variant")
     ap.add_argument("--no-other", action="store_true", help="skip the other full-size workloads")
+    ap.add_argument("--no-backward", action="store_true", help="skip the backward kernels")
     ap.add_argument("--workload", choices=["dsv3_bf16", "sparse_share", "mixtral_mxfp8", "mixtral_mxfp4"],
                     default=None,
                     help="time only this other workload (its layer and grouped MLP) and print its line")
@@ -449,10 +450,11 @@ def main():
                      "frac": round(tflops / BF16_PEAK_TFLOPS, 4), "traffic": measured_traffic(),
                      "traffic_unit": "HBM bytes per launch", "algorithmic_flops_per_launch": flops},
     }
-    try:
-        line["backward"] = backward_stages(layer, cfg, N)
-    except Exception as ex:  # report, do not hide the main line
-        line["backward"] = {"error": repr(ex)}
+    if not a.no_backward:
+        try:
+            line["backward"] = backward_stages(layer, cfg, N)
+        except Exception as ex:  # report, do not hide the main line
+            line["backward"] = {"error": repr(ex)}
     if not a.no_mx:
         try:
             del layer
