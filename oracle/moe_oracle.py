@@ -35,6 +35,8 @@ is computed here by plain definitions:
                         the adjoint sums and the derivative of the scores)
   grouped_mlp_backward_data   the data gradient of the grouped MLP (chain rule
                         through both GEMMs and SwiGLU, h recomputed)
+  grouped_mlp_backward_weights the weight gradient (per-expert contractions
+                        over the expert's own rows)
 
 Every function is parity-pinned by tests/test_oracle_*.py (pages' worked sizes,
 closed forms, brute force, a second algorithm, library reductions); the whole
@@ -687,6 +689,32 @@ def grouped_mlp_backward_data(x_perm, offsets, W1, W2, d_y, dtype):
         d_h = rnd(swiglu_backward(h, d_a, F))
         out[lo:hi] = rnd(d_h @ W1e.T)
     return out
+
+
+def grouped_mlp_backward_weights(x_perm, offsets, W1, W2, d_y, dtype):
+    """Weight gradient of the grouped SwiGLU MLP: for each expert's rows X,
+    dW1[e] = X^T d_h and dW2[e] = a^T d_y (contractions over the expert's own
+    rows), with h = X W1[e] recomputed, a = silu(g) u, d_a = d_y W2[e]^T and
+    d_h = swiglu'(h, d_a).  Rounding points of the bf16 path: h, a and d_h
+    are bf16; the gradients are fp32.  "f64" rounds nothing.  Empty experts
+    get zero gradients.  Returns (dW1 [L][H][2F], dW2 [L][F][H])."""
+    x_perm = np.asarray(x_perm, np.float64)
+    d_y = np.asarray(d_y, np.float64)
+    rnd = (lambda v: v) if dtype == "f64" else bf16_round
+    out = (lambda v: v) if dtype == "f64" else (lambda v: v.astype(np.float32).astype(np.float64))
+    dW1, dW2 = [], []
+    for e in range(len(offsets) - 1):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        W1e = np.asarray(W1[e], np.float64)
+        W2e = np.asarray(W2[e], np.float64)
+        F = W2e.shape[0]
+        X, dY = x_perm[lo:hi], d_y[lo:hi]
+        h = rnd(X @ W1e)
+        a = rnd(swiglu(h, F))
+        d_h = rnd(swiglu_backward(h, dY @ W2e.T, F))
+        dW1.append(out(X.T @ d_h))
+        dW2.append(out(a.T @ dY))
+    return np.stack(dW1), np.stack(dW2)
 
 
 # ---------------------------------------------------------------------------

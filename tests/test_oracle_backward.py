@@ -194,3 +194,29 @@ def test_swiglu_backward_closed_form():
     h = np.array([[0.0, 0.0, 3.0, -2.0]])
     d = O.swiglu_backward(h, np.array([[1.0, 4.0]]), 2)
     np.testing.assert_allclose(d, [[1.5, -4.0, 0.0, 0.0]])
+
+
+def test_mlp_backward_weights_matches_torch_autograd():
+    """Two experts and an empty one, float64: the weight gradients equal
+    torch's autograd of each expert's dense SwiGLU MLP; the empty expert's
+    are zero."""
+    import torch
+    rng = np.random.default_rng(42)
+    H, F = 10, 6
+    counts = [4, 0, 7]
+    off = np.concatenate([[0], np.cumsum(counts)])
+    W1 = [rng.standard_normal((H, 2 * F)) * 0.3 for _ in counts]
+    W2 = [rng.standard_normal((F, H)) * 0.3 for _ in counts]
+    x = rng.standard_normal((off[-1], H))
+    dy = rng.standard_normal((off[-1], H))
+    dW1, dW2 = O.grouped_mlp_backward_weights(x, off, W1, W2, dy, "f64")
+    assert (dW1[1] == 0).all() and (dW2[1] == 0).all()
+    for e in (0, 2):
+        lo, hi = off[e], off[e + 1]
+        w1 = torch.tensor(W1[e], requires_grad=True)
+        w2 = torch.tensor(W2[e], requires_grad=True)
+        h = torch.tensor(x[lo:hi]) @ w1
+        y = (torch.nn.functional.silu(h[:, :F]) * h[:, F:]) @ w2
+        y.backward(torch.tensor(dy[lo:hi]))
+        np.testing.assert_allclose(dW1[e], w1.grad.numpy(), rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(dW2[e], w2.grad.numpy(), rtol=1e-12, atol=1e-12)
