@@ -377,7 +377,22 @@ def backward_stages(layer, cfg, N):
     e1.record()
     torch.cuda.synchronize()
     t_mb = e0.elapsed_time(e1) / 3 * 1000.0
-    del ws, w1t, w2t
+    # weight gradient (after the data gradient, from the h and d_h it left in ws): 6 N H F flops
+    wws = torch.empty(D.moe_grouped_mlp_backward_weights_workspace_bytes(cfg.E, layer.capacity, H, F, D.BF16),
+                      dtype=torch.uint8, device="cuda")
+    dW1 = torch.empty((cfg.E, H, 2 * F), dtype=torch.float32, device="cuda")
+    dW2 = torch.empty((cfg.E, F, H), dtype=torch.float32, device="cuda")
+    wg = lambda: D.moe_grouped_mlp_backward_weights(layer.x_perm, layer.offsets, d_y, ws, dW1, dW2, wws, H, F)
+    for _ in range(2):
+        wg()
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(3):
+        wg()
+    e1.record()
+    torch.cuda.synchronize()
+    t_wg = e0.elapsed_time(e1) / 3 * 1000.0
+    del ws, w1t, w2t, wws, dW1, dW2
     cb_bytes = T * H * 2 + 2 * N * H * 2 + T * K * 12
     pb_bytes = N * H * 2 + T * H * 2 + T * K * 4
     return {"combine_backward_us": round(t_cb, 2), "combine_backward_gbs": round(cb_bytes / (t_cb * 1e-6) / 1e9, 1),
@@ -385,8 +400,11 @@ def backward_stages(layer, cfg, N):
             "route_backward_us": round(t_rb, 2),
             "grouped_mlp_backward_data_us": round(t_mb, 1),
             "grouped_mlp_backward_data_tflops": round(10.0 * N * H * F / (t_mb * 1e-6) / 1e12, 1),
+            "grouped_mlp_backward_weights_us": round(t_wg, 1),
+            "grouped_mlp_backward_weights_tflops": round(6.0 * N * H * F / (t_wg * 1e-6) / 1e12, 1),
             "note": "GPU time per call from HIP-graph replays (the MLP data gradient: events around 3 eager "
-                    "calls; flops 10 N H F: h recomputed 4, d_a 2, d_x 4); GB/s = algorithmic bytes (combine backward: dout, "
+                    "calls; flops 10 N H F: h recomputed 4, d_a 2, d_x 4; the weight gradient likewise, 6 N H F, "
+                    "its operand regrouping included); GB/s = algorithmic bytes (combine backward: dout, "
                     "y_perm read, d_y_perm written, maps/probs/d_probs; permute backward: rows read, token rows "
                     "written, map) / time"}
 

@@ -12,5 +12,6 @@ from ._lib import (  # noqa: F401
     moe_route_workspace_bytes, moe_router_prepared_bytes, moe_unpermute_combine,
     moe_unpermute_combine_backward, moe_permute_backward, moe_route_backward, moe_prepare_weights_backward,
     moe_grouped_mlp_backward_workspace_bytes, moe_grouped_mlp_backward_data,
+    moe_grouped_mlp_backward_weights_workspace_bytes, moe_grouped_mlp_backward_weights,
 )
 from .layer import MoELayer  # noqa: F401

@@ -40,6 +40,8 @@ _SIGS = {
     "moe_prepare_weights_backward": (_I, [_I, _I, _I, _I, _P, _P, _P, _P, _P]),
     "moe_grouped_mlp_backward_workspace_bytes": (_SZ, [_I64, _I, _I]),
     "moe_grouped_mlp_backward_data": (_I, [_I, _I, _I, _I64, _I, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "moe_grouped_mlp_backward_weights_workspace_bytes": (_SZ, [_I, _I64, _I, _I, _I]),
+    "moe_grouped_mlp_backward_weights": (_I, [_I, _I, _I, _I64, _I, _P, _P, _P, _P, _SZ, _P, _P, _P, _SZ, _P]),
     "moe_permute_backward": (_I, [_I, _I, _I, _I, _P, _P, _P, _P]),
     "moe_route_backward": (_I, [_I, _I, _I, _I, ctypes.c_float, _P, _P, _P, _P, _P, _P, _P]),
 }
@@ -250,3 +252,19 @@ def moe_grouped_mlp_backward_data(x_perm, offsets, w1p, w1t, w2t, d_y_perm, d_x_
     _check(lib.moe_grouped_mlp_backward_data(L, H, F, cap, BF16, _p(x_perm), _p(offsets), _p(w1p), _p(w1t), _p(w2t),
                                              _p(d_y_perm), _p(d_x_perm), _p(workspace), _nbytes(workspace), _stream()),
            "moe_grouped_mlp_backward_data")
+
+
+def moe_grouped_mlp_backward_weights_workspace_bytes(L, capacity, H, F, dtype):
+    return lib.moe_grouped_mlp_backward_weights_workspace_bytes(L, capacity, H, F, dtype)
+
+
+def moe_grouped_mlp_backward_weights(x_perm, offsets, d_y_perm, data_workspace, dW1, dW2, workspace, H, F):
+    _need(offsets, torch.int32, "offsets")
+    _need(dW1, torch.float32, "dW1")
+    _need(dW2, torch.float32, "dW2")
+    L = offsets.shape[0] - 1
+    cap = x_perm.shape[0]
+    _check(lib.moe_grouped_mlp_backward_weights(L, H, F, cap, BF16, _p(x_perm), _p(offsets), _p(d_y_perm),
+                                                _p(data_workspace), _nbytes(data_workspace), _p(dW1), _p(dW2),
+                                                _p(workspace), _nbytes(workspace), _stream()),
+           "moe_grouped_mlp_backward_weights")

@@ -69,6 +69,12 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 //        columns): acc = d_a; with g, u read from `aux` (EPI 3's output) the
 //        epilogue stores d_h = [d_a u silu'(g), d_a silu(g)] k-blocked
 //        [2N/32][capacity][32] in natural column order (gates, then ups)
+// EPI 5: (backward) weight gradient dW[e] = P_e^T Q_e over expert e's own
+//        rows: A = P^T and B = Q^T in token-blocked form [blocks][I or J][32
+//        tokens] (each expert's rows padded with zeros to a multiple of 128,
+//        block prefix `offsets` = pb[L+1]), `capacity` = I output rows, N = J
+//        columns; tiles (expert, I tile, J tile) of experts with rows, each over
+//        its expert's blocks (no split); out = fp32 [L][I][J]
 // EPI 2: the router projection, one dense GEMM of the `capacity` = T token
 //        rows of x [T][Kd] with the prepared router weights [ceil(N/32)*32][Kd]
 //        (row-major, loaded like A), N = E output columns.  Every tile is cut
@@ -136,6 +142,12 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[NI][2], int i0, c
           const int col = col0 + wn * 64 + j * 32 + r32;
           if (col < N) out[((long)(col >> 5) * capacity + grow) * GB_BK + (col & 31)] = (bf16_t)f32_to_bf16(acc[ii][j][v]);
         }
+      } else if (EPI == 5) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int col = col0 + wn * 64 + j * 32 + r32;
+          if (col < N) ((float*)out)[((long)ti.e * capacity + grow) * N + col] = acc[ii][j][v];
+        }
       } else if (EPI == 4) {
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
@@ -174,10 +186,15 @@ __global__ __launch_bounds__(GB_THREADS, 1) void k_gemm_bf16(int L, int N, int K
   const int NT = (N + GB_BN - 1) / GB_BN;
   const int KT = Kd / GB_BK;
   SplitPlan plan;
+  const int NTI = EPI == 5 ? (int)((capacity + GB_BM - 1) / GB_BM) : 1;  // EPI 5: I tiles
   if constexpr (EPI == 2) {  // every tile in L pieces, piece-major unit order
     plan.dp = 0;
     plan.S = L;
     plan.units = (int)((capacity + GB_BM - 1) / GB_BM) * NT * L;
+  } else if constexpr (EPI == 5) {  // NTI x NT tiles per expert with rows (pb[e+1] > pb[e]), no split
+    build_schedule(L, (int64_t)1 << 40, 1 << 30, NTI * NT, offsets, s_pre, s_tmp, 0);
+    plan.dp = plan.units = s_pre[L];
+    plan.S = 1;
   } else {
     plan = gb_schedule(L, capacity, NT, Kd, gridDim.x, offsets, s_pre, s_tmp);
   }
@@ -209,7 +226,15 @@ __global__ __launch_bounds__(GB_THREADS, 1) void k_gemm_bf16(int L, int N, int K
     w.piece = -1;
     w.k0 = 0;
     w.k1 = KT;
-    if constexpr (EPI == 2) {  // unit u: piece u / tiles of tile u % tiles
+    if constexpr (EPI == 5) {  // tile u: expert e, I tile fastest, then J tile
+      const int e = find_expert(s_pre, L, u);
+      const int local = u - s_pre[e];
+      w.ti.e = e;
+      w.ti.row0 = (local % NTI) * GB_BM;
+      w.ti.rows = min(GB_BM, (int)capacity - w.ti.row0);
+      w.ti.nt = local / NTI;
+      w.k1 = offsets[e + 1] - offsets[e];  // the expert's 32-token blocks (a multiple of 4)
+    } else if constexpr (EPI == 2) {  // unit u: piece u / tiles of tile u % tiles
       const int tiles = plan.units / plan.S;
       const int q = u / tiles, nq = KT / 4;
       tile = u - q * tiles;
@@ -236,27 +261,39 @@ __global__ __launch_bounds__(GB_THREADS, 1) void k_gemm_bf16(int L, int N, int K
     w.ti.row0 = __builtin_amdgcn_readfirstlane(w.ti.row0);
     w.ti.rows = __builtin_amdgcn_readfirstlane(w.ti.rows);
     w.ti.nt = __builtin_amdgcn_readfirstlane(w.ti.nt);
+    int eb = 0;  // EPI 5: the expert's first 32-token block
+    if constexpr (EPI == 5) eb = __builtin_amdgcn_readfirstlane(offsets[w.ti.e]);
     if constexpr (EPI == 2) {
       // the router weight rows of column tile nt, [rows][Kd]; rows past the
       // prepared ceil(N/32)*32 read as zeros
       const int c0 = w.ti.nt * GB_BN, crows = min(GB_BN, ((N + 31) & ~31) - c0);
       w.rB = __builtin_amdgcn_make_buffer_rsrc((void*)(B + (long)c0 * Kd), (short)0, crows * Kd * 2, 0x00020000);
+    } else if constexpr (EPI == 5) {
+      // Q^T blocks of the expert: step k at k * N * 32, the tile's columns
+      // from nt * 256 within it
+      const long b0 = ((long)eb * N + (long)w.ti.nt * GB_BN) * GB_BK;
+      w.rB = __builtin_amdgcn_make_buffer_rsrc((void*)(B + b0), (short)0,
+                                               (int)(((long)w.k1 * N - (long)w.ti.nt * GB_BN) * GB_BK * 2), 0x00020000);
     } else {
       // the (expert, panel) B tile: KT blocks of [256 columns][32 k]
       w.rB = __builtin_amdgcn_make_buffer_rsrc(
           (void*)(B + ((long)w.ti.e * NT + w.ti.nt) * (long)KT * GB_BN * GB_BK), (short)0,
           KT * GB_BN * GB_BK * 2, 0x00020000);
     }
-    w.rA = EPI != 0 ? __builtin_amdgcn_make_buffer_rsrc((void*)(A + (long)w.ti.row0 * Kd), (short)0,
-                                                        w.ti.rows * Kd * 2, 0x00020000)
-                    : __builtin_amdgcn_make_buffer_rsrc((void*)A, (short)0, (int)(KT * capacity * GB_BK * 2),
-                                                        0x00020000);
+    if constexpr (EPI == 5)  // P^T blocks of the expert: [k1][capacity = I][32]
+      w.rA = __builtin_amdgcn_make_buffer_rsrc((void*)(A + (long)eb * capacity * GB_BK), (short)0,
+                                               (int)((long)w.k1 * capacity * GB_BK * 2), 0x00020000);
+    else
+      w.rA = EPI != 0 ? __builtin_amdgcn_make_buffer_rsrc((void*)(A + (long)w.ti.row0 * Kd), (short)0,
+                                                          w.ti.rows * Kd * 2, 0x00020000)
+                      : __builtin_amdgcn_make_buffer_rsrc((void*)A, (short)0, (int)(KT * capacity * GB_BK * 2),
+                                                          0x00020000);
     // per-lane byte offsets of the 2 A and the 2 B blocks of a wavefront; the
     // k step enters through the scalar offset
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
       const int r = wv * 32 + q * 16 + drow;
-      w.va[q] = EPI != 0 ? (r * Kd + dch * 8) * 2 : ((w.ti.row0 + r) * GB_BK + dch * 8) * 2;
+      w.va[q] = (EPI != 0 && EPI != 5) ? (r * Kd + dch * 8) * 2 : ((w.ti.row0 + r) * GB_BK + dch * 8) * 2;
       w.vb[q] = EPI == 2 ? (r * Kd + dch * 8) * 2 : r * 64 + dch * 16;
     }
     {  // the dword of the extra rows (tall tile) that this lane moves: row
@@ -264,8 +301,8 @@ __global__ __launch_bounds__(GB_THREADS, 1) void k_gemm_bf16(int L, int N, int K
       const int xr = 4 * wv + (l >> 4), xc = (((l & 15) >> 2) ^ swz4(xr)) * 16 + (l & 3) * 4;
       w.vx = EPI != 0 ? (GB_BM + xr) * Kd * 2 + xc : ((w.ti.row0 + GB_BM + xr) * GB_BK) * 2 + xc;
     }
-    w.akstep = EPI != 0 ? GB_BK * 2 : (int)(capacity * GB_BK * 2);
-    w.bkstep = EPI == 2 ? GB_BK * 2 : GB_BN * GB_BK * 2;
+    w.akstep = (EPI != 0 && EPI != 5) ? GB_BK * 2 : (int)(capacity * GB_BK * 2);
+    w.bkstep = EPI == 2 ? GB_BK * 2 : EPI == 5 ? N * GB_BK * 2 : GB_BN * GB_BK * 2;
     return w;
   };
 
@@ -672,6 +709,36 @@ hipError_t launch_grouped_mlp_bf16_backward(int L, int H, int F, int64_t capacit
   hipLaunchKernelGGL(k_gemm_bf16<0>, dim3(G0), blk, lds, s, L, H, 2 * F, capacity, dhbuf, offsets, w1t, dx, part,
                      nul);
   hipLaunchKernelGGL(k_splitk_reduce<0>, rgrid, rblk, 0, s, L, H, 2 * F, capacity, G0, offsets, part, dx, nul);
+  return hipGetLastError();
+}
+
+// Weight gradient of the grouped SwiGLU MLP (bf16 operands, fp32 results):
+// the token-blocked operand layouts (launch_wgrad_layouts), then dW1 = X^T d_h
+// and dW2 = a^T d_y as EPI 5 GEMMs over each expert's own blocks.
+hipError_t launch_grouped_mlp_bf16_wgrad(int L, int H, int F, int64_t capacity, int nbmax, const bf16_t* x,
+                                         const int32_t* offsets, const bf16_t* dy, const bf16_t* hbuf,
+                                         const bf16_t* dhbuf, int32_t* pb, bf16_t* xt, bf16_t* dht, bf16_t* at,
+                                         bf16_t* dyt, float* dW1, float* dW2, hipStream_t s) {
+  if (capacity == 0) return hipSuccess;
+  hipError_t e = launch_wgrad_layouts(L, H, F, capacity, nbmax, x, offsets, dy, hbuf, dhbuf, pb, xt, dht, at, dyt,
+                                      dW1, dW2, s);
+  if (e != hipSuccess) return e;
+  const size_t lds = gemm_bf16_lds(L);
+  static bool attr_done = false;
+  if (!attr_done) {
+    (void)hipFuncSetAttribute((const void*)k_gemm_bf16<5>, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    attr_done = true;
+  }
+  auto grid = [&](int I, int J) {
+    const long tiles = (long)((I + GB_BM - 1) / GB_BM) * ((J + GB_BN - 1) / GB_BN) * L;
+    return (int)(tiles < num_cus() ? tiles : num_cus());
+  };
+  const dim3 blk(GB_THREADS);
+  const bf16_t* nul = nullptr;
+  hipLaunchKernelGGL(k_gemm_bf16<5>, dim3(grid(H, 2 * F)), blk, lds, s, L, 2 * F, 0, (int64_t)H, xt, pb, dht,
+                     (bf16_t*)dW1, (float*)nullptr, nul);
+  hipLaunchKernelGGL(k_gemm_bf16<5>, dim3(grid(F, H)), blk, lds, s, L, H, 0, (int64_t)F, at, pb, dyt,
+                     (bf16_t*)dW2, (float*)nullptr, nul);
   return hipGetLastError();
 }
 

@@ -67,6 +67,26 @@ __device__ inline void build_schedule(int L, int64_t capacity, int BM, int NT, c
   __syncthreads();
 }
 
+// rows of expert e: [min(offsets[e], cap), min(offsets[e+1], cap))
+__device__ __forceinline__ int expert_rows(const int32_t* __restrict__ offsets, int e, int64_t capacity, int* r0) {
+  int64_t lo = offsets[e], hi = offsets[e + 1];
+  lo = lo < capacity ? lo : capacity;
+  hi = hi < capacity ? hi : capacity;
+  *r0 = (int)lo;
+  return hi > lo ? (int)(hi - lo) : 0;
+}
+
+// largest e in [0, L) with pre[e] <= it (empty experts share their start
+// with the next one)
+__device__ __forceinline__ int find_expert(const int32_t* pre, int L, int it) {
+  int lo = 0, hi = L - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (pre[mid] <= it) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
 #define TILE_MGROUP 4
 
 struct TileInfo {

@@ -336,6 +336,55 @@ int moe_grouped_mlp_backward_data(int L, int H, int F, int64_t capacity, int dty
                                                         (bf16_t*)d_x_perm, (hipStream_t)stream));
 }
 
+// weight gradient: 32-token blocks of all experts' rows, each expert padded to 128
+static int64_t wgrad_blocks_max(int L, int64_t capacity) { return (capacity + 128 * (int64_t)L + 31) / 32; }
+
+size_t moe_grouped_mlp_backward_weights_workspace_bytes(int L, int64_t capacity, int H, int F, int dtype) {
+  if (L <= 0 || capacity <= 0 || H <= 0 || F <= 0 || dtype != MOE_BF16) return 256;
+  const size_t tok = (size_t)wgrad_blocks_max(L, capacity) * 32 * 2;  // bytes per column of a token-blocked operand
+  return round_up((size_t)(L + 1) * 4, 256) + round_up(tok * H, 256) + round_up(tok * 2 * F, 256) +
+         round_up(tok * F, 256) + round_up(tok * H, 256);
+}
+
+int moe_grouped_mlp_backward_weights(int L, int H, int F, int64_t capacity, int dtype, const void* x_perm,
+                                     const int32_t* offsets, const void* d_y_perm, const void* data_workspace,
+                                     size_t data_workspace_bytes, float* dW1, float* dW2, void* workspace,
+                                     size_t workspace_bytes, void* stream) {
+  if (L < 1 || L > MOE_MAX_L || H <= 0 || F <= 0 || capacity < 0 || capacity > (int64_t)1 << 31)
+    return MOE_ERR_SHAPE;
+  if (dtype != MOE_BF16) return MOE_ERR_DTYPE;
+  if (H % 128 || F % 128) return MOE_ERR_SHAPE;
+  if (capacity * (int64_t)(H > 2 * F ? H : 2 * F) * 2 > (int64_t)INT32_MAX) return MOE_ERR_SHAPE;
+  // token-blocked operands and the per-expert weight slices stay within 31-bit byte offsets
+  const int64_t nbmax = wgrad_blocks_max(L, capacity);
+  if (nbmax * 32 * (int64_t)(H > 2 * F ? H : 2 * F) * 2 > (int64_t)INT32_MAX) return MOE_ERR_SHAPE;
+  if (!offsets || !dW1 || !dW2) return MOE_ERR_NULL;
+  if (capacity > 0 && (!x_perm || !d_y_perm || !data_workspace || !workspace)) return MOE_ERR_NULL;
+  if (!aligned16(x_perm) || !aligned16(d_y_perm) || !aligned16(data_workspace) || !aligned16(dW1) ||
+      !aligned16(dW2) || !aligned16(workspace))
+    return MOE_ERR_ALIGN;
+  if (capacity > 0 && (data_workspace_bytes < moe_grouped_mlp_backward_workspace_bytes(capacity, F, dtype) ||
+                       workspace_bytes < moe_grouped_mlp_backward_weights_workspace_bytes(L, capacity, H, F, dtype)))
+    return MOE_ERR_WORKSPACE;
+  if (capacity == 0) return MOE_OK;
+  const bf16_t* hbuf = (const bf16_t*)data_workspace;
+  const bf16_t* dhbuf = (const bf16_t*)((const uint8_t*)data_workspace + round_up((size_t)capacity * 2 * F * 2, 256));
+  const size_t tok = (size_t)nbmax * 32 * 2;
+  uint8_t* w = (uint8_t*)workspace;
+  int32_t* pb = (int32_t*)w;
+  w += round_up((size_t)(L + 1) * 4, 256);
+  bf16_t* xt = (bf16_t*)w;
+  w += round_up(tok * H, 256);
+  bf16_t* dht = (bf16_t*)w;
+  w += round_up(tok * 2 * F, 256);
+  bf16_t* at = (bf16_t*)w;
+  w += round_up(tok * F, 256);
+  bf16_t* dyt = (bf16_t*)w;
+  return launch_status(launch_grouped_mlp_bf16_wgrad(L, H, F, capacity, (int)nbmax, (const bf16_t*)x_perm, offsets,
+                                                     (const bf16_t*)d_y_perm, hbuf, dhbuf, pb, xt, dht, at, dyt, dW1,
+                                                     dW2, (hipStream_t)stream));
+}
+
 // ---------------------------------------------------------------------------
 // Backward of the routing steps
 // ---------------------------------------------------------------------------

@@ -14,7 +14,7 @@
  *   moe_unpermute_combine  probability-weighted sum back in token order
  *
  * and the backward of the routing steps (combine, permute, route gates) and
- * the data gradient of the grouped MLP,
+ * the data and weight gradients of the grouped MLP,
  * plus one-time weight preparation and a standalone MX quantizer.
  *
  * Conventions shared by every call
@@ -335,6 +335,27 @@ int moe_grouped_mlp_backward_data(int L, int H, int F, int64_t capacity, int dty
                                   const int32_t* offsets, const void* w1p, const void* w1t, const void* w2t,
                                   const void* d_y_perm, void* d_x_perm, void* workspace, size_t workspace_bytes,
                                   void* stream);
+
+/* ------------------------------------------------------------------------
+ * Weight gradient of the grouped SwiGLU MLP (bf16 operands, fp32 results):
+ * for each expert e with rows X_e (of x_perm), dW1[e] = X_e^T d_h_e [H][2F]
+ * and dW2[e] = a_e^T d_y_e [F][H], contracted over the expert's own rows,
+ * with a = bf16(silu(g) * u) and h, d_h as moe_grouped_mlp_backward_data
+ * computed them: call this after that call, on the same stream, passing its
+ * workspace as `data_workspace` (it holds h and d_h).  dW1 [L][H][2F] and dW2
+ * [L][F][H] fp32 device; experts without rows get zeros.  The operands are
+ * regrouped into 32-token blocks with the contraction index contiguous, each
+ * expert's rows padded with zeros to a multiple of 128; the GEMMs run on the
+ * grouped GEMM's pipeline, one tile per (expert, 256 x 256 block of dW).
+ * Workspace: moe_grouped_mlp_backward_weights_workspace_bytes(L, capacity, H,
+ * F, MOE_BF16) bytes.  Limits as moe_grouped_mlp_backward_data, and
+ * (capacity + 128 L) * max(H, 2F) * 2 < 2^31.
+ * ------------------------------------------------------------------------ */
+size_t moe_grouped_mlp_backward_weights_workspace_bytes(int L, int64_t capacity, int H, int F, int dtype);
+int moe_grouped_mlp_backward_weights(int L, int H, int F, int64_t capacity, int dtype, const void* x_perm,
+                                     const int32_t* offsets, const void* d_y_perm, const void* data_workspace,
+                                     size_t data_workspace_bytes, float* dW1, float* dW2, void* workspace,
+                                     size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
  * Backward of the routing steps (the pages' router work covered forward and

@@ -75,3 +75,52 @@ def test_grouped_mlp_backward_data_mixtral_size():
     """The Mixtral-like shape (H = 4096, F = 14336, 8192 rows), checked on 48
     rows per expert."""
     _run(MIXTRAL_COUNTS, 4096, 14336, seed=7, sample=48)
+
+
+def _run_wgrad(counts, H, F, seed):
+    rng = np.random.default_rng(seed)
+    L = len(counts)
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    N = int(offsets[-1])
+    cap = N + 24
+    W1, W2 = _weights(rng, L, H, F, "bf16")
+    x = O.bf16_round(rng.standard_normal((cap, H)))
+    dy = O.bf16_round(rng.standard_normal((cap, H)))
+    w1 = torch.stack([bf16_from_f64(w) for w in W1])
+    w2 = torch.stack([bf16_from_f64(w) for w in W2])
+    w1p = torch.empty(D.moe_prepared_weight_bytes(L, H, F, D.BF16, 1), dtype=torch.uint8, device=DEV)
+    w2p = torch.empty(D.moe_prepared_weight_bytes(L, H, F, D.BF16, 2), dtype=torch.uint8, device=DEV)
+    w1t = torch.empty(D.moe_prepared_weight_bytes(L, H, F, D.BF16, 5), dtype=torch.uint8, device=DEV)
+    w2t = torch.empty(D.moe_prepared_weight_bytes(L, H, F, D.BF16, 6), dtype=torch.uint8, device=DEV)
+    D.moe_prepare_weights(w1, w2, D.BF16, w1p.view(torch.bfloat16), w2p.view(torch.bfloat16))
+    D.moe_prepare_weights_backward(w1, w2, w1t, w2t)
+    ws = torch.empty(D.moe_grouped_mlp_backward_workspace_bytes(cap, F, D.BF16), dtype=torch.uint8, device=DEV)
+    wws = torch.empty(D.moe_grouped_mlp_backward_weights_workspace_bytes(L, cap, H, F, D.BF16), dtype=torch.uint8,
+                      device=DEV)
+    dx = torch.empty((cap, H), dtype=torch.bfloat16, device=DEV)
+    dW1 = torch.full((L, H, 2 * F), 7.0, dtype=torch.float32, device=DEV)
+    dW2 = torch.full((L, F, H), 7.0, dtype=torch.float32, device=DEV)
+    off_d = torch.from_numpy(offsets).to(DEV)
+    xd, dyd = bf16_from_f64(x), bf16_from_f64(dy)
+    say("mlp backward weights L", L, "H", H, "F", F, "N", N)
+    D.moe_grouped_mlp_backward_data(xd, off_d, w1p, w1t, w2t, dyd, dx, ws, H, F)
+    D.moe_grouped_mlp_backward_weights(xd, off_d, dyd, ws, dW1, dW2, wws, H, F)
+    torch.cuda.synchronize()
+    want1, want2 = O.grouped_mlp_backward_weights(x[:N], offsets, W1, W2, dy[:N], "bf16")
+    got1, got2 = dW1.cpu().numpy().astype(np.float64), dW2.cpu().numpy().astype(np.float64)
+    for e, c in enumerate(counts):
+        if c == 0:
+            assert (got1[e] == 0).all() and (got2[e] == 0).all()
+    e1, e2 = rel_inf(got1, want1), rel_inf(got2, want2)
+    say("  dW1 rel err", e1, "dW2 rel err", e2)
+    # bf16 intermediates (a, d_h) may differ by one rounding from the oracle's
+    assert e1 <= TOL["bf16"] and e2 <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("counts,H,F", [
+    ([0, 1, 31, 128, 129, 300, 0], 256, 256),   # empty experts, rows not a multiple of 32 or 128
+    ([70, 300, 0, 5], 384, 128),                 # partial I and J tiles
+    (MIXTRAL_COUNTS, 512, 512),
+])
+def test_grouped_mlp_backward_weights(counts, H, F):
+    _run_wgrad(counts, H, F, seed=sum(counts) + 3 * H + F)
