@@ -27,6 +27,7 @@ is computed here by plain definitions:
                         the DeepSeek-V3 Technical Report's, not the pages')
   count_and_permute     stable counting sort of the valid local routes
   mx_quantize_rows      OCP Microscaling (MX) v1.0 block quantization, E4M3
+  mx_quantize_columns_grouped  the same along columns, blocked per expert group
   mx4_quantize_rows     the same with E2M1 (MXFP4) elements
   grouped_mlp           per-expert dense SwiGLU MLP in float64
   combine               probability-weighted sum in k order
@@ -181,6 +182,41 @@ def mx_quantize_rows(v):
     codes = e4m3_encode(e4m3_round(q)).reshape(R, C)
     scales = (E + 127).astype(np.uint8)
     return codes, scales
+
+
+def mx_quantize_columns_grouped(v, offsets, pad_rows=128):
+    """Group-aware column-wise MX quantization (E4M3 elements, E8M0 scales):
+    MX blocks of 32 consecutive rows of one column, the rows of each expert
+    group [offsets[e], offsets[e+1]) blocked on their own (padded with zero
+    rows to a multiple of pad_rows), so no block holds rows of two groups.
+    This is the form the expert GEMMs' weight gradient contracts over (the
+    pages' group-aware MXFP8 building block; bpdata article, "Transformer
+    Engine building blocks for dropless MoE in JAX").
+    Returns (pb [L+1] first block of each group, codes [nb][C][32] uint8 with
+    the code of the group's row 32*j + i of column c at [pb[e] + j][c][i],
+    scales [nb][C] uint8)."""
+    v = np.asarray(v, dtype=np.float64)
+    C = v.shape[1]
+    L = len(offsets) - 1
+    pb = [0]
+    codes, scales = [], []
+    for e in range(L):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        m = hi - lo
+        mp = -(-m // pad_rows) * pad_rows
+        blk = np.zeros((mp, C))
+        blk[:m] = v[lo:hi]
+        nb = mp // 32
+        pb.append(pb[-1] + nb)
+        if nb:
+            # [nb, 32, C] -> [nb, C, 32]: each column of a block is one row for the row quantizer
+            t = blk.reshape(nb, 32, C).transpose(0, 2, 1).reshape(nb * C, 32)
+            c, s_ = mx_quantize_rows(t)
+            codes.append(c.reshape(nb, C, 32))
+            scales.append(s_.reshape(nb, C))
+    codes = np.concatenate(codes) if codes else np.zeros((0, C, 32), np.uint8)
+    scales = np.concatenate(scales) if scales else np.zeros((0, C), np.uint8)
+    return np.array(pb, np.int64), codes, scales
 
 
 def mx_dequantize_rows(codes, scales) -> np.ndarray:

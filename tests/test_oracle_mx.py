@@ -227,3 +227,30 @@ def test_mx4_special_blocks_and_packing():
     p = O.pack_fp4(np.array([[1, 2, 0xF, 0x3]], np.uint8))
     assert p.tolist() == [[0x21, 0x3F]]
     np.testing.assert_array_equal(O.unpack_fp4(p), [[1, 2, 0xF, 0x3]])
+
+
+def test_columns_grouped_blocks_stay_inside_groups():
+    """Column-wise, group-aware MX blocks: each group blocked on its own (zero
+    rows pad it to a multiple of 128), a block's scale follows its own 32
+    values only, and the blocks dequantize back to the group's rows."""
+    rng = np.random.default_rng(5)
+    counts = [40, 0, 130, 1]
+    off = np.concatenate([[0], np.cumsum(counts)])
+    C = 64
+    v = O.bf16_round(rng.standard_normal((off[-1], C)) * np.exp(rng.uniform(-8, 8, (off[-1], 1))))
+    pb, codes, scales = O.mx_quantize_columns_grouped(v, off)
+    assert list(pb) == [0, 4, 4, 12, 16]
+    for e, m in enumerate(counts):
+        for j in range(pb[e + 1] - pb[e]):
+            rows = v[off[e] + 32 * j: off[e] + min(m, 32 * j + 32)]
+            blk = np.zeros((32, C))
+            blk[:len(rows)] = rows
+            for c in range(C):
+                # the row quantizer on the block's column alone (a group's
+                # neighbour never enters its scale)
+                cc, ss = O.mx_quantize_rows(blk[:, c][None, :])
+                assert (codes[pb[e] + j, c] == cc[0]).all() and scales[pb[e] + j, c] == ss[0, 0]
+            deq = O.mx_dequantize_rows(codes[pb[e] + j].reshape(C, 32), scales[pb[e] + j][:, None]).T
+            assert (deq[len(rows):] == 0).all()   # padding rows of the group stay zero
+    # a zero padding block: scale byte 0, codes 0
+    assert (scales[15] == 0).all() and (codes[15] == 0).all()
