@@ -13,5 +13,6 @@ from ._lib import (  # noqa: F401
     moe_unpermute_combine_backward, moe_permute_backward, moe_route_backward, moe_prepare_weights_backward,
     moe_grouped_mlp_backward_workspace_bytes, moe_grouped_mlp_backward_data,
     moe_grouped_mlp_backward_weights_workspace_bytes, moe_grouped_mlp_backward_weights,
+    moe_mx_columns_grouped_max_blocks, moe_mx_quantize_columns_grouped,
 )
 from .layer import MoELayer  # noqa: F401

@@ -41,6 +41,8 @@ _SIGS = {
     "moe_grouped_mlp_backward_workspace_bytes": (_SZ, [_I64, _I, _I]),
     "moe_grouped_mlp_backward_data": (_I, [_I, _I, _I, _I64, _I, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "moe_grouped_mlp_backward_weights_workspace_bytes": (_SZ, [_I, _I64, _I, _I, _I]),
+    "moe_mx_columns_grouped_max_blocks": (_I64, [_I, _I64]),
+    "moe_mx_quantize_columns_grouped": (_I, [_I, _I64, _I, _P, _P, _P, _P, _P, _P]),
     "moe_grouped_mlp_backward_weights": (_I, [_I, _I, _I, _I64, _I, _P, _P, _P, _P, _SZ, _P, _P, _P, _SZ, _P]),
     "moe_permute_backward": (_I, [_I, _I, _I, _I, _P, _P, _P, _P]),
     "moe_route_backward": (_I, [_I, _I, _I, _I, ctypes.c_float, _P, _P, _P, _P, _P, _P, _P]),
@@ -268,3 +270,16 @@ def moe_grouped_mlp_backward_weights(x_perm, offsets, d_y_perm, data_workspace, 
                                                 _p(data_workspace), _nbytes(data_workspace), _p(dW1), _p(dW2),
                                                 _p(workspace), _nbytes(workspace), _stream()),
            "moe_grouped_mlp_backward_weights")
+
+
+def moe_mx_columns_grouped_max_blocks(L, capacity):
+    return lib.moe_mx_columns_grouped_max_blocks(L, capacity)
+
+
+def moe_mx_quantize_columns_grouped(x, offsets, pb, codes, scales):
+    _need(offsets, torch.int32, "offsets")
+    _need(pb, torch.int32, "pb")
+    L = offsets.shape[0] - 1
+    cap, C = x.shape
+    _check(lib.moe_mx_quantize_columns_grouped(L, cap, C, _p(x), _p(offsets), _p(pb), _p(codes), _p(scales),
+                                               _stream()), "moe_mx_quantize_columns_grouped")

@@ -339,6 +339,23 @@ int moe_grouped_mlp_backward_data(int L, int H, int F, int64_t capacity, int dty
 // weight gradient: 32-token blocks of all experts' rows, each expert padded to 128
 static int64_t wgrad_blocks_max(int L, int64_t capacity) { return (capacity + 128 * (int64_t)L + 31) / 32; }
 
+int64_t moe_mx_columns_grouped_max_blocks(int L, int64_t capacity) {
+  if (L < 1 || capacity < 0) return 0;
+  return wgrad_blocks_max(L, capacity);
+}
+
+int moe_mx_quantize_columns_grouped(int L, int64_t capacity, int C, const void* in, const int32_t* offsets,
+                                    int32_t* pb, uint8_t* codes, uint8_t* scales, void* stream) {
+  if (L < 1 || L > MOE_MAX_L || capacity < 0 || capacity > (int64_t)1 << 31 || C <= 0 || C % 64) return MOE_ERR_SHAPE;
+  const int64_t nbmax = wgrad_blocks_max(L, capacity);
+  if (nbmax * 32 * (int64_t)C > (int64_t)INT32_MAX) return MOE_ERR_SHAPE;
+  if (!offsets || !pb) return MOE_ERR_NULL;
+  if (capacity > 0 && (!in || !codes || !scales)) return MOE_ERR_NULL;
+  if (!aligned16(in) || !aligned16(codes)) return MOE_ERR_ALIGN;
+  return launch_status(launch_mx_columns_grouped(L, capacity, C, capacity > 0 ? (int)nbmax : 0, (const bf16_t*)in,
+                                                 offsets, pb, codes, scales, (hipStream_t)stream));
+}
+
 size_t moe_grouped_mlp_backward_weights_workspace_bytes(int L, int64_t capacity, int H, int F, int dtype) {
   if (L <= 0 || capacity <= 0 || H <= 0 || F <= 0 || dtype != MOE_BF16) return 256;
   const size_t tok = (size_t)wgrad_blocks_max(L, capacity) * 32 * 2;  // bytes per column of a token-blocked operand

@@ -85,6 +85,69 @@ __global__ __launch_bounds__(256) void k_wgrad_pack(int L, int C, int64_t capaci
   *(uint4*)(out + ((long)b * C + c0 + oc) * 32 + part * 8) = make_uint4(o[0], o[1], o[2], o[3]);
 }
 
+// Group-aware column-wise MX quantization of rows [capacity][C] bf16: the
+// token blocks of k_wgrad_pack<0>, each column of a block one MX block (E4M3
+// codes, E8M0 scale, OCP MX v1.0): codes [b][C][32], scales [b][C].  Four
+// lanes hold one column's 32 values; their block maximum meets by two xor
+// shuffles.
+__global__ __launch_bounds__(256) void k_mx_columns_grouped(int L, int C, int64_t capacity,
+                                                            const bf16_t* __restrict__ src,
+                                                            const int32_t* __restrict__ offsets,
+                                                            const int32_t* __restrict__ pb, uint8_t* __restrict__ codes,
+                                                            uint8_t* __restrict__ scales) {
+  __shared__ uint16_t tile[64][34];
+  __shared__ int s_info[2];
+  const int b = blockIdx.y, c0 = blockIdx.x * 64, tid = threadIdx.x;
+  if (b >= pb[L]) return;  // uniform
+  if (tid == 0) {
+    const int e = find_expert(pb, L, b);
+    int r0;
+    const int m = expert_rows(offsets, e, capacity, &r0);
+    s_info[0] = r0 + (b - pb[e]) * 32;
+    s_info[1] = min(32, max(0, m - (b - pb[e]) * 32));
+  }
+  __syncthreads();
+  const int t0 = s_info[0], nt = s_info[1];
+  const int tt = tid >> 3, cg = tid & 7;
+  uint4 q = make_uint4(0, 0, 0, 0);
+  if (tt < nt) q = *(const uint4*)(src + (long)(t0 + tt) * C + c0 + cg * 8);
+  const uint32_t w4[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    tile[cg * 8 + 2 * i][tt] = (uint16_t)(w4[i] & 0xffffu);
+    tile[cg * 8 + 2 * i + 1][tt] = (uint16_t)(w4[i] >> 16);
+  }
+  __syncthreads();
+  const int oc = tid >> 2, part = tid & 3;
+  uint32_t v[8], am = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    v[i] = tile[oc][part * 8 + i];
+    am = max(am, v[i] & 0x7fffu);
+  }
+  am = max(am, (uint32_t)__shfl_xor((int)am, 1, 64));
+  am = max(am, (uint32_t)__shfl_xor((int)am, 2, 64));
+  const int E = mx_scale_exp(am);
+  uint32_t lo = 0, hi = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    lo |= mx_e4m3(v[i], E) << (8 * i);
+    hi |= mx_e4m3(v[4 + i], E) << (8 * i);
+  }
+  *(uint2*)(codes + ((long)b * C + c0 + oc) * 32 + part * 8) = make_uint2(lo, hi);
+  if (part == 0) scales[(long)b * C + c0 + oc] = (uint8_t)(E + 127);
+}
+
+hipError_t launch_mx_columns_grouped(int L, int64_t capacity, int C, int nbmax, const bf16_t* in,
+                                     const int32_t* offsets, int32_t* pb, uint8_t* codes, uint8_t* scales,
+                                     hipStream_t s) {
+  hipLaunchKernelGGL(k_wgrad_blocks, dim3(1), dim3(1024), 0, s, L, capacity, offsets, pb);
+  if (nbmax > 0)
+    hipLaunchKernelGGL(k_mx_columns_grouped, dim3(C / 64, nbmax), dim3(256), 0, s, L, C, capacity, in, offsets, pb,
+                       codes, scales);
+  return hipGetLastError();
+}
+
 // dW[e] = 0 for the experts without rows (the GEMM has no tiles for them)
 __global__ __launch_bounds__(256) void k_wgrad_zero_empty(int L, int64_t capacity, long per_expert,
                                                           const int32_t* __restrict__ offsets, float* __restrict__ dw) {

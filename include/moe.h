@@ -352,6 +352,23 @@ int moe_grouped_mlp_backward_data(int L, int H, int F, int64_t capacity, int dty
  * (capacity + 128 L) * max(H, 2F) * 2 < 2^31.
  * ------------------------------------------------------------------------ */
 size_t moe_grouped_mlp_backward_weights_workspace_bytes(int L, int64_t capacity, int H, int F, int dtype);
+
+/* Group-aware column-wise MX quantization, the operand form of an MXFP8
+ * weight gradient (the pages' group-aware MXFP8 quantization; bpdata
+ * article, "Transformer Engine building blocks for dropless MoE in JAX"): the
+ * rows [offsets[e], offsets[e+1]) (bounded by capacity) of each expert group
+ * of in [capacity][C] bf16 are cut into blocks of 32 consecutive rows of that
+ * group alone (zero rows pad each group to a multiple of 128, so no block
+ * holds rows of two groups), and each column of a block is one MX block (OCP
+ * MX v1.0: E8M0 scale E = floor(log2 amax) - 8 clamped to [-127, 127], E4M3
+ * codes rounded to nearest even, saturating).  Outputs (device): pb [L+1]
+ * int32, the first block of each group (pb[L] = blocks written); codes
+ * [blocks][C][32] uint8 (row 32 j + i of group e, column c at [pb[e] + j][c][i]);
+ * scales [blocks][C] uint8 (E + 127).  codes and scales must hold
+ * moe_mx_columns_grouped_max_blocks(L, capacity) blocks.  C % 64 == 0. */
+int64_t moe_mx_columns_grouped_max_blocks(int L, int64_t capacity);
+int moe_mx_quantize_columns_grouped(int L, int64_t capacity, int C, const void* in, const int32_t* offsets,
+                                    int32_t* pb, uint8_t* codes, uint8_t* scales, void* stream);
 int moe_grouped_mlp_backward_weights(int L, int H, int F, int64_t capacity, int dtype, const void* x_perm,
                                      const int32_t* offsets, const void* d_y_perm, const void* data_workspace,
                                      size_t data_workspace_bytes, float* dW1, float* dW2, void* workspace,

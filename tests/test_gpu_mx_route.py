@@ -198,3 +198,28 @@ def test_route_bias_and_mask_small_and_large():
         ids, probs, lo, err = _route_gpu(T, E, K, D.SIGMOID, logits=z.to(DEV), bias=bias.to(DEV), mask=mask.to(DEV))
         _check_route(ids, probs, lo, T, K, "sigmoid", bias.numpy(), mask.numpy())
         assert (ids[mask.numpy() == 1] == -1).all()
+
+
+@pytest.mark.parametrize("counts,C", [([40, 0, 130, 1, 300], 128), ([0, 0], 64), ([1011, 1049, 983, 992], 4096)])
+def test_mx_quantize_columns_grouped(counts, C):
+    """Group-aware column-wise MX quantization: block offsets, codes and scales
+    bit-exact against the oracle (each group blocked on its own, zero padding);
+    blocks past the last group untouched."""
+    rng = np.random.default_rng(sum(counts) + C)
+    L = len(counts)
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    cap = int(offsets[-1]) + 20
+    v = O.bf16_round(rng.standard_normal((cap, C)) * np.exp(rng.uniform(-6, 6, (cap, 1))))
+    nbmax = D.moe_mx_columns_grouped_max_blocks(L, cap)
+    pb = torch.full((L + 1,), -5, dtype=torch.int32, device=DEV)
+    codes = torch.full((nbmax, C, 32), 0xAB, dtype=torch.uint8, device=DEV)
+    scales = torch.full((nbmax, C), 0xCD, dtype=torch.uint8, device=DEV)
+    say("mx columns grouped", counts, C)
+    D.moe_mx_quantize_columns_grouped(bf16_from_f64(v), torch.from_numpy(offsets).to(DEV), pb, codes, scales)
+    torch.cuda.synchronize()
+    opb, oc, os_ = O.mx_quantize_columns_grouped(v, offsets)
+    np.testing.assert_array_equal(np_of(pb), opb)
+    nb = int(opb[-1])
+    np.testing.assert_array_equal(np_of(codes)[:nb], oc)
+    np.testing.assert_array_equal(np_of(scales)[:nb], os_)
+    assert (np_of(codes)[nb:] == 0xAB).all() and (np_of(scales)[nb:] == 0xCD).all()
