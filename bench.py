@@ -412,7 +412,7 @@ def backward_stages(layer, cfg, N):
 def main():
     a = parse()
     if a.gpus != 1:
-        print(f"bench.py measures one GPU only; --gpus {a.gpus} is not supported (this build has no multi-GPU "
+        print(f"bench.py measures one GPU only; --gpus {a.gpus} is not supported (the library has no multi-GPU "
               f"path)", file=sys.stderr)
         sys.exit(2)
     if a.workload:
