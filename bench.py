@@ -392,6 +392,21 @@ def backward_stages(layer, cfg, N):
     e1.record()
     torch.cuda.synchronize()
     t_wg = e0.elapsed_time(e1) / 3 * 1000.0
+    # the same with MXFP8 operands (group-aware column-wise quantization included)
+    del wws
+    wws = torch.empty(D.moe_grouped_mlp_backward_weights_workspace_bytes(cfg.E, layer.capacity, H, F, D.MXFP8),
+                      dtype=torch.uint8, device="cuda")
+    wgm = lambda: D.moe_grouped_mlp_backward_weights(layer.x_perm, layer.offsets, d_y, ws, dW1, dW2, wws, H, F,
+                                                     dtype=D.MXFP8)
+    for _ in range(2):
+        wgm()
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(3):
+        wgm()
+    e1.record()
+    torch.cuda.synchronize()
+    t_wgm = e0.elapsed_time(e1) / 3 * 1000.0
     del ws, w1t, w2t, wws, dW1, dW2
     cb_bytes = T * H * 2 + 2 * N * H * 2 + T * K * 12
     pb_bytes = N * H * 2 + T * H * 2 + T * K * 4
@@ -402,6 +417,8 @@ def backward_stages(layer, cfg, N):
             "grouped_mlp_backward_data_tflops": round(10.0 * N * H * F / (t_mb * 1e-6) / 1e12, 1),
             "grouped_mlp_backward_weights_us": round(t_wg, 1),
             "grouped_mlp_backward_weights_tflops": round(6.0 * N * H * F / (t_wg * 1e-6) / 1e12, 1),
+            "grouped_mlp_backward_weights_mxfp8_us": round(t_wgm, 1),
+            "grouped_mlp_backward_weights_mxfp8_tflops": round(6.0 * N * H * F / (t_wgm * 1e-6) / 1e12, 1),
             "note": "GPU time per call from HIP-graph replays (the MLP data gradient: events around 3 eager "
                     "calls; flops 10 N H F: h recomputed 4, d_a 2, d_x 4; the weight gradient likewise, 6 N H F, "
                     "its operand regrouping included); GB/s = algorithmic bytes (combine backward: dout, "

@@ -260,13 +260,14 @@ def moe_grouped_mlp_backward_weights_workspace_bytes(L, capacity, H, F, dtype):
     return lib.moe_grouped_mlp_backward_weights_workspace_bytes(L, capacity, H, F, dtype)
 
 
-def moe_grouped_mlp_backward_weights(x_perm, offsets, d_y_perm, data_workspace, dW1, dW2, workspace, H, F):
+def moe_grouped_mlp_backward_weights(x_perm, offsets, d_y_perm, data_workspace, dW1, dW2, workspace, H, F,
+                                     dtype=BF16):
     _need(offsets, torch.int32, "offsets")
     _need(dW1, torch.float32, "dW1")
     _need(dW2, torch.float32, "dW2")
     L = offsets.shape[0] - 1
     cap = x_perm.shape[0]
-    _check(lib.moe_grouped_mlp_backward_weights(L, H, F, cap, BF16, _p(x_perm), _p(offsets), _p(d_y_perm),
+    _check(lib.moe_grouped_mlp_backward_weights(L, H, F, cap, dtype, _p(x_perm), _p(offsets), _p(d_y_perm),
                                                 _p(data_workspace), _nbytes(data_workspace), _p(dW1), _p(dW2),
                                                 _p(workspace), _nbytes(workspace), _stream()),
            "moe_grouped_mlp_backward_weights")

@@ -143,17 +143,31 @@ __global__ __launch_bounds__(GM_THREADS, 1) void k_gemm_mx(int L, int N, int Kd,
                                                            const int32_t* __restrict__ offsets,
                                                            const uint8_t* __restrict__ B,
                                                            const uint8_t* __restrict__ Bs, uint8_t* __restrict__ out,
-                                                           uint8_t* __restrict__ out_s, float* __restrict__ part) {
+                                                           uint8_t* __restrict__ out_s, float* __restrict__ part,
+                                                           const int32_t* __restrict__ aux_i) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   int32_t* s_pre = (int32_t*)(smem + GM_LDS_SCALES + 2 * GM_SGROUP_BYTES);  // [L+1]
   int32_t* s_tmp = s_pre + (L + 1);                                          // [16]
   const int NT = (N + GM_BN - 1) / GM_BN;
-  build_schedule(L, capacity, GM_BM, NT, offsets, s_pre, s_tmp, TALL ? GM_TALL : 0);
+  // EPI 5 (the MXFP8 weight gradient): offsets = pk (each expert's padded
+  // rows, prefix), aux_i = png (its 512-row scale groups, prefix), capacity =
+  // I rows of dW, N = J columns; NTI x NT tiles per expert with rows, no split
+  const int NTI = EPI == 5 ? (int)((capacity + GM_BM - 1) / GM_BM) : 1;
+  if (EPI == 5)
+    build_schedule(L, (int64_t)1 << 40, 1 << 30, NTI * NT, offsets, s_pre, s_tmp, 0);
+  else
+    build_schedule(L, capacity, GM_BM, NT, offsets, s_pre, s_tmp, TALL ? GM_TALL : 0);
   // RB code bytes per row; KT stages of 64 bytes; SG stages per 16-block scale group
   constexpr int SG = FP4 ? 4 : 8, LG = FP4 ? 2 : 3;
   const int RB = FP4 ? Kd / 2 : Kd;
   const int KT = RB / GM_BK, KB = Kd / 32, NG = (Kd + 511) / 512;
-  const SplitPlan plan = gm_split_plan(s_pre[L], gridDim.x, KT);
+  SplitPlan plan;
+  if (EPI == 5) {
+    plan.dp = plan.units = s_pre[L];
+    plan.S = 1;
+  } else {
+    plan = gm_split_plan(s_pre[L], gridDim.x, KT);
+  }
   const int tid = threadIdx.x, l = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wv >> 2, wn = wv & 3;
@@ -176,7 +190,7 @@ __global__ __launch_bounds__(GM_THREADS, 1) void k_gemm_mx(int L, int N, int Kd,
     TileInfo ti;
     int piece, k0, k1;
     __amdgpu_buffer_rsrc_t rA, rB, rS;
-    int va[2], vb[2], vs, sgstep, vx, vxs;
+    int va[2], vb[2], vs, sgstep, vx, vxs, ng;
   };
   auto setup = [&](int u) {
     Unit w;
@@ -184,6 +198,52 @@ __global__ __launch_bounds__(GM_THREADS, 1) void k_gemm_mx(int L, int N, int Kd,
     w.piece = -1;
     w.k0 = 0;
     w.k1 = KT;
+    w.ng = NG;
+    if constexpr (EPI == 5) {
+      const int e = find_expert(s_pre, L, u);
+      const int local = u - s_pre[e];
+      w.ti.e = e;
+      w.ti.row0 = (local % NTI) * GM_BM;
+      w.ti.rows = min(GM_BM, (int)capacity - w.ti.row0);
+      w.ti.nt = local / NTI;
+      const int Kp = offsets[e + 1] - offsets[e];  // the expert's padded rows
+      w.k1 = Kp / GM_BK;
+      w.ng = (Kp + 511) / 512;
+      w.ti.e = __builtin_amdgcn_readfirstlane(w.ti.e);
+      w.ti.row0 = __builtin_amdgcn_readfirstlane(w.ti.row0);
+      w.ti.rows = __builtin_amdgcn_readfirstlane(w.ti.rows);
+      w.ti.nt = __builtin_amdgcn_readfirstlane(w.ti.nt);
+      w.k1 = __builtin_amdgcn_readfirstlane(w.k1);
+      w.ng = __builtin_amdgcn_readfirstlane(w.ng);
+      const long pke = __builtin_amdgcn_readfirstlane(offsets[e]), pge = __builtin_amdgcn_readfirstlane(aux_i[e]);
+      const long CP = (long)NT * GM_BN;
+      // A: codes [I][Kp] and scales [I][Kp/32] of the expert
+      w.rA = __builtin_amdgcn_make_buffer_rsrc((void*)(A + pke * capacity + (long)w.ti.row0 * Kp), (short)0,
+                                               w.ti.rows * Kp, 0x00020000);
+      // B: the expert's panels [NT][Kp/64][256][64], scales [NT][ng][256][16]
+      w.rB = __builtin_amdgcn_make_buffer_rsrc((void*)(B + pke * CP + (long)w.ti.nt * w.k1 * (GM_BN * GM_BK)),
+                                               (short)0, w.k1 * GM_BN * GM_BK, 0x00020000);
+      if (wv < 4) {
+        w.rS = __builtin_amdgcn_make_buffer_rsrc((void*)(As + (pke / 32) * capacity + (long)w.ti.row0 * (Kp / 32)),
+                                                 (short)0, w.ti.rows * (Kp / 32), 0x00020000);
+        w.vs = srow * (Kp / 32);
+        w.sgstep = 16;
+      } else {
+        w.rS = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(Bs + pge * CP * 16 + (long)w.ti.nt * w.ng * GM_SGROUP_HALF), (short)0, w.ng * GM_SGROUP_HALF,
+            0x00020000);
+        w.vs = srow * 16;
+        w.sgstep = GM_SGROUP_HALF;
+      }
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int r = wv * 32 + q * 16 + drow;
+        w.va[q] = r * Kp + dch * 16;
+        w.vb[q] = r * GM_BK + dch * 16;
+      }
+      w.vx = w.vxs = 0;
+      return w;
+    }
     if (u >= plan.dp) {  // split-K piece: stages [k0, k1), whole groups of 4
       w.piece = u - plan.dp;
       tile = plan.dp + w.piece / plan.S;
@@ -398,8 +458,8 @@ __global__ __launch_bounds__(GM_THREADS, 1) void k_gemm_mx(int L, int N, int Kd,
       if (XM) GM_READX(h, kt + h);                                                          \
       {                                                                                     \
         const int kn = min(kt + h + 3, k1 - 1);                                             \
-        GM_SDMA_IF(cu, min(((kt + h) >> LG) + 1, NG - 1), (kt + h) & (SG - 1), SG - 3);     \
-        if ((NL) == 5) GM_XSDMA_IF(cu, min(((kt + h) >> LG) + 1, NG - 1), (kt + h) & (SG - 1), SG - 3); \
+        GM_SDMA_IF(cu, min(((kt + h) >> LG) + 1, cu.ng - 1), (kt + h) & (SG - 1), SG - 3);  \
+        if ((NL) == 5) GM_XSDMA_IF(cu, min(((kt + h) >> LG) + 1, cu.ng - 1), (kt + h) & (SG - 1), SG - 3); \
         _Pragma("unroll") for (int q = 0; q < (NL); ++q) GM_DMA(cu, (h + 3) & 3, kn, q);   \
       }                                                                                     \
       if ((NL) == 5) asm volatile("s_waitcnt vmcnt(10) lgkmcnt(0)\n\ts_barrier" ::: "memory"); \
@@ -451,7 +511,22 @@ __global__ __launch_bounds__(GM_THREADS, 1) void k_gemm_mx(int L, int N, int Kd,
       cu = setup(u);
       GM_PROLOGUE(cu);
     }
-    if (done.piece < 0) {
+    if constexpr (EPI == 5) {  // fp32 dW[e][row][col]
+      int gg = g, rr = r32;  // opaque, as in mx_store_tile: no row numbers held across the k loop
+      asm volatile("" : "+v"(gg), "+v"(rr));
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int row = wm * 128 + i * 32 + 8 * (v >> 2) + 4 * gg + (v & 3);
+          if (row >= done.ti.rows) continue;
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            const int col = done.ti.nt * GM_BN + wn * 64 + j * 32 + rr;
+            if (col < N) ((float*)out)[((long)done.ti.e * capacity + done.ti.row0 + row) * N + col] = acc[i][j][v];
+          }
+        }
+    } else if (done.piece < 0) {
       mx_store_tile<EPI, 4, FP4>(acc, 0, done.ti, N, wm, wn, g, r32, out, out_s);
       if (TALL && done.ti.rows > GM_BM) {
         // the extra rows: wavefront (1, wn) hands its block (columns wn * 64 +
@@ -573,11 +648,11 @@ static void launch_mx(int L, int H, int F, int64_t capacity, const uint8_t* x, c
   const int G1 = grid(2 * F), G2 = grid(H);
   const dim3 rgrid(GEMM_SPLIT_UNITS / 2 * 8), rblk(320), blk(GM_THREADS);
   hipLaunchKernelGGL((k_gemm_mx<1, FP4, TALL>), dim3(G1), blk, lds, s, L, 2 * F, H, capacity, x, xs, offsets, w1p,
-                     w1s, act, act_s, part);
+                     w1s, act, act_s, part, (const int32_t*)nullptr);
   hipLaunchKernelGGL((k_mx_splitk_reduce<1, FP4, TALL>), rgrid, rblk, 0, s, L, 2 * F, H, capacity, G1, offsets,
                      part, act, act_s);
   hipLaunchKernelGGL((k_gemm_mx<0, FP4, TALL>), dim3(G2), blk, lds, s, L, H, F, capacity, act, act_s, offsets,
-                     w2p, w2s, (uint8_t*)y, (uint8_t*)nullptr, part);
+                     w2p, w2s, (uint8_t*)y, (uint8_t*)nullptr, part, (const int32_t*)nullptr);
   hipLaunchKernelGGL((k_mx_splitk_reduce<0, FP4, TALL>), rgrid, rblk, 0, s, L, H, F, capacity, G2, offsets, part,
                      (uint8_t*)y, (uint8_t*)nullptr);
 }
@@ -597,6 +672,37 @@ hipError_t launch_grouped_mlp_mx(int L, int H, int F, int64_t capacity, bool fp4
     launch_mx<false, true>(L, H, F, capacity, x, xs, offsets, w1p, w1s, w2p, w2s, act, act_s, part, y, s);
   else
     launch_mx<false, false>(L, H, F, capacity, x, xs, offsets, w1p, w1s, w2p, w2s, act, act_s, part, y, s);
+  return hipGetLastError();
+}
+
+// MXFP8 weight gradient: the group-aware column-wise MX operands in the MX
+// GEMM's own layouts (launch_wgrad_mx_layouts), then dW1 = X^T d_h and
+// dW2 = a^T d_y as EPI 5 GEMMs over each expert's padded rows.
+hipError_t launch_grouped_mlp_mx_wgrad(int L, int H, int F, int64_t capacity, int nbmax, const bf16_t* x,
+                                       const int32_t* offsets, const bf16_t* dy, const bf16_t* hbuf,
+                                       const bf16_t* dhbuf, int32_t* pk, int32_t* png, uint8_t* xa, uint8_t* xas,
+                                       uint8_t* dhb, uint8_t* dhbs, uint8_t* aa, uint8_t* aas, uint8_t* dyb,
+                                       uint8_t* dybs, float* dW1, float* dW2, hipStream_t s) {
+  if (capacity == 0) return hipSuccess;
+  hipError_t e = launch_wgrad_mx_layouts(L, H, F, capacity, nbmax, x, offsets, dy, hbuf, dhbuf, pk, png, xa, xas, dhb,
+                                         dhbs, aa, aas, dyb, dybs, dW1, dW2, s);
+  if (e != hipSuccess) return e;
+  static bool attr_done = false;
+  if (!attr_done) {
+    (void)hipFuncSetAttribute((const void*)k_gemm_mx<5, false, false>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              160 * 1024);
+    attr_done = true;
+  }
+  const size_t lds = mx_lds_bytes(L, false);
+  auto grid = [&](int I, int J) {
+    const long tiles = (long)((I + GM_BM - 1) / GM_BM) * ((J + GM_BN - 1) / GM_BN) * L;
+    return (int)(tiles < num_cus() ? tiles : num_cus());
+  };
+  const dim3 blk(GM_THREADS);
+  hipLaunchKernelGGL((k_gemm_mx<5, false, false>), dim3(grid(H, 2 * F)), blk, lds, s, L, 2 * F, 0, (int64_t)H, xa,
+                     xas, pk, dhb, dhbs, (uint8_t*)dW1, (uint8_t*)nullptr, (float*)nullptr, (const int32_t*)png);
+  hipLaunchKernelGGL((k_gemm_mx<5, false, false>), dim3(grid(F, H)), blk, lds, s, L, H, 0, (int64_t)F, aa, aas, pk,
+                     dyb, dybs, (uint8_t*)dW2, (uint8_t*)nullptr, (float*)nullptr, (const int32_t*)png);
   return hipGetLastError();
 }
 

@@ -356,8 +356,27 @@ int moe_mx_quantize_columns_grouped(int L, int64_t capacity, int C, const void* 
                                                  offsets, pb, codes, scales, (hipStream_t)stream));
 }
 
+// MXFP8 weight gradient: rows of all experts, each padded to a multiple of
+// 256, and their 512-row scale groups
+static int64_t wgrad_mx_rows_max(int L, int64_t capacity) { return capacity + 256 * (int64_t)L; }
+static int64_t wgrad_mx_groups_max(int L, int64_t capacity) { return capacity / 512 + L + 1; }
+
+// byte sizes of the MXFP8 operands: A-form (rows = C columns) and B-form (256-column panels)
+static size_t mx_a_codes(int L, int64_t cap, int C) { return round_up((size_t)wgrad_mx_rows_max(L, cap) * C, 256); }
+static size_t mx_a_scales(int L, int64_t cap, int C) { return round_up((size_t)wgrad_mx_rows_max(L, cap) / 32 * C, 256); }
+static size_t mx_b_codes(int L, int64_t cap, int C) {
+  return round_up((size_t)wgrad_mx_rows_max(L, cap) * ((C + 255) / 256 * 256), 256);
+}
+static size_t mx_b_scales(int L, int64_t cap, int C) {
+  return round_up((size_t)wgrad_mx_groups_max(L, cap) * ((C + 255) / 256 * 256) * 16, 256);
+}
+
 size_t moe_grouped_mlp_backward_weights_workspace_bytes(int L, int64_t capacity, int H, int F, int dtype) {
-  if (L <= 0 || capacity <= 0 || H <= 0 || F <= 0 || dtype != MOE_BF16) return 256;
+  if (L <= 0 || capacity <= 0 || H <= 0 || F <= 0 || (dtype != MOE_BF16 && dtype != MOE_MXFP8)) return 256;
+  if (dtype == MOE_MXFP8)
+    return 2 * round_up((size_t)(L + 1) * 4, 256) + mx_a_codes(L, capacity, H) + mx_a_scales(L, capacity, H) +
+           mx_b_codes(L, capacity, 2 * F) + mx_b_scales(L, capacity, 2 * F) + mx_a_codes(L, capacity, F) +
+           mx_a_scales(L, capacity, F) + mx_b_codes(L, capacity, H) + mx_b_scales(L, capacity, H);
   const size_t tok = (size_t)wgrad_blocks_max(L, capacity) * 32 * 2;  // bytes per column of a token-blocked operand
   return round_up((size_t)(L + 1) * 4, 256) + round_up(tok * H, 256) + round_up(tok * 2 * F, 256) +
          round_up(tok * F, 256) + round_up(tok * H, 256);
@@ -369,9 +388,11 @@ int moe_grouped_mlp_backward_weights(int L, int H, int F, int64_t capacity, int 
                                      size_t workspace_bytes, void* stream) {
   if (L < 1 || L > MOE_MAX_L || H <= 0 || F <= 0 || capacity < 0 || capacity > (int64_t)1 << 31)
     return MOE_ERR_SHAPE;
-  if (dtype != MOE_BF16) return MOE_ERR_DTYPE;
+  if (dtype != MOE_BF16 && dtype != MOE_MXFP8) return MOE_ERR_DTYPE;
   if (H % 128 || F % 128) return MOE_ERR_SHAPE;
   if (capacity * (int64_t)(H > 2 * F ? H : 2 * F) * 2 > (int64_t)INT32_MAX) return MOE_ERR_SHAPE;
+  if (dtype == MOE_MXFP8 && wgrad_mx_rows_max(L, capacity) * (int64_t)((2 * F > H ? 2 * F : H) + 255) > (int64_t)INT32_MAX)
+    return MOE_ERR_SHAPE;
   // token-blocked operands and the per-expert weight slices stay within 31-bit byte offsets
   const int64_t nbmax = wgrad_blocks_max(L, capacity);
   if (nbmax * 32 * (int64_t)(H > 2 * F ? H : 2 * F) * 2 > (int64_t)INT32_MAX) return MOE_ERR_SHAPE;
@@ -380,12 +401,31 @@ int moe_grouped_mlp_backward_weights(int L, int H, int F, int64_t capacity, int 
   if (!aligned16(x_perm) || !aligned16(d_y_perm) || !aligned16(data_workspace) || !aligned16(dW1) ||
       !aligned16(dW2) || !aligned16(workspace))
     return MOE_ERR_ALIGN;
-  if (capacity > 0 && (data_workspace_bytes < moe_grouped_mlp_backward_workspace_bytes(capacity, F, dtype) ||
+  if (capacity > 0 && (data_workspace_bytes < moe_grouped_mlp_backward_workspace_bytes(capacity, F, MOE_BF16) ||
                        workspace_bytes < moe_grouped_mlp_backward_weights_workspace_bytes(L, capacity, H, F, dtype)))
     return MOE_ERR_WORKSPACE;
   if (capacity == 0) return MOE_OK;
   const bf16_t* hbuf = (const bf16_t*)data_workspace;
   const bf16_t* dhbuf = (const bf16_t*)((const uint8_t*)data_workspace + round_up((size_t)capacity * 2 * F * 2, 256));
+  if (dtype == MOE_MXFP8) {
+    uint8_t* w = (uint8_t*)workspace;
+    int32_t* pk = (int32_t*)w;
+    w += round_up((size_t)(L + 1) * 4, 256);
+    int32_t* png = (int32_t*)w;
+    w += round_up((size_t)(L + 1) * 4, 256);
+    uint8_t* xa = w;   w += mx_a_codes(L, capacity, H);
+    uint8_t* xas = w;  w += mx_a_scales(L, capacity, H);
+    uint8_t* dhb = w;  w += mx_b_codes(L, capacity, 2 * F);
+    uint8_t* dhbs = w; w += mx_b_scales(L, capacity, 2 * F);
+    uint8_t* aa = w;   w += mx_a_codes(L, capacity, F);
+    uint8_t* aas = w;  w += mx_a_scales(L, capacity, F);
+    uint8_t* dyb = w;  w += mx_b_codes(L, capacity, H);
+    uint8_t* dybs = w;
+    const int nbmx = (int)(wgrad_mx_rows_max(L, capacity) / 32);
+    return launch_status(launch_grouped_mlp_mx_wgrad(L, H, F, capacity, nbmx, (const bf16_t*)x_perm, offsets,
+                                                     (const bf16_t*)d_y_perm, hbuf, dhbuf, pk, png, xa, xas, dhb, dhbs,
+                                                     aa, aas, dyb, dybs, dW1, dW2, (hipStream_t)stream));
+  }
   const size_t tok = (size_t)nbmax * 32 * 2;
   uint8_t* w = (uint8_t*)workspace;
   int32_t* pb = (int32_t*)w;

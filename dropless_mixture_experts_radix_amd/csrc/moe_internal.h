@@ -220,6 +220,16 @@ hipError_t launch_prepare_weights_backward(int L, int H, int F, const void* w1, 
 hipError_t launch_mx_columns_grouped(int L, int64_t capacity, int C, int nbmax, const bf16_t* in,
                                      const int32_t* offsets, int32_t* pb, uint8_t* codes, uint8_t* scales,
                                      hipStream_t s);
+hipError_t launch_wgrad_mx_layouts(int L, int H, int F, int64_t capacity, int nbmax, const bf16_t* x,
+                                   const int32_t* offsets, const bf16_t* dy, const bf16_t* hbuf,
+                                   const bf16_t* dhbuf, int32_t* pk, int32_t* png, uint8_t* xa, uint8_t* xas,
+                                   uint8_t* dhb, uint8_t* dhbs, uint8_t* aa, uint8_t* aas, uint8_t* dyb,
+                                   uint8_t* dybs, float* dW1, float* dW2, hipStream_t s);
+hipError_t launch_grouped_mlp_mx_wgrad(int L, int H, int F, int64_t capacity, int nbmax, const bf16_t* x,
+                                       const int32_t* offsets, const bf16_t* dy, const bf16_t* hbuf,
+                                       const bf16_t* dhbuf, int32_t* pk, int32_t* png, uint8_t* xa, uint8_t* xas,
+                                       uint8_t* dhb, uint8_t* dhbs, uint8_t* aa, uint8_t* aas, uint8_t* dyb,
+                                       uint8_t* dybs, float* dW1, float* dW2, hipStream_t s);
 hipError_t launch_wgrad_layouts(int L, int H, int F, int64_t capacity, int nbmax, const bf16_t* x,
                                 const int32_t* offsets, const bf16_t* dy, const bf16_t* hbuf, const bf16_t* dhbuf,
                                 int32_t* pb, bf16_t* xt, bf16_t* dht, bf16_t* at, bf16_t* dyt, float* dW1,

@@ -337,7 +337,8 @@ int moe_grouped_mlp_backward_data(int L, int H, int F, int64_t capacity, int dty
                                   void* stream);
 
 /* ------------------------------------------------------------------------
- * Weight gradient of the grouped SwiGLU MLP (bf16 operands, fp32 results):
+ * Weight gradient of the grouped SwiGLU MLP (bf16 or MXFP8 operands, fp32
+ * results):
  * for each expert e with rows X_e (of x_perm), dW1[e] = X_e^T d_h_e [H][2F]
  * and dW2[e] = a_e^T d_y_e [F][H], contracted over the expert's own rows,
  * with a = bf16(silu(g) * u) and h, d_h as moe_grouped_mlp_backward_data
@@ -347,9 +348,15 @@ int moe_grouped_mlp_backward_data(int L, int H, int F, int64_t capacity, int dty
  * regrouped into 32-token blocks with the contraction index contiguous, each
  * expert's rows padded with zeros to a multiple of 128; the GEMMs run on the
  * grouped GEMM's pipeline, one tile per (expert, 256 x 256 block of dW).
+ * dtype MOE_MXFP8: the four operands are quantized group-aware and column-wise
+ * (as moe_mx_quantize_columns_grouped: MX blocks of 32 rows of one expert in
+ * one column; each expert padded to a multiple of 256 rows here) and the
+ * GEMMs run on the MX matrix-core instruction (fp32 accumulation); h, a and
+ * d_h come from the bf16 data gradient as for MOE_BF16.
  * Workspace: moe_grouped_mlp_backward_weights_workspace_bytes(L, capacity, H,
- * F, MOE_BF16) bytes.  Limits as moe_grouped_mlp_backward_data, and
- * (capacity + 128 L) * max(H, 2F) * 2 < 2^31.
+ * F, dtype) bytes.  Limits as moe_grouped_mlp_backward_data, and
+ * (capacity + 128 L) * max(H, 2F) * 2 < 2^31 (MOE_MXFP8 also
+ * (capacity + 256 L) * (max(H, 2F) + 255) < 2^31).
  * ------------------------------------------------------------------------ */
 size_t moe_grouped_mlp_backward_weights_workspace_bytes(int L, int64_t capacity, int H, int F, int dtype);
 

@@ -732,8 +732,11 @@ def grouped_mlp_backward_weights(x_perm, offsets, W1, W2, d_y, dtype):
     dW1[e] = X^T d_h and dW2[e] = a^T d_y (contractions over the expert's own
     rows), with h = X W1[e] recomputed, a = silu(g) u, d_a = d_y W2[e]^T and
     d_h = swiglu'(h, d_a).  Rounding points of the bf16 path: h, a and d_h
-    are bf16; the gradients are fp32.  "f64" rounds nothing.  Empty experts
-    get zero gradients.  Returns (dW1 [L][H][2F], dW2 [L][F][H])."""
+    are bf16; the gradients are fp32.  "f64" rounds nothing.  "mxfp8": the
+    bf16 path's operands X, a, d_h, d_y are MX-quantized column-wise in
+    32-row blocks of the expert (mx_quantize_columns_grouped) before the
+    contractions.  Empty experts get zero gradients.  Returns (dW1 [L][H][2F],
+    dW2 [L][F][H])."""
     x_perm = np.asarray(x_perm, np.float64)
     d_y = np.asarray(d_y, np.float64)
     rnd = (lambda v: v) if dtype == "f64" else bf16_round
@@ -748,9 +751,23 @@ def grouped_mlp_backward_weights(x_perm, offsets, W1, W2, d_y, dtype):
         h = rnd(X @ W1e)
         a = rnd(swiglu(h, F))
         d_h = rnd(swiglu_backward(h, dY @ W2e.T, F))
+        if dtype == "mxfp8":
+            X, a, d_h, dY = (_mx_columns_roundtrip(V) for V in (X, a, d_h, dY))
         dW1.append(out(X.T @ d_h))
         dW2.append(out(a.T @ dY))
     return np.stack(dW1), np.stack(dW2)
+
+
+def _mx_columns_roundtrip(V):
+    """Values of the rows V [m][C] after column-wise MX quantization in
+    32-row blocks (one group) and dequantization."""
+    m, C = V.shape
+    if m == 0:
+        return V
+    pb, codes, scales = mx_quantize_columns_grouped(V, np.array([0, m]), pad_rows=32)
+    nb = int(pb[-1])
+    deq = mx_dequantize_rows(codes.reshape(nb * C, 32), scales.reshape(nb * C, 1))
+    return deq.reshape(nb, C, 32).transpose(0, 2, 1).reshape(nb * 32, C)[:m]
 
 
 # ---------------------------------------------------------------------------

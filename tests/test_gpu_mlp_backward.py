@@ -77,7 +77,7 @@ def test_grouped_mlp_backward_data_mixtral_size():
     _run(MIXTRAL_COUNTS, 4096, 14336, seed=7, sample=48)
 
 
-def _run_wgrad(counts, H, F, seed):
+def _run_wgrad(counts, H, F, seed, dt="bf16"):
     rng = np.random.default_rng(seed)
     L = len(counts)
     offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
@@ -95,7 +95,8 @@ def _run_wgrad(counts, H, F, seed):
     D.moe_prepare_weights(w1, w2, D.BF16, w1p.view(torch.bfloat16), w2p.view(torch.bfloat16))
     D.moe_prepare_weights_backward(w1, w2, w1t, w2t)
     ws = torch.empty(D.moe_grouped_mlp_backward_workspace_bytes(cap, F, D.BF16), dtype=torch.uint8, device=DEV)
-    wws = torch.empty(D.moe_grouped_mlp_backward_weights_workspace_bytes(L, cap, H, F, D.BF16), dtype=torch.uint8,
+    code = D.BF16 if dt == "bf16" else D.MXFP8
+    wws = torch.empty(D.moe_grouped_mlp_backward_weights_workspace_bytes(L, cap, H, F, code), dtype=torch.uint8,
                       device=DEV)
     dx = torch.empty((cap, H), dtype=torch.bfloat16, device=DEV)
     dW1 = torch.full((L, H, 2 * F), 7.0, dtype=torch.float32, device=DEV)
@@ -104,9 +105,9 @@ def _run_wgrad(counts, H, F, seed):
     xd, dyd = bf16_from_f64(x), bf16_from_f64(dy)
     say("mlp backward weights L", L, "H", H, "F", F, "N", N)
     D.moe_grouped_mlp_backward_data(xd, off_d, w1p, w1t, w2t, dyd, dx, ws, H, F)
-    D.moe_grouped_mlp_backward_weights(xd, off_d, dyd, ws, dW1, dW2, wws, H, F)
+    D.moe_grouped_mlp_backward_weights(xd, off_d, dyd, ws, dW1, dW2, wws, H, F, dtype=code)
     torch.cuda.synchronize()
-    want1, want2 = O.grouped_mlp_backward_weights(x[:N], offsets, W1, W2, dy[:N], "bf16")
+    want1, want2 = O.grouped_mlp_backward_weights(x[:N], offsets, W1, W2, dy[:N], dt)
     got1, got2 = dW1.cpu().numpy().astype(np.float64), dW2.cpu().numpy().astype(np.float64)
     for e, c in enumerate(counts):
         if c == 0:
@@ -114,7 +115,7 @@ def _run_wgrad(counts, H, F, seed):
     e1, e2 = rel_inf(got1, want1), rel_inf(got2, want2)
     say("  dW1 rel err", e1, "dW2 rel err", e2)
     # bf16 intermediates (a, d_h) may differ by one rounding from the oracle's
-    assert e1 <= TOL["bf16"] and e2 <= TOL["bf16"]
+    assert e1 <= TOL[dt] and e2 <= TOL[dt]
 
 
 @pytest.mark.parametrize("counts,H,F", [
@@ -124,3 +125,14 @@ def _run_wgrad(counts, H, F, seed):
 ])
 def test_grouped_mlp_backward_weights(counts, H, F):
     _run_wgrad(counts, H, F, seed=sum(counts) + 3 * H + F)
+
+
+@pytest.mark.parametrize("counts,H,F", [
+    ([0, 1, 31, 128, 129, 300, 0], 256, 256),   # empty experts, rows padded to 256 per expert
+    ([70, 300, 0, 5], 384, 128),                 # partial I and J tiles
+    (MIXTRAL_COUNTS, 512, 512),                  # several 512-row scale groups per expert
+])
+def test_grouped_mlp_backward_weights_mxfp8(counts, H, F):
+    """MXFP8 weight gradient: group-aware column-wise MX operands, MX matrix-core
+    GEMMs; against the oracle's MXFP8 path within the MX tolerance."""
+    _run_wgrad(counts, H, F, seed=sum(counts) + 5 * H + F, dt="mxfp8")

@@ -220,3 +220,26 @@ def test_mlp_backward_weights_matches_torch_autograd():
         y.backward(torch.tensor(dy[lo:hi]))
         np.testing.assert_allclose(dW1[e], w1.grad.numpy(), rtol=1e-12, atol=1e-12)
         np.testing.assert_allclose(dW2[e], w2.grad.numpy(), rtol=1e-12, atol=1e-12)
+
+
+def test_mlp_backward_weights_mxfp8_close_to_bf16_and_exact_on_grid():
+    """The MXFP8 weight gradient: operands whose 32-row column blocks are on
+    the E4M3 grid of their block scale give exactly the bf16 result; general
+    operands stay within the MX rounding of it."""
+    rng = np.random.default_rng(43)
+    H, F = 64, 32
+    counts = [40, 0, 33]
+    off = np.concatenate([[0], np.cumsum(counts)])
+    W1 = [O.bf16_round(rng.standard_normal((H, 2 * F)) * 0.1) for _ in counts]
+    W2 = [O.bf16_round(rng.standard_normal((F, H)) * 0.1) for _ in counts]
+    x = O.bf16_round(rng.standard_normal((off[-1], H)))
+    dy = O.bf16_round(rng.standard_normal((off[-1], H)))
+    b1, b2 = O.grouped_mlp_backward_weights(x, off, W1, W2, dy, "bf16")
+    m1, m2 = O.grouped_mlp_backward_weights(x, off, W1, W2, dy, "mxfp8")
+    assert np.abs(m1 - b1).max() <= 0.1 * np.abs(b1).max() and np.abs(m2 - b2).max() <= 0.1 * np.abs(b2).max()
+    assert (m1[1] == 0).all() and (m2[1] == 0).all()
+    # on-grid rows: integers in [-8, 8] with 8 in every 32-row block of every
+    # column (block scale 2^-5; 32 k for |k| <= 8 are E4M3 values)
+    grid = rng.integers(-8, 9, size=(50, 16)).astype(np.float64)
+    grid[0] = grid[32] = 8.0
+    np.testing.assert_array_equal(O._mx_columns_roundtrip(grid), grid)
