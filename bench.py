@@ -361,8 +361,13 @@ def backward_stages(layer, cfg, N):
         w1[e].copy_(a1)
         w2[e].copy_(a2)
     D.moe_prepare_weights_backward(w1, w2, w1t, w2t)
-    del w1, w2
-    ws = torch.empty(D.moe_grouped_mlp_backward_workspace_bytes(layer.capacity, F, D.BF16), dtype=torch.uint8,
+    # the MXFP8 panels: the forward's W1p and the backward's W1^T / W2^T, codes and scales
+    mx = {k: torch.empty(D.moe_prepared_weight_bytes(cfg.E, H, F, D.MXFP8, k), dtype=torch.uint8, device="cuda")
+          for k in (1, 2, 3, 4, 5, 6, 7, 8)}
+    D.moe_prepare_weights(w1, w2, D.MXFP8, mx[1], mx[2], mx[3], mx[4])
+    D.moe_prepare_weights_backward(w1, w2, mx[5], mx[6], mx[7], mx[8], dtype=D.MXFP8)
+    del w1, w2, mx[2], mx[4]
+    ws = torch.empty(D.moe_grouped_mlp_backward_workspace_bytes(layer.capacity, H, F, D.BF16), dtype=torch.uint8,
                      device="cuda")
     d_xp = torch.empty_like(layer.x_perm)
     bwd = lambda: D.moe_grouped_mlp_backward_data(layer.x_perm, layer.offsets, layer.w1p, w1t, w2t, d_y, d_xp, ws,
@@ -408,6 +413,22 @@ def backward_stages(layer, cfg, N):
     torch.cuda.synchronize()
     t_wgm = e0.elapsed_time(e1) / 3 * 1000.0
     del ws, w1t, w2t, wws, dW1, dW2
+    # the data gradient with MXFP8 operands (x_perm and d_y quantization included)
+    ws = torch.empty(D.moe_grouped_mlp_backward_workspace_bytes(layer.capacity, H, F, D.MXFP8), dtype=torch.uint8,
+                     device="cuda")
+    bwdm = lambda: D.moe_grouped_mlp_backward_data(layer.x_perm, layer.offsets, mx[1], mx[5], mx[6], d_y, d_xp, ws,
+                                                   H, F, dtype=D.MXFP8, w1p_scales=mx[3], w1t_scales=mx[7],
+                                                   w2t_scales=mx[8])
+    for _ in range(2):
+        bwdm()
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(3):
+        bwdm()
+    e1.record()
+    torch.cuda.synchronize()
+    t_mbm = e0.elapsed_time(e1) / 3 * 1000.0
+    del ws, mx
     cb_bytes = T * H * 2 + 2 * N * H * 2 + T * K * 12
     pb_bytes = N * H * 2 + T * H * 2 + T * K * 4
     return {"combine_backward_us": round(t_cb, 2), "combine_backward_gbs": round(cb_bytes / (t_cb * 1e-6) / 1e9, 1),
@@ -415,6 +436,8 @@ def backward_stages(layer, cfg, N):
             "route_backward_us": round(t_rb, 2),
             "grouped_mlp_backward_data_us": round(t_mb, 1),
             "grouped_mlp_backward_data_tflops": round(10.0 * N * H * F / (t_mb * 1e-6) / 1e12, 1),
+            "grouped_mlp_backward_data_mxfp8_us": round(t_mbm, 1),
+            "grouped_mlp_backward_data_mxfp8_tflops": round(10.0 * N * H * F / (t_mbm * 1e-6) / 1e12, 1),
             "grouped_mlp_backward_weights_us": round(t_wg, 1),
             "grouped_mlp_backward_weights_tflops": round(6.0 * N * H * F / (t_wg * 1e-6) / 1e12, 1),
             "grouped_mlp_backward_weights_mxfp8_us": round(t_wgm, 1),

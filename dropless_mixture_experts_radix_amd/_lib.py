@@ -37,9 +37,10 @@ _SIGS = {
     "moe_unpermute_combine": (_I, [_I, _I, _I, _I, _P, _P, _P, _P, _P]),
     "moe_mx_quantize": (_I, [_I64, _I, _P, _P, _P, _P, _P]),
     "moe_unpermute_combine_backward": (_I, [_I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P]),
-    "moe_prepare_weights_backward": (_I, [_I, _I, _I, _I, _P, _P, _P, _P, _P]),
-    "moe_grouped_mlp_backward_workspace_bytes": (_SZ, [_I64, _I, _I]),
-    "moe_grouped_mlp_backward_data": (_I, [_I, _I, _I, _I64, _I, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "moe_prepare_weights_backward": (_I, [_I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P]),
+    "moe_grouped_mlp_backward_workspace_bytes": (_SZ, [_I64, _I, _I, _I]),
+    "moe_grouped_mlp_backward_data": (_I, [_I, _I, _I, _I64, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ,
+                                           _P]),
     "moe_grouped_mlp_backward_weights_workspace_bytes": (_SZ, [_I, _I64, _I, _I, _I]),
     "moe_mx_columns_grouped_max_blocks": (_I64, [_I, _I64]),
     "moe_mx_quantize_columns_grouped": (_I, [_I, _I64, _I, _P, _P, _P, _P, _P, _P]),
@@ -237,22 +238,24 @@ def moe_route_backward(ids, d_probs, d_z, score, *, probs=None, logits=None, sco
                                   _p(score_bias), _p(d_z), _stream()), "moe_route_backward")
 
 
-def moe_prepare_weights_backward(w1, w2, w1t, w2t):
+def moe_prepare_weights_backward(w1, w2, w1t, w2t, w1t_scales=None, w2t_scales=None, dtype=BF16):
     L, H, F2 = w1.shape
-    _check(lib.moe_prepare_weights_backward(L, H, F2 // 2, dtype_code(w1.dtype), _p(w1), _p(w2), _p(w1t), _p(w2t),
-                                            _stream()), "moe_prepare_weights_backward")
+    _check(lib.moe_prepare_weights_backward(L, H, F2 // 2, dtype, _p(w1), _p(w2), _p(w1t), _p(w2t), _p(w1t_scales),
+                                            _p(w2t_scales), _stream()), "moe_prepare_weights_backward")
 
 
-def moe_grouped_mlp_backward_workspace_bytes(capacity, F, dtype):
-    return lib.moe_grouped_mlp_backward_workspace_bytes(capacity, F, dtype)
+def moe_grouped_mlp_backward_workspace_bytes(capacity, H, F, dtype):
+    return lib.moe_grouped_mlp_backward_workspace_bytes(capacity, H, F, dtype)
 
 
-def moe_grouped_mlp_backward_data(x_perm, offsets, w1p, w1t, w2t, d_y_perm, d_x_perm, workspace, H, F):
+def moe_grouped_mlp_backward_data(x_perm, offsets, w1p, w1t, w2t, d_y_perm, d_x_perm, workspace, H, F, dtype=BF16,
+                                  w1p_scales=None, w1t_scales=None, w2t_scales=None):
     _need(offsets, torch.int32, "offsets")
     L = offsets.shape[0] - 1
     cap = x_perm.shape[0]
-    _check(lib.moe_grouped_mlp_backward_data(L, H, F, cap, BF16, _p(x_perm), _p(offsets), _p(w1p), _p(w1t), _p(w2t),
-                                             _p(d_y_perm), _p(d_x_perm), _p(workspace), _nbytes(workspace), _stream()),
+    _check(lib.moe_grouped_mlp_backward_data(L, H, F, cap, dtype, _p(x_perm), _p(offsets), _p(w1p), _p(w1p_scales),
+                                             _p(w1t), _p(w1t_scales), _p(w2t), _p(w2t_scales), _p(d_y_perm),
+                                             _p(d_x_perm), _p(workspace), _nbytes(workspace), _stream()),
            "moe_grouped_mlp_backward_data")
 
 

@@ -29,6 +29,16 @@
 // EPI 1 (GEMM1): a = silu(gate) * up is rounded to bf16 and MX-quantized along
 // F in the epilogue (one 32-column gate chunk = one MX block of a row).
 // EPI 0 (GEMM2): y stored as bf16.
+// The data gradient (MXFP8):
+// EPI 3: h = x_perm . W1 recomputed, stored bf16 k-blocked [N/32][capacity][32]
+//        in the prepared (gate/up interleaved) column order.
+// EPI 4: A = d_y (row-wise MX along H), B = the MX W2^T panels (N = F
+//        columns): acc = d_a; with g, u read from `aux` (EPI 3's output) the
+//        epilogue forms d_h = [d_a u silu'(g), d_a silu(g)] (natural column
+//        order, gates then ups), rounds it to bf16, stores that k-blocked
+//        [2N/32][capacity][32] in `aux_o` (the weight gradient's input) and
+//        its row-wise MX codes [capacity][2N] and scales [capacity][2N/32] in
+//        out / out_s (the A operand of d_x = d_h . W1^T, an EPI 0 GEMM).
 #include "gemm_common.h"
 
 namespace moe {
@@ -71,6 +81,54 @@ __device__ __forceinline__ uint32_t max_half_wave(uint32_t v) {
   return max(v, (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x401F));                 // lane ^ 16
 }
 
+// EPI 4 epilogue of row blocks [i0 + II, i0 + NI) (see mx_store_tile).
+template <int NI, int II>
+__device__ __forceinline__ void mx_epi4_blocks(const f32x16 (&acc)[NI][2], int i0, int msub, const TileInfo& ti,
+                                               int N, int wm, int wn, int g, int r32, uint8_t* __restrict__ out,
+                                               uint8_t* __restrict__ out_s, int64_t capacity,
+                                               const bf16_t* __restrict__ aux, bf16_t* __restrict__ aux_o) {
+  if constexpr (II < NI) {
+    if (i0 + II < msub) {  // uniform over the wavefront
+      const int N2 = 2 * N;
+      const int col0 = ti.nt * GM_BN;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int row = wm * 128 + (i0 + II) * 32 + 8 * (v >> 2) + 4 * g + (v & 3);
+        const bool live = row < ti.rows;  // the same for the 32 lanes of a half
+        const long grow = ti.row0 + row;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int f = col0 + wn * 64 + j * 32 + r32;  // column of d_a
+          const bool ok = live && f < N;
+          const int pg = (f >> 5) * 64 + (f & 31);      // gate's prepared column; up's is pg + 32
+          float gt = 0.0f, up = 0.0f;
+          if (ok) {
+            gt = bf16_to_f32(aux[((long)(pg >> 5) * capacity + grow) * 32 + (f & 31)]);
+            up = bf16_to_f32(aux[((long)((pg >> 5) + 1) * capacity + grow) * 32 + (f & 31)]);
+          }
+          const float da = acc[II][j][v];
+          const float sg = 1.0f / (1.0f + expf(-gt));
+          const uint32_t dg = f32_to_bf16(da * up * sg * (1.0f + gt * (1.0f - sg)));
+          const uint32_t du = f32_to_bf16(da * gt * sg);
+          const int Eg = mx_scale_exp(max_half_wave(dg & 0x7fffu));
+          const int Eu = mx_scale_exp(max_half_wave(du & 0x7fffu));
+          if (ok) {
+            aux_o[((long)(f >> 5) * capacity + grow) * 32 + (f & 31)] = (bf16_t)dg;
+            aux_o[((long)((N + f) >> 5) * capacity + grow) * 32 + (f & 31)] = (bf16_t)du;
+            out[grow * N2 + f] = (uint8_t)mx_e4m3(dg, Eg);
+            out[grow * N2 + N + f] = (uint8_t)mx_e4m3(du, Eu);
+            if (r32 == 0) {
+              out_s[grow * (N2 >> 5) + (f >> 5)] = (uint8_t)(Eg + 127);
+              out_s[grow * (N2 >> 5) + ((N + f) >> 5)] = (uint8_t)(Eu + 127);
+            }
+          }
+        }
+      }
+    }
+    mx_epi4_blocks<NI, II + 1>(acc, i0, msub, ti, N, wm, wn, g, r32, out, out_s, capacity, aux, aux_o);
+  }
+}
+
 // Epilogue of row blocks [i0, i0+NI) of one wavefront's 128 x 64 part of a
 // tile (MFMA D layout: lane l holds column l%32, rows 8 (v/4) + 4 (l/32) + v%4
 // of each 32 x 32 block).  Every lane of the wavefront must call it (EPI 1
@@ -78,7 +136,8 @@ __device__ __forceinline__ uint32_t max_half_wave(uint32_t v) {
 template <int EPI, int NI, bool FP4>
 __device__ __forceinline__ void mx_store_tile(const f32x16 (&acc)[NI][2], int i0, const TileInfo& ti, int N, int wm, int wn,
                                               int g, int r32, uint8_t* __restrict__ out,
-                                              uint8_t* __restrict__ out_s) {
+                                              uint8_t* __restrict__ out_s, int64_t capacity,
+                                              const bf16_t* __restrict__ aux, bf16_t* __restrict__ aux_o) {
   const int col0 = ti.nt * GM_BN;
   const int msub = max(0, (ti.rows - wm * 128 + 31) / 32);  // row blocks with rows (9: tall tile)
   // opaque lane offsets: the compiler cannot hoist the per-row numbers out of
@@ -101,6 +160,28 @@ __device__ __forceinline__ void mx_store_tile(const f32x16 (&acc)[NI][2], int i0
         }
       }
     }
+  } else if (EPI == 3) {
+    bf16_t* h = (bf16_t*)out;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      if (i0 + i >= msub) continue;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int row = wm * 128 + (i0 + i) * 32 + 8 * (v >> 2) + 4 * g + (v & 3);
+        if (row >= ti.rows) continue;
+        const long grow = ti.row0 + row;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int col = col0 + wn * 64 + j * 32 + r32;
+          if (col < N) h[((long)(col >> 5) * capacity + grow) * 32 + (col & 31)] = (bf16_t)f32_to_bf16(acc[i][j][v]);
+        }
+      }
+    }
+  } else if (EPI == 4) {
+    // one row block at a time with a constant index into acc (a loop over the
+    // blocks is not unrolled at this body size, and a variable index would put
+    // acc in scratch memory for the whole kernel)
+    mx_epi4_blocks<NI, 0>(acc, i0, msub, ti, N, wm, wn, g, r32, out, out_s, capacity, aux, aux_o);
   } else {
     const int Fh = N >> 1;
     const int jcol = (col0 >> 1) + wn * 32 + r32;  // this lane's column of a
@@ -144,7 +225,9 @@ __global__ __launch_bounds__(GM_THREADS, 1) void k_gemm_mx(int L, int N, int Kd,
                                                            const uint8_t* __restrict__ B,
                                                            const uint8_t* __restrict__ Bs, uint8_t* __restrict__ out,
                                                            uint8_t* __restrict__ out_s, float* __restrict__ part,
-                                                           const int32_t* __restrict__ aux_i) {
+                                                           const void* __restrict__ aux,
+                                                           bf16_t* __restrict__ aux_o) {
+  const int32_t* aux_i = (const int32_t*)aux;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   int32_t* s_pre = (int32_t*)(smem + GM_LDS_SCALES + 2 * GM_SGROUP_BYTES);  // [L+1]
   int32_t* s_tmp = s_pre + (L + 1);                                          // [16]
@@ -527,7 +610,7 @@ __global__ __launch_bounds__(GM_THREADS, 1) void k_gemm_mx(int L, int N, int Kd,
           }
         }
     } else if (done.piece < 0) {
-      mx_store_tile<EPI, 4, FP4>(acc, 0, done.ti, N, wm, wn, g, r32, out, out_s);
+      mx_store_tile<EPI, 4, FP4>(acc, 0, done.ti, N, wm, wn, g, r32, out, out_s, capacity, (const bf16_t*)aux, aux_o);
       if (TALL && done.ti.rows > GM_BM) {
         // the extra rows: wavefront (1, wn) hands its block (columns wn * 64 +
         // 32) to wavefront (0, wn) through ring stage 3, which no load of this
@@ -551,7 +634,8 @@ __global__ __launch_bounds__(GM_THREADS, 1) void k_gemm_mx(int L, int N, int Kd,
             pair[0][1][4 * c + 2] = v[2];
             pair[0][1][4 * c + 3] = v[3];
           }
-          mx_store_tile<EPI, 1, FP4>(pair, 8, done.ti, N, 0, wn, g, r32, out, out_s);
+          mx_store_tile<EPI, 1, FP4>(pair, 8, done.ti, N, 0, wn, g, r32, out, out_s, capacity, (const bf16_t*)aux,
+                                     aux_o);
         }
       }
     } else {
@@ -595,7 +679,8 @@ template <int EPI, bool FP4, bool TALL>
 __global__ __launch_bounds__(320) void k_mx_splitk_reduce(int L, int N, int Kd, int64_t capacity, int G,
                                                           const int32_t* __restrict__ offsets,
                                                           const float* __restrict__ part, uint8_t* __restrict__ out,
-                                                          uint8_t* __restrict__ out_s) {
+                                                          uint8_t* __restrict__ out_s,
+                                                          const bf16_t* __restrict__ aux, bf16_t* __restrict__ aux_o) {
   __shared__ int32_t s_pre[MOE_MAX_L + 1];
   __shared__ int32_t s_tmp[16];
   const int NT = (N + GM_BN - 1) / GM_BN;
@@ -610,11 +695,11 @@ __global__ __launch_bounds__(320) void k_mx_splitk_reduce(int L, int N, int Kd, 
   if (i < 4) {
     if (ti.rows <= (wv >> 2) * 128 + i * 32) return;  // row block past the tile's rows
     sum_partials(src + wv * 8192 + i * 2048, plan.S, acc, GM_PART_FLOATS);
-    mx_store_tile<EPI, 1, FP4>(acc, i, ti, N, wv >> 2, wv & 3, l >> 5, l & 31, out, out_s);
+    mx_store_tile<EPI, 1, FP4>(acc, i, ti, N, wv >> 2, wv & 3, l >> 5, l & 31, out, out_s, capacity, aux, aux_o);
   } else {
     if (wv >= 4 || ti.rows <= GM_BM) return;
     sum_partials(src + GM_PART_X + wv * 2048, plan.S, acc, GM_PART_FLOATS);
-    mx_store_tile<EPI, 1, FP4>(acc, 8, ti, N, 0, wv, l >> 5, l & 31, out, out_s);
+    mx_store_tile<EPI, 1, FP4>(acc, 8, ti, N, 0, wv, l >> 5, l & 31, out, out_s, capacity, aux, aux_o);
   }
 }
 
@@ -648,13 +733,13 @@ static void launch_mx(int L, int H, int F, int64_t capacity, const uint8_t* x, c
   const int G1 = grid(2 * F), G2 = grid(H);
   const dim3 rgrid(GEMM_SPLIT_UNITS / 2 * 8), rblk(320), blk(GM_THREADS);
   hipLaunchKernelGGL((k_gemm_mx<1, FP4, TALL>), dim3(G1), blk, lds, s, L, 2 * F, H, capacity, x, xs, offsets, w1p,
-                     w1s, act, act_s, part, (const int32_t*)nullptr);
+                     w1s, act, act_s, part, nullptr, (bf16_t*)nullptr);
   hipLaunchKernelGGL((k_mx_splitk_reduce<1, FP4, TALL>), rgrid, rblk, 0, s, L, 2 * F, H, capacity, G1, offsets,
-                     part, act, act_s);
+                     part, act, act_s, (const bf16_t*)nullptr, (bf16_t*)nullptr);
   hipLaunchKernelGGL((k_gemm_mx<0, FP4, TALL>), dim3(G2), blk, lds, s, L, H, F, capacity, act, act_s, offsets,
-                     w2p, w2s, (uint8_t*)y, (uint8_t*)nullptr, part, (const int32_t*)nullptr);
+                     w2p, w2s, (uint8_t*)y, (uint8_t*)nullptr, part, nullptr, (bf16_t*)nullptr);
   hipLaunchKernelGGL((k_mx_splitk_reduce<0, FP4, TALL>), rgrid, rblk, 0, s, L, H, F, capacity, G2, offsets, part,
-                     (uint8_t*)y, (uint8_t*)nullptr);
+                     (uint8_t*)y, (uint8_t*)nullptr, (const bf16_t*)nullptr, (bf16_t*)nullptr);
 }
 
 hipError_t launch_grouped_mlp_mx(int L, int H, int F, int64_t capacity, bool fp4, const uint8_t* x,
@@ -672,6 +757,69 @@ hipError_t launch_grouped_mlp_mx(int L, int H, int F, int64_t capacity, bool fp4
     launch_mx<false, true>(L, H, F, capacity, x, xs, offsets, w1p, w1s, w2p, w2s, act, act_s, part, y, s);
   else
     launch_mx<false, false>(L, H, F, capacity, x, xs, offsets, w1p, w1s, w2p, w2s, act, act_s, part, y, s);
+  return hipGetLastError();
+}
+
+// MXFP8 data gradient: row-wise MX of x_perm and d_y (along H), then
+// h = x_perm . W1 (EPI 3), d_h from d_a = d_y . W2^T (EPI 4, which also
+// MX-quantizes d_h along 2F) and d_x = d_h . W1^T (EPI 0), each followed by
+// its split-K reduce.
+template <bool TALL>
+static void launch_mx_backward(int L, int H, int F, int64_t capacity, const uint8_t* xq, const uint8_t* xqs,
+                               const int32_t* offsets, const uint8_t* w1p, const uint8_t* w1s, const uint8_t* w1t,
+                               const uint8_t* w1ts, const uint8_t* w2t, const uint8_t* w2ts, const uint8_t* dyq,
+                               const uint8_t* dyqs, bf16_t* hbuf, bf16_t* dhbuf, uint8_t* dhq, uint8_t* dhqs,
+                               float* part, bf16_t* dx, hipStream_t s) {
+  static bool attr_done = false;
+  if (!attr_done) {
+    (void)hipFuncSetAttribute((const void*)k_gemm_mx<0, false, TALL>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              160 * 1024);
+    (void)hipFuncSetAttribute((const void*)k_gemm_mx<3, false, TALL>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              160 * 1024);
+    (void)hipFuncSetAttribute((const void*)k_gemm_mx<4, false, TALL>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              160 * 1024);
+    attr_done = true;
+  }
+  const size_t lds = mx_lds_bytes(L, TALL);
+  auto grid = [&](int N) {
+    const int NT = (N + GM_BN - 1) / GM_BN;
+    const int64_t upper = ((capacity + GM_BM - 1) / GM_BM + L) * (int64_t)NT;
+    int64_t gsz = num_cus();
+    if (upper < gsz) gsz = upper;
+    return (int)(gsz > 0 ? gsz : 1);
+  };
+  const int G1 = grid(2 * F), G2 = grid(F), G3 = grid(H);
+  const dim3 rgrid(GEMM_SPLIT_UNITS / 2 * 8), rblk(320), blk(GM_THREADS);
+  hipLaunchKernelGGL((k_gemm_mx<3, false, TALL>), dim3(G1), blk, lds, s, L, 2 * F, H, capacity, xq, xqs, offsets,
+                     w1p, w1s, (uint8_t*)hbuf, (uint8_t*)nullptr, part, nullptr, (bf16_t*)nullptr);
+  hipLaunchKernelGGL((k_mx_splitk_reduce<3, false, TALL>), rgrid, rblk, 0, s, L, 2 * F, H, capacity, G1, offsets,
+                     part, (uint8_t*)hbuf, (uint8_t*)nullptr, (const bf16_t*)nullptr, (bf16_t*)nullptr);
+  hipLaunchKernelGGL((k_gemm_mx<4, false, TALL>), dim3(G2), blk, lds, s, L, F, H, capacity, dyq, dyqs, offsets,
+                     w2t, w2ts, dhq, dhqs, part, (const void*)hbuf, dhbuf);
+  hipLaunchKernelGGL((k_mx_splitk_reduce<4, false, TALL>), rgrid, rblk, 0, s, L, F, H, capacity, G2, offsets, part,
+                     dhq, dhqs, (const bf16_t*)hbuf, dhbuf);
+  hipLaunchKernelGGL((k_gemm_mx<0, false, TALL>), dim3(G3), blk, lds, s, L, H, 2 * F, capacity, dhq, dhqs, offsets,
+                     w1t, w1ts, (uint8_t*)dx, (uint8_t*)nullptr, part, nullptr, (bf16_t*)nullptr);
+  hipLaunchKernelGGL((k_mx_splitk_reduce<0, false, TALL>), rgrid, rblk, 0, s, L, H, 2 * F, capacity, G3, offsets,
+                     part, (uint8_t*)dx, (uint8_t*)nullptr, (const bf16_t*)nullptr, (bf16_t*)nullptr);
+}
+
+hipError_t launch_grouped_mlp_mx_backward(int L, int H, int F, int64_t capacity, const bf16_t* x,
+                                          const int32_t* offsets, const uint8_t* w1p, const uint8_t* w1s,
+                                          const uint8_t* w1t, const uint8_t* w1ts, const uint8_t* w2t,
+                                          const uint8_t* w2ts, const bf16_t* dy, uint8_t* xq, uint8_t* xqs,
+                                          uint8_t* dyq, uint8_t* dyqs, bf16_t* hbuf, bf16_t* dhbuf, uint8_t* dhq,
+                                          uint8_t* dhqs, float* part, bf16_t* dx, hipStream_t s) {
+  if (capacity == 0) return hipSuccess;
+  hipError_t e = launch_mx_quantize(capacity, H, x, offsets + L, xq, xqs, s);
+  if (e == hipSuccess) e = launch_mx_quantize(capacity, H, dy, offsets + L, dyq, dyqs, s);
+  if (e != hipSuccess) return e;
+  if (mx_lds_bytes(L, true) <= 160 * 1024)
+    launch_mx_backward<true>(L, H, F, capacity, xq, xqs, offsets, w1p, w1s, w1t, w1ts, w2t, w2ts, dyq, dyqs, hbuf,
+                             dhbuf, dhq, dhqs, part, dx, s);
+  else
+    launch_mx_backward<false>(L, H, F, capacity, xq, xqs, offsets, w1p, w1s, w1t, w1ts, w2t, w2ts, dyq, dyqs, hbuf,
+                              dhbuf, dhq, dhqs, part, dx, s);
   return hipGetLastError();
 }
 
@@ -700,9 +848,9 @@ hipError_t launch_grouped_mlp_mx_wgrad(int L, int H, int F, int64_t capacity, in
   };
   const dim3 blk(GM_THREADS);
   hipLaunchKernelGGL((k_gemm_mx<5, false, false>), dim3(grid(H, 2 * F)), blk, lds, s, L, 2 * F, 0, (int64_t)H, xa,
-                     xas, pk, dhb, dhbs, (uint8_t*)dW1, (uint8_t*)nullptr, (float*)nullptr, (const int32_t*)png);
+                     xas, pk, dhb, dhbs, (uint8_t*)dW1, (uint8_t*)nullptr, (float*)nullptr, (const void*)png, (bf16_t*)nullptr);
   hipLaunchKernelGGL((k_gemm_mx<5, false, false>), dim3(grid(F, H)), blk, lds, s, L, H, 0, (int64_t)F, aa, aas, pk,
-                     dyb, dybs, (uint8_t*)dW2, (uint8_t*)nullptr, (float*)nullptr, (const int32_t*)png);
+                     dyb, dybs, (uint8_t*)dW2, (uint8_t*)nullptr, (float*)nullptr, (const void*)png, (bf16_t*)nullptr);
   return hipGetLastError();
 }
 

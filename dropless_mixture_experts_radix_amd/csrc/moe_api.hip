@@ -193,8 +193,13 @@ size_t moe_prepared_weight_bytes(int L, int H, int F, int dtype, int which) {
     case 3: return mx ? n1 / H * (((size_t)H + 511) / 512) * 16 : 0;
     case 4: return mx ? n2 / F * (((size_t)F + 511) / 512) * 16 : 0;
     // the backward's bf16 panels: W1^T (ceil(H/256) panels over 2F), W2^T (ceil(F/256) panels over H)
-    case 5: return dtype == MOE_BF16 ? (size_t)L * (((size_t)H + 255) / 256 * 256) * 2 * F * 2 : 0;
-    case 6: return dtype == MOE_BF16 ? (size_t)L * (((size_t)F + 255) / 256 * 256) * H * 2 : 0;
+    case 5: return dtype == MOE_BF16 || dtype == MOE_MXFP8
+                       ? (size_t)L * (((size_t)H + 255) / 256 * 256) * 2 * F * (dtype == MOE_BF16 ? 2 : 1) : 0;
+    case 6: return dtype == MOE_BF16 || dtype == MOE_MXFP8
+                       ? (size_t)L * (((size_t)F + 255) / 256 * 256) * H * (dtype == MOE_BF16 ? 2 : 1) : 0;
+    // scales of the backward's MXFP8 panels
+    case 7: return dtype == MOE_MXFP8 ? (size_t)L * (((size_t)H + 255) / 256 * 256) * ((2 * (size_t)F + 511) / 512) * 16 : 0;
+    case 8: return dtype == MOE_MXFP8 ? (size_t)L * (((size_t)F + 255) / 256 * 256) * (((size_t)H + 511) / 512) * 16 : 0;
     default: return 0;
   }
 }
@@ -296,28 +301,44 @@ int moe_unpermute_combine(int T, int K, int H, int dtype, const void* y_perm, co
 // Data gradient of the grouped MLP
 // ---------------------------------------------------------------------------
 int moe_prepare_weights_backward(int L, int H, int F, int dtype, const void* w1, const void* w2, void* w1t,
-                                 void* w2t, void* stream) {
+                                 void* w2t, uint8_t* w1t_scales, uint8_t* w2t_scales, void* stream) {
   if (L < 1 || L > MOE_MAX_L || H <= 0 || F <= 0 || H % 128 || F % 128) return MOE_ERR_SHAPE;
-  if (dtype != MOE_BF16) return MOE_ERR_DTYPE;
+  if (dtype != MOE_BF16 && dtype != MOE_MXFP8) return MOE_ERR_DTYPE;
+  if (dtype == MOE_MXFP8 && (H % 256 || F % 256)) return MOE_ERR_SHAPE;  // groups of 4 64-wide k stages
   if (!w1 || !w2 || !w1t || !w2t) return MOE_ERR_NULL;
+  if (dtype == MOE_MXFP8 && (!w1t_scales || !w2t_scales)) return MOE_ERR_NULL;
   if (!aligned16(w1) || !aligned16(w2) || !aligned16(w1t) || !aligned16(w2t)) return MOE_ERR_ALIGN;
-  return launch_status(launch_prepare_weights_backward(L, H, F, w1, w2, w1t, w2t, (hipStream_t)stream));
+  return launch_status(launch_prepare_weights_backward(L, H, F, dtype, w1, w2, w1t, w2t, w1t_scales, w2t_scales,
+                                                       (hipStream_t)stream));
 }
 
-size_t moe_grouped_mlp_backward_workspace_bytes(int64_t capacity, int F, int dtype) {
-  if (capacity <= 0 || F <= 0 || dtype != MOE_BF16) return 256;
-  // h and d_h ([2F/32][capacity][32] bf16 each), then the split-K partials
-  return round_up(2 * round_up((size_t)capacity * 2 * F * 2, 256) + grouped_mlp_bf16_part_bytes(), 256);
+// MXFP8 data gradient: row-wise MX codes and scales of x_perm, d_y (C = H) and d_h (C = 2F)
+static size_t mx_rows_bytes(int64_t capacity, int C) {
+  return round_up((size_t)capacity * C, 256) + round_up((size_t)capacity * (C / 32), 256);
+}
+
+size_t moe_grouped_mlp_backward_workspace_bytes(int64_t capacity, int H, int F, int dtype) {
+  if (capacity <= 0 || H <= 0 || F <= 0 || (dtype != MOE_BF16 && dtype != MOE_MXFP8)) return 256;
+  // h and d_h ([2F/32][capacity][32] bf16 each), the split-K partials, then
+  // (MXFP8) the MX operands of x_perm, d_y and d_h
+  const size_t part = grouped_mlp_bf16_part_bytes() > grouped_mlp_mx_part_bytes() ? grouped_mlp_bf16_part_bytes()
+                                                                                  : grouped_mlp_mx_part_bytes();
+  size_t b = 2 * round_up((size_t)capacity * 2 * F * 2, 256) + round_up(part, 256);
+  if (dtype == MOE_MXFP8) b += 2 * mx_rows_bytes(capacity, H) + mx_rows_bytes(capacity, 2 * F);
+  return b;
 }
 
 int moe_grouped_mlp_backward_data(int L, int H, int F, int64_t capacity, int dtype, const void* x_perm,
-                                  const int32_t* offsets, const void* w1p, const void* w1t, const void* w2t,
-                                  const void* d_y_perm, void* d_x_perm, void* workspace, size_t workspace_bytes,
-                                  void* stream) {
+                                  const int32_t* offsets, const void* w1p, const uint8_t* w1p_scales,
+                                  const void* w1t, const uint8_t* w1t_scales, const void* w2t,
+                                  const uint8_t* w2t_scales, const void* d_y_perm, void* d_x_perm, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
   if (L < 1 || L > MOE_MAX_L || H <= 0 || F <= 0 || capacity < 0 || capacity > (int64_t)1 << 31)
     return MOE_ERR_SHAPE;
-  if (dtype != MOE_BF16) return MOE_ERR_DTYPE;
+  if (dtype != MOE_BF16 && dtype != MOE_MXFP8) return MOE_ERR_DTYPE;
   if (H % 128 || F % 128) return MOE_ERR_SHAPE;
+  if (dtype == MOE_MXFP8 && (H % 256 || F % 256)) return MOE_ERR_SHAPE;
+  if (dtype == MOE_MXFP8 && (!w1p_scales || !w1t_scales || !w2t_scales)) return MOE_ERR_NULL;
   // byte offsets of the k-blocked h / d_h buffers and of the rows stay within 31 bits
   if (capacity * (int64_t)(H > 2 * F ? H : 2 * F) * 2 > (int64_t)INT32_MAX) return MOE_ERR_SHAPE;
   if (!offsets || !w1p || !w1t || !w2t) return MOE_ERR_NULL;
@@ -325,11 +346,26 @@ int moe_grouped_mlp_backward_data(int L, int H, int F, int64_t capacity, int dty
   if (!aligned16(x_perm) || !aligned16(w1p) || !aligned16(w1t) || !aligned16(w2t) || !aligned16(d_y_perm) ||
       !aligned16(d_x_perm) || !aligned16(workspace))
     return MOE_ERR_ALIGN;
-  if (capacity > 0 && workspace_bytes < moe_grouped_mlp_backward_workspace_bytes(capacity, F, dtype))
+  if (capacity > 0 && workspace_bytes < moe_grouped_mlp_backward_workspace_bytes(capacity, H, F, dtype))
     return MOE_ERR_WORKSPACE;
   bf16_t* hbuf = (bf16_t*)workspace;
   bf16_t* dhbuf = (bf16_t*)((uint8_t*)workspace + round_up((size_t)capacity * 2 * F * 2, 256));
   float* part = (float*)((uint8_t*)workspace + 2 * round_up((size_t)capacity * 2 * F * 2, 256));
+  if (dtype == MOE_MXFP8) {
+    uint8_t* w = (uint8_t*)part + round_up(grouped_mlp_bf16_part_bytes() > grouped_mlp_mx_part_bytes()
+                                               ? grouped_mlp_bf16_part_bytes()
+                                               : grouped_mlp_mx_part_bytes(), 256);
+    uint8_t* xq = w;   w += round_up((size_t)capacity * H, 256);
+    uint8_t* xqs = w;  w += round_up((size_t)capacity * (H / 32), 256);
+    uint8_t* dyq = w;  w += round_up((size_t)capacity * H, 256);
+    uint8_t* dyqs = w; w += round_up((size_t)capacity * (H / 32), 256);
+    uint8_t* dhq = w;  w += round_up((size_t)capacity * 2 * F, 256);
+    uint8_t* dhqs = w;
+    return launch_status(launch_grouped_mlp_mx_backward(
+        L, H, F, capacity, (const bf16_t*)x_perm, offsets, (const uint8_t*)w1p, w1p_scales, (const uint8_t*)w1t,
+        w1t_scales, (const uint8_t*)w2t, w2t_scales, (const bf16_t*)d_y_perm, xq, xqs, dyq, dyqs, hbuf, dhbuf, dhq,
+        dhqs, part, (bf16_t*)d_x_perm, (hipStream_t)stream));
+  }
   return launch_status(launch_grouped_mlp_bf16_backward(L, H, F, capacity, (const bf16_t*)x_perm, offsets,
                                                         (const bf16_t*)w1p, (const bf16_t*)w1t, (const bf16_t*)w2t,
                                                         (const bf16_t*)d_y_perm, hbuf, dhbuf, part,
@@ -401,7 +437,7 @@ int moe_grouped_mlp_backward_weights(int L, int H, int F, int64_t capacity, int 
   if (!aligned16(x_perm) || !aligned16(d_y_perm) || !aligned16(data_workspace) || !aligned16(dW1) ||
       !aligned16(dW2) || !aligned16(workspace))
     return MOE_ERR_ALIGN;
-  if (capacity > 0 && (data_workspace_bytes < moe_grouped_mlp_backward_workspace_bytes(capacity, F, MOE_BF16) ||
+  if (capacity > 0 && (data_workspace_bytes < moe_grouped_mlp_backward_workspace_bytes(capacity, H, F, MOE_BF16) ||
                        workspace_bytes < moe_grouped_mlp_backward_weights_workspace_bytes(L, capacity, H, F, dtype)))
     return MOE_ERR_WORKSPACE;
   if (capacity == 0) return MOE_OK;

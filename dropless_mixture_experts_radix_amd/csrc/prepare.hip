@@ -124,10 +124,16 @@ hipError_t launch_prepare_weights(int L, int H, int F, int dtype, const void* w1
 // The backward's bf16 panels: W2^T (columns f of F, k = h of H) from W2
 // [F][H], and W1^T (columns h of H, k = j of 2F in natural order) from W1
 // [H][2F]; layout as MODE 1.
-hipError_t launch_prepare_weights_backward(int L, int H, int F, const void* w1, const void* w2, void* w1t,
-                                           void* w2t, hipStream_t s) {
+hipError_t launch_prepare_weights_backward(int L, int H, int F, int dtype, const void* w1, const void* w2,
+                                           void* w1t, void* w2t, uint8_t* w1ts, uint8_t* w2ts, hipStream_t s) {
   if (L == 0) return hipSuccess;
   const dim3 b(256);
+  if (dtype == MOE_MXFP8) {  // MODE 2 panels (E4M3 codes, E8M0 scales per 32 along k)
+    hipLaunchKernelGGL((k_prepare<2, true>), dim3((F + 255) / 256 * 8, H / 32, L), b, 0, s, H, F, 0, w2, w2t, w2ts);
+    hipLaunchKernelGGL((k_prepare<2, true>), dim3((H + 255) / 256 * 8, 2 * F / 32, L), b, 0, s, 2 * F, H, 0, w1,
+                       w1t, w1ts);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL((k_prepare<1, true>), dim3((F + 255) / 256 * 8, H / 32, L), b, 0, s, H, F, 0, w2, w2t,
                      (uint8_t*)nullptr);
   hipLaunchKernelGGL((k_prepare<1, true>), dim3((H + 255) / 256 * 8, 2 * F / 32, L), b, 0, s, 2 * F, H, 0, w1, w1t,

@@ -242,8 +242,9 @@ int moe_permute(int T, int H, int K, int E_global, int e0, int L, int64_t capaci
  *   F % 512 == 0.
  * Requires H % 32 == 0 and F % 32 == 0 (MOE_F32).  Byte sizes:
  * moe_prepared_weight_bytes(L, H, F, dtype, which) with which = 1 (W1p),
- * 2 (W2p), 3 (W1p scales), 4 (W2p scales), and for the backward's bf16
- * panels (moe_prepare_weights_backward) 5 (W1t), 6 (W2t).
+ * 2 (W2p), 3 (W1p scales), 4 (W2p scales), and for the backward's panels
+ * (moe_prepare_weights_backward) 5 (W1t), 6 (W2t), 7 (W1t scales), 8 (W2t
+ * scales).
  * ------------------------------------------------------------------------ */
 size_t moe_prepared_weight_bytes(int L, int H, int F, int dtype, int which);
 
@@ -320,21 +321,32 @@ int moe_unpermute_combine(int T, int K, int H, int dtype,
  *   (w1t: columns h of H, k = j of 2F in natural order, gate columns then up
  *   columns) and the W2^T panels (w2t: columns f of F, k = h of H), both
  *   bf16 [L][panel][k/32][256 rows][32 k], zero-padded to whole 256-row
- *   panels; sizes moe_prepared_weight_bytes(..., 5) and (..., 6).
+ *   panels; sizes moe_prepared_weight_bytes(..., 5) and (..., 6).  dtype
+ *   MOE_MXFP8 (H % 256 == 0, F % 256 == 0): the same panels as E4M3 codes and
+ *   E8M0 scales in the layout of moe_prepare_weights' MOE_MXFP8 (codes
+ *   [L][panel][k/64][256][64], scales [L][panel][ceil(k/512)][256][16] in
+ *   w1t_scales / w2t_scales, sizes (..., 7) and (..., 8)); NULL for bf16.
  * moe_grouped_mlp_backward_data: x_perm, d_y_perm, d_x_perm [capacity][H]
- *   bf16 device; offsets as moe_grouped_mlp; w1p = moe_prepare_weights' W1p
- *   (bf16); rows >= offsets[L] of d_x_perm are not written.  Workspace:
- *   moe_grouped_mlp_backward_workspace_bytes(capacity, F, MOE_BF16) bytes
- *   (h, d_h, split-K partials).  dtype MOE_BF16 only; H % 128 == 0,
- *   F % 128 == 0, capacity * max(H, 2F) * 2 < 2^31.
+ *   bf16 device; offsets as moe_grouped_mlp; w1p = moe_prepare_weights' W1p,
+ *   w1t / w2t = moe_prepare_weights_backward's panels, all of `dtype`; the
+ *   three scale pointers are NULL for MOE_BF16.  rows >= offsets[L] of
+ *   d_x_perm are not written.  Workspace:
+ *   moe_grouped_mlp_backward_workspace_bytes(capacity, H, F, dtype) bytes (h,
+ *   d_h k-blocked bf16 at its start, which the weight gradient reads; the
+ *   split-K partials; for MOE_MXFP8 the row-wise MX operands).  dtype
+ *   MOE_BF16 (H % 128 == 0, F % 128 == 0) or MOE_MXFP8 (H % 256 == 0,
+ *   F % 256 == 0: x_perm and d_y are MX-quantized along H, d_h is rounded to
+ *   bf16 and MX-quantized along 2F in the GEMM that forms it; fp32
+ *   accumulation); capacity * max(H, 2F) * 2 < 2^31.
  * ------------------------------------------------------------------------ */
 int moe_prepare_weights_backward(int L, int H, int F, int dtype, const void* w1, const void* w2, void* w1t,
-                                 void* w2t, void* stream);
-size_t moe_grouped_mlp_backward_workspace_bytes(int64_t capacity, int F, int dtype);
+                                 void* w2t, uint8_t* w1t_scales, uint8_t* w2t_scales, void* stream);
+size_t moe_grouped_mlp_backward_workspace_bytes(int64_t capacity, int H, int F, int dtype);
 int moe_grouped_mlp_backward_data(int L, int H, int F, int64_t capacity, int dtype, const void* x_perm,
-                                  const int32_t* offsets, const void* w1p, const void* w1t, const void* w2t,
-                                  const void* d_y_perm, void* d_x_perm, void* workspace, size_t workspace_bytes,
-                                  void* stream);
+                                  const int32_t* offsets, const void* w1p, const uint8_t* w1p_scales,
+                                  const void* w1t, const uint8_t* w1t_scales, const void* w2t,
+                                  const uint8_t* w2t_scales, const void* d_y_perm, void* d_x_perm, void* workspace,
+                                  size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
  * Weight gradient of the grouped SwiGLU MLP (bf16 or MXFP8 operands, fp32

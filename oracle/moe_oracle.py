@@ -706,7 +706,12 @@ def grouped_mlp_backward_data(x_perm, offsets, W1, W2, d_y, dtype):
     d_x = d_h . W1[e]^T with d_h = swiglu'(h, d_a), d_a = d_y . W2[e]^T and
     h = X . W1[e] recomputed.  Rounding points of the bf16 path: h and d_h
     are stored as bf16 (d_a is not stored), d_x is bf16; "f64" rounds
-    nothing.  Returns d_x over rows [0, N)."""
+    nothing.  "mxfp8": every contraction takes MX (E4M3) operands blocked
+    along its contraction dimension, as the forward's (bpdata article,
+    "Optimization 1: Grouped GEMM", MXFP8 block scaling): X and W1[e]'s
+    columns along H for h; d_y and W2[e]'s rows along H for d_a; d_h (after
+    its bf16 rounding) and W1[e]'s rows along 2F for d_x.  Returns d_x over
+    rows [0, N)."""
     x_perm = np.asarray(x_perm, np.float64)
     d_y = np.asarray(d_y, np.float64)
     N = int(offsets[-1])
@@ -720,6 +725,13 @@ def grouped_mlp_backward_data(x_perm, offsets, W1, W2, d_y, dtype):
         W1e = np.asarray(W1[e], np.float64)
         W2e = np.asarray(W2[e], np.float64)
         F = W2e.shape[0]
+        if dtype == "mxfp8":
+            q = lambda V: mx_dequantize_rows(*mx_quantize_rows(V))  # MX round trip along the last axis
+            h = bf16_round(q(x_perm[lo:hi]) @ q(W1e.T).T)
+            d_a = q(d_y[lo:hi]) @ q(W2e).T
+            d_h = bf16_round(swiglu_backward(h, d_a, F))
+            out[lo:hi] = bf16_round(q(d_h) @ q(W1e).T)
+            continue
         h = rnd(x_perm[lo:hi] @ W1e)
         d_a = d_y[lo:hi] @ W2e.T
         d_h = rnd(swiglu_backward(h, d_a, F))

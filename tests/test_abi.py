@@ -111,6 +111,21 @@ def test_backward_validation():
     assert L.moe_route_backward(4, 8, 2, 0, 0.0, P, P, P, None, None, P, None) == 2    # scale
     assert L.moe_route_backward(4, 8, 2, 0, 1.0, P, None, P, None, None, P, None) == 1  # softmax needs probs
     assert L.moe_route_backward(4, 8, 2, 1, 1.0, P, P, P, None, None, P, None) == 1    # sigmoid needs logits
+    # backward panels: (L, H, F, dtype, w1, w2, w1t, w2t, w1t_s, w2t_s, stream)
+    assert L.moe_prepare_weights_backward(2, 256, 128, 2, P, P, P, P, P, P, None) == 2   # MXFP8: F % 256
+    assert L.moe_prepare_weights_backward(2, 256, 256, 2, P, P, P, P, None, P, None) == 1  # MXFP8 needs scales
+    assert L.moe_prepare_weights_backward(2, 256, 256, 3, P, P, P, P, P, P, None) == 4   # MXFP4: no panels
+    # data gradient: (L, H, F, cap, dtype, x, offs, w1p, w1p_s, w1t, w1t_s, w2t, w2t_s, d_y, d_x, ws, wsb, stream)
+    dg = lambda dt, H=256, F=256, s=P, wsb=1 << 30: L.moe_grouped_mlp_backward_data(
+        2, H, F, 64, dt, P, P, P, s, P, s, P, s, P, P, P, wsb, None)
+    assert dg(3) == 4                       # MXFP4
+    assert dg(2, F=128) == 2                # MXFP8: F % 256
+    assert dg(2, s=None) == 1               # MXFP8 needs the scales
+    assert dg(2, wsb=L.moe_grouped_mlp_backward_workspace_bytes(64, 256, 256, 2) - 1) == 5
+    assert (L.moe_grouped_mlp_backward_workspace_bytes(64, 256, 256, 2) >
+            L.moe_grouped_mlp_backward_workspace_bytes(64, 256, 256, 1))
+    assert L.moe_prepared_weight_bytes(2, 256, 512, 2, 7) == 2 * 256 * 2 * 16   # W1t scales
+    assert L.moe_prepared_weight_bytes(2, 256, 512, 2, 8) == 2 * 512 * 1 * 16   # W2t scales
 
 
 def test_permute_validation():

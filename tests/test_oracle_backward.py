@@ -243,3 +243,55 @@ def test_mlp_backward_weights_mxfp8_close_to_bf16_and_exact_on_grid():
     grid = rng.integers(-8, 9, size=(50, 16)).astype(np.float64)
     grid[0] = grid[32] = 8.0
     np.testing.assert_array_equal(O._mx_columns_roundtrip(grid), grid)
+
+
+def test_mlp_backward_data_mxfp8_large_gate_closed_form():
+    """The MXFP8 data gradient on operands that every MX quantization keeps
+    exactly: one-hot rows of x (+1) and d_y (+-1), W1's gate columns all 16,
+    its up columns and W2 in {-2..2}.  Then g = 16 and u, d_a are small
+    integers; silu(16) and silu'(16) equal 16 and 1 to within 2e-6, below half
+    a bf16 step of the stored d_h, so d_h = [d_a u, 16 d_a] exactly and
+    d_x = bf16(d_a u . W1_gate^T + 16 d_a . W1_up^T) in integers; the bf16
+    path gives the same."""
+    rng = np.random.default_rng(44)
+    H, F = 64, 32
+    counts = [5, 0, 9]
+    off = np.concatenate([[0], np.cumsum(counts)])
+    N = int(off[-1])
+    W1 = [np.concatenate([np.full((H, F), 16.0), rng.integers(-2, 3, (H, F)).astype(np.float64)], axis=1)
+          for _ in counts]
+    W2 = [rng.integers(-2, 3, (F, H)).astype(np.float64) for _ in counts]
+    x = np.zeros((N, H))
+    x[np.arange(N), rng.integers(0, H, N)] = 1.0
+    dy = np.zeros((N, H))
+    dy[np.arange(N), rng.integers(0, H, N)] = rng.choice([-1.0, 1.0], N)
+    got = O.grouped_mlp_backward_data(x, off, W1, W2, dy, "mxfp8")
+    want = np.zeros((N, H))
+    for e in range(len(counts)):
+        lo, hi = off[e], off[e + 1]
+        u = x[lo:hi] @ W1[e][:, F:]
+        d_a = dy[lo:hi] @ W2[e].T
+        want[lo:hi] = O.bf16_round((d_a * u) @ W1[e][:, :F].T + (16.0 * d_a) @ W1[e][:, F:].T)
+    np.testing.assert_array_equal(got, want)
+    np.testing.assert_array_equal(O.grouped_mlp_backward_data(x, off, W1, W2, dy, "bf16"), want)
+
+
+def test_mlp_backward_data_mxfp8_within_mx_rounding_of_f64():
+    """General operands: the MXFP8 data gradient stays within the E4M3
+    rounding of the float64 chain rule (six quantized operands, each with an
+    RMS relative error of about 2^-4 / sqrt(3): about sqrt(6) * 0.036 = 0.09
+    in all; bound 0.12), and a transposed W2 (a plausible mistake) does not."""
+    rng = np.random.default_rng(45)
+    H, F = 64, 64
+    counts = [37, 0, 64]
+    off = np.concatenate([[0], np.cumsum(counts)])
+    W1 = [O.bf16_round(rng.standard_normal((H, 2 * F)) * 0.2) for _ in counts]
+    W2 = [O.bf16_round(rng.standard_normal((F, H)) * 0.2) for _ in counts]
+    x = O.bf16_round(rng.standard_normal((off[-1], H)))
+    dy = O.bf16_round(rng.standard_normal((off[-1], H)))
+    ref = O.grouped_mlp_backward_data(x, off, W1, W2, dy, "f64")
+    got = O.grouped_mlp_backward_data(x, off, W1, W2, dy, "mxfp8")
+    rel = np.linalg.norm(got - ref) / np.linalg.norm(ref)
+    assert rel <= 0.12
+    bad = O.grouped_mlp_backward_data(x, off, W1, [w.T.copy() for w in W2], dy, "f64")
+    assert np.linalg.norm(bad - ref) / np.linalg.norm(ref) > 0.5
