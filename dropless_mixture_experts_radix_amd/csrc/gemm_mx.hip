@@ -32,13 +32,11 @@
 // The data gradient (MXFP8):
 // EPI 3: h = x_perm . W1 recomputed, stored bf16 k-blocked [N/32][capacity][32]
 //        in the prepared (gate/up interleaved) column order.
-// EPI 4: A = d_y (row-wise MX along H), B = the MX W2^T panels (N = F
-//        columns): acc = d_a; with g, u read from `aux` (EPI 3's output) the
-//        epilogue forms d_h = [d_a u silu'(g), d_a silu(g)] (natural column
-//        order, gates then ups), rounds it to bf16, stores that k-blocked
-//        [2N/32][capacity][32] in `aux_o` (the weight gradient's input) and
-//        its row-wise MX codes [capacity][2N] and scales [capacity][2N/32] in
-//        out / out_s (the A operand of d_x = d_h . W1^T, an EPI 0 GEMM).
+// EPI 6: A = d_y (row-wise MX along H), B = the MX W2^T panels (N = F
+//        columns): d_a stored fp32 row-major [capacity][N]; k_swiglu_bwd_mx
+//        then forms d_h from it and h (a fused epilogue that read g and u of
+//        every element from memory was latency bound: at the kernel's
+//        register budget those loads went one at a time).
 #include "gemm_common.h"
 
 namespace moe {
@@ -79,54 +77,6 @@ __device__ __forceinline__ uint32_t max_half_wave(uint32_t v) {
   v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false));  // row_half_mirror
   v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xF, 0xF, false));  // row_mirror
   return max(v, (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x401F));                 // lane ^ 16
-}
-
-// EPI 4 epilogue of row blocks [i0 + II, i0 + NI) (see mx_store_tile).
-template <int NI, int II>
-__device__ __forceinline__ void mx_epi4_blocks(const f32x16 (&acc)[NI][2], int i0, int msub, const TileInfo& ti,
-                                               int N, int wm, int wn, int g, int r32, uint8_t* __restrict__ out,
-                                               uint8_t* __restrict__ out_s, int64_t capacity,
-                                               const bf16_t* __restrict__ aux, bf16_t* __restrict__ aux_o) {
-  if constexpr (II < NI) {
-    if (i0 + II < msub) {  // uniform over the wavefront
-      const int N2 = 2 * N;
-      const int col0 = ti.nt * GM_BN;
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int row = wm * 128 + (i0 + II) * 32 + 8 * (v >> 2) + 4 * g + (v & 3);
-        const bool live = row < ti.rows;  // the same for the 32 lanes of a half
-        const long grow = ti.row0 + row;
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const int f = col0 + wn * 64 + j * 32 + r32;  // column of d_a
-          const bool ok = live && f < N;
-          const int pg = (f >> 5) * 64 + (f & 31);      // gate's prepared column; up's is pg + 32
-          float gt = 0.0f, up = 0.0f;
-          if (ok) {
-            gt = bf16_to_f32(aux[((long)(pg >> 5) * capacity + grow) * 32 + (f & 31)]);
-            up = bf16_to_f32(aux[((long)((pg >> 5) + 1) * capacity + grow) * 32 + (f & 31)]);
-          }
-          const float da = acc[II][j][v];
-          const float sg = 1.0f / (1.0f + expf(-gt));
-          const uint32_t dg = f32_to_bf16(da * up * sg * (1.0f + gt * (1.0f - sg)));
-          const uint32_t du = f32_to_bf16(da * gt * sg);
-          const int Eg = mx_scale_exp(max_half_wave(dg & 0x7fffu));
-          const int Eu = mx_scale_exp(max_half_wave(du & 0x7fffu));
-          if (ok) {
-            aux_o[((long)(f >> 5) * capacity + grow) * 32 + (f & 31)] = (bf16_t)dg;
-            aux_o[((long)((N + f) >> 5) * capacity + grow) * 32 + (f & 31)] = (bf16_t)du;
-            out[grow * N2 + f] = (uint8_t)mx_e4m3(dg, Eg);
-            out[grow * N2 + N + f] = (uint8_t)mx_e4m3(du, Eu);
-            if (r32 == 0) {
-              out_s[grow * (N2 >> 5) + (f >> 5)] = (uint8_t)(Eg + 127);
-              out_s[grow * (N2 >> 5) + ((N + f) >> 5)] = (uint8_t)(Eu + 127);
-            }
-          }
-        }
-      }
-    }
-    mx_epi4_blocks<NI, II + 1>(acc, i0, msub, ti, N, wm, wn, g, r32, out, out_s, capacity, aux, aux_o);
-  }
 }
 
 // Epilogue of row blocks [i0, i0+NI) of one wavefront's 128 x 64 part of a
@@ -177,11 +127,23 @@ __device__ __forceinline__ void mx_store_tile(const f32x16 (&acc)[NI][2], int i0
         }
       }
     }
-  } else if (EPI == 4) {
-    // one row block at a time with a constant index into acc (a loop over the
-    // blocks is not unrolled at this body size, and a variable index would put
-    // acc in scratch memory for the whole kernel)
-    mx_epi4_blocks<NI, 0>(acc, i0, msub, ti, N, wm, wn, g, r32, out, out_s, capacity, aux, aux_o);
+  } else if (EPI == 6) {
+    float* da = (float*)out;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      if (i0 + i >= msub) continue;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int row = wm * 128 + (i0 + i) * 32 + 8 * (v >> 2) + 4 * g + (v & 3);
+        if (row >= ti.rows) continue;
+        const long grow = ti.row0 + row;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int col = col0 + wn * 64 + j * 32 + r32;
+          if (col < N) da[grow * N + col] = acc[i][j][v];
+        }
+      }
+    }
   } else {
     const int Fh = N >> 1;
     const int jcol = (col0 >> 1) + wn * 32 + r32;  // this lane's column of a
@@ -760,23 +722,69 @@ hipError_t launch_grouped_mlp_mx(int L, int H, int F, int64_t capacity, bool fp4
   return hipGetLastError();
 }
 
+// d_h from d_a (fp32 [capacity][F]) and h (bf16 k-blocked [2F/32][capacity][32],
+// gate/up chunks of 32 interleaved): d_h = [d_a u silu'(g), d_a silu(g)]
+// rounded to bf16, stored k-blocked [2F/32][capacity][32] in natural column
+// order (gates, then ups) in dh, and MX-quantized along 2F (one 32-column
+// chunk = one block) into codes [capacity][2F] and scales [capacity][2F/32].
+// Each half wavefront handles one (row, 32-column chunk of F); the rows are
+// those below *n_rows.
+__global__ __launch_bounds__(256) void k_swiglu_bwd_mx(int F, int64_t capacity, const int32_t* __restrict__ n_rows,
+                                                       const float* __restrict__ da, const bf16_t* __restrict__ h,
+                                                       bf16_t* __restrict__ dh, uint8_t* __restrict__ codes,
+                                                       uint8_t* __restrict__ scales) {
+  const int64_t rows = min((int64_t)*n_rows, capacity);
+  const int C = F >> 5;                       // chunks per row
+  const int64_t items = rows * C;
+  const int r = threadIdx.x & 31;
+  const int64_t step = (int64_t)gridDim.x * 8;
+  // the loop bound is the same for both halves of a wavefront (pairs of items)
+  for (int64_t base = (int64_t)blockIdx.x * 8 + (threadIdx.x >> 6) * 2; base < items; base += step) {
+    const int64_t it = base + ((threadIdx.x >> 5) & 1);
+    const bool ok = it < items;
+    const int64_t row = ok ? it / C : 0;
+    const int c = ok ? (int)(it - row * C) : 0;
+    float a = 0.0f, gt = 0.0f, up = 0.0f;
+    if (ok) {
+      a = da[row * F + c * 32 + r];
+      gt = bf16_to_f32(h[((int64_t)(2 * c) * capacity + row) * 32 + r]);
+      up = bf16_to_f32(h[((int64_t)(2 * c + 1) * capacity + row) * 32 + r]);
+    }
+    const float sg = 1.0f / (1.0f + expf(-gt));
+    const uint32_t dg = f32_to_bf16(a * up * sg * (1.0f + gt * (1.0f - sg)));
+    const uint32_t du = f32_to_bf16(a * gt * sg);
+    const int Eg = mx_scale_exp(max_half_wave(dg & 0x7fffu));
+    const int Eu = mx_scale_exp(max_half_wave(du & 0x7fffu));
+    if (ok) {
+      dh[((int64_t)c * capacity + row) * 32 + r] = (bf16_t)dg;
+      dh[((int64_t)(C + c) * capacity + row) * 32 + r] = (bf16_t)du;
+      codes[row * 2 * F + c * 32 + r] = (uint8_t)mx_e4m3(dg, Eg);
+      codes[row * 2 * F + F + c * 32 + r] = (uint8_t)mx_e4m3(du, Eu);
+      if (r == 0) {
+        scales[row * (F >> 4) + c] = (uint8_t)(Eg + 127);
+        scales[row * (F >> 4) + C + c] = (uint8_t)(Eu + 127);
+      }
+    }
+  }
+}
+
 // MXFP8 data gradient: row-wise MX of x_perm and d_y (along H), then
-// h = x_perm . W1 (EPI 3), d_h from d_a = d_y . W2^T (EPI 4, which also
-// MX-quantizes d_h along 2F) and d_x = d_h . W1^T (EPI 0), each followed by
-// its split-K reduce.
+// h = x_perm . W1 (EPI 3), d_a = d_y . W2^T (EPI 6) and from it d_h (bf16,
+// and MX along 2F: k_swiglu_bwd_mx), then d_x = d_h . W1^T (EPI 0); each GEMM
+// followed by its split-K reduce.
 template <bool TALL>
 static void launch_mx_backward(int L, int H, int F, int64_t capacity, const uint8_t* xq, const uint8_t* xqs,
                                const int32_t* offsets, const uint8_t* w1p, const uint8_t* w1s, const uint8_t* w1t,
                                const uint8_t* w1ts, const uint8_t* w2t, const uint8_t* w2ts, const uint8_t* dyq,
                                const uint8_t* dyqs, bf16_t* hbuf, bf16_t* dhbuf, uint8_t* dhq, uint8_t* dhqs,
-                               float* part, bf16_t* dx, hipStream_t s) {
+                               float* da, float* part, bf16_t* dx, hipStream_t s) {
   static bool attr_done = false;
   if (!attr_done) {
     (void)hipFuncSetAttribute((const void*)k_gemm_mx<0, false, TALL>, hipFuncAttributeMaxDynamicSharedMemorySize,
                               160 * 1024);
     (void)hipFuncSetAttribute((const void*)k_gemm_mx<3, false, TALL>, hipFuncAttributeMaxDynamicSharedMemorySize,
                               160 * 1024);
-    (void)hipFuncSetAttribute((const void*)k_gemm_mx<4, false, TALL>, hipFuncAttributeMaxDynamicSharedMemorySize,
+    (void)hipFuncSetAttribute((const void*)k_gemm_mx<6, false, TALL>, hipFuncAttributeMaxDynamicSharedMemorySize,
                               160 * 1024);
     attr_done = true;
   }
@@ -794,10 +802,12 @@ static void launch_mx_backward(int L, int H, int F, int64_t capacity, const uint
                      w1p, w1s, (uint8_t*)hbuf, (uint8_t*)nullptr, part, nullptr, (bf16_t*)nullptr);
   hipLaunchKernelGGL((k_mx_splitk_reduce<3, false, TALL>), rgrid, rblk, 0, s, L, 2 * F, H, capacity, G1, offsets,
                      part, (uint8_t*)hbuf, (uint8_t*)nullptr, (const bf16_t*)nullptr, (bf16_t*)nullptr);
-  hipLaunchKernelGGL((k_gemm_mx<4, false, TALL>), dim3(G2), blk, lds, s, L, F, H, capacity, dyq, dyqs, offsets,
-                     w2t, w2ts, dhq, dhqs, part, (const void*)hbuf, dhbuf);
-  hipLaunchKernelGGL((k_mx_splitk_reduce<4, false, TALL>), rgrid, rblk, 0, s, L, F, H, capacity, G2, offsets, part,
-                     dhq, dhqs, (const bf16_t*)hbuf, dhbuf);
+  hipLaunchKernelGGL((k_gemm_mx<6, false, TALL>), dim3(G2), blk, lds, s, L, F, H, capacity, dyq, dyqs, offsets,
+                     w2t, w2ts, (uint8_t*)da, (uint8_t*)nullptr, part, nullptr, (bf16_t*)nullptr);
+  hipLaunchKernelGGL((k_mx_splitk_reduce<6, false, TALL>), rgrid, rblk, 0, s, L, F, H, capacity, G2, offsets, part,
+                     (uint8_t*)da, (uint8_t*)nullptr, (const bf16_t*)nullptr, (bf16_t*)nullptr);
+  hipLaunchKernelGGL(k_swiglu_bwd_mx, dim3(num_cus() * 16), dim3(256), 0, s, F, capacity, offsets + L, da, hbuf,
+                     dhbuf, dhq, dhqs);
   hipLaunchKernelGGL((k_gemm_mx<0, false, TALL>), dim3(G3), blk, lds, s, L, H, 2 * F, capacity, dhq, dhqs, offsets,
                      w1t, w1ts, (uint8_t*)dx, (uint8_t*)nullptr, part, nullptr, (bf16_t*)nullptr);
   hipLaunchKernelGGL((k_mx_splitk_reduce<0, false, TALL>), rgrid, rblk, 0, s, L, H, 2 * F, capacity, G3, offsets,
@@ -809,17 +819,17 @@ hipError_t launch_grouped_mlp_mx_backward(int L, int H, int F, int64_t capacity,
                                           const uint8_t* w1t, const uint8_t* w1ts, const uint8_t* w2t,
                                           const uint8_t* w2ts, const bf16_t* dy, uint8_t* xq, uint8_t* xqs,
                                           uint8_t* dyq, uint8_t* dyqs, bf16_t* hbuf, bf16_t* dhbuf, uint8_t* dhq,
-                                          uint8_t* dhqs, float* part, bf16_t* dx, hipStream_t s) {
+                                          uint8_t* dhqs, float* da, float* part, bf16_t* dx, hipStream_t s) {
   if (capacity == 0) return hipSuccess;
   hipError_t e = launch_mx_quantize(capacity, H, x, offsets + L, xq, xqs, s);
   if (e == hipSuccess) e = launch_mx_quantize(capacity, H, dy, offsets + L, dyq, dyqs, s);
   if (e != hipSuccess) return e;
   if (mx_lds_bytes(L, true) <= 160 * 1024)
     launch_mx_backward<true>(L, H, F, capacity, xq, xqs, offsets, w1p, w1s, w1t, w1ts, w2t, w2ts, dyq, dyqs, hbuf,
-                             dhbuf, dhq, dhqs, part, dx, s);
+                             dhbuf, dhq, dhqs, da, part, dx, s);
   else
     launch_mx_backward<false>(L, H, F, capacity, xq, xqs, offsets, w1p, w1s, w1t, w1ts, w2t, w2ts, dyq, dyqs, hbuf,
-                              dhbuf, dhq, dhqs, part, dx, s);
+                              dhbuf, dhq, dhqs, da, part, dx, s);
   return hipGetLastError();
 }
 

@@ -324,7 +324,8 @@ size_t moe_grouped_mlp_backward_workspace_bytes(int64_t capacity, int H, int F, 
   const size_t part = grouped_mlp_bf16_part_bytes() > grouped_mlp_mx_part_bytes() ? grouped_mlp_bf16_part_bytes()
                                                                                   : grouped_mlp_mx_part_bytes();
   size_t b = 2 * round_up((size_t)capacity * 2 * F * 2, 256) + round_up(part, 256);
-  if (dtype == MOE_MXFP8) b += 2 * mx_rows_bytes(capacity, H) + mx_rows_bytes(capacity, 2 * F);
+  if (dtype == MOE_MXFP8)  // (and d_a, fp32 [capacity][F])
+    b += 2 * mx_rows_bytes(capacity, H) + mx_rows_bytes(capacity, 2 * F) + round_up((size_t)capacity * F * 4, 256);
   return b;
 }
 
@@ -360,11 +361,12 @@ int moe_grouped_mlp_backward_data(int L, int H, int F, int64_t capacity, int dty
     uint8_t* dyq = w;  w += round_up((size_t)capacity * H, 256);
     uint8_t* dyqs = w; w += round_up((size_t)capacity * (H / 32), 256);
     uint8_t* dhq = w;  w += round_up((size_t)capacity * 2 * F, 256);
-    uint8_t* dhqs = w;
+    uint8_t* dhqs = w; w += round_up((size_t)capacity * (2 * F / 32), 256);
+    float* da = (float*)w;
     return launch_status(launch_grouped_mlp_mx_backward(
         L, H, F, capacity, (const bf16_t*)x_perm, offsets, (const uint8_t*)w1p, w1p_scales, (const uint8_t*)w1t,
         w1t_scales, (const uint8_t*)w2t, w2t_scales, (const bf16_t*)d_y_perm, xq, xqs, dyq, dyqs, hbuf, dhbuf, dhq,
-        dhqs, part, (bf16_t*)d_x_perm, (hipStream_t)stream));
+        dhqs, da, part, (bf16_t*)d_x_perm, (hipStream_t)stream));
   }
   return launch_status(launch_grouped_mlp_bf16_backward(L, H, F, capacity, (const bf16_t*)x_perm, offsets,
                                                         (const bf16_t*)w1p, (const bf16_t*)w1t, (const bf16_t*)w2t,

@@ -220,7 +220,7 @@ hipError_t launch_grouped_mlp_mx_backward(int L, int H, int F, int64_t capacity,
                                           const uint8_t* w1t, const uint8_t* w1ts, const uint8_t* w2t,
                                           const uint8_t* w2ts, const bf16_t* dy, uint8_t* xq, uint8_t* xqs,
                                           uint8_t* dyq, uint8_t* dyqs, bf16_t* hbuf, bf16_t* dhbuf, uint8_t* dhq,
-                                          uint8_t* dhqs, float* part, bf16_t* dx, hipStream_t s);
+                                          uint8_t* dhqs, float* da, float* part, bf16_t* dx, hipStream_t s);
 hipError_t launch_prepare_weights_backward(int L, int H, int F, int dtype, const void* w1, const void* w2,
                                            void* w1t, void* w2t, uint8_t* w1ts, uint8_t* w2ts, hipStream_t s);
 hipError_t launch_mx_columns_grouped(int L, int64_t capacity, int C, int nbmax, const bf16_t* in,
