@@ -727,43 +727,54 @@ hipError_t launch_grouped_mlp_mx(int L, int H, int F, int64_t capacity, bool fp4
 // rounded to bf16, stored k-blocked [2F/32][capacity][32] in natural column
 // order (gates, then ups) in dh, and MX-quantized along 2F (one 32-column
 // chunk = one block) into codes [capacity][2F] and scales [capacity][2F/32].
-// Each half wavefront handles one (row, 32-column chunk of F); the rows are
-// those below *n_rows.
+// One wavefront per (row, 256 columns of F), 4 columns per lane: 8 lanes
+// share a chunk (block amax by xor shuffles within the 8), d_a is read as
+// 16-byte pieces and the codes written as 4-byte words.  F % 256 == 0; the
+// rows are those below *n_rows.
 __global__ __launch_bounds__(256) void k_swiglu_bwd_mx(int F, int64_t capacity, const int32_t* __restrict__ n_rows,
                                                        const float* __restrict__ da, const bf16_t* __restrict__ h,
                                                        bf16_t* __restrict__ dh, uint8_t* __restrict__ codes,
                                                        uint8_t* __restrict__ scales) {
   const int64_t rows = min((int64_t)*n_rows, capacity);
   const int C = F >> 5;                       // chunks per row
-  const int64_t items = rows * C;
-  const int r = threadIdx.x & 31;
-  const int64_t step = (int64_t)gridDim.x * 8;
-  // the loop bound is the same for both halves of a wavefront (pairs of items)
-  for (int64_t base = (int64_t)blockIdx.x * 8 + (threadIdx.x >> 6) * 2; base < items; base += step) {
-    const int64_t it = base + ((threadIdx.x >> 5) & 1);
-    const bool ok = it < items;
-    const int64_t row = ok ? it / C : 0;
-    const int c = ok ? (int)(it - row * C) : 0;
-    float a = 0.0f, gt = 0.0f, up = 0.0f;
-    if (ok) {
-      a = da[row * F + c * 32 + r];
-      gt = bf16_to_f32(h[((int64_t)(2 * c) * capacity + row) * 32 + r]);
-      up = bf16_to_f32(h[((int64_t)(2 * c + 1) * capacity + row) * 32 + r]);
+  const int NG = F >> 8;                      // 256-column groups per row
+  const int64_t items = rows * NG;
+  const int l = threadIdx.x & 63, q = l & 7;
+  const int64_t step = (int64_t)gridDim.x * 4;
+  for (int64_t it = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); it < items; it += step) {  // uniform per wave
+    const int64_t row = it / NG;
+    const int c = (int)(it - row * NG) * 8 + (l >> 3);   // this lane's chunk
+    const int f0 = c * 32 + q * 4;                        // its first column
+    const f32x4 a = *(const f32x4*)(da + row * F + f0);
+    const uint2 gb = *(const uint2*)(h + ((int64_t)(2 * c) * capacity + row) * 32 + q * 4);
+    const uint2 ub = *(const uint2*)(h + ((int64_t)(2 * c + 1) * capacity + row) * 32 + q * 4);
+    uint32_t dg[4], du[4], mg = 0, mu = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t gw = k < 2 ? gb.x : gb.y, uw = k < 2 ? ub.x : ub.y;
+      const float gt = __uint_as_float((k & 1) ? (gw & 0xffff0000u) : (gw << 16));
+      const float up = __uint_as_float((k & 1) ? (uw & 0xffff0000u) : (uw << 16));
+      const float sg = 1.0f / (1.0f + expf(-gt));
+      dg[k] = f32_to_bf16(a[k] * up * sg * (1.0f + gt * (1.0f - sg)));
+      du[k] = f32_to_bf16(a[k] * gt * sg);
+      mg = max(mg, dg[k] & 0x7fffu);
+      mu = max(mu, du[k] & 0x7fffu);
     }
-    const float sg = 1.0f / (1.0f + expf(-gt));
-    const uint32_t dg = f32_to_bf16(a * up * sg * (1.0f + gt * (1.0f - sg)));
-    const uint32_t du = f32_to_bf16(a * gt * sg);
-    const int Eg = mx_scale_exp(max_half_wave(dg & 0x7fffu));
-    const int Eu = mx_scale_exp(max_half_wave(du & 0x7fffu));
-    if (ok) {
-      dh[((int64_t)c * capacity + row) * 32 + r] = (bf16_t)dg;
-      dh[((int64_t)(C + c) * capacity + row) * 32 + r] = (bf16_t)du;
-      codes[row * 2 * F + c * 32 + r] = (uint8_t)mx_e4m3(dg, Eg);
-      codes[row * 2 * F + F + c * 32 + r] = (uint8_t)mx_e4m3(du, Eu);
-      if (r == 0) {
-        scales[row * (F >> 4) + c] = (uint8_t)(Eg + 127);
-        scales[row * (F >> 4) + C + c] = (uint8_t)(Eu + 127);
-      }
+#pragma unroll
+    for (int m = 1; m < 8; m <<= 1) {  // the 8 lanes of the chunk
+      mg = max(mg, (uint32_t)__shfl_xor((int)mg, m));
+      mu = max(mu, (uint32_t)__shfl_xor((int)mu, m));
+    }
+    const int Eg = mx_scale_exp(mg), Eu = mx_scale_exp(mu);
+    const uint32_t pg0 = dg[0] | (dg[1] << 16), pg1 = dg[2] | (dg[3] << 16);
+    const uint32_t pu0 = du[0] | (du[1] << 16), pu1 = du[2] | (du[3] << 16);
+    *(uint2*)(dh + ((int64_t)c * capacity + row) * 32 + q * 4) = make_uint2(pg0, pg1);
+    *(uint2*)(dh + ((int64_t)(C + c) * capacity + row) * 32 + q * 4) = make_uint2(pu0, pu1);
+    *(uint32_t*)(codes + row * 2 * F + f0) = mx_e4m3x4(pg0, pg1, Eg);
+    *(uint32_t*)(codes + row * 2 * F + F + f0) = mx_e4m3x4(pu0, pu1, Eu);
+    if (q == 0) {
+      scales[row * (F >> 4) + c] = (uint8_t)(Eg + 127);
+      scales[row * (F >> 4) + C + c] = (uint8_t)(Eu + 127);
     }
   }
 }
