@@ -6,12 +6,18 @@ Workload: the Mixtral-like layer, T=4096 tokens, H=4096, E=8 experts, top-2,
 SwiGLU F=14336, bf16 activations/weights, fp32 router; synthetic seeded
 inputs resident in HBM before the timed region.
 
-    python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--no-cpu] [--no-mx]
+    python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--iters 160] [--no-cpu] [--no-mx]
 
-Prints one JSON line: layer microseconds (the metric), per-stage times, the
-grouped-GEMM TFLOP/s, route/permute/combine GB/s, the roofline of the dominant
-launch pair (the two grouped GEMMs of moe_grouped_mlp, timed with events on the
-stream they run on), and the CPU oracle timed on a bounded sample.
+Prints one JSON line: layer microseconds (the metric: the mean of the K timed
+steps), the layer and every stage over 160 single calls timed with events both
+cold (a 512 MiB buffer written just before each call, outside the events:
+more than the 256 MB last-level cache and the L2s) and warm (HIP-graph
+replays of back-to-back calls), as median, p10 and p90; the grouped-GEMM
+TFLOP/s and the route/permute/combine GB/s, each as a fraction of the
+datasheet peak and of the ceilings measured in the same run by the library's
+calibration kernels (streaming copy, read and write; matrix-core loops); the
+roofline of the dominant launch (moe_grouped_mlp, timed with events on the
+stream it runs on); and the CPU oracle timed on bounded samples.
 """
 import argparse
 import json
@@ -26,6 +32,7 @@ HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
 FP8_PEAK_TFLOPS = 5000.0
 FP4_PEAK_TFLOPS = 10100.0
+FLUSH_BYTES = 512 << 20
 
 
 def parse():
@@ -41,6 +48,7 @@ def parse():
                     default=None,
                     help="time only this other workload (its layer and grouped MLP) and print its line")
     ap.add_argument("--cpu-tokens", type=int, default=4096, help="tokens in the CPU oracle sample")
+    ap.add_argument("--iters", type=int, default=160, help="single calls timed per stage, cold and warm")
     return ap.parse_args()
 
 
@@ -78,55 +86,6 @@ def time_steps(layer, x, steps, warmup):
     t1.record(s)
     torch.cuda.synchronize()
     return t0.elapsed_time(t1) / steps
-
-
-def time_stages(layer, x, reps):
-    """Per-stage times with events between the four calls (same stream)."""
-    s = torch.cuda.current_stream()
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
-    acc = np.zeros(4)
-    for _ in range(reps):
-        ev[0].record(s)
-        layer.route(x=x)
-        ev[1].record(s)
-        layer.permute(x)
-        ev[2].record(s)
-        layer.mlp()
-        ev[3].record(s)
-        layer.combine()
-        ev[4].record(s)
-        torch.cuda.synchronize()
-        acc += [ev[i].elapsed_time(ev[i + 1]) for i in range(4)]
-    return acc / reps * 1000.0  # us
-
-
-def time_stages_graph(layer, x, reps):
-    """Per-stage GPU times without host launch gaps: each stage captured
-    `inner` times back to back in one HIP graph (same stream), the graph
-    replayed `reps` times between two events."""
-    stages = [(lambda: layer.route(x=x), 20), (lambda: layer.permute(x), 20), (layer.mlp, 2), (layer.combine, 20)]
-    out = []
-    for fn, inner in stages:
-        s = torch.cuda.Stream()
-        s.wait_stream(torch.cuda.current_stream())
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g, stream=s):
-            for _ in range(inner):
-                fn()
-        torch.cuda.synchronize()
-        for _ in range(2):
-            g.replay()
-        torch.cuda.synchronize()
-        t0 = torch.cuda.Event(enable_timing=True)
-        t1 = torch.cuda.Event(enable_timing=True)
-        t0.record()
-        for _ in range(reps):
-            g.replay()
-        t1.record()
-        torch.cuda.synchronize()
-        out.append(t0.elapsed_time(t1) / (reps * inner) * 1000.0)
-        del g
-    return np.array(out)  # us
 
 
 def time_graph(layer, x, reps):
@@ -205,18 +164,45 @@ def algorithmic(cfg, N):
     return route_b, permute_b, combine_b, flops
 
 
-def cpu_baseline(cfg, layer, x, r, ntok):
-    """The oracle as it stands, on the first `ntok` tokens of the same workload
-    (route from the projection, count/permute, float64 grouped MLP, combine),
-    scaled to the whole layer (x T/ntok).  Weights are converted to float64
-    before the clock starts."""
-    from oracle import moe_oracle as O
-    from workloads.gen import make_expert_weights, to_numpy_f64
+def _blas_threads():
     try:
         from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+        return max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
     except Exception:
-        cores = len(os.sched_getaffinity(0))
+        return len(os.sched_getaffinity(0))
+
+
+def _one_thread():
+    """Context that limits the BLAS pool to one thread (numpy's own loops are
+    single-threaded anyway)."""
+    try:
+        from threadpoolctl import threadpool_limits
+        return threadpool_limits(limits=1)
+    except Exception:
+        import contextlib
+        return contextlib.nullcontext()
+
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for ln in fh:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(cfg, layer, x, r, ntok):
+    """The oracle as it stands, stage by stage, on the first `ntok` tokens of
+    the same workload: route (projection + top-K), count/permute and combine
+    on one thread; the float64 grouped MLP on all BLAS threads of the process
+    affinity mask.  Scaled to the whole layer (x T/ntok).  Weights are
+    converted to float64 before the clock starts."""
+    from oracle import moe_oracle as O
+    from workloads.gen import make_expert_weights, to_numpy_f64
+    cores = _blas_threads()
     xs = to_numpy_f64(x[:ntok])
     wr = to_numpy_f64(r["w_router"])
     W1, W2 = [], []
@@ -225,32 +211,87 @@ def cpu_baseline(cfg, layer, x, r, ntok):
         W1.append(to_numpy_f64(w1))
         W2.append(to_numpy_f64(w2))
         del w1, w2
+    t = {}
+    with _one_thread():
+        t0 = time.perf_counter()
+        logits = O.router_logits(xs, wr)
+        ids, probs = O.route_topk(logits, cfg.K, cfg.score)
+        t["route"] = time.perf_counter() - t0
+        t0 = time.perf_counter()
+        perm = O.count_and_permute(ids, cfg.e0, cfg.local, xs, E_global=cfg.E)
+        t["permute"] = time.perf_counter() - t0
     t0 = time.perf_counter()
-    res = O.layer(xs, cfg.K, W1, W2, cfg.dtype, w_router=wr, score=cfg.score, e0=cfg.e0, L=cfg.local)
-    dt = time.perf_counter() - t0
+    y, _ = O.grouped_mlp(perm["x_perm"], perm["offsets"], W1, W2, cfg.dtype)
+    t["grouped_mlp"] = time.perf_counter() - t0
+    with _one_thread():
+        t0 = time.perf_counter()
+        out = O.combine(y, perm["slot_to_row"], probs, "bf16")
+        t["combine"] = time.perf_counter() - t0
     del W1, W2
+    dt = sum(t.values())
     # sanity: the sample's output agrees with the GPU layer on the same tokens
     gpu = to_numpy_f64(layer.out[:ntok])
-    err = float(np.abs(gpu - res["out"]).max() / max(np.abs(res["out"]).max(), 1e-30))
-    return {"value": dt * 1e6 * cfg.T / ntok, "unit": "us", "cores": int(cores), "kind": "oracle",
-            "sample": f"first {ntok} of {cfg.T} tokens, whole layer (route, permute, fp64 grouped MLP, combine), "
-                      f"{dt:.2f} s measured, scaled x{cfg.T // ntok}; max rel diff vs GPU on the sample {err:.2e}"}
+    err = float(np.abs(gpu - out).max() / max(np.abs(out).max(), 1e-30))
+    scale = cfg.T / ntok
+    return {"value": round(dt * 1e6 * scale, 1), "unit": "us", "cores": int(cores), "kind": "oracle",
+            "stage_us": {k: round(v * 1e6 * scale, 1) for k, v in t.items()},
+            "cpu": _cpu_model(), "affinity_cpus": len(os.sched_getaffinity(0)),
+            "sample": f"first {ntok} of {cfg.T} tokens, whole layer: route, count/permute and combine on 1 thread, "
+                      f"fp64 grouped MLP on {cores} BLAS threads; {dt:.2f} s measured, scaled x{scale:g}; max rel "
+                      f"diff vs GPU on the sample {err:.2e}"}
 
 
-def mx_variant(steps, warmup, name="mixtral_mxfp8"):
+def cpu_one_core(name, ntok):
+    """The whole oracle layer on one thread for another workload, on its
+    first `ntok` tokens (all of them when ntok >= T), scaled to T tokens;
+    min of 3 runs."""
+    from oracle import moe_oracle as O
+    from workloads import get_config
+    from workloads.gen import make_expert_weights, make_router_inputs, make_tokens, to_numpy_f64
+    cfg = get_config(name)
+    ntok = min(ntok, cfg.T)
+    x = to_numpy_f64(make_tokens(cfg)[:ntok])
+    r = make_router_inputs(cfg)
+    W1, W2 = [], []
+    for e in range(cfg.local):
+        w1, w2 = make_expert_weights(cfg, cfg.e0 + e, device="cpu")
+        W1.append(to_numpy_f64(w1))
+        W2.append(to_numpy_f64(w2))
+    kw = dict(score=cfg.score, e0=cfg.e0, L=cfg.local)
+    if r["logits"] is not None:
+        kw["logits"] = to_numpy_f64(r["logits"][:ntok])
+    else:
+        kw["w_router"] = to_numpy_f64(r["w_router"])
+    if r["mask"] is not None:
+        kw["mask"] = r["mask"][:ntok].numpy().astype(bool)
+    best = None
+    with _one_thread():
+        for _ in range(3):
+            t0 = time.perf_counter()
+            O.layer(x, cfg.K, W1, W2, cfg.dtype, **kw)
+            dt = time.perf_counter() - t0
+            best = dt if best is None else min(best, dt)
+    return {"workload": name, "value": round(best * 1e6 * cfg.T / ntok, 1), "unit": "us", "cores": 1,
+            "kind": "oracle", "sample": f"first {ntok} of {cfg.T} tokens, whole layer, 1 thread, min of 3: "
+                                        f"{best:.3f} s measured, scaled x{cfg.T / ntok:g}"}
+
+
+def mx_variant(steps, warmup, name="mixtral_mxfp8", iters=40):
     cfg, layer, x, r = build(name)
     ms = time_steps(layer, x, steps, warmup)
-    st = time_stages(layer, x, 10)
+    flush = Flusher()
+    fns = {"route": lambda: layer.route(x=x), "permute": lambda: layer.permute(x), "grouped_mlp": layer.mlp,
+           "combine": layer.combine}
+    st = {k: float(np.median(dist_cold(f, iters, flush))) for k, f in fns.items()}
     N = int(layer.offsets[-1].item())
     route_b, permute_b, combine_b, flops = algorithmic(cfg, N)
-    out = {"layer_us": ms * 1000.0, "stage_us": dict(zip(["route", "permute", "grouped_mlp", "combine"],
-                                                         [round(v, 2) for v in st])),
-           "grouped_gemm_tflops": flops / (st[2] * 1e-6) / 1e12,
-           "peak_tflops": FP8_PEAK_TFLOPS if cfg.dtype == "mxfp8" else FP4_PEAK_TFLOPS,
-           "grouped_gemm_frac_peak": flops / (st[2] * 1e-6) / 1e12 /
-           (FP8_PEAK_TFLOPS if cfg.dtype == "mxfp8" else FP4_PEAK_TFLOPS),
-           "permute_quantize_gbs": permute_b / (st[1] * 1e-6) / 1e9}
-    del layer
+    peak = FP8_PEAK_TFLOPS if cfg.dtype == "mxfp8" else FP4_PEAK_TFLOPS
+    tf = flops / (st["grouped_mlp"] * 1e-6) / 1e12
+    out = {"layer_us": round(ms * 1000.0, 2), "stage_us": {k: round(v, 2) for k, v in st.items()},
+           "stage_us_note": f"median of {iters} cold single calls", "grouped_gemm_tflops": round(tf, 1),
+           "peak_tflops": peak, "grouped_gemm_frac_peak": round(tf / peak, 4),
+           "permute_quantize_gbs": round(permute_b / (st["permute"] * 1e-6) / 1e9, 1)}
+    del layer, flush
     torch.cuda.empty_cache()
     return out
 
@@ -280,11 +321,13 @@ def graph_us(fn, inner=20, reps=5):
     return us
 
 
-def other_workload(name, steps, warmup):
+def other_workload(name, steps, warmup, iters=40):
     """Layer time of another full-size workload of the method (not the metric's
     configuration): the DeepSeek-like layer (256 experts, Zipf-skewed loads,
     sigmoid scores) and the sparse large-top-K share (32 of 2304 experts, K=36,
-    routed from given logits with masked tokens)."""
+    routed from given logits with masked tokens); per stage, the median of
+    `iters` cold single calls (each after a 512 MiB flush) and the warm time
+    per call from graph replays."""
     cfg, layer, x, r = build(name)
     logits = None if r["logits"] is None else r["logits"].cuda()
     mask = None if r["mask"] is None else r["mask"].cuda()
@@ -306,16 +349,25 @@ def other_workload(name, steps, warmup):
     us = t0.elapsed_time(t1) / steps * 1000.0
     N = int(layer.offsets[-1].item())
     flops = 6.0 * N * cfg.H * cfg.F
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-    ev[0].record(s)
-    for _ in range(steps):
-        layer.mlp()
-    ev[1].record(s)
-    torch.cuda.synchronize()
-    mlp_us = ev[0].elapsed_time(ev[1]) / steps * 1000.0
+    flush = Flusher()
+    fns = {"route": lambda: layer.route(x=None if logits is not None else x, logits=logits, mask=mask),
+           "permute": lambda: layer.permute(x), "grouped_mlp": layer.mlp, "combine": layer.combine}
+    cold = {k: float(np.median(dist_cold(f, iters, flush))) for k, f in fns.items()}
+    warm = {k: float(np.median(dist_warm(f, iters, inner=2 if k == "grouped_mlp" else 8))) for k, f in fns.items()}
+    mlp_us = cold["grouped_mlp"]
     out = {"workload": f"{name}: T={cfg.T} H={cfg.H} E={cfg.E} local={cfg.local} K={cfg.K} F={cfg.F}",
            "layer_us": round(us, 2), "grouped_mlp_us": round(mlp_us, 2), "routed_rows": N,
-           "grouped_gemm_tflops": round(flops / (mlp_us * 1e-6) / 1e12, 1)}
+           "grouped_gemm_tflops": round(flops / (mlp_us * 1e-6) / 1e12, 1),
+           "stage_us_cold": {k: round(v, 2) for k, v in cold.items()},
+           "stage_us_warm": {k: round(v, 2) for k, v in warm.items()}}
+    # algorithmic bytes (each token row read once, routed rows written once)
+    T, H, K, E = cfg.T, cfg.H, cfg.K, cfg.E
+    route_b = T * E * 4 + T * K * 6 if logits is not None else T * H * 2 + H * E * 2 + T * K * 6
+    t_act = T - (T // cfg.mask_every if cfg.mask_every else 0)
+    perm_b = t_act * H * 2 + N * H * 2 + T * K * 6 + N * 4
+    comb_b = N * H * 2 + T * K * 8 + T * H * 2
+    out["gbs_cold"] = {k: round(b / (cold[k] * 1e-6) / 1e9, 1)
+                       for k, b in (("route", route_b), ("permute", perm_b), ("combine", comb_b))}
     if logits is None:
         import dropless_mixture_experts_radix_amd as D
         # route alone (projection + selection), and its group-limited variant
@@ -326,7 +378,17 @@ def other_workload(name, steps, warmup):
             out["grouped_route_us"] = round(graph_us(lambda: D.moe_route_topk_grouped(
                 layer.ids, layer.probs, 8, 4, 2.5, x=x, w_prepared=layer.w_prep, w_dtype=layer.w_dtype, E=cfg.E,
                 bias=bias, err=layer.err, workspace=layer.route_ws)), 2)
-    del layer, x
+    else:
+        # the route on plain i.i.d. N(0,1) logits (no group structure: 0.5 local routes per token)
+        g = torch.Generator(device="cuda").manual_seed(5)
+        plain = torch.randn((T, E), generator=g, device="cuda")
+        rf = lambda: layer.route(logits=plain)
+        c = float(np.median(dist_cold(rf, iters, flush)))
+        w = float(np.median(dist_warm(rf, iters)))
+        out["route_plain_logits_us"] = {"cold": round(c, 2), "warm": round(w, 2),
+                                        "gbs_cold": round((T * E * 4 + T * K * 6) / (c * 1e-6) / 1e9, 1)}
+        del plain
+    del layer, x, flush
     torch.cuda.empty_cache()
     return out
 
@@ -449,6 +511,110 @@ def backward_stages(layer, cfg, N):
                     "written, map) / time"}
 
 
+def pct(v):
+    """median, p10 and p90 of a list of microsecond values."""
+    a = np.asarray(v, np.float64)
+    return {"p50": round(float(np.percentile(a, 50)), 2), "p10": round(float(np.percentile(a, 10)), 2),
+            "p90": round(float(np.percentile(a, 90)), 2)}
+
+
+class Flusher:
+    """Writes a 512 MiB buffer (the library's streaming-write calibration
+    kernel): more than the 256 MB last-level cache plus the 32 MB of L2, so
+    the next call finds none of its operands cached."""
+
+    def __init__(self):
+        self.buf = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device="cuda")
+        self.n = 0
+
+    def __call__(self):
+        import dropless_mixture_experts_radix_amd as D
+        self.n += 1
+        D.moe_calib_write(self.buf, self.n & 0xFF)
+
+
+def dist_cold(fn, iters, flush):
+    """GPU time of single calls of fn, each right after a cache flush (the
+    flush is outside the events; the host enqueues while the flush runs)."""
+    s = torch.cuda.current_stream()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
+    for a, b in evs:
+        flush()
+        a.record(s)
+        fn()
+        b.record(s)
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) * 1000.0 for a, b in evs]
+
+
+def dist_warm(fn, iters, inner=8):
+    """GPU time per call of fn with its operands cached: `inner` calls back to
+    back in one HIP graph, the graph replayed iters/inner times, each replay
+    between two events (per-call time = replay time / inner)."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        for _ in range(inner):
+            fn()
+    torch.cuda.synchronize()
+    for _ in range(2):
+        g.replay()
+    torch.cuda.synchronize()
+    reps = max(iters // inner, 4)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    cs = torch.cuda.current_stream()
+    for a, b in evs:
+        a.record(cs)
+        g.replay()
+        b.record(cs)
+    torch.cuda.synchronize()
+    out = [a.elapsed_time(b) * 1000.0 / inner for a, b in evs]
+    del g
+    return out
+
+
+def measure_ceilings():
+    """Achievable rates of this GPU from the library's calibration kernels:
+    streaming copy, read and write of 1 GiB, and matrix-core loops (bf16 and
+    MX-scaled E4M3) on register operands; best of 5 (GB/s, TFLOP/s)."""
+    import dropless_mixture_experts_radix_amd as D
+    nb = 1 << 30
+    src = torch.ones(nb, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    red = torch.empty(D.moe_calib_read_out_words(nb), dtype=torch.int32, device="cuda")
+
+    def best(fn, work, reps=5):
+        fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b) * 1e-3)
+        return work / min(ts)
+
+    out = {"copy_gbs": round(best(lambda: D.moe_calib_copy(src, dst), 2 * nb) / 1e9, 1),
+           "read_gbs": round(best(lambda: D.moe_calib_read(src, red), nb) / 1e9, 1),
+           "write_gbs": round(best(lambda: D.moe_calib_write(dst, 7), nb) / 1e9, 1)}
+    del src, dst, red
+    blocks = 256 * 4
+    acc = torch.empty(blocks * 512, dtype=torch.float32, device="cuda")
+    for dt, key in ((D.BF16, "mfma_bf16_tflops"), (D.MXFP8, "mfma_mxfp8_tflops")):
+        iters = 4096 if dt == D.BF16 else 2048
+        flops = blocks * 8 * 4 * iters * (32768 if dt == D.BF16 else 131072)
+        out[key] = round(best(lambda: D.moe_calib_mfma(dt, blocks, iters, acc), flops) / 1e12, 1)
+    del acc
+    torch.cuda.empty_cache()
+    out["note"] = ("calibration kernels of the library (moe_calib_*), best of 5: copy counts bytes read + written; "
+                   "matrix-core loops: 4 independent accumulators per wavefront, 8 wavefronts per CU, 4 workgroups "
+                   "per CU")
+    return out
+
+
 def main():
     a = parse()
     if a.gpus != 1:
@@ -463,19 +629,32 @@ def main():
         print(json.dumps(line), flush=True)
         return
     calibration_copy()
+    ceil = measure_ceilings()
     cfg, layer, x, r = build("mixtral_bf16")
     layer.forward(x)
     torch.cuda.synchronize()
     N = int(layer.offsets[-1].item())
     torch.cuda.synchronize()
     ms = time_steps(layer, x, a.steps, a.warmup)
-    st_eager = time_stages(layer, x, 20)
-    st = time_stages_graph(layer, x, 5)
+    flush = Flusher()
+    fns = {"route": lambda: layer.route(x=x), "permute": lambda: layer.permute(x), "grouped_mlp": layer.mlp,
+           "combine": layer.combine}
+    cold = {k: dist_cold(f, a.iters, flush) for k, f in fns.items()}
+    warm = {k: dist_warm(f, a.iters, inner=2 if k == "grouped_mlp" else 8) for k, f in fns.items()}
+    layer_cold = dist_cold(lambda: layer.forward(x), a.iters, flush)
+    layer_warm = dist_warm(lambda: layer.forward(x), a.iters, inner=2)
     gus = time_graph(layer, x, a.steps)
     route_b, permute_b, combine_b, flops = algorithmic(cfg, N)
-    t_route, t_perm, t_comb = st[0], st[1], st[3]
-    t_mlp = st_eager[2]  # events on the launch stream around the call
+    med = {k: float(np.median(v)) for k, v in cold.items()}
+    medw = {k: float(np.median(v)) for k, v in warm.items()}
+    t_mlp = med["grouped_mlp"]  # events on the launch stream around single calls
     tflops = flops / (t_mlp * 1e-6) / 1e12
+    gbs = {k: b / (med[k] * 1e-6) / 1e9 for k, b in (("route", route_b), ("permute", permute_b),
+                                                     ("combine", combine_b))}
+    gbs_w = {k: b / (medw[k] * 1e-6) / 1e9 for k, b in (("route", route_b), ("permute", permute_b),
+                                                        ("combine", combine_b))}
+    # the route reads (x, then a few bytes of ids and probs); permute and combine read and write
+    ceiling_of = {"route": ceil["read_gbs"], "permute": ceil["copy_gbs"], "combine": ceil["copy_gbs"]}
     line = {
         "metric": "MoE layer us; grouped-GEMM TFLOPS + permute/combine GB/s, 1 MI355X",
         "value": round(ms * 1000.0, 2),
@@ -491,22 +670,29 @@ def main():
         "data": "synthetic",
         "config": {"workload": "mixtral_bf16: T=4096 H=4096 E=8 K=2 SwiGLU F=14336, bf16 rows/weights, "
                                "fp32 router", "tokens": cfg.T, "routed_rows": N},
-        "stage_us": {"route": round(t_route, 2), "permute": round(t_perm, 2), "grouped_mlp": round(t_mlp, 2),
-                     "combine": round(t_comb, 2)},
-        "stage_us_note": "route/permute/combine: GPU time per call from HIP-graph replays of 20 back-to-back "
-                         "calls; grouped_mlp: events around the eager call",
-        "stage_us_eager": {k: round(float(v), 2) for k, v in
-                           zip(["route", "permute", "grouped_mlp", "combine"], st_eager)},
+        "stage_us": {k: round(v, 2) for k, v in med.items()},
+        "stage_us_note": f"median of {a.iters} single calls, each after a 512 MiB cache flush (cold; events on "
+                         f"the launch stream); stage_us_warm: HIP-graph replays of back-to-back calls",
+        "stage_us_cold": {k: pct(v) for k, v in cold.items()},
+        "stage_us_warm": {k: pct(v) for k, v in warm.items()},
+        "layer_us_cold": pct(layer_cold),
+        "layer_us_warm": pct(layer_warm),
         "graph_replay_us": round(gus, 2),
         "grouped_gemm_tflops": round(tflops, 1),
-        "route_gbs": round(route_b / (t_route * 1e-6) / 1e9, 1),
-        "permute_gbs": round(permute_b / (t_perm * 1e-6) / 1e9, 1),
-        "combine_gbs": round(combine_b / (t_comb * 1e-6) / 1e9, 1),
+        "route_gbs": round(gbs["route"], 1),
+        "permute_gbs": round(gbs["permute"], 1),
+        "combine_gbs": round(gbs["combine"], 1),
+        "gbs_warm": {k: round(v, 1) for k, v in gbs_w.items()},
+        "frac_of_hbm_peak": {k: round(v / HBM_PEAK_GBS, 3) for k, v in gbs.items()},
+        "frac_of_measured_ceiling": {**{k: round(v / ceiling_of[k], 3) for k, v in gbs.items()},
+                                     "grouped_mlp": round(tflops / ceil["mfma_bf16_tflops"], 3)},
+        "ceilings": ceil,
         "roofline": {"kernel": "moe_grouped_mlp: k_gemm_bf16<1> (GEMM1+SwiGLU) + k_gemm_bf16<0> (GEMM2) "
                                "+ k_splitk_reduce<1,0>",
                      "bound": "mfma", "achieved": round(tflops, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tflops / BF16_PEAK_TFLOPS, 4), "traffic": measured_traffic(),
-                     "traffic_unit": "HBM bytes per launch", "algorithmic_flops_per_launch": flops},
+                     "traffic_unit": "HBM bytes per launch", "algorithmic_flops_per_launch": flops,
+                     "time_us": round(t_mlp, 2)},
     }
     if not a.no_backward:
         try:
@@ -529,6 +715,7 @@ def main():
             line["mx"] = {"error": repr(ex)}
     if not a.no_cpu:
         line["cpu_baseline"] = cpu_baseline(cfg, layer, x, r, a.cpu_tokens)
+        line["cpu_one_core"] = [cpu_one_core("tiny_f32", 256), cpu_one_core("sparse_share", 512)]
     if not a.no_other:
         del layer, x
         torch.cuda.empty_cache()

@@ -12,15 +12,39 @@ import torch
 
 F32, BF16, MXFP8, MXFP4 = 0, 1, 2, 3
 SOFTMAX, SIGMOID = 0, 1
-DEVERR_BAD_ID, DEVERR_OVERFLOW, DEVERR_NONFINITE = 1, 2, 4
+DEVERR_BAD_ID, DEVERR_OVERFLOW, DEVERR_NONFINITE, DEVERR_WORKSPACE = 1, 2, 4, 8
 MAX_K, MAX_E, MAX_L = 64, 4096, 2048
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_mi355x.so")
 
 _I, _I64, _SZ, _P = ctypes.c_int, ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p
 
+class MoeShape(ctypes.Structure):
+    """moe_shape of include/moe.h."""
+    _fields_ = [(n, _I) for n in ("T", "H", "E", "K", "L", "F", "x_dtype", "w_dtype", "dtype")]
+
+
+class MoeSizes(ctypes.Structure):
+    """moe_sizes of include/moe.h."""
+    _fields_ = ([("capacity", _I64), ("capacity_any_ids", _I64)] +
+                [(n, _SZ) for n in ("router_prepared_bytes", "route_workspace_bytes", "permute_workspace_bytes",
+                                    "permute_state_bytes", "w1p_bytes", "w2p_bytes", "w1p_scales_bytes", "w2p_scales_bytes",
+                                    "mlp_workspace_bytes", "mlp_act_offset", "mlp_act_scales_offset",
+                                    "w1t_bytes", "w2t_bytes", "w1t_scales_bytes", "w2t_scales_bytes",
+                                    "mlp_backward_workspace_bytes", "bwd_h_offset", "bwd_dh_offset",
+                                    "bwd_dh_codes_offset", "bwd_dh_scales_offset",
+                                    "mlp_backward_weights_workspace_bytes")])
+
+
 _SIGS = {
     "moe_abi_version": (_I, []),
+    "moe_query_sizes": (_I, [ctypes.POINTER(MoeShape), ctypes.POINTER(MoeSizes)]),
+    "moe_grouped_mlp_with_act": (_I, [_I, _I, _I, _I64, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P, _P]),
+    "moe_calib_copy": (_I, [_P, _P, _SZ, _P]),
+    "moe_calib_read_out_words": (_SZ, [_SZ]),
+    "moe_calib_read": (_I, [_P, _SZ, _P, _P]),
+    "moe_calib_write": (_I, [_P, _SZ, ctypes.c_uint32, _P]),
+    "moe_calib_mfma": (_I, [_I, _I, _I, _P, _P]),
     "moe_status_str": (ctypes.c_char_p, [_I]),
     "moe_router_prepared_bytes": (_SZ, [_I, _I, _I, _I]),
     "moe_prepare_router": (_I, [_P, _I, _I, _I, _I, _P, _P]),
@@ -36,11 +60,11 @@ _SIGS = {
     "moe_grouped_mlp": (_I, [_I, _I, _I, _I64, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "moe_unpermute_combine": (_I, [_I, _I, _I, _I, _P, _P, _P, _P, _P]),
     "moe_mx_quantize": (_I, [_I64, _I, _P, _P, _P, _P, _P]),
-    "moe_unpermute_combine_backward": (_I, [_I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P]),
+    "moe_unpermute_combine_backward": (_I, [_I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
     "moe_prepare_weights_backward": (_I, [_I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P]),
     "moe_grouped_mlp_backward_workspace_bytes": (_SZ, [_I64, _I, _I, _I]),
-    "moe_grouped_mlp_backward_data": (_I, [_I, _I, _I, _I64, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ,
-                                           _P]),
+    "moe_grouped_mlp_backward_data": (_I, [_I, _I, _I, _I64, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                           _P, _P, _P, _SZ, _P]),
     "moe_grouped_mlp_backward_weights_workspace_bytes": (_SZ, [_I, _I64, _I, _I, _I]),
     "moe_mx_columns_grouped_max_blocks": (_I64, [_I, _I64]),
     "moe_mx_quantize_columns_grouped": (_I, [_I, _I64, _I, _P, _P, _P, _P, _P, _P]),
@@ -63,7 +87,7 @@ def _load():
         fn = getattr(lib, name)
         fn.restype = res
         fn.argtypes = args
-    if lib.moe_abi_version() != 1:
+    if lib.moe_abi_version() != 2:
         raise ImportError("libmoe_mi355x.so ABI version mismatch")
     return lib
 
@@ -187,6 +211,59 @@ def moe_grouped_mlp(x_perm, offsets, w1p, w2p, y_perm, workspace, dtype, H, F, x
                                _nbytes(workspace), _stream()), "moe_grouped_mlp")
 
 
+def moe_grouped_mlp_with_act(x_perm, offsets, w1p, w2p, y_perm, workspace, dtype, H, F, act_bf16,
+                             x_perm_scales=None, w1p_scales=None, w2p_scales=None):
+    """moe_grouped_mlp (MX dtypes) that also stores the bf16 `a` its GEMM1
+    epilogue quantizes into act_bf16 [capacity][F] (a test hook)."""
+    L = offsets.shape[0] - 1
+    capacity = y_perm.shape[0]
+    _check(lib.moe_grouped_mlp_with_act(L, H, F, capacity, dtype, _p(x_perm), _p(x_perm_scales), _p(offsets),
+                                        _p(w1p), _p(w1p_scales), _p(w2p), _p(w2p_scales), _p(y_perm),
+                                        _p(workspace), _nbytes(workspace), _p(act_bf16), _stream()),
+           "moe_grouped_mlp_with_act")
+
+
+# ----------------------------------------------------------------- calibration kernels
+def moe_calib_copy(src, dst):
+    n = min(_nbytes(src), _nbytes(dst)) // 16 * 16
+    _check(lib.moe_calib_copy(_p(src), _p(dst), n, _stream()), "moe_calib_copy")
+    return n
+
+
+def moe_calib_read(src, out):
+    n = _nbytes(src) // 16 * 16
+    if out.numel() < lib.moe_calib_read_out_words(n):
+        raise MoEError("moe_calib_read: out too small")
+    _check(lib.moe_calib_read(_p(src), n, _p(out), _stream()), "moe_calib_read")
+    return n
+
+
+def moe_calib_read_out_words(nbytes):
+    return lib.moe_calib_read_out_words(nbytes)
+
+
+def moe_calib_write(dst, value=0):
+    n = _nbytes(dst) // 16 * 16
+    _check(lib.moe_calib_write(_p(dst), n, value, _stream()), "moe_calib_write")
+    return n
+
+
+def moe_calib_mfma(dtype, blocks, iters, out):
+    if out.numel() < blocks * 512:
+        raise MoEError("moe_calib_mfma: out too small")
+    _check(lib.moe_calib_mfma(dtype, blocks, iters, _p(out), _stream()), "moe_calib_mfma")
+    return blocks * 8 * 4 * iters * (32768 if dtype == BF16 else 131072)
+
+
+# ----------------------------------------------------------------- sizes
+def moe_query_sizes(T, H, E, K, F, dtype, x_dtype=BF16, w_dtype=F32, L=0):
+    """All buffer sizes of one layer shape (moe_query_sizes), as a dict."""
+    sh = MoeShape(T, H, E, K, L, F, x_dtype, w_dtype, dtype)
+    out = MoeSizes()
+    _check(lib.moe_query_sizes(ctypes.byref(sh), ctypes.byref(out)), "moe_query_sizes")
+    return {n: getattr(out, n) for n, _ in MoeSizes._fields_}
+
+
 # ----------------------------------------------------------------- combine
 def moe_unpermute_combine(y_perm, slot_to_row, probs, out):
     T, K = slot_to_row.shape
@@ -208,14 +285,16 @@ def _need(t, dtype, name):
         raise MoEError(f"{name} must be {dtype}, got {t.dtype}")
 
 
-def moe_unpermute_combine_backward(dout, y_perm, slot_to_row, probs, d_y_perm, d_probs):
+def moe_unpermute_combine_backward(dout, y_perm, slot_to_row, probs, d_y_perm, d_probs, d_y_perm_q=None,
+                                   d_y_perm_q_scales=None):
     _need(slot_to_row, torch.int32, "slot_to_row")
     _need(probs, torch.float32, "probs")
     _need(d_probs, torch.float32, "d_probs")
     T, K = slot_to_row.shape
     H = dout.shape[1]
     _check(lib.moe_unpermute_combine_backward(T, K, H, dtype_code(dout.dtype), _p(dout), _p(y_perm),
-                                              _p(slot_to_row), _p(probs), _p(d_y_perm), _p(d_probs), _stream()),
+                                              _p(slot_to_row), _p(probs), _p(d_y_perm), _p(d_probs),
+                                              _p(d_y_perm_q), _p(d_y_perm_q_scales), _stream()),
            "moe_unpermute_combine_backward")
 
 
@@ -249,13 +328,15 @@ def moe_grouped_mlp_backward_workspace_bytes(capacity, H, F, dtype):
 
 
 def moe_grouped_mlp_backward_data(x_perm, offsets, w1p, w1t, w2t, d_y_perm, d_x_perm, workspace, H, F, dtype=BF16,
-                                  w1p_scales=None, w1t_scales=None, w2t_scales=None):
+                                  w1p_scales=None, w1t_scales=None, w2t_scales=None, x_perm_q=None,
+                                  x_perm_q_scales=None, d_y_perm_q=None, d_y_perm_q_scales=None):
     _need(offsets, torch.int32, "offsets")
     L = offsets.shape[0] - 1
-    cap = x_perm.shape[0]
+    cap = d_x_perm.shape[0]
     _check(lib.moe_grouped_mlp_backward_data(L, H, F, cap, dtype, _p(x_perm), _p(offsets), _p(w1p), _p(w1p_scales),
                                              _p(w1t), _p(w1t_scales), _p(w2t), _p(w2t_scales), _p(d_y_perm),
-                                             _p(d_x_perm), _p(workspace), _nbytes(workspace), _stream()),
+                                             _p(d_x_perm), _p(x_perm_q), _p(x_perm_q_scales), _p(d_y_perm_q),
+                                             _p(d_y_perm_q_scales), _p(workspace), _nbytes(workspace), _stream()),
            "moe_grouped_mlp_backward_data")
 
 

@@ -86,13 +86,17 @@ __global__ __launch_bounds__(256) void k_combine(int T, int K, int H, const uint
 // a row r (k order) d_y[r] = p * dout[t] (rounded like y) and d_probs[t,k] =
 // <dout[t], y[r]> (each lane's fixed-order fp32 partial, then the wavefront's
 // fixed tree); slots without a row get d_probs 0.  The token's dout pieces are
-// re-read per slot (cache hits after the first).
-template <bool BF16>
+// re-read per slot (cache hits after the first).  MX (bf16 rows): the bf16
+// d_y row is also MX-quantized along H as it is written (E4M3 codes [.][H],
+// E8M0 scales [.][H/32]; 4 lanes hold one 32-element block), the operand form
+// the MXFP8 data gradient takes, so no separate quantization pass reads it.
+template <bool BF16, bool MX>
 __global__ __launch_bounds__(256) void k_combine_backward(int T, int K, int H, const uint8_t* __restrict__ dout,
                                                           const uint8_t* __restrict__ y,
                                                           const int32_t* __restrict__ s2r,
                                                           const float* __restrict__ probs,
-                                                          uint8_t* __restrict__ dy, float* __restrict__ dprobs) {
+                                                          uint8_t* __restrict__ dy, float* __restrict__ dprobs,
+                                                          uint8_t* __restrict__ dyq, uint8_t* __restrict__ dyqs) {
   const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + w;
   if (t >= T) return;
@@ -146,6 +150,19 @@ __global__ __launch_bounds__(256) void k_combine_backward(int T, int K, int H, c
           }
         }
         if (p0 + j < npiece && off < row_bytes) *(u32x4*)(dst + off) = o;
+        if (MX) {  // H % 32 == 0: the 4 lanes of a block are all in the row or all past it
+          uint32_t am = 0;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) am = max(am, max(o[q] & 0x7fffu, (o[q] >> 16) & 0x7fffu));
+          am = max(am, (uint32_t)__shfl_xor((int)am, 1, 64));
+          am = max(am, (uint32_t)__shfl_xor((int)am, 2, 64));
+          const int E = mx_scale_exp(am);
+          const uint32_t lo = mx_e4m3x4(o[0], o[1], E), hi = mx_e4m3x4(o[2], o[3], E);
+          if (p0 + j < npiece && off < row_bytes) {
+            *(uint2*)(dyq + (long)d * H + (off >> 1)) = make_uint2(lo, hi);
+            if ((l & 3) == 0) dyqs[(long)d * (H >> 5) + (off >> 6)] = (uint8_t)(E + 127);
+          }
+        }
       }
     }
     const float dot = wave_sum_f(part);
@@ -204,16 +221,19 @@ __global__ __launch_bounds__(256) void k_route_backward(int T, int E, int K, int
 }
 
 hipError_t launch_combine_backward(int T, int K, int H, int dtype, const void* dout, const void* y,
-                                   const int32_t* s2r, const float* probs, void* dy, float* dprobs,
-                                   hipStream_t s) {
+                                   const int32_t* s2r, const float* probs, void* dy, float* dprobs, uint8_t* dyq,
+                                   uint8_t* dyqs, hipStream_t s) {
   if (T == 0) return hipSuccess;
   const dim3 g((T + 3) / 4), b(256);
   if (dtype == MOE_F32)
-    hipLaunchKernelGGL(k_combine_backward<false>, g, b, 0, s, T, K, H, (const uint8_t*)dout, (const uint8_t*)y,
-                       s2r, probs, (uint8_t*)dy, dprobs);
+    hipLaunchKernelGGL((k_combine_backward<false, false>), g, b, 0, s, T, K, H, (const uint8_t*)dout,
+                       (const uint8_t*)y, s2r, probs, (uint8_t*)dy, dprobs, (uint8_t*)nullptr, (uint8_t*)nullptr);
+  else if (dyq)
+    hipLaunchKernelGGL((k_combine_backward<true, true>), g, b, 0, s, T, K, H, (const uint8_t*)dout,
+                       (const uint8_t*)y, s2r, probs, (uint8_t*)dy, dprobs, dyq, dyqs);
   else
-    hipLaunchKernelGGL(k_combine_backward<true>, g, b, 0, s, T, K, H, (const uint8_t*)dout, (const uint8_t*)y,
-                       s2r, probs, (uint8_t*)dy, dprobs);
+    hipLaunchKernelGGL((k_combine_backward<true, false>), g, b, 0, s, T, K, H, (const uint8_t*)dout,
+                       (const uint8_t*)y, s2r, probs, (uint8_t*)dy, dprobs, (uint8_t*)nullptr, (uint8_t*)nullptr);
   return hipGetLastError();
 }
 

@@ -644,11 +644,13 @@ int router_gemm_pieces(int T, int E, int H) {
 hipError_t launch_router_gemm_bf16(int T, int E, int H, int S, const bf16_t* x, const bf16_t* wp, float* partial,
                                    hipStream_t s) {
   if (T == 0) return hipSuccess;
-  static bool attr_done = false;
-  if (!attr_done) {
+  // function attributes are set once per process; the initializer of a
+  // function-local static runs exactly once even under concurrent first calls
+  static const bool attr_done = [] {
     (void)hipFuncSetAttribute((const void*)k_gemm_bf16<2>, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-    attr_done = true;
-  }
+    return true;
+  }();
+  (void)attr_done;
   const long units = (long)((T + GB_BM - 1) / GB_BM) * ((E + GB_BN - 1) / GB_BN) * S;
   const int G = (int)(units < num_cus() ? units : num_cus());
   hipLaunchKernelGGL(k_gemm_bf16<2>, dim3(G), dim3(GB_THREADS), gemm_bf16_lds(S), s, S, E, H, (int64_t)T, x,
@@ -661,12 +663,14 @@ hipError_t launch_grouped_mlp_bf16(int L, int H, int F, int64_t capacity, const 
                                    bf16_t* act, float* part, bf16_t* y, hipStream_t s) {
   if (capacity == 0) return hipSuccess;
   const size_t lds = gemm_bf16_lds(L);
-  static bool attr_done = false;
-  if (!attr_done) {
+  // function attributes are set once per process; the initializer of a
+  // function-local static runs exactly once even under concurrent first calls
+  static const bool attr_done = [] {
     (void)hipFuncSetAttribute((const void*)k_gemm_bf16<0>, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     (void)hipFuncSetAttribute((const void*)k_gemm_bf16<1>, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-    attr_done = true;
-  }
+    return true;
+  }();
+  (void)attr_done;
   const int N1 = 2 * F, N2 = H;
   const int G1 = grid_for(capacity, L, GB_BM, (N1 + GB_BN - 1) / GB_BN, 1);
   const int G2 = grid_for(capacity, L, GB_BM, (N2 + GB_BN - 1) / GB_BN, 1);
@@ -688,13 +692,15 @@ hipError_t launch_grouped_mlp_bf16_backward(int L, int H, int F, int64_t capacit
                                             float* part, bf16_t* dx, hipStream_t s) {
   if (capacity == 0) return hipSuccess;
   const size_t lds = gemm_bf16_lds(L);
-  static bool attr_done = false;
-  if (!attr_done) {
+  // function attributes are set once per process; the initializer of a
+  // function-local static runs exactly once even under concurrent first calls
+  static const bool attr_done = [] {
     (void)hipFuncSetAttribute((const void*)k_gemm_bf16<0>, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     (void)hipFuncSetAttribute((const void*)k_gemm_bf16<3>, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     (void)hipFuncSetAttribute((const void*)k_gemm_bf16<4>, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-    attr_done = true;
-  }
+    return true;
+  }();
+  (void)attr_done;
   const bf16_t* nul = nullptr;
   const int G3 = grid_for(capacity, L, GB_BM, (2 * F + GB_BN - 1) / GB_BN, 1);
   const int G4 = grid_for(capacity, L, GB_BM, (F + GB_BN - 1) / GB_BN, 1);
@@ -724,11 +730,13 @@ hipError_t launch_grouped_mlp_bf16_wgrad(int L, int H, int F, int64_t capacity, 
                                       dW1, dW2, s);
   if (e != hipSuccess) return e;
   const size_t lds = gemm_bf16_lds(L);
-  static bool attr_done = false;
-  if (!attr_done) {
+  // function attributes are set once per process; the initializer of a
+  // function-local static runs exactly once even under concurrent first calls
+  static const bool attr_done = [] {
     (void)hipFuncSetAttribute((const void*)k_gemm_bf16<5>, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-    attr_done = true;
-  }
+    return true;
+  }();
+  (void)attr_done;
   auto grid = [&](int I, int J) {
     const long tiles = (long)((I + GB_BM - 1) / GB_BM) * ((J + GB_BN - 1) / GB_BN) * L;
     return (int)(tiles < num_cus() ? tiles : num_cus());

@@ -4,17 +4,17 @@
 
 namespace moe {
 
+// compute units of the device (queried once per process: the initializer of
+// a function-local static runs exactly once even under concurrent first calls)
 static inline int num_cus() {
-  static int g_num_cus = 0;
-  if (g_num_cus == 0) {
+  static const int n_cus = [] {
     int dev = 0, n = 0;
     if (hipGetDevice(&dev) == hipSuccess &&
         hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
-      g_num_cus = n;
-    else
-      g_num_cus = 256;
-  }
-  return g_num_cus;
+      return n;
+    return 256;
+  }();
+  return n_cus;
 }
 
 // ---------------------------------------------------------------------------

@@ -27,7 +27,9 @@
 // of a last, partial round of the CUs are split along k and summed by
 // k_mx_splitk_reduce in a fixed order (the split plan of the bf16 kernel).
 // EPI 1 (GEMM1): a = silu(gate) * up is rounded to bf16 and MX-quantized along
-// F in the epilogue (one 32-column gate chunk = one MX block of a row).
+// F in the epilogue (one 32-column gate chunk = one MX block of a row); with a
+// non-null aux_o the bf16 values are also stored row-major [capacity][F] (a
+// test hook that lets the quantization be checked bit for bit).
 // EPI 0 (GEMM2): y stored as bf16.
 // The data gradient (MXFP8):
 // EPI 3: h = x_perm . W1 recomputed, stored bf16 k-blocked [N/32][capacity][32]
@@ -156,6 +158,8 @@ __device__ __forceinline__ void mx_store_tile(const f32x16 (&acc)[NI][2], int i0
         // bf16 value of a, then the amax of its MX block (the 32 lanes of this half)
         const uint32_t ab = f32_to_bf16(silu_mul(acc[i][0][v], acc[i][1][v]));
         const uint32_t am = max_half_wave(ab & 0x7fffu);
+        // test hook: the bf16 value itself, row-major [capacity][F], when asked for
+        if (aux_o && row < ti.rows && jcol < Fh) aux_o[(long)(ti.row0 + row) * Fh + jcol] = (bf16_t)ab;
         if (FP4) {
           // E2M1 codes of columns 2c and 2c+1 share byte c (low nibble first)
           const int E = mx4_scale_exp(am);
@@ -675,15 +679,18 @@ static size_t mx_lds_bytes(int L, bool TALL) {
 template <bool FP4, bool TALL>
 static void launch_mx(int L, int H, int F, int64_t capacity, const uint8_t* x, const uint8_t* xs,
                       const int32_t* offsets, const uint8_t* w1p, const uint8_t* w1s, const uint8_t* w2p,
-                      const uint8_t* w2s, uint8_t* act, uint8_t* act_s, float* part, bf16_t* y, hipStream_t s) {
-  static bool attr_done = false;
-  if (!attr_done) {
+                      const uint8_t* w2s, uint8_t* act, uint8_t* act_s, float* part, bf16_t* y, bf16_t* act_bf16,
+                      hipStream_t s) {
+  // function attributes are set once per process; the initializer of a
+  // function-local static runs exactly once even under concurrent first calls
+  static const bool attr_done = [] {
     (void)hipFuncSetAttribute((const void*)k_gemm_mx<0, FP4, TALL>, hipFuncAttributeMaxDynamicSharedMemorySize,
                               160 * 1024);
     (void)hipFuncSetAttribute((const void*)k_gemm_mx<1, FP4, TALL>, hipFuncAttributeMaxDynamicSharedMemorySize,
                               160 * 1024);
-    attr_done = true;
-  }
+    return true;
+  }();
+  (void)attr_done;
   const size_t lds = mx_lds_bytes(L, TALL);
   auto grid = [&](int N) {
     const int NT = (N + GM_BN - 1) / GM_BN;
@@ -695,9 +702,9 @@ static void launch_mx(int L, int H, int F, int64_t capacity, const uint8_t* x, c
   const int G1 = grid(2 * F), G2 = grid(H);
   const dim3 rgrid(GEMM_SPLIT_UNITS / 2 * 8), rblk(320), blk(GM_THREADS);
   hipLaunchKernelGGL((k_gemm_mx<1, FP4, TALL>), dim3(G1), blk, lds, s, L, 2 * F, H, capacity, x, xs, offsets, w1p,
-                     w1s, act, act_s, part, nullptr, (bf16_t*)nullptr);
+                     w1s, act, act_s, part, nullptr, act_bf16);
   hipLaunchKernelGGL((k_mx_splitk_reduce<1, FP4, TALL>), rgrid, rblk, 0, s, L, 2 * F, H, capacity, G1, offsets,
-                     part, act, act_s, (const bf16_t*)nullptr, (bf16_t*)nullptr);
+                     part, act, act_s, (const bf16_t*)nullptr, act_bf16);
   hipLaunchKernelGGL((k_gemm_mx<0, FP4, TALL>), dim3(G2), blk, lds, s, L, H, F, capacity, act, act_s, offsets,
                      w2p, w2s, (uint8_t*)y, (uint8_t*)nullptr, part, nullptr, (bf16_t*)nullptr);
   hipLaunchKernelGGL((k_mx_splitk_reduce<0, FP4, TALL>), rgrid, rblk, 0, s, L, H, F, capacity, G2, offsets, part,
@@ -707,18 +714,19 @@ static void launch_mx(int L, int H, int F, int64_t capacity, const uint8_t* x, c
 hipError_t launch_grouped_mlp_mx(int L, int H, int F, int64_t capacity, bool fp4, const uint8_t* x,
                                  const uint8_t* xs, const int32_t* offsets, const uint8_t* w1p,
                                  const uint8_t* w1s, const uint8_t* w2p, const uint8_t* w2s,
-                                 uint8_t* act, uint8_t* act_s, float* part, bf16_t* y, hipStream_t s) {
+                                 uint8_t* act, uint8_t* act_s, float* part, bf16_t* y, bf16_t* act_bf16,
+                                 hipStream_t s) {
   if (capacity == 0) return hipSuccess;
   // E4M3: tall tiles when their larger LDS layout leaves room for the
   // schedule of L experts.  E2M1: plain tiles (measured on the Mixtral-like
   // shape: tall tiles 3% faster with E4M3 codes, 2.5% slower with E2M1).
   const bool tall = mx_lds_bytes(L, true) <= 160 * 1024;
   if (fp4)
-    launch_mx<true, false>(L, H, F, capacity, x, xs, offsets, w1p, w1s, w2p, w2s, act, act_s, part, y, s);
+    launch_mx<true, false>(L, H, F, capacity, x, xs, offsets, w1p, w1s, w2p, w2s, act, act_s, part, y, act_bf16, s);
   else if (tall)
-    launch_mx<false, true>(L, H, F, capacity, x, xs, offsets, w1p, w1s, w2p, w2s, act, act_s, part, y, s);
+    launch_mx<false, true>(L, H, F, capacity, x, xs, offsets, w1p, w1s, w2p, w2s, act, act_s, part, y, act_bf16, s);
   else
-    launch_mx<false, false>(L, H, F, capacity, x, xs, offsets, w1p, w1s, w2p, w2s, act, act_s, part, y, s);
+    launch_mx<false, false>(L, H, F, capacity, x, xs, offsets, w1p, w1s, w2p, w2s, act, act_s, part, y, act_bf16, s);
   return hipGetLastError();
 }
 
@@ -779,7 +787,8 @@ __global__ __launch_bounds__(256) void k_swiglu_bwd_mx(int F, int64_t capacity, 
   }
 }
 
-// MXFP8 data gradient: row-wise MX of x_perm and d_y (along H), then
+// MXFP8 data gradient: row-wise MX of x_perm and d_y (along H, unless the
+// caller passes them), then
 // h = x_perm . W1 (EPI 3), d_a = d_y . W2^T (EPI 6) and from it d_h (bf16,
 // and MX along 2F: k_swiglu_bwd_mx), then d_x = d_h . W1^T (EPI 0); each GEMM
 // followed by its split-K reduce.
@@ -789,16 +798,18 @@ static void launch_mx_backward(int L, int H, int F, int64_t capacity, const uint
                                const uint8_t* w1ts, const uint8_t* w2t, const uint8_t* w2ts, const uint8_t* dyq,
                                const uint8_t* dyqs, bf16_t* hbuf, bf16_t* dhbuf, uint8_t* dhq, uint8_t* dhqs,
                                float* da, float* part, bf16_t* dx, hipStream_t s) {
-  static bool attr_done = false;
-  if (!attr_done) {
+  // function attributes are set once per process; the initializer of a
+  // function-local static runs exactly once even under concurrent first calls
+  static const bool attr_done = [] {
     (void)hipFuncSetAttribute((const void*)k_gemm_mx<0, false, TALL>, hipFuncAttributeMaxDynamicSharedMemorySize,
                               160 * 1024);
     (void)hipFuncSetAttribute((const void*)k_gemm_mx<3, false, TALL>, hipFuncAttributeMaxDynamicSharedMemorySize,
                               160 * 1024);
     (void)hipFuncSetAttribute((const void*)k_gemm_mx<6, false, TALL>, hipFuncAttributeMaxDynamicSharedMemorySize,
                               160 * 1024);
-    attr_done = true;
-  }
+    return true;
+  }();
+  (void)attr_done;
   const size_t lds = mx_lds_bytes(L, TALL);
   auto grid = [&](int N) {
     const int NT = (N + GM_BN - 1) / GM_BN;
@@ -830,10 +841,14 @@ hipError_t launch_grouped_mlp_mx_backward(int L, int H, int F, int64_t capacity,
                                           const uint8_t* w1t, const uint8_t* w1ts, const uint8_t* w2t,
                                           const uint8_t* w2ts, const bf16_t* dy, uint8_t* xq, uint8_t* xqs,
                                           uint8_t* dyq, uint8_t* dyqs, bf16_t* hbuf, bf16_t* dhbuf, uint8_t* dhq,
-                                          uint8_t* dhqs, float* da, float* part, bf16_t* dx, hipStream_t s) {
+                                          uint8_t* dhqs, float* da, float* part, bf16_t* dx, bool x_given,
+                                          bool dy_given, hipStream_t s) {
   if (capacity == 0) return hipSuccess;
-  hipError_t e = launch_mx_quantize(capacity, H, x, offsets + L, xq, xqs, s);
-  if (e == hipSuccess) e = launch_mx_quantize(capacity, H, dy, offsets + L, dyq, dyqs, s);
+  // row-wise MX operands of x_perm and d_y: given by their producers (the
+  // MXFP8 permute, the combine backward with MX output), else quantized here
+  hipError_t e = hipSuccess;
+  if (!x_given) e = launch_mx_quantize(capacity, H, x, offsets + L, xq, xqs, s);
+  if (e == hipSuccess && !dy_given) e = launch_mx_quantize(capacity, H, dy, offsets + L, dyq, dyqs, s);
   if (e != hipSuccess) return e;
   if (mx_lds_bytes(L, true) <= 160 * 1024)
     launch_mx_backward<true>(L, H, F, capacity, xq, xqs, offsets, w1p, w1s, w1t, w1ts, w2t, w2ts, dyq, dyqs, hbuf,
@@ -856,12 +871,14 @@ hipError_t launch_grouped_mlp_mx_wgrad(int L, int H, int F, int64_t capacity, in
   hipError_t e = launch_wgrad_mx_layouts(L, H, F, capacity, nbmax, x, offsets, dy, hbuf, dhbuf, pk, png, xa, xas, dhb,
                                          dhbs, aa, aas, dyb, dybs, dW1, dW2, s);
   if (e != hipSuccess) return e;
-  static bool attr_done = false;
-  if (!attr_done) {
+  // function attributes are set once per process; the initializer of a
+  // function-local static runs exactly once even under concurrent first calls
+  static const bool attr_done = [] {
     (void)hipFuncSetAttribute((const void*)k_gemm_mx<5, false, false>, hipFuncAttributeMaxDynamicSharedMemorySize,
                               160 * 1024);
-    attr_done = true;
-  }
+    return true;
+  }();
+  (void)attr_done;
   const size_t lds = mx_lds_bytes(L, false);
   auto grid = [&](int I, int J) {
     const long tiles = (long)((I + GM_BM - 1) / GM_BM) * ((J + GM_BN - 1) / GM_BN) * L;

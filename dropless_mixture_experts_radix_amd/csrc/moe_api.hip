@@ -142,18 +142,17 @@ int moe_route_topk_grouped(int T, int E, int K, int H, int n_group, int topk_gro
 // ---------------------------------------------------------------------------
 size_t moe_permute_workspace_bytes(int T, int K, int L) {
   if (T < 0 || K <= 0 || L <= 0) return 0;
-  const int TT = permute_tile_tokens(T, K);
-  const size_t ntiles = (size_t)((T + TT - 1) / TT);
-  return round_up((ntiles * L + (size_t)T * K) * sizeof(int32_t), 256) + 256;
+  return permute_workspace_bytes(T, K, L);
 }
 
-int moe_permute(int T, int H, int K, int E_global, int e0, int L, int64_t capacity, int x_dtype,
-                int out_dtype, const void* x, const int16_t* ids, int32_t* counts, int32_t* offsets,
-                void* x_perm, uint8_t* x_perm_scales, int32_t* row_to_slot, int32_t* slot_to_row,
-                int32_t* err, void* workspace, size_t workspace_bytes, void* stream) {
+// argument checks of moe_permute
+static int permute_check(int T, int H, int K, int E_global, int e0, int L, int64_t capacity, int x_dtype,
+                         int out_dtype, const void* x, const int16_t* ids, int32_t* counts, int32_t* offsets,
+                         void* x_perm, uint8_t* x_perm_scales, int32_t* row_to_slot, int32_t* slot_to_row) {
   if (T < 0 || H <= 0 || K < 1 || K > MOE_MAX_K || E_global <= 0 || E_global > 32767 || L < 1 ||
       L > MOE_MAX_L || e0 < 0 || e0 + L > E_global || capacity < 0)
     return MOE_ERR_SHAPE;
+  if ((int64_t)T * K >= ((int64_t)1 << 30)) return MOE_ERR_SHAPE;  // counts fit the 30-bit look-back flags
   if (x_dtype != MOE_BF16 && x_dtype != MOE_F32) return MOE_ERR_DTYPE;
   const bool mx_out = out_dtype == MOE_MXFP8 || out_dtype == MOE_MXFP4;
   if (!(out_dtype == x_dtype || (mx_out && x_dtype == MOE_BF16))) return MOE_ERR_DTYPE;
@@ -164,6 +163,16 @@ int moe_permute(int T, int H, int K, int E_global, int e0, int L, int64_t capaci
   if (capacity > 0 && (!x_perm || !row_to_slot)) return MOE_ERR_NULL;
   if (mx_out && capacity > 0 && !x_perm_scales) return MOE_ERR_NULL;
   if (!aligned16(x) || !aligned16(x_perm)) return MOE_ERR_ALIGN;
+  return MOE_OK;
+}
+
+int moe_permute(int T, int H, int K, int E_global, int e0, int L, int64_t capacity, int x_dtype,
+                int out_dtype, const void* x, const int16_t* ids, int32_t* counts, int32_t* offsets,
+                void* x_perm, uint8_t* x_perm_scales, int32_t* row_to_slot, int32_t* slot_to_row,
+                int32_t* err, void* workspace, size_t workspace_bytes, void* stream) {
+  const int st = permute_check(T, H, K, E_global, e0, L, capacity, x_dtype, out_dtype, x, ids, counts, offsets,
+                               x_perm, x_perm_scales, row_to_slot, slot_to_row);
+  if (st != MOE_OK) return st;
   if (!workspace || workspace_bytes < moe_permute_workspace_bytes(T, K, L)) return MOE_ERR_WORKSPACE;
   if (!aligned16(workspace)) return MOE_ERR_ALIGN;
   return launch_status(launch_permute(T, H, K, E_global, e0, L, capacity, x_dtype, out_dtype, x, ids, counts,
@@ -233,10 +242,10 @@ size_t moe_grouped_mlp_workspace_bytes(int64_t capacity, int F, int dtype) {
   return round_up(a, 256);
 }
 
-int moe_grouped_mlp(int L, int H, int F, int64_t capacity, int dtype, const void* x_perm,
-                    const uint8_t* x_perm_scales, const int32_t* offsets, const void* w1p,
-                    const uint8_t* w1p_scales, const void* w2p, const uint8_t* w2p_scales, void* y_perm,
-                    void* workspace, size_t workspace_bytes, void* stream) {
+static int grouped_mlp(int L, int H, int F, int64_t capacity, int dtype, const void* x_perm,
+                       const uint8_t* x_perm_scales, const int32_t* offsets, const void* w1p, const uint8_t* w1p_scales,
+                       const void* w2p, const uint8_t* w2p_scales, void* y_perm, void* workspace, size_t workspace_bytes,
+                       void* act_bf16, void* stream) {
   if (L < 1 || L > MOE_MAX_L || H <= 0 || F <= 0 || capacity < 0 || capacity > (int64_t)1 << 31)
     return MOE_ERR_SHAPE;
   if (dtype == MOE_F32) {
@@ -255,10 +264,12 @@ int moe_grouped_mlp(int L, int H, int F, int64_t capacity, int dtype, const void
     return MOE_ERR_DTYPE;
   }
   const bool mx = dtype == MOE_MXFP8 || dtype == MOE_MXFP4;
+  if (act_bf16 && !mx) return MOE_ERR_DTYPE;  // the bf16 / fp32 workspace already holds `a`
   if (!offsets) return MOE_ERR_NULL;
   if (capacity > 0 && (!x_perm || !w1p || !w2p || !y_perm)) return MOE_ERR_NULL;
   if (mx && capacity > 0 && (!x_perm_scales || !w1p_scales || !w2p_scales)) return MOE_ERR_NULL;
-  if (!aligned16(x_perm) || !aligned16(w1p) || !aligned16(w2p) || !aligned16(y_perm)) return MOE_ERR_ALIGN;
+  if (!aligned16(x_perm) || !aligned16(w1p) || !aligned16(w2p) || !aligned16(y_perm) || !aligned16(act_bf16))
+    return MOE_ERR_ALIGN;
   if (mx && (((uintptr_t)x_perm_scales | (uintptr_t)w1p_scales | (uintptr_t)w2p_scales) & 3u))
     return MOE_ERR_ALIGN;  // scale words are read 4 bytes at a time
   if (!workspace || workspace_bytes < moe_grouped_mlp_workspace_bytes(capacity, F, dtype))
@@ -280,9 +291,26 @@ int moe_grouped_mlp(int L, int H, int F, int64_t capacity, int dtype, const void
     float* part = (float*)(act_s + round_up((size_t)capacity * (F / 32), 256));
     e = launch_grouped_mlp_mx(L, H, F, capacity, fp4, (const uint8_t*)x_perm, x_perm_scales, offsets,
                               (const uint8_t*)w1p, w1p_scales, (const uint8_t*)w2p, w2p_scales, act, act_s,
-                              part, (bf16_t*)y_perm, s);
+                              part, (bf16_t*)y_perm, (bf16_t*)act_bf16, s);
   }
   return launch_status(e);
+}
+
+int moe_grouped_mlp(int L, int H, int F, int64_t capacity, int dtype, const void* x_perm,
+                    const uint8_t* x_perm_scales, const int32_t* offsets, const void* w1p,
+                    const uint8_t* w1p_scales, const void* w2p, const uint8_t* w2p_scales, void* y_perm,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+  return grouped_mlp(L, H, F, capacity, dtype, x_perm, x_perm_scales, offsets, w1p, w1p_scales, w2p, w2p_scales,
+                     y_perm, workspace, workspace_bytes, nullptr, stream);
+}
+
+int moe_grouped_mlp_with_act(int L, int H, int F, int64_t capacity, int dtype, const void* x_perm,
+                             const uint8_t* x_perm_scales, const int32_t* offsets, const void* w1p,
+                             const uint8_t* w1p_scales, const void* w2p, const uint8_t* w2p_scales, void* y_perm,
+                             void* workspace, size_t workspace_bytes, void* act_bf16, void* stream) {
+  if (!act_bf16) return MOE_ERR_NULL;
+  return grouped_mlp(L, H, F, capacity, dtype, x_perm, x_perm_scales, offsets, w1p, w1p_scales, w2p, w2p_scales,
+                     y_perm, workspace, workspace_bytes, act_bf16, stream);
 }
 
 // ---------------------------------------------------------------------------
@@ -332,21 +360,32 @@ size_t moe_grouped_mlp_backward_workspace_bytes(int64_t capacity, int H, int F, 
 int moe_grouped_mlp_backward_data(int L, int H, int F, int64_t capacity, int dtype, const void* x_perm,
                                   const int32_t* offsets, const void* w1p, const uint8_t* w1p_scales,
                                   const void* w1t, const uint8_t* w1t_scales, const void* w2t,
-                                  const uint8_t* w2t_scales, const void* d_y_perm, void* d_x_perm, void* workspace,
-                                  size_t workspace_bytes, void* stream) {
+                                  const uint8_t* w2t_scales, const void* d_y_perm, void* d_x_perm,
+                                  const uint8_t* x_perm_q, const uint8_t* x_perm_q_scales, const uint8_t* d_y_perm_q,
+                                  const uint8_t* d_y_perm_q_scales, void* workspace, size_t workspace_bytes,
+                                  void* stream) {
   if (L < 1 || L > MOE_MAX_L || H <= 0 || F <= 0 || capacity < 0 || capacity > (int64_t)1 << 31)
     return MOE_ERR_SHAPE;
   if (dtype != MOE_BF16 && dtype != MOE_MXFP8) return MOE_ERR_DTYPE;
   if (H % 128 || F % 128) return MOE_ERR_SHAPE;
   if (dtype == MOE_MXFP8 && (H % 256 || F % 256)) return MOE_ERR_SHAPE;
   if (dtype == MOE_MXFP8 && (!w1p_scales || !w1t_scales || !w2t_scales)) return MOE_ERR_NULL;
+  if (dtype == MOE_MXFP8 && (((uintptr_t)w1p_scales | (uintptr_t)w1t_scales | (uintptr_t)w2t_scales) & 3u))
+    return MOE_ERR_ALIGN;  // scale words are read 4 bytes at a time, as in the forward
   // byte offsets of the k-blocked h / d_h buffers and of the rows stay within 31 bits
   if (capacity * (int64_t)(H > 2 * F ? H : 2 * F) * 2 > (int64_t)INT32_MAX) return MOE_ERR_SHAPE;
   if (!offsets || !w1p || !w1t || !w2t) return MOE_ERR_NULL;
-  if (capacity > 0 && (!x_perm || !d_y_perm || !d_x_perm || !workspace)) return MOE_ERR_NULL;
+  // MXFP8: row-wise MX operands of x_perm and d_y may come from their producers
+  const bool xq_given = x_perm_q || x_perm_q_scales, dyq_given = d_y_perm_q || d_y_perm_q_scales;
+  if ((xq_given || dyq_given) && dtype != MOE_MXFP8) return MOE_ERR_DTYPE;
+  if ((xq_given && (!x_perm_q || !x_perm_q_scales)) || (dyq_given && (!d_y_perm_q || !d_y_perm_q_scales)))
+    return MOE_ERR_NULL;
+  if (capacity > 0 && ((!x_perm && !xq_given) || (!d_y_perm && !dyq_given) || !d_x_perm || !workspace))
+    return MOE_ERR_NULL;
   if (!aligned16(x_perm) || !aligned16(w1p) || !aligned16(w1t) || !aligned16(w2t) || !aligned16(d_y_perm) ||
-      !aligned16(d_x_perm) || !aligned16(workspace))
+      !aligned16(d_x_perm) || !aligned16(workspace) || !aligned16(x_perm_q) || !aligned16(d_y_perm_q))
     return MOE_ERR_ALIGN;
+  if (((uintptr_t)x_perm_q_scales | (uintptr_t)d_y_perm_q_scales) & 3u) return MOE_ERR_ALIGN;
   if (capacity > 0 && workspace_bytes < moe_grouped_mlp_backward_workspace_bytes(capacity, H, F, dtype))
     return MOE_ERR_WORKSPACE;
   bf16_t* hbuf = (bf16_t*)workspace;
@@ -363,10 +402,18 @@ int moe_grouped_mlp_backward_data(int L, int H, int F, int64_t capacity, int dty
     uint8_t* dhq = w;  w += round_up((size_t)capacity * 2 * F, 256);
     uint8_t* dhqs = w; w += round_up((size_t)capacity * (2 * F / 32), 256);
     float* da = (float*)w;
+    if (xq_given) {
+      xq = (uint8_t*)x_perm_q;
+      xqs = (uint8_t*)x_perm_q_scales;
+    }
+    if (dyq_given) {
+      dyq = (uint8_t*)d_y_perm_q;
+      dyqs = (uint8_t*)d_y_perm_q_scales;
+    }
     return launch_status(launch_grouped_mlp_mx_backward(
         L, H, F, capacity, (const bf16_t*)x_perm, offsets, (const uint8_t*)w1p, w1p_scales, (const uint8_t*)w1t,
         w1t_scales, (const uint8_t*)w2t, w2t_scales, (const bf16_t*)d_y_perm, xq, xqs, dyq, dyqs, hbuf, dhbuf, dhq,
-        dhqs, da, part, (bf16_t*)d_x_perm, (hipStream_t)stream));
+        dhqs, da, part, (bf16_t*)d_x_perm, xq_given, dyq_given, (hipStream_t)stream));
   }
   return launch_status(launch_grouped_mlp_bf16_backward(L, H, F, capacity, (const bf16_t*)x_perm, offsets,
                                                         (const bf16_t*)w1p, (const bf16_t*)w1t, (const bf16_t*)w2t,
@@ -485,13 +532,19 @@ int moe_grouped_mlp_backward_weights(int L, int H, int F, int64_t capacity, int 
 // ---------------------------------------------------------------------------
 int moe_unpermute_combine_backward(int T, int K, int H, int dtype, const void* dout, const void* y_perm,
                                    const int32_t* slot_to_row, const float* probs, void* d_y_perm,
-                                   float* d_probs, void* stream) {
+                                   float* d_probs, uint8_t* d_y_perm_q, uint8_t* d_y_perm_q_scales, void* stream) {
   if (T < 0 || K < 1 || K > MOE_MAX_K || H <= 0 || H % 8) return MOE_ERR_SHAPE;
   if (dtype != MOE_BF16 && dtype != MOE_F32) return MOE_ERR_DTYPE;
   if (T > 0 && (!dout || !slot_to_row || !probs || !d_probs)) return MOE_ERR_NULL;
   if (!aligned16(dout) || !aligned16(y_perm) || !aligned16(d_y_perm)) return MOE_ERR_ALIGN;
+  if (d_y_perm_q || d_y_perm_q_scales) {  // the MX operand form of d_y as well
+    if (dtype != MOE_BF16) return MOE_ERR_DTYPE;
+    if (H % 32) return MOE_ERR_SHAPE;
+    if (!d_y_perm_q || !d_y_perm_q_scales) return MOE_ERR_NULL;
+    if (!aligned16(d_y_perm_q)) return MOE_ERR_ALIGN;
+  }
   return launch_status(launch_combine_backward(T, K, H, dtype, dout, y_perm, slot_to_row, probs, d_y_perm,
-                                               d_probs, (hipStream_t)stream));
+                                               d_probs, d_y_perm_q, d_y_perm_q_scales, (hipStream_t)stream));
 }
 
 int moe_permute_backward(int T, int K, int H, int dtype, const void* d_x_perm, const int32_t* slot_to_row,
@@ -517,6 +570,59 @@ int moe_route_backward(int T, int E, int K, int score, float scale, const int16_
 }
 
 // ---------------------------------------------------------------------------
+// Size queries (host only: no HIP call)
+// ---------------------------------------------------------------------------
+int moe_query_sizes(const moe_shape* sh, moe_sizes* out) {
+  if (!sh || !out) return MOE_ERR_NULL;
+  const int T = sh->T, H = sh->H, E = sh->E, K = sh->K, F = sh->F, dt = sh->dtype;
+  const int L = sh->L > 0 ? sh->L : E;
+  if (T < 0 || H <= 0 || E <= 0 || E > MOE_MAX_E || K < 1 || K > E || K > MOE_MAX_K || F <= 0 || L > E ||
+      L > MOE_MAX_L)
+    return MOE_ERR_SHAPE;
+  if (dt != MOE_F32 && dt != MOE_BF16 && dt != MOE_MXFP8 && dt != MOE_MXFP4) return MOE_ERR_DTYPE;
+  if (sh->x_dtype != MOE_F32 && sh->x_dtype != MOE_BF16) return MOE_ERR_DTYPE;
+  if (sh->w_dtype != MOE_F32 && sh->w_dtype != MOE_BF16) return MOE_ERR_DTYPE;
+  moe_sizes z = {};
+  // moe_route_topk gives each token K distinct experts, so at most min(K, L)
+  // of its slots are local; caller-supplied ids may repeat an expert (each
+  // slot then has its own row), which needs T * K rows
+  z.capacity = (int64_t)T * (K < L ? K : L);
+  z.capacity_any_ids = (int64_t)T * K;
+  const int64_t cap = z.capacity;
+  z.router_prepared_bytes = moe_router_prepared_bytes(H, E, sh->w_dtype, sh->x_dtype);
+  z.route_workspace_bytes = moe_route_workspace_bytes(T, E, H, sh->x_dtype);
+  z.permute_workspace_bytes = moe_permute_workspace_bytes(T, K, L);
+  z.permute_state_bytes = permute_state_bytes(T, K, L);
+  z.w1p_bytes = moe_prepared_weight_bytes(L, H, F, dt, 1);
+  z.w2p_bytes = moe_prepared_weight_bytes(L, H, F, dt, 2);
+  z.w1p_scales_bytes = moe_prepared_weight_bytes(L, H, F, dt, 3);
+  z.w2p_scales_bytes = moe_prepared_weight_bytes(L, H, F, dt, 4);
+  z.mlp_workspace_bytes = moe_grouped_mlp_workspace_bytes(cap, F, dt);
+  z.mlp_act_offset = 0;
+  if (dt == MOE_MXFP8 || dt == MOE_MXFP4)
+    z.mlp_act_scales_offset = round_up((size_t)cap * (dt == MOE_MXFP4 ? F / 2 : F), 256);
+  if (dt == MOE_BF16 || dt == MOE_MXFP8) {
+    z.w1t_bytes = moe_prepared_weight_bytes(L, H, F, dt, 5);
+    z.w2t_bytes = moe_prepared_weight_bytes(L, H, F, dt, 6);
+    z.w1t_scales_bytes = moe_prepared_weight_bytes(L, H, F, dt, 7);
+    z.w2t_scales_bytes = moe_prepared_weight_bytes(L, H, F, dt, 8);
+    z.mlp_backward_workspace_bytes = moe_grouped_mlp_backward_workspace_bytes(cap, H, F, dt);
+    z.bwd_h_offset = 0;
+    z.bwd_dh_offset = round_up((size_t)cap * 2 * F * 2, 256);
+    if (dt == MOE_MXFP8) {
+      const size_t part = grouped_mlp_bf16_part_bytes() > grouped_mlp_mx_part_bytes() ? grouped_mlp_bf16_part_bytes()
+                                                                                      : grouped_mlp_mx_part_bytes();
+      const size_t w = 2 * z.bwd_dh_offset + round_up(part, 256) + 2 * mx_rows_bytes(cap, H);
+      z.bwd_dh_codes_offset = w;
+      z.bwd_dh_scales_offset = w + round_up((size_t)cap * 2 * F, 256);
+    }
+    z.mlp_backward_weights_workspace_bytes = moe_grouped_mlp_backward_weights_workspace_bytes(L, cap, H, F, dt);
+  }
+  *out = z;
+  return MOE_OK;
+}
+
+// ---------------------------------------------------------------------------
 // Standalone MX quantizer
 // ---------------------------------------------------------------------------
 int moe_mx_quantize(int64_t rows, int cols, const void* in, const int32_t* row_limit, uint8_t* codes,
@@ -526,6 +632,47 @@ int moe_mx_quantize(int64_t rows, int cols, const void* in, const int32_t* row_l
   if (!aligned16(in) || !aligned16(codes)) return MOE_ERR_ALIGN;
   return launch_status(launch_mx_quantize(rows, cols, (const bf16_t*)in, row_limit, codes, scales,
                                           (hipStream_t)stream));
+}
+
+// ---------------------------------------------------------------------------
+// Calibration kernels (measurement support)
+// ---------------------------------------------------------------------------
+int moe_calib_copy(const void* src, void* dst, size_t bytes, void* stream) {
+  if (bytes == 0) return MOE_OK;
+  if (!src || !dst) return MOE_ERR_NULL;
+  if (bytes % 16) return MOE_ERR_SHAPE;
+  if (!aligned16(src) || !aligned16(dst)) return MOE_ERR_ALIGN;
+  return launch_status(launch_calib_copy(src, dst, bytes, (hipStream_t)stream));
+}
+
+size_t moe_calib_read_out_words(size_t bytes) {
+  int blocks = 0;
+  (void)launch_calib_read(nullptr, bytes, nullptr, &blocks, nullptr);
+  return (size_t)blocks;
+}
+
+int moe_calib_read(const void* src, size_t bytes, uint32_t* out, void* stream) {
+  if (bytes == 0) return MOE_OK;
+  if (!src || !out) return MOE_ERR_NULL;
+  if (bytes % 16) return MOE_ERR_SHAPE;
+  if (!aligned16(src)) return MOE_ERR_ALIGN;
+  int blocks = 0;
+  return launch_status(launch_calib_read(src, bytes, out, &blocks, (hipStream_t)stream));
+}
+
+int moe_calib_write(void* dst, size_t bytes, uint32_t value, void* stream) {
+  if (bytes == 0) return MOE_OK;
+  if (!dst) return MOE_ERR_NULL;
+  if (bytes % 16) return MOE_ERR_SHAPE;
+  if (!aligned16(dst)) return MOE_ERR_ALIGN;
+  return launch_status(launch_calib_write(dst, bytes, value, (hipStream_t)stream));
+}
+
+int moe_calib_mfma(int dtype, int blocks, int iters, float* out, void* stream) {
+  if (dtype != MOE_BF16 && dtype != MOE_MXFP8) return MOE_ERR_DTYPE;
+  if (blocks < 1 || blocks > (1 << 20) || iters < 1) return MOE_ERR_SHAPE;
+  if (!out) return MOE_ERR_NULL;
+  return launch_status(launch_calib_mfma(dtype == MOE_MXFP8, blocks, iters, out, (hipStream_t)stream));
 }
 
 }  // extern "C"

@@ -195,6 +195,8 @@ hipError_t launch_route_select(int T, int E, int K, int S, int score, const floa
                                const RouteGroups* grp = nullptr, float* scores_out = nullptr);
 
 int permute_tile_tokens(int T, int K);
+size_t permute_workspace_bytes(int T, int K, int L);
+size_t permute_state_bytes(int T, int K, int L);  // the zero-between-calls prefix
 hipError_t launch_permute(int T, int H, int K, int E_global, int e0, int L, int64_t capacity,
                           int x_dtype, int out_dtype, const void* x, const int16_t* ids,
                           int32_t* counts, int32_t* offsets, void* x_perm, uint8_t* x_scales,
@@ -220,7 +222,8 @@ hipError_t launch_grouped_mlp_mx_backward(int L, int H, int F, int64_t capacity,
                                           const uint8_t* w1t, const uint8_t* w1ts, const uint8_t* w2t,
                                           const uint8_t* w2ts, const bf16_t* dy, uint8_t* xq, uint8_t* xqs,
                                           uint8_t* dyq, uint8_t* dyqs, bf16_t* hbuf, bf16_t* dhbuf, uint8_t* dhq,
-                                          uint8_t* dhqs, float* da, float* part, bf16_t* dx, hipStream_t s);
+                                          uint8_t* dhqs, float* da, float* part, bf16_t* dx, bool x_given,
+                                          bool dy_given, hipStream_t s);
 hipError_t launch_prepare_weights_backward(int L, int H, int F, int dtype, const void* w1, const void* w2,
                                            void* w1t, void* w2t, uint8_t* w1ts, uint8_t* w2ts, hipStream_t s);
 hipError_t launch_mx_columns_grouped(int L, int64_t capacity, int C, int nbmax, const bf16_t* in,
@@ -248,16 +251,22 @@ size_t grouped_mlp_mx_part_bytes();
 hipError_t launch_grouped_mlp_mx(int L, int H, int F, int64_t capacity, bool fp4, const uint8_t* x,
                                  const uint8_t* xs, const int32_t* offsets, const uint8_t* w1p,
                                  const uint8_t* w1s, const uint8_t* w2p, const uint8_t* w2s,
-                                 uint8_t* act, uint8_t* act_s, float* part, bf16_t* y, hipStream_t s);
+                                 uint8_t* act, uint8_t* act_s, float* part, bf16_t* y, bf16_t* act_bf16,
+                                 hipStream_t s);
 
 hipError_t launch_combine(int T, int K, int H, int dtype, const void* y, const int32_t* s2r,
                           const float* probs, void* out, hipStream_t s);
 hipError_t launch_combine_backward(int T, int K, int H, int dtype, const void* dout, const void* y,
-                                   const int32_t* s2r, const float* probs, void* dy, float* dprobs,
-                                   hipStream_t s);
+                                   const int32_t* s2r, const float* probs, void* dy, float* dprobs, uint8_t* dyq,
+                                   uint8_t* dyqs, hipStream_t s);
 hipError_t launch_route_backward(int T, int E, int K, int score, float scale, const int16_t* ids,
                                  const float* probs, const float* dprobs, const float* logits,
                                  const float* score_bias, float* dz, hipStream_t s);
+
+hipError_t launch_calib_copy(const void* src, void* dst, size_t bytes, hipStream_t s);
+hipError_t launch_calib_read(const void* src, size_t bytes, uint32_t* out, int* blocks, hipStream_t s);
+hipError_t launch_calib_write(void* dst, size_t bytes, uint32_t v, hipStream_t s);
+hipError_t launch_calib_mfma(int fp8, int blocks, int iters, float* out, hipStream_t s);
 
 hipError_t launch_mx_quantize(int64_t rows, int cols, const bf16_t* in, const int32_t* row_limit,
                               uint8_t* codes, uint8_t* scales, hipStream_t s);

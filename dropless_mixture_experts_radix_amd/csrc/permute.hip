@@ -5,14 +5,15 @@
 // wavefront ballot over its K slots, iterating the set bits).  bpdata article,
 // "Optimization 1: Grouped GEMM": expert token counts stay on the device.
 //
-// Three kernels, no host round trip:
-//  k_count    per tile of TT tokens: per-local-expert histogram (LDS), and the
-//             stable rank of every local slot among the tile's slots of the
-//             same expert (wavefront ballots, flat slot order).
-//  k_scan     one workgroup, one pass over the tile histograms: per-tile
-//             expert bases, counts[L], offsets[L+1], overflow check.
-//  k_permute  one wavefront per token: ballot over its K slots, read the row
-//             once, write it to each selected local expert row.
+// Two kernels, no host round trip:
+//  k_count_scan  per tile of TT tokens: per-local-expert histogram (LDS), the
+//                stable rank of every local slot among the tile's slots of
+//                the same expert (wavefront ballots, flat slot order), and a
+//                single-pass decoupled look-back scan across tiles: per-tile
+//                expert bases; the last tile writes counts[L], offsets[L+1]
+//                and the overflow flag.
+//  k_permute     one wavefront per token: ballot over its K slots, read the
+//                row once, write it to each selected local expert row.
 #include "moe_internal.h"
 
 namespace moe {
@@ -31,25 +32,107 @@ int permute_tile_tokens(int T, int K) {
 }
 
 // ---------------------------------------------------------------------------
-// k_count: grid = ntiles, 256 threads.  Dynamic LDS: cnt[4][L] int32 +
-// rank[TT*K] int32.
+// Workspace of the permute (byte offsets; ntiles tiles of TT tokens):
+//   [0, 256)                    the tile ticket counter (uint32)
+//   [256, ...)                  look-back flags [ntiles][L] uint32
+//   next 256-byte boundary      each slot's row within its expert [T*K] int32
+// All of it is zero between calls: the caller zero-fills the workspace once,
+// and k_permute returns everything a call wrote to zero (the flags, the
+// counter, and each slot's row once it has been read), so calls of different
+// shapes can share one workspace.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void k_count(int T, int K, int E_global, int e0, int L, int TT,
-                                               const int16_t* __restrict__ ids,
-                                               int32_t* __restrict__ hist, int32_t* __restrict__ rank,
-                                               int32_t* err) {
+struct PermuteWs {
+  uint32_t* ticket;
+  uint32_t* flags;
+  int32_t* rank;
+};
+
+static inline size_t ws_round(size_t v) { return (v + 255) / 256 * 256; }
+
+static PermuteWs permute_ws(void* ws, int ntiles, int L) {
+  uint8_t* b = (uint8_t*)ws;
+  PermuteWs w;
+  w.ticket = (uint32_t*)b;
+  w.flags = (uint32_t*)(b + 256);
+  w.rank = (int32_t*)(b + 256 + ws_round((size_t)ntiles * L * 4));
+  return w;
+}
+
+size_t permute_state_bytes(int T, int K, int L) {
+  const int TT = permute_tile_tokens(T, K);
+  const size_t ntiles = (size_t)(T > 0 ? (T + TT - 1) / TT : 0);
+  return 256 + ws_round(ntiles * L * 4);
+}
+
+size_t permute_workspace_bytes(int T, int K, int L) {
+  const int TT = permute_tile_tokens(T, K);
+  const size_t ntiles = (size_t)(T > 0 ? (T + TT - 1) / TT : 0);
+  return 256 + ws_round(ntiles * L * 4) + ws_round((size_t)T * K * 4);
+}
+
+// A look-back flag: the tile's count of one expert (AGG: its own slots; INCL:
+// its slots and every earlier tile's) in the low 30 bits.  0: not yet known.
+#define PERM_AGG (1u << 30)
+#define PERM_INCL (2u << 30)
+#define PERM_VALUE ((1u << 30) - 1)
+// bound on the polls of one flag (each after s_sleep 2, about 0.1 us): a
+// predecessor tile publishes its count within microseconds of starting, so
+// the bound is only reached when the workspace was not zero-filled; the
+// tile then reports MOE_DEVERR_WORKSPACE instead of waiting forever
+#define PERM_MAX_POLLS (1 << 20)
+
+__device__ __forceinline__ uint32_t flag_load(const uint32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void flag_store(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// ---------------------------------------------------------------------------
+// k_count_scan: grid = ntiles, 256 threads.  Dynamic LDS: cnt[4][L] + tot[L]
+// + base[L] + rank[TT*K] int32.
+//
+// A workgroup takes the next tile from the ticket counter (so every earlier
+// tile belongs to a workgroup that has started), counts its local slots per
+// expert (LDS histograms; the stable rank of each slot among the tile's slots
+// of its expert from wavefront ballots, flat slot order), and then finds each
+// expert's count in all earlier tiles by a decoupled look-back (Merrill and
+// Garland, "Single-pass Parallel Prefix Scan with Decoupled Look-back", 2016):
+// it publishes its own count (AGG), adds the predecessors' published counts
+// until one of them is inclusive (INCL), and publishes its inclusive count.
+// The exclusive count is the tile's base for that expert; each local slot's
+// row within its expert (base + its rank in the tile) goes to `rank`.  The
+// last tile's inclusive counts are the expert totals: it writes counts,
+// offsets (their exclusive scan) and the overflow flag.  One pass over the
+// ids, no second kernel over the tile histograms.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_count_scan(int T, int K, int E_global, int e0, int L, int TT, int ntiles,
+                                                    int64_t capacity, const int16_t* __restrict__ ids,
+                                                    uint32_t* __restrict__ ticket, uint32_t* __restrict__ flags,
+                                                    int32_t* __restrict__ rank,
+                                                    int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+                                                    int32_t* err) {
   extern __shared__ int32_t lds[];
   int32_t* cnt = lds;              // [4][L]
-  int32_t* srank = lds + 4 * L;    // [TT*K]
+  int32_t* tot = lds + 4 * L;      // [L] inclusive counts (last tile)
+  int32_t* base = lds + 5 * L;     // [L] exclusive counts: the tile's base per expert
+  int32_t* srank = lds + 6 * L;    // [TT*K]
+  __shared__ int s_tile;
+  __shared__ int s_wsum[4];
   const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
-  const int tile = blockIdx.x;
+  if (threadIdx.x == 0) s_tile = (int)atomicAdd(ticket, 1u);
+  for (int i = threadIdx.x; i < 4 * L; i += 256) cnt[i] = 0;
+  __syncthreads();
+  const int tile = s_tile;
+  if ((unsigned)tile >= (unsigned)ntiles) {  // the counter was not zero: a workspace that was not zero-filled
+    if (threadIdx.x == 0) set_err(err, MOE_DEVERR_WORKSPACE);
+    return;
+  }
   const long f0 = (long)tile * TT * K;
   long fend = f0 + (long)TT * K;
   const long ftot = (long)T * K;
   if (fend > ftot) fend = ftot;
   const int nslot = (int)(fend - f0);
-  for (int i = threadIdx.x; i < 4 * L; i += 256) cnt[i] = 0;
-  __syncthreads();
   // wave w handles slots [w*part, (w+1)*part) of the tile, 64 at a time
   const int part = (((nslot + 3) / 4) + 63) / 64 * 64;
   const int s_begin = w * part, s_end = min(nslot, s_begin + part);
@@ -78,171 +161,118 @@ __global__ __launch_bounds__(256) void k_count(int T, int K, int E_global, int e
   }
   if (wave_ballot(bad) && l == 0) set_err(err, MOE_DEVERR_BAD_ID);
   __syncthreads();
-  // tile histogram and per-wave bases
+  // per-wave bases, the tile's count of each expert, the look-back
+  bool stuck = false;
   for (int e = threadIdx.x; e < L; e += 256) {
     const int c0 = cnt[e], c1 = cnt[L + e], c2 = cnt[2 * L + e], c3 = cnt[3 * L + e];
-    hist[(long)tile * L + e] = c0 + c1 + c2 + c3;
+    const int agg = c0 + c1 + c2 + c3;
     cnt[e] = 0;
     cnt[L + e] = c0;
     cnt[2 * L + e] = c0 + c1;
     cnt[3 * L + e] = c0 + c1 + c2;
+    uint32_t* mine = flags + (long)tile * L + e;
+    int excl = 0;
+    if (tile == 0) {
+      flag_store(mine, PERM_INCL | (uint32_t)agg);
+    } else {
+      flag_store(mine, PERM_AGG | (uint32_t)agg);
+      for (int p = tile - 1; p >= 0; --p) {
+        const uint32_t* fp = flags + (long)p * L + e;
+        uint32_t f = flag_load(fp);
+        for (int polls = 0; f == 0u; ++polls) {
+          if (polls >= PERM_MAX_POLLS) { stuck = true; break; }
+          __builtin_amdgcn_s_sleep(2);
+          f = flag_load(fp);
+        }
+        if (stuck) break;
+        excl += (int)(f & PERM_VALUE);
+        if ((f & ~PERM_VALUE) == PERM_INCL) break;
+      }
+      flag_store(mine, PERM_INCL | (uint32_t)(excl + agg));
+    }
+    // a count outside [0, T*K] can only come from flags that were not zero
+    // before the call: report it, and keep the offsets monotone and >= 0
+    const int tk = T * K;
+    if (excl < 0 || excl > tk - agg) {
+      stuck = true;
+      excl = excl < 0 ? 0 : tk - agg;
+    }
+    base[e] = excl;
+    tot[e] = excl + agg;
   }
+  if (stuck) set_err(err, MOE_DEVERR_WORKSPACE);
   __syncthreads();
   for (int sl = threadIdx.x; sl < nslot; sl += 256) {
     const int id = ids[f0 + sl];
     int r = 0;
-    if (id >= e0 && id < e0 + L && id < E_global) {
-      const int ww = sl / part;
-      r = srank[sl] + cnt[ww * L + (id - e0)];
-    }
+    if (id >= e0 && id < e0 + L && id < E_global)
+      r = base[id - e0] + srank[sl] + cnt[(sl / part) * L + (id - e0)];
     rank[f0 + sl] = r;
   }
-}
-
-// ---------------------------------------------------------------------------
-// k_scan: one workgroup of 1024 threads.  hist [ntiles][L] -> exclusive tile
-// bases (in place), counts, offsets, overflow flag.
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(1024) void k_scan(int ntiles, int L, int64_t capacity,
-                                               int32_t* __restrict__ hist, int32_t* __restrict__ counts,
-                                               int32_t* __restrict__ offsets, int32_t* err) {
-  __shared__ int32_t s_part[1024];
-  __shared__ int32_t s_tot[MOE_MAX_L];
-  __shared__ int32_t s_wsum[16];
-  const int tid = threadIdx.x;
-  // experts handled in groups of up to 1024; each expert column split in nparts
-  for (int eb = 0; eb < L; eb += 1024) {
-    const int Lb = min(1024, L - eb);
-    int nparts = 1024 / Lb;
-    if (nparts > ntiles) nparts = ntiles > 0 ? ntiles : 1;
-    const int per = (ntiles + nparts - 1) / nparts;
-    const int e = tid % Lb, part = tid / Lb;
-    const bool act = part < nparts;
-    int sum = 0;
-    if (act) {
-      const int t0 = part * per, t1 = min(ntiles, t0 + per);
-      for (int t = t0; t < t1; ++t) sum += hist[(long)t * L + eb + e];
-    }
-    __syncthreads();
-    s_part[tid] = act ? sum : 0;
-    __syncthreads();
-    if (act) {
-      int base = 0;
-      for (int p = 0; p < part; ++p) base += s_part[p * Lb + e];
-      const int t0 = part * per, t1 = min(ntiles, t0 + per);
-      // 16 tiles at a time: all their loads are issued before the in-place
-      // stores, which the compiler could not move the next loads across
-      for (int tb = t0; tb < t1; tb += 16) {
-        int c[16];
-#pragma unroll
-        for (int u = 0; u < 16; ++u) c[u] = tb + u < t1 ? hist[(long)(tb + u) * L + eb + e] : 0;
-#pragma unroll
-        for (int u = 0; u < 16; ++u) {
-          if (tb + u < t1) hist[(long)(tb + u) * L + eb + e] = base;
-          base += c[u];
-        }
-      }
-      if (part == nparts - 1) s_tot[eb + e] = base;
-    }
-    __syncthreads();
-  }
-  // offsets: exclusive scan of the totals (each thread owns up to 4 experts)
-  const int per = (L + 1023) / 1024;
-  const int b0 = tid * per;
+  if (tile != ntiles - 1) return;
+  // the last tile: expert totals -> counts, offsets (exclusive scan), overflow
+  const int per = (L + 255) / 256;
+  const int b0 = threadIdx.x * per;
   int loc = 0;
   for (int i = 0; i < per; ++i)
-    if (b0 + i < L) loc += s_tot[b0 + i];
+    if (b0 + i < L) loc += tot[b0 + i];
   const int incl = wave_incl_scan(loc);
-  const int wv = tid >> 6, l = tid & 63;
-  if (l == 63) s_wsum[wv] = incl;
+  if (l == 63) s_wsum[w] = incl;
   __syncthreads();
-  int wbase = 0;
-  for (int i = 0; i < wv; ++i) wbase += s_wsum[i];
-  int run = wbase + incl - loc;
+  int run = incl - loc;
+  for (int i = 0; i < w; ++i) run += s_wsum[i];
   for (int i = 0; i < per; ++i) {
     const int e = b0 + i;
     if (e < L) {
-      counts[e] = s_tot[e];
+      counts[e] = tot[e];
       offsets[e] = run;
-      run += s_tot[e];
+      run += tot[e];
     }
   }
-  if (tid == 1023) {
-    int total = 0;
-    for (int i = 0; i < 16; ++i) total += s_wsum[i];
-    offsets[L] = total;
-    if ((int64_t)total > capacity) set_err(err, MOE_DEVERR_OVERFLOW);
+  if (threadIdx.x == 255) {
+    offsets[L] = run;
+    if ((int64_t)run > capacity) set_err(err, MOE_DEVERR_OVERFLOW);
+  }
+}
+
+// counts and offsets of an empty batch
+__global__ void k_zero_counts(int L, int32_t* __restrict__ counts, int32_t* __restrict__ offsets) {
+  for (int e = threadIdx.x; e <= L; e += blockDim.x) {
+    if (e < L) counts[e] = 0;
+    offsets[e] = 0;
   }
 }
 
 // ---------------------------------------------------------------------------
-// k_permute: one wavefront per token, 4 per workgroup.
+// k_permute: one wavefront per token, 4 per workgroup.  It also returns the
+// workspace to zero for the next call: the look-back state of k_count_scan
+// (which has finished: same stream) and each slot's row once read.
 // ---------------------------------------------------------------------------
-// Fused scan (SCAN = 1, for ntiles * L <= PERMUTE_SCAN_MAX and L <= 64, TT a
-// multiple of 4): `tilebase` holds the raw tile histograms of k_count; every
-// workgroup sums the ones it needs (the tiles before its own, and all of them
-// for the offsets) instead of a separate k_scan, and workgroup 0 writes
-// counts, offsets and the overflow flag.
-#define PERMUTE_SCAN_MAX 4096
-template <int OUT, int SCAN>  // OUT 0: copy rows (bf16 or fp32, row_bytes), 1: MXFP8-, 2: MXFP4-quantize bf16 rows
+template <int OUT>  // OUT 0: copy rows (bf16 or fp32, row_bytes), 1: MXFP8-, 2: MXFP4-quantize bf16 rows
 __global__ __launch_bounds__(256) void k_permute(int T, int K, int e0, int L, int TT, int64_t capacity,
                                                  int row_bytes, const uint8_t* __restrict__ x,
                                                  const int16_t* __restrict__ ids,
-                                                 const int32_t* __restrict__ tilebase,
-                                                 const int32_t* __restrict__ rank,
+                                                 int32_t* __restrict__ rank,
                                                  const int32_t* __restrict__ offsets,
                                                  uint8_t* __restrict__ x_perm, uint8_t* __restrict__ x_scales,
                                                  int32_t* __restrict__ row_to_slot,
-                                                 int32_t* __restrict__ slot_to_row, int32_t* __restrict__ counts_out,
-                                                 int32_t* __restrict__ offsets_out, int32_t* err) {
+                                                 int32_t* __restrict__ slot_to_row, uint32_t* __restrict__ ticket,
+                                                 uint32_t* __restrict__ flags, long nflags) {
   const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + w;
-  __shared__ int32_t s_sum[2][256];  // SCAN: partial sums (before the tile, total)
-  __shared__ int32_t s_base[64], s_off[64];
-  if (SCAN) {
-    // the workgroup's 4 tokens share one tile (TT % 4 == 0); thread i sums
-    // entries (tile' , e) with e = i % L, tile' = i / L, i / L + 256 / L, ...
-    const int tile0 = (blockIdx.x * 4) / TT, ntiles = (T + TT - 1) / TT;
-    const int e = threadIdx.x % L, step = 256 / L;
-    int before = 0, all = 0;
-    if (threadIdx.x < step * L) {
-      for (int tt = threadIdx.x / L; tt < ntiles; tt += step) {
-        const int c = tilebase[(long)tt * L + e];
-        all += c;
-        before += tt < tile0 ? c : 0;
-      }
-    }
-    s_sum[0][threadIdx.x] = before;
-    s_sum[1][threadIdx.x] = all;
-    __syncthreads();
-    if (w == 0) {
-      int b = 0, a = 0;
-      if (l < L)
-        for (int q = 0; q < step; ++q) { b += s_sum[0][q * L + l]; a += s_sum[1][q * L + l]; }
-      const int incl = wave_incl_scan(l < L ? a : 0);
-      if (l < L) { s_base[l] = b; s_off[l] = incl - a; }
-      if (blockIdx.x == 0) {
-        if (l < L) { counts_out[l] = a; offsets_out[l] = incl - a; }
-        if (l == 63) {
-          offsets_out[L] = incl;
-          if ((int64_t)incl > capacity) set_err(err, MOE_DEVERR_OVERFLOW);
-        }
-      }
-    }
-    __syncthreads();
-  }
+  for (long i = (long)blockIdx.x * 256 + threadIdx.x; i < nflags; i += (long)gridDim.x * 256) flags[i] = 0u;
+  if (blockIdx.x == 0 && threadIdx.x == 0) *ticket = 0u;
   if (t >= T) return;
-  const int tile = t / TT;
   int dest = -1;
   if (l < K) {
     const long f = (long)t * K + l;
     const int id = ids[f];
     if (id >= e0 && id < e0 + L) {
       const int le = id - e0;
-      const int64_t d = SCAN ? (int64_t)s_off[le] + s_base[le] + rank[f]
-                             : (int64_t)offsets[le] + tilebase[(long)tile * L + le] + rank[f];
-      dest = d < capacity ? (int)d : -1;
+      const int64_t d = (int64_t)offsets[le] + rank[f];
+      dest = (d >= 0 && d < capacity) ? (int)d : -1;
     }
+    rank[f] = 0;
     slot_to_row[f] = dest;
   }
   uint64_t bits = wave_ballot(dest >= 0);
@@ -331,58 +361,34 @@ __global__ __launch_bounds__(256) void k_permute(int T, int K, int e0, int L, in
   }
 }
 
-template <int SCAN>
-static void launch_permute_rows(int T, int K, int e0, int L, int TT, int64_t capacity, int row_bytes, int out_dtype,
-                                const void* x, const int16_t* ids, const int32_t* hist, const int32_t* rank,
-                                int32_t* offsets, void* x_perm, uint8_t* x_scales, int32_t* row_to_slot,
-                                int32_t* slot_to_row, int32_t* counts, int32_t* err, hipStream_t s) {
-  const dim3 g((T + 3) / 4), b(256);
-  if (out_dtype == MOE_MXFP8)
-    hipLaunchKernelGGL((k_permute<1, SCAN>), g, b, 0, s, T, K, e0, L, TT, capacity, row_bytes, (const uint8_t*)x,
-                       ids, hist, rank, offsets, (uint8_t*)x_perm, x_scales, row_to_slot, slot_to_row, counts,
-                       offsets, err);
-  else if (out_dtype == MOE_MXFP4)
-    hipLaunchKernelGGL((k_permute<2, SCAN>), g, b, 0, s, T, K, e0, L, TT, capacity, row_bytes, (const uint8_t*)x,
-                       ids, hist, rank, offsets, (uint8_t*)x_perm, x_scales, row_to_slot, slot_to_row, counts,
-                       offsets, err);
-  else
-    hipLaunchKernelGGL((k_permute<0, SCAN>), g, b, 0, s, T, K, e0, L, TT, capacity, row_bytes, (const uint8_t*)x,
-                       ids, hist, rank, offsets, (uint8_t*)x_perm, x_scales, row_to_slot, slot_to_row, counts,
-                       offsets, err);
-}
-
 hipError_t launch_permute(int T, int H, int K, int E_global, int e0, int L, int64_t capacity,
                           int x_dtype, int out_dtype, const void* x, const int16_t* ids,
                           int32_t* counts, int32_t* offsets, void* x_perm, uint8_t* x_scales,
                           int32_t* row_to_slot, int32_t* slot_to_row, int32_t* err, void* ws,
                           hipStream_t s) {
-  int TT = permute_tile_tokens(T, K);
-  int ntiles = (T + TT - 1) / TT;
-  // few tiles and experts: the scan is done inside k_permute (tiles of a
-  // multiple of 4 tokens, so that a permute workgroup's tokens share a tile)
-  const int TT4 = (TT + 3) / 4 * 4;
-  const bool fused = T > 0 && L <= 64 && (long)((T + TT4 - 1) / TT4) * L <= PERMUTE_SCAN_MAX;
-  if (fused) {
-    TT = TT4;
-    ntiles = (T + TT - 1) / TT;
+  if (T == 0) {
+    hipLaunchKernelGGL(k_zero_counts, dim3(1), dim3(256), 0, s, L, counts, offsets);
+    return hipGetLastError();
   }
-  int32_t* hist = (int32_t*)ws;
-  int32_t* rank = hist + (size_t)ntiles * L;  // within the workspace (sized for the unrounded tiling)
-  if (ntiles > 0) {
-    const size_t lds = (size_t)(4 * L + TT * K) * sizeof(int32_t);
-    hipLaunchKernelGGL(k_count, dim3(ntiles), dim3(256), lds, s, T, K, E_global, e0, L, TT, ids, hist,
-                       rank, err);
-  }
+  const int TT = permute_tile_tokens(T, K);
+  const int ntiles = (T + TT - 1) / TT;
+  const PermuteWs w = permute_ws(ws, ntiles, L);
+  const size_t lds = (size_t)(6 * L + TT * K) * sizeof(int32_t);
+  hipLaunchKernelGGL(k_count_scan, dim3(ntiles), dim3(256), lds, s, T, K, E_global, e0, L, TT, ntiles, capacity, ids,
+                     w.ticket, w.flags, w.rank, counts, offsets, err);
   const int row_bytes = H * (x_dtype == MOE_F32 ? 4 : 2);
-  if (fused) {
-    launch_permute_rows<1>(T, K, e0, L, TT, capacity, row_bytes, out_dtype, x, ids, hist, rank, offsets, x_perm,
-                           x_scales, row_to_slot, slot_to_row, counts, err, s);
-  } else {
-    hipLaunchKernelGGL(k_scan, dim3(1), dim3(1024), 0, s, ntiles, L, capacity, hist, counts, offsets, err);
-    if (T > 0)
-      launch_permute_rows<0>(T, K, e0, L, TT, capacity, row_bytes, out_dtype, x, ids, hist, rank, offsets, x_perm,
-                             x_scales, row_to_slot, slot_to_row, counts, err, s);
-  }
+  const dim3 g((T + 3) / 4), b(256);
+  const long nflags = (long)ntiles * L;
+#define PERMUTE_ARGS                                                                                                 \
+  T, K, e0, L, TT, capacity, row_bytes, (const uint8_t*)x, ids, w.rank,                                          \
+      (const int32_t*)offsets, (uint8_t*)x_perm, x_scales, row_to_slot, slot_to_row, w.ticket, w.flags, nflags
+  if (out_dtype == MOE_MXFP8)
+    hipLaunchKernelGGL(k_permute<1>, g, b, 0, s, PERMUTE_ARGS);
+  else if (out_dtype == MOE_MXFP4)
+    hipLaunchKernelGGL(k_permute<2>, g, b, 0, s, PERMUTE_ARGS);
+  else
+    hipLaunchKernelGGL(k_permute<0>, g, b, 0, s, PERMUTE_ARGS);
+#undef PERMUTE_ARGS
   return hipGetLastError();
 }
 

@@ -24,7 +24,10 @@ class MoELayer:
         self.L = E if L is None else L
         self.e0, self.score, self.dtype, self.x_dtype = e0, score, dtype, x_dtype
         self.device = torch.device(device)
-        self.capacity = T * min(K, self.L) if capacity is None else capacity
+        sizes = M.moe_query_sizes(T, H, E, K, F, dtype, x_dtype=x_dtype,
+                                  w_dtype=M.dtype_code(w_router.dtype) if w_router is not None else M.F32,
+                                  L=self.L)
+        self.capacity = sizes["capacity"] if capacity is None else capacity
         dev = self.device
         L, cap = self.L, self.capacity
         self.bias = bias
@@ -63,7 +66,8 @@ class MoELayer:
         self.x_perm_scales = torch.empty((cap, H // 32), dtype=torch.uint8, device=dev) if mx else None
         self.row_to_slot = torch.empty(cap, **i32)
         self.slot_to_row = torch.empty((T, K), **i32)
-        self.perm_ws = torch.empty(M.moe_permute_workspace_bytes(T, K, L), dtype=torch.uint8, device=dev)
+        # zero-filled once: the permute's look-back state starts (and is left) at zero
+        self.perm_ws = torch.zeros(M.moe_permute_workspace_bytes(T, K, L), dtype=torch.uint8, device=dev)
         self.y_perm = torch.empty((cap, H), dtype=act, device=dev)
         self.mlp_ws = torch.empty(M.moe_grouped_mlp_workspace_bytes(cap, F, dtype), dtype=torch.uint8, device=dev)
         self.out = torch.empty((T, H), dtype=act, device=dev)

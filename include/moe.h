@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 1
+#define MOE_ABI_VERSION 2
 
 /* Status codes. */
 enum {
@@ -84,7 +84,9 @@ enum {
 enum {
   MOE_DEVERR_BAD_ID = 1,    /* an expert id < -1 or >= E_global reached moe_permute */
   MOE_DEVERR_OVERFLOW = 2,  /* more routed local rows than `capacity` */
-  MOE_DEVERR_NONFINITE = 4  /* a router key was NaN or +-inf */
+  MOE_DEVERR_NONFINITE = 4, /* a router key was NaN or +-inf */
+  MOE_DEVERR_WORKSPACE = 8  /* moe_permute found its workspace not zero-filled
+                               (its outputs are then unspecified) */
 };
 
 /* Limits of this implementation (checked; MOE_ERR_SHAPE otherwise). */
@@ -94,6 +96,50 @@ enum {
 
 int moe_abi_version(void);
 const char* moe_status_str(int status);
+
+/* ------------------------------------------------------------------------
+ * Sizes of every buffer of one layer shape (host only: no HIP call, so it
+ * works on a machine without a GPU).
+ *
+ * bpdata article, "How to get started" (reproduction settings): buffers are
+ * pre-sized and an overflow is checked for; "Optimization 1: Grouped GEMM":
+ * the grouped GEMM computes only valid regions with no worst-case padding.
+ * On one GPU the routed rows have an exact bound, so `capacity` never drops
+ * a route: moe_route_topk gives a token K distinct experts, at most
+ * min(K, L) of them local, hence capacity = T * min(K, L); ids supplied by
+ * the caller may repeat an expert within a token (each slot gets its own
+ * row), which needs capacity_any_ids = T * K.
+ *
+ * shape: T tokens, H hidden, E experts seen by the router, K routes per
+ * token, L local experts (0 = all E), F expert FFN width, x_dtype (token
+ * rows, MOE_BF16 / MOE_F32), w_dtype (router weights, MOE_F32 / MOE_BF16),
+ * dtype (expert path: MOE_F32, MOE_BF16, MOE_MXFP8, MOE_MXFP4).
+ * out: byte sizes for the calls below with capacity = out->capacity, and
+ * the byte offsets of the documented parts of the MLP workspaces (the
+ * activations `a` and their MX scales in moe_grouped_mlp's workspace; h,
+ * d_h and, for MOE_MXFP8, d_h's row-wise MX codes and scales in
+ * moe_grouped_mlp_backward_data's workspace).  Sizes of parts a dtype does
+ * not have are 0.  Returns MOE_ERR_NULL, MOE_ERR_SHAPE or MOE_ERR_DTYPE for
+ * bad arguments (out untouched).
+ * ------------------------------------------------------------------------ */
+typedef struct moe_shape {
+  int T, H, E, K, L, F;
+  int x_dtype, w_dtype, dtype;
+} moe_shape;
+
+typedef struct moe_sizes {
+  int64_t capacity;          /* T * min(K, L): rows for ids from moe_route_topk */
+  int64_t capacity_any_ids;  /* T * K: rows for any ids, repeats included */
+  size_t router_prepared_bytes, route_workspace_bytes, permute_workspace_bytes;
+  size_t permute_state_bytes;  /* the permute workspace's first bytes, zero between calls */
+  size_t w1p_bytes, w2p_bytes, w1p_scales_bytes, w2p_scales_bytes;
+  size_t mlp_workspace_bytes, mlp_act_offset, mlp_act_scales_offset;
+  size_t w1t_bytes, w2t_bytes, w1t_scales_bytes, w2t_scales_bytes;
+  size_t mlp_backward_workspace_bytes, bwd_h_offset, bwd_dh_offset, bwd_dh_codes_offset, bwd_dh_scales_offset;
+  size_t mlp_backward_weights_workspace_bytes;
+} moe_sizes;
+
+int moe_query_sizes(const moe_shape* shape, moe_sizes* out);
 
 /* ------------------------------------------------------------------------
  * Route: score + top-K selection (+ optional fused router projection)
@@ -200,7 +246,16 @@ int moe_route_topk_grouped(int T, int E, int K, int H, int n_group, int topk_gro
  * x_perm receives packed E2M1 codes [capacity,H/2] uint8 and x_perm_scales
  * the E8M0 scales [capacity,H/32] (scale exponent floor(log2 max|v|) - 2,
  * round to nearest even, saturate at 6).
- * Workspace: moe_permute_workspace_bytes(T, K, L) bytes.
+ * Scan: the counts of tiles of consecutive tokens are combined in one pass
+ * over the ids by a decoupled look-back (each tile publishes its own counts,
+ * then adds its predecessors' until it meets an inclusive count; Merrill and
+ * Garland 2016), so the scan needs no second kernel over the tile counts.
+ * Workspace: moe_permute_workspace_bytes(T, K, L) bytes, zero-filled before
+ * its first use; every byte a call writes to it is zero again when the
+ * call's kernels end, so one workspace serves any number of calls, on one
+ * stream at a time, of any shape whose size fits.  A workspace found not
+ * zero-filled sets MOE_DEVERR_WORKSPACE (the outputs are then unspecified;
+ * the call still ends, and leaves the workspace zero).  Limit: T * K < 2^30.
  * ------------------------------------------------------------------------ */
 size_t moe_permute_workspace_bytes(int T, int K, int L);
 
@@ -277,11 +332,11 @@ int moe_prepare_weights(int L, int H, int F, int in_dtype, int dtype,
  * F % 32 == 0 for MOE_F32.
  * Workspace: moe_grouped_mlp_workspace_bytes(capacity, F, dtype) bytes; it
  * starts with `a`: MOE_F32 [capacity][F] fp32; MOE_BF16 k-blocked
- * [F/32][capacity][32] bf16, followed at the next 256-byte boundary by 64 MiB
+ * [F/32][capacity][32] bf16, followed at the next 256-byte boundary by 72 MiB
  * of fp32 split-K partial tiles (the tiles of a last, partial round of the
  * CUs are split along the contraction and summed in a fixed order); MOE_MXFP8
  * the codes [capacity][F], then at the next 256-byte boundary the scales
- * [capacity][F/32], then at the next 256-byte boundary 64 MiB of split-K
+ * [capacity][F/32], then at the next 256-byte boundary 72 MiB of split-K
  * partial tiles; MOE_MXFP4 the same with packed codes [capacity][F/2].
  * ------------------------------------------------------------------------ */
 size_t moe_grouped_mlp_workspace_bytes(int64_t capacity, int F, int dtype);
@@ -291,6 +346,20 @@ int moe_grouped_mlp(int L, int H, int F, int64_t capacity, int dtype,
                     const void* w1p, const uint8_t* w1p_scales,
                     const void* w2p, const uint8_t* w2p_scales,
                     void* y_perm, void* workspace, size_t workspace_bytes, void* stream);
+
+/* moe_grouped_mlp for MOE_MXFP8 / MOE_MXFP4 that also stores the bf16 values
+ * of `a` the GEMM1 epilogue quantizes, row-major [capacity][F] bf16 in
+ * act_bf16 (device, 16-byte aligned; rows < N written).  A test hook: with
+ * it the MX codes and scales of `a` can be checked bit for bit against the
+ * quantizer's definition applied to the GPU's own `a` (for MOE_BF16 and
+ * MOE_F32 the workspace already holds `a`: MOE_ERR_DTYPE).  act_bf16 NULL:
+ * MOE_ERR_NULL. */
+int moe_grouped_mlp_with_act(int L, int H, int F, int64_t capacity, int dtype,
+                             const void* x_perm, const uint8_t* x_perm_scales, const int32_t* offsets,
+                             const void* w1p, const uint8_t* w1p_scales,
+                             const void* w2p, const uint8_t* w2p_scales,
+                             void* y_perm, void* workspace, size_t workspace_bytes, void* act_bf16,
+                             void* stream);
 
 /* ------------------------------------------------------------------------
  * Unpermute + probability-weighted combine
@@ -311,7 +380,8 @@ int moe_unpermute_combine(int T, int K, int H, int dtype,
  * variable-length groups, bpdata article, "Optimization 1: Grouped GEMM"; its
  * backward is the chain rule through them and SwiGLU).  For the rows of each
  * expert e: h = x_perm . W1[e] is recomputed and stored as bf16; d_a =
- * d_y_perm . W2[e]^T (fp32, not stored); d_h = [d_a * u * silu'(g),
+ * d_y_perm . W2[e]^T (fp32; MOE_BF16 keeps it in registers, MOE_MXFP8 stores
+ * it in the workspace); d_h = [d_a * u * silu'(g),
  * d_a * silu(g)] with g = h[:, :F], u = h[:, F:], silu'(g) = sigma(g)
  * (1 + g (1 - sigma(g))), stored as bf16; d_x_perm = d_h . W1[e]^T (bf16).
  * All three are ragged grouped GEMMs on the device-built tile schedule.
@@ -335,9 +405,26 @@ int moe_unpermute_combine(int T, int K, int H, int dtype,
  *   d_h k-blocked bf16 at its start, which the weight gradient reads; the
  *   split-K partials; for MOE_MXFP8 the row-wise MX operands).  dtype
  *   MOE_BF16 (H % 128 == 0, F % 128 == 0) or MOE_MXFP8 (H % 256 == 0,
- *   F % 256 == 0: x_perm and d_y are MX-quantized along H, d_h is rounded to
- *   bf16 and MX-quantized along 2F in the GEMM that forms it; fp32
- *   accumulation); capacity * max(H, 2F) * 2 < 2^31.
+ *   F % 256 == 0, the three scale pointers 4-byte aligned: x_perm and d_y are
+ *   MX-quantized along H; the d_a GEMM stores d_a as fp32 [capacity][F] in
+ *   the workspace, and one elementwise kernel forms d_h from d_a and h,
+ *   stores it as bf16 and MX-quantizes it along 2F in the same pass; fp32
+ *   accumulation); capacity * max(H, 2F) * 2 < 2^31.  The byte offsets of h,
+ *   d_h and (MOE_MXFP8) d_h's MX codes [capacity][2F] and scales
+ *   [capacity][2F/32] (gates, then ups) in the workspace are given by
+ *   moe_query_sizes.
+ *   x_perm_q / x_perm_q_scales and d_y_perm_q / d_y_perm_q_scales (MOE_MXFP8
+ *   only; NULL otherwise): the row-wise MX operands of x_perm and d_y along H
+ *   (E4M3 codes [capacity][H], E8M0 scales [capacity][H/32]) as their
+ *   producers write them: moe_permute with MOE_MXFP8 output (the forward's
+ *   operand of GEMM1) and moe_unpermute_combine_backward with its MX output.
+ *   Given, they are used as they are (the bf16 operand may then be NULL) and
+ *   the call runs no quantization pass of its own over that operand
+ *   (quantization fused with the kernels that produce the operands: the
+ *   pages' planned "quantization fused with GEMM", bpdata article, closing
+ *   paragraph of "Measured training impact"); not given, the call quantizes
+ *   the bf16 operand into its workspace first.  Codes 16-byte and scales
+ *   4-byte aligned.
  * ------------------------------------------------------------------------ */
 int moe_prepare_weights_backward(int L, int H, int F, int dtype, const void* w1, const void* w2, void* w1t,
                                  void* w2t, uint8_t* w1t_scales, uint8_t* w2t_scales, void* stream);
@@ -345,8 +432,10 @@ size_t moe_grouped_mlp_backward_workspace_bytes(int64_t capacity, int H, int F, 
 int moe_grouped_mlp_backward_data(int L, int H, int F, int64_t capacity, int dtype, const void* x_perm,
                                   const int32_t* offsets, const void* w1p, const uint8_t* w1p_scales,
                                   const void* w1t, const uint8_t* w1t_scales, const void* w2t,
-                                  const uint8_t* w2t_scales, const void* d_y_perm, void* d_x_perm, void* workspace,
-                                  size_t workspace_bytes, void* stream);
+                                  const uint8_t* w2t_scales, const void* d_y_perm, void* d_x_perm,
+                                  const uint8_t* x_perm_q, const uint8_t* x_perm_q_scales, const uint8_t* d_y_perm_q,
+                                  const uint8_t* d_y_perm_q_scales, void* workspace, size_t workspace_bytes,
+                                  void* stream);
 
 /* ------------------------------------------------------------------------
  * Weight gradient of the grouped SwiGLU MLP (bf16 or MXFP8 operands, fp32
@@ -363,8 +452,11 @@ int moe_grouped_mlp_backward_data(int L, int H, int F, int64_t capacity, int dty
  * dtype MOE_MXFP8: the four operands are quantized group-aware and column-wise
  * (as moe_mx_quantize_columns_grouped: MX blocks of 32 rows of one expert in
  * one column; each expert padded to a multiple of 256 rows here) and the
- * GEMMs run on the MX matrix-core instruction (fp32 accumulation); h, a and
- * d_h come from the bf16 data gradient as for MOE_BF16.
+ * GEMMs run on the MX matrix-core instruction (fp32 accumulation).  h and d_h
+ * are the ones the preceding moe_grouped_mlp_backward_data call left in
+ * data_workspace, whichever its dtype: after a MOE_MXFP8 data pass they are
+ * the values computed from MX operands, as a quantized training step uses
+ * them (a is formed from that h).
  * Workspace: moe_grouped_mlp_backward_weights_workspace_bytes(L, capacity, H,
  * F, dtype) bytes.  Limits as moe_grouped_mlp_backward_data, and
  * (capacity + 128 L) * max(H, 2F) * 2 < 2^31 (MOE_MXFP8 also
@@ -404,6 +496,10 @@ int moe_grouped_mlp_backward_weights(int L, int H, int F, int64_t capacity, int 
  *   fp32; rows without a slot untouched); d_probs[t,k] = <dout[t], y_perm[r]>
  *   (fp32, each lane's fixed-order sum then a fixed tree: deterministic), 0 for
  *   slots without a row.  dout [T,H], y_perm and d_y_perm [capacity,H] device.
+ *   d_y_perm_q, d_y_perm_q_scales (optional, bf16 only, H % 32 == 0; NULL
+ *   for none): each d_y_perm row written is also MX-quantized along H as it
+ *   is formed (E4M3 codes [capacity][H], E8M0 scales [capacity][H/32], OCP MX
+ *   v1.0 as moe_mx_quantize) -- the d_y operand of the MXFP8 data gradient.
  * moe_permute_backward: gradient of moe_permute's x_perm[r] = x[t]:
  *   d_x[t] = sum over the token's slots with a row (k order, fp32) of
  *   d_x_perm[r]; tokens without one get a zero row.
@@ -421,7 +517,7 @@ int moe_grouped_mlp_backward_weights(int L, int H, int F, int64_t capacity, int 
  * ------------------------------------------------------------------------ */
 int moe_unpermute_combine_backward(int T, int K, int H, int dtype, const void* dout, const void* y_perm,
                                    const int32_t* slot_to_row, const float* probs, void* d_y_perm,
-                                   float* d_probs, void* stream);
+                                   float* d_probs, uint8_t* d_y_perm_q, uint8_t* d_y_perm_q_scales, void* stream);
 int moe_permute_backward(int T, int K, int H, int dtype, const void* d_x_perm, const int32_t* slot_to_row,
                          void* d_x, void* stream);
 int moe_route_backward(int T, int E, int K, int score, float scale, const int16_t* ids, const float* probs,
@@ -437,6 +533,33 @@ int moe_route_backward(int T, int E, int K, int score, float scale, const int16_
  * ------------------------------------------------------------------------ */
 int moe_mx_quantize(int64_t rows, int cols, const void* in, const int32_t* row_limit,
                     uint8_t* codes, uint8_t* scales, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Calibration kernels: measurement support, not an operation of the layer.
+ * The pages state their results as kernel times and rates; these kernels
+ * measure the rates this GPU actually sustains, so that the layer's kernels
+ * can be given as fractions of them next to the datasheet peaks.
+ *
+ * moe_calib_copy: dst = src, `bytes` (a multiple of 16; both 16-byte
+ *   aligned, device) with streaming 16-byte loads and stores.
+ * moe_calib_read: reads `bytes` of src (multiple of 16, 16-byte aligned) and
+ *   writes one word per workgroup (an xor fold) to out, which holds
+ *   moe_calib_read_out_words(bytes) words.
+ * moe_calib_write: fills `bytes` of dst (multiple of 16, 16-byte aligned)
+ *   with the 32-bit `value`.
+ * moe_calib_mfma: `blocks` workgroups of 8 wavefronts, each wavefront `iters`
+ *   rounds of 4 independent matrix-core instructions on register operands:
+ *   MOE_BF16 v_mfma_f32_32x32x16_bf16 (32768 flops each), MOE_MXFP8
+ *   v_mfma_scale_f32_32x32x64_f8f6f4 on E4M3 codes with unit E8M0 scales
+ *   (131072 flops each); flops = blocks * 8 * 4 * iters * that.  out [blocks *
+ *   512] fp32 (device) receives the accumulators' sums.
+ * Zero bytes: a no-op.  Errors as for the other calls.
+ * ------------------------------------------------------------------------ */
+int moe_calib_copy(const void* src, void* dst, size_t bytes, void* stream);
+size_t moe_calib_read_out_words(size_t bytes);
+int moe_calib_read(const void* src, size_t bytes, uint32_t* out, void* stream);
+int moe_calib_write(void* dst, size_t bytes, uint32_t value, void* stream);
+int moe_calib_mfma(int dtype, int blocks, int iters, float* out, void* stream);
 
 #ifdef __cplusplus
 }

@@ -701,17 +701,45 @@ def swiglu_backward(h, d_a, F):
     return np.concatenate([d_a * u * sg * (1.0 + g * (1.0 - sg)), d_a * g * sg], axis=1)
 
 
+def mlp_backward_intermediates(X, dY, W1e, W2e, dtype):
+    """One expert's data pass on its rows X with output gradient dY: returns
+    (h, d_a, d_h) as the data gradient computes them, with h = X . W1e
+    recomputed, d_a = dY . W2e^T and d_h = swiglu'(h, d_a).
+
+    "bf16": h and d_h are stored as bf16 (d_a is not rounded).  "f64": nothing
+    is rounded.  "mxfp8": every contraction takes MX (E4M3) operands blocked
+    along its own contraction dimension, as the forward's (bpdata article,
+    "Optimization 1: Grouped GEMM", MXFP8 block scaling): X and W1e's columns
+    along H for h; dY and W2e's rows along H for d_a; h and d_h are bf16."""
+    X = np.asarray(X, np.float64)
+    dY = np.asarray(dY, np.float64)
+    W1e = np.asarray(W1e, np.float64)
+    W2e = np.asarray(W2e, np.float64)
+    F = W2e.shape[0]
+    if dtype == "mxfp8":
+        h = bf16_round(_mx_rows_roundtrip(X) @ _mx_rows_roundtrip(W1e.T).T)
+        d_a = _mx_rows_roundtrip(dY) @ _mx_rows_roundtrip(W2e).T
+        return h, d_a, bf16_round(swiglu_backward(h, d_a, F))
+    rnd = (lambda v: v) if dtype == "f64" else bf16_round
+    h = rnd(X @ W1e)
+    d_a = dY @ W2e.T
+    return h, d_a, rnd(swiglu_backward(h, d_a, F))
+
+
+def _mx_rows_roundtrip(V):
+    """V after row-wise MX (E4M3) quantization along its last axis and exact
+    dequantization."""
+    return mx_dequantize_rows(*mx_quantize_rows(V))
+
+
 def grouped_mlp_backward_data(x_perm, offsets, W1, W2, d_y, dtype):
     """Data gradient of the grouped SwiGLU MLP: for each expert's rows,
-    d_x = d_h . W1[e]^T with d_h = swiglu'(h, d_a), d_a = d_y . W2[e]^T and
-    h = X . W1[e] recomputed.  Rounding points of the bf16 path: h and d_h
-    are stored as bf16 (d_a is not stored), d_x is bf16; "f64" rounds
-    nothing.  "mxfp8": every contraction takes MX (E4M3) operands blocked
-    along its contraction dimension, as the forward's (bpdata article,
-    "Optimization 1: Grouped GEMM", MXFP8 block scaling): X and W1[e]'s
-    columns along H for h; d_y and W2[e]'s rows along H for d_a; d_h (after
-    its bf16 rounding) and W1[e]'s rows along 2F for d_x.  Returns d_x over
-    rows [0, N)."""
+    d_x = d_h . W1[e]^T with d_h, h as mlp_backward_intermediates computes
+    them.  Rounding points of the bf16 path: h and d_h are stored as bf16,
+    d_x is bf16; "f64" rounds nothing; "mxfp8": d_h (after its bf16
+    rounding) and W1[e]'s rows are MX operands along 2F for d_x, as the
+    other two contractions' operands are along H.  Returns d_x over rows
+    [0, N)."""
     x_perm = np.asarray(x_perm, np.float64)
     d_y = np.asarray(d_y, np.float64)
     N = int(offsets[-1])
@@ -723,50 +751,68 @@ def grouped_mlp_backward_data(x_perm, offsets, W1, W2, d_y, dtype):
         if hi == lo:
             continue
         W1e = np.asarray(W1[e], np.float64)
-        W2e = np.asarray(W2[e], np.float64)
-        F = W2e.shape[0]
+        _, _, d_h = mlp_backward_intermediates(x_perm[lo:hi], d_y[lo:hi], W1e, W2[e], dtype)
         if dtype == "mxfp8":
-            q = lambda V: mx_dequantize_rows(*mx_quantize_rows(V))  # MX round trip along the last axis
-            h = bf16_round(q(x_perm[lo:hi]) @ q(W1e.T).T)
-            d_a = q(d_y[lo:hi]) @ q(W2e).T
-            d_h = bf16_round(swiglu_backward(h, d_a, F))
-            out[lo:hi] = bf16_round(q(d_h) @ q(W1e).T)
-            continue
-        h = rnd(x_perm[lo:hi] @ W1e)
-        d_a = d_y[lo:hi] @ W2e.T
-        d_h = rnd(swiglu_backward(h, d_a, F))
-        out[lo:hi] = rnd(d_h @ W1e.T)
+            out[lo:hi] = bf16_round(_mx_rows_roundtrip(d_h) @ _mx_rows_roundtrip(W1e).T)
+        else:
+            out[lo:hi] = rnd(d_h @ W1e.T)
     return out
 
 
-def grouped_mlp_backward_weights(x_perm, offsets, W1, W2, d_y, dtype):
+def weight_gradient_operands(X, dY, W1e, W2e, data_dtype):
+    """The four operands of one expert's weight gradient as the weight GEMMs
+    take them (before any quantization of their own): the rows X and dY, and
+    a = silu(g) u and d_h from the data pass of type data_dtype ("bf16",
+    "mxfp8" or "f64"; see mlp_backward_intermediates), a rounded to bf16
+    (not rounded for "f64").  Returns (X, a, d_h, dY)."""
+    X = np.asarray(X, np.float64)
+    dY = np.asarray(dY, np.float64)
+    F = np.asarray(W2e).shape[0]
+    h, _, d_h = mlp_backward_intermediates(X, dY, W1e, W2e, data_dtype)
+    a = swiglu(h, F)
+    return X, (a if data_dtype == "f64" else bf16_round(a)), d_h, dY
+
+
+def weight_gradient_quantize(V):
+    """The MXFP8 operand form of a weight-gradient operand V [m][C] (the rows
+    of one expert group): each column is cut into blocks of 32 consecutive
+    rows of the group and each block is one MX block (group-aware column-wise
+    quantization, mx_quantize_columns_grouped); returns the dequantized values
+    [m][C] (exact)."""
+    return _mx_columns_roundtrip(V)
+
+
+def weight_gradient_contract(X, a, d_h, dY, dtype):
+    """One expert's weight gradients from its four operands: dW1 = X^T d_h
+    [H][2F] and dW2 = a^T dY [F][H], contracted over the expert's rows in
+    float64.  "mxfp8": each of the four operands first goes through
+    weight_gradient_quantize.  The results are fp32 ("f64": not rounded)."""
+    X, a, d_h, dY = (np.asarray(v, np.float64) for v in (X, a, d_h, dY))
+    if dtype == "mxfp8":
+        X, a, d_h, dY = (weight_gradient_quantize(v) for v in (X, a, d_h, dY))
+    out = (lambda v: v) if dtype == "f64" else (lambda v: v.astype(np.float32).astype(np.float64))
+    return out(X.T @ d_h), out(a.T @ dY)
+
+
+def grouped_mlp_backward_weights(x_perm, offsets, W1, W2, d_y, dtype, data_dtype=None):
     """Weight gradient of the grouped SwiGLU MLP: for each expert's rows X,
     dW1[e] = X^T d_h and dW2[e] = a^T d_y (contractions over the expert's own
     rows), with h = X W1[e] recomputed, a = silu(g) u, d_a = d_y W2[e]^T and
-    d_h = swiglu'(h, d_a).  Rounding points of the bf16 path: h, a and d_h
-    are bf16; the gradients are fp32.  "f64" rounds nothing.  "mxfp8": the
-    bf16 path's operands X, a, d_h, d_y are MX-quantized column-wise in
-    32-row blocks of the expert (mx_quantize_columns_grouped) before the
-    contractions.  Empty experts get zero gradients.  Returns (dW1 [L][H][2F],
-    dW2 [L][F][H])."""
+    d_h = swiglu'(h, d_a) from the data pass of type data_dtype (default: the
+    bf16 one; "f64" for dtype "f64"), the operands taken by
+    weight_gradient_contract of type dtype ("bf16", "mxfp8" or "f64").  Empty
+    experts get zero gradients.  Returns (dW1 [L][H][2F], dW2 [L][F][H])."""
     x_perm = np.asarray(x_perm, np.float64)
     d_y = np.asarray(d_y, np.float64)
-    rnd = (lambda v: v) if dtype == "f64" else bf16_round
-    out = (lambda v: v) if dtype == "f64" else (lambda v: v.astype(np.float32).astype(np.float64))
+    if data_dtype is None:
+        data_dtype = "f64" if dtype == "f64" else "bf16"
     dW1, dW2 = [], []
     for e in range(len(offsets) - 1):
         lo, hi = int(offsets[e]), int(offsets[e + 1])
-        W1e = np.asarray(W1[e], np.float64)
-        W2e = np.asarray(W2[e], np.float64)
-        F = W2e.shape[0]
-        X, dY = x_perm[lo:hi], d_y[lo:hi]
-        h = rnd(X @ W1e)
-        a = rnd(swiglu(h, F))
-        d_h = rnd(swiglu_backward(h, dY @ W2e.T, F))
-        if dtype == "mxfp8":
-            X, a, d_h, dY = (_mx_columns_roundtrip(V) for V in (X, a, d_h, dY))
-        dW1.append(out(X.T @ d_h))
-        dW2.append(out(a.T @ dY))
+        ops = weight_gradient_operands(x_perm[lo:hi], d_y[lo:hi], W1[e], W2[e], data_dtype)
+        g1, g2 = weight_gradient_contract(*ops, dtype)
+        dW1.append(g1)
+        dW2.append(g2)
     return np.stack(dW1), np.stack(dW2)
 
 

@@ -23,7 +23,7 @@ def test_library_exports_every_declared_symbol():
     for n in names:
         assert hasattr(_lib.lib, n), n
     assert set(names) == set(_lib.symbols())
-    assert _lib.lib.moe_abi_version() == 1
+    assert _lib.lib.moe_abi_version() == 2
 
 
 def test_status_strings():
@@ -94,11 +94,17 @@ def test_backward_validation():
     from dropless_mixture_experts_radix_amd import _lib
     L = _lib.lib
     # combine backward: (T, K, H, dtype, dout, y, s2r, probs, d_y, d_probs, stream)
-    assert L.moe_unpermute_combine_backward(0, 2, 64, 1, None, None, None, None, None, None, None) == 0
-    assert L.moe_unpermute_combine_backward(4, 2, 60, 1, P, P, P, P, P, P, None) == 2   # H % 8
-    assert L.moe_unpermute_combine_backward(4, 2, 64, 3, P, P, P, P, P, P, None) == 4   # dtype
-    assert L.moe_unpermute_combine_backward(4, 2, 64, 1, P, P, P, None, P, P, None) == 1
-    assert L.moe_unpermute_combine_backward(4, 2, 64, 1, P + 8, P, P, P, P, P, None) == 3
+    cb = L.moe_unpermute_combine_backward
+    assert cb(0, 2, 64, 1, None, None, None, None, None, None, None, None, None) == 0
+    assert cb(4, 2, 60, 1, P, P, P, P, P, P, None, None, None) == 2   # H % 8
+    assert cb(4, 2, 64, 3, P, P, P, P, P, P, None, None, None) == 4   # dtype
+    assert cb(4, 2, 64, 1, P, P, P, None, P, P, None, None, None) == 1
+    assert cb(4, 2, 64, 1, P + 8, P, P, P, P, P, None, None, None) == 3
+    # the MX form of d_y: bf16 rows only, H % 32, both pointers, codes 16-byte aligned
+    assert cb(4, 2, 64, 0, P, P, P, P, P, P, P, P, None) == 4
+    assert cb(4, 2, 48, 1, P, P, P, P, P, P, P, P, None) == 2
+    assert cb(4, 2, 64, 1, P, P, P, P, P, P, P, None, None) == 1
+    assert cb(4, 2, 64, 1, P, P, P, P, P, P, P + 4, P, None) == 3
     # permute backward: (T, K, H, dtype, d_x_perm, s2r, d_x, stream)
     assert L.moe_permute_backward(0, 2, 64, 1, None, None, None, None) == 0
     assert L.moe_permute_backward(4, 65, 64, 1, P, P, P, None) == 2
@@ -116,12 +122,20 @@ def test_backward_validation():
     assert L.moe_prepare_weights_backward(2, 256, 256, 2, P, P, P, P, None, P, None) == 1  # MXFP8 needs scales
     assert L.moe_prepare_weights_backward(2, 256, 256, 3, P, P, P, P, P, P, None) == 4   # MXFP4: no panels
     # data gradient: (L, H, F, cap, dtype, x, offs, w1p, w1p_s, w1t, w1t_s, w2t, w2t_s, d_y, d_x, ws, wsb, stream)
-    dg = lambda dt, H=256, F=256, s=P, wsb=1 << 30: L.moe_grouped_mlp_backward_data(
-        2, H, F, 64, dt, P, P, P, s, P, s, P, s, P, P, P, wsb, None)
+    dg = lambda dt, H=256, F=256, s=P, wsb=1 << 30, xq=None, xqs=None, dq=None, dqs=None, x=P, dy=P: \
+        L.moe_grouped_mlp_backward_data(2, H, F, 64, dt, x, P, P, s, P, s, P, s, dy, P, xq, xqs, dq, dqs, P, wsb, None)
     assert dg(3) == 4                       # MXFP4
     assert dg(2, F=128) == 2                # MXFP8: F % 256
     assert dg(2, s=None) == 1               # MXFP8 needs the scales
     assert dg(2, wsb=L.moe_grouped_mlp_backward_workspace_bytes(64, 256, 256, 2) - 1) == 5
+    # row-wise MX operands from their producers: MXFP8 only, codes and scales together, then the bf16 operand
+    # may be absent; scales 4-byte aligned
+    assert dg(1, H=256, F=256, s=None, xq=P, xqs=P) == 4
+    assert dg(2, xq=P) == 1
+    assert dg(2, dqs=P) == 1
+    assert dg(2, x=None) == 1
+    assert dg(2, xq=P, xqs=P + 2) == 3
+    assert dg(2, dq=P + 8, dqs=P) == 3
     assert (L.moe_grouped_mlp_backward_workspace_bytes(64, 256, 256, 2) >
             L.moe_grouped_mlp_backward_workspace_bytes(64, 256, 256, 1))
     assert L.moe_prepared_weight_bytes(2, 256, 512, 2, 7) == 2 * 256 * 2 * 16   # W1t scales
@@ -215,3 +229,66 @@ def test_size_queries():
             lib.moe_grouped_mlp_workspace_bytes(8192, 14336, 2))
     assert lib.moe_grouped_mlp_workspace_bytes(8192, 14336, 1) >= 8192 * 14336 * 2
     assert lib.moe_permute_workspace_bytes(8192, 36, 32) >= 8192 * 36 * 4
+
+
+def test_query_sizes():
+    """moe_query_sizes agrees with the per-buffer size functions, gives the exact
+    routed-row bounds T*min(K, L) and T*K, and rejects bad shapes (host only)."""
+    from dropless_mixture_experts_radix_amd import _lib
+    lib = _lib.lib
+    q = lambda **kw: _lib.moe_query_sizes(**kw)
+    z = q(T=4096, H=4096, E=8, K=2, F=14336, dtype=1, x_dtype=1, w_dtype=0)
+    assert z["capacity"] == 8192 and z["capacity_any_ids"] == 8192
+    assert z["router_prepared_bytes"] == lib.moe_router_prepared_bytes(4096, 8, 0, 1)
+    assert z["route_workspace_bytes"] == lib.moe_route_workspace_bytes(4096, 8, 4096, 1)
+    assert z["permute_workspace_bytes"] == lib.moe_permute_workspace_bytes(4096, 2, 8)
+    assert z["mlp_workspace_bytes"] == lib.moe_grouped_mlp_workspace_bytes(8192, 14336, 1)
+    assert z["w1p_bytes"] == lib.moe_prepared_weight_bytes(8, 4096, 14336, 1, 1)
+    assert z["w1t_bytes"] == lib.moe_prepared_weight_bytes(8, 4096, 14336, 1, 5)
+    assert z["mlp_backward_workspace_bytes"] == lib.moe_grouped_mlp_backward_workspace_bytes(8192, 4096, 14336, 1)
+    assert z["bwd_dh_offset"] == (8192 * 2 * 14336 * 2 + 255) // 256 * 256 and z["bwd_dh_codes_offset"] == 0
+    # sparse share: 32 local experts of 2304, K = 36 > L
+    z = q(T=8192, H=512, E=2304, K=36, L=32, F=512, dtype=1)
+    assert z["capacity"] == 8192 * 32 and z["capacity_any_ids"] == 8192 * 36
+    # MXFP8: the MX activations' scales follow the codes; d_h's MX operands sit inside the backward workspace
+    z = q(T=4096, H=4096, E=8, K=2, F=14336, dtype=2)
+    assert z["mlp_act_scales_offset"] == 8192 * 14336
+    assert 0 < z["bwd_dh_codes_offset"] < z["bwd_dh_scales_offset"]
+    assert z["bwd_dh_scales_offset"] + 8192 * 2 * 14336 // 32 <= z["mlp_backward_workspace_bytes"]
+    assert z["w1p_scales_bytes"] == lib.moe_prepared_weight_bytes(8, 4096, 14336, 2, 3)
+    # MXFP4 has no backward panels
+    z = q(T=64, H=512, E=8, K=2, F=512, dtype=3)
+    assert z["w1t_bytes"] == 0 and z["mlp_backward_workspace_bytes"] == 0
+    for bad in (dict(K=9), dict(K=0), dict(E=5000), dict(L=9), dict(T=-1)):
+        kw = dict(T=16, H=64, E=8, K=2, F=128, dtype=1)
+        kw.update(bad)
+        with pytest.raises(_lib.MoEError):
+            q(**kw)
+    with pytest.raises(_lib.MoEError):
+        q(T=16, H=64, E=8, K=2, F=128, dtype=7)
+    assert lib.moe_query_sizes(None, None) == 1
+
+
+def test_mlp_with_act_validation():
+    from dropless_mixture_experts_radix_amd import _lib
+    f = _lib.lib.moe_grouped_mlp_with_act
+
+    def call(dt=2, H=256, F=256, xs=P, w1s=P, w2s=P, act=P, wsb=1 << 28):
+        return f(8, H, F, 64, dt, P, xs, P, P, w1s, P, w2s, P, P, wsb, act, None)
+
+    assert call(act=None) == 1           # the hook's output is required
+    assert call(dt=1, H=128, F=128) == 4  # bf16: `a` is in the workspace already
+    assert call(act=P + 8) == 3
+    assert call(w2s=P + 1) == 3
+
+
+def test_backward_scale_alignment():
+    """The MXFP8 data gradient reads its weight scales 4 bytes at a time, as the
+    forward does: misaligned scale pointers are rejected."""
+    from dropless_mixture_experts_radix_amd import _lib
+    L = _lib.lib
+    dg = lambda s1=P, s2=P, s3=P: L.moe_grouped_mlp_backward_data(2, 256, 256, 64, 2, P, P, P, s1, P, s2, P, s3, P,
+                                                                   P, None, None, None, None, P, 1 << 30, None)
+    assert dg(s1=P + 2) == 3
+    assert dg(s2=P + 1) == 3
+    assert dg(s3=P + 3) == 3

@@ -62,6 +62,39 @@ def test_combine_backward(T, E, K, H, dt, mask_every):
     assert (np_of(dp)[s2r < 0] == 0).all()
 
 
+@pytest.mark.parametrize("T,E,K,H,mask_every", [(4096, 8, 2, 4096, 0), (300, 16, 6, 96, 7), (1, 4, 4, 32, 0)])
+def test_combine_backward_mx_output(T, E, K, H, mask_every):
+    """The combine backward's MX output (the MXFP8 data gradient's d_y operand,
+    quantized as the rows are formed): E4M3 codes and E8M0 scales bit-exact
+    against the quantizer's definition applied to the bf16 d_y the same call
+    writes; that bf16 d_y is the same as without the MX output; rows past N
+    untouched."""
+    rng, _, ids, probs, perm = _routing(T, E, K, 3 * T + H, mask_every)
+    s2r = perm["slot_to_row"]
+    N = int(perm["offsets"][-1])
+    cap = N + 16
+    # rows of very different magnitudes, so the block scales vary
+    y = rng.standard_normal((cap, H))
+    dout = rng.standard_normal((T, H)) * np.exp(rng.uniform(-20, 20, size=(T, 1)))
+    yd, gd = _dev_rows(y, "bf16"), _dev_rows(dout, "bf16")
+    s2r_d, p_d = torch.from_numpy(s2r).to(DEV), torch.from_numpy(probs).to(DEV)
+    dy = torch.full((cap, H), 3.0, dtype=torch.bfloat16, device=DEV)
+    dy0 = torch.full((cap, H), 3.0, dtype=torch.bfloat16, device=DEV)
+    dq = torch.full((cap, H), 0x5A, dtype=torch.uint8, device=DEV)
+    dqs = torch.full((cap, H // 32), 0xC3, dtype=torch.uint8, device=DEV)
+    dp = torch.empty((T, K), dtype=torch.float32, device=DEV)
+    say("combine backward with MX output", T, E, K, H)
+    D.moe_unpermute_combine_backward(gd, yd, s2r_d, p_d, dy, dp, d_y_perm_q=dq, d_y_perm_q_scales=dqs)
+    D.moe_unpermute_combine_backward(gd, yd, s2r_d, p_d, dy0, dp)
+    torch.cuda.synchronize()
+    got = to_f64(dy)
+    np.testing.assert_array_equal(got, to_f64(dy0))
+    codes, scales = O.mx_quantize_rows(got[:N])
+    np.testing.assert_array_equal(np_of(dq)[:N], codes)
+    np.testing.assert_array_equal(np_of(dqs)[:N], scales)
+    assert (np_of(dq)[N:] == 0x5A).all() and (np_of(dqs)[N:] == 0xC3).all()
+
+
 @pytest.mark.parametrize("T,E,K,H,dt,mask_every", [(4096, 8, 2, 4096, "bf16", 0), (300, 16, 6, 64, "bf16", 7),
                                                    (97, 32, 4, 200, "f32", 5)])
 def test_permute_backward(T, E, K, H, dt, mask_every):

@@ -25,7 +25,12 @@ def _rand_ids(rng, T, K, E, p_inv=0.1, distinct=False):
     return ids.astype(np.int16)
 
 
-def _permute_gpu(x, ids, E, e0, L, capacity, out_dtype=None):
+def _state_bytes(T, K, L):
+    """Bytes of the permute workspace's look-back state (zero between calls)."""
+    return D.moe_query_sizes(T=T, H=64, E=max(L, K), K=K, F=128, dtype=D.BF16, L=L)["permute_state_bytes"]
+
+
+def _permute_gpu(x, ids, E, e0, L, capacity, out_dtype=None, ws=None, check_ws=True):
     T, H = x.shape
     K = ids.shape[1]
     counts = torch.full((L,), SENT, dtype=torch.int32, device=DEV)
@@ -37,17 +42,30 @@ def _permute_gpu(x, ids, E, e0, L, capacity, out_dtype=None):
     xs = torch.full((max(capacity, 1), H // 32), 0xC3, dtype=torch.uint8, device=DEV)[:capacity] if mx else None
     r2s = torch.full((capacity,), SENT, dtype=torch.int32, device=DEV)
     s2r = torch.full((T, K), SENT, dtype=torch.int32, device=DEV)
-    ws = torch.full((D.moe_permute_workspace_bytes(T, K, L),), 0xEE, dtype=torch.uint8, device=DEV)  # poisoned
+    state = _state_bytes(T, K, L) if T > 0 else 0
+    if ws is None:
+        # zero-filled look-back state; the slot rows after it poisoned (written before they are read)
+        ws = torch.full((D.moe_permute_workspace_bytes(T, K, L),), 0xEE, dtype=torch.uint8, device=DEV)
+        ws[:state] = 0
     err = torch.zeros(1, dtype=torch.int32, device=DEV)
     D.moe_permute(x, torch.from_numpy(ids).to(DEV), E, e0, L, counts, offsets, x_perm, r2s, s2r, ws,
                   x_perm_scales=xs, err=err, out_dtype=out_dtype)
     torch.cuda.synchronize()
+    # the call leaves the look-back state (tile counter, flags) and the slot
+    # rows that follow it zero again
+    if T > 0:
+        rows = ws[state: state + T * K * 4]
+        assert int((rows != 0).sum().item()) == 0
+        if check_ws:
+            assert int((ws[:state] != 0).sum().item()) == 0
     return dict(counts=np_of(counts), offsets=np_of(offsets), x_perm=x_perm, xs=xs, r2s=np_of(r2s),
-                s2r=np_of(s2r), err=int(err.item()))
+                s2r=np_of(s2r), err=int(err.item()), ws=ws)
 
 
 CASES = [(1000, 2, 8, 0, 8, 64), (257, 36, 2304, 0, 32, 512), (3000, 8, 256, 0, 256, 256), (100, 4, 16, 4, 8, 136),
-         (1, 1, 1, 0, 1, 8), (5000, 1, 3, 1, 2, 64), (700, 64, 64, 0, 64, 32)]
+         (1, 1, 1, 0, 1, 8), (5000, 1, 3, 1, 2, 64), (700, 64, 64, 0, 64, 32),
+         # long look-back chains: 586 tiles of 14 tokens (the sparse share's shape), 2048 local experts
+         (8192, 36, 2304, 0, 32, 512), (4096, 8, 4096, 1024, 2048, 64)]
 
 
 @pytest.mark.parametrize("T,K,E,e0,L,H", CASES)
@@ -166,6 +184,46 @@ def test_permute_overflow_and_bad_ids():
     ref = O.count_and_permute(fixed, 0, E, None)
     np.testing.assert_array_equal(got["offsets"], ref["offsets"])
     np.testing.assert_array_equal(got["s2r"], ref["slot_to_row"])
+
+
+def test_permute_workspace_reused_across_shapes():
+    """One zero-filled workspace serves calls of different shapes in a row:
+    each call leaves the look-back state zero for the next."""
+    rng = np.random.default_rng(13)
+    E, L, H = 64, 64, 64
+    ws = torch.zeros(D.moe_permute_workspace_bytes(6000, 8, L), dtype=torch.uint8, device=DEV)
+    for T, K in ((6000, 8), (257, 3), (6000, 8), (1, 1), (4000, 6)):
+        ids = _rand_ids(rng, T, K, E)
+        x64 = O.bf16_round(rng.standard_normal((T, H)))
+        ref = O.count_and_permute(ids, 0, L, x64, E_global=E)
+        N = int(ref["offsets"][-1])
+        say("reuse", T, K, "N", N)
+        got = _permute_gpu(bf16_from_f64(x64), ids, E, 0, L, T * K, ws=ws)
+        assert got["err"] == 0
+        np.testing.assert_array_equal(got["offsets"], ref["offsets"])
+        np.testing.assert_array_equal(got["s2r"], ref["slot_to_row"])
+        np.testing.assert_array_equal(to_f64(got["x_perm"])[:N], ref["x_perm"])
+
+
+def test_permute_workspace_not_zero_filled_is_reported():
+    """A workspace whose look-back state was not zero-filled (here: every
+    byte 0xEE, so the tile counter is far past the tile count) is reported with
+    MOE_DEVERR_WORKSPACE by the host-visible error word; every kernel ends
+    normally (no tile waits: all of them see the bad counter at once), and the
+    call returns the state to zero, so the next call is exact again."""
+    rng = np.random.default_rng(14)
+    T, K, E, H = 900, 4, 32, 64
+    ids = _rand_ids(rng, T, K, E)
+    x64 = O.bf16_round(rng.standard_normal((T, H)))
+    ws = torch.full((D.moe_permute_workspace_bytes(T, K, E),), 0xEE, dtype=torch.uint8, device=DEV)
+    bad = _permute_gpu(bf16_from_f64(x64), ids, E, 0, E, T * K, ws=ws, check_ws=False)
+    assert bad["err"] & D.DEVERR_WORKSPACE
+    assert int(ws[:4].view(torch.int32).item()) == 0   # the tile counter is zero again
+    ref = O.count_and_permute(ids, 0, E, x64, E_global=E)
+    good = _permute_gpu(bf16_from_f64(x64), ids, E, 0, E, T * K, ws=ws, check_ws=False)
+    assert good["err"] == 0
+    np.testing.assert_array_equal(good["offsets"], ref["offsets"])
+    np.testing.assert_array_equal(good["s2r"], ref["slot_to_row"])
 
 
 def test_permute_empty_and_all_invalid():

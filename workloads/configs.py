@@ -45,7 +45,7 @@ class MoEConfig:
 # (bisection to 1e-3) for which the seeded draw leaves at least 26 of 256
 # experts (~10%) with no routed token under top-8 selection.  It is produced
 # by tests/golden/calibrate_zipf_gain.py, which runs only the CPU oracle, and
-# re-checked by tests/test_workloads.py.
+# re-checked by tests/test_oracle_route.py.
 ZIPF_GAIN_CFG3 = 1.341
 
 # Offset added to the logits of the 8 expert groups a token draws in the
