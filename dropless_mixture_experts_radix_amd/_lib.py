@@ -54,6 +54,8 @@ _SIGS = {
                                     _P, _P, _P, _P, _SZ, _P]),
     "moe_permute_workspace_bytes": (_SZ, [_I, _I, _I]),
     "moe_permute": (_I, [_I, _I, _I, _I, _I, _I, _I64, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "moe_permute_noalloc_max_workspace_bytes": (_SZ, []),
+    "moe_permute_noalloc": (_I, [_I, _I, _I, _I, _I, _I, _I64, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
     "moe_prepared_weight_bytes": (_SZ, [_I, _I, _I, _I, _I]),
     "moe_prepare_weights": (_I, [_I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P]),
     "moe_grouped_mlp_workspace_bytes": (_SZ, [_I64, _I, _I]),
@@ -184,6 +186,19 @@ def moe_permute(x, ids, E_global, e0, L, counts, offsets, x_perm, row_to_slot, s
     _check(lib.moe_permute(T, H, K, E_global, e0, L, capacity, x_dtype, out_dtype, _p(x), _p(ids), _p(counts),
                            _p(offsets), _p(x_perm), _p(x_perm_scales), _p(row_to_slot), _p(slot_to_row), _p(err),
                            _p(workspace), _nbytes(workspace), _stream()), "moe_permute")
+
+
+def moe_permute_noalloc(x, ids, E_global, e0, L, counts, offsets, x_perm, row_to_slot, slot_to_row,
+                        x_perm_scales=None, err=None, out_dtype=None):
+    """moe_permute with the library's fixed device workspace (allocates nothing)."""
+    T, H = x.shape
+    K = ids.shape[1]
+    capacity = row_to_slot.shape[0]
+    x_dtype = dtype_code(x.dtype)
+    out_dtype = x_dtype if out_dtype is None else out_dtype
+    _check(lib.moe_permute_noalloc(T, H, K, E_global, e0, L, capacity, x_dtype, out_dtype, _p(x), _p(ids),
+                                   _p(counts), _p(offsets), _p(x_perm), _p(x_perm_scales), _p(row_to_slot),
+                                   _p(slot_to_row), _p(err), _stream()), "moe_permute_noalloc")
 
 
 # ----------------------------------------------------------------- weights

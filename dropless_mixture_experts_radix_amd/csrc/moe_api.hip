@@ -145,7 +145,7 @@ size_t moe_permute_workspace_bytes(int T, int K, int L) {
   return permute_workspace_bytes(T, K, L);
 }
 
-// argument checks of moe_permute
+// argument checks shared by moe_permute and moe_permute_noalloc
 static int permute_check(int T, int H, int K, int E_global, int e0, int L, int64_t capacity, int x_dtype,
                          int out_dtype, const void* x, const int16_t* ids, int32_t* counts, int32_t* offsets,
                          void* x_perm, uint8_t* x_perm_scales, int32_t* row_to_slot, int32_t* slot_to_row) {
@@ -178,6 +178,21 @@ int moe_permute(int T, int H, int K, int E_global, int e0, int L, int64_t capaci
   return launch_status(launch_permute(T, H, K, E_global, e0, L, capacity, x_dtype, out_dtype, x, ids, counts,
                                       offsets, x_perm, x_perm_scales, row_to_slot, slot_to_row, err, workspace,
                                       (hipStream_t)stream));
+}
+
+size_t moe_permute_noalloc_max_workspace_bytes(void) { return permute_noalloc_max_bytes(); }
+
+int moe_permute_noalloc(int T, int H, int K, int E_global, int e0, int L, int64_t capacity, int x_dtype,
+                        int out_dtype, const void* x, const int16_t* ids, int32_t* counts, int32_t* offsets,
+                        void* x_perm, uint8_t* x_perm_scales, int32_t* row_to_slot, int32_t* slot_to_row,
+                        int32_t* err, void* stream) {
+  const int st = permute_check(T, H, K, E_global, e0, L, capacity, x_dtype, out_dtype, x, ids, counts, offsets,
+                               x_perm, x_perm_scales, row_to_slot, slot_to_row);
+  if (st != MOE_OK) return st;
+  if (moe_permute_workspace_bytes(T, K, L) > permute_noalloc_max_bytes()) return MOE_ERR_WORKSPACE;
+  return launch_status(launch_permute_noalloc(T, H, K, E_global, e0, L, capacity, x_dtype, out_dtype, x, ids,
+                                              counts, offsets, x_perm, x_perm_scales, row_to_slot, slot_to_row, err,
+                                              (hipStream_t)stream));
 }
 
 // ---------------------------------------------------------------------------

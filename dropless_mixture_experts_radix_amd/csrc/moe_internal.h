@@ -197,6 +197,11 @@ hipError_t launch_route_select(int T, int E, int K, int S, int score, const floa
 int permute_tile_tokens(int T, int K);
 size_t permute_workspace_bytes(int T, int K, int L);
 size_t permute_state_bytes(int T, int K, int L);  // the zero-between-calls prefix
+size_t permute_noalloc_max_bytes();
+hipError_t launch_permute_noalloc(int T, int H, int K, int E_global, int e0, int L, int64_t capacity, int x_dtype,
+                                  int out_dtype, const void* x, const int16_t* ids, int32_t* counts,
+                                  int32_t* offsets, void* x_perm, uint8_t* x_scales, int32_t* row_to_slot,
+                                  int32_t* slot_to_row, int32_t* err, hipStream_t s);
 hipError_t launch_permute(int T, int H, int K, int E_global, int e0, int L, int64_t capacity,
                           int x_dtype, int out_dtype, const void* x, const int16_t* ids,
                           int32_t* counts, int32_t* offsets, void* x_perm, uint8_t* x_scales,

@@ -16,6 +16,8 @@
 //                row once, write it to each selected local expert row.
 #include "moe_internal.h"
 
+#include <mutex>
+
 namespace moe {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -390,6 +392,58 @@ hipError_t launch_permute(int T, int H, int K, int E_global, int e0, int L, int6
     hipLaunchKernelGGL(k_permute<0>, g, b, 0, s, PERMUTE_ARGS);
 #undef PERMUTE_ARGS
   return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// moe_permute_noalloc: the permute with its workspace in a fixed device array
+// (for callers that cannot allocate).  Each GPU the library runs on holds its
+// own copy of `scratch` until the process ends; host code reaches it only
+// through the address hipGetSymbolAddress returns for the current device
+// (the array's name on the host is a stand-in, not a device address).  Every
+// call first clears the look-back state with a fill kernel (no memset node,
+// so the call can be captured in a graph), then runs the usual two kernels.
+// Calls that overlap on one GPU share the array and race.
+// ---------------------------------------------------------------------------
+#define PERMUTE_SCRATCH_BYTES ((size_t)16 << 20)
+static __device__ __align__(256) uint8_t scratch[PERMUTE_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::once_flag g_scratch_once[kMaxDevices];
+void* g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+}  // namespace
+
+size_t permute_noalloc_max_bytes() { return PERMUTE_SCRATCH_BYTES; }
+
+__global__ void k_fill_u32(uint32_t* __restrict__ p, long n, uint32_t v) {
+  for (long i = (long)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (long)gridDim.x * blockDim.x) p[i] = v;
+}
+
+hipError_t launch_permute_noalloc(int T, int H, int K, int E_global, int e0, int L, int64_t capacity, int x_dtype,
+                                  int out_dtype, const void* x, const int16_t* ids, int32_t* counts,
+                                  int32_t* offsets, void* x_perm, uint8_t* x_scales, int32_t* row_to_slot,
+                                  int32_t* slot_to_row, int32_t* err, hipStream_t s) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  // once per device, with that device current: the device address of its copy
+  std::call_once(g_scratch_once[dev], [dev] {
+    void* ptr = nullptr;
+    g_scratch_err[dev] = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    g_scratch_ptr[dev] = ptr;
+  });
+  if (g_scratch_err[dev] != hipSuccess) return g_scratch_err[dev];
+  void* ws = g_scratch_ptr[dev];
+  const long state_words = (long)(permute_state_bytes(T, K, L) / 4);
+  if (T > 0) {
+    const long blocks = (state_words + 255) / 256;
+    hipLaunchKernelGGL(k_fill_u32, dim3((unsigned)(blocks < 1024 ? blocks : 1024)), dim3(256), 0, s, (uint32_t*)ws,
+                       state_words, 0u);
+  }
+  return launch_permute(T, H, K, E_global, e0, L, capacity, x_dtype, out_dtype, x, ids, counts, offsets, x_perm,
+                        x_scales, row_to_slot, slot_to_row, err, ws, s);
 }
 
 }  // namespace moe

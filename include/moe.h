@@ -266,6 +266,22 @@ int moe_permute(int T, int H, int K, int E_global, int e0, int L, int64_t capaci
                 int32_t* row_to_slot, int32_t* slot_to_row, int32_t* err,
                 void* workspace, size_t workspace_bytes, void* stream);
 
+/* moe_permute for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation): the
+ * same arguments, results and errors without the workspace, which is instead
+ * a fixed array of moe_permute_noalloc_max_workspace_bytes() (16 MiB) that
+ * the library holds on each GPU it runs on until the process ends.  Shapes
+ * whose moe_permute_workspace_bytes(T, K, L) exceed it return
+ * MOE_ERR_WORKSPACE before any launch.  No call allocates or frees memory;
+ * each first clears the array's look-back state with a fill kernel.  Calls
+ * on one GPU share that GPU's array: calls that overlap in time on one GPU
+ * (other streams, other threads) race and must be ordered by the caller. */
+size_t moe_permute_noalloc_max_workspace_bytes(void);
+int moe_permute_noalloc(int T, int H, int K, int E_global, int e0, int L, int64_t capacity,
+                        int x_dtype, int out_dtype, const void* x, const int16_t* ids,
+                        int32_t* counts, int32_t* offsets, void* x_perm, uint8_t* x_perm_scales,
+                        int32_t* row_to_slot, int32_t* slot_to_row, int32_t* err, void* stream);
+
 /* ------------------------------------------------------------------------
  * Expert weights: one-time layout (+ MX quantization)
  *
