@@ -152,7 +152,7 @@ static int permute_check(int T, int H, int K, int E_global, int e0, int L, int64
   if (T < 0 || H <= 0 || K < 1 || K > MOE_MAX_K || E_global <= 0 || E_global > 32767 || L < 1 ||
       L > MOE_MAX_L || e0 < 0 || e0 + L > E_global || capacity < 0)
     return MOE_ERR_SHAPE;
-  if ((int64_t)T * K >= ((int64_t)1 << 30)) return MOE_ERR_SHAPE;  // counts fit the 30-bit look-back flags
+  if ((int64_t)T * K >= ((int64_t)1 << 30)) return MOE_ERR_SHAPE;  // counts fit the 30-bit published tile counts
   if (x_dtype != MOE_BF16 && x_dtype != MOE_F32) return MOE_ERR_DTYPE;
   const bool mx_out = out_dtype == MOE_MXFP8 || out_dtype == MOE_MXFP4;
   if (!(out_dtype == x_dtype || (mx_out && x_dtype == MOE_BF16))) return MOE_ERR_DTYPE;

@@ -194,7 +194,7 @@ hipError_t launch_route_select(int T, int E, int K, int S, int score, const floa
                                float* logits_out, int32_t* err, hipStream_t s,
                                const RouteGroups* grp = nullptr, float* scores_out = nullptr);
 
-int permute_tile_tokens(int T, int K);
+int permute_tile_tokens(int T, int K, int L);
 size_t permute_workspace_bytes(int T, int K, int L);
 size_t permute_state_bytes(int T, int K, int L);  // the zero-between-calls prefix
 size_t permute_noalloc_max_bytes();

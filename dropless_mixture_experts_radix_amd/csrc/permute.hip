@@ -5,15 +5,17 @@
 // wavefront ballot over its K slots, iterating the set bits).  bpdata article,
 // "Optimization 1: Grouped GEMM": expert token counts stay on the device.
 //
-// Two kernels, no host round trip:
-//  k_count_scan  per tile of TT tokens: per-local-expert histogram (LDS), the
-//                stable rank of every local slot among the tile's slots of
-//                the same expert (wavefront ballots, flat slot order), and a
-//                single-pass decoupled look-back scan across tiles: per-tile
-//                expert bases; the last tile writes counts[L], offsets[L+1]
-//                and the overflow flag.
-//  k_permute     one wavefront per token: ballot over its K slots, read the
-//                row once, write it to each selected local expert row.
+// k_count_scan: one workgroup per tile of TT consecutive tokens counts the
+// tile's slots per local expert (ids staged in LDS), gives each local slot
+// its row within the tile and expert, publishes the tile's counts and counts
+// itself finished on a device counter.  The workgroup that finishes last
+// scans every tile's counts (read at once, in parallel): each tile's base row
+// per expert, the expert counts and offsets.  No workgroup waits for
+// another (a single-pass scan without a look-back chain: the last arrival
+// sees all counts).
+// k_permute: one wavefront per token; each local slot's row is its expert's
+// offset + its tile's base + its row within the tile; the token's row is
+// copied (or MX-quantized) to each of them.
 #include "moe_internal.h"
 
 #include <mutex>
@@ -22,198 +24,179 @@ namespace moe {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-// Tokens per count tile: about T*K/256 slots per tile (at least 64, at most
-// 512), so that small-K layers still spread the counting over many CUs.
-int permute_tile_tokens(int T, int K) {
+// Tiles: about PERM_TILE_SLOTS slots each, at most PERM_SCAN_MAX / L tiles
+// (the scan reads ntiles * L counts); a tile is counted PERM_CHUNK slots at a
+// time (its ids staged in LDS) by PERM_WAVES wavefronts.
+#define PERM_TILE_SLOTS 2048
+#define PERM_SCAN_MAX 16384
+#define PERM_CHUNK 8192
+#ifndef PERM_SINGLE_SLOTS
+#define PERM_SINGLE_SLOTS PERM_TILE_SLOTS  // batches of at most this many slots are one tile
+#endif
+#define PERM_WAVES 8
+#define PERM_THREADS (PERM_WAVES * 64)
+int permute_tile_tokens(int T, int K, int L) {
   if (K < 1) K = 1;
-  long slots = (long)T * K / 256;
-  slots = slots < 64 ? 64 : (slots > 512 ? 512 : slots);
-  int tt = (int)(slots / K);
-  if (tt < 1) tt = 1;
-  return tt;
+  if (L < 1) L = 1;
+  if ((long)T * K <= PERM_SINGLE_SLOTS) return T > 0 ? T : 1;  // one tile: no scan across tiles
+  long tt = (PERM_TILE_SLOTS + K - 1) / K;
+  long nt = ((long)T + tt - 1) / tt;
+  const long ntmax = PERM_SCAN_MAX / L > 0 ? PERM_SCAN_MAX / L : 1;
+  if (nt > ntmax) tt = ((long)T + ntmax - 1) / ntmax;
+  return (int)(tt < 1 ? 1 : tt);
 }
 
 // ---------------------------------------------------------------------------
 // Workspace of the permute (byte offsets; ntiles tiles of TT tokens):
-//   [0, 256)                    the tile ticket counter (uint32)
-//   [256, ...)                  look-back flags [ntiles][L] uint32
-//   next 256-byte boundary      each slot's row within its expert [T*K] int32
-// All of it is zero between calls: the caller zero-fills the workspace once,
-// and k_permute returns everything a call wrote to zero (the flags, the
-// counter, and each slot's row once it has been read), so calls of different
-// shapes can share one workspace.
+//   0                       the count of finished tiles (uint32)
+//   256                     tile counts [ntiles][L] uint32 (bit 30: published)
+//   next 256-byte boundary  tile bases [ntiles][L] int32
+//   next 256-byte boundary  each local slot's row within its tile and expert [T*K]
+// The counter and the tile counts (the state) are zero between calls: the
+// caller zero-fills the workspace once, and the scanning workgroup returns
+// them to zero.  The bases and rows are written before they are read.
 // ---------------------------------------------------------------------------
+#define PERM_FLAGS_OFF 256
+
 struct PermuteWs {
-  uint32_t* ticket;
+  uint32_t* done;
   uint32_t* flags;
+  int32_t* tilebase;
   int32_t* rank;
 };
 
 static inline size_t ws_round(size_t v) { return (v + 255) / 256 * 256; }
 
+static int permute_ntiles(int T, int K, int L) {
+  const int TT = permute_tile_tokens(T, K, L);
+  return T > 0 ? (T + TT - 1) / TT : 0;
+}
+
 static PermuteWs permute_ws(void* ws, int ntiles, int L) {
   uint8_t* b = (uint8_t*)ws;
+  const size_t fl = ws_round((size_t)ntiles * L * 4);
   PermuteWs w;
-  w.ticket = (uint32_t*)b;
-  w.flags = (uint32_t*)(b + 256);
-  w.rank = (int32_t*)(b + 256 + ws_round((size_t)ntiles * L * 4));
+  w.done = (uint32_t*)b;
+  w.flags = (uint32_t*)(b + PERM_FLAGS_OFF);
+  w.tilebase = (int32_t*)(b + PERM_FLAGS_OFF + fl);
+  w.rank = (int32_t*)(b + PERM_FLAGS_OFF + 2 * fl);
   return w;
 }
 
 size_t permute_state_bytes(int T, int K, int L) {
-  const int TT = permute_tile_tokens(T, K);
-  const size_t ntiles = (size_t)(T > 0 ? (T + TT - 1) / TT : 0);
-  return 256 + ws_round(ntiles * L * 4);
+  return PERM_FLAGS_OFF + ws_round((size_t)permute_ntiles(T, K, L) * L * 4);
 }
 
 size_t permute_workspace_bytes(int T, int K, int L) {
-  const int TT = permute_tile_tokens(T, K);
-  const size_t ntiles = (size_t)(T > 0 ? (T + TT - 1) / TT : 0);
-  return 256 + ws_round(ntiles * L * 4) + ws_round((size_t)T * K * 4);
+  const size_t fl = ws_round((size_t)permute_ntiles(T, K, L) * L * 4);
+  return PERM_FLAGS_OFF + 2 * fl + ws_round((size_t)T * K * 4);
 }
 
-// A look-back flag: the tile's count of one expert (AGG: its own slots; INCL:
-// its slots and every earlier tile's) in the low 30 bits.  0: not yet known.
-#define PERM_AGG (1u << 30)
-#define PERM_INCL (2u << 30)
+#define PERM_PUBLISHED (1u << 30)
 #define PERM_VALUE ((1u << 30) - 1)
-// bound on the polls of one flag (each after s_sleep 2, about 0.1 us): a
-// predecessor tile publishes its count within microseconds of starting, so
-// the bound is only reached when the workspace was not zero-filled; the
-// tile then reports MOE_DEVERR_WORKSPACE instead of waiting forever
+// bound on the polls of one tile's counts by the scanning workgroup: every
+// tile has published its counts before it counts itself finished, so the
+// polls only wait for those stores to become visible; the bound (about a
+// second) is reached only when the counter was not zero at the start, and
+// the call then reports MOE_DEVERR_WORKSPACE
 #define PERM_MAX_POLLS (1 << 20)
 
-__device__ __forceinline__ uint32_t flag_load(const uint32_t* p) {
+__device__ __forceinline__ uint32_t flag_load_relaxed(const uint32_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ void flag_store(uint32_t* p, uint32_t v) {
+__device__ __forceinline__ void flag_store_relaxed(uint32_t* p, uint32_t v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+// Poll a tile's count until published (relaxed loads at device scope),
+// backing off from 64 to 2048 clocks between polls; still unpublished after
+// the bound, it returns 0.  Out of line: the scan's unrolled loads each keep
+// only a call.  The count is the data itself, so no acquire is needed.
+__device__ __attribute__((noinline)) uint32_t flag_wait_slow(const uint32_t* p) {
+  uint32_t f = flag_load_relaxed(p);
+  for (int polls = 0; !(f & PERM_PUBLISHED); ++polls) {
+    if (polls >= PERM_MAX_POLLS) return 0u;
+    if (polls < 8) __builtin_amdgcn_s_sleep(1);
+    else if (polls < 16) __builtin_amdgcn_s_sleep(4);
+    else __builtin_amdgcn_s_sleep(32);
+    f = flag_load_relaxed(p);
+  }
+  return f;
+}
 
-// ---------------------------------------------------------------------------
-// k_count_scan: grid = ntiles, 256 threads.  Dynamic LDS: cnt[4][L] + tot[L]
-// + base[L] + rank[TT*K] int32.
-//
-// A workgroup takes the next tile from the ticket counter (so every earlier
-// tile belongs to a workgroup that has started), counts its local slots per
-// expert (LDS histograms; the stable rank of each slot among the tile's slots
-// of its expert from wavefront ballots, flat slot order), and then finds each
-// expert's count in all earlier tiles by a decoupled look-back (Merrill and
-// Garland, "Single-pass Parallel Prefix Scan with Decoupled Look-back", 2016):
-// it publishes its own count (AGG), adds the predecessors' published counts
-// until one of them is inclusive (INCL), and publishes its inclusive count.
-// The exclusive count is the tile's base for that expert; each local slot's
-// row within its expert (base + its rank in the tile) goes to `rank`.  The
-// last tile's inclusive counts are the expert totals: it writes counts,
-// offsets (their exclusive scan) and the overflow flag.  One pass over the
-// ids, no second kernel over the tile histograms.
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void k_count_scan(int T, int K, int E_global, int e0, int L, int TT, int ntiles,
-                                                    int64_t capacity, const int16_t* __restrict__ ids,
-                                                    uint32_t* __restrict__ ticket, uint32_t* __restrict__ flags,
-                                                    int32_t* __restrict__ rank,
-                                                    int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
-                                                    int32_t* err) {
-  extern __shared__ int32_t lds[];
-  int32_t* cnt = lds;              // [4][L]
-  int32_t* tot = lds + 4 * L;      // [L] inclusive counts (last tile)
-  int32_t* base = lds + 5 * L;     // [L] exclusive counts: the tile's base per expert
-  int32_t* srank = lds + 6 * L;    // [TT*K]
-  __shared__ int s_tile;
-  __shared__ int s_wsum[4];
+// The lanes of the wavefront holding the same local expert as this lane
+// (among the lanes with one, mask `valid`), from one ballot per bit of the
+// expert index: O(log L) wavefront instructions per 64 slots, however many
+// distinct experts they hold.
+__device__ __forceinline__ uint64_t same_expert_lanes(int le, uint64_t valid, int nbits) {
+  uint64_t peers = valid;
+  for (int b = 0; b < nbits; ++b) {
+    const bool bit = (le >> b) & 1;
+    const uint64_t m = wave_ballot(bit);
+    peers &= bit ? m : ~m;
+  }
+  return peers;
+}
+
+// One pass over a chunk of a tile's slots (staged in LDS, PERM_CHUNK
+// entries), each wavefront over a contiguous part, 4 x 64 slots per step:
+// for each 64 slots the lanes of each local expert (bit ballots); PASS 0
+// adds their number to the wavefront's count of that expert, PASS 1 gives
+// each local slot its row within the tile and expert (the wavefront's
+// running row of that expert, read before the lowest of those lanes
+// advances it, + the slot's rank among them).  The wavefront's LDS
+// operations run in order, so the counts need no wait between the read and
+// the add; the four id reads of a step are unconditional (clamped index,
+// masked after), so one wait covers them.
+template <int PASS>
+__device__ __forceinline__ bool count_pass(int nslot, int e0, int L, int E_global, int nbits, const int16_t* s_ids,
+                                           int32_t* mycnt, int32_t* __restrict__ rank, long f0) {
   const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
-  if (threadIdx.x == 0) s_tile = (int)atomicAdd(ticket, 1u);
-  for (int i = threadIdx.x; i < 4 * L; i += 256) cnt[i] = 0;
-  __syncthreads();
-  const int tile = s_tile;
-  if ((unsigned)tile >= (unsigned)ntiles) {  // the counter was not zero: a workspace that was not zero-filled
-    if (threadIdx.x == 0) set_err(err, MOE_DEVERR_WORKSPACE);
-    return;
-  }
-  const long f0 = (long)tile * TT * K;
-  long fend = f0 + (long)TT * K;
-  const long ftot = (long)T * K;
-  if (fend > ftot) fend = ftot;
-  const int nslot = (int)(fend - f0);
-  // wave w handles slots [w*part, (w+1)*part) of the tile, 64 at a time
-  const int part = (((nslot + 3) / 4) + 63) / 64 * 64;
+  const int part = (((nslot + PERM_WAVES - 1) / PERM_WAVES) + 63) / 64 * 64;
   const int s_begin = w * part, s_end = min(nslot, s_begin + part);
-  int32_t* mycnt = cnt + w * L;
+  const uint64_t lt = (1ull << l) - 1;
   bool bad = false;
-  for (int c = s_begin; c < s_end; c += 64) {
-    const int sl = c + l;
-    int le = -1;
-    if (sl < s_end) {
-      const int id = ids[f0 + sl];
-      if (id < -1 || id >= E_global) bad = true;
-      else if (id >= e0 && id < e0 + L) le = id - e0;
+  for (int c = s_begin; c < s_end; c += 256) {
+    int id[4], le[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) id[u] = s_ids[min(c + u * 64 + l, PERM_CHUNK - 1)];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const bool in = c + u * 64 + l < s_end;
+      bad |= in && (id[u] < -1 || id[u] >= E_global);
+      le[u] = (in && id[u] >= e0 && id[u] < e0 + L && id[u] < E_global) ? id[u] - e0 : -1;
     }
-    uint64_t active = wave_ballot(le >= 0);
-    int myrank = 0;
-    while (active) {  // one iteration per distinct expert among the 64 slots
-      const int leader = __builtin_ctzll(active);
-      const int v = readlane_i(le, leader);
-      const uint64_t m = wave_ballot(le == v);
-      const int base = readlane_i(l == leader ? mycnt[v] : 0, leader);
-      if (le == v) myrank = base + mask_rank(m);
-      if (l == leader) mycnt[v] = base + __builtin_popcountll(m);
-      active &= ~m;
+    uint64_t peers[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const uint64_t valid = wave_ballot(le[u] >= 0);
+      peers[u] = valid ? same_expert_lanes(le[u], valid, nbits) : 0ull;
     }
-    if (sl < s_end) srank[sl] = myrank;
-  }
-  if (wave_ballot(bad) && l == 0) set_err(err, MOE_DEVERR_BAD_ID);
-  __syncthreads();
-  // per-wave bases, the tile's count of each expert, the look-back
-  bool stuck = false;
-  for (int e = threadIdx.x; e < L; e += 256) {
-    const int c0 = cnt[e], c1 = cnt[L + e], c2 = cnt[2 * L + e], c3 = cnt[3 * L + e];
-    const int agg = c0 + c1 + c2 + c3;
-    cnt[e] = 0;
-    cnt[L + e] = c0;
-    cnt[2 * L + e] = c0 + c1;
-    cnt[3 * L + e] = c0 + c1 + c2;
-    uint32_t* mine = flags + (long)tile * L + e;
-    int excl = 0;
-    if (tile == 0) {
-      flag_store(mine, PERM_INCL | (uint32_t)agg);
-    } else {
-      flag_store(mine, PERM_AGG | (uint32_t)agg);
-      for (int p = tile - 1; p >= 0; --p) {
-        const uint32_t* fp = flags + (long)p * L + e;
-        uint32_t f = flag_load(fp);
-        for (int polls = 0; f == 0u; ++polls) {
-          if (polls >= PERM_MAX_POLLS) { stuck = true; break; }
-          __builtin_amdgcn_s_sleep(2);
-          f = flag_load(fp);
-        }
-        if (stuck) break;
-        excl += (int)(f & PERM_VALUE);
-        if ((f & ~PERM_VALUE) == PERM_INCL) break;
+    int base[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      base[u] = 0;
+      if (le[u] >= 0) {
+        int32_t* cp = mycnt + le[u];
+        if (PASS == 1) base[u] = __hip_atomic_load(cp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        if (!(peers[u] & lt))
+          __hip_atomic_fetch_add(cp, __builtin_popcountll(peers[u]), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
       }
-      flag_store(mine, PERM_INCL | (uint32_t)(excl + agg));
     }
-    // a count outside [0, T*K] can only come from flags that were not zero
-    // before the call: report it, and keep the offsets monotone and >= 0
-    const int tk = T * K;
-    if (excl < 0 || excl > tk - agg) {
-      stuck = true;
-      excl = excl < 0 ? 0 : tk - agg;
+    if (PASS == 1) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (le[u] >= 0) rank[f0 + c + u * 64 + l] = base[u] + __builtin_popcountll(peers[u] & lt);
     }
-    base[e] = excl;
-    tot[e] = excl + agg;
   }
-  if (stuck) set_err(err, MOE_DEVERR_WORKSPACE);
-  __syncthreads();
-  for (int sl = threadIdx.x; sl < nslot; sl += 256) {
-    const int id = ids[f0 + sl];
-    int r = 0;
-    if (id >= e0 && id < e0 + L && id < E_global)
-      r = base[id - e0] + srank[sl] + cnt[(sl / part) * L + (id - e0)];
-    rank[f0 + sl] = r;
-  }
-  if (tile != ntiles - 1) return;
-  // the last tile: expert totals -> counts, offsets (exclusive scan), overflow
-  const int per = (L + 255) / 256;
+  return bad;
+}
+
+// Expert totals (LDS) -> counts, offsets (exclusive scan, offsets[L] = N),
+// MOE_DEVERR_OVERFLOW when N > capacity; all threads of the workgroup.
+__device__ __forceinline__ void expert_offsets(int L, int64_t capacity, const int32_t* tot, int32_t* __restrict__ counts,
+                                               int32_t* __restrict__ offsets, int32_t* err, int* s_wsum) {
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+  const int per = (L + PERM_THREADS - 1) / PERM_THREADS;
   const int b0 = threadIdx.x * per;
   int loc = 0;
   for (int i = 0; i < per; ++i)
@@ -221,49 +204,198 @@ __global__ __launch_bounds__(256) void k_count_scan(int T, int K, int E_global, 
   const int incl = wave_incl_scan(loc);
   if (l == 63) s_wsum[w] = incl;
   __syncthreads();
-  int run = incl - loc;
-  for (int i = 0; i < w; ++i) run += s_wsum[i];
+  int r = incl - loc;
+  for (int i = 0; i < w; ++i) r += s_wsum[i];
   for (int i = 0; i < per; ++i) {
     const int e = b0 + i;
     if (e < L) {
       counts[e] = tot[e];
-      offsets[e] = run;
-      run += tot[e];
+      offsets[e] = r;
+      r += tot[e];
     }
   }
-  if (threadIdx.x == 255) {
-    offsets[L] = run;
-    if ((int64_t)run > capacity) set_err(err, MOE_DEVERR_OVERFLOW);
-  }
-}
-
-// counts and offsets of an empty batch
-__global__ void k_zero_counts(int L, int32_t* __restrict__ counts, int32_t* __restrict__ offsets) {
-  for (int e = threadIdx.x; e <= L; e += blockDim.x) {
-    if (e < L) counts[e] = 0;
-    offsets[e] = 0;
+  if (threadIdx.x == PERM_THREADS - 1) {
+    offsets[L] = r;
+    if ((int64_t)r > capacity) set_err(err, MOE_DEVERR_OVERFLOW);
   }
 }
 
 // ---------------------------------------------------------------------------
-// k_permute: one wavefront per token, 4 per workgroup.  It also returns the
-// workspace to zero for the next call: the look-back state of k_count_scan
-// (which has finished: same stream) and each slot's row once read.
+// k_count_scan: one workgroup of PERM_THREADS threads per tile.
+// Dynamic LDS: cnt[PERM_WAVES][L] + run[L] int32, then the chunk's ids int16
+// [PERM_CHUNK].
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(PERM_THREADS) void k_count_scan(int T, int K, int E_global, int e0, int L, int TT, int ntiles,
+                                                    int64_t capacity, const int16_t* __restrict__ ids,
+                                                    uint32_t* __restrict__ done, uint32_t* __restrict__ flags,
+                                                    int32_t* __restrict__ tilebase, int32_t* __restrict__ rank,
+                                                    int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+                                                    int32_t* err) {
+  extern __shared__ int32_t lds[];
+  int32_t* cnt = lds;                   // [PERM_WAVES][L]: per-wavefront counts of a chunk, then running rows
+  int32_t* run = lds + PERM_WAVES * L;  // [L]: the tile's count so far (the scan: expert totals)
+  int16_t* s_ids = (int16_t*)(lds + (PERM_WAVES + 1) * L);
+  __shared__ int s_last;
+  __shared__ int s_wsum[PERM_WAVES];
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+  const int tile = blockIdx.x;
+  int nbits = 0;
+  while ((1 << nbits) < L) ++nbits;
+  const long f0 = (long)tile * TT * K;
+  long fend = f0 + (long)TT * K;
+  if (fend > (long)T * K) fend = (long)T * K;
+  for (int e = threadIdx.x; e < L; e += PERM_THREADS) run[e] = 0;
+  bool bad = false;
+  for (long c0 = f0; c0 < fend; c0 += PERM_CHUNK) {
+    const int n = (int)(fend - c0 < PERM_CHUNK ? fend - c0 : PERM_CHUNK);
+    for (int i = threadIdx.x; i < PERM_WAVES * L; i += PERM_THREADS) cnt[i] = 0;
+    for (int i0 = 0; i0 < n; i0 += PERM_THREADS * 4) {  // the chunk's ids, four loads in flight per thread
+      int16_t v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int i = i0 + u * PERM_THREADS + threadIdx.x;
+        v[u] = i < n ? ids[c0 + i] : (int16_t)-1;
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int i = i0 + u * PERM_THREADS + threadIdx.x;
+        if (i < n) s_ids[i] = v[u];
+      }
+    }
+    __syncthreads();
+    bad |= count_pass<0>(n, e0, L, E_global, nbits, s_ids, cnt + w * L, rank, c0);
+    __syncthreads();
+    for (int e = threadIdx.x; e < L; e += PERM_THREADS) {  // each wavefront's running rows start after the earlier slots'
+      int r = run[e];
+#pragma unroll
+      for (int v = 0; v < PERM_WAVES; ++v) {
+        const int c = cnt[v * L + e];
+        cnt[v * L + e] = r;
+        r += c;
+      }
+      run[e] = r;
+    }
+    __syncthreads();
+    count_pass<1>(n, e0, L, E_global, nbits, s_ids, cnt + w * L, rank, c0);
+    __syncthreads();
+  }
+  if (wave_ballot(bad) && l == 0) set_err(err, MOE_DEVERR_BAD_ID);
+  if (ntiles == 1) {  // the whole batch in one tile: its counts are the totals
+    __syncthreads();
+    for (int e = threadIdx.x; e < L; e += PERM_THREADS) tilebase[e] = 0;
+    expert_offsets(L, capacity, run, counts, offsets, err, s_wsum);
+    return;
+  }
+  // publish the tile's counts, then count the tile finished.  Each count
+  // carries the published bit, and the scanning workgroup polls every count
+  // it reads until the bit is set, so neither store needs to be ordered
+  // before the other (no fence: a release here would write back the L2 once
+  // per wavefront of every tile).  The rows within the tile are read only
+  // by the next kernel.
+  for (int e = threadIdx.x; e < L; e += PERM_THREADS) flag_store_relaxed(flags + (long)tile * L + e, PERM_PUBLISHED | (uint32_t)run[e]);
+  if (threadIdx.x == 0) {
+    const uint32_t old = __hip_atomic_fetch_add(done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (old >= (uint32_t)ntiles) set_err(err, MOE_DEVERR_WORKSPACE);  // the counter was not zero
+    s_last = old == (uint32_t)ntiles - 1;
+  }
+  __syncthreads();
+  if (!s_last) return;
+  // ---- the last tile to finish: each tile's base row per expert (an
+  // exclusive prefix of the counts over the tiles) and each expert's total.
+  // Experts in chunks of NE columns (a power of two), tiles in batches whose
+  // counts fit the LDS stage [tile][NE]; R threads per column (a power of
+  // two, at most 64: a segment of a wavefront), each summing a contiguous run
+  // of the batch's tiles, one segmented scan of those sums across the
+  // column's threads, the batches chained by a running carry.  Rolled loops
+  // throughout: this code runs in one workgroup only, so its instructions
+  // are fetched cold, and its length is its latency.
+  bool stuck = false;
+  int lne = 0;
+  while ((1 << lne) < L && (1 << lne) < PERM_THREADS) ++lne;
+  const int NE = 1 << lne;
+  int lr = 0;
+  while ((1 << lr) * NE < PERM_THREADS && lr < 6) ++lr;
+  const int R = 1 << lr;
+  const int jc = threadIdx.x >> lr, rr = threadIdx.x & (R - 1);
+  const int cap = TT * K;
+  const int nbt = (PERM_CHUNK / 2) >> lne;  // tiles per batch (the stage holds PERM_CHUNK / 2 words)
+  int32_t* s_stage = (int32_t*)s_ids;
+  for (int ec = 0; ec < L; ec += NE) {
+    const int e = ec + jc;
+    const bool col = jc < NE && e < L;
+    int carry = 0;
+    for (int p0 = 0; p0 < ntiles; p0 += nbt) {
+      const int nb = min(nbt, ntiles - p0), words = nb << lne;
+      __syncthreads();
+      // plain loads, eight in flight per thread: a count read stale reads
+      // unpublished and is polled again
+      for (int i0 = 0; i0 < words; i0 += PERM_THREADS * 8) {
+        uint32_t f[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int i = i0 + u * PERM_THREADS + threadIdx.x, ee = ec + (i & (NE - 1));
+          f[u] = (i < words && ee < L) ? __hip_atomic_load(flags + (long)(p0 + (i >> lne)) * L + ee, __ATOMIC_RELAXED,
+                                                           __HIP_MEMORY_SCOPE_WORKGROUP)
+                                       : PERM_PUBLISHED;
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int i = i0 + u * PERM_THREADS + threadIdx.x;
+          if (i < words) s_stage[i] = (int32_t)f[u];
+        }
+      }
+      __syncthreads();
+      const int per = (nb + R - 1) >> lr, pa = min(nb, rr * per), pe = min(nb, pa + per);
+      int mine = 0;
+      if (col)
+        for (int p = pa; p < pe; ++p) {
+          uint32_t f = (uint32_t)s_stage[(p << lne) + jc];
+          if (!(f & PERM_PUBLISHED)) {
+            f = flag_wait_slow(flags + (long)(p0 + p) * L + e);
+            stuck |= !(f & PERM_PUBLISHED);
+            s_stage[(p << lne) + jc] = (int32_t)f;
+          }
+          mine += min((int)(f & PERM_VALUE), cap);
+        }
+      int incl = mine;
+      for (int d = 1; d < R; d <<= 1) {
+        const int y = __shfl_up(incl, d, R);
+        if (rr >= d) incl += y;
+      }
+      if (col) {
+        int base = carry + incl - mine;
+        for (int p = pa; p < pe; ++p) {
+          tilebase[(long)(p0 + p) * L + e] = base;
+          base += min((int)((uint32_t)s_stage[(p << lne) + jc] & PERM_VALUE), cap);
+        }
+      }
+      carry += __shfl(incl, R - 1, R);
+    }
+    if (col && rr == 0) run[e] = carry;
+  }
+  __syncthreads();
+  expert_offsets(L, capacity, run, counts, offsets, err, s_wsum);
+  if (stuck) set_err(err, MOE_DEVERR_WORKSPACE);
+  // the state back to zero for the next call (every tile has published and
+  // counted itself finished; the stream orders the next call after this one)
+  const long nflags = (long)ntiles * L;
+  for (long i = threadIdx.x; i < nflags; i += PERM_THREADS) flags[i] = 0u;
+  if (threadIdx.x == 0) *done = 0u;
+}
+
+// ---------------------------------------------------------------------------
+// k_permute: 4 tokens per workgroup, one wavefront each.
 // ---------------------------------------------------------------------------
 template <int OUT>  // OUT 0: copy rows (bf16 or fp32, row_bytes), 1: MXFP8-, 2: MXFP4-quantize bf16 rows
-__global__ __launch_bounds__(256) void k_permute(int T, int K, int e0, int L, int TT, int64_t capacity,
-                                                 int row_bytes, const uint8_t* __restrict__ x,
-                                                 const int16_t* __restrict__ ids,
-                                                 int32_t* __restrict__ rank,
-                                                 const int32_t* __restrict__ offsets,
-                                                 uint8_t* __restrict__ x_perm, uint8_t* __restrict__ x_scales,
-                                                 int32_t* __restrict__ row_to_slot,
-                                                 int32_t* __restrict__ slot_to_row, uint32_t* __restrict__ ticket,
-                                                 uint32_t* __restrict__ flags, long nflags) {
-  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + w;
-  for (long i = (long)blockIdx.x * 256 + threadIdx.x; i < nflags; i += (long)gridDim.x * 256) flags[i] = 0u;
-  if (blockIdx.x == 0 && threadIdx.x == 0) *ticket = 0u;
+__global__ __launch_bounds__(256) void k_permute(int T, int K, int e0, int L, int TT, int64_t capacity, int row_bytes,
+                                                 const uint8_t* __restrict__ x, const int16_t* __restrict__ ids,
+                                                 const int32_t* __restrict__ tilebase,
+                                                 const int32_t* __restrict__ rank,
+                                                 const int32_t* __restrict__ offsets, uint8_t* __restrict__ x_perm,
+                                                 uint8_t* __restrict__ x_scales, int32_t* __restrict__ row_to_slot,
+                                                 int32_t* __restrict__ slot_to_row) {
+  const int l = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
   int dest = -1;
   if (l < K) {
@@ -271,24 +403,22 @@ __global__ __launch_bounds__(256) void k_permute(int T, int K, int e0, int L, in
     const int id = ids[f];
     if (id >= e0 && id < e0 + L) {
       const int le = id - e0;
-      const int64_t d = (int64_t)offsets[le] + rank[f];
+      const int64_t d = (int64_t)offsets[le] + tilebase[(long)(t / TT) * L + le] + rank[f];
       dest = (d >= 0 && d < capacity) ? (int)d : -1;
     }
-    rank[f] = 0;
     slot_to_row[f] = dest;
   }
-  uint64_t bits = wave_ballot(dest >= 0);
-  if (!bits) return;  // no selected local slot: the row is never read
+  const uint64_t bits = wave_ballot(dest >= 0);
+  if (!bits) return;
   const uint8_t* src = x + (long)t * row_bytes;
-  // rows move in 1 KiB pieces (16 bytes per lane), up to 8 pieces in flight
   const int npiece = (row_bytes + 1023) / 1024;
+  // rows move in 1 KiB pieces (16 bytes per lane), eight pieces in flight
   for (int p0 = 0; p0 < npiece; p0 += 8) {
     u32x4 v[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int off = (p0 + j) * 1024 + l * 16;
-      if (p0 + j < npiece && off < row_bytes) v[j] = *(const u32x4*)(src + off);
-      else v[j] = u32x4{0, 0, 0, 0};
+      v[j] = (p0 + j < npiece && off < row_bytes) ? *(const u32x4*)(src + off) : u32x4{0, 0, 0, 0};
     }
     if (OUT == 0) {
       uint64_t b = bits;
@@ -363,6 +493,14 @@ __global__ __launch_bounds__(256) void k_permute(int T, int K, int e0, int L, in
   }
 }
 
+// counts and offsets of an empty batch
+__global__ void k_zero_counts(int L, int32_t* __restrict__ counts, int32_t* __restrict__ offsets) {
+  for (int e = threadIdx.x; e <= L; e += blockDim.x) {
+    if (e < L) counts[e] = 0;
+    offsets[e] = 0;
+  }
+}
+
 hipError_t launch_permute(int T, int H, int K, int E_global, int e0, int L, int64_t capacity,
                           int x_dtype, int out_dtype, const void* x, const int16_t* ids,
                           int32_t* counts, int32_t* offsets, void* x_perm, uint8_t* x_scales,
@@ -372,18 +510,24 @@ hipError_t launch_permute(int T, int H, int K, int E_global, int e0, int L, int6
     hipLaunchKernelGGL(k_zero_counts, dim3(1), dim3(256), 0, s, L, counts, offsets);
     return hipGetLastError();
   }
-  const int TT = permute_tile_tokens(T, K);
+  const int TT = permute_tile_tokens(T, K, L);
   const int ntiles = (T + TT - 1) / TT;
   const PermuteWs w = permute_ws(ws, ntiles, L);
-  const size_t lds = (size_t)(6 * L + TT * K) * sizeof(int32_t);
-  hipLaunchKernelGGL(k_count_scan, dim3(ntiles), dim3(256), lds, s, T, K, E_global, e0, L, TT, ntiles, capacity, ids,
-                     w.ticket, w.flags, w.rank, counts, offsets, err);
+  // at most (PERM_WAVES + 1) * MOE_MAX_L * 4 + 16 KiB = 88 KiB
+  const size_t lds = (size_t)((PERM_WAVES + 1) * L) * sizeof(int32_t) + PERM_CHUNK * sizeof(int16_t);
+  static const bool attr_done = [] {
+    (void)hipFuncSetAttribute((const void*)k_count_scan, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              (int)((PERM_WAVES + 1) * MOE_MAX_L * sizeof(int32_t) + PERM_CHUNK * sizeof(int16_t)));
+    return true;
+  }();
+  (void)attr_done;
+  hipLaunchKernelGGL(k_count_scan, dim3(ntiles), dim3(PERM_THREADS), lds, s, T, K, E_global, e0, L, TT, ntiles, capacity, ids,
+                     w.done, w.flags, w.tilebase, w.rank, counts, offsets, err);
   const int row_bytes = H * (x_dtype == MOE_F32 ? 4 : 2);
   const dim3 g((T + 3) / 4), b(256);
-  const long nflags = (long)ntiles * L;
-#define PERMUTE_ARGS                                                                                                 \
-  T, K, e0, L, TT, capacity, row_bytes, (const uint8_t*)x, ids, w.rank,                                          \
-      (const int32_t*)offsets, (uint8_t*)x_perm, x_scales, row_to_slot, slot_to_row, w.ticket, w.flags, nflags
+#define PERMUTE_ARGS                                                                                          \
+  T, K, e0, L, TT, capacity, row_bytes, (const uint8_t*)x, ids, (const int32_t*)w.tilebase,                 \
+      (const int32_t*)w.rank, (const int32_t*)offsets, (uint8_t*)x_perm, x_scales, row_to_slot, slot_to_row
   if (out_dtype == MOE_MXFP8)
     hipLaunchKernelGGL(k_permute<1>, g, b, 0, s, PERMUTE_ARGS);
   else if (out_dtype == MOE_MXFP4)
@@ -400,8 +544,8 @@ hipError_t launch_permute(int T, int H, int K, int E_global, int e0, int L, int6
 // own copy of `scratch` until the process ends; host code reaches it only
 // through the address hipGetSymbolAddress returns for the current device
 // (the array's name on the host is a stand-in, not a device address).  Every
-// call first clears the look-back state with a fill kernel (no memset node,
-// so the call can be captured in a graph), then runs the usual two kernels.
+// call first clears the counter and tile counts with a fill kernel (no memset
+// node, so the call can be captured in a graph), then runs the two kernels.
 // Calls that overlap on one GPU share the array and race.
 // ---------------------------------------------------------------------------
 #define PERMUTE_SCRATCH_BYTES ((size_t)16 << 20)

@@ -66,7 +66,7 @@ class MoELayer:
         self.x_perm_scales = torch.empty((cap, H // 32), dtype=torch.uint8, device=dev) if mx else None
         self.row_to_slot = torch.empty(cap, **i32)
         self.slot_to_row = torch.empty((T, K), **i32)
-        # zero-filled once: the permute's look-back state starts (and is left) at zero
+        # zero-filled once: the permute's state (counter, tile counts) starts and is left at zero
         self.perm_ws = torch.zeros(M.moe_permute_workspace_bytes(T, K, L), dtype=torch.uint8, device=dev)
         self.y_perm = torch.empty((cap, H), dtype=act, device=dev)
         self.mlp_ws = torch.empty(M.moe_grouped_mlp_workspace_bytes(cap, F, dtype), dtype=torch.uint8, device=dev)

@@ -246,16 +246,20 @@ int moe_route_topk_grouped(int T, int E, int K, int H, int n_group, int topk_gro
  * x_perm receives packed E2M1 codes [capacity,H/2] uint8 and x_perm_scales
  * the E8M0 scales [capacity,H/32] (scale exponent floor(log2 max|v|) - 2,
  * round to nearest even, saturate at 6).
- * Scan: the counts of tiles of consecutive tokens are combined in one pass
- * over the ids by a decoupled look-back (each tile publishes its own counts,
- * then adds its predecessors' until it meets an inclusive count; Merrill and
- * Garland 2016), so the scan needs no second kernel over the tile counts.
+ * Two kernels: the first counts tiles of consecutive tokens (one workgroup
+ * per tile, ids staged in LDS), gives each local slot its row within its
+ * tile and expert, and publishes the tile's counts; the workgroup that
+ * finishes last scans all tiles' counts (each tile's base row per expert,
+ * the expert counts and offsets: a single-pass scan in which no workgroup
+ * waits for another).  The second moves (or MX-quantizes) each token's row
+ * to its rows.
  * Workspace: moe_permute_workspace_bytes(T, K, L) bytes, zero-filled before
- * its first use; every byte a call writes to it is zero again when the
- * call's kernels end, so one workspace serves any number of calls, on one
- * stream at a time, of any shape whose size fits.  A workspace found not
- * zero-filled sets MOE_DEVERR_WORKSPACE (the outputs are then unspecified;
- * the call still ends, and leaves the workspace zero).  Limit: T * K < 2^30.
+ * its first use; each call returns its state (a counter and the tile counts,
+ * the first bytes) to zero when its kernels end, so one workspace serves any
+ * number of calls, on one stream at a time, of any shape whose size fits.
+ * A workspace found not zero-filled sets MOE_DEVERR_WORKSPACE: the outputs
+ * are then unspecified, the call still ends, and the workspace must be
+ * zero-filled again before the next call.  Limit: T * K < 2^30.
  * ------------------------------------------------------------------------ */
 size_t moe_permute_workspace_bytes(int T, int K, int L);
 
@@ -273,7 +277,7 @@ int moe_permute(int T, int H, int K, int E_global, int e0, int L, int64_t capaci
  * the library holds on each GPU it runs on until the process ends.  Shapes
  * whose moe_permute_workspace_bytes(T, K, L) exceed it return
  * MOE_ERR_WORKSPACE before any launch.  No call allocates or frees memory;
- * each first clears the array's look-back state with a fill kernel.  Calls
+ * each first clears the array's counters and flags with a fill kernel.  Calls
  * on one GPU share that GPU's array: calls that overlap in time on one GPU
  * (other streams, other threads) race and must be ordered by the caller. */
 size_t moe_permute_noalloc_max_workspace_bytes(void);
