@@ -29,7 +29,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 // time (its ids staged in LDS) by PERM_WAVES wavefronts.
 #define PERM_TILE_SLOTS 2048
 #define PERM_SCAN_MAX 16384
-#define PERM_CHUNK 8192
+#define PERM_CHUNK 16384
 #ifndef PERM_SINGLE_SLOTS
 #define PERM_SINGLE_SLOTS PERM_TILE_SLOTS  // batches of at most this many slots are one tile
 #endif
@@ -138,12 +138,12 @@ __device__ __forceinline__ uint64_t same_expert_lanes(int le, uint64_t valid, in
 }
 
 // One pass over a chunk of a tile's slots (staged in LDS, PERM_CHUNK
-// entries), each wavefront over a contiguous part, 4 x 64 slots per step:
-// for each 64 slots the lanes of each local expert (bit ballots); PASS 0
-// adds their number to the wavefront's count of that expert, PASS 1 gives
-// each local slot its row within the tile and expert (the wavefront's
-// running row of that expert, read before the lowest of those lanes
-// advances it, + the slot's rank among them).  The wavefront's LDS
+// entries), each wavefront over a contiguous part, 4 x 64 slots per step.
+// PASS 0 adds each local slot to its wavefront's count of its expert (an
+// LDS add per slot).  PASS 1 finds, for each 64 slots, the lanes of each
+// local expert (bit ballots) and gives each local slot its row within the
+// tile and expert (the wavefront's running row of that expert, read before
+// the lowest of those lanes advances it, + the slot's rank among them).  The wavefront's LDS
 // operations run in order, so the counts need no wait between the read and
 // the add; the four id reads of a step are unconditional (clamped index,
 // masked after), so one wait covers them.
@@ -164,6 +164,12 @@ __device__ __forceinline__ bool count_pass(int nslot, int e0, int L, int E_globa
       const bool in = c + u * 64 + l < s_end;
       bad |= in && (id[u] < -1 || id[u] >= E_global);
       le[u] = (in && id[u] >= e0 && id[u] < e0 + L && id[u] < E_global) ? id[u] - e0 : -1;
+    }
+    if (PASS == 0) {  // counting only: one LDS add per local slot (the order does not matter)
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (le[u] >= 0) __hip_atomic_fetch_add(mycnt + le[u], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      continue;
     }
     uint64_t peers[4];
 #pragma unroll
@@ -226,6 +232,7 @@ __device__ __forceinline__ void expert_offsets(int L, int64_t capacity, const in
 // [PERM_CHUNK].
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(PERM_THREADS) void k_count_scan(int T, int K, int E_global, int e0, int L, int TT, int ntiles,
+                                                             bool fold,
                                                     int64_t capacity, const int16_t* __restrict__ ids,
                                                     uint32_t* __restrict__ done, uint32_t* __restrict__ flags,
                                                     int32_t* __restrict__ tilebase, int32_t* __restrict__ rank,
@@ -280,6 +287,11 @@ __global__ __launch_bounds__(PERM_THREADS) void k_count_scan(int T, int K, int E
     __syncthreads();
   }
   if (wave_ballot(bad) && l == 0) set_err(err, MOE_DEVERR_BAD_ID);
+  if (fold) {  // few tiles and experts: the permute kernel combines the tiles' counts itself
+    __syncthreads();
+    for (int e = threadIdx.x; e < L; e += PERM_THREADS) tilebase[(long)tile * L + e] = run[e];
+    return;
+  }
   if (ntiles == 1) {  // the whole batch in one tile: its counts are the totals
     __syncthreads();
     for (int e = threadIdx.x; e < L; e += PERM_THREADS) tilebase[e] = 0;
@@ -386,39 +398,93 @@ __global__ __launch_bounds__(PERM_THREADS) void k_count_scan(int T, int K, int E
 // ---------------------------------------------------------------------------
 // k_permute: 4 tokens per workgroup, one wavefront each.
 // ---------------------------------------------------------------------------
+// PERM_FOLD_WORDS: with ntiles * L at most this (and L <= 64), the count
+// kernel leaves each tile's counts in the tile-base array and every permute
+// workgroup turns them into the bases and offsets itself (in LDS, while its
+// rows load), so the count kernel needs no scan.
+#define PERM_FOLD_WORDS 256
 template <int OUT>  // OUT 0: copy rows (bf16 or fp32, row_bytes), 1: MXFP8-, 2: MXFP4-quantize bf16 rows
-__global__ __launch_bounds__(256) void k_permute(int T, int K, int e0, int L, int TT, int64_t capacity, int row_bytes,
-                                                 const uint8_t* __restrict__ x, const int16_t* __restrict__ ids,
+__global__ __launch_bounds__(256) void k_permute(int T, int K, int e0, int L, int TT, int ntiles, bool fold,
+                                                 int64_t capacity, int row_bytes, const uint8_t* __restrict__ x,
+                                                 const int16_t* __restrict__ ids,
                                                  const int32_t* __restrict__ tilebase,
-                                                 const int32_t* __restrict__ rank,
-                                                 const int32_t* __restrict__ offsets, uint8_t* __restrict__ x_perm,
+                                                 const int32_t* __restrict__ rank, int32_t* __restrict__ counts,
+                                                 int32_t* __restrict__ offsets, uint8_t* __restrict__ x_perm,
                                                  uint8_t* __restrict__ x_scales, int32_t* __restrict__ row_to_slot,
-                                                 int32_t* __restrict__ slot_to_row) {
+                                                 int32_t* __restrict__ slot_to_row, int32_t* err) {
+  __shared__ int32_t s_tb[PERM_FOLD_WORDS];  // fold: tile counts, then their exclusive prefix over the tiles
+  __shared__ int32_t s_off[64];              // fold: expert offsets
   const int l = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= T) return;
+  const bool active = t < T;
+  const int nw = ntiles * L;
+  const long f = (long)t * K + l;
+  int le = -1;
+  if (active && l < K) {
+    const int id = ids[f];
+    if (id >= e0 && id < e0 + L) le = id - e0;
+  }
+  const int cw = (fold && (int)threadIdx.x < nw) ? tilebase[threadIdx.x] : 0;
+  const long tl = (long)(t / TT) * L + le;
+  // the slot's row within its tile and expert (and, without fold, its
+  // expert's offset + its tile's base), issued before the row loads
+  int64_t base = 0;
+  if (le >= 0) base = (int64_t)rank[f] + (fold ? 0 : (int64_t)offsets[le] + tilebase[tl]);
+  const uint64_t local = wave_ballot(le >= 0);
+  // the row's first 8 KiB in flight while the bases are formed
+  const uint8_t* src = x + (long)t * row_bytes;
+  const int npiece = (row_bytes + 1023) / 1024;
+  u32x4 v[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int off = j * 1024 + l * 16;
+    v[j] = (local && j < npiece && off < row_bytes) ? *(const u32x4*)(src + off) : u32x4{0, 0, 0, 0};
+  }
+  if (fold) {
+    if ((int)threadIdx.x < nw) s_tb[threadIdx.x] = cw;
+    __syncthreads();
+    if (threadIdx.x < 64) {  // wavefront 0, lane e: expert e's prefix over the tiles, then the offsets
+      int tot = 0;
+      if (l < L)
+        for (int p = 0; p < ntiles; ++p) {
+          const int c = s_tb[p * L + l];
+          s_tb[p * L + l] = tot;
+          tot += c;
+        }
+      const int incl = wave_incl_scan(tot);
+      s_off[l] = incl - tot;
+      if (blockIdx.x == 0) {
+        if (l < L) {
+          counts[l] = tot;
+          offsets[l] = incl - tot;
+        }
+        if (l == 63) {
+          offsets[L] = incl;
+          if ((int64_t)incl > capacity) set_err(err, MOE_DEVERR_OVERFLOW);
+        }
+      }
+    }
+    __syncthreads();
+  }
+  if (!active) return;
   int dest = -1;
   if (l < K) {
-    const long f = (long)t * K + l;
-    const int id = ids[f];
-    if (id >= e0 && id < e0 + L) {
-      const int le = id - e0;
-      const int64_t d = (int64_t)offsets[le] + tilebase[(long)(t / TT) * L + le] + rank[f];
+    if (le >= 0) {
+      const int64_t d = fold ? base + s_off[le] + s_tb[tl] : base;
       dest = (d >= 0 && d < capacity) ? (int)d : -1;
     }
     slot_to_row[f] = dest;
   }
   const uint64_t bits = wave_ballot(dest >= 0);
   if (!bits) return;
-  const uint8_t* src = x + (long)t * row_bytes;
-  const int npiece = (row_bytes + 1023) / 1024;
   // rows move in 1 KiB pieces (16 bytes per lane), eight pieces in flight
   for (int p0 = 0; p0 < npiece; p0 += 8) {
-    u32x4 v[8];
+    if (p0 > 0) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int off = (p0 + j) * 1024 + l * 16;
-      v[j] = (p0 + j < npiece && off < row_bytes) ? *(const u32x4*)(src + off) : u32x4{0, 0, 0, 0};
+      for (int j = 0; j < 8; ++j) {
+        const int off = (p0 + j) * 1024 + l * 16;
+        v[j] = (p0 + j < npiece && off < row_bytes) ? *(const u32x4*)(src + off) : u32x4{0, 0, 0, 0};
+      }
     }
     if (OUT == 0) {
       uint64_t b = bits;
@@ -513,7 +579,7 @@ hipError_t launch_permute(int T, int H, int K, int E_global, int e0, int L, int6
   const int TT = permute_tile_tokens(T, K, L);
   const int ntiles = (T + TT - 1) / TT;
   const PermuteWs w = permute_ws(ws, ntiles, L);
-  // at most (PERM_WAVES + 1) * MOE_MAX_L * 4 + 16 KiB = 88 KiB
+  // at most (PERM_WAVES + 1) * MOE_MAX_L * 4 + 32 KiB = 104 KiB
   const size_t lds = (size_t)((PERM_WAVES + 1) * L) * sizeof(int32_t) + PERM_CHUNK * sizeof(int16_t);
   static const bool attr_done = [] {
     (void)hipFuncSetAttribute((const void*)k_count_scan, hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -521,13 +587,15 @@ hipError_t launch_permute(int T, int H, int K, int E_global, int e0, int L, int6
     return true;
   }();
   (void)attr_done;
-  hipLaunchKernelGGL(k_count_scan, dim3(ntiles), dim3(PERM_THREADS), lds, s, T, K, E_global, e0, L, TT, ntiles, capacity, ids,
+  const bool fold = (long)ntiles * L <= PERM_FOLD_WORDS && L <= 64;
+  hipLaunchKernelGGL(k_count_scan, dim3(ntiles), dim3(PERM_THREADS), lds, s, T, K, E_global, e0, L, TT, ntiles, fold,
+                     capacity, ids,
                      w.done, w.flags, w.tilebase, w.rank, counts, offsets, err);
   const int row_bytes = H * (x_dtype == MOE_F32 ? 4 : 2);
   const dim3 g((T + 3) / 4), b(256);
 #define PERMUTE_ARGS                                                                                          \
-  T, K, e0, L, TT, capacity, row_bytes, (const uint8_t*)x, ids, (const int32_t*)w.tilebase,                 \
-      (const int32_t*)w.rank, (const int32_t*)offsets, (uint8_t*)x_perm, x_scales, row_to_slot, slot_to_row
+  T, K, e0, L, TT, ntiles, fold, capacity, row_bytes, (const uint8_t*)x, ids, (const int32_t*)w.tilebase,     \
+      (const int32_t*)w.rank, counts, offsets, (uint8_t*)x_perm, x_scales, row_to_slot, slot_to_row, err
   if (out_dtype == MOE_MXFP8)
     hipLaunchKernelGGL(k_permute<1>, g, b, 0, s, PERMUTE_ARGS);
   else if (out_dtype == MOE_MXFP4)

@@ -213,7 +213,7 @@ def test_permute_workspace_not_zero_filled_is_reported():
     normally (none waits, none scans).  After zero-filling the workspace
     again the next call is exact."""
     rng = np.random.default_rng(14)
-    T, K, E, H = 900, 4, 32, 64
+    T, K, E, H = 3000, 8, 256, 64  # 256 local experts: the tiles' counts are scanned by the last tile
     ids = _rand_ids(rng, T, K, E)
     x64 = O.bf16_round(rng.standard_normal((T, H)))
     ws = torch.full((D.moe_permute_workspace_bytes(T, K, E),), 0xEE, dtype=torch.uint8, device=DEV)
