@@ -98,6 +98,8 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ SplitPlan gb_split_plan(int total, int G, int Kd) {
   return split_plan(total, G, Kd / 64);
 }
+// whether a bf16 GEMM over Kd may split a tile (else its reduce has no work)
+static inline bool gb_may_split(int Kd) { return split_max_pieces(Kd / 64) >= 2; }
 
 // Tile schedule and split plan of the bf16 kernel on a grid of G workgroups,
 // with tall tiles: a remainder of up to GB_TALL rows joins the expert's last
@@ -168,6 +170,79 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[NI][2], int i0, c
         if (jcol < (N >> 1))
           out[((long)(jcol >> 5) * capacity + grow) * GB_BK + (jcol & 31)] =
               (bf16_t)f32_to_bf16(silu_mul(acc[ii][0][v], acc[ii][1][v]));
+      }
+    }
+  }
+}
+
+// fp32 -> bf16 bits with the conversion instruction (round to nearest even)
+__device__ __forceinline__ bf16_t bf16_rne(float f) { return __builtin_bit_cast(bf16_t, (__bf16)f); }
+// silu(g) * u with the reciprocal instruction (about 1 ulp), for the bf16
+// activations (well inside their rounding)
+__device__ __forceinline__ float silu_mul_fast(float g, float u) {
+  return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
+}
+
+// Epilogue of a whole tile's 256 rows (EPI 0 and 1) through LDS: each
+// wavefront turns its 128 x 64 part, 32 rows at a time, from the MFMA layout
+// (a lane holds one column) into rows in its own 4 KiB of LDS (ring stage 3,
+// free between the k loops: the next unit's prologue fills stages 0-2), and
+// stores whole 16-byte pieces of rows: EPI 0 writes 128 contiguous bytes of
+// each output row, EPI 1 one contiguous 2 KiB block of the k-blocked
+// activations per 32 rows (instead of one 2-byte store per value).  The 32
+// rows of a lane group g = 1 sit 4 rows below those of g = 0, so their half
+// of each LDS row is swapped to keep the two groups on distinct banks.
+template <int EPI>
+__device__ __forceinline__ void store_tile_lds(const f32x16 (&acc)[4][2], const TileInfo& ti, int N,
+                                               int64_t capacity, int wm, int wn, int g, int r32, int l,
+                                               uint8_t* ep, bf16_t* __restrict__ out) {
+  const int col0 = ti.nt * GB_BN;
+  // lane-dependent offsets made opaque (as in store_tile): recomputed here
+  // rather than hoisted out of the persistent loop and spilled
+  asm volatile("" : "+v"(g), "+v"(r32), "+v"(l));
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int rb = wm * 128 + i * 32;  // the chunk's first row in the tile
+    if (rb >= ti.rows) continue;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    if (EPI == 0) {  // [32 rows][64 columns] bf16, 128-byte rows
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int r = 8 * (v >> 2) + 4 * g + (v & 3);
+          *(bf16_t*)(ep + r * 128 + (((j * 32 + r32) * 2) ^ (g << 6))) = bf16_rne(acc[i][j][v]);
+        }
+    } else {  // [32 rows][32 activations] bf16, 64-byte rows
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int r = 8 * (v >> 2) + 4 * g + (v & 3);
+        *(bf16_t*)(ep + r * 64 + ((r32 * 2) ^ (g << 5))) = bf16_rne(silu_mul_fast(acc[i][0][v], acc[i][1][v]));
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    if (EPI == 0) {  // 256 pieces of 16 bytes: row q / 8, piece q % 8
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int q = k * 64 + l, r = q >> 3, c = q & 7;
+        const u32x4 val = *(const u32x4*)(ep + r * 128 + ((c ^ (((r >> 2) & 1) << 2)) << 4));
+        const int row = rb + r, col = col0 + wn * 64 + c * 8;
+        if (row < ti.rows && col < N) *(u32x4*)(out + (ti.row0 + row) * (long)N + col) = val;
+      }
+    } else {  // 128 pieces of 16 bytes: row q / 4, piece q % 4
+      const int jcol = (col0 >> 1) + wn * 32;  // the wavefront's 32 activations: one k block
+      if (jcol < (N >> 1)) {
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+          const int q = k * 64 + l, r = q >> 2, c = q & 3;
+          const u32x4 val = *(const u32x4*)(ep + r * 64 + ((c ^ (((r >> 2) & 1) << 1)) << 4));
+          const int row = rb + r;
+          if (row < ti.rows) *(u32x4*)(out + ((long)(jcol >> 5) * capacity + ti.row0 + row) * GB_BK + c * 8) = val;
+        }
       }
     }
   }
@@ -458,7 +533,10 @@ __global__ __launch_bounds__(GB_THREADS, 1) void k_gemm_bf16(int L, int N, int K
           }
         }
     } else if (done.piece < 0) {
-      store_tile<EPI, 4>(acc, 0, done.ti, N, capacity, wm, wn, g, r32, out, aux);
+      if constexpr (EPI == 0 || EPI == 1)
+        store_tile_lds<EPI>(acc, done.ti, N, capacity, wm, wn, g, r32, l, smem + 3 * GB_STAGE_BYTES + wv * 4096, out);
+      else
+        store_tile<EPI, 4>(acc, 0, done.ti, N, capacity, wm, wn, g, r32, out, aux);
       if (done.ti.rows > GB_BM && wm == 0)
         store_tile<EPI, 1>(accx, 8, done.ti, N, capacity, 0, wn, g, r32, out, aux);
     } else {
@@ -676,9 +754,11 @@ hipError_t launch_grouped_mlp_bf16(int L, int H, int F, int64_t capacity, const 
   const int G2 = grid_for(capacity, L, GB_BM, (N2 + GB_BN - 1) / GB_BN, 1);
   const dim3 rgrid(GEMM_SPLIT_UNITS / 2 * 8), rblk(320), blk(GB_THREADS);
   hipLaunchKernelGGL(k_gemm_bf16<1>, dim3(G1), blk, lds, s, L, N1, H, capacity, x, offsets, w1p, act, part, (const bf16_t*)nullptr);
-  hipLaunchKernelGGL(k_splitk_reduce<1>, rgrid, rblk, 0, s, L, N1, H, capacity, G1, offsets, part, act, (const bf16_t*)nullptr);
+  if (gb_may_split(H))
+    hipLaunchKernelGGL(k_splitk_reduce<1>, rgrid, rblk, 0, s, L, N1, H, capacity, G1, offsets, part, act, (const bf16_t*)nullptr);
   hipLaunchKernelGGL(k_gemm_bf16<0>, dim3(G2), blk, lds, s, L, N2, F, capacity, act, offsets, w2p, y, part, (const bf16_t*)nullptr);
-  hipLaunchKernelGGL(k_splitk_reduce<0>, rgrid, rblk, 0, s, L, N2, F, capacity, G2, offsets, part, y, (const bf16_t*)nullptr);
+  if (gb_may_split(F))
+    hipLaunchKernelGGL(k_splitk_reduce<0>, rgrid, rblk, 0, s, L, N2, F, capacity, G2, offsets, part, y, (const bf16_t*)nullptr);
   return hipGetLastError();
 }
 
@@ -707,14 +787,17 @@ hipError_t launch_grouped_mlp_bf16_backward(int L, int H, int F, int64_t capacit
   const int G0 = grid_for(capacity, L, GB_BM, (H + GB_BN - 1) / GB_BN, 1);
   const dim3 rgrid(GEMM_SPLIT_UNITS / 2 * 8), rblk(320), blk(GB_THREADS);
   hipLaunchKernelGGL(k_gemm_bf16<3>, dim3(G3), blk, lds, s, L, 2 * F, H, capacity, x, offsets, w1p, hbuf, part, nul);
-  hipLaunchKernelGGL(k_splitk_reduce<3>, rgrid, rblk, 0, s, L, 2 * F, H, capacity, G3, offsets, part, hbuf, nul);
+  if (gb_may_split(H))
+    hipLaunchKernelGGL(k_splitk_reduce<3>, rgrid, rblk, 0, s, L, 2 * F, H, capacity, G3, offsets, part, hbuf, nul);
   hipLaunchKernelGGL(k_gemm_bf16<4>, dim3(G4), blk, lds, s, L, F, H, capacity, dy, offsets, w2t, dhbuf, part,
                      (const bf16_t*)hbuf);
-  hipLaunchKernelGGL(k_splitk_reduce<4>, rgrid, rblk, 0, s, L, F, H, capacity, G4, offsets, part, dhbuf,
-                     (const bf16_t*)hbuf);
+  if (gb_may_split(H))
+    hipLaunchKernelGGL(k_splitk_reduce<4>, rgrid, rblk, 0, s, L, F, H, capacity, G4, offsets, part, dhbuf,
+                       (const bf16_t*)hbuf);
   hipLaunchKernelGGL(k_gemm_bf16<0>, dim3(G0), blk, lds, s, L, H, 2 * F, capacity, dhbuf, offsets, w1t, dx, part,
                      nul);
-  hipLaunchKernelGGL(k_splitk_reduce<0>, rgrid, rblk, 0, s, L, H, 2 * F, capacity, G0, offsets, part, dx, nul);
+  if (gb_may_split(2 * F))
+    hipLaunchKernelGGL(k_splitk_reduce<0>, rgrid, rblk, 0, s, L, H, 2 * F, capacity, G0, offsets, part, dx, nul);
   return hipGetLastError();
 }
 

@@ -141,14 +141,17 @@ struct SplitPlan {
   int units;  // dp + (total - dp) * S
 };
 
+// The most pieces a split tile of KT pairs of k steps may have: pieces of at
+// least 8 groups of 4 k steps (shorter pieces cost more in partial-tile
+// traffic and the reduce than they save), at most 16.  Below 2, no tile of
+// that depth is ever split, and the host skips the reduce kernel.
+__host__ __device__ inline int split_max_pieces(int KT) { return KT / 16 < 16 ? KT / 16 : 16; }
+
 __device__ __forceinline__ SplitPlan split_plan(int total, int G, int KT) {
   SplitPlan p;
   const int left = total % G;
   p.dp = total - left;
-  // pieces of at least 8 groups of 4 k steps: shorter pieces cost more in
-  // partial-tile traffic and the reduce than they save
-  int S = left > 0 ? min(min(G, GEMM_SPLIT_UNITS) / left, KT / 16) : 1;
-  S = min(S, 16);
+  int S = left > 0 ? min(min(G, GEMM_SPLIT_UNITS) / left, split_max_pieces(KT)) : 1;
   if (S < 2) {
     p.dp = total;
     S = 1;

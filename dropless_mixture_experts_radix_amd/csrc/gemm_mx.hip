@@ -68,6 +68,8 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ SplitPlan gm_split_plan(int total, int G, int KT) {
   return split_plan(total, G, KT / 2);
 }
+// whether an MX GEMM over Kd elements may split a tile (else its reduce has no work)
+static inline bool gm_may_split(int Kd, bool fp4) { return split_max_pieces((fp4 ? Kd / 2 : Kd) / GM_BK / 2) >= 2; }
 
 // Largest value over the 32 lanes of a half wavefront (lanes 32g .. 32g+31):
 // DPP within each row of 16 lanes (quad swaps 1 and 2, then the half-row and
@@ -703,12 +705,14 @@ static void launch_mx(int L, int H, int F, int64_t capacity, const uint8_t* x, c
   const dim3 rgrid(GEMM_SPLIT_UNITS / 2 * 8), rblk(320), blk(GM_THREADS);
   hipLaunchKernelGGL((k_gemm_mx<1, FP4, TALL>), dim3(G1), blk, lds, s, L, 2 * F, H, capacity, x, xs, offsets, w1p,
                      w1s, act, act_s, part, nullptr, act_bf16);
-  hipLaunchKernelGGL((k_mx_splitk_reduce<1, FP4, TALL>), rgrid, rblk, 0, s, L, 2 * F, H, capacity, G1, offsets,
-                     part, act, act_s, (const bf16_t*)nullptr, act_bf16);
+  if (gm_may_split(H, FP4))
+    hipLaunchKernelGGL((k_mx_splitk_reduce<1, FP4, TALL>), rgrid, rblk, 0, s, L, 2 * F, H, capacity, G1, offsets,
+                       part, act, act_s, (const bf16_t*)nullptr, act_bf16);
   hipLaunchKernelGGL((k_gemm_mx<0, FP4, TALL>), dim3(G2), blk, lds, s, L, H, F, capacity, act, act_s, offsets,
                      w2p, w2s, (uint8_t*)y, (uint8_t*)nullptr, part, nullptr, (bf16_t*)nullptr);
-  hipLaunchKernelGGL((k_mx_splitk_reduce<0, FP4, TALL>), rgrid, rblk, 0, s, L, H, F, capacity, G2, offsets, part,
-                     (uint8_t*)y, (uint8_t*)nullptr, (const bf16_t*)nullptr, (bf16_t*)nullptr);
+  if (gm_may_split(F, FP4))
+    hipLaunchKernelGGL((k_mx_splitk_reduce<0, FP4, TALL>), rgrid, rblk, 0, s, L, H, F, capacity, G2, offsets, part,
+                       (uint8_t*)y, (uint8_t*)nullptr, (const bf16_t*)nullptr, (bf16_t*)nullptr);
 }
 
 hipError_t launch_grouped_mlp_mx(int L, int H, int F, int64_t capacity, bool fp4, const uint8_t* x,
@@ -822,18 +826,21 @@ static void launch_mx_backward(int L, int H, int F, int64_t capacity, const uint
   const dim3 rgrid(GEMM_SPLIT_UNITS / 2 * 8), rblk(320), blk(GM_THREADS);
   hipLaunchKernelGGL((k_gemm_mx<3, false, TALL>), dim3(G1), blk, lds, s, L, 2 * F, H, capacity, xq, xqs, offsets,
                      w1p, w1s, (uint8_t*)hbuf, (uint8_t*)nullptr, part, nullptr, (bf16_t*)nullptr);
-  hipLaunchKernelGGL((k_mx_splitk_reduce<3, false, TALL>), rgrid, rblk, 0, s, L, 2 * F, H, capacity, G1, offsets,
-                     part, (uint8_t*)hbuf, (uint8_t*)nullptr, (const bf16_t*)nullptr, (bf16_t*)nullptr);
+  if (gm_may_split(H, false))
+    hipLaunchKernelGGL((k_mx_splitk_reduce<3, false, TALL>), rgrid, rblk, 0, s, L, 2 * F, H, capacity, G1, offsets,
+                       part, (uint8_t*)hbuf, (uint8_t*)nullptr, (const bf16_t*)nullptr, (bf16_t*)nullptr);
   hipLaunchKernelGGL((k_gemm_mx<6, false, TALL>), dim3(G2), blk, lds, s, L, F, H, capacity, dyq, dyqs, offsets,
                      w2t, w2ts, (uint8_t*)da, (uint8_t*)nullptr, part, nullptr, (bf16_t*)nullptr);
-  hipLaunchKernelGGL((k_mx_splitk_reduce<6, false, TALL>), rgrid, rblk, 0, s, L, F, H, capacity, G2, offsets, part,
-                     (uint8_t*)da, (uint8_t*)nullptr, (const bf16_t*)nullptr, (bf16_t*)nullptr);
+  if (gm_may_split(H, false))
+    hipLaunchKernelGGL((k_mx_splitk_reduce<6, false, TALL>), rgrid, rblk, 0, s, L, F, H, capacity, G2, offsets, part,
+                       (uint8_t*)da, (uint8_t*)nullptr, (const bf16_t*)nullptr, (bf16_t*)nullptr);
   hipLaunchKernelGGL(k_swiglu_bwd_mx, dim3(num_cus() * 16), dim3(256), 0, s, F, capacity, offsets + L, da, hbuf,
                      dhbuf, dhq, dhqs);
   hipLaunchKernelGGL((k_gemm_mx<0, false, TALL>), dim3(G3), blk, lds, s, L, H, 2 * F, capacity, dhq, dhqs, offsets,
                      w1t, w1ts, (uint8_t*)dx, (uint8_t*)nullptr, part, nullptr, (bf16_t*)nullptr);
-  hipLaunchKernelGGL((k_mx_splitk_reduce<0, false, TALL>), rgrid, rblk, 0, s, L, H, 2 * F, capacity, G3, offsets,
-                     part, (uint8_t*)dx, (uint8_t*)nullptr, (const bf16_t*)nullptr, (bf16_t*)nullptr);
+  if (gm_may_split(2 * F, false))
+    hipLaunchKernelGGL((k_mx_splitk_reduce<0, false, TALL>), rgrid, rblk, 0, s, L, H, 2 * F, capacity, G3, offsets,
+                       part, (uint8_t*)dx, (uint8_t*)nullptr, (const bf16_t*)nullptr, (bf16_t*)nullptr);
 }
 
 hipError_t launch_grouped_mlp_mx_backward(int L, int H, int F, int64_t capacity, const bf16_t* x,
