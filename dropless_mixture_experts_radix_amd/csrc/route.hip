@@ -278,17 +278,25 @@ __global__ __launch_bounds__(64) void k_route_select_small(int T, int E, int K, 
   float z[EMAX];
 #pragma unroll
   for (int e = 0; e < EMAX; ++e) z[e] = 0.f;
-  // the S partial sets in order; a token's E logits of one set are contiguous
+  // the S partial sets in order, four sets' loads in flight at a time; a
+  // token's E logits of one set are contiguous
   if ((E & 3) == 0) {
-    for (int s = 0; s < S; ++s) {
-      const float4* ps = (const float4*)(partial + ((long)s * T + t) * E);
+    for (int s0 = 0; s0 < S; s0 += 4) {
+      float4 q[4][EMAX / 4];
 #pragma unroll
-      for (int c = 0; c < EMAX / 4; ++c) {
-        if (4 * c < E) {
-          const float4 q = ps[c];
-          z[4 * c] += q.x; z[4 * c + 1] += q.y; z[4 * c + 2] += q.z; z[4 * c + 3] += q.w;
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int c = 0; c < EMAX / 4; ++c)
+          q[j][c] = (s0 + j < S && 4 * c < E) ? ((const float4*)(partial + ((long)(s0 + j) * T + t) * E))[c]
+                                              : float4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int c = 0; c < EMAX / 4; ++c) {
+          if (s0 + j < S && 4 * c < E) {
+            z[4 * c] += q[j][c].x; z[4 * c + 1] += q[j][c].y; z[4 * c + 2] += q[j][c].z; z[4 * c + 3] += q[j][c].w;
+          }
         }
-      }
     }
   } else {
     for (int s = 0; s < S; ++s) {
@@ -308,7 +316,7 @@ __global__ __launch_bounds__(64) void k_route_select_small(int T, int E, int K, 
 // and one thread per token selects.  No partial logits go through HBM.  With
 // the 16-row instruction four lanes share a token row, so one 16-byte-per-lane
 // load covers 64 contiguous bytes of each of 16 rows.  The prepared rows past
-// P*E are zero and are not read.
+// the last term row in use ((P-1)*ept + E) are zero and are not read.
 #define RF_WAVES 16
 template <int EMAX>
 __global__ __launch_bounds__(64 * RF_WAVES) void k_route_fused_small(int T, int E, int K, int H, int P, int score,
@@ -322,7 +330,7 @@ __global__ __launch_bounds__(64 * RF_WAVES) void k_route_fused_small(int T, int 
   const int w = threadIdx.x >> 6, l = threadIdx.x & 63, q = l >> 4, r = l & 15;
   const int t0 = blockIdx.x * 16;
   const int ra = min(t0 + r, T - 1);
-  const int PE = P * E;  // prepared rows in use
+  const int PE = (P - 1) * router_ept(P) + E;  // prepared rows in use: term p of expert e is row p * ept + e
   // 32-wide k slices of this wavefront: [k0s, k1s)
   const int nks = H / 32, per = (nks + RF_WAVES - 1) / RF_WAVES;
   const int k0s = min(w * per, nks), k1s = min(k0s + per, nks);

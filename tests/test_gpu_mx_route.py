@@ -120,6 +120,24 @@ def test_route_small_router_from_x(E, K, H, wdt, T):
     _check_route(ids, probs, lo, T, K, "softmax", bias.numpy(), mask.numpy())
 
 
+@pytest.mark.parametrize("E", [4, 8, 10])
+def test_route_small_router_uses_every_weight_term(E):
+    """fp32 router weights reach the matrix cores as three bf16 terms
+    (hi + mid + lo; term p of expert e is prepared row p * 10 + e).  With all
+    of them summed, the projection is fp32-accurate: within 2e-6 of the
+    float64 definition, where dropping the lo terms of some experts costs
+    about 1e-5 (2^-17 of a weight)."""
+    g = torch.Generator().manual_seed(77 + E)
+    T, H, K = 64, 4096, 2
+    x = torch.randn((T, H), generator=g).to(torch.bfloat16)
+    w = torch.randn((H, E), generator=g) * 0.05
+    say("route small router weight terms", E)
+    ids, probs, lo, err = _route_gpu(T, E, K, D.SOFTMAX, x=x.to(DEV), w_router=w.to(DEV))
+    assert err == 0
+    want = O.router_logits(to_numpy_f64(x), to_numpy_f64(w))
+    assert rel_inf(lo, want) <= 2e-6
+
+
 @pytest.mark.parametrize("E,K,H,T", [(160, 6, 640, 1000), (300, 8, 1152, 777), (256, 8, 128, 100),
                                      (4096, 64, 256, 300)])
 def test_route_gemm_projection(E, K, H, T):
