@@ -10,14 +10,19 @@ namespace moe {
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 // One wavefront per token, 4 per workgroup.  Each lane owns 16 bytes of every
-// 1 KiB piece of the row; up to 8 pieces are accumulated at once.  With probs
-// NULL every weight is 1: the backward of the permute (a token's gradient is
-// the sum of its routed rows' gradients, k order).
-template <bool BF16>
+// 1 KiB piece of the row.  The token's rows are gathered RB = 8 / PCS at a
+// time, PCS pieces of each (all RB x PCS loads in flight together), and added
+// in k order; rows of more than 8 pieces go in chunks of 8 pieces, one row at
+// a time.  Short rows (a 512-wide bf16 row is one piece) so wait for one
+// memory round trip per 8 rows instead of one per row.  With probs NULL every
+// weight is 1: the backward of the permute (a token's gradient is the sum of
+// its routed rows' gradients, k order).
+template <bool BF16, int PCS>
 __global__ __launch_bounds__(256) void k_combine(int T, int K, int H, const uint8_t* __restrict__ y,
                                                  const int32_t* __restrict__ s2r,
                                                  const float* __restrict__ probs, uint8_t* __restrict__ out) {
   constexpr int EPL = BF16 ? 8 : 4;  // elements per lane per piece
+  constexpr int RB = 8 / PCS;        // rows per batch
   const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + w;
   if (t >= T) return;
@@ -31,41 +36,54 @@ __global__ __launch_bounds__(256) void k_combine(int T, int K, int H, const uint
   const int row_bytes = H * (BF16 ? 2 : 4);
   const int npiece = (row_bytes + 1023) / 1024;
   uint8_t* dst = out + (long)t * row_bytes;
-  for (int p0 = 0; p0 < npiece; p0 += 8) {
-    float acc[8][EPL];
+  for (int p0 = 0; p0 < npiece; p0 += PCS) {
+    float acc[PCS][EPL];
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
+    for (int j = 0; j < PCS; ++j)
 #pragma unroll
       for (int i = 0; i < EPL; ++i) acc[j][i] = 0.f;
     uint64_t b = bits;
-    while (b) {  // k order
-      const int k = __builtin_ctzll(b);
-      b &= b - 1;
-      const int d = readlane_i(r, k);
-      const float pk = readlane_f(p, k);
-      const uint8_t* src = y + (long)d * row_bytes;
-      u32x4 v[8];
+    while (b) {  // batches of RB rows, k order
+      int d[RB];
+      float pk[RB];
+      bool ok[RB];  // wave-uniform
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int off = (p0 + j) * 1024 + l * 16;
-        v[j] = (p0 + j < npiece && off < row_bytes) ? *(const u32x4*)(src + off) : u32x4{0, 0, 0, 0};
+      for (int i = 0; i < RB; ++i) {
+        ok[i] = b != 0;
+        const int k = ok[i] ? __builtin_ctzll(b) : 0;
+        b &= b - 1;
+        d[i] = readlane_i(r, k);
+        pk[i] = readlane_f(p, k);
       }
+      u32x4 v[RB][PCS];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        if (BF16) {
+      for (int i = 0; i < RB; ++i)
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            acc[j][2 * q] = fmaf(pk, bf16_to_f32(v[j][q] & 0xffffu), acc[j][2 * q]);
-            acc[j][2 * q + 1] = fmaf(pk, bf16_to_f32(v[j][q] >> 16), acc[j][2 * q + 1]);
+        for (int j = 0; j < PCS; ++j) {
+          const int off = (p0 + j) * 1024 + l * 16;
+          v[i][j] = (ok[i] && p0 + j < npiece && off < row_bytes) ? *(const u32x4*)(y + (long)d[i] * row_bytes + off)
+                                                                  : u32x4{0, 0, 0, 0};
+        }
+#pragma unroll
+      for (int i = 0; i < RB; ++i) {
+        if (!ok[i]) continue;
+#pragma unroll
+        for (int j = 0; j < PCS; ++j) {
+          if (BF16) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              acc[j][2 * q] = fmaf(pk[i], bf16_to_f32(v[i][j][q] & 0xffffu), acc[j][2 * q]);
+              acc[j][2 * q + 1] = fmaf(pk[i], bf16_to_f32(v[i][j][q] >> 16), acc[j][2 * q + 1]);
+            }
+          } else {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) acc[j][q] = fmaf(pk[i], __uint_as_float(v[i][j][q]), acc[j][q]);
           }
-        } else {
-#pragma unroll
-          for (int q = 0; q < 4; ++q) acc[j][q] = fmaf(pk, __uint_as_float(v[j][q]), acc[j][q]);
         }
       }
     }
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
+    for (int j = 0; j < PCS; ++j) {
       const int off = (p0 + j) * 1024 + l * 16;
       if (p0 + j < npiece && off < row_bytes) {
         u32x4 o;
@@ -250,10 +268,21 @@ hipError_t launch_combine(int T, int K, int H, int dtype, const void* y, const i
                           const float* probs, void* out, hipStream_t s) {
   if (T == 0) return hipSuccess;
   const dim3 g((T + 3) / 4), b(256);
-  if (dtype == MOE_F32)
-    hipLaunchKernelGGL(k_combine<false>, g, b, 0, s, T, K, H, (const uint8_t*)y, s2r, probs, (uint8_t*)out);
-  else
-    hipLaunchKernelGGL(k_combine<true>, g, b, 0, s, T, K, H, (const uint8_t*)y, s2r, probs, (uint8_t*)out);
+  const int npiece = (int)(((long)H * (dtype == MOE_F32 ? 4 : 2) + 1023) / 1024);
+#define MOE_COMBINE(BF, PCS)                                                                             \
+  hipLaunchKernelGGL((k_combine<BF, PCS>), g, b, 0, s, T, K, H, (const uint8_t*)y, s2r, probs, (uint8_t*)out)
+  if (dtype == MOE_F32) {
+    if (npiece == 1) MOE_COMBINE(false, 1);
+    else if (npiece == 2) MOE_COMBINE(false, 2);
+    else if (npiece <= 4) MOE_COMBINE(false, 4);
+    else MOE_COMBINE(false, 8);
+  } else {
+    if (npiece == 1) MOE_COMBINE(true, 1);
+    else if (npiece == 2) MOE_COMBINE(true, 2);
+    else if (npiece <= 4) MOE_COMBINE(true, 4);
+    else MOE_COMBINE(true, 8);
+  }
+#undef MOE_COMBINE
   return hipGetLastError();
 }
 

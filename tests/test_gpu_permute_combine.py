@@ -246,8 +246,10 @@ def _combine_gpu(y, s2r, p):
     return to_f64(out)
 
 
+# rows of 1, 2, 3-4 and more than 4 KiB pieces: 8, 4, 2 and 1 rows gathered at a time
 @pytest.mark.parametrize("T,K,H,dt", [(500, 2, 4096, "bf16"), (300, 36, 512, "bf16"), (64, 8, 7168, "bf16"),
-                                      (256, 2, 64, "f32"), (100, 64, 136, "bf16"), (77, 3, 1032, "f32")])
+                                      (256, 2, 64, "f32"), (100, 64, 136, "bf16"), (77, 3, 1032, "f32"),
+                                      (200, 6, 1024, "bf16"), (150, 5, 768, "f32"), (120, 9, 2000, "bf16")])
 def test_combine_matches_oracle(T, K, H, dt):
     rng = np.random.default_rng(T * H)
     N = T * K
