@@ -34,13 +34,12 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 // the other keeps the matrix core busy.  A wavefront tile of 128 x 64 reads
 // 12 KiB of MFMA fragments per k step from LDS for its 16 MFMAs.
 //
-// Pipeline of k step kt (stage kt % 4), 2 sub-steps of k = 16:
-//   read the fragments of sub-step 1; MFMAs of sub-step 0 and the first 2 of
-//   sub-step 1; wait until this wavefront's loads of step kt+1 have landed and
-//   its fragment reads are done; barrier (step kt+1 is complete in LDS for
-//   every wavefront, and stage kt % 4 is free); read the fragments of step
-//   kt+1, sub-step 0; load step kt+4 into stage kt % 4, interleaved with the
-//   remaining 6 MFMAs.
+// Pipeline: the wavefronts form two groups (0-3 and 4-7, one of each per
+// SIMD) that alternate between a memory phase (read both sub-steps' fragments
+// of step kt from stage kt % 4, load step kt+3 into stage (kt+3) % 4, wait for
+// this wavefront's loads of step kt+1) and a compute phase (the 16 MFMAs of
+// step kt), one phase apart, with a barrier of all 8 wavefronts between
+// phases; the k loop below spells out which stage is free when.
 //
 // LDS layout: stage s at s * 32 KiB, A rows then B rows (256 each, 64 bytes:
 // 32 k values); a 1 KiB block holds 16 rows and is written by one load
