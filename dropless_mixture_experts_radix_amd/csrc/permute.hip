@@ -395,86 +395,14 @@ __global__ __launch_bounds__(PERM_THREADS) void k_count_scan(int T, int K, int E
   if (threadIdx.x == 0) *done = 0u;
 }
 
-// ---------------------------------------------------------------------------
-// k_permute: 4 tokens per workgroup, one wavefront each.
-// ---------------------------------------------------------------------------
-// PERM_FOLD_WORDS: with ntiles * L at most this (and L <= 64), the count
-// kernel leaves each tile's counts in the tile-base array and every permute
-// workgroup turns them into the bases and offsets itself (in LDS, while its
-// rows load), so the count kernel needs no scan.
-#define PERM_FOLD_WORDS 256
-template <int OUT>  // OUT 0: copy rows (bf16 or fp32, row_bytes), 1: MXFP8-, 2: MXFP4-quantize bf16 rows
-__global__ __launch_bounds__(256) void k_permute(int T, int K, int e0, int L, int TT, int ntiles, bool fold,
-                                                 int64_t capacity, int row_bytes, const uint8_t* __restrict__ x,
-                                                 const int16_t* __restrict__ ids,
-                                                 const int32_t* __restrict__ tilebase,
-                                                 const int32_t* __restrict__ rank, int32_t* __restrict__ counts,
-                                                 int32_t* __restrict__ offsets, uint8_t* __restrict__ x_perm,
-                                                 uint8_t* __restrict__ x_scales, int32_t* __restrict__ row_to_slot,
-                                                 int32_t* __restrict__ slot_to_row, int32_t* err) {
-  __shared__ int32_t s_tb[PERM_FOLD_WORDS];  // fold: tile counts, then their exclusive prefix over the tiles
-  __shared__ int32_t s_off[64];              // fold: expert offsets
-  const int l = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const bool active = t < T;
-  const int nw = ntiles * L;
-  const long f = (long)t * K + l;
-  int le = -1;
-  if (active && l < K) {
-    const int id = ids[f];
-    if (id >= e0 && id < e0 + L) le = id - e0;
-  }
-  const int cw = (fold && (int)threadIdx.x < nw) ? tilebase[threadIdx.x] : 0;
-  const long tl = (long)(t / TT) * L + le;
-  // the slot's row within its tile and expert (and, without fold, its
-  // expert's offset + its tile's base), issued before the row loads
-  int64_t base = 0;
-  if (le >= 0) base = (int64_t)rank[f] + (fold ? 0 : (int64_t)offsets[le] + tilebase[tl]);
-  const uint64_t local = wave_ballot(le >= 0);
-  // the row's first 8 KiB in flight while the bases are formed
-  const uint8_t* src = x + (long)t * row_bytes;
-  const int npiece = (row_bytes + 1023) / 1024;
-  u32x4 v[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int off = j * 1024 + l * 16;
-    v[j] = (local && j < npiece && off < row_bytes) ? *(const u32x4*)(src + off) : u32x4{0, 0, 0, 0};
-  }
-  if (fold) {
-    if ((int)threadIdx.x < nw) s_tb[threadIdx.x] = cw;
-    __syncthreads();
-    if (threadIdx.x < 64) {  // wavefront 0, lane e: expert e's prefix over the tiles, then the offsets
-      int tot = 0;
-      if (l < L)
-        for (int p = 0; p < ntiles; ++p) {
-          const int c = s_tb[p * L + l];
-          s_tb[p * L + l] = tot;
-          tot += c;
-        }
-      const int incl = wave_incl_scan(tot);
-      s_off[l] = incl - tot;
-      if (blockIdx.x == 0) {
-        if (l < L) {
-          counts[l] = tot;
-          offsets[l] = incl - tot;
-        }
-        if (l == 63) {
-          offsets[L] = incl;
-          if ((int64_t)incl > capacity) set_err(err, MOE_DEVERR_OVERFLOW);
-        }
-      }
-    }
-    __syncthreads();
-  }
-  if (!active) return;
-  int dest = -1;
-  if (l < K) {
-    if (le >= 0) {
-      const int64_t d = fold ? base + s_off[le] + s_tb[tl] : base;
-      dest = (d >= 0 && d < capacity) ? (int)d : -1;
-    }
-    slot_to_row[f] = dest;
-  }
+// Copy (OUT 0) or MX-quantize (OUT 1: MXFP8, 2: MXFP4) token t's row to the
+// rows `dest` of its slots (lane k < K: slot k's row, or -1), k order; the
+// first 8 KiB of the row are already in v.  One wavefront.
+template <int OUT>
+__device__ __forceinline__ void permute_rows(int t, int K, int l, int dest, int npiece, int row_bytes,
+                                             const uint8_t* __restrict__ src, u32x4 (&v)[8],
+                                             uint8_t* __restrict__ x_perm, uint8_t* __restrict__ x_scales,
+                                             int32_t* __restrict__ row_to_slot) {
   const uint64_t bits = wave_ballot(dest >= 0);
   if (!bits) return;
   // rows move in 1 KiB pieces (16 bytes per lane), eight pieces in flight
@@ -559,6 +487,212 @@ __global__ __launch_bounds__(256) void k_permute(int T, int K, int e0, int L, in
   }
 }
 
+// ---------------------------------------------------------------------------
+// k_permute: 4 tokens per workgroup, one wavefront each.
+// ---------------------------------------------------------------------------
+// PERM_FOLD_WORDS: with ntiles * L at most this (and L <= 64), the count
+// kernel leaves each tile's counts in the tile-base array and every permute
+// workgroup turns them into the bases and offsets itself (in LDS, while its
+// rows load), so the count kernel needs no scan.
+#define PERM_FOLD_WORDS 256
+template <int OUT>  // OUT 0: copy rows (bf16 or fp32, row_bytes), 1: MXFP8-, 2: MXFP4-quantize bf16 rows
+__global__ __launch_bounds__(256) void k_permute(int T, int K, int e0, int L, int TT, int ntiles, bool fold,
+                                                 int64_t capacity, int row_bytes, const uint8_t* __restrict__ x,
+                                                 const int16_t* __restrict__ ids,
+                                                 const int32_t* __restrict__ tilebase,
+                                                 const int32_t* __restrict__ rank, int32_t* __restrict__ counts,
+                                                 int32_t* __restrict__ offsets, uint8_t* __restrict__ x_perm,
+                                                 uint8_t* __restrict__ x_scales, int32_t* __restrict__ row_to_slot,
+                                                 int32_t* __restrict__ slot_to_row, int32_t* err) {
+  __shared__ int32_t s_tb[PERM_FOLD_WORDS];  // fold: tile counts, then their exclusive prefix over the tiles
+  __shared__ int32_t s_off[64];              // fold: expert offsets
+  const int l = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const bool active = t < T;
+  const int nw = ntiles * L;
+  const long f = (long)t * K + l;
+  int le = -1;
+  if (active && l < K) {
+    const int id = ids[f];
+    if (id >= e0 && id < e0 + L) le = id - e0;
+  }
+  const int cw = (fold && (int)threadIdx.x < nw) ? tilebase[threadIdx.x] : 0;
+  const long tl = (long)(t / TT) * L + le;
+  // the slot's row within its tile and expert (and, without fold, its
+  // expert's offset + its tile's base), issued before the row loads
+  int64_t base = 0;
+  if (le >= 0) base = (int64_t)rank[f] + (fold ? 0 : (int64_t)offsets[le] + tilebase[tl]);
+  const uint64_t local = wave_ballot(le >= 0);
+  // the row's first 8 KiB in flight while the bases are formed
+  const uint8_t* src = x + (long)t * row_bytes;
+  const int npiece = (row_bytes + 1023) / 1024;
+  u32x4 v[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int off = j * 1024 + l * 16;
+    v[j] = (local && j < npiece && off < row_bytes) ? *(const u32x4*)(src + off) : u32x4{0, 0, 0, 0};
+  }
+  if (fold) {
+    if ((int)threadIdx.x < nw) s_tb[threadIdx.x] = cw;
+    __syncthreads();
+    if (threadIdx.x < 64) {  // wavefront 0, lane e: expert e's prefix over the tiles, then the offsets
+      int tot = 0;
+      if (l < L)
+        for (int p = 0; p < ntiles; ++p) {
+          const int c = s_tb[p * L + l];
+          s_tb[p * L + l] = tot;
+          tot += c;
+        }
+      const int incl = wave_incl_scan(tot);
+      s_off[l] = incl - tot;
+      if (blockIdx.x == 0) {
+        if (l < L) {
+          counts[l] = tot;
+          offsets[l] = incl - tot;
+        }
+        if (l == 63) {
+          offsets[L] = incl;
+          if ((int64_t)incl > capacity) set_err(err, MOE_DEVERR_OVERFLOW);
+        }
+      }
+    }
+    __syncthreads();
+  }
+  if (!active) return;
+  int dest = -1;
+  if (l < K) {
+    if (le >= 0) {
+      const int64_t d = fold ? base + s_off[le] + s_tb[tl] : base;
+      dest = (d >= 0 && d < capacity) ? (int)d : -1;
+    }
+    slot_to_row[f] = dest;
+  }
+  permute_rows<OUT>(t, K, l, dest, npiece, row_bytes, src, v, x_perm, x_scales, row_to_slot);
+}
+
+// A workgroup barrier that waits only for this wavefront's LDS operations
+// (__syncthreads also waits for every outstanding global load).
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// ---------------------------------------------------------------------------
+// k_permute_small: batches of at most PERM_SMALL_SLOTS slots and at most 64
+// local experts in one kernel, no workspace.  A workgroup of PSM_TOK
+// wavefronts takes PSM_TOK consecutive tokens (one per wavefront) and, while
+// its rows load, counts every slot of the batch itself (the ids are a few
+// KiB, read from L2 by every workgroup): per local expert, the slots in the
+// whole batch (the counts and offsets) and those before its first slot.  A
+// slot's row is its expert's offset + the expert's slots before the
+// workgroup + those of the workgroup's earlier tokens + its rank among the
+// token's slots of that expert: the same rows as the two-kernel path (slot
+// order within each expert), with no communication between workgroups.
+// ---------------------------------------------------------------------------
+#define PERM_SMALL_SLOTS 16384
+#define PSM_TOK 16
+template <int OUT>
+__global__ __launch_bounds__(64 * PSM_TOK) void k_permute_small(int T, int K, int E_global, int e0, int L,
+                                                                int64_t capacity, int row_bytes,
+                                                                const uint8_t* __restrict__ x,
+                                                                const int16_t* __restrict__ ids,
+                                                                int32_t* __restrict__ counts,
+                                                                int32_t* __restrict__ offsets,
+                                                                uint8_t* __restrict__ x_perm,
+                                                                uint8_t* __restrict__ x_scales,
+                                                                int32_t* __restrict__ row_to_slot,
+                                                                int32_t* __restrict__ slot_to_row, int32_t* err) {
+  __shared__ int32_t s_tot[PSM_TOK][64];  // per wavefront: its share of the batch's slots, per expert
+  __shared__ int32_t s_bef[PSM_TOK][64];  // ... of those before the workgroup's first slot
+  __shared__ int32_t s_tok[PSM_TOK][64];  // per token of the workgroup
+  __shared__ int32_t s_base[64];          // offset + the expert's slots before the workgroup
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+  const int t = blockIdx.x * PSM_TOK + w;
+  const bool active = t < T;
+  const long nslot = (long)T * K, s0 = (long)blockIdx.x * PSM_TOK * K;
+  s_tot[w][l] = 0;
+  s_bef[w][l] = 0;
+  s_tok[w][l] = 0;
+  const long f = (long)t * K + l;
+  int le = -1;
+  if (active && l < K) {
+    const int id = ids[f];
+    if (id >= e0 && id < e0 + L && id < E_global) le = id - e0;
+  }
+  const uint64_t local = wave_ballot(le >= 0);
+  // the batch's ids first (slot u * 64 * PSM_TOK + 64 w + l in id[u]), then
+  // the row's first 8 KiB: the count waits only for the ids, which were
+  // issued first, while the row is still loading
+  // (buffer loads, unconditional: reads past a buffer's end return zeros
+  // without touching memory, so the compiler sees no branches and waits for
+  // the ids alone)
+  int id[PERM_SMALL_SLOTS / (64 * PSM_TOK)];
+  const __amdgpu_buffer_rsrc_t rid =
+      __builtin_amdgcn_make_buffer_rsrc((void*)ids, (short)0, (int)(nslot * 2), 0x00020000);
+#pragma unroll
+  for (int u = 0; u < PERM_SMALL_SLOTS / (64 * PSM_TOK); ++u) {
+    const int i = u * 64 * PSM_TOK + w * 64 + l;
+    id[u] = (int)(int16_t)__builtin_amdgcn_raw_buffer_load_b16(rid, 2 * i, 0, 0);
+  }
+  __builtin_amdgcn_sched_barrier(0);  // keep the id loads ahead of the row loads
+  const uint8_t* src = x + (long)(active ? t : 0) * row_bytes;
+  const int npiece = (row_bytes + 1023) / 1024;
+  // the row's bytes, or none for a token without a local slot
+  const __amdgpu_buffer_rsrc_t rrow =
+      __builtin_amdgcn_make_buffer_rsrc((void*)src, (short)0, local ? row_bytes : 0, 0x00020000);
+  u32x4 v[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) v[j] = __builtin_amdgcn_raw_buffer_load_b128(rrow, j * 1024 + l * 16, 0, 0);
+  lds_barrier();  // the counts are zero (the row loads stay in flight)
+  bool bad = false;
+#pragma unroll
+  for (int u = 0; u < PERM_SMALL_SLOTS / (64 * PSM_TOK); ++u) {
+    const long i = (long)u * 64 * PSM_TOK + w * 64 + l;
+    if (i >= nslot) id[u] = -1;
+    bad |= id[u] < -1 || id[u] >= E_global;
+    if (id[u] >= e0 && id[u] < e0 + L && id[u] < E_global) {
+      __hip_atomic_fetch_add(&s_tot[w][id[u] - e0], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      if (i < s0) __hip_atomic_fetch_add(&s_bef[w][id[u] - e0], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    }
+  }
+  if (blockIdx.x == 0 && wave_ballot(bad) && l == 0) set_err(err, MOE_DEVERR_BAD_ID);
+  if (le >= 0) __hip_atomic_fetch_add(&s_tok[w][le], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  lds_barrier();
+  if (w == 0) {  // lane e: expert e's total, offset and base
+    int tot = 0, bef = 0;
+    if (l < L)
+      for (int u = 0; u < PSM_TOK; ++u) {
+        tot += s_tot[u][l];
+        bef += s_bef[u][l];
+      }
+    const int incl = wave_incl_scan(tot);
+    s_base[l] = incl - tot + bef;
+    if (blockIdx.x == 0) {
+      if (l < L) {
+        counts[l] = tot;
+        offsets[l] = incl - tot;
+      }
+      if (l == 63) {
+        offsets[L] = incl;
+        if ((int64_t)incl > capacity) set_err(err, MOE_DEVERR_OVERFLOW);
+      }
+    }
+  }
+  lds_barrier();
+  if (!active) return;
+  int dest = -1;
+  if (l < K) {
+    if (le >= 0) {
+      int pre = 0;  // the expert's slots in the workgroup's earlier tokens
+      for (int u = 0; u < w; ++u) pre += s_tok[u][le];
+      int nbits = 0;
+      while ((1 << nbits) < L) ++nbits;
+      const uint64_t peers = same_expert_lanes(le, local, nbits);
+      const int64_t d = (int64_t)s_base[le] + pre + __builtin_popcountll(peers & ((1ull << l) - 1));
+      dest = (d >= 0 && d < capacity) ? (int)d : -1;
+    }
+    slot_to_row[f] = dest;
+  }
+  permute_rows<OUT>(t, K, l, dest, npiece, row_bytes, src, v, x_perm, x_scales, row_to_slot);
+}
+
 // counts and offsets of an empty batch
 __global__ void k_zero_counts(int L, int32_t* __restrict__ counts, int32_t* __restrict__ offsets) {
   for (int e = threadIdx.x; e <= L; e += blockDim.x) {
@@ -576,6 +710,21 @@ hipError_t launch_permute(int T, int H, int K, int E_global, int e0, int L, int6
     hipLaunchKernelGGL(k_zero_counts, dim3(1), dim3(256), 0, s, L, counts, offsets);
     return hipGetLastError();
   }
+  const int row_bytes = H * (x_dtype == MOE_F32 ? 4 : 2);
+  if ((long)T * K <= PERM_SMALL_SLOTS && L <= 64) {  // one kernel, no workspace
+    const dim3 g((T + PSM_TOK - 1) / PSM_TOK), b(64 * PSM_TOK);
+#define PERMUTE_SMALL_ARGS                                                                                    \
+  T, K, E_global, e0, L, capacity, row_bytes, (const uint8_t*)x, ids, counts, offsets, (uint8_t*)x_perm,      \
+      x_scales, row_to_slot, slot_to_row, err
+    if (out_dtype == MOE_MXFP8)
+      hipLaunchKernelGGL(k_permute_small<1>, g, b, 0, s, PERMUTE_SMALL_ARGS);
+    else if (out_dtype == MOE_MXFP4)
+      hipLaunchKernelGGL(k_permute_small<2>, g, b, 0, s, PERMUTE_SMALL_ARGS);
+    else
+      hipLaunchKernelGGL(k_permute_small<0>, g, b, 0, s, PERMUTE_SMALL_ARGS);
+#undef PERMUTE_SMALL_ARGS
+    return hipGetLastError();
+  }
   const int TT = permute_tile_tokens(T, K, L);
   const int ntiles = (T + TT - 1) / TT;
   const PermuteWs w = permute_ws(ws, ntiles, L);
@@ -591,7 +740,6 @@ hipError_t launch_permute(int T, int H, int K, int E_global, int e0, int L, int6
   hipLaunchKernelGGL(k_count_scan, dim3(ntiles), dim3(PERM_THREADS), lds, s, T, K, E_global, e0, L, TT, ntiles, fold,
                      capacity, ids,
                      w.done, w.flags, w.tilebase, w.rank, counts, offsets, err);
-  const int row_bytes = H * (x_dtype == MOE_F32 ? 4 : 2);
   const dim3 g((T + 3) / 4), b(256);
 #define PERMUTE_ARGS                                                                                          \
   T, K, e0, L, TT, ntiles, fold, capacity, row_bytes, (const uint8_t*)x, ids, (const int32_t*)w.tilebase,     \

@@ -246,13 +246,16 @@ int moe_route_topk_grouped(int T, int E, int K, int H, int n_group, int topk_gro
  * x_perm receives packed E2M1 codes [capacity,H/2] uint8 and x_perm_scales
  * the E8M0 scales [capacity,H/32] (scale exponent floor(log2 max|v|) - 2,
  * round to nearest even, saturate at 6).
- * Two kernels: the first counts tiles of consecutive tokens (one workgroup
- * per tile, ids staged in LDS), gives each local slot its row within its
- * tile and expert, and publishes the tile's counts; the workgroup that
- * finishes last scans all tiles' counts (each tile's base row per expert,
- * the expert counts and offsets: a single-pass scan in which no workgroup
- * waits for another).  The second moves (or MX-quantizes) each token's row
- * to its rows.
+ * Batches of at most 16384 slots (T * K) with at most 64 local experts run
+ * one kernel that leaves the workspace untouched: each workgroup of 16
+ * tokens counts every slot of the batch itself while its rows load, then
+ * moves them.  Larger batches run two kernels: the first counts tiles of
+ * consecutive tokens (one workgroup per tile, ids staged in LDS), gives each
+ * local slot its row within its tile and expert, and publishes the tile's
+ * counts; the workgroup that finishes last scans all tiles' counts (each
+ * tile's base row per expert, the expert counts and offsets: a single-pass
+ * scan in which no workgroup waits for another).  The second moves (or
+ * MX-quantizes) each token's row to its rows.  Both give the same rows.
  * Workspace: moe_permute_workspace_bytes(T, K, L) bytes, zero-filled before
  * its first use; each call returns its state (a counter and the tile counts,
  * the first bytes) to zero when its kernels end, so one workspace serves any
