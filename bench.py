@@ -628,6 +628,7 @@ def main():
                      "dtype": "bf16", "data": "synthetic"})
         print(json.dumps(line), flush=True)
         return
+    import dropless_mixture_experts_radix_amd as D
     calibration_copy()
     ceil = measure_ceilings()
     cfg, layer, x, r = build("mixtral_bf16")
@@ -641,6 +642,11 @@ def main():
            "combine": layer.combine}
     cold = {k: dist_cold(f, a.iters, flush) for k, f in fns.items()}
     warm = {k: dist_warm(f, a.iters, inner=2 if k == "grouped_mlp" else 8) for k, f in fns.items()}
+    # the floor of a cold route: the library's streaming read of the same x
+    # (33.5 MB), each call after the same flush
+    xr = x.view(torch.uint8).reshape(-1)
+    red = torch.empty(D.moe_calib_read_out_words(xr.numel()), dtype=torch.int32, device="cuda")
+    read_x = dist_cold(lambda: D.moe_calib_read(xr, red), a.iters, flush)
     layer_cold = dist_cold(lambda: layer.forward(x), a.iters, flush)
     layer_warm = dist_warm(lambda: layer.forward(x), a.iters, inner=2)
     gus = time_graph(layer, x, a.steps)
@@ -687,6 +693,9 @@ def main():
         "frac_of_measured_ceiling": {**{k: round(v / ceiling_of[k], 3) for k, v in gbs.items()},
                                      "grouped_mlp": round(tflops / ceil["mfma_bf16_tflops"], 3)},
         "ceilings": ceil,
+        "cold_read_x_us": pct(read_x),
+        "cold_read_x_note": "the library's streaming read (moe_calib_read) of x alone, cold like the stages: the "
+                            "floor under a cold route, which must read x",
         "roofline": {"kernel": "moe_grouped_mlp: k_gemm_bf16<1> (GEMM1+SwiGLU) + k_gemm_bf16<0> (GEMM2) "
                                "+ k_splitk_reduce<1,0>",
                      "bound": "mfma", "achieved": round(tflops, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",

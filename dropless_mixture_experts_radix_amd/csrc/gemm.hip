@@ -85,13 +85,13 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 #define GB_BN 256
 #define GB_BK 32
 #define GB_THREADS 512
-#define GB_X_OFF 32768              // the 32 extra A rows of a tall tile, after A and B
-#define GB_STAGE_BYTES (GB_X_OFF + 2048)
-#define GB_TALL 32                  // rows a tall tile has beyond GB_BM
+#define GB_X_OFF 32768              // the 64 extra A rows of a tall tile, after A and B
+#define GB_STAGE_BYTES (GB_X_OFF + 4096)
+#define GB_TALL 64                  // rows a tall tile has beyond GB_BM
 // a split-K partial tile: the 8 wavefront parts of 128 x 64, then the 32 x 64
-// extra-row blocks of wavefronts 0-3 (tall tiles)
+// extra-row blocks of the 8 wavefronts (tall tiles)
 #define GB_PART_X (GB_BM * GB_BN)
-#define GB_PART_FLOATS (GB_PART_X + 4 * 2048)
+#define GB_PART_FLOATS (GB_PART_X + 8 * 2048)
 
 // split plan of the bf16 kernel: pieces are whole groups of 4 k steps
 __device__ __forceinline__ SplitPlan gb_split_plan(int total, int G, int Kd) {
@@ -101,8 +101,9 @@ __device__ __forceinline__ SplitPlan gb_split_plan(int total, int G, int Kd) {
 static inline bool gb_may_split(int Kd) { return split_max_pieces(Kd / 64) >= 2; }
 
 // Tile schedule and split plan of the bf16 kernel on a grid of G workgroups,
-// with tall tiles: a remainder of up to GB_TALL rows joins the expert's last
-// full tile, which then has up to GB_BM + GB_TALL rows.
+// with tall tiles: an expert takes the fewest tiles of at most GB_BM + GB_TALL
+// rows (tall tiles of GB_BM + up to GB_TALL rows where GB_BM rows per tile do
+// not cover its rows).
 __device__ __forceinline__ SplitPlan gb_schedule(int L, int64_t capacity, int NT, int Kd, int G,
                                                  const int32_t* __restrict__ offsets, int32_t* s_pre,
                                                  int32_t* s_tmp) {
@@ -292,7 +293,7 @@ __global__ __launch_bounds__(GB_THREADS, 1) void k_gemm_bf16(int L, int N, int K
     TileInfo ti;
     int piece, k0, k1, akstep, bkstep;
     __amdgpu_buffer_rsrc_t rA, rB;
-    int va[2], vb[2], vx;
+    int va[2], vb[2], vx[2];
   };
   auto setup = [&](int u) {
     Unit w;
@@ -370,10 +371,11 @@ __global__ __launch_bounds__(GB_THREADS, 1) void k_gemm_bf16(int L, int N, int K
       w.va[q] = (EPI != 0 && EPI != 5) ? (r * Kd + dch * 8) * 2 : ((w.ti.row0 + r) * GB_BK + dch * 8) * 2;
       w.vb[q] = EPI == 2 ? (r * Kd + dch * 8) * 2 : r * 64 + dch * 16;
     }
-    {  // the dword of the extra rows (tall tile) that this lane moves: row
-       // GB_BM + 4 wv + l/16, chunk position (l%16)/4, dword l%4
-      const int xr = 4 * wv + (l >> 4), xc = (((l & 15) >> 2) ^ swz4(xr)) * 16 + (l & 3) * 4;
-      w.vx = EPI != 0 ? (GB_BM + xr) * Kd * 2 + xc : ((w.ti.row0 + GB_BM + xr) * GB_BK) * 2 + xc;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {  // the two dwords of the extra rows (tall tile) that this lane moves: row
+                                   // GB_BM + 4 (wv + 8h) + l/16, chunk position (l%16)/4, dword l%4
+      const int xr = 4 * (wv + 8 * h) + (l >> 4), xc = (((l & 15) >> 2) ^ swz4(xr)) * 16 + (l & 3) * 4;
+      w.vx[h] = EPI != 0 ? (GB_BM + xr) * Kd * 2 + xc : ((w.ti.row0 + GB_BM + xr) * GB_BK) * 2 + xc;
     }
     w.akstep = (EPI != 0 && EPI != 5) ? GB_BK * 2 : (int)(capacity * GB_BK * 2);
     w.bkstep = EPI == 2 ? GB_BK * 2 : EPI == 5 ? N * GB_BK * 2 : GB_BN * GB_BK * 2;
@@ -383,8 +385,9 @@ __global__ __launch_bounds__(GB_THREADS, 1) void k_gemm_bf16(int L, int N, int K
 #define GB_DMA(W, ST, KT_, Q)                                                               \
   {                                                                                         \
     const int kq = (KT_);                                                                   \
-    if ((Q) == 4)                                                                           \
-      lds_dma_b32(lds0 + (ST) * GB_STAGE_BYTES + GB_X_OFF + wv * 256, (W).vx, (W).rA, kq * (W).akstep); \
+    if ((Q) >= 4)                                                                           \
+      lds_dma_b32(lds0 + (ST) * GB_STAGE_BYTES + GB_X_OFF + (wv + 8 * ((Q) - 4)) * 256, (W).vx[(Q) - 4], (W).rA, \
+                  kq * (W).akstep);                                                         \
     else if ((Q) < 2)                                                                       \
       lds_dma_b128(lds0 + (ST) * GB_STAGE_BYTES + (wv * 2 + (Q)) * 1024, (W).va[Q], (W).rA, kq * (W).akstep); \
     else                                                                                    \
@@ -392,12 +395,12 @@ __global__ __launch_bounds__(GB_THREADS, 1) void k_gemm_bf16(int L, int N, int K
                    kq * (W).bkstep);                                                        \
   }
 // the ring prologue of a unit: its steps k0 .. k0+2 into stages 0..2 (a tall
-// tile's steps also carry its extra rows: 5 loads per step instead of 4)
+// tile's steps also carry its extra rows: 6 loads per step instead of 4)
 #define GB_PROLOGUE(W)                                                                      \
   {                                                                                         \
     if ((W).ti.rows > GB_BM) {                                                              \
       _Pragma("unroll") for (int st = 0; st < 3; ++st) {                                    \
-        _Pragma("unroll") for (int q = 0; q < 5; ++q) GB_DMA(W, st, min((W).k0 + st, (W).k1 - 1), q); \
+        _Pragma("unroll") for (int q = 0; q < 6; ++q) GB_DMA(W, st, min((W).k0 + st, (W).k1 - 1), q); \
       }                                                                                     \
     } else {                                                                                \
       _Pragma("unroll") for (int st = 0; st < 3; ++st) {                                    \
@@ -414,7 +417,7 @@ __global__ __launch_bounds__(GB_THREADS, 1) void k_gemm_bf16(int L, int N, int K
       _Pragma("unroll") for (int j = 0; j < 2; ++j) FB[j] = *(const bf16x8*)(pb + j * 2048); \
     }                                                                                       \
   }
-#define GB_READX(FX, ST, FR) FX = *(const bf16x8*)(smem + (ST) * GB_STAGE_BYTES + GB_X_OFF + (FR));
+#define GB_READX(FX, ST, FR) FX = *(const bf16x8*)(smem + (ST) * GB_STAGE_BYTES + GB_X_OFF + wm * 2048 + (FR));
 #define GB_MMA1(FA, FB, T)                                                                  \
   acc[(T) >> 1][(T) & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(FA[(T) >> 1], FB[(T) & 1], acc[(T) >> 1][(T) & 1], 0, 0, 0);
 #define GB_FENCE __builtin_amdgcn_sched_barrier(0);
@@ -463,7 +466,7 @@ __global__ __launch_bounds__(GB_THREADS, 1) void k_gemm_bf16(int L, int N, int K
         const int kn = min(kt + h + 3, k1 - 1);                                             \
         _Pragma("unroll") for (int q = 0; q < (NL); ++q) GB_DMA(cu, (h + 3) & 3, kn, q);   \
       }                                                                                     \
-      if ((NL) == 5) asm volatile("s_waitcnt vmcnt(10) lgkmcnt(0)\n\ts_barrier" ::: "memory"); \
+      if ((NL) == 6) asm volatile("s_waitcnt vmcnt(12) lgkmcnt(0)\n\ts_barrier" ::: "memory"); \
       else asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory");       \
       GB_FENCE;                                                                             \
       _Pragma("unroll") for (int t = 0; t < 8; ++t) {                                       \
@@ -481,7 +484,7 @@ __global__ __launch_bounds__(GB_THREADS, 1) void k_gemm_bf16(int L, int N, int K
         accx[0][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fx[1], fb[1][1], accx[0][1], 0, 0, 0); \
       }                                                                                     \
       GB_FENCE;                                                                             \
-      if ((NL) == 5) asm volatile("s_waitcnt vmcnt(10)\n\ts_barrier" ::: "memory");       \
+      if ((NL) == 6) asm volatile("s_waitcnt vmcnt(12)\n\ts_barrier" ::: "memory");       \
       else asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");                  \
     }                                                                                       \
   }
@@ -489,13 +492,14 @@ __global__ __launch_bounds__(GB_THREADS, 1) void k_gemm_bf16(int L, int N, int K
     // its 128 rows that hold rows of the tile (the short last tile of an
     // expert); all versions of the loop have the same loads and barriers.  A
     // tall tile (GB_BM + up to GB_TALL rows) moves its extra rows with a fifth
-    // load per step in every wavefront, and wavefronts 0-3 multiply them by
-    // the B fragments they hold (rows 256.. of their 64 columns).
+    // and sixth load per step in every wavefront, and wavefront (wm, wn)
+    // multiplies extra rows 32 wm .. 32 wm + 31 (when the tile has them) by
+    // the B fragments it holds (its 64 columns).
     if (cu.ti.rows > GB_BM) {
-      if (wm == 0) {
-        GB_KLOOP(4, 5, 1);
+      if (cu.ti.rows > GB_BM + 32 * wm) {
+        GB_KLOOP(4, 6, 1);
       } else {
-        GB_KLOOP(4, 5, 0);
+        GB_KLOOP(4, 6, 0);
       }
     } else {
       switch (min(4, max(0, (cu.ti.rows - wm * 128 + 31) / 32))) {
@@ -536,8 +540,8 @@ __global__ __launch_bounds__(GB_THREADS, 1) void k_gemm_bf16(int L, int N, int K
         store_tile_lds<EPI>(acc, done.ti, N, capacity, wm, wn, g, r32, l, smem + 3 * GB_STAGE_BYTES + wv * 4096, out);
       else
         store_tile<EPI, 4>(acc, 0, done.ti, N, capacity, wm, wn, g, r32, out, aux);
-      if (done.ti.rows > GB_BM && wm == 0)
-        store_tile<EPI, 1>(accx, 8, done.ti, N, capacity, 0, wn, g, r32, out, aux);
+      if (done.ti.rows > GB_BM + 32 * wm)
+        store_tile<EPI, 1>(accx, 8 + wm, done.ti, N, capacity, 0, wn, g, r32, out, aux);
     } else {
       // partial tile, per wavefront [i][j][lane][16 values of the MFMA D layout]
       float* dst = part + (long)done.piece * GB_PART_FLOATS + wv * 8192 + l * 16;
@@ -549,7 +553,7 @@ __global__ __launch_bounds__(GB_THREADS, 1) void k_gemm_bf16(int L, int N, int K
           for (int c = 0; c < 4; ++c)
             *(f32x4*)(dst + (i * 2 + j) * 1024 + c * 4) =
                 f32x4{acc[i][j][4 * c], acc[i][j][4 * c + 1], acc[i][j][4 * c + 2], acc[i][j][4 * c + 3]};
-      if (done.ti.rows > GB_BM && wm == 0) {  // the extra rows: [wavefront][j][lane][16]
+      if (done.ti.rows > GB_BM + 32 * wm) {  // the extra rows: [wavefront][j][lane][16]
         float* dx = part + (long)done.piece * GB_PART_FLOATS + GB_PART_X + wv * 2048 + l * 16;
 #pragma unroll
         for (int j = 0; j < 2; ++j)
@@ -574,7 +578,7 @@ __global__ __launch_bounds__(GB_THREADS, 1) void k_gemm_bf16(int L, int N, int K
 // epilogue.  Launched with the GEMM's grid size G on GEMM_SPLIT_UNITS / 2 x 8
 // workgroups of five wavefronts: workgroup (b, w) handles the part of GEMM
 // wavefront w of split tile b of the plan, its wavefront i < 4 row block i,
-// and its wavefront 4 the extra rows of a tall tile (GEMM wavefronts 0-3).
+// and its wavefront 4 GEMM wavefront w's extra rows of a tall tile.
 template <int EPI>
 __global__ __launch_bounds__(320) void k_splitk_reduce(int L, int N, int Kd, int64_t capacity, int G,
                                                        const int32_t* __restrict__ offsets,
@@ -595,9 +599,9 @@ __global__ __launch_bounds__(320) void k_splitk_reduce(int L, int N, int Kd, int
     sum_partials(src + wv * 8192 + i * 2048, plan.S, acc, GB_PART_FLOATS);
     store_tile<EPI, 1>(acc, i, ti, N, capacity, wv >> 2, wv & 3, l >> 5, l & 31, out, aux);
   } else {
-    if (wv >= 4 || ti.rows <= GB_BM) return;
+    if (ti.rows <= GB_BM + 32 * (wv >> 2)) return;
     sum_partials(src + GB_PART_X + wv * 2048, plan.S, acc, GB_PART_FLOATS);
-    store_tile<EPI, 1>(acc, 8, ti, N, capacity, 0, wv, l >> 5, l & 31, out, aux);
+    store_tile<EPI, 1>(acc, 8 + (wv >> 2), ti, N, capacity, 0, wv & 3, l >> 5, l & 31, out, aux);
   }
 }
 

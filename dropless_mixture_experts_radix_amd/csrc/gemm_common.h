@@ -21,12 +21,26 @@ static inline int num_cus() {
 // Device tile schedule.  s_pre[e] = first tile of expert e, s_pre[L] = total.
 // Row range of expert e: [min(offsets[e], cap), min(offsets[e+1], cap)).
 // ---------------------------------------------------------------------------
-// Row tiles of an expert with m rows: ceil(m/BM); with tall > 0, a remainder
-// of at most `tall` rows after at least one full tile joins the last full tile
-// instead (that tile then has BM + remainder rows).
-__device__ __forceinline__ int row_tiles(int m, int BM, int tall) {
-  const int f = m / BM, r = m - f * BM;
-  return (r > 0 && (r > tall || f == 0)) ? f + 1 : f;
+// Row tiles of an expert with m rows: the fewest tiles of at most BM + tall
+// rows, ceil(m / (BM + tall)) (tall = 0: ceil(m / BM)).
+__device__ __forceinline__ int row_tiles(int m, int BM, int tall) { return (m + BM + tall - 1) / (BM + tall); }
+
+// First row (within the expert) and row count of row tile i of an expert with
+// m rows in nt = row_tiles(m, BM, tall) tiles.  When nt tiles of BM rows hold
+// the m rows, they are BM rows each and the last takes the remainder;
+// otherwise every tile has BM rows plus extra rows, `tall` each for the first
+// ones, then what is left for one tile, then none (tall tiles; tall = 0
+// never gets here).
+__device__ __forceinline__ void tile_rows(int m, int nt, int BM, int tall, int i, int* r0, int* rows) {
+  const int ex = m - nt * BM;  // rows beyond nt tiles of BM
+  if (ex <= 0) {
+    *r0 = i * BM;
+    *rows = min(BM, m - i * BM);
+    return;
+  }
+  const int q = ex / tall, rem = ex - q * tall;  // tiles [0, q) take `tall` extra rows, tile q takes rem
+  *r0 = i * BM + min(i, q) * tall + (i > q ? rem : 0);
+  *rows = BM + (i < q ? tall : (i == q ? rem : 0));
 }
 
 __device__ inline void build_schedule(int L, int64_t capacity, int BM, int NT, const int32_t* __restrict__ offsets,
@@ -121,8 +135,10 @@ __device__ __forceinline__ TileInfo locate_tile(int it, int L, int64_t capacity,
   ti.e = e;
   ti.nt = rem / mg;
   const int mt = g * TILE_MGROUP + rem % mg;
-  ti.row0 = (int)r0 + mt * BM;
-  ti.rows = mt == mt_e - 1 ? m - mt * BM : BM;  // the last one takes the remainder
+  int tr0, trows;
+  tile_rows(m, mt_e, BM, tall, mt, &tr0, &trows);
+  ti.row0 = (int)r0 + tr0;
+  ti.rows = trows;
   return ti;
 }
 

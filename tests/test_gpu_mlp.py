@@ -225,9 +225,14 @@ def test_grouped_mlp_f32(counts, H, F):
     # k = 4096, 32 groups), tall tiles among them
     (MIXTRAL_COUNTS, 3584, 256),
     (MIXTRAL_COUNTS, 512, 4096),
-    # tall tiles: remainders of 1, 16 and 32 rows join the expert's last full
-    # tile (257, 272, 288, 544 rows); 289 rows and a lone 31 do not
+    # tall tiles (an expert takes ceil(m / 320) tiles of up to 256 + 64 rows):
+    # 257-321 rows in one tile (the extra rows of one or both wavefront
+    # groups), 544 as 288 + 256, a lone 31
     ([257, 272, 288, 289, 544, 0, 31], 512, 512),
+    # the extra rows spread over an expert's first tiles: 1124 = 320 + 292 +
+    # 256 + 256, 1201 = 320 + 320 + 305 + 256, 1088 = 320 + 3 x 256, and 321
+    # as 256 + 65
+    ([1124, 320, 321, 1201, 0, 7, 1088], 512, 512),
     # tall tiles in whole rounds of the first GEMM (256 tiles on 256 CUs)
     ([1054, 994, 1030, 1018, 1040, 1008, 1024, 1024], 512, 1024),
 ])
@@ -244,8 +249,8 @@ def test_grouped_mlp_bf16(counts, H, F):
     # into 2 pieces (first GEMM: k = 4096; second GEMM: k = 4096)
     (MIXTRAL_COUNTS, 4096, 256),
     (MIXTRAL_COUNTS, 512, 4096),
-    # tall tiles: remainders of 1, 16 and 32 rows join the expert's last full
-    # tile (257, 272, 288, 544 rows); 289 rows and a lone 31 do not
+    # tall tiles (an expert takes ceil(m / 288) tiles of up to 256 + 32 rows):
+    # 257-288 rows in one tile, 289 as 256 + 33, 544 as 288 + 256, a lone 31
     ([257, 272, 288, 289, 544, 0, 31], 512, 512),
     ([1054, 994, 1030, 1018, 1040, 1008, 1024, 1024], 512, 1024),
 ])

@@ -122,6 +122,7 @@ def _check_dh_mx(ws, cap, H, F, L, offsets, rows, x, dy, W1, W2):
     ([70, 300, 0, 5], 384, 128),                      # partial column tiles in all three GEMMs
     ([0, 0, 0], 128, 128),                            # no rows
     (MIXTRAL_COUNTS, 512, 512),                       # split-K pieces with tall tiles
+    ([1124, 320, 321, 1201, 0, 7], 256, 256),         # extra rows over an expert's first tiles
 ])
 def test_grouped_mlp_backward_data(counts, H, F):
     _run(counts, H, F, seed=sum(counts) + H + F)
