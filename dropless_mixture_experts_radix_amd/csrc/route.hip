@@ -862,6 +862,9 @@ hipError_t launch_route_select(int T, int E, int K, int S, int score, const floa
     else if (E <= 1024)
       hipLaunchKernelGGL((k_route_select_wave<16, false>), g, b, 0, s, T, E, K, S, score, partial, bias, mask,
                          ids, probs, logits_out, err, g0, nullptr);
+    else if (E <= 2304)
+      hipLaunchKernelGGL((k_route_select_wave<36, false>), g, b, 0, s, T, E, K, S, score, partial, bias, mask,
+                         ids, probs, logits_out, err, g0, nullptr);
     else if (E <= 2560)
       hipLaunchKernelGGL((k_route_select_wave<40, false>), g, b, 0, s, T, E, K, S, score, partial, bias, mask,
                          ids, probs, logits_out, err, g0, nullptr);
