@@ -197,6 +197,12 @@ __device__ __forceinline__ bool count_pass(int nslot, int e0, int L, int E_globa
   return bad;
 }
 
+// A workgroup barrier that waits only for this wavefront's LDS operations:
+// __syncthreads also waits for every outstanding global load and store (the
+// slot ranks, the published counts, the rows in flight), which nothing
+// behind these barriers reads.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 // Expert totals (LDS) -> counts, offsets (exclusive scan, offsets[L] = N),
 // MOE_DEVERR_OVERFLOW when N > capacity; all threads of the workgroup.
 __device__ __forceinline__ void expert_offsets(int L, int64_t capacity, const int32_t* tot, int32_t* __restrict__ counts,
@@ -209,7 +215,7 @@ __device__ __forceinline__ void expert_offsets(int L, int64_t capacity, const in
     if (b0 + i < L) loc += tot[b0 + i];
   const int incl = wave_incl_scan(loc);
   if (l == 63) s_wsum[w] = incl;
-  __syncthreads();
+  lds_barrier();
   int r = incl - loc;
   for (int i = 0; i < w; ++i) r += s_wsum[i];
   for (int i = 0; i < per; ++i) {
@@ -269,9 +275,9 @@ __global__ __launch_bounds__(PERM_THREADS) void k_count_scan(int T, int K, int E
         if (i < n) s_ids[i] = v[u];
       }
     }
-    __syncthreads();
+    lds_barrier();
     bad |= count_pass<0>(n, e0, L, E_global, nbits, s_ids, cnt + w * L, rank, c0);
-    __syncthreads();
+    lds_barrier();
     for (int e = threadIdx.x; e < L; e += PERM_THREADS) {  // each wavefront's running rows start after the earlier slots'
       int r = run[e];
 #pragma unroll
@@ -282,18 +288,18 @@ __global__ __launch_bounds__(PERM_THREADS) void k_count_scan(int T, int K, int E
       }
       run[e] = r;
     }
-    __syncthreads();
+    lds_barrier();
     count_pass<1>(n, e0, L, E_global, nbits, s_ids, cnt + w * L, rank, c0);
-    __syncthreads();
+    lds_barrier();
   }
   if (wave_ballot(bad) && l == 0) set_err(err, MOE_DEVERR_BAD_ID);
   if (fold) {  // few tiles and experts: the permute kernel combines the tiles' counts itself
-    __syncthreads();
+    lds_barrier();
     for (int e = threadIdx.x; e < L; e += PERM_THREADS) tilebase[(long)tile * L + e] = run[e];
     return;
   }
   if (ntiles == 1) {  // the whole batch in one tile: its counts are the totals
-    __syncthreads();
+    lds_barrier();
     for (int e = threadIdx.x; e < L; e += PERM_THREADS) tilebase[e] = 0;
     expert_offsets(L, capacity, run, counts, offsets, err, s_wsum);
     return;
@@ -310,7 +316,7 @@ __global__ __launch_bounds__(PERM_THREADS) void k_count_scan(int T, int K, int E
     if (old >= (uint32_t)ntiles) set_err(err, MOE_DEVERR_WORKSPACE);  // the counter was not zero
     s_last = old == (uint32_t)ntiles - 1;
   }
-  __syncthreads();
+  lds_barrier();
   if (!s_last) return;
   // ---- the last tile to finish: each tile's base row per expert (an
   // exclusive prefix of the counts over the tiles) and each expert's total.
@@ -338,25 +344,25 @@ __global__ __launch_bounds__(PERM_THREADS) void k_count_scan(int T, int K, int E
     int carry = 0;
     for (int p0 = 0; p0 < ntiles; p0 += nbt) {
       const int nb = min(nbt, ntiles - p0), words = nb << lne;
-      __syncthreads();
-      // plain loads, eight in flight per thread: a count read stale reads
-      // unpublished and is polled again
-      for (int i0 = 0; i0 < words; i0 += PERM_THREADS * 8) {
-        uint32_t f[8];
+      lds_barrier();
+      // plain loads, sixteen in flight per thread (one round for up to 8K
+      // counts): a count read stale reads unpublished and is polled again
+      for (int i0 = 0; i0 < words; i0 += PERM_THREADS * 16) {
+        uint32_t f[16];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
+        for (int u = 0; u < 16; ++u) {
           const int i = i0 + u * PERM_THREADS + threadIdx.x, ee = ec + (i & (NE - 1));
           f[u] = (i < words && ee < L) ? __hip_atomic_load(flags + (long)(p0 + (i >> lne)) * L + ee, __ATOMIC_RELAXED,
                                                            __HIP_MEMORY_SCOPE_WORKGROUP)
                                        : PERM_PUBLISHED;
         }
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
+        for (int u = 0; u < 16; ++u) {
           const int i = i0 + u * PERM_THREADS + threadIdx.x;
           if (i < words) s_stage[i] = (int32_t)f[u];
         }
       }
-      __syncthreads();
+      lds_barrier();
       const int per = (nb + R - 1) >> lr, pa = min(nb, rr * per), pe = min(nb, pa + per);
       int mine = 0;
       if (col)
@@ -385,7 +391,7 @@ __global__ __launch_bounds__(PERM_THREADS) void k_count_scan(int T, int K, int E
     }
     if (col && rr == 0) run[e] = carry;
   }
-  __syncthreads();
+  lds_barrier();
   expert_offsets(L, capacity, run, counts, offsets, err, s_wsum);
   if (stuck) set_err(err, MOE_DEVERR_WORKSPACE);
   // the state back to zero for the next call (every tile has published and
@@ -569,10 +575,6 @@ __global__ __launch_bounds__(256) void k_permute(int T, int K, int e0, int L, in
   }
   permute_rows<OUT>(t, K, l, dest, npiece, row_bytes, src, v, x_perm, x_scales, row_to_slot);
 }
-
-// A workgroup barrier that waits only for this wavefront's LDS operations
-// (__syncthreads also waits for every outstanding global load).
-__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 // ---------------------------------------------------------------------------
 // k_permute_small: batches of at most PERM_SMALL_SLOTS slots and at most 64
